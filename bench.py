@@ -1,0 +1,174 @@
+"""Benchmark: C = A*A for R-MAT scale 18, edge factor 16 (262,144 x 262,144).
+
+One step is the whole hot path: spgemm_symbolic + spgemm_numeric (setup,
+light rows, outer product, multisplit levels, accumulation, prefix sums),
+on inputs already resident in HBM. Protocol after the gMAGNUS page
+(Section IV-A): warmup runs, then timed runs, mean reported. Prints one
+JSON line.
+
+value  = intermediate products per second (sum of u(i) over all rows / step time)
+roofline = the dominant kernel's algorithmic bytes per launch / its mean
+           launch time (HIP events recorded by the library on the stream the
+           kernel runs on), against MI355X's 8 TB/s HBM peak
+cpu_baseline = the CPU oracle on a bounded row sample of the same product
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="rmat18_ef16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--tau", type=int, default=0)
+    ap.add_argument("--width", type=int, default=0)
+    ap.add_argument("--cap", type=int, default=0)
+    return ap.parse_args()
+
+
+def cpu_baseline(A, B, target_s: float):
+    """Time the oracle on an evenly spaced row sample sized for ~target_s seconds."""
+    import oracle
+
+    oracle.build(force=False)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    u = oracle.row_products(A, B)
+    total = int(u.sum())
+    frac = 1.0 / 4096
+    while True:
+        step = max(1, int(round(1.0 / frac)))
+        rows = np.arange(0, A.nrows, step, dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.spgemm_rows(A, B, rows, nthreads=cores)
+        dt = time.perf_counter() - t0
+        prods = int(u[rows].sum())
+        if dt >= target_s * 0.5 or step == 1:
+            break
+        frac = min(1.0, frac * max(2.0, min(16.0, target_s / max(dt, 1e-3))))
+    return {"value": prods / dt, "unit": "products/s", "cores": cores, "kind": "oracle",
+            "sample": f"every {step}th row of C ({rows.size} rows, {prods} of {total} products)",
+            "seconds": dt, "gflops": 2.0 * prods / dt / 1e9}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the product is not sharded across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from spgemm_irregular_matrices_amd import binding, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load()
+    A, B = synth.workload(args.workload)
+    dA = binding.DeviceCSR.from_host(A)
+    dB = dA if B is A else binding.DeviceCSR.from_host(B)
+    torch.cuda.synchronize()
+
+    plan = binding.Plan(timing=True, tau_override=args.tau, chunk_width_override=args.width,
+                        nchunks_cap=args.cap)
+
+    def step():
+        rp, nnz = plan.symbolic(dA, dB)
+        col = torch.empty(nnz, dtype=torch.int32, device="cuda")
+        val = torch.empty(nnz, dtype=torch.float64, device="cuda")
+        plan.numeric(dA, dB, rp, col, val)
+        return rp, col, val
+
+    for _ in range(args.warmup):
+        out = step()
+        del out
+    torch.cuda.synchronize()
+
+    per_phase = {}
+    step_ms = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ts = time.perf_counter()
+        out = step()
+        st = plan.stats()   # waits for this step's events
+        step_ms.append((time.perf_counter() - ts) * 1e3)
+        for pn in ("symbolic", "numeric"):
+            for ph, rec in st[pn].items():
+                d = per_phase.setdefault((pn, ph), {"ms": 0.0, "launches": 0, "bytes": 0.0})
+                d["ms"] += rec["ms"]
+                d["launches"] += rec["launches"]
+                d["bytes"] += rec["bytes"]
+        del out
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / args.steps * 1e3
+
+    products = st["sum_products"]
+    value = products * args.steps / elapsed
+
+    # dominant kernel of the heavy path by measured time
+    cands = [k for k in per_phase if k[1] in ("outer_prod", "multisplit", "heavy_accum",
+                                               "histo", "light_accum")]
+    dom = max(cands, key=lambda k: per_phase[k]["ms"])
+    d = per_phase[dom]
+    launch_ms = d["ms"] / max(d["launches"], 1)
+    bytes_per_launch = d["bytes"] / max(d["launches"], 1)
+    achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9 if launch_ms > 0 else 0.0
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": f"{dom[0]}:{dom[1]}", "launch_ms": launch_ms,
+                "bytes_per_launch": bytes_per_launch}
+    heavy_bytes = sum(v["bytes"] for k, v in per_phase.items()
+                      if k[1] in ("outer_prod", "multisplit", "heavy_accum", "histo"))
+    heavy_ms = sum(v["ms"] for k, v in per_phase.items()
+                   if k[1] in ("outer_prod", "multisplit", "heavy_accum", "histo"))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(A, B, args.cpu_seconds)
+
+    line = {
+        "metric": "SpGEMM intermediate products/s (GFLOP/s) and HBM GB/s fraction, R-MAT A*A",
+        "value": value, "unit": "products/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": args.workload, "description": synth.WORKLOADS[args.workload],
+                   "nrows": A.nrows, "nnz_A": A.nnz, "sum_products": products,
+                   "nnz_C": st["nnz_c"], "heavy_rows": st["heavy_rows"],
+                   "heavy_products": st["heavy_products"], "tau": st["tau"],
+                   "vchunks": st["vchunks"], "final_chunk_width": st["final_chunk_width"]},
+        "gflops": 2.0 * value / 1e9,
+        "roofline": roofline,
+        "heavy_path": {"ms_per_step": heavy_ms / args.steps,
+                       "algorithmic_GBps": heavy_bytes / (heavy_ms * 1e-3) / 1e9 if heavy_ms else 0,
+                       "frac": (heavy_bytes / (heavy_ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if heavy_ms else 0},
+        "phase_ms_per_step": {f"{k[0]}:{k[1]}": v["ms"] / args.steps for k, v in per_phase.items()
+                              if v["launches"]},
+        "step_ms_min_max": [min(step_ms), max(step_ms)],
+        "cpu_baseline": cpu,
+    }
+    plan.close()
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

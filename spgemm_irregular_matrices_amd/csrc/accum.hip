@@ -1,0 +1,369 @@
+// Local-memory accumulators (gMAGNUS page, Section III-E).
+//
+// * Hash accumulator, for light rows of C and light chunks of C-hat-reord:
+//   an LDS hash map keyed by column (multiplicative hashing, linear
+//   probing, at least two slots per item element, i.e. alpha = 2), then a
+//   bitonic sort of the table to emit the row or chunk with ascending
+//   columns.
+// * Dense window accumulator, for heavy chunks of the last multisplit level
+//   and for light rows whose output columns fall in a short window (the
+//   "shortened dense accumulator" of banded matrices, Section II-B): an LDS
+//   array over the window plus a one-bit-per-column bitmap; a prefix sum
+//   over the bitmap's word popcounts gives each present column its rank, so
+//   the output comes out sorted without a sort.
+//
+// The symbolic pass counts distinct columns per item; the numeric pass sums
+// values and writes columns and values at the item's output offset.
+#include "kernels.h"
+#include "primitives.h"
+
+namespace sg {
+
+enum { MODE_ROW = 0, MODE_CHUNK = 1 };
+
+struct ItemHdr {
+    int64_t count;  // products (rows) or elements (chunks)
+    int64_t out;    // output index: row id, or chunk's map entry
+    int64_t a0, a1, s0;  // row mode: A entry range and its product offset
+    int64_t start;       // chunk mode: first element
+};
+
+template <int MODE>
+__device__ __forceinline__ ItemHdr load_item(const RowItems& ri, const ChunkItems& ci,
+                                             int64_t p) {
+    ItemHdr h;
+    if constexpr (MODE == MODE_ROW) {
+        int32_t r = ri.perm[p];
+        h.out = r;
+        h.a0 = ri.A.rp[r];
+        h.a1 = ri.A.rp[r + 1];
+        h.s0 = ri.S[h.a0];
+        h.count = ri.S[h.a1] - h.s0;
+        h.start = 0;
+    } else {
+        h.start = ci.rp[p];
+        h.count = ci.rp[p + 1] - h.start;
+        h.out = ci.map[p];
+        h.a0 = h.a1 = h.s0 = 0;
+    }
+    return h;
+}
+
+// Element t of an item. Row mode walks the products of row i in Gustavson
+// order: the product's A entry is the last entry q whose product offset
+// S[q] is <= s0 + t, and its B entry is t's distance from that offset.
+// `cur` is a per-thread cursor over q (t only grows within a thread).
+template <int MODE, bool NUM>
+__device__ __forceinline__ void load_elem(const RowItems& ri, const ChunkItems& ci,
+                                          const ItemHdr& h, int64_t t, int64_t& cur,
+                                          int32_t& col, double& val) {
+    if constexpr (MODE == MODE_ROW) {
+        int64_t target = h.s0 + t;
+        int64_t q = upper_index(ri.S, cur, h.a1, target);
+        cur = q;
+        int32_t k = ri.A.col[q];
+        int64_t b = ri.B.rp[k] + (target - ri.S[q]);
+        col = ri.B.col[b];
+        if constexpr (NUM) val = ri.A.val[q] * ri.B.val[b];
+    } else {
+        col = ci.bcol[h.start + t];
+        if constexpr (NUM) val = ci.bval[h.start + t];
+    }
+}
+
+template <int MODE>
+__device__ __forceinline__ int64_t out_offset(const RowItems& ri, const ChunkItems& ci,
+                                              const ItemHdr& h) {
+    if constexpr (MODE == MODE_ROW) return ri.Crp[h.out];
+    else return ci.off[h.out];
+}
+
+template <int MODE>
+__device__ __forceinline__ void write_count(const RowItems& ri, const ChunkItems& ci,
+                                            const ItemHdr& h, int64_t n) {
+    if constexpr (MODE == MODE_ROW) ri.cnt[h.out] = n;
+    else ci.cnt[h.out] = n;
+}
+
+template <int MODE>
+__device__ __forceinline__ int32_t* out_cols(const RowItems& ri, const ChunkItems& ci) {
+    if constexpr (MODE == MODE_ROW) return ri.Ccol;
+    else return ci.Ccol;
+}
+template <int MODE>
+__device__ __forceinline__ double* out_vals(const RowItems& ri, const ChunkItems& ci) {
+    if constexpr (MODE == MODE_ROW) return ri.Cval;
+    else return ci.Cval;
+}
+
+template <int TW>
+__device__ __forceinline__ int team_exclusive_scan(int v, int* sh, int* total) {
+    if constexpr (TW == kWave) {
+        int inc = wave_inclusive_scan(v);
+        *total = __shfl(inc, kWave - 1, kWave);
+        return inc - v;
+    } else {
+        return block_exclusive_scan<TW>(v, sh, total);
+    }
+}
+
+template <int TW>
+__device__ __forceinline__ int team_sum(int v, int* sh) {
+    if constexpr (TW == kWave) return wave_reduce_sum(v);
+    else return block_reduce_sum<TW>(v, sh);
+}
+
+// ---------------------------------------------------------------- hash
+template <int MODE, bool NUM, int TW, int NI>
+__global__ __launch_bounds__(TW* NI) void k_acc_hash(RowItems ri, ChunkItems ci, int64_t p0,
+                                                     int64_t nitems, int logS) {
+    static_assert(TW == kWave || NI == 1, "block-wide teams hold one item");
+    extern __shared__ int64_t lds_a[];
+    const int S = 1 << logS;
+    const int team = threadIdx.x / TW;
+    const int tt = threadIdx.x % TW;
+    uint32_t* keys = (uint32_t*)lds_a + team * S;
+    double* vals = (double*)((uint32_t*)lds_a + NI * S) + team * S;
+    __shared__ int cnt_sh[NI];
+    __shared__ int red_sh[TW / kWave + 1];
+
+    const int64_t item = (int64_t)blockIdx.x * NI + team;
+    const bool active = item < nitems;
+    ItemHdr h;
+    if (active) h = load_item<MODE>(ri, ci, p0 + item);
+    for (int s = tt; s < S; s += TW) {
+        keys[s] = 0xffffffffu;
+        if constexpr (NUM) vals[s] = 0.0;
+    }
+    if (tt == 0) cnt_sh[team] = 0;
+    __syncthreads();
+
+    int fresh = 0;
+    if (active) {
+        int64_t cur = h.a0;
+        const uint32_t smask = (uint32_t)S - 1;
+        for (int64_t t = tt; t < h.count; t += TW) {
+            int32_t c;
+            double v = 0.0;
+            load_elem<MODE, NUM>(ri, ci, h, t, cur, c, v);
+            uint32_t key = (uint32_t)c;
+            uint32_t slot = (key * 2654435769u) >> (32 - logS);
+            for (;;) {
+                uint32_t old = atomicCAS(&keys[slot], 0xffffffffu, key);
+                if (old == 0xffffffffu) {
+                    ++fresh;
+                    break;
+                }
+                if (old == key) break;
+                slot = (slot + 1) & smask;
+            }
+            if constexpr (NUM) atomicAdd(&vals[slot], v);
+        }
+    }
+    if constexpr (TW == kWave) {
+        fresh = wave_reduce_sum(fresh);
+        if (tt == 0) cnt_sh[team] = fresh;
+    } else {
+        fresh = block_reduce_sum<TW>(fresh, red_sh);
+        if (tt == 0) cnt_sh[team] = fresh;
+    }
+    __syncthreads();
+    const int nnz = cnt_sh[team];
+    if constexpr (!NUM) {
+        if (active && tt == 0) write_count<MODE>(ri, ci, h, nnz);
+        return;
+    } else {
+        // bitonic sort of the whole table; empty slots (0xffffffff) sort last
+        for (int k = 2; k <= S; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int pi = tt; pi < (S >> 1); pi += TW) {
+                    int i = ((pi & ~(j - 1)) << 1) | (pi & (j - 1));
+                    int ix = i | j;
+                    uint32_t ka = keys[i], kb = keys[ix];
+                    bool asc = (i & k) == 0;
+                    if ((ka > kb) == asc) {
+                        keys[i] = kb;
+                        keys[ix] = ka;
+                        double va = vals[i];
+                        vals[i] = vals[ix];
+                        vals[ix] = va;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        if (active) {
+            int64_t off = out_offset<MODE>(ri, ci, h);
+            int32_t* oc = out_cols<MODE>(ri, ci);
+            double* ov = out_vals<MODE>(ri, ci);
+            for (int s = tt; s < nnz; s += TW) {
+                oc[off + s] = (int32_t)keys[s];
+                ov[off + s] = vals[s];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- dense window
+template <int MODE, bool NUM, int TW, int NI>
+__global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, ChunkItems ci, int64_t p0,
+                                                       int64_t nitems, int logW) {
+    static_assert(TW == kWave || NI == 1, "block-wide teams hold one item");
+    extern __shared__ int64_t lds_w[];
+    const int W = 1 << logW;
+    const int NWD = W >> 5;  // bitmap words
+    const int team = threadIdx.x / TW;
+    const int tt = threadIdx.x % TW;
+    double* acc = (double*)lds_w + (NUM ? team * W : 0);
+    uint32_t* bits = (uint32_t*)((double*)lds_w + (NUM ? NI * W : 0)) + team * NWD;
+    int* wpre = (int*)((uint32_t*)((double*)lds_w + (NUM ? NI * W : 0)) + NI * NWD) + team * NWD;
+    __shared__ int red_sh[TW / kWave + 1];
+    __shared__ int32_t lo_sh[NI];
+
+    const int64_t item = (int64_t)blockIdx.x * NI + team;
+    const bool active = item < nitems;
+    ItemHdr h;
+    if (active) h = load_item<MODE>(ri, ci, p0 + item);
+    for (int w = tt; w < NWD; w += TW) bits[w] = 0u;
+    if constexpr (NUM)
+        for (int s = tt; s < W; s += TW) acc[s] = 0.0;
+    if (tt == 0 && active) {
+        if constexpr (MODE == MODE_ROW) {
+            lo_sh[team] = ri.rowlo[h.out];
+        } else {
+            lo_sh[team] = (int32_t)(ci.bcol[h.start] & ~(int32_t)(ci.width - 1));
+        }
+    }
+    __syncthreads();
+    const int32_t lo = active ? lo_sh[team] : 0;
+    if (active) {
+        int64_t cur = h.a0;
+        for (int64_t t = tt; t < h.count; t += TW) {
+            int32_t c;
+            double v = 0.0;
+            load_elem<MODE, NUM>(ri, ci, h, t, cur, c, v);
+            uint32_t idx = (uint32_t)(c - lo);
+            if (idx < (uint32_t)W) {
+                atomicOr(&bits[idx >> 5], 1u << (idx & 31));
+                if constexpr (NUM) atomicAdd(&acc[idx], v);
+            }
+        }
+    }
+    __syncthreads();
+    // each thread owns a contiguous run of bitmap words
+    const int per = (NWD + TW - 1) / TW;
+    const int w0 = min(NWD, tt * per), w1 = min(NWD, w0 + per);
+    int pc = 0;
+    for (int w = w0; w < w1; ++w) pc += __popc(bits[w]);
+    if constexpr (!NUM) {
+        int tot = team_sum<TW>(pc, red_sh);
+        if (active && tt == 0) write_count<MODE>(ri, ci, h, tot);
+    } else {
+        int tot;
+        int pre = team_exclusive_scan<TW>(pc, red_sh, &tot);
+        for (int w = w0; w < w1; ++w) {
+            wpre[w] = pre;
+            pre += __popc(bits[w]);
+        }
+        __syncthreads();
+        if (active) {
+            int64_t off = out_offset<MODE>(ri, ci, h);
+            int32_t* oc = out_cols<MODE>(ri, ci);
+            double* ov = out_vals<MODE>(ri, ci);
+            for (int idx = tt; idx < W; idx += TW) {
+                uint32_t word = bits[idx >> 5];
+                uint32_t bit = 1u << (idx & 31);
+                if (word & bit) {
+                    int rank = wpre[idx >> 5] + __popc(word & (bit - 1));
+                    oc[off + rank] = lo + idx;
+                    ov[off + rank] = acc[idx];
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+template <int MODE, bool NUM, int TW, int NI>
+static void launch_hash(const RowItems& ri, const ChunkItems& ci, int64_t p0, int64_t n, int S,
+                        hipStream_t st) {
+    size_t lds = (size_t)NI * S * (4 + (NUM ? 8 : 0));
+    auto kern = k_acc_hash<MODE, NUM, TW, NI>;
+    SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds));
+    hipLaunchKernelGGL(kern, dim3(grid_1d(ceil_div(n, NI))), dim3(TW * NI), lds, st, ri, ci, p0,
+                       n, ilog2(S));
+    SG_LAUNCH_CHECK();
+}
+
+template <int MODE, bool NUM, int TW, int NI>
+static void launch_window(const RowItems& ri, const ChunkItems& ci, int64_t p0, int64_t n,
+                          int64_t W, hipStream_t st) {
+    if (W < 32 || (W & (W - 1))) throw std::logic_error("window width must be a power of two >= 32");
+    size_t lds = (size_t)NI * ((NUM ? W * 8 : 0) + (W / 32) * 4 * (NUM ? 2 : 1));
+    if (lds > 160 * 1024) throw OverflowError("dense window exceeds LDS");
+    auto kern = k_acc_window<MODE, NUM, TW, NI>;
+    SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds));
+    hipLaunchKernelGGL(kern, dim3(grid_1d(ceil_div(n, NI))), dim3(TW * NI), lds, st, ri, ci, p0,
+                       n, ilog2(W));
+    SG_LAUNCH_CHECK();
+}
+
+template <int MODE, bool NUM>
+static void launch_hash_bin(int hb, const RowItems& ri, const ChunkItems& ci, int64_t p0,
+                            int64_t n, hipStream_t st) {
+    switch (hb) {
+        case 0: launch_hash<MODE, NUM, 64, 4>(ri, ci, p0, n, kHashSlots[0], st); break;
+        case 1: launch_hash<MODE, NUM, 64, 4>(ri, ci, p0, n, kHashSlots[1], st); break;
+        case 2: launch_hash<MODE, NUM, 256, 1>(ri, ci, p0, n, kHashSlots[2], st); break;
+        default: launch_hash<MODE, NUM, 512, 1>(ri, ci, p0, n, kHashSlots[3], st); break;
+    }
+}
+
+template <bool NUM>
+static void rows_impl(const RowItems& it, int bin, int64_t p0, int64_t n, hipStream_t st) {
+    ChunkItems none{};
+    switch (bin) {
+        case RB_WIN64: launch_window<MODE_ROW, NUM, 64, 4>(it, none, p0, n, kWinSmall, st); break;
+        case RB_WIN1024:
+            launch_window<MODE_ROW, NUM, 256, 1>(it, none, p0, n, kWinLarge, st);
+            break;
+        case RB_H128: launch_hash_bin<MODE_ROW, NUM>(0, it, none, p0, n, st); break;
+        case RB_H512: launch_hash_bin<MODE_ROW, NUM>(1, it, none, p0, n, st); break;
+        case RB_H2048: launch_hash_bin<MODE_ROW, NUM>(2, it, none, p0, n, st); break;
+        case RB_H8192: launch_hash_bin<MODE_ROW, NUM>(3, it, none, p0, n, st); break;
+        default: throw std::logic_error("not a light row bin");
+    }
+}
+
+void accumulate_rows(const RowItems& it, int bin, int64_t p0, int64_t n, bool numeric,
+                     hipStream_t st) {
+    if (n <= 0) return;
+    if (numeric) rows_impl<true>(it, bin, p0, n, st);
+    else rows_impl<false>(it, bin, p0, n, st);
+}
+
+template <bool NUM>
+static void chunks_impl(const ChunkItems& it, int bin, int64_t p0, int64_t n, hipStream_t st) {
+    RowItems none{};
+    switch (bin) {
+        case CB_DENSE:
+            launch_window<MODE_CHUNK, NUM, 1024, 1>(none, it, p0, n, it.width, st);
+            break;
+        case CB_H128: launch_hash_bin<MODE_CHUNK, NUM>(0, none, it, p0, n, st); break;
+        case CB_H512: launch_hash_bin<MODE_CHUNK, NUM>(1, none, it, p0, n, st); break;
+        case CB_H2048: launch_hash_bin<MODE_CHUNK, NUM>(2, none, it, p0, n, st); break;
+        case CB_H8192: launch_hash_bin<MODE_CHUNK, NUM>(3, none, it, p0, n, st); break;
+        default: throw std::logic_error("not an accumulated chunk bin");
+    }
+}
+
+void accumulate_chunks(const ChunkItems& it, int bin, int64_t p0, int64_t n, bool numeric,
+                       hipStream_t st) {
+    if (n <= 0) return;
+    if (numeric) chunks_impl<true>(it, bin, p0, n, st);
+    else chunks_impl<false>(it, bin, p0, n, st);
+}
+
+}  // namespace sg

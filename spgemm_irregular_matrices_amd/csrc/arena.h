@@ -1,0 +1,76 @@
+// Plan-owned device workspace: named buffers that only grow.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <string>
+#include <unordered_map>
+
+#include "common.h"
+
+namespace sg {
+
+class Arena {
+  public:
+    Arena() = default;
+    Arena(const Arena&) = delete;
+    Arena& operator=(const Arena&) = delete;
+    ~Arena() { release(); }
+
+    // Device buffer `name` with room for at least `bytes`. Growing frees the
+    // old buffer (hipFree waits for the device, so no kernel still uses it).
+    void* get(const std::string& name, size_t bytes) {
+        Buf& b = bufs_[name];
+        if (bytes == 0) bytes = 1;
+        if (b.cap < bytes) {
+            if (b.p) {
+                (void)hipFree(b.p);
+                total_ -= b.cap;
+                b.p = nullptr;
+                b.cap = 0;
+            }
+            size_t extra = bytes / 8;
+            if (extra > (size_t(256) << 20)) extra = size_t(256) << 20;
+            size_t cap = (bytes + extra + (size_t(2) << 20) - 1) & ~((size_t(2) << 20) - 1);
+            void* p = nullptr;
+            if (hipMalloc(&p, cap) != hipSuccess) {
+                (void)hipGetLastError();
+                // retry without headroom before giving up
+                cap = (bytes + 255) & ~size_t(255);
+                if (hipMalloc(&p, cap) != hipSuccess) {
+                    (void)hipGetLastError();
+                    throw OomError("device workspace '" + name + "' (" + std::to_string(bytes) +
+                                   " bytes)");
+                }
+            }
+            b.p = p;
+            b.cap = cap;
+            total_ += cap;
+        }
+        return b.p;
+    }
+
+    template <class T>
+    T* get(const std::string& name, size_t count) {
+        return static_cast<T*>(get(name, count * sizeof(T)));
+    }
+
+    size_t total_bytes() const { return total_; }
+
+    void release() {
+        for (auto& kv : bufs_)
+            if (kv.second.p) (void)hipFree(kv.second.p);
+        bufs_.clear();
+        total_ = 0;
+    }
+
+  private:
+    struct Buf {
+        void* p = nullptr;
+        size_t cap = 0;
+    };
+    std::unordered_map<std::string, Buf> bufs_;
+    size_t total_ = 0;
+};
+
+}  // namespace sg

@@ -1,0 +1,450 @@
+// Heavy-row path of the gMAGNUS page (Algorithm 3 lines 6-20):
+// masked CSR-to-CSC of the heavy rows, the outer product into C-hat
+// (Section III-B, Algorithm 4), and the hierarchical multisplit that
+// reorders every heavy row into column-range chunks (Section III-C,
+// Algorithm 5), plus the small kernels that turn chunk counts into C's
+// row counts and chunk output offsets.
+#include "kernels.h"
+#include "primitives.h"
+
+namespace sg {
+
+// ---------------------------------------------------------------- C-hat rowptr
+struct HeavyRowProducts {
+    const int64_t* arp;
+    const int64_t* S;
+    const int32_t* hrows;
+    __device__ int64_t operator()(int64_t h) const {
+        int32_t r = hrows[h];
+        return S[arp[r + 1]] - S[arp[r]];
+    }
+};
+
+void heavy_rowptr(const DevCSR& A, const int64_t* S, const int32_t* hrows, int64_t H,
+                  int64_t* chat_rp, Arena& ar, hipStream_t st) {
+    scan_exclusive(HeavyRowProducts{A.rp, S, hrows}, H, chat_rp, ar, st);
+}
+
+// ---------------------------------------------------------------- masked CSR -> CSC
+// One wavefront per heavy row walks its A entries. Entries whose B row is
+// empty produce nothing and are dropped (they would be empty slices).
+__global__ __launch_bounds__(256) void k_csc_count(const int64_t* arp, const int32_t* acol,
+                                                   const int64_t* brp, const int32_t* hrows,
+                                                   int64_t H, int32_t* colcnt) {
+    int64_t h = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    if (h >= H) return;
+    int32_t r = hrows[h];
+    for (int64_t q = arp[r] + lane_id(); q < arp[r + 1]; q += kWave) {
+        int32_t k = acol[q];
+        if (brp[k + 1] > brp[k]) atomicAdd(&colcnt[k], 1);
+    }
+}
+
+// The position of an entry's first product inside its C-hat row is the
+// number of products of the entries before it in the same A row, which the
+// InterOffsets prefix S already holds: no atomics on C-hat.rowPtr are needed.
+__global__ __launch_bounds__(256) void k_csc_fill(const int64_t* arp, const int32_t* acol,
+                                                  const int64_t* brp, const int32_t* hrows,
+                                                  int64_t H, const int64_t* S,
+                                                  const int64_t* chat_rp,
+                                                  unsigned long long* cursor, int32_t* ent_k,
+                                                  int64_t* ent_q, int64_t* ent_dest) {
+    int64_t h = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    if (h >= H) return;
+    int32_t r = hrows[h];
+    int64_t a0 = arp[r];
+    int64_t base = chat_rp[h] - S[a0];
+    for (int64_t q = a0 + lane_id(); q < arp[r + 1]; q += kWave) {
+        int32_t k = acol[q];
+        if (brp[k + 1] > brp[k]) {
+            int64_t slot = (int64_t)atomicAdd(&cursor[k], 1ull);
+            ent_k[slot] = k;
+            ent_q[slot] = q;
+            ent_dest[slot] = base + S[q];
+        }
+    }
+}
+
+struct LoadI32AsI64 {
+    const int32_t* p;
+    __device__ int64_t operator()(int64_t i) const { return p[i]; }
+};
+struct SliceLen {
+    const int32_t* ent_k;
+    const int64_t* brp;
+    __device__ int64_t operator()(int64_t e) const {
+        int32_t k = ent_k[e];
+        return brp[k + 1] - brp[k];
+    }
+};
+
+int64_t masked_csr2csc(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
+                       int64_t H, const int64_t* chat_rp, int32_t** ent_k, int64_t** ent_q,
+                       int64_t** ent_dest, int64_t** P, Arena& ar, hipStream_t st) {
+    int32_t* colcnt = ar.get<int32_t>("csc_colcnt", (size_t)A.m + 1);
+    int64_t* colptr = ar.get<int64_t>("csc_colptr", (size_t)A.m + 1);
+    fill<int32_t>(colcnt, A.m, 0, st);
+    int64_t blocks = ceil_div(H * kWave, 256);
+    hipLaunchKernelGGL(k_csc_count, dim3(grid_1d(blocks)), dim3(256), 0, st, A.rp, A.col, B.rp,
+                       hrows, H, colcnt);
+    SG_LAUNCH_CHECK();
+    scan_exclusive(LoadI32AsI64{colcnt}, A.m, colptr, ar, st);
+    int64_t ne = 0;
+    SG_HIP(hipMemcpyAsync(&ne, colptr + A.m, sizeof(int64_t), hipMemcpyDeviceToHost, st));
+    SG_HIP(hipStreamSynchronize(st));
+    *ent_k = ar.get<int32_t>("csc_ent_k", (size_t)ne);
+    *ent_q = ar.get<int64_t>("csc_ent_q", (size_t)ne);
+    *ent_dest = ar.get<int64_t>("csc_ent_dest", (size_t)ne);
+    *P = ar.get<int64_t>("csc_slice_off", (size_t)ne + 1);
+    unsigned long long* cursor = ar.get<unsigned long long>("csc_cursor", (size_t)A.m + 1);
+    copy<int64_t>((int64_t*)cursor, colptr, A.m, st);
+    hipLaunchKernelGGL(k_csc_fill, dim3(grid_1d(blocks)), dim3(256), 0, st, A.rp, A.col, B.rp,
+                       hrows, H, S, chat_rp, cursor, *ent_k, *ent_q, *ent_dest);
+    SG_LAUNCH_CHECK();
+    scan_exclusive(SliceLen{*ent_k, B.rp}, ne, *P, ar, st);
+    return ne;
+}
+
+// ---------------------------------------------------------------- outer product
+// Static partition of the flattened product space (Section III-B, Fig. 2):
+// work group g takes elements [g*E, (g+1)*E). Each round of 256 elements
+// finds its CSC entry by a binary search in an LDS copy of the flattened
+// offsets P (an element's entry is the last one whose offset <= it); the
+// element's place inside the entry's B row is its distance from that
+// offset. Consecutive threads read consecutive B entries and write
+// consecutive C-hat entries.
+constexpr int kExpandNT = 256;
+constexpr int64_t kExpandEPB = 8192;
+
+template <bool NUM>
+__global__ __launch_bounds__(kExpandNT) void k_expand(ExpandArgs a, int64_t total) {
+    __shared__ int64_t win[kExpandNT];
+    __shared__ int64_t ecur_sh;
+    const int64_t g0 = (int64_t)blockIdx.x * kExpandEPB;
+    const int64_t g1 = min(total, g0 + kExpandEPB);
+    if (threadIdx.x == 0) ecur_sh = upper_index(a.P, int64_t(0), a.ne, g0);
+    __syncthreads();
+    for (int64_t r0 = g0; r0 < g1; r0 += kExpandNT) {
+        const int64_t ec = ecur_sh;
+        {
+            int64_t e = ec + threadIdx.x;
+            win[threadIdx.x] = e <= a.ne ? a.P[e] : INT64_MAX;
+        }
+        __syncthreads();
+        const int64_t t = r0 + threadIdx.x;
+        const int64_t rend = min(g1, r0 + kExpandNT);
+        if (t < rend) {
+            int j = (int)upper_index(win, int64_t(0), int64_t(kExpandNT), t);
+            int64_t e = ec + j;
+            int64_t off = t - win[j];
+            int32_t k = a.ent_k[e];
+            int64_t dest = a.ent_dest[e] + off;
+            int64_t bi = a.Brp[k] + off;
+            a.out_col[dest] = a.Bcol[bi];
+            if constexpr (NUM) a.out_val[dest] = a.Aval[a.ent_q[e]] * a.Bval[bi];
+            if (t == rend - 1) ecur_sh = e;
+        }
+        __syncthreads();
+    }
+}
+
+void expand(const ExpandArgs& a, int64_t total, hipStream_t st) {
+    if (total <= 0) return;
+    int64_t blocks = ceil_div(total, kExpandEPB);
+    if (a.out_val)
+        hipLaunchKernelGGL(k_expand<true>, dim3(grid_1d(blocks)), dim3(kExpandNT), 0, st, a, total);
+    else
+        hipLaunchKernelGGL(k_expand<false>, dim3(grid_1d(blocks)), dim3(kExpandNT), 0, st, a,
+                           total);
+    SG_LAUNCH_CHECK();
+}
+
+// ---------------------------------------------------------------- level geometry
+// Rows of a level's input all hold more than tau elements, so a range of E
+// consecutive elements touches at most this many rows (the ngroupRows of
+// Section III-C).
+inline int rows_per_range(int64_t E, int64_t tau) {
+    return (int)((E + tau) / (tau + 1)) + 1;
+}
+
+// ---------------------------------------------------------------- histogram
+constexpr int kHistNT = 256;
+
+__global__ __launch_bounds__(kHistNT) void k_histogram(LevelGeom g, const int32_t* in_col,
+                                                       int64_t* counts, int64_t epb, int nr_max) {
+    extern __shared__ int64_t lds_h[];
+    int64_t* rb = lds_h;                          // nr_max + 1 row bounds
+    int* hist = (int*)(lds_h + nr_max + 1);       // nr_max * nch counters
+    __shared__ int64_t r0_sh;
+    const int64_t g0 = (int64_t)blockIdx.x * epb;
+    const int64_t g1 = min(g.total, g0 + epb);
+    const int nkeys = nr_max * g.nch;
+    if (threadIdx.x == 0) r0_sh = upper_index(g.rp, int64_t(0), g.nrows, g0);
+    for (int x = threadIdx.x; x < nkeys; x += kHistNT) hist[x] = 0;
+    __syncthreads();
+    const int64_t r0 = r0_sh;
+    for (int j = threadIdx.x; j <= nr_max; j += kHistNT)
+        rb[j] = (r0 + j <= g.nrows) ? g.rp[r0 + j] : INT64_MAX;
+    __syncthreads();
+    int lr = 0;
+    const int mask = g.nch - 1;
+    for (int64_t t = g0 + threadIdx.x; t < g1; t += kHistNT) {
+        while (lr + 1 < nr_max && t >= rb[lr + 1]) ++lr;
+        int c = (in_col[t] >> g.shift) & mask;
+        atomicAdd(&hist[lr * g.nch + c], 1);
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < nkeys; x += kHistNT) {
+        int v = hist[x];
+        if (v) {
+            int64_t r = r0 + x / g.nch;
+            atomicAdd((unsigned long long*)&counts[r * g.nch + (x & mask)],
+                      (unsigned long long)v);
+        }
+    }
+}
+
+static int64_t hist_epb(int64_t tau, int nch, int* nr_max) {
+    int64_t epb = 16384;
+    while (epb > 256 && (int64_t)rows_per_range(epb, tau) * nch * 4 > 32768) epb /= 2;
+    *nr_max = rows_per_range(epb, tau);
+    return epb;
+}
+
+void histogram(const LevelGeom& g, const int32_t* in_col, int64_t* counts, hipStream_t st) {
+    if (g.total <= 0) return;
+    int nr_max;
+    int64_t epb = hist_epb(g.tau, g.nch, &nr_max);
+    size_t lds = (size_t)(nr_max + 1) * 8 + (size_t)nr_max * g.nch * 4;
+    int64_t blocks = ceil_div(g.total, epb);
+    hipLaunchKernelGGL(k_histogram, dim3(grid_1d(blocks)), dim3(kHistNT), lds, st, g, in_col,
+                       counts, epb, nr_max);
+    SG_LAUNCH_CHECK();
+}
+
+// ---------------------------------------------------------------- chunk bins
+struct ChunkBinOf {
+    const int64_t* counts;
+    int64_t tau;
+    bool last;
+    __device__ int operator()(int64_t x) const {
+        int64_t c = counts[x];
+        if (c == 0) return CB_EMPTY;
+        if (c > tau) return last ? CB_DENSE : CB_NEXT;
+        if (c <= kHashMaxItems[0]) return CB_H128;
+        if (c <= kHashMaxItems[1]) return CB_H512;
+        if (c <= kHashMaxItems[2]) return CB_H2048;
+        return CB_H8192;
+    }
+};
+
+void classify_chunks(const int64_t* counts, int64_t nchunks, int64_t tau, bool last_level,
+                     int32_t* inv, int32_t* pos_of, int64_t* bin_start, Arena& ar,
+                     hipStream_t st) {
+    partition(ChunkBinOf{counts, tau, last_level}, nchunks, CB_COUNT, inv, pos_of, bin_start, ar,
+              st);
+}
+
+struct CountAt {
+    const int64_t* counts;
+    const int32_t* inv;
+    __device__ int64_t operator()(int64_t p) const { return counts[inv[p]]; }
+};
+
+void reord_rowptr(const int64_t* counts, const int32_t* inv, int64_t npos, int64_t* rp_out,
+                  Arena& ar, hipStream_t st) {
+    scan_exclusive(CountAt{counts, inv}, npos, rp_out, ar, st);
+}
+
+// ---------------------------------------------------------------- multisplit
+// One work group per E = NT*K consecutive input elements (Algorithm 5):
+//  1. local histogram of (local row, chunk) keys; the LDS atomic's return
+//     value is the element's rank inside its key;
+//  2. exclusive scan of the local histogram, and one global reservation per
+//     nonempty key on the chunk's cursor in C-hat-reord;
+//  3. permute the elements into LDS, grouped by key;
+//  4. write the LDS buffer out in order, so consecutive threads write
+//     consecutive slots of each chunk (the coalesced write of Alg. 5).
+// Elements inside a chunk end up in no particular order.
+constexpr int kMsNT = 256;
+constexpr int kMsK = 16;
+constexpr int64_t kMsEPB = kMsNT * kMsK;
+
+template <bool NUM>
+__global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t* in_col,
+                                                      const double* in_val,
+                                                      const int32_t* pos_of,
+                                                      unsigned long long* cursor,
+                                                      int32_t* out_col, double* out_val,
+                                                      int64_t epb, int nr_max) {
+    extern __shared__ int64_t lds_m[];
+    const int nkeys = nr_max * g.nch;
+    int64_t* gbase = lds_m;                          // nkeys
+    int64_t* rb = gbase + nkeys;                     // nr_max + 1
+    double* valbuf = (double*)(rb + nr_max + 1);     // epb (NUM only)
+    int* hist = (int*)(valbuf + (NUM ? epb : 0));    // nkeys
+    int* loff = hist + nkeys;                        // nkeys + 1
+    int* colbuf = loff + nkeys + 1;                  // epb
+    __shared__ int64_t r0_sh;
+    __shared__ int scan_sh[kMsNT / kWave + 1];
+
+    const int64_t g0 = (int64_t)blockIdx.x * epb;
+    const int64_t g1 = min(g.total, g0 + epb);
+    const int n_wg = (int)(g1 - g0);
+    const int mask = g.nch - 1;
+    if (threadIdx.x == 0) r0_sh = upper_index(g.rp, int64_t(0), g.nrows, g0);
+    for (int x = threadIdx.x; x < nkeys; x += kMsNT) hist[x] = 0;
+    __syncthreads();
+    const int64_t r0 = r0_sh;
+    for (int j = threadIdx.x; j <= nr_max; j += kMsNT)
+        rb[j] = (r0 + j <= g.nrows) ? g.rp[r0 + j] : INT64_MAX;
+    __syncthreads();
+
+    // 1. load and local histogram
+    int32_t col[kMsK];
+    double val[kMsK];
+    int key[kMsK];
+    int rank[kMsK];
+    int lr = 0;
+#pragma unroll
+    for (int k = 0; k < kMsK; ++k) {
+        int64_t t = g0 + (int64_t)k * kMsNT + threadIdx.x;
+        key[k] = -1;
+        if (t < g1) {
+            col[k] = in_col[t];
+            if constexpr (NUM) val[k] = in_val[t];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kMsK; ++k) {
+        int64_t t = g0 + (int64_t)k * kMsNT + threadIdx.x;
+        if (t < g1) {
+            while (lr + 1 < nr_max && t >= rb[lr + 1]) ++lr;
+            key[k] = lr * g.nch + ((col[k] >> g.shift) & mask);
+            rank[k] = atomicAdd(&hist[key[k]], 1);
+        }
+    }
+    __syncthreads();
+
+    // 2. local exclusive scan (each thread a contiguous run of keys) + reservation
+    {
+        const int per = (nkeys + kMsNT - 1) / kMsNT;
+        const int k0 = min(nkeys, (int)threadIdx.x * per);
+        const int k1 = min(nkeys, k0 + per);
+        int s = 0;
+        for (int x = k0; x < k1; ++x) s += hist[x];
+        int tot;
+        int pre = block_exclusive_scan<kMsNT>(s, scan_sh, &tot);
+        for (int x = k0; x < k1; ++x) {
+            int v = hist[x];
+            loff[x] = pre;
+            pre += v;
+            if (v) {
+                int64_t nat = (r0 + x / g.nch) * g.nch + (x & mask);
+                int p = pos_of[nat];
+                gbase[x] = (int64_t)atomicAdd(&cursor[p], (unsigned long long)v);
+            }
+        }
+        if (threadIdx.x == 0) loff[nkeys] = tot;
+    }
+    __syncthreads();
+
+    // 3. permute into LDS
+#pragma unroll
+    for (int k = 0; k < kMsK; ++k) {
+        if (key[k] >= 0) {
+            int d = loff[key[k]] + rank[k];
+            colbuf[d] = col[k];
+            if constexpr (NUM) valbuf[d] = val[k];
+        }
+    }
+    __syncthreads();
+
+    // 4. ordered write: slot d's local row is found from the row starts in loff
+    lr = 0;
+    for (int d = threadIdx.x; d < n_wg; d += kMsNT) {
+        while (lr + 1 < nr_max && d >= loff[(lr + 1) * g.nch]) ++lr;
+        int32_t c = colbuf[d];
+        int kk = lr * g.nch + ((c >> g.shift) & mask);
+        int64_t ga = gbase[kk] + (d - loff[kk]);
+        out_col[ga] = c;
+        if constexpr (NUM) out_val[ga] = valbuf[d];
+    }
+}
+
+static size_t ms_lds(int64_t epb, int nr_max, int nch, bool num) {
+    size_t nkeys = (size_t)nr_max * nch;
+    return nkeys * 8 + (size_t)(nr_max + 1) * 8 + (num ? (size_t)epb * 8 : 0) + nkeys * 4 +
+           (nkeys + 1) * 4 + (size_t)epb * 4;
+}
+
+void multisplit(const LevelGeom& g, const int32_t* in_col, const double* in_val,
+                const int32_t* pos_of, int64_t* cursor, int32_t* out_col, double* out_val,
+                hipStream_t st) {
+    if (g.total <= 0) return;
+    bool num = out_val != nullptr;
+    // Elements per work group: the full register tile unless the local
+    // histogram (rows per range x chunks) pushes LDS past 64 KiB.
+    int64_t epb = kMsEPB;
+    int nr_max = rows_per_range(epb, g.tau);
+    while (epb > 64 && ms_lds(epb, nr_max, g.nch, num) > 65536) {
+        epb /= 2;
+        nr_max = rows_per_range(epb, g.tau);
+    }
+    size_t lds = ms_lds(epb, nr_max, g.nch, num);
+    if (lds > 160 * 1024) throw OverflowError("multisplit local histogram exceeds LDS");
+    int64_t blocks = ceil_div(g.total, epb);
+    if (num) {
+        SG_HIP(hipFuncSetAttribute((const void*)k_multisplit<true>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+        hipLaunchKernelGGL(k_multisplit<true>, dim3(grid_1d(blocks)), dim3(kMsNT), lds, st, g,
+                           in_col, in_val, pos_of, (unsigned long long*)cursor, out_col, out_val,
+                           epb, nr_max);
+    } else {
+        SG_HIP(hipFuncSetAttribute((const void*)k_multisplit<false>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+        hipLaunchKernelGGL(k_multisplit<false>, dim3(grid_1d(blocks)), dim3(kMsNT), lds, st, g,
+                           in_col, in_val, pos_of, (unsigned long long*)cursor, out_col,
+                           (double*)nullptr, epb, nr_max);
+    }
+    SG_LAUNCH_CHECK();
+}
+
+// ---------------------------------------------------------------- chunk tree
+__global__ void k_reduce_children(const int64_t* nnz_child, int nch, int64_t nparents,
+                                  const int32_t* inv, int64_t* nnz_parent) {
+    int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= nparents) return;
+    int64_t s = 0;
+    for (int c = 0; c < nch; ++c) s += nnz_child[p * nch + c];
+    nnz_parent[inv ? inv[p] : p] = s;
+}
+
+void reduce_children(const int64_t* nnz_child, int nch, int64_t nparents, const int32_t* inv,
+                     int64_t* nnz_parent, hipStream_t st) {
+    if (nparents <= 0) return;
+    hipLaunchKernelGGL(k_reduce_children, dim3(grid_1d(ceil_div(nparents, 256))), dim3(256), 0,
+                       st, nnz_child, nch, nparents, inv, nnz_parent);
+    SG_LAUNCH_CHECK();
+}
+
+__global__ void k_child_offsets(const int64_t* nnz_child, int nch, int64_t nparents,
+                                const int32_t* map, const int64_t* base, int64_t* off_child) {
+    int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= nparents) return;
+    int64_t o = base[map[p]];
+    for (int c = 0; c < nch; ++c) {
+        off_child[p * nch + c] = o;
+        o += nnz_child[p * nch + c];
+    }
+}
+
+void child_offsets(const int64_t* nnz_child, int nch, int64_t nparents, const int32_t* map,
+                   const int64_t* base, int64_t* off_child, hipStream_t st) {
+    if (nparents <= 0) return;
+    hipLaunchKernelGGL(k_child_offsets, dim3(grid_1d(ceil_div(nparents, 256))), dim3(256), 0, st,
+                       nnz_child, nch, nparents, map, base, off_child);
+    SG_LAUNCH_CHECK();
+}
+
+}  // namespace sg

@@ -1,0 +1,164 @@
+// Launchers of the HIP kernels, called by the host orchestration (plan.cpp).
+// Names follow the steps of Algorithm 3 on the gMAGNUS page.
+#pragma once
+
+#include "arena.h"
+#include "common.h"
+
+namespace sg {
+
+struct DevCSR {
+    int64_t n = 0, m = 0, nnz = 0;
+    const int64_t* rp = nullptr;
+    const int32_t* col = nullptr;
+    const double* val = nullptr;
+};
+
+// Row bins: the light/heavy split of Algorithm 3 (ThreshPartition at tau)
+// and the work-group-size binning of Section III-E. Partition order is
+// bin order, so heavy rows come first.
+enum RowBin : int {
+    RB_HEAVY = 0,  // u > tau: outer product + multisplit path
+    RB_WIN64,      // light, output span <= 64: wave-per-row dense window
+    RB_WIN1024,    // light, output span <= 1024: block dense window
+    RB_H128,       // light hash bins by u (table slots >= 2u, alpha = 2)
+    RB_H512,
+    RB_H2048,
+    RB_H8192,
+    RB_EMPTY,      // u = 0
+    RB_COUNT
+};
+
+// Chunk bins of one multisplit level. Heavy chunks (> tau) of a non-final
+// level go first: they are the next level's input (Section III-A).
+enum ChunkBin : int {
+    CB_NEXT = 0,  // > tau, not the last level: split again
+    CB_DENSE,     // > tau at the last level: dense LDS accumulation
+    CB_H128,      // light chunks: LDS hash accumulation
+    CB_H512,
+    CB_H2048,
+    CB_H8192,
+    CB_EMPTY,
+    CB_COUNT
+};
+
+// Hash-table slots per light bin and the largest item each bin takes.
+constexpr int kHashSlots[4] = {128, 512, 2048, 8192};
+constexpr int64_t kHashMaxItems[4] = {64, 256, 1024, 8191};
+constexpr int kWinSmall = 64;
+constexpr int kWinLarge = 1024;
+
+// ---------------------------------------------------------------- setup
+// Validation: rowptr monotone with rowptr[0] = 0 and rowptr[n] = nnz, and
+// every column in [0, ncols). Sets bit 1 (rowptr) or 2 (column) in *flag.
+void launch_validate(const DevCSR& M, int* flag, hipStream_t st);
+
+// S[q] = sum_{q' < q} nnz(B[A.col[q'],:]) for q in [0, A.nnz] (InterOffsets,
+// Algorithm 3 line 3, at entry granularity: u(i) = S[rp[i+1]] - S[rp[i]]).
+void entry_prefix(const DevCSR& A, const DevCSR& B, int64_t* S, Arena& ar, hipStream_t st);
+
+// Per B row: smallest and largest column (INT32_MAX / -1 for empty rows).
+void brow_minmax(const DevCSR& B, int32_t* bmin, int32_t* bmax, hipStream_t st);
+
+// Row classification and stable partition into RowBins.
+// stats[0]=sum u, [1]=max u, [2]=heavy rows, [3]=heavy products.
+void classify_rows(const DevCSR& A, const int64_t* S, const int32_t* bmin, const int32_t* bmax,
+                   int64_t tau, int32_t* rowlo, int32_t* perm, int64_t* bin_start,
+                   int64_t* stats, Arena& ar, hipStream_t st);
+
+// ---------------------------------------------------------------- heavy path
+// C-hat row pointers: exclusive scan of u over the heavy rows perm[0..H).
+void heavy_rowptr(const DevCSR& A, const int64_t* S, const int32_t* hrows, int64_t H,
+                  int64_t* chat_rp, Arena& ar, hipStream_t st);
+
+// Masked CSR-to-CSC of A[heavy rows, :], keeping only entries whose B row
+// is nonempty. ent_k = column of A (the slice), ent_q = A entry index,
+// ent_dest = position in C-hat of the entry's first product; P = flattened
+// slice offsets (exclusive scan of nnz(B[ent_k,:])). Returns the entry count.
+int64_t masked_csr2csc(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
+                       int64_t H, const int64_t* chat_rp, int32_t** ent_k, int64_t** ent_q,
+                       int64_t** ent_dest, int64_t** P, Arena& ar, hipStream_t st);
+
+struct ExpandArgs {
+    const int32_t* ent_k;
+    const int64_t* ent_q;
+    const int64_t* ent_dest;
+    const int64_t* P;
+    int64_t ne;
+    const double* Aval;
+    const int64_t* Brp;
+    const int32_t* Bcol;
+    const double* Bval;
+    int32_t* out_col;
+    double* out_val;  // null: columns only
+};
+// OuterProduct (Algorithm 4): every (a, B-row) pair of every slice written
+// to its C-hat position. Returns the number of launches (1).
+void expand(const ExpandArgs& a, int64_t total, hipStream_t st);
+
+struct LevelGeom {
+    const int64_t* rp;  // input row pointers, nrows+1
+    int64_t nrows;
+    int64_t total;      // rp[nrows]
+    int shift;          // log2 of this level's chunk width
+    int nch;            // chunks per input row (power of two)
+    int64_t tau;        // every input row has > tau elements
+};
+
+// Histogram (Section III-C): counts[r*nch + c] += elements of row r in chunk c.
+void histogram(const LevelGeom& g, const int32_t* in_col, int64_t* counts, hipStream_t st);
+
+// Classify the level's chunks and partition them (CB_* order). inv[pos] =
+// natural chunk index, pos_of[natural] = pos. bin_start has CB_COUNT+1.
+void classify_chunks(const int64_t* counts, int64_t nchunks, int64_t tau, bool last_level,
+                     int32_t* inv, int32_t* pos_of, int64_t* bin_start, Arena& ar,
+                     hipStream_t st);
+
+// rp_out[p] = exclusive scan of counts[inv[p]] over p in [0, npos).
+void reord_rowptr(const int64_t* counts, const int32_t* inv, int64_t npos, int64_t* rp_out,
+                  Arena& ar, hipStream_t st);
+
+// Multisplit (Algorithm 5): permute the level's input into C-hat-reord.
+// cursor[pos] starts at rp_out[pos] and is advanced by reservations.
+void multisplit(const LevelGeom& g, const int32_t* in_col, const double* in_val,
+                const int32_t* pos_of, int64_t* cursor, int32_t* out_col, double* out_val,
+                hipStream_t st);
+
+// nnz_parent[inv[p]] = sum_c nnz_child[p*nch + c] for p < nparents.
+void reduce_children(const int64_t* nnz_child, int nch, int64_t nparents, const int32_t* inv,
+                     int64_t* nnz_parent, hipStream_t st);
+// off_child[p*nch + c] = base[map[p]] + sum_{c'<c} nnz_child[p*nch + c'].
+void child_offsets(const int64_t* nnz_child, int nch, int64_t nparents, const int32_t* map,
+                   const int64_t* base, int64_t* off_child, hipStream_t st);
+
+// ---------------------------------------------------------------- accumulation
+// Light rows, straight from A and B (Gustavson, Algorithm 1 per row).
+struct RowItems {
+    DevCSR A, B;
+    const int64_t* S;
+    const int32_t* perm;   // row ids in bin order
+    const int32_t* rowlo;  // window base per row (window bins)
+    int64_t* cnt;          // symbolic: nnz per row
+    const int64_t* Crp;    // numeric: row offsets
+    int32_t* Ccol;
+    double* Cval;
+};
+void accumulate_rows(const RowItems& it, int bin, int64_t p0, int64_t n, bool numeric,
+                     hipStream_t st);
+
+// Chunks (or whole C-hat rows when no multisplit level is needed).
+struct ChunkItems {
+    const int64_t* rp;     // element range per position
+    const int32_t* map;    // output index per position
+    const int32_t* bcol;
+    const double* bval;
+    int64_t* cnt;          // symbolic: cnt[map[p]]
+    const int64_t* off;    // numeric: off[map[p]]
+    int32_t* Ccol;
+    double* Cval;
+    int64_t width;         // column width of every chunk (power of two)
+};
+void accumulate_chunks(const ChunkItems& it, int bin, int64_t p0, int64_t n, bool numeric,
+                       hipStream_t st);
+
+}  // namespace sg

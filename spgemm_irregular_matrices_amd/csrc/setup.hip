@@ -1,0 +1,182 @@
+// Setup phase of Algorithm 3 on the gMAGNUS page: input validation,
+// InterOffsets (per-row intermediate-product counts and their prefix sum)
+// and ThreshPartition of the rows into heavy rows and light-row bins.
+#include "kernels.h"
+#include "primitives.h"
+
+namespace sg {
+
+__global__ void k_part_bin_starts(const int64_t* offs, int nb, int64_t nblocks, int64_t n,
+                                  int64_t* bin_start) {
+    int b = threadIdx.x;
+    if (b < nb) bin_start[b] = offs[(int64_t)b * nblocks];
+    if (b == nb) bin_start[nb] = n;
+}
+
+// ---------------------------------------------------------------- validation
+__global__ void k_validate_rowptr(const int64_t* rp, int64_t n, int64_t nnz, int* flag) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (; i <= n; i += stride) {
+        int64_t v = rp[i];
+        bool bad = (i == 0 && v != 0) || (i == n && v != nnz) || (i < n && rp[i + 1] < v) ||
+                   v < 0 || v > nnz;
+        if (bad) atomicOr(flag, 1);
+    }
+}
+
+__global__ void k_validate_cols(const int32_t* col, int64_t nnz, int64_t ncols, int* flag) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    bool bad = false;
+    for (; i < nnz; i += stride) {
+        int32_t c = col[i];
+        bad |= (c < 0) || ((int64_t)c >= ncols);
+    }
+    if (__ballot(bad) != 0 && lane_id() == 0) atomicOr(flag, 2);
+}
+
+void launch_validate(const DevCSR& M, int* flag, hipStream_t st) {
+    int64_t blocks = std::min<int64_t>(ceil_div(M.n + 1, 256), 4096);
+    hipLaunchKernelGGL(k_validate_rowptr, dim3(grid_1d(blocks)), dim3(256), 0, st, M.rp, M.n,
+                       M.nnz, flag);
+    SG_LAUNCH_CHECK();
+    if (M.nnz > 0) {
+        blocks = std::min<int64_t>(ceil_div(M.nnz, 256), 8192);
+        hipLaunchKernelGGL(k_validate_cols, dim3(grid_1d(blocks)), dim3(256), 0, st, M.col, M.nnz,
+                           M.m, flag);
+        SG_LAUNCH_CHECK();
+    }
+}
+
+// ---------------------------------------------------------------- InterOffsets
+struct EntryProducts {
+    const int32_t* acol;
+    const int64_t* brp;
+    __device__ int64_t operator()(int64_t q) const {
+        int32_t k = acol[q];
+        return brp[k + 1] - brp[k];
+    }
+};
+
+void entry_prefix(const DevCSR& A, const DevCSR& B, int64_t* S, Arena& ar, hipStream_t st) {
+    scan_exclusive(EntryProducts{A.col, B.rp}, A.nnz, S, ar, st);
+}
+
+// ---------------------------------------------------------------- B row spans
+// One wavefront per B row: smallest and largest column of the row.
+__global__ __launch_bounds__(256) void k_brow_minmax(const int64_t* rp, const int32_t* col,
+                                                     int64_t n, int32_t* bmin, int32_t* bmax) {
+    int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    if (row >= n) return;
+    int64_t s = rp[row], e = rp[row + 1];
+    int32_t lo = 0x7fffffff, hi = -1;
+    for (int64_t q = s + lane_id(); q < e; q += kWave) {
+        int32_t c = col[q];
+        lo = min(lo, c);
+        hi = max(hi, c);
+    }
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) {
+        lo = min(lo, __shfl_xor(lo, d, kWave));
+        hi = max(hi, __shfl_xor(hi, d, kWave));
+    }
+    if (lane_id() == 0) {
+        bmin[row] = lo;
+        bmax[row] = hi;
+    }
+}
+
+void brow_minmax(const DevCSR& B, int32_t* bmin, int32_t* bmax, hipStream_t st) {
+    if (B.n <= 0) return;
+    int64_t blocks = ceil_div(B.n * kWave, 256);
+    hipLaunchKernelGGL(k_brow_minmax, dim3(grid_1d(blocks)), dim3(256), 0, st, B.rp, B.col, B.n,
+                       bmin, bmax);
+    SG_LAUNCH_CHECK();
+}
+
+// ---------------------------------------------------------------- classification
+// Per row: u(i), the row's output column span (from the B rows' spans), and
+// its bin. Heavy rows (u > tau) are the rows whose intermediate products
+// would overflow a local-memory accumulator (Section II-B, Eq. 4).
+__global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const int32_t* acol,
+                                                       int64_t n, const int64_t* S,
+                                                       const int32_t* bmin, const int32_t* bmax,
+                                                       int64_t tau, uint8_t* bin, int32_t* rowlo,
+                                                       int64_t* stats) {
+    __shared__ int64_t sh[8];
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t u = 0, heavy = 0, hprod = 0;
+    if (i < n) {
+        int64_t a0 = arp[i], a1 = arp[i + 1];
+        u = S[a1] - S[a0];
+        int b;
+        if (u == 0) {
+            b = RB_EMPTY;
+        } else if (u > tau) {
+            b = RB_HEAVY;
+            heavy = 1;
+            hprod = u;
+        } else {
+            int32_t lo = 0x7fffffff, hi = -1;
+            for (int64_t q = a0; q < a1; ++q) {
+                int32_t k = acol[q];
+                lo = min(lo, bmin[k]);
+                hi = max(hi, bmax[k]);
+            }
+            int64_t span = (int64_t)hi - lo + 1;
+            rowlo[i] = lo;
+            if (span <= kWinSmall) {
+                b = RB_WIN64;
+            } else if (span <= kWinLarge) {
+                b = RB_WIN1024;
+            } else if (u <= kHashMaxItems[0]) {
+                b = RB_H128;
+            } else if (u <= kHashMaxItems[1]) {
+                b = RB_H512;
+            } else if (u <= kHashMaxItems[2]) {
+                b = RB_H2048;
+            } else {
+                b = RB_H8192;
+            }
+        }
+        bin[i] = (uint8_t)b;
+    }
+    int64_t su = block_reduce_sum<256>(u, sh);
+    int64_t sh_heavy = block_reduce_sum<256>(heavy, sh);
+    int64_t sh_hprod = block_reduce_sum<256>(hprod, sh);
+    // max via wave shuffles, then one atomic per wave
+    int64_t mu = u;
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) {
+        int64_t o = __shfl_xor(mu, d, kWave);
+        mu = mu > o ? mu : o;
+    }
+    if (lane_id() == 0 && mu > 0)
+        atomicMax((unsigned long long*)&stats[1], (unsigned long long)mu);
+    if (threadIdx.x == 0) {
+        atomicAdd((unsigned long long*)&stats[0], (unsigned long long)su);
+        atomicAdd((unsigned long long*)&stats[2], (unsigned long long)sh_heavy);
+        atomicAdd((unsigned long long*)&stats[3], (unsigned long long)sh_hprod);
+    }
+}
+
+struct RowBinOf {
+    const uint8_t* bin;
+    __device__ int operator()(int64_t i) const { return bin[i]; }
+};
+
+void classify_rows(const DevCSR& A, const int64_t* S, const int32_t* bmin, const int32_t* bmax,
+                   int64_t tau, int32_t* rowlo, int32_t* perm, int64_t* bin_start,
+                   int64_t* stats, Arena& ar, hipStream_t st) {
+    uint8_t* bin = ar.get<uint8_t>("row_bin", (size_t)A.n + 1);
+    fill<int64_t>(stats, 4, 0, st);
+    if (A.n > 0) {
+        hipLaunchKernelGGL(k_classify_rows, dim3(grid_1d(ceil_div(A.n, 256))), dim3(256), 0, st,
+                           A.rp, A.col, A.n, S, bmin, bmax, tau, bin, rowlo, stats);
+        SG_LAUNCH_CHECK();
+    }
+    partition(RowBinOf{bin}, A.n, RB_COUNT, perm, (int32_t*)nullptr, bin_start, ar, st);
+}
+
+}  // namespace sg

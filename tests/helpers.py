@@ -1,0 +1,88 @@
+"""Shared helpers for the GPU parity tests: run the HIP path, compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from spgemm_irregular_matrices_amd import synth
+
+BOUND = 1e-12  # |c_gpu - c_ref| <= BOUND * sum|a_ik * b_kj| for every entry
+
+
+def gather_ranges(starts: np.ndarray, lens: np.ndarray) -> np.ndarray:
+    """Concatenation of arange(starts[i], starts[i]+lens[i]) over i (vectorised)."""
+    starts = np.asarray(starts, dtype=np.int64)
+    lens = np.asarray(lens, dtype=np.int64)
+    total = int(lens.sum())
+    if total == 0:
+        return np.zeros(0, dtype=np.int64)
+    excl = np.cumsum(lens) - lens
+    return np.repeat(starts - excl, lens) + np.arange(total, dtype=np.int64)
+
+
+def run_gpu(A, B, **plan_kwargs):
+    """C = A*B on the GPU through the C ABI; returns host arrays and the plan's stats."""
+    import torch
+    from spgemm_irregular_matrices_amd import binding
+
+    dA = binding.DeviceCSR.from_host(A)
+    dB = dA if B is A else binding.DeviceCSR.from_host(B)
+    with binding.Plan(**plan_kwargs) as p:
+        C = p.multiply(dA, dB)
+        torch.cuda.synchronize()
+        stats = p.stats()
+    return (C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy(), stats)
+
+
+def compare(A, B, rp, col, val, rows=None, nthreads=None, check_all_rowptr=True,
+            exact_values=False):
+    """Check GPU output rows against the oracle; returns the worst error ratio.
+
+    Structure must match bit for bit; each value must sit within
+    BOUND * abssum of the oracle's (or equal it when ``exact_values``).
+    """
+    n = A.nrows
+    assert rp.shape == (n + 1,) and rp[0] == 0
+    assert np.all(np.diff(rp) >= 0)
+    assert col.shape == val.shape == (int(rp[-1]),)
+    assert not np.any(np.isnan(val)) and not np.any(np.isinf(val))
+    if rows is None:
+        rows = np.arange(n, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    ref = oracle.spgemm_rows(A, B, rows, nthreads=nthreads)
+    glen = rp[rows + 1] - rp[rows]
+    rlen = np.diff(ref.rowptr)
+    bad = np.nonzero(glen != rlen)[0]
+    assert bad.size == 0, f"row lengths differ at rows {rows[bad[:10]]}: gpu {glen[bad[:10]]} ref {rlen[bad[:10]]}"
+    gi = gather_ranges(rp[rows], glen)
+    gcol = col[gi]
+    gval = val[gi]
+    badc = np.nonzero(gcol != ref.col)[0]
+    assert badc.size == 0, f"{badc.size} column mismatches, first at entry {badc[0]}"
+    err = np.abs(gval - ref.val)
+    if exact_values:
+        badv = np.nonzero(err != 0)[0]
+        assert badv.size == 0, f"{badv.size} inexact values (first err {err[badv[0]]})"
+        worst = 0.0
+    else:
+        lim = BOUND * ref.abssum
+        badv = np.nonzero(err > lim)[0]
+        assert badv.size == 0, (f"{badv.size} values outside the bound, first: gpu {gval[badv[0]]} "
+                                f"ref {ref.val[badv[0]]} abssum {ref.abssum[badv[0]]}")
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ratio = np.where(lim > 0, err / np.where(lim > 0, lim, 1), 0.0)
+        worst = float(ratio.max()) if ratio.size else 0.0
+    if check_all_rowptr and rows.size == n:
+        assert np.array_equal(rp[1:], np.cumsum(rlen))
+    return worst
+
+
+def sample_rows(A, B, n_heavy=8, n_random=200, seed=0, tau=6826):
+    """Row sample for full-size checks: the heaviest rows, rows near tau and random rows."""
+    u = oracle.row_products(A, B)
+    order = np.argsort(-u, kind="stable")
+    heavy = order[:n_heavy]
+    near = np.nonzero((u > tau * 0.8) & (u < tau * 1.5))[0][:n_heavy]
+    rnd = (synth.splitmix64(seed, np.arange(n_random, dtype=np.uint64)) % np.uint64(A.nrows)).astype(np.int64)
+    rows = np.unique(np.concatenate([heavy, near, rnd, [0, A.nrows - 1]]))
+    return rows.astype(np.int64), u

@@ -1,0 +1,329 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Structure (row pointers and columns) must match bit for bit; every value
+must be within 1e-12 * sum|a*b| of the oracle's long-double sum, or equal
+to it for small-integer inputs where every partial sum is exact. Forced
+parameters (tau, final chunk width, chunks per level) push small inputs
+through the heavy path with one to five multisplit levels, so every kernel
+runs at sizes the oracle checks in seconds.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import stages
+from spgemm_irregular_matrices_amd import synth
+from tests.helpers import compare, run_gpu
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.build(force=False)
+    from spgemm_irregular_matrices_amd import binding
+    binding.load()
+
+
+def _rmat10():
+    return synth.workload("rmat10_ef8")[0]
+
+
+def test_rmat10_default_light_path():
+    A = _rmat10()
+    rp, col, val, st = run_gpu(A, A)
+    assert st["heavy_rows"] == 0  # max u of this matrix is below tau
+    compare(A, A, rp, col, val)
+
+
+@pytest.mark.parametrize("tau,width,cap,levels", [
+    (64, 0, 0, 0),        # heavy rows accumulate densely without any multisplit
+    (64, 256, 32, 1),     # one level of 4 chunks
+    (64, 64, 4, 2),       # 16 chunks over two levels
+    (16, 32, 2, 5),       # 32 chunks over five levels of 2
+    (200, 128, 8, 1),
+])
+def test_rmat10_forced_heavy(tau, width, cap, levels):
+    A = _rmat10()
+    rp, col, val, st = run_gpu(A, A, tau_override=tau, chunk_width_override=width,
+                               nchunks_cap=cap)
+    assert st["heavy_rows"] > 0
+    assert st["nlevels"] == levels, st
+    compare(A, A, rp, col, val)
+
+
+def test_fig1_stages_and_product():
+    with open(os.path.join(GOLDEN, "fig1_heavy_rows.json")) as f:
+        g = json.load(f)
+    na, ma = g["shape_A"]
+    nb, mb = g["shape_B"]
+    A0 = synth.from_rows(na, ma, [g["A_rows"].get(str(i), []) for i in range(na)])
+    B0 = synth.from_rows(nb, mb, [g["B_rows"].get(str(i), []) for i in range(nb)])
+    A = synth.CSR(na, ma, A0.rowptr, A0.col, synth.uniform_values(31, A0.nnz))
+    B = synth.CSR(nb, mb, B0.rowptr, B0.col, synth.uniform_values(32, B0.nnz))
+    import torch
+    from spgemm_irregular_matrices_amd import binding
+    dA, dB = binding.DeviceCSR.from_host(A), binding.DeviceCSR.from_host(B)
+    # tau=2: rows 1 (7 products) and 2 (3 products) are heavy; width 4 over C.m=8
+    # gives the figure's two chunks in one level (the window floor is 32, so
+    # the chunk width is forced through the column range: see below)
+    with binding.Plan(tau_override=2, chunk_width_override=32, debug_dump=True) as p:
+        C = p.multiply(dA, dB)
+        torch.cuda.synchronize()
+        chat = p.debug(-1)
+        st = p.stats()
+    assert st["heavy_rows"] == 2
+    # C-hat in the figure's order (Gustavson order inside each heavy row)
+    assert chat["rowptr"].tolist() == g["C_hat"]["rowptr"]
+    assert chat["col"].tolist() == g["C_hat"]["col"]
+    assert chat["row_key"].tolist() == g["heavy_rows"]
+    Ad, Bd = A.to_dense(), B.to_dense()
+    exp_vals = [Ad[int(t[1]), int(t[2])] * Bd[int(t[4]), int(t[5])] for t in g["C_hat"]["val"]]
+    assert chat["val"].tolist() == exp_vals  # one IEEE multiply each: bit-exact
+    compare(A, B, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy())
+
+
+def test_fig1_chunks_on_wider_columns():
+    """The figure's chunking (two chunks per heavy row) on a column range of 64.
+
+    Columns are scaled by 8 so that the figure's width-4 chunks become the
+    width-32 chunks of the smallest dense window; the multisets of each
+    (row, chunk) must be the figure's.
+    """
+    with open(os.path.join(GOLDEN, "fig1_heavy_rows.json")) as f:
+        g = json.load(f)
+    na, ma = g["shape_A"]
+    nb, _ = g["shape_B"]
+    scale = 8
+    brows = [[c * scale for c in g["B_rows"].get(str(i), [])] for i in range(nb)]
+    A0 = synth.from_rows(na, ma, [g["A_rows"].get(str(i), []) for i in range(na)])
+    B0 = synth.from_rows(nb, 8 * scale, brows)
+    A = synth.CSR(na, ma, A0.rowptr, A0.col, synth.uniform_values(33, A0.nnz))
+    B = synth.CSR(nb, 8 * scale, B0.rowptr, B0.col, synth.uniform_values(34, B0.nnz))
+    import torch
+    from spgemm_irregular_matrices_amd import binding
+    dA, dB = binding.DeviceCSR.from_host(A), binding.DeviceCSR.from_host(B)
+    with binding.Plan(tau_override=2, chunk_width_override=32, nchunks_cap=2,
+                      debug_dump=True) as p:
+        C = p.multiply(dA, dB)
+        torch.cuda.synchronize()
+        lvl = p.debug(0)
+        st = p.stats()
+    assert st["nlevels"] == 1 and st["vchunks"] == [2]
+    Ad, Bd = A.to_dense(), B.to_dense()
+    got = {}
+    for r in range(lvl["rowptr"].size - 1):
+        key = int(lvl["row_key"][r])            # natural index: heavy row * 2 + chunk
+        s, e = lvl["rowptr"][r], lvl["rowptr"][r + 1]
+        got[key] = sorted(zip(((lvl["col"][s:e] % (4 * scale)) // scale).tolist(),
+                              lvl["val"][s:e].tolist()))
+    for k, (row, chunk) in enumerate(g["C_hat_reord"]["rows"]):
+        h = g["heavy_rows"].index(row)
+        vals = [Ad[int(t[1]), int(t[2])] * Bd[int(t[4]), int(t[5]) * scale]
+                for t in g["C_hat_reord"]["val"][k]]
+        assert got[h * 2 + chunk] == sorted(zip(g["C_hat_reord"]["local_col"][k], vals))
+    compare(A, B, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy())
+
+
+def test_chat_stage_matches_oracle():
+    """C-hat rows are bit-exact against the oracle's expansion, in Gustavson order."""
+    A = synth.random_csr(400, 300, seed=41, value_seed=42, mean_len=10, skew=1.2)
+    B = synth.random_csr(300, 500, seed=43, value_seed=44, mean_len=8, skew=1.2)
+    import torch
+    from spgemm_irregular_matrices_amd import binding
+    dA, dB = binding.DeviceCSR.from_host(A), binding.DeviceCSR.from_host(B)
+    with binding.Plan(tau_override=40, chunk_width_override=64, nchunks_cap=2,
+                      debug_dump=True) as p:
+        C = p.multiply(dA, dB)
+        torch.cuda.synchronize()
+        chat = p.debug(-1)
+        levels = [p.debug(l) for l in range(p.stats()["nlevels"])]
+    rows = chat["row_key"]
+    rp, col, val = stages.expand(A, B, rows)
+    assert np.array_equal(chat["rowptr"], rp)
+    assert np.array_equal(chat["col"], col)
+    assert np.array_equal(chat["val"], val)
+    # level 0: each chunk is its parent row's entries in that column range
+    l0 = levels[0]
+    W = l0["chunk_width"]
+    nch = 512 // W  # B.ncols=500 rounds up to 512
+    for r in range(l0["rowptr"].size - 1):
+        key = int(l0["row_key"][r])
+        h, c = divmod(key, nch)
+        s, e = rp[h], rp[h + 1]
+        m = (col[s:e] >= c * W) & (col[s:e] < (c + 1) * W)
+        exp = sorted(zip(col[s:e][m].tolist(), val[s:e][m].tolist()))
+        a, b = l0["rowptr"][r], l0["rowptr"][r + 1]
+        assert sorted(zip(l0["col"][a:b].tolist(), l0["val"][a:b].tolist())) == exp
+    compare(A, B, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy())
+
+
+@pytest.mark.parametrize("tau", [6826, 1, 20, 300])
+@pytest.mark.parametrize("seed", [1, 2])
+def test_random_skewed_paths(tau, seed):
+    A = synth.random_csr(600, 500, seed=seed, value_seed=seed + 10, mean_len=12, skew=1.1,
+                         empty_frac=0.05)
+    B = synth.random_csr(500, 700, seed=seed + 20, value_seed=seed + 30, mean_len=9, skew=1.1,
+                         empty_frac=0.05)
+    rp, col, val, st = run_gpu(A, B, tau_override=tau, chunk_width_override=32, nchunks_cap=4)
+    compare(A, B, rp, col, val)
+
+
+def test_small_integer_values_exact():
+    A = synth.rmat(11, 8, seed=61, value_seed=62, values="int")
+    rp, col, val, st = run_gpu(A, A, tau_override=100, chunk_width_override=64, nchunks_cap=4)
+    assert st["heavy_rows"] > 0 and st["nlevels"] >= 2
+    compare(A, A, rp, col, val, exact_values=True)
+    rp, col, val, st = run_gpu(A, A)
+    compare(A, A, rp, col, val, exact_values=True)
+
+
+def test_banded_window_path():
+    A = synth.banded(20000, 8, value_seed=71)
+    rp, col, val, st = run_gpu(A, A)
+    assert st["heavy_rows"] == 0
+    assert rp[-1] == 33 * 20000 - 272
+    compare(A, A, rp, col, val)
+    Aw = synth.banded(3000, 200, value_seed=72)   # spans of 801 columns: the larger window
+    rp, col, val, st = run_gpu(Aw, Aw, tau_override=8191)
+    compare(Aw, Aw, rp, col, val)
+
+
+def test_banded_forced_heavy():
+    A = synth.banded(4096, 8, value_seed=73)
+    rp, col, val, st = run_gpu(A, A, tau_override=100, chunk_width_override=32, nchunks_cap=8)
+    assert st["heavy_rows"] > 0
+    compare(A, A, rp, col, val)
+
+
+def test_edge_cases():
+    from spgemm_irregular_matrices_amd import binding
+    # no rows
+    E = synth.CSR(0, 5, np.zeros(1, np.int64), np.zeros(0, np.int32), np.zeros(0))
+    B = synth.random_csr(5, 7, seed=81, value_seed=82, mean_len=2)
+    rp, col, val, _ = run_gpu(E, B)
+    assert rp.tolist() == [0] and col.size == 0
+    # inner dimension zero
+    A0 = synth.CSR(4, 0, np.zeros(5, np.int64), np.zeros(0, np.int32), np.zeros(0))
+    B0 = synth.CSR(0, 6, np.zeros(1, np.int64), np.zeros(0, np.int32), np.zeros(0))
+    rp, col, val, _ = run_gpu(A0, B0)
+    assert rp.tolist() == [0] * 5
+    # 1x1
+    one = synth.CSR(1, 1, np.array([0, 1], np.int64), np.array([0], np.int32), np.array([-3.0]))
+    rp, col, val, _ = run_gpu(one, one)
+    assert col.tolist() == [0] and val.tolist() == [9.0]
+    # rank one, forced heavy
+    x = synth.random_csr(50, 1, seed=83, value_seed=84, mean_len=1)
+    y = synth.random_csr(1, 3000, seed=85, value_seed=86, mean_len=1500)
+    for kw in ({}, {"tau_override": 10, "chunk_width_override": 64, "nchunks_cap": 4}):
+        rp, col, val, _ = run_gpu(x, y, **kw)
+        compare(x, y, rp, col, val)
+    # empty rows everywhere
+    A = synth.random_csr(300, 200, seed=87, value_seed=88, mean_len=6, empty_frac=0.6)
+    Bm = synth.random_csr(200, 260, seed=89, value_seed=90, mean_len=6, empty_frac=0.6)
+    for kw in ({}, {"tau_override": 3, "chunk_width_override": 32, "nchunks_cap": 2}):
+        rp, col, val, _ = run_gpu(A, Bm, **kw)
+        compare(A, Bm, rp, col, val)
+    # cancellation zeros stay in the structure
+    Ac = synth.from_rows(1, 2, [[0, 1]], [[1.0, 1.0]])
+    Bc = synth.from_rows(2, 3, [[0, 2], [0]], [[2.5, 1.0], [-2.5]])
+    rp, col, val, _ = run_gpu(Ac, Bc)
+    assert rp.tolist() == [0, 2] and col.tolist() == [0, 2] and val.tolist() == [0.0, 1.0]
+
+
+def test_rectangular_and_unsorted_input_columns():
+    A = synth.random_csr(700, 90, seed=91, value_seed=92, mean_len=20, skew=1.3)
+    B = synth.random_csr(90, 3000, seed=93, value_seed=94, mean_len=60, skew=1.3)
+    # shuffle columns inside every row of A and B: the product must not care
+    for M, sd in ((A, 95), (B, 96)):
+        keys = synth.splitmix64(sd, np.arange(M.nnz, dtype=np.uint64))
+        rows = np.repeat(np.arange(M.nrows), np.diff(M.rowptr))
+        order = np.lexsort((keys, rows))
+        M.col = M.col[order].copy()
+        M.val = M.val[order].copy()
+    for kw in ({}, {"tau_override": 200, "chunk_width_override": 128, "nchunks_cap": 4}):
+        rp, col, val, _ = run_gpu(A, B, **kw)
+        compare(A, B, rp, col, val)
+
+
+def test_numeric_rerun_with_new_values_and_determinism():
+    import torch
+    from spgemm_irregular_matrices_amd import binding
+    A = synth.rmat(11, 8, seed=101, value_seed=102)
+    A2 = synth.CSR(A.nrows, A.ncols, A.rowptr, A.col, synth.uniform_values(103, A.nnz))
+    dA = binding.DeviceCSR.from_host(A)
+    dA2 = binding.DeviceCSR.from_host(A2)
+    with binding.Plan(tau_override=80, chunk_width_override=64, nchunks_cap=4) as p:
+        rp, nnz = p.symbolic(dA, dA)
+        col = torch.empty(nnz, dtype=torch.int32, device="cuda")
+        val = torch.empty(nnz, dtype=torch.float64, device="cuda")
+        p.numeric(dA, dA, rp, col, val)
+        torch.cuda.synchronize()
+        compare(A, A, rp.cpu().numpy(), col.cpu().numpy(), val.cpu().numpy())
+        p.numeric(dA2, dA2, rp, col, val)   # same structure, new values
+        torch.cuda.synchronize()
+        compare(A2, A2, rp.cpu().numpy(), col.cpu().numpy(), val.cpu().numpy())
+        first = (rp.cpu().numpy().copy(), col.cpu().numpy().copy())
+        for _ in range(5):
+            rp2, nnz2 = p.symbolic(dA, dA)
+            p.numeric(dA, dA, rp2, col, val)
+            torch.cuda.synchronize()
+            assert nnz2 == nnz
+            assert np.array_equal(rp2.cpu().numpy(), first[0])
+            assert np.array_equal(col.cpu().numpy(), first[1])
+
+
+def test_error_paths():
+    import torch
+    from spgemm_irregular_matrices_amd import binding
+    A = synth.random_csr(50, 40, seed=111, value_seed=112, mean_len=4)
+    B = synth.random_csr(30, 60, seed=113, value_seed=114, mean_len=4)
+    dA, dB = binding.DeviceCSR.from_host(A), binding.DeviceCSR.from_host(B)
+    with binding.Plan() as p:
+        with pytest.raises(binding.SpgemmError) as e:
+            p.symbolic(dA, dB)
+        assert e.value.code == -2
+        rp = torch.zeros(51, dtype=torch.int64, device="cuda")
+        with pytest.raises(binding.SpgemmError) as e:
+            p.numeric(dA, dA, rp, None, None)
+        assert e.value.code in (-8, -6)
+    # out-of-range column is caught by validation before any kernel uses it
+    Bb = synth.random_csr(40, 60, seed=115, value_seed=116, mean_len=4)
+    bad = Bb.col.copy()
+    bad[3] = 60
+    dBb = binding.DeviceCSR(Bb.nrows, Bb.ncols, torch.from_numpy(Bb.rowptr).cuda(),
+                            torch.from_numpy(bad).cuda(), torch.from_numpy(Bb.val).cuda())
+    with binding.Plan() as p:
+        with pytest.raises(binding.SpgemmError) as e:
+            p.symbolic(dA, dBb)
+        assert e.value.code == -3
+    # a broken row pointer is caught too
+    badrp = Bb.rowptr.copy()
+    badrp[5] = badrp[6] + 1
+    dBr = binding.DeviceCSR(Bb.nrows, Bb.ncols, torch.from_numpy(badrp).cuda(),
+                            torch.from_numpy(Bb.col).cuda(), torch.from_numpy(Bb.val).cuda())
+    with binding.Plan() as p:
+        with pytest.raises(binding.SpgemmError) as e:
+            p.symbolic(dA, dBr)
+        assert e.value.code == -3
+        # the plan stays usable after an error
+        dBg = binding.DeviceCSR.from_host(Bb)
+        C = p.multiply(dA, dBg)
+        torch.cuda.synchronize()
+        compare(A, Bb, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy())
+        # numeric with other shapes than symbolic
+        A51 = binding.DeviceCSR.from_host(synth.random_csr(51, 40, seed=117, value_seed=118,
+                                                           mean_len=4))
+        with pytest.raises(binding.SpgemmError) as e:
+            p.numeric(A51, dBg, C.rowptr, C.col, C.val)
+        assert e.value.code == -6
+    with pytest.raises(binding.SpgemmError) as e:
+        binding.Plan(chunk_width_override=48)
+    assert e.value.code == -1
