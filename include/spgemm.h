@@ -77,6 +77,9 @@ typedef struct {
     int32_t debug_dump;           /* 1 = keep copies of C-hat and each C-hat-reord level  */
     int32_t timing;               /* 1 = time every phase with HIP events                 */
     int64_t max_batch_products;   /* heavy products per row batch; 0 = one batch          */
+    int32_t symbolic_mode;        /* heavy-row symbolic pass: 0 = auto, 1 = fused per-row
+                                     bitmap pass, 2 = multisplit of column-only C-hat      */
+    int32_t reserved;
 } spgemm_options;
 
 /* Phases, named after the gMAGNUS page's phase breakdown (Section IV-C,

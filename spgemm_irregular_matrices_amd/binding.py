@@ -45,7 +45,8 @@ class Options(ctypes.Structure):
     _fields_ = [("lds_budget_bytes", ctypes.c_int64), ("tau_override", ctypes.c_int64),
                 ("chunk_width_override", ctypes.c_int64), ("nchunks_cap", ctypes.c_int32),
                 ("validate_inputs", ctypes.c_int32), ("debug_dump", ctypes.c_int32),
-                ("timing", ctypes.c_int32), ("max_batch_products", ctypes.c_int64)]
+                ("timing", ctypes.c_int32), ("max_batch_products", ctypes.c_int64),
+                ("symbolic_mode", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 NPH = len(PHASES)
@@ -164,7 +165,8 @@ class Plan:
     """An spgemm plan: owns device workspace and the symbolic structure."""
 
     def __init__(self, tau_override=0, chunk_width_override=0, nchunks_cap=0, lds_budget_bytes=0,
-                 validate_inputs=True, debug_dump=False, timing=False, max_batch_products=0):
+                 validate_inputs=True, debug_dump=False, timing=False, max_batch_products=0,
+                 symbolic_mode=0):
         lib = load()
         o = Options()
         lib.spgemm_options_default(ctypes.byref(o))
@@ -176,6 +178,7 @@ class Plan:
         o.debug_dump = 1 if debug_dump else 0
         o.timing = 1 if timing else 0
         o.max_batch_products = max_batch_products
+        o.symbolic_mode = symbolic_mode
         h = ctypes.c_void_p()
         _check(lib.spgemm_plan_create(ctypes.byref(h), ctypes.byref(o)), "spgemm_plan_create")
         self._h = h

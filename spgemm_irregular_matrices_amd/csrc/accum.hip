@@ -1,16 +1,20 @@
 // Local-memory accumulators (gMAGNUS page, Section III-E).
 //
-// * Hash accumulator, for light rows of C and light chunks of C-hat-reord:
-//   an LDS hash map keyed by column (multiplicative hashing, linear
-//   probing, at least two slots per item element, i.e. alpha = 2), then a
-//   bitonic sort of the table to emit the row or chunk with ascending
-//   columns.
+// * Hash accumulator, for light rows of C (and light chunks too wide for a
+//   bitmap): an LDS hash map keyed by column (multiplicative hashing,
+//   linear probing, at least two slots per item element, i.e. alpha = 2);
+//   the occupied slots are compacted and bitonic-sorted to emit the row
+//   with ascending columns.
+// * Bitmap-rank accumulator, for light chunks of C-hat-reord: after the
+//   multisplit every chunk spans a bounded column width, so a one-bit-per-
+//   column bitmap fits in LDS; a prefix sum over its word popcounts ranks
+//   the present columns, values are summed at their rank, and the chunk
+//   comes out sorted without a sort.
 // * Dense window accumulator, for heavy chunks of the last multisplit level
 //   and for light rows whose output columns fall in a short window (the
 //   "shortened dense accumulator" of banded matrices, Section II-B): an LDS
-//   array over the window plus a one-bit-per-column bitmap; a prefix sum
-//   over the bitmap's word popcounts gives each present column its rank, so
-//   the output comes out sorted without a sort.
+//   array over the window plus the bitmap; the word-popcount prefix sum
+//   over the bitmap gives each present column its output rank.
 //
 // The symbolic pass counts distinct columns per item; the numeric pass sums
 // values and writes columns and values at the item's output offset.
@@ -114,40 +118,37 @@ __device__ __forceinline__ int team_sum(int v, int* sh) {
 }
 
 // ---------------------------------------------------------------- hash
-template <int MODE, bool NUM, int TW, int NI>
-__global__ __launch_bounds__(TW* NI) void k_acc_hash(RowItems ri, ChunkItems ci, int64_t p0,
-                                                     int64_t nitems, int logS) {
-    static_assert(TW == kWave || NI == 1, "block-wide teams hold one item");
+// One item per work group of TW threads; the table has S = 2^LOGS slots.
+template <int MODE, bool NUM, int TW, int LOGS>
+__global__ __launch_bounds__(TW) void k_acc_hash(RowItems ri, ChunkItems ci, int64_t p0,
+                                                 int64_t nitems) {
+    constexpr int S = 1 << LOGS;
+    constexpr int SPT = S / TW;  // slots per thread in the compaction step
+    static_assert(SPT >= 1 && SPT * TW == S, "table must be a multiple of the team");
     extern __shared__ int64_t lds_a[];
-    const int S = 1 << logS;
-    const int team = threadIdx.x / TW;
-    const int tt = threadIdx.x % TW;
-    uint32_t* keys = (uint32_t*)lds_a + team * S;
-    double* vals = (double*)((uint32_t*)lds_a + NI * S) + team * S;
-    __shared__ int cnt_sh[NI];
+    uint32_t* keys = (uint32_t*)lds_a;
+    double* vals = (double*)(keys + S);
     __shared__ int red_sh[TW / kWave + 1];
-
-    const int64_t item = (int64_t)blockIdx.x * NI + team;
-    const bool active = item < nitems;
-    ItemHdr h;
-    if (active) h = load_item<MODE>(ri, ci, p0 + item);
+    const int tt = threadIdx.x;
+    const int64_t item = blockIdx.x;
+    if (item >= nitems) return;
+    const ItemHdr h = load_item<MODE>(ri, ci, p0 + item);
     for (int s = tt; s < S; s += TW) {
         keys[s] = 0xffffffffu;
         if constexpr (NUM) vals[s] = 0.0;
     }
-    if (tt == 0) cnt_sh[team] = 0;
     __syncthreads();
 
     int fresh = 0;
-    if (active) {
+    {
         int64_t cur = h.a0;
-        const uint32_t smask = (uint32_t)S - 1;
+        constexpr uint32_t smask = (uint32_t)S - 1;
         for (int64_t t = tt; t < h.count; t += TW) {
             int32_t c;
             double v = 0.0;
             load_elem<MODE, NUM>(ri, ci, h, t, cur, c, v);
             uint32_t key = (uint32_t)c;
-            uint32_t slot = (key * 2654435769u) >> (32 - logS);
+            uint32_t slot = (key * 2654435769u) >> (32 - LOGS);
             for (;;) {
                 uint32_t old = atomicCAS(&keys[slot], 0xffffffffu, key);
                 if (old == 0xffffffffu) {
@@ -160,23 +161,42 @@ __global__ __launch_bounds__(TW* NI) void k_acc_hash(RowItems ri, ChunkItems ci,
             if constexpr (NUM) atomicAdd(&vals[slot], v);
         }
     }
-    if constexpr (TW == kWave) {
-        fresh = wave_reduce_sum(fresh);
-        if (tt == 0) cnt_sh[team] = fresh;
-    } else {
-        fresh = block_reduce_sum<TW>(fresh, red_sh);
-        if (tt == 0) cnt_sh[team] = fresh;
-    }
-    __syncthreads();
-    const int nnz = cnt_sh[team];
+    const int nnz = team_sum<TW>(fresh, red_sh);
     if constexpr (!NUM) {
-        if (active && tt == 0) write_count<MODE>(ri, ci, h, nnz);
+        if (tt == 0) write_count<MODE>(ri, ci, h, nnz);
         return;
     } else {
-        // bitonic sort of the whole table; empty slots (0xffffffff) sort last
-        for (int k = 2; k <= S; k <<= 1) {
+        // compact the occupied slots to the front, in slot order
+        __syncthreads();
+        uint32_t kk[SPT];
+        double vv[SPT];
+        int occ = 0;
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            kk[j] = keys[tt * SPT + j];
+            vv[j] = vals[tt * SPT + j];
+            occ += kk[j] != 0xffffffffu;
+        }
+        int tot;
+        int pre = team_exclusive_scan<TW>(occ, red_sh, &tot);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            if (kk[j] != 0xffffffffu) {
+                keys[pre] = kk[j];
+                vals[pre] = vv[j];
+                ++pre;
+            }
+        }
+        int P2 = 1;
+        while (P2 < nnz) P2 <<= 1;
+        __syncthreads();
+        for (int s = nnz + tt; s < P2; s += TW) keys[s] = 0xffffffffu;
+        __syncthreads();
+        // bitonic sort of the next power of two above nnz
+        for (int k = 2; k <= P2; k <<= 1) {
             for (int j = k >> 1; j > 0; j >>= 1) {
-                for (int pi = tt; pi < (S >> 1); pi += TW) {
+                for (int pi = tt; pi < (P2 >> 1); pi += TW) {
                     int i = ((pi & ~(j - 1)) << 1) | (pi & (j - 1));
                     int ix = i | j;
                     uint32_t ka = keys[i], kb = keys[ix];
@@ -192,14 +212,103 @@ __global__ __launch_bounds__(TW* NI) void k_acc_hash(RowItems ri, ChunkItems ci,
                 __syncthreads();
             }
         }
-        if (active) {
-            int64_t off = out_offset<MODE>(ri, ci, h);
-            int32_t* oc = out_cols<MODE>(ri, ci);
-            double* ov = out_vals<MODE>(ri, ci);
-            for (int s = tt; s < nnz; s += TW) {
-                oc[off + s] = (int32_t)keys[s];
-                ov[off + s] = vals[s];
+        int64_t off = out_offset<MODE>(ri, ci, h);
+        int32_t* oc = out_cols<MODE>(ri, ci);
+        double* ov = out_vals<MODE>(ri, ci);
+        for (int s = tt; s < nnz; s += TW) {
+            oc[off + s] = (int32_t)keys[s];
+            ov[off + s] = vals[s];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- bitmap rank
+// Chunks whose column width W is small enough for a one-bit-per-column
+// bitmap in LDS. Pass 1 sets the bitmap from the chunk's columns (kept in
+// registers); a prefix sum over the word popcounts gives every present
+// column its rank, i.e. its place in the sorted output; pass 2 adds each
+// value into a compact array at that rank. Output r is written by thread
+// r mod TW after finding the r-th set bit (binary search over the word
+// prefix, then a select inside the word), so writes are coalesced and the
+// work is proportional to the chunk, not to W.
+template <bool NUM, int TW, int KPT>
+__global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int64_t nitems,
+                                                 int logW) {
+    extern __shared__ int64_t lds_r[];
+    const int W = 1 << logW;
+    const int NWD = W >> 5;
+    double* vals = (double*)lds_r;                                // TW*KPT (NUM)
+    uint32_t* bits = (uint32_t*)(vals + (NUM ? TW * KPT : 0));    // NWD
+    int* wpre = (int*)(bits + NWD);                               // NWD (NUM)
+    __shared__ int red_sh[TW / kWave + 1];
+    __shared__ int32_t lo_sh;
+    const int tt = threadIdx.x;
+    const int64_t item = blockIdx.x;
+    if (item >= nitems) return;
+    const int64_t start = ci.rp[p0 + item];
+    const int count = (int)(ci.rp[p0 + item + 1] - start);
+    const int64_t out = ci.map[p0 + item];
+    for (int w = tt; w < NWD; w += TW) bits[w] = 0u;
+    if (tt == 0) lo_sh = (int32_t)(ci.bcol[start] & ~(int32_t)(W - 1));
+    __syncthreads();
+    const int32_t lo = lo_sh;
+    uint32_t idx[KPT];
+    double v[KPT];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+        int t = tt + k * TW;
+        idx[k] = 0xffffffffu;
+        if (t < count) {
+            idx[k] = (uint32_t)(ci.bcol[start + t] - lo);
+            if constexpr (NUM) v[k] = ci.bval[start + t];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < KPT; ++k)
+        if (idx[k] < (uint32_t)W) atomicOr(&bits[idx[k] >> 5], 1u << (idx[k] & 31));
+    __syncthreads();
+    const int per = (NWD + TW - 1) / TW;
+    const int w0 = min(NWD, tt * per), w1 = min(NWD, w0 + per);
+    int pc = 0;
+    for (int w = w0; w < w1; ++w) pc += __popc(bits[w]);
+    if constexpr (!NUM) {
+        int tot = team_sum<TW>(pc, red_sh);
+        if (tt == 0) ci.cnt[out] = tot;
+    } else {
+        int tot;
+        int pre = team_exclusive_scan<TW>(pc, red_sh, &tot);
+        for (int w = w0; w < w1; ++w) {
+            wpre[w] = pre;
+            pre += __popc(bits[w]);
+        }
+        for (int r = tt; r < tot; r += TW) vals[r] = 0.0;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            if (idx[k] < (uint32_t)W) {
+                uint32_t w = idx[k] >> 5;
+                int rank = wpre[w] + __popc(bits[w] & ((1u << (idx[k] & 31)) - 1u));
+                atomicAdd(&vals[rank], v[k]);
             }
+        }
+        __syncthreads();
+        const int64_t off = ci.off[out];
+        for (int r = tt; r < tot; r += TW) {
+            int w = (int)upper_index(wpre, int64_t(0), int64_t(NWD), r);
+            int j = r - wpre[w];
+            uint32_t x = bits[w];
+            int pos = 0;
+#pragma unroll
+            for (int sh = 16; sh > 0; sh >>= 1) {
+                int c = __popc(x & ((1u << sh) - 1u));
+                if (j >= c) {
+                    j -= c;
+                    x >>= sh;
+                    pos += sh;
+                }
+            }
+            ci.Ccol[off + r] = lo + w * 32 + pos;
+            ci.Cval[off + r] = vals[r];
         }
     }
 }
@@ -284,15 +393,25 @@ __global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, ChunkItems c
 }
 
 // ---------------------------------------------------------------- launchers
-template <int MODE, bool NUM, int TW, int NI>
-static void launch_hash(const RowItems& ri, const ChunkItems& ci, int64_t p0, int64_t n, int S,
+template <int MODE, bool NUM, int TW, int LOGS>
+static void launch_hash(const RowItems& ri, const ChunkItems& ci, int64_t p0, int64_t n,
                         hipStream_t st) {
-    size_t lds = (size_t)NI * S * (4 + (NUM ? 8 : 0));
-    auto kern = k_acc_hash<MODE, NUM, TW, NI>;
+    size_t lds = (size_t)(1 << LOGS) * (4 + (NUM ? 8 : 0));
+    auto kern = k_acc_hash<MODE, NUM, TW, LOGS>;
     SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds));
-    hipLaunchKernelGGL(kern, dim3(grid_1d(ceil_div(n, NI))), dim3(TW * NI), lds, st, ri, ci, p0,
-                       n, ilog2(S));
+    hipLaunchKernelGGL(kern, dim3(grid_1d(n)), dim3(TW), lds, st, ri, ci, p0, n);
+    SG_LAUNCH_CHECK();
+}
+
+template <bool NUM, int TW, int KPT>
+static void launch_rank(const ChunkItems& ci, int64_t p0, int64_t n, hipStream_t st) {
+    const int64_t W = ci.width;
+    size_t lds = (NUM ? (size_t)TW * KPT * 8 : 0) + (size_t)(W / 32) * 4 * (NUM ? 2 : 1);
+    auto kern = k_acc_rank<NUM, TW, KPT>;
+    SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds));
+    hipLaunchKernelGGL(kern, dim3(grid_1d(n)), dim3(TW), lds, st, ci, p0, n, ilog2(W));
     SG_LAUNCH_CHECK();
 }
 
@@ -311,13 +430,26 @@ static void launch_window(const RowItems& ri, const ChunkItems& ci, int64_t p0, 
 }
 
 template <int MODE, bool NUM>
-static void launch_hash_bin(int hb, const RowItems& ri, const ChunkItems& ci, int64_t p0,
-                            int64_t n, hipStream_t st) {
+static void launch_hash_bin(int hb, int top_logS, const RowItems& ri, const ChunkItems& ci,
+                            int64_t p0, int64_t n, hipStream_t st) {
     switch (hb) {
-        case 0: launch_hash<MODE, NUM, 64, 4>(ri, ci, p0, n, kHashSlots[0], st); break;
-        case 1: launch_hash<MODE, NUM, 64, 4>(ri, ci, p0, n, kHashSlots[1], st); break;
-        case 2: launch_hash<MODE, NUM, 256, 1>(ri, ci, p0, n, kHashSlots[2], st); break;
-        default: launch_hash<MODE, NUM, 512, 1>(ri, ci, p0, n, kHashSlots[3], st); break;
+        case 0: launch_hash<MODE, NUM, 64, 7>(ri, ci, p0, n, st); break;
+        case 1: launch_hash<MODE, NUM, 64, 9>(ri, ci, p0, n, st); break;
+        case 2: launch_hash<MODE, NUM, 256, 11>(ri, ci, p0, n, st); break;
+        default:
+            if (top_logS <= 12) launch_hash<MODE, NUM, 512, 12>(ri, ci, p0, n, st);
+            else launch_hash<MODE, NUM, 512, 13>(ri, ci, p0, n, st);
+            break;
+    }
+}
+
+template <bool NUM>
+static void launch_rank_bin(int hb, const ChunkItems& ci, int64_t p0, int64_t n, hipStream_t st) {
+    switch (hb) {
+        case 0: launch_rank<NUM, 64, 1>(ci, p0, n, st); break;
+        case 1: launch_rank<NUM, 64, 4>(ci, p0, n, st); break;
+        case 2: launch_rank<NUM, 128, 8>(ci, p0, n, st); break;
+        default: launch_rank<NUM, 512, 16>(ci, p0, n, st); break;
     }
 }
 
@@ -329,10 +461,10 @@ static void rows_impl(const RowItems& it, int bin, int64_t p0, int64_t n, hipStr
         case RB_WIN1024:
             launch_window<MODE_ROW, NUM, 256, 1>(it, none, p0, n, kWinLarge, st);
             break;
-        case RB_H128: launch_hash_bin<MODE_ROW, NUM>(0, it, none, p0, n, st); break;
-        case RB_H512: launch_hash_bin<MODE_ROW, NUM>(1, it, none, p0, n, st); break;
-        case RB_H2048: launch_hash_bin<MODE_ROW, NUM>(2, it, none, p0, n, st); break;
-        case RB_H8192: launch_hash_bin<MODE_ROW, NUM>(3, it, none, p0, n, st); break;
+        case RB_H128: launch_hash_bin<MODE_ROW, NUM>(0, it.hash_top_logS, it, none, p0, n, st); break;
+        case RB_H512: launch_hash_bin<MODE_ROW, NUM>(1, it.hash_top_logS, it, none, p0, n, st); break;
+        case RB_H2048: launch_hash_bin<MODE_ROW, NUM>(2, it.hash_top_logS, it, none, p0, n, st); break;
+        case RB_H8192: launch_hash_bin<MODE_ROW, NUM>(3, it.hash_top_logS, it, none, p0, n, st); break;
         default: throw std::logic_error("not a light row bin");
     }
 }
@@ -351,10 +483,16 @@ static void chunks_impl(const ChunkItems& it, int bin, int64_t p0, int64_t n, hi
         case CB_DENSE:
             launch_window<MODE_CHUNK, NUM, 1024, 1>(none, it, p0, n, it.width, st);
             break;
-        case CB_H128: launch_hash_bin<MODE_CHUNK, NUM>(0, none, it, p0, n, st); break;
-        case CB_H512: launch_hash_bin<MODE_CHUNK, NUM>(1, none, it, p0, n, st); break;
-        case CB_H2048: launch_hash_bin<MODE_CHUNK, NUM>(2, none, it, p0, n, st); break;
-        case CB_H8192: launch_hash_bin<MODE_CHUNK, NUM>(3, none, it, p0, n, st); break;
+        case CB_H128:
+        case CB_H512:
+        case CB_H2048:
+        case CB_H8192:
+            if (it.width <= kRankMaxWidth)
+                launch_rank_bin<NUM>(bin - CB_H128, it, p0, n, st);
+            else
+                launch_hash_bin<MODE_CHUNK, NUM>(bin - CB_H128, it.hash_top_logS, none, it, p0, n,
+                                                 st);
+            break;
         default: throw std::logic_error("not an accumulated chunk bin");
     }
 }

@@ -410,6 +410,195 @@ void multisplit(const LevelGeom& g, const int32_t* in_col, const double* in_val,
     SG_LAUNCH_CHECK();
 }
 
+// ---------------------------------------------------------------- fused symbolic
+// Symbolic pass of the heavy rows without materialising C-hat-reord: the
+// structure of every level (chunk element counts for Histogram, and the
+// distinct columns per chunk that Symbolic counts on C-hat-reord) depends
+// only on which columns each heavy row produces and how often, not on the
+// order of elements inside a chunk. Counts per finest chunk slot (width
+// W_fin) are enough: a chunk of any level is a run of consecutive slots.
+//
+// Element counts: B row k contributes the same per-slot counts to every
+// row that uses it, so bslot[k][s] is counted once over B and each heavy
+// row sums the vectors of its A entries.
+__global__ void k_bslot_counts(const int64_t* brp, const int32_t* bcol, int64_t nb_rows,
+                               int logW, int req, int32_t* bslot) {
+    int64_t k = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    if (k >= nb_rows) return;
+    for (int64_t e = brp[k] + lane_id(); e < brp[k + 1]; e += kWave)
+        atomicAdd(&bslot[k * req + (bcol[e] >> logW)], 1);
+}
+
+// One work group per heavy row; thread tt owns slot tt % req and sums the
+// B-row vectors of every (TW/req)-th entry of the row.
+constexpr int kElemNT = 256;
+__global__ __launch_bounds__(kElemNT) void k_heavy_elem_counts(const int64_t* arp,
+                                                               const int32_t* acol,
+                                                               const int32_t* hrows, int req,
+                                                               const int32_t* bslot,
+                                                               int64_t* elem_fin) {
+    extern __shared__ int64_t lds_e[];
+    unsigned long long* acc = (unsigned long long*)lds_e;  // req
+    const int tt = threadIdx.x;
+    const int64_t h = blockIdx.x;
+    for (int s = tt; s < req; s += kElemNT) acc[s] = 0ull;
+    __syncthreads();
+    const int32_t r = hrows[h];
+    const int64_t a0 = arp[r], a1 = arp[r + 1];
+    if (req <= kElemNT) {
+        const int s = tt % req;
+        const int jstep = kElemNT / req;
+        int64_t sum = 0;
+        for (int64_t q = a0 + tt / req; q < a1; q += jstep) sum += bslot[(int64_t)acol[q] * req + s];
+        if (tt < jstep * req && sum) atomicAdd(&acc[s], (unsigned long long)sum);
+    } else {
+        for (int s = tt; s < req; s += kElemNT) {
+            int64_t sum = 0;
+            for (int64_t q = a0; q < a1; ++q) sum += bslot[(int64_t)acol[q] * req + s];
+            acc[s] += (unsigned long long)sum;
+        }
+    }
+    __syncthreads();
+    for (int s = tt; s < req; s += kElemNT) elem_fin[h * req + s] = (int64_t)acc[s];
+}
+
+// Distinct columns: one work group per heavy row keeps a one-bit-per-column
+// bitmap of the row's column range in LDS. The row's A entries are taken in
+// windows staged in LDS; each entry's B row is cut into pieces of 64
+// products and the waves take pieces in turn, one product per lane, so the
+// reads of B are coalesced and no product needs a search.
+constexpr int kHsymNT = 1024;
+constexpr int kHsymEW = 1024;  // entries per staged window
+
+__global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
+    const int64_t* arp, const int32_t* acol, const int64_t* brp, const int32_t* bcol,
+    const int32_t* hrows, int req, int nwords, int64_t* dist_fin) {
+    extern __shared__ int64_t lds_s[];
+    constexpr int NW = kHsymNT / kWave;
+    int64_t* bst = lds_s;                          // kHsymEW B row starts
+    int* nbv = (int*)(bst + kHsymEW);              // kHsymEW B row lengths
+    int* ppre = nbv + kHsymEW;                     // kHsymEW + 1 piece prefix
+    int* dsl = ppre + kHsymEW + 1;                 // req distinct counts
+    uint32_t* bits = (uint32_t*)(dsl + req);       // nwords
+    __shared__ int scan_sh[NW + 1];
+    const int tt = threadIdx.x;
+    const int w = tt / kWave, lane = lane_id();
+    const int64_t h = blockIdx.x;
+    for (int i = tt; i < nwords; i += kHsymNT) bits[i] = 0u;
+    for (int i = tt; i < req; i += kHsymNT) dsl[i] = 0;
+    const int32_t r = hrows[h];
+    const int64_t a0 = arp[r], a1 = arp[r + 1];
+    for (int64_t ew = a0; ew < a1; ew += kHsymEW) {
+        const int ne = (int)min((int64_t)kHsymEW, a1 - ew);
+        int pc = 0;
+        if (tt < ne) {
+            int32_t k = acol[ew + tt];
+            int64_t b0 = brp[k];
+            int nb = (int)(brp[k + 1] - b0);
+            bst[tt] = b0;
+            nbv[tt] = nb;
+            pc = (nb + kWave - 1) / kWave;
+        }
+        int tot;
+        int pre = block_exclusive_scan<kHsymNT>(pc, scan_sh, &tot);
+        if (tt < ne) ppre[tt] = pre;
+        if (tt == 0) ppre[ne] = tot;
+        __syncthreads();
+        int j = 0;
+        for (int piece = w; piece < tot; piece += NW) {
+            while (ppre[j + 1] <= piece) ++j;
+            int off = (piece - ppre[j]) * kWave + lane;
+            if (off < nbv[j]) {
+                uint32_t c = (uint32_t)bcol[bst[j] + off];
+                atomicOr(&bits[c >> 5], 1u << (c & 31));
+            }
+        }
+        __syncthreads();
+    }
+    // distinct columns per finest slot: popcounts of the slot's words
+    const int wps = nwords / req;  // words per slot (>= 1)
+    for (int i = tt; i < nwords; i += kHsymNT) {
+        int pc = __popc(bits[i]);
+        const int sl = i / wps;
+        // a wave's 64 words lie in one slot when slots hold >= 64 words
+        if (wps >= kWave) {
+            pc = wave_reduce_sum(pc);
+            if (lane == 0 && pc) atomicAdd(&dsl[sl], pc);
+        } else if (pc) {
+            atomicAdd(&dsl[sl], pc);
+        }
+    }
+    __syncthreads();
+    for (int sl = tt; sl < req; sl += kHsymNT) dist_fin[h * req + sl] = dsl[sl];
+}
+
+size_t heavy_symbolic_lds(int64_t ppow, int64_t req) {
+    return (size_t)kHsymEW * 8 + (size_t)kHsymEW * 4 + (size_t)(kHsymEW + 1) * 4 +
+           (size_t)req * 4 + (size_t)(ppow / 32) * 4;
+}
+
+void heavy_symbolic(const DevCSR& A, const DevCSR& B, const int32_t* hrows, int64_t H,
+                    int64_t ppow, int64_t wfin, int32_t* bslot, int64_t* elem_fin,
+                    int64_t* dist_fin, hipStream_t st) {
+    if (H <= 0) return;
+    const int64_t req = ppow / wfin;
+    const int logW = ilog2(wfin);
+    fill<int32_t>(bslot, B.n * req, 0, st);
+    if (B.n > 0) {
+        hipLaunchKernelGGL(k_bslot_counts, dim3(grid_1d(ceil_div(B.n * kWave, 256))), dim3(256),
+                           0, st, B.rp, B.col, B.n, logW, (int)req, bslot);
+        SG_LAUNCH_CHECK();
+    }
+    const size_t elds = (size_t)req * 8;
+    SG_HIP(hipFuncSetAttribute((const void*)k_heavy_elem_counts,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)elds));
+    hipLaunchKernelGGL(k_heavy_elem_counts, dim3(grid_1d(H)), dim3(kElemNT), elds, st, A.rp,
+                       A.col, hrows, (int)req, bslot, elem_fin);
+    SG_LAUNCH_CHECK();
+    const size_t lds = heavy_symbolic_lds(ppow, req);
+    SG_HIP(hipFuncSetAttribute((const void*)k_heavy_symbolic,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    hipLaunchKernelGGL(k_heavy_symbolic, dim3(grid_1d(H)), dim3(kHsymNT), lds, st, A.rp, A.col,
+                       B.rp, B.col, hrows, (int)req, (int)(ppow / 32), dist_fin);
+    SG_LAUNCH_CHECK();
+}
+
+// Per natural chunk of a level: its first finest slot, and its element and
+// distinct-column counts as sums over its `g` finest slots. Level 0's
+// parents are the heavy rows (slot base h*req); a deeper level's parents are
+// the previous level's heavy chunks, found through that level's inv map.
+__global__ void k_level_from_slots(const int64_t* parent_slot0, const int32_t* parent_inv,
+                                   int64_t nparents, int nch, int g, int64_t req,
+                                   const int64_t* elem_fin, const int64_t* dist_fin,
+                                   int64_t* counts, int64_t* nnz, int64_t* slot0) {
+    int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= nparents * nch) return;
+    int64_t p = x / nch;
+    int c = (int)(x - p * nch);
+    int64_t ps = parent_inv ? parent_slot0[parent_inv[p]] : p * req;
+    int64_t s = ps + (int64_t)c * g;
+    int64_t e = 0, d = 0;
+    for (int j = 0; j < g; ++j) {
+        e += elem_fin[s + j];
+        d += dist_fin[s + j];
+    }
+    counts[x] = e;
+    nnz[x] = d;
+    slot0[x] = s;
+}
+
+void level_from_slots(const int64_t* parent_slot0, const int32_t* parent_inv, int64_t nparents,
+                      int nch, int g, int64_t req, const int64_t* elem_fin,
+                      const int64_t* dist_fin, int64_t* counts, int64_t* nnz, int64_t* slot0,
+                      hipStream_t st) {
+    int64_t n = nparents * nch;
+    if (n <= 0) return;
+    hipLaunchKernelGGL(k_level_from_slots, dim3(grid_1d(ceil_div(n, 256))), dim3(256), 0, st,
+                       parent_slot0, parent_inv, nparents, nch, g, req, elem_fin, dist_fin, counts,
+                       nnz, slot0);
+    SG_LAUNCH_CHECK();
+}
+
 // ---------------------------------------------------------------- chunk tree
 __global__ void k_reduce_children(const int64_t* nnz_child, int nch, int64_t nparents,
                                   const int32_t* inv, int64_t* nnz_parent) {

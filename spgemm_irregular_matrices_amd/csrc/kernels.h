@@ -45,6 +45,8 @@ enum ChunkBin : int {
 // Hash-table slots per light bin and the largest item each bin takes.
 constexpr int kHashSlots[4] = {128, 512, 2048, 8192};
 constexpr int64_t kHashMaxItems[4] = {64, 256, 1024, 8191};
+// Light chunks no wider than this use the bitmap-rank accumulator.
+constexpr int64_t kRankMaxWidth = 65536;
 constexpr int kWinSmall = 64;
 constexpr int kWinLarge = 1024;
 
@@ -124,6 +126,21 @@ void multisplit(const LevelGeom& g, const int32_t* in_col, const double* in_val,
                 const int32_t* pos_of, int64_t* cursor, int32_t* out_col, double* out_val,
                 hipStream_t st);
 
+// Fused symbolic pass over the heavy rows (one work group per row): per
+// finest chunk slot of width wfin, the element count and the number of
+// distinct columns. Needs heavy_symbolic_lds(ppow, ppow/wfin) bytes of LDS.
+size_t heavy_symbolic_lds(int64_t ppow, int64_t req);
+// bslot is scratch of B.n * (ppow/wfin) int32.
+void heavy_symbolic(const DevCSR& A, const DevCSR& B, const int32_t* hrows, int64_t H,
+                    int64_t ppow, int64_t wfin, int32_t* bslot, int64_t* elem_fin,
+                    int64_t* dist_fin, hipStream_t st);
+// Counts, distinct counts and first finest slot of every natural chunk of a
+// level, summed from the finest slots (g slots per chunk).
+void level_from_slots(const int64_t* parent_slot0, const int32_t* parent_inv, int64_t nparents,
+                      int nch, int g, int64_t req, const int64_t* elem_fin,
+                      const int64_t* dist_fin, int64_t* counts, int64_t* nnz, int64_t* slot0,
+                      hipStream_t st);
+
 // nnz_parent[inv[p]] = sum_c nnz_child[p*nch + c] for p < nparents.
 void reduce_children(const int64_t* nnz_child, int nch, int64_t nparents, const int32_t* inv,
                      int64_t* nnz_parent, hipStream_t st);
@@ -142,6 +159,7 @@ struct RowItems {
     const int64_t* Crp;    // numeric: row offsets
     int32_t* Ccol;
     double* Cval;
+    int hash_top_logS;     // slots (log2) of the largest light hash table
 };
 void accumulate_rows(const RowItems& it, int bin, int64_t p0, int64_t n, bool numeric,
                      hipStream_t st);
@@ -157,6 +175,7 @@ struct ChunkItems {
     int32_t* Ccol;
     double* Cval;
     int64_t width;         // column width of every chunk (power of two)
+    int hash_top_logS;     // slots (log2) of the largest light hash table
 };
 void accumulate_chunks(const ChunkItems& it, int bin, int64_t p0, int64_t n, bool numeric,
                        hipStream_t st);

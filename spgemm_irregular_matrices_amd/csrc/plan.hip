@@ -34,6 +34,7 @@ struct Params {
     int64_t final_width = 0;
     int64_t nchunks_required = 1;
     int64_t nchunks_max = 0;
+    int hash_top_logS = 13;  // slots of the largest light hash table (log2)
 };
 
 struct LevelState {
@@ -74,6 +75,7 @@ struct spgemm_plan_s {
     size_t evnext = 0;
     std::vector<Ev> evs;
     // debug dumps
+    bool fused_sym = false;
     bool dbg_valid = false;
     bool dbg_has_val = false;
     int dbg_levels = 0;
@@ -128,6 +130,8 @@ int64_t* d2h(spgemm_plan p, const int64_t* dsrc, int64_t n, hipStream_t st) {
 // GetMagnusParams (Section III-D). Readings of the garbled formulas:
 // Eq. (4): tau = s_LM / (alpha * (s_col + s_val)), alpha = 2, so that a hash
 // table of tau entries at load factor 1/alpha fills the local memory;
+// because this library's hash tables have power-of-two sizes, tau is the
+// half of the largest such table that fits in s_LM;
 // n_denseNumeric = s_LM / (s_val + s_bitmap), with a one-byte flag per
 // column; the dense width is floored to a power of two and the required
 // chunk count is the column range (rounded up to a power of two) divided by
@@ -135,19 +139,26 @@ int64_t* d2h(spgemm_plan p, const int64_t* dsrc, int64_t n, hipStream_t st) {
 // capped; nlevels is the smallest count with nchunksMax^nlevels >=
 // nchunksRequired (Eq. 7), every level but the last uses nchunksMax and the
 // last takes the remaining factor nchunksRequired / nchunksMax^(nlevels-1).
+// s_LM defaults to half of a compute unit's LDS: two work groups of each
+// LDS-heavy kernel stay resident per CU, so one group's memory phase
+// overlaps the other's LDS phase.
 Params get_params(spgemm_plan p, int64_t ncols_c) {
     Params q;
     const spgemm_options& o = p->opt;
-    q.slm = o.lds_budget_bytes > 0 ? std::min(o.lds_budget_bytes, p->dev_lds) : p->dev_lds;
+    q.slm = o.lds_budget_bytes > 0 ? std::min(o.lds_budget_bytes, p->dev_lds) : p->dev_lds / 2;
     const int64_t s_col = 4, s_val = 8, alpha = 2, s_bitmap = 1, s_histo = 4, s_rowptr = 8;
-    q.tau = q.slm / (alpha * (s_col + s_val));
+    int64_t table = std::min<int64_t>(floor_pow2(q.slm / (s_col + s_val)), 8192);
+    table = std::max<int64_t>(table, 2048);
+    q.tau = std::min(q.slm / (alpha * (s_col + s_val)), table / alpha);
     if (o.tau_override > 0) q.tau = o.tau_override;
     q.tau = std::min<int64_t>(q.tau, kHashMaxItems[3]);
     q.tau = std::max<int64_t>(q.tau, 1);
+    q.hash_top_logS = q.tau * alpha <= 4096 ? 12 : 13;
     int64_t ndense = q.slm / (s_val + s_bitmap);
     q.wdense = floor_pow2(ndense);
     // the dense-window kernel also keeps a 4-byte word prefix per 32 columns
-    while (q.wdense > 32 && q.wdense * 8 + (q.wdense / 32) * 8 > p->dev_lds) q.wdense /= 2;
+    while (q.wdense > 32 && q.wdense * 8 + (q.wdense / 32) * 8 > std::max(q.slm, int64_t(4096)))
+        q.wdense /= 2;
     if (o.chunk_width_override > 0) q.wdense = std::min(q.wdense, o.chunk_width_override);
     q.ppow = std::max<int64_t>(ceil_pow2(std::max<int64_t>(ncols_c, 1)), 32);
     const int64_t nmin = q.slm / (2 * (s_col + s_val));
@@ -208,6 +219,213 @@ void debug_copy_level(spgemm_plan p, int l, const int64_t* rp, int64_t npos, con
 __global__ void k_i32_to_i64(const int32_t* a, int64_t n, int64_t* b) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) b[i] = a[i];
+}
+
+// Symbolic pass of the heavy rows the way Algorithm 3 lays it out: expand
+// C-hat (columns only), then per level Histogram, ThreshPartition and
+// Multisplit, and count distinct columns of every final chunk.
+void heavy_symbolic_multisplit(spgemm_plan p, const DevCSR& A, const DevCSR& B,
+                               const int64_t* chat_rp, const int32_t* ent_k, const int64_t* ent_q,
+                               const int64_t* ent_dest, const int64_t* P, const int32_t* hrows,
+                               int64_t* cnt_row, hipStream_t st) {
+    Arena& ar = p->ar;
+    const Params& q = p->prm;
+    int32_t* buf0c = ar.get<int32_t>("buf0c", (size_t)p->Nh);
+    {
+        ExpandArgs ea{ent_k, ent_q, ent_dest, P, p->ne, A.val, B.rp, B.col, B.val, buf0c,
+                      nullptr};
+        PhaseScope ps(p, 0, SPGEMM_PHASE_OUTER_PROD, st);
+        expand(ea, p->Nh, st);
+        add_bytes(p, 0, SPGEMM_PHASE_OUTER_PROD, 4.0 * p->Nh + 20.0 * p->ne);
+    }
+    if (p->opt.debug_dump) debug_copy_chat(p, chat_rp, buf0c, nullptr, hrows, st);
+
+    if (q.nlevels == 0) {
+        ChunkItems ci{};
+            ci.hash_top_logS = p->prm.hash_top_logS;
+        ci.rp = chat_rp;
+        ci.map = hrows;
+        ci.bcol = buf0c;
+        ci.cnt = cnt_row;
+        ci.width = q.final_width;
+        PhaseScope ps(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, st);
+        accumulate_chunks(ci, CB_DENSE, 0, p->H, false, st);
+        add_bytes(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, 4.0 * p->Nh);
+    } else {
+        int32_t* bufc[2] = {buf0c, ar.get<int32_t>("buf1c", (size_t)p->Nh)};
+        const int64_t* rp_in = chat_rp;
+        int64_t R = p->H, total = p->Nh;
+        int L = 0;
+        for (int l = 0; l < q.nlevels; ++l) {
+            const bool last = (l == q.nlevels - 1);
+            LevelState& S_l = p->lv[l];
+            S_l.R = R;
+            S_l.total_in = total;
+            S_l.nch = q.vchunks[l];
+            S_l.shift = ilog2(q.width[l]);
+            S_l.nnat = R * S_l.nch;
+            S_l.in_buf = l & 1;
+            if (S_l.nnat >= (int64_t(1) << 31)) throw OverflowError("too many chunks in a level");
+            int64_t* counts = ar.get<int64_t>(lvname("_counts", l), (size_t)S_l.nnat);
+            int32_t* inv = ar.get<int32_t>(lvname("_inv", l), (size_t)S_l.nnat);
+            int32_t* pos = ar.get<int32_t>(lvname("_pos", l), (size_t)S_l.nnat);
+            int64_t* bins = ar.get<int64_t>(lvname("_bins", l), CB_COUNT + 1);
+            LevelGeom g{rp_in, R, total, S_l.shift, S_l.nch, q.tau};
+            {
+                PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
+                fill<int64_t>(counts, S_l.nnat, 0, st);
+                histogram(g, bufc[l & 1], counts, st);
+                classify_chunks(counts, S_l.nnat, q.tau, last, inv, pos, bins, ar, st);
+                add_bytes(p, 0, SPGEMM_PHASE_HISTO,
+                          4.0 * total + 8.0 * (R + 1) + 8.0 * S_l.nnat);
+            }
+            int64_t* hb = d2h(p, bins, CB_COUNT + 1, st);
+            for (int b = 0; b <= CB_COUNT; ++b) S_l.bins[b] = hb[b];
+            S_l.npos = S_l.bins[CB_EMPTY];
+            int64_t* rp = ar.get<int64_t>(lvname("_rp", l), (size_t)S_l.npos + 1);
+            int64_t* cursor = ar.get<int64_t>("cursor", (size_t)S_l.npos + 1);
+            {
+                PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
+                reord_rowptr(counts, inv, S_l.npos, rp, ar, st);
+                copy<int64_t>(cursor, rp, S_l.npos, st);
+            }
+            int32_t* out = bufc[(l + 1) & 1];
+            {
+                PhaseScope ps(p, 0, SPGEMM_PHASE_MULTISPLIT, st);
+                multisplit(g, bufc[l & 1], nullptr, pos, cursor, out, nullptr, st);
+                add_bytes(p, 0, SPGEMM_PHASE_MULTISPLIT, 8.0 * total + 8.0 * (R + 1));
+            }
+            if (p->opt.debug_dump) debug_copy_level(p, l, rp, S_l.npos, out, nullptr, inv, st);
+            int64_t* nnz_l = ar.get<int64_t>(lvname("_nnz", l), (size_t)S_l.nnat);
+            fill<int64_t>(nnz_l, S_l.nnat, 0, st);
+            const int64_t nheavy = S_l.bins[CB_NEXT + 1] - S_l.bins[CB_NEXT];
+            {
+                ChunkItems ci{};
+            ci.hash_top_logS = p->prm.hash_top_logS;
+                ci.rp = rp;
+                ci.map = inv;
+                ci.bcol = out;
+                ci.cnt = nnz_l;
+                ci.width = q.width[l];
+                PhaseScope ps(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, st);
+                for (int b = CB_DENSE; b <= CB_H8192; ++b)
+                    accumulate_chunks(ci, b, S_l.bins[b], S_l.bins[b + 1] - S_l.bins[b], false,
+                                      st);
+            }
+            p->stats.vchunks[l] = S_l.nch;
+            p->stats.level_in_elems[l] = total;
+            p->stats.level_heavy_chunks[l] = nheavy;
+            p->stats.level_final_chunks[l] = S_l.bins[CB_EMPTY] - S_l.bins[CB_DENSE];
+            L = l + 1;
+            if (nheavy == 0) {
+                S_l.final_elems = total;
+                add_bytes(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, 4.0 * total);
+                break;
+            }
+            int64_t elems_heavy = d2h(p, rp + nheavy, 1, st)[0];
+            S_l.final_elems = total - elems_heavy;
+            add_bytes(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, 4.0 * S_l.final_elems);
+            rp_in = rp;
+            R = nheavy;
+            total = elems_heavy;
+        }
+        p->L = L;
+        // bottom-up: a heavy chunk's count is the sum of its sub-chunks' counts
+        {
+            PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
+            for (int l = L - 2; l >= 0; --l) {
+                LevelState& a = p->lv[l];
+                const int64_t nheavy = a.bins[CB_NEXT + 1] - a.bins[CB_NEXT];
+                reduce_children(ar.get<int64_t>(lvname("_nnz", l + 1), 1), p->lv[l + 1].nch,
+                                nheavy, ar.get<int32_t>(lvname("_inv", l), 1),
+                                ar.get<int64_t>(lvname("_nnz", l), 1), st);
+            }
+            reduce_children(ar.get<int64_t>(lvname("_nnz", 0), 1), p->lv[0].nch, p->H, hrows,
+                            cnt_row, st);
+        }
+    }
+}
+
+// Symbolic pass of the heavy rows without C-hat: per finest chunk slot, the
+// element and distinct-column counts from one bitmap pass per heavy row;
+// every level's chunk counts (the Histogram of Algorithm 3) and distinct
+// counts (its Symbolic) are sums over slots. ThreshPartition then orders
+// each level's chunks exactly as the multisplit path would.
+void heavy_symbolic_fused(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t* S,
+                          const int32_t* hrows, int64_t* cnt_row, hipStream_t st) {
+    Arena& ar = p->ar;
+    const Params& q = p->prm;
+    const int64_t req = q.nlevels == 0 ? 1 : q.nchunks_required;
+    const int64_t wfin = q.nlevels == 0 ? q.ppow : q.final_width;
+    int64_t* elem_fin = ar.get<int64_t>("elem_fin", (size_t)(p->H * req));
+    int64_t* dist_fin = ar.get<int64_t>("dist_fin", (size_t)(p->H * req));
+    {
+        PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
+        int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
+        heavy_symbolic(A, B, hrows, p->H, q.ppow, wfin, bslot, elem_fin, dist_fin, st);
+        add_bytes(p, 0, SPGEMM_PHASE_HISTO, 4.0 * p->Nh + 16.0 * p->H * req);
+    }
+    if (q.nlevels == 0) {
+        PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
+        reduce_children(dist_fin, 1, p->H, hrows, cnt_row, st);
+        return;
+    }
+    const int64_t* parent_slot0 = nullptr;
+    const int32_t* parent_inv = nullptr;
+    int64_t R = p->H, total = p->Nh;
+    int64_t slots_per_chunk = req;
+    int L = 0;
+    for (int l = 0; l < q.nlevels; ++l) {
+        const bool last = (l == q.nlevels - 1);
+        LevelState& S_l = p->lv[l];
+        S_l.R = R;
+        S_l.total_in = total;
+        S_l.nch = q.vchunks[l];
+        S_l.shift = ilog2(q.width[l]);
+        S_l.nnat = R * S_l.nch;
+        S_l.in_buf = l & 1;
+        if (S_l.nnat >= (int64_t(1) << 31)) throw OverflowError("too many chunks in a level");
+        slots_per_chunk /= S_l.nch;
+        int64_t* counts = ar.get<int64_t>(lvname("_counts", l), (size_t)S_l.nnat);
+        int64_t* nnz_l = ar.get<int64_t>(lvname("_nnz", l), (size_t)S_l.nnat);
+        int64_t* slot0 = ar.get<int64_t>(lvname("_slot0", l), (size_t)S_l.nnat);
+        int32_t* inv = ar.get<int32_t>(lvname("_inv", l), (size_t)S_l.nnat);
+        int32_t* pos = ar.get<int32_t>(lvname("_pos", l), (size_t)S_l.nnat);
+        int64_t* bins = ar.get<int64_t>(lvname("_bins", l), CB_COUNT + 1);
+        {
+            PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
+            level_from_slots(parent_slot0, parent_inv, R, S_l.nch, (int)slots_per_chunk, req,
+                             elem_fin, dist_fin, counts, nnz_l, slot0, st);
+            classify_chunks(counts, S_l.nnat, q.tau, last, inv, pos, bins, ar, st);
+        }
+        int64_t* hb = d2h(p, bins, CB_COUNT + 1, st);
+        for (int b = 0; b <= CB_COUNT; ++b) S_l.bins[b] = hb[b];
+        S_l.npos = S_l.bins[CB_EMPTY];
+        int64_t* rp = ar.get<int64_t>(lvname("_rp", l), (size_t)S_l.npos + 1);
+        {
+            PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
+            reord_rowptr(counts, inv, S_l.npos, rp, ar, st);
+        }
+        const int64_t nheavy = S_l.bins[CB_NEXT + 1] - S_l.bins[CB_NEXT];
+        p->stats.vchunks[l] = S_l.nch;
+        p->stats.level_in_elems[l] = total;
+        p->stats.level_heavy_chunks[l] = nheavy;
+        p->stats.level_final_chunks[l] = S_l.bins[CB_EMPTY] - S_l.bins[CB_DENSE];
+        L = l + 1;
+        if (nheavy == 0) {
+            S_l.final_elems = total;
+            break;
+        }
+        int64_t elems_heavy = d2h(p, rp + nheavy, 1, st)[0];
+        S_l.final_elems = total - elems_heavy;
+        parent_slot0 = slot0;
+        parent_inv = inv;
+        R = nheavy;
+        total = elems_heavy;
+    }
+    p->L = L;
+    PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
+    reduce_children(ar.get<int64_t>(lvname("_nnz", 0), 1), p->lv[0].nch, p->H, hrows, cnt_row, st);
 }
 
 // ---------------------------------------------------------------- symbolic
@@ -281,6 +499,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     ri.perm = rowperm;
     ri.rowlo = rowlo;
     ri.cnt = cnt_row;
+    ri.hash_top_logS = q.hash_top_logS;
     {
         PhaseScope ps(p, 0, SPGEMM_PHASE_LIGHT_ACCUM, st);
         for (int b = RB_WIN64; b <= RB_H8192; ++b)
@@ -300,119 +519,20 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
                                    ar, st);
             add_bytes(p, 0, SPGEMM_PHASE_CSR_TO_CSC, 36.0 * p->ne);
         }
-        int32_t* buf0c = ar.get<int32_t>("buf0c", (size_t)p->Nh);
-        {
-            ExpandArgs ea{ent_k, ent_q, ent_dest, P, p->ne, A.val, B.rp, B.col, B.val, buf0c,
-                          nullptr};
-            PhaseScope ps(p, 0, SPGEMM_PHASE_OUTER_PROD, st);
-            expand(ea, p->Nh, st);
-            add_bytes(p, 0, SPGEMM_PHASE_OUTER_PROD, 4.0 * p->Nh + 20.0 * p->ne);
-        }
-        if (p->opt.debug_dump) debug_copy_chat(p, chat_rp, buf0c, nullptr, hrows, st);
         p->stats.chat_bytes = 12 * p->Nh + 8 * (p->H + 1);
-
-        if (q.nlevels == 0) {
-            ChunkItems ci{};
-            ci.rp = chat_rp;
-            ci.map = hrows;
-            ci.bcol = buf0c;
-            ci.cnt = cnt_row;
-            ci.width = q.final_width;
-            PhaseScope ps(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, st);
-            accumulate_chunks(ci, CB_DENSE, 0, p->H, false, st);
-            add_bytes(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, 4.0 * p->Nh);
-        } else {
-            int32_t* bufc[2] = {buf0c, ar.get<int32_t>("buf1c", (size_t)p->Nh)};
-            const int64_t* rp_in = chat_rp;
-            int64_t R = p->H, total = p->Nh;
-            int L = 0;
-            for (int l = 0; l < q.nlevels; ++l) {
-                const bool last = (l == q.nlevels - 1);
-                LevelState& S_l = p->lv[l];
-                S_l.R = R;
-                S_l.total_in = total;
-                S_l.nch = q.vchunks[l];
-                S_l.shift = ilog2(q.width[l]);
-                S_l.nnat = R * S_l.nch;
-                S_l.in_buf = l & 1;
-                if (S_l.nnat >= (int64_t(1) << 31)) throw OverflowError("too many chunks in a level");
-                int64_t* counts = ar.get<int64_t>(lvname("_counts", l), (size_t)S_l.nnat);
-                int32_t* inv = ar.get<int32_t>(lvname("_inv", l), (size_t)S_l.nnat);
-                int32_t* pos = ar.get<int32_t>(lvname("_pos", l), (size_t)S_l.nnat);
-                int64_t* bins = ar.get<int64_t>(lvname("_bins", l), CB_COUNT + 1);
-                LevelGeom g{rp_in, R, total, S_l.shift, S_l.nch, q.tau};
-                {
-                    PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
-                    fill<int64_t>(counts, S_l.nnat, 0, st);
-                    histogram(g, bufc[l & 1], counts, st);
-                    classify_chunks(counts, S_l.nnat, q.tau, last, inv, pos, bins, ar, st);
-                    add_bytes(p, 0, SPGEMM_PHASE_HISTO,
-                              4.0 * total + 8.0 * (R + 1) + 8.0 * S_l.nnat);
-                }
-                int64_t* hb = d2h(p, bins, CB_COUNT + 1, st);
-                for (int b = 0; b <= CB_COUNT; ++b) S_l.bins[b] = hb[b];
-                S_l.npos = S_l.bins[CB_EMPTY];
-                int64_t* rp = ar.get<int64_t>(lvname("_rp", l), (size_t)S_l.npos + 1);
-                int64_t* cursor = ar.get<int64_t>("cursor", (size_t)S_l.npos + 1);
-                {
-                    PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
-                    reord_rowptr(counts, inv, S_l.npos, rp, ar, st);
-                    copy<int64_t>(cursor, rp, S_l.npos, st);
-                }
-                int32_t* out = bufc[(l + 1) & 1];
-                {
-                    PhaseScope ps(p, 0, SPGEMM_PHASE_MULTISPLIT, st);
-                    multisplit(g, bufc[l & 1], nullptr, pos, cursor, out, nullptr, st);
-                    add_bytes(p, 0, SPGEMM_PHASE_MULTISPLIT, 8.0 * total + 8.0 * (R + 1));
-                }
-                if (p->opt.debug_dump) debug_copy_level(p, l, rp, S_l.npos, out, nullptr, inv, st);
-                int64_t* nnz_l = ar.get<int64_t>(lvname("_nnz", l), (size_t)S_l.nnat);
-                fill<int64_t>(nnz_l, S_l.nnat, 0, st);
-                const int64_t nheavy = S_l.bins[CB_NEXT + 1] - S_l.bins[CB_NEXT];
-                {
-                    ChunkItems ci{};
-                    ci.rp = rp;
-                    ci.map = inv;
-                    ci.bcol = out;
-                    ci.cnt = nnz_l;
-                    ci.width = q.width[l];
-                    PhaseScope ps(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, st);
-                    for (int b = CB_DENSE; b <= CB_H8192; ++b)
-                        accumulate_chunks(ci, b, S_l.bins[b], S_l.bins[b + 1] - S_l.bins[b], false,
-                                          st);
-                }
-                p->stats.vchunks[l] = S_l.nch;
-                p->stats.level_in_elems[l] = total;
-                p->stats.level_heavy_chunks[l] = nheavy;
-                p->stats.level_final_chunks[l] = S_l.bins[CB_EMPTY] - S_l.bins[CB_DENSE];
-                L = l + 1;
-                if (nheavy == 0) {
-                    S_l.final_elems = total;
-                    add_bytes(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, 4.0 * total);
-                    break;
-                }
-                int64_t elems_heavy = d2h(p, rp + nheavy, 1, st)[0];
-                S_l.final_elems = total - elems_heavy;
-                add_bytes(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, 4.0 * S_l.final_elems);
-                rp_in = rp;
-                R = nheavy;
-                total = elems_heavy;
-            }
-            p->L = L;
-            // bottom-up: a heavy chunk's count is the sum of its sub-chunks' counts
-            {
-                PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
-                for (int l = L - 2; l >= 0; --l) {
-                    LevelState& a = p->lv[l];
-                    const int64_t nheavy = a.bins[CB_NEXT + 1] - a.bins[CB_NEXT];
-                    reduce_children(ar.get<int64_t>(lvname("_nnz", l + 1), 1), p->lv[l + 1].nch,
-                                    nheavy, ar.get<int32_t>(lvname("_inv", l), 1),
-                                    ar.get<int64_t>(lvname("_nnz", l), 1), st);
-                }
-                reduce_children(ar.get<int64_t>(lvname("_nnz", 0), 1), p->lv[0].nch, p->H, hrows,
-                                cnt_row, st);
-            }
-        }
+        const int64_t req = q.nlevels == 0 ? 1 : q.nchunks_required;
+        // the fused pass needs the row's bitmap in LDS and a per-B-row slot
+        // histogram (B.nrows x slots int32) in HBM
+        const bool fused_fits = heavy_symbolic_lds(q.ppow, req) <= (size_t)p->dev_lds &&
+                                B.n * req <= (int64_t(1) << 28);
+        p->fused_sym = p->opt.symbolic_mode == 1 || (p->opt.symbolic_mode == 0 && fused_fits);
+        if (p->fused_sym && !fused_fits)
+            throw OverflowError("fused symbolic pass needs more LDS than the device has");
+        if (p->fused_sym)
+            heavy_symbolic_fused(p, A, B, S, hrows, cnt_row, st);
+        else
+            heavy_symbolic_multisplit(p, A, B, chat_rp, ent_k, ent_q, ent_dest, P, hrows, cnt_row,
+                                      st);
     }
 
     // C.rowPtr (Algorithm 3 lines 23-25)
@@ -475,6 +595,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
     ri.S = S;
     ri.perm = rowperm;
     ri.rowlo = rowlo;
+    ri.hash_top_logS = q.hash_top_logS;
     ri.Crp = C_rp;
     ri.Ccol = C_col;
     ri.Cval = C_val;
@@ -503,6 +624,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
 
     if (q.nlevels == 0) {
         ChunkItems ci{};
+            ci.hash_top_logS = p->prm.hash_top_logS;
         ci.rp = chat_rp;
         ci.map = hrows;
         ci.bcol = bufc[0];
@@ -537,6 +659,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         if (p->opt.debug_dump) debug_copy_level(p, l, rp, S_l.npos, bufc[outb], bufv[outb], inv, st);
         {
             ChunkItems ci{};
+            ci.hash_top_logS = p->prm.hash_top_logS;
             ci.rp = rp;
             ci.map = inv;
             ci.bcol = bufc[outb];

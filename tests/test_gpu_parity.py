@@ -36,13 +36,16 @@ def _rmat10():
     return synth.workload("rmat10_ef8")[0]
 
 
-def test_rmat10_default_light_path():
+def test_rmat10_default_and_all_light():
     A = _rmat10()
     rp, col, val, st = run_gpu(A, A)
-    assert st["heavy_rows"] == 0  # max u of this matrix is below tau
+    compare(A, A, rp, col, val)
+    rp, col, val, st = run_gpu(A, A, tau_override=6000)  # max u of this matrix is 4557
+    assert st["heavy_rows"] == 0
     compare(A, A, rp, col, val)
 
 
+@pytest.mark.parametrize("mode", [1, 2])  # fused bitmap symbolic / multisplit symbolic
 @pytest.mark.parametrize("tau,width,cap,levels", [
     (64, 0, 0, 0),        # heavy rows accumulate densely without any multisplit
     (64, 256, 32, 1),     # one level of 4 chunks
@@ -50,10 +53,10 @@ def test_rmat10_default_light_path():
     (16, 32, 2, 5),       # 32 chunks over five levels of 2
     (200, 128, 8, 1),
 ])
-def test_rmat10_forced_heavy(tau, width, cap, levels):
+def test_rmat10_forced_heavy(tau, width, cap, levels, mode):
     A = _rmat10()
     rp, col, val, st = run_gpu(A, A, tau_override=tau, chunk_width_override=width,
-                               nchunks_cap=cap)
+                               nchunks_cap=cap, symbolic_mode=mode)
     assert st["heavy_rows"] > 0
     assert st["nlevels"] == levels, st
     compare(A, A, rp, col, val)
@@ -140,7 +143,7 @@ def test_chat_stage_matches_oracle():
     from spgemm_irregular_matrices_amd import binding
     dA, dB = binding.DeviceCSR.from_host(A), binding.DeviceCSR.from_host(B)
     with binding.Plan(tau_override=40, chunk_width_override=64, nchunks_cap=2,
-                      debug_dump=True) as p:
+                      debug_dump=True, symbolic_mode=2) as p:
         C = p.multiply(dA, dB)
         torch.cuda.synchronize()
         chat = p.debug(-1)
@@ -165,22 +168,26 @@ def test_chat_stage_matches_oracle():
     compare(A, B, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy())
 
 
+@pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("tau", [6826, 1, 20, 300])
 @pytest.mark.parametrize("seed", [1, 2])
-def test_random_skewed_paths(tau, seed):
+def test_random_skewed_paths(tau, seed, mode):
     A = synth.random_csr(600, 500, seed=seed, value_seed=seed + 10, mean_len=12, skew=1.1,
                          empty_frac=0.05)
     B = synth.random_csr(500, 700, seed=seed + 20, value_seed=seed + 30, mean_len=9, skew=1.1,
                          empty_frac=0.05)
-    rp, col, val, st = run_gpu(A, B, tau_override=tau, chunk_width_override=32, nchunks_cap=4)
+    rp, col, val, st = run_gpu(A, B, tau_override=tau, chunk_width_override=32, nchunks_cap=4,
+                               symbolic_mode=mode)
     compare(A, B, rp, col, val)
 
 
 def test_small_integer_values_exact():
     A = synth.rmat(11, 8, seed=61, value_seed=62, values="int")
-    rp, col, val, st = run_gpu(A, A, tau_override=100, chunk_width_override=64, nchunks_cap=4)
-    assert st["heavy_rows"] > 0 and st["nlevels"] >= 2
-    compare(A, A, rp, col, val, exact_values=True)
+    for mode in (1, 2):
+        rp, col, val, st = run_gpu(A, A, tau_override=100, chunk_width_override=64, nchunks_cap=4,
+                                   symbolic_mode=mode)
+        assert st["heavy_rows"] > 0 and st["nlevels"] >= 2
+        compare(A, A, rp, col, val, exact_values=True)
     rp, col, val, st = run_gpu(A, A)
     compare(A, A, rp, col, val, exact_values=True)
 
