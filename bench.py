@@ -39,7 +39,72 @@ def parse():
     ap.add_argument("--tau", type=int, default=0)
     ap.add_argument("--width", type=int, default=0)
     ap.add_argument("--cap", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    """A plain device copy of known size.
+
+    HBM counters read on it scale the counters of the other kernels, and its
+    rate is the measured speed of light (read + write bytes per second) that
+    the gMAGNUS page uses as the kernels' peak (Section IV-C).
+    """
+    import torch
+    n = mib * (1 << 20) // 8
+    src = torch.empty(n, dtype=torch.float64, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    # a plain streaming elementwise kernel: reads n*8 bytes, writes n*8 bytes
+    torch.add(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record()
+    for _ in range(reps):
+        torch.add(src, 1.0, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_calibration_bytes_each_way": n * 8, "launches": reps + 1,
+                      "copy_ms": ms, "copy_GBps_read_plus_write": 2 * n * 8 / (ms * 1e-3) / 1e9}))
+
+
+# kernels behind each timed phase, for the HBM traffic the counters measured
+PHASE_KERNELS = {
+    "numeric:multisplit": ["k_multisplit<true,"],
+    "numeric:outer_prod": ["k_expand<true>"],
+    "numeric:heavy_accum": ["k_acc_window<1,true,", "k_acc_rank<true,", "k_acc_hash<1,true,"],
+}
+
+
+def measured_traffic(workload: str, phase: str):
+    """HBM bytes per launch of a phase's kernels from profiles/hbm_traffic_<workload>.txt.
+
+    The file holds FETCH_SIZE and WRITE_SIZE per dispatch (already scaled by the
+    plain-copy calibration) together with a hash of the kernel's source file;
+    a kernel whose source changed since is not reported (None).
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    prefixes = PHASE_KERNELS.get(phase)
+    if not prefixes or not os.path.exists(path):
+        return None
+    total, found = 0, False
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        name, wl, src, digest, fetch, write = line.split()
+        if wl != workload or not any(name.startswith(p) for p in prefixes):
+            continue
+        src_path = os.path.join(ROOT, "spgemm_irregular_matrices_amd", "csrc", src)
+        now = hashlib.sha256(open(src_path, "rb").read()).hexdigest()[:16]
+        if now != digest:
+            return None
+        total += int(fetch) + int(write)
+        found = True
+    return total if found else None
 
 
 def cpu_baseline(A, B, target_s: float):
@@ -72,6 +137,9 @@ def cpu_baseline(A, B, target_s: float):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the product is not sharded across GPUs in this build", file=sys.stderr)
@@ -133,8 +201,9 @@ def main():
     launch_ms = d["ms"] / max(d["launches"], 1)
     bytes_per_launch = d["bytes"] / max(d["launches"], 1)
     achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9 if launch_ms > 0 else 0.0
+    traffic = measured_traffic(args.workload, f"{dom[0]}:{dom[1]}")
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "kernel": f"{dom[0]}:{dom[1]}", "launch_ms": launch_ms,
                 "bytes_per_launch": bytes_per_launch}
     heavy_bytes = sum(v["bytes"] for k, v in per_phase.items()

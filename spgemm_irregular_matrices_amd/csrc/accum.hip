@@ -117,6 +117,18 @@ __device__ __forceinline__ int team_sum(int v, int* sh) {
     else return block_reduce_sum<TW>(v, sh);
 }
 
+// Pack 32 one-byte presence flags (each 0 or 1) into a 32-bit mask.
+__device__ __forceinline__ uint32_t pack_flags32(const uint32_t* f) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t x = f[i];
+        uint32_t b = (x & 1u) | ((x >> 7) & 2u) | ((x >> 14) & 4u) | ((x >> 21) & 8u);
+        m |= b << (4 * i);
+    }
+    return m;
+}
+
 // ---------------------------------------------------------------- hash
 // One item per work group of TW threads; the table has S = 2^LOGS slots.
 template <int MODE, bool NUM, int TW, int LOGS>
@@ -324,8 +336,9 @@ __global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, ChunkItems c
     const int team = threadIdx.x / TW;
     const int tt = threadIdx.x % TW;
     double* acc = (double*)lds_w + (NUM ? team * W : 0);
-    uint32_t* bits = (uint32_t*)((double*)lds_w + (NUM ? NI * W : 0)) + team * NWD;
-    int* wpre = (int*)((uint32_t*)((double*)lds_w + (NUM ? NI * W : 0)) + NI * NWD) + team * NWD;
+    uint32_t* flags = (uint32_t*)((double*)lds_w + (NUM ? NI * W : 0)) + team * NWD * 8;
+    uint32_t* bits = (uint32_t*)((double*)lds_w + (NUM ? NI * W : 0)) + NI * NWD * 8 + team * NWD;
+    int* wpre = (int*)((uint32_t*)((double*)lds_w + (NUM ? NI * W : 0)) + NI * NWD * 9) + team * NWD;
     __shared__ int red_sh[TW / kWave + 1];
     __shared__ int32_t lo_sh[NI];
 
@@ -333,7 +346,7 @@ __global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, ChunkItems c
     const bool active = item < nitems;
     ItemHdr h;
     if (active) h = load_item<MODE>(ri, ci, p0 + item);
-    for (int w = tt; w < NWD; w += TW) bits[w] = 0u;
+    for (int w = tt; w < NWD * 8; w += TW) flags[w] = 0u;
     if constexpr (NUM)
         for (int s = tt; s < W; s += TW) acc[s] = 0.0;
     if (tt == 0 && active) {
@@ -345,16 +358,27 @@ __global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, ChunkItems c
     }
     __syncthreads();
     const int32_t lo = active ? lo_sh[team] : 0;
+    uint8_t* fb = (uint8_t*)flags;
     if (active) {
         int64_t cur = h.a0;
-        for (int64_t t = tt; t < h.count; t += TW) {
-            int32_t c;
-            double v = 0.0;
-            load_elem<MODE, NUM>(ri, ci, h, t, cur, c, v);
-            uint32_t idx = (uint32_t)(c - lo);
-            if (idx < (uint32_t)W) {
-                atomicOr(&bits[idx >> 5], 1u << (idx & 31));
-                if constexpr (NUM) atomicAdd(&acc[idx], v);
+        constexpr int U = (MODE == MODE_CHUNK) ? 4 : 1;  // loads in flight per thread
+        for (int64_t t0 = tt; t0 < h.count; t0 += (int64_t)TW * U) {
+            int32_t c[U];
+            double v[U];
+#pragma unroll
+            for (int uu = 0; uu < U; ++uu) {
+                const int64_t t = t0 + (int64_t)uu * TW;
+                c[uu] = lo - 1;  // out of the window: skipped below
+                v[uu] = 0.0;
+                if (t < h.count) load_elem<MODE, NUM>(ri, ci, h, t, cur, c[uu], v[uu]);
+            }
+#pragma unroll
+            for (int uu = 0; uu < U; ++uu) {
+                uint32_t idx = (uint32_t)(c[uu] - lo);
+                if (idx < (uint32_t)W) {
+                    fb[idx] = 1;
+                    if constexpr (NUM) atomicAdd(&acc[idx], v[uu]);
+                }
             }
         }
     }
@@ -363,7 +387,11 @@ __global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, ChunkItems c
     const int per = (NWD + TW - 1) / TW;
     const int w0 = min(NWD, tt * per), w1 = min(NWD, w0 + per);
     int pc = 0;
-    for (int w = w0; w < w1; ++w) pc += __popc(bits[w]);
+    for (int w = w0; w < w1; ++w) {
+        uint32_t m = pack_flags32(flags + w * 8);
+        bits[w] = m;
+        pc += __popc(m);
+    }
     if constexpr (!NUM) {
         int tot = team_sum<TW>(pc, red_sh);
         if (active && tt == 0) write_count<MODE>(ri, ci, h, tot);
@@ -419,7 +447,7 @@ template <int MODE, bool NUM, int TW, int NI>
 static void launch_window(const RowItems& ri, const ChunkItems& ci, int64_t p0, int64_t n,
                           int64_t W, hipStream_t st) {
     if (W < 32 || (W & (W - 1))) throw std::logic_error("window width must be a power of two >= 32");
-    size_t lds = (size_t)NI * ((NUM ? W * 8 : 0) + (W / 32) * 4 * (NUM ? 2 : 1));
+    size_t lds = (size_t)NI * ((NUM ? W * 8 : 0) + W + (W / 32) * 4 * 2);
     if (lds > 160 * 1024) throw OverflowError("dense window exceeds LDS");
     auto kern = k_acc_window<MODE, NUM, TW, NI>;
     SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -449,7 +477,11 @@ static void launch_rank_bin(int hb, const ChunkItems& ci, int64_t p0, int64_t n,
         case 0: launch_rank<NUM, 64, 1>(ci, p0, n, st); break;
         case 1: launch_rank<NUM, 64, 4>(ci, p0, n, st); break;
         case 2: launch_rank<NUM, 128, 8>(ci, p0, n, st); break;
-        default: launch_rank<NUM, 512, 16>(ci, p0, n, st); break;
+        default:
+            // the top light class holds chunks of at most tau elements
+            if (ci.hash_top_logS <= 12) launch_rank<NUM, 256, 8>(ci, p0, n, st);
+            else launch_rank<NUM, 512, 16>(ci, p0, n, st);
+            break;
     }
 }
 

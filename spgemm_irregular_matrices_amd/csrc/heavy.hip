@@ -69,18 +69,20 @@ struct LoadI32AsI64 {
     const int32_t* p;
     __device__ int64_t operator()(int64_t i) const { return p[i]; }
 };
-struct SliceLen {
+// Pieces of 64 products (one per lane of a wavefront) per CSC entry.
+struct SlicePieces {
     const int32_t* ent_k;
     const int64_t* brp;
     __device__ int64_t operator()(int64_t e) const {
         int32_t k = ent_k[e];
-        return brp[k + 1] - brp[k];
+        return (brp[k + 1] - brp[k] + kWave - 1) / kWave;
     }
 };
 
 int64_t masked_csr2csc(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
                        int64_t H, const int64_t* chat_rp, int32_t** ent_k, int64_t** ent_q,
-                       int64_t** ent_dest, int64_t** P, Arena& ar, hipStream_t st) {
+                       int64_t** ent_dest, int64_t** P, int64_t* total_pieces, Arena& ar,
+                       hipStream_t st) {
     int32_t* colcnt = ar.get<int32_t>("csc_colcnt", (size_t)A.m + 1);
     int64_t* colptr = ar.get<int64_t>("csc_colptr", (size_t)A.m + 1);
     fill<int32_t>(colcnt, A.m, 0, st);
@@ -101,61 +103,120 @@ int64_t masked_csr2csc(const DevCSR& A, const DevCSR& B, const int64_t* S, const
     hipLaunchKernelGGL(k_csc_fill, dim3(grid_1d(blocks)), dim3(256), 0, st, A.rp, A.col, B.rp,
                        hrows, H, S, chat_rp, cursor, *ent_k, *ent_q, *ent_dest);
     SG_LAUNCH_CHECK();
-    scan_exclusive(SliceLen{*ent_k, B.rp}, ne, *P, ar, st);
+    scan_exclusive(SlicePieces{*ent_k, B.rp}, ne, *P, ar, st);
+    SG_HIP(hipMemcpyAsync(total_pieces, *P + ne, sizeof(int64_t), hipMemcpyDeviceToHost, st));
+    SG_HIP(hipStreamSynchronize(st));
     return ne;
 }
 
 // ---------------------------------------------------------------- outer product
-// Static partition of the flattened product space (Section III-B, Fig. 2):
-// work group g takes elements [g*E, (g+1)*E). Each round of 256 elements
-// finds its CSC entry by a binary search in an LDS copy of the flattened
-// offsets P (an element's entry is the last one whose offset <= it); the
-// element's place inside the entry's B row is its distance from that
-// offset. Consecutive threads read consecutive B entries and write
-// consecutive C-hat entries.
+// Static partition of the flattened product space (Section III-B, Fig. 2).
+// The space is cut into pieces of 64 products, one per lane: piece j of CSC
+// entry e (slice k = ent_k[e], value a) covers products [64j, 64j+64) of
+// B row k, scaled by a and written to the entry's contiguous run of its
+// C-hat row. Work group g takes pieces [g*PPB, (g+1)*PPB): it stages the
+// descriptors of the (at most PPB) entries those pieces belong to in LDS,
+// then its waves take pieces in turn, several at once, so B reads and C-hat
+// writes are coalesced and no element needs a search. Reads of B rows are
+// shared across the entries of one slice (CSC order keeps them adjacent).
 constexpr int kExpandNT = 256;
-constexpr int64_t kExpandEPB = 8192;
+constexpr int kExpandPPB = 128;   // pieces per work group (8192 products at most)
+constexpr int kExpandU = 2;       // pieces in flight per wave
 
 template <bool NUM>
-__global__ __launch_bounds__(kExpandNT) void k_expand(ExpandArgs a, int64_t total) {
-    __shared__ int64_t win[kExpandNT];
-    __shared__ int64_t ecur_sh;
-    const int64_t g0 = (int64_t)blockIdx.x * kExpandEPB;
-    const int64_t g1 = min(total, g0 + kExpandEPB);
-    if (threadIdx.x == 0) ecur_sh = upper_index(a.P, int64_t(0), a.ne, g0);
+__global__ __launch_bounds__(kExpandNT) void k_expand(ExpandArgs a, int64_t total_pieces) {
+    constexpr int NW = kExpandNT / kWave;
+    __shared__ int64_t s_pp[kExpandPPB + 1];
+    __shared__ int64_t s_dest[kExpandPPB];
+    __shared__ int64_t s_bst[kExpandPPB];
+    __shared__ int s_nb[kExpandPPB];
+    __shared__ double s_a[kExpandPPB];
+    __shared__ int64_t s_e0;
+    __shared__ int s_ne;
+    const int tt = threadIdx.x, w = tt / kWave, lane = lane_id();
+    const int64_t P0 = (int64_t)blockIdx.x * kExpandPPB;
+    const int64_t P1 = min(total_pieces, P0 + kExpandPPB);
+    if (tt == 0) {
+        // first entry of this tile and of the next: the last entry is the
+        // next tile's first one unless that entry starts exactly at P1
+        const int64_t e0 = a.tile_e0[blockIdx.x];
+        int64_t e1 = a.ne - 1;
+        if (P1 < total_pieces) {
+            const int64_t en = a.tile_e0[blockIdx.x + 1];
+            e1 = (a.P[en] == P1) ? en - 1 : en;
+        }
+        s_e0 = e0;
+        s_ne = (int)(e1 - e0 + 1);
+    }
     __syncthreads();
-    for (int64_t r0 = g0; r0 < g1; r0 += kExpandNT) {
-        const int64_t ec = ecur_sh;
-        {
-            int64_t e = ec + threadIdx.x;
-            win[threadIdx.x] = e <= a.ne ? a.P[e] : INT64_MAX;
+    const int64_t e0 = s_e0;
+    const int ne = s_ne;
+    for (int j = tt; j <= ne; j += kExpandNT) {
+        const int64_t e = e0 + j;
+        s_pp[j] = a.P[e];
+        if (j < ne) {
+            const int32_t k = a.ent_k[e];
+            const int64_t b0 = a.Brp[k];
+            s_bst[j] = b0;
+            s_nb[j] = (int)(a.Brp[k + 1] - b0);
+            s_dest[j] = a.ent_dest[e];
+            if constexpr (NUM) s_a[j] = a.Aval[a.ent_q[e]];
         }
-        __syncthreads();
-        const int64_t t = r0 + threadIdx.x;
-        const int64_t rend = min(g1, r0 + kExpandNT);
-        if (t < rend) {
-            int j = (int)upper_index(win, int64_t(0), int64_t(kExpandNT), t);
-            int64_t e = ec + j;
-            int64_t off = t - win[j];
-            int32_t k = a.ent_k[e];
-            int64_t dest = a.ent_dest[e] + off;
-            int64_t bi = a.Brp[k] + off;
-            a.out_col[dest] = a.Bcol[bi];
-            if constexpr (NUM) a.out_val[dest] = a.Aval[a.ent_q[e]] * a.Bval[bi];
-            if (t == rend - 1) ecur_sh = e;
+    }
+    __syncthreads();
+    int jj = 0;
+    for (int64_t p = P0 + w; p < P1; p += (int64_t)NW * kExpandU) {
+        int32_t col[kExpandU];
+        double bv[kExpandU];
+        int64_t dst[kExpandU];
+        bool ok[kExpandU];
+        double av[kExpandU];
+#pragma unroll
+        for (int u = 0; u < kExpandU; ++u) {
+            const int64_t pu = p + (int64_t)u * NW;
+            ok[u] = false;
+            if (pu < P1) {
+                while (s_pp[jj + 1] <= pu) ++jj;
+                const int off = (int)(pu - s_pp[jj]) * kWave + lane;
+                if (off < s_nb[jj]) {
+                    ok[u] = true;
+                    const int64_t bi = s_bst[jj] + off;
+                    dst[u] = s_dest[jj] + off;
+                    col[u] = a.Bcol[bi];
+                    if constexpr (NUM) {
+                        bv[u] = a.Bval[bi];
+                        av[u] = s_a[jj];
+                    }
+                }
+            }
         }
-        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kExpandU; ++u) {
+            if (ok[u]) {
+                a.out_col[dst[u]] = col[u];
+                if constexpr (NUM) a.out_val[dst[u]] = av[u] * bv[u];
+            }
+        }
     }
 }
 
-void expand(const ExpandArgs& a, int64_t total, hipStream_t st) {
-    if (total <= 0) return;
-    int64_t blocks = ceil_div(total, kExpandEPB);
+int64_t expand_tiles(int64_t total_pieces) { return ceil_div(total_pieces, kExpandPPB); }
+
+void expand_tile_starts(const int64_t* P, int64_t ne, int64_t total_pieces, int64_t* tile_e0,
+                        hipStream_t st) {
+    tile_starts(P, ne, kExpandPPB, expand_tiles(total_pieces), tile_e0, st);
+}
+
+void expand(const ExpandArgs& a, hipStream_t st) {
+    const int64_t total_pieces = a.total_pieces;
+    if (a.ne <= 0 || total_pieces <= 0) return;
+    int64_t blocks = ceil_div(total_pieces, kExpandPPB);
     if (a.out_val)
-        hipLaunchKernelGGL(k_expand<true>, dim3(grid_1d(blocks)), dim3(kExpandNT), 0, st, a, total);
+        hipLaunchKernelGGL(k_expand<true>, dim3(grid_1d(blocks)), dim3(kExpandNT), 0, st, a,
+                           total_pieces);
     else
         hipLaunchKernelGGL(k_expand<false>, dim3(grid_1d(blocks)), dim3(kExpandNT), 0, st, a,
-                           total);
+                           total_pieces);
     SG_LAUNCH_CHECK();
 }
 
@@ -171,7 +232,8 @@ inline int rows_per_range(int64_t E, int64_t tau) {
 constexpr int kHistNT = 256;
 
 __global__ __launch_bounds__(kHistNT) void k_histogram(LevelGeom g, const int32_t* in_col,
-                                                       int64_t* counts, int64_t epb, int nr_max) {
+                                                       int64_t* counts, const int64_t* tile_r0,
+                                                       int64_t epb, int nr_max) {
     extern __shared__ int64_t lds_h[];
     int64_t* rb = lds_h;                          // nr_max + 1 row bounds
     int* hist = (int*)(lds_h + nr_max + 1);       // nr_max * nch counters
@@ -179,7 +241,7 @@ __global__ __launch_bounds__(kHistNT) void k_histogram(LevelGeom g, const int32_
     const int64_t g0 = (int64_t)blockIdx.x * epb;
     const int64_t g1 = min(g.total, g0 + epb);
     const int nkeys = nr_max * g.nch;
-    if (threadIdx.x == 0) r0_sh = upper_index(g.rp, int64_t(0), g.nrows, g0);
+    if (threadIdx.x == 0) r0_sh = tile_r0[blockIdx.x];
     for (int x = threadIdx.x; x < nkeys; x += kHistNT) hist[x] = 0;
     __syncthreads();
     const int64_t r0 = r0_sh;
@@ -211,14 +273,17 @@ static int64_t hist_epb(int64_t tau, int nch, int* nr_max) {
     return epb;
 }
 
-void histogram(const LevelGeom& g, const int32_t* in_col, int64_t* counts, hipStream_t st) {
+void histogram(const LevelGeom& g, const int32_t* in_col, int64_t* counts, Arena& ar,
+               hipStream_t st) {
     if (g.total <= 0) return;
     int nr_max;
     int64_t epb = hist_epb(g.tau, g.nch, &nr_max);
     size_t lds = (size_t)(nr_max + 1) * 8 + (size_t)nr_max * g.nch * 4;
     int64_t blocks = ceil_div(g.total, epb);
+    int64_t* tile_r0 = ar.get<int64_t>("hist_tile_r0", (size_t)blocks + 1);
+    tile_starts(g.rp, g.nrows, epb, blocks, tile_r0, st);
     hipLaunchKernelGGL(k_histogram, dim3(grid_1d(blocks)), dim3(kHistNT), lds, st, g, in_col,
-                       counts, epb, nr_max);
+                       counts, tile_r0, epb, nr_max);
     SG_LAUNCH_CHECK();
 }
 
@@ -257,157 +322,203 @@ void reord_rowptr(const int64_t* counts, const int32_t* inv, int64_t npos, int64
 }
 
 // ---------------------------------------------------------------- multisplit
-// One work group per E = NT*K consecutive input elements (Algorithm 5):
-//  1. local histogram of (local row, chunk) keys; the LDS atomic's return
-//     value is the element's rank inside its key;
-//  2. exclusive scan of the local histogram, and one global reservation per
-//     nonempty key on the chunk's cursor in C-hat-reord;
-//  3. permute the elements into LDS, grouped by key;
-//  4. write the LDS buffer out in order, so consecutive threads write
-//     consecutive slots of each chunk (the coalesced write of Alg. 5).
-// Elements inside a chunk end up in no particular order.
-constexpr int kMsNT = 256;
-constexpr int kMsK = 16;
-constexpr int64_t kMsEPB = kMsNT * kMsK;
-
-template <bool NUM>
+// One work group per tile of E = NT*K consecutive input elements
+// (Algorithm 5):
+//  1. local histogram of (local row, chunk) keys. Each wave ranks its
+//     elements by matching keys across lanes with ballots (one ballot per
+//     key bit), so equal keys are found without LDS atomics; the first lane
+//     of each key group adds the group to the wave's private histogram
+//     (subgroup-private histograms, Section III-C);
+//  2. per key: the waves' exclusive prefix, the key's offset in the tile
+//     (block-wide scan) and one global reservation on the chunk's cursor in
+//     C-hat-reord;
+//  3. permute the elements into LDS, grouped by key, recording each slot's
+//     key;
+//  4. write the LDS buffer out in slot order: slot d goes to
+//     (reserved base of its key) - (key's tile offset) + d, so consecutive
+//     threads write consecutive slots of each chunk (the coalesced write of
+//     Algorithm 5).
+// Inside a tile, elements keep their input order within each chunk; across
+// tiles the order follows the reservations.
+template <bool NUM, int kMsNT, int kMsK>
 __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t* in_col,
                                                       const double* in_val,
                                                       const int32_t* pos_of,
                                                       unsigned long long* cursor,
                                                       int32_t* out_col, double* out_val,
-                                                      int64_t epb, int nr_max) {
+                                                      const int64_t* tile_r0, int64_t epb,
+                                                      int nr_max) {
+    constexpr int NW = kMsNT / kWave;
     extern __shared__ int64_t lds_m[];
     const int nkeys = nr_max * g.nch;
-    int64_t* gbase = lds_m;                          // nkeys
-    int64_t* rb = gbase + nkeys;                     // nr_max + 1
+    int64_t* delta = lds_m;                          // nkeys
+    int64_t* rb = delta + nkeys;                     // nr_max + 1
     double* valbuf = (double*)(rb + nr_max + 1);     // epb (NUM only)
-    int* hist = (int*)(valbuf + (NUM ? epb : 0));    // nkeys
-    int* loff = hist + nkeys;                        // nkeys + 1
+    int* whist = (int*)(valbuf + (NUM ? epb : 0));   // NW * nkeys
+    int* loff = whist + NW * nkeys;                  // nkeys + 1
     int* colbuf = loff + nkeys + 1;                  // epb
+    uint16_t* keybuf = (uint16_t*)(colbuf + epb);    // epb
     __shared__ int64_t r0_sh;
-    __shared__ int scan_sh[kMsNT / kWave + 1];
+    __shared__ int scan_sh[NW + 1];
 
+    const int tt = threadIdx.x, w = tt / kWave;
     const int64_t g0 = (int64_t)blockIdx.x * epb;
     const int64_t g1 = min(g.total, g0 + epb);
     const int n_wg = (int)(g1 - g0);
     const int mask = g.nch - 1;
-    if (threadIdx.x == 0) r0_sh = upper_index(g.rp, int64_t(0), g.nrows, g0);
-    for (int x = threadIdx.x; x < nkeys; x += kMsNT) hist[x] = 0;
+    if (tt == 0) r0_sh = tile_r0[blockIdx.x];
+    for (int x = tt; x < NW * nkeys; x += kMsNT) whist[x] = 0;
     __syncthreads();
     const int64_t r0 = r0_sh;
-    for (int j = threadIdx.x; j <= nr_max; j += kMsNT)
+    for (int j = tt; j <= nr_max; j += kMsNT)
         rb[j] = (r0 + j <= g.nrows) ? g.rp[r0 + j] : INT64_MAX;
     __syncthreads();
 
-    // 1. load and local histogram
+    // 1. load, key, rank within the wave by ballot matching
+    int nbits = 0;
+    while ((1 << nbits) < nkeys) ++nbits;
     int32_t col[kMsK];
     double val[kMsK];
     int key[kMsK];
     int rank[kMsK];
-    int lr = 0;
 #pragma unroll
     for (int k = 0; k < kMsK; ++k) {
-        int64_t t = g0 + (int64_t)k * kMsNT + threadIdx.x;
+        int64_t t = g0 + (int64_t)k * kMsNT + tt;
         key[k] = -1;
         if (t < g1) {
             col[k] = in_col[t];
             if constexpr (NUM) val[k] = in_val[t];
         }
     }
+    int lr = 0;
+    int* myhist = whist + w * nkeys;
+    const uint64_t lt = (lane_id() == 0) ? 0ull : (~0ull >> (kWave - lane_id()));
 #pragma unroll
     for (int k = 0; k < kMsK; ++k) {
-        int64_t t = g0 + (int64_t)k * kMsNT + threadIdx.x;
+        int64_t t = g0 + (int64_t)k * kMsNT + tt;
+        int kk = -1;
         if (t < g1) {
             while (lr + 1 < nr_max && t >= rb[lr + 1]) ++lr;
-            key[k] = lr * g.nch + ((col[k] >> g.shift) & mask);
-            rank[k] = atomicAdd(&hist[key[k]], 1);
+            kk = lr * g.nch + ((col[k] >> g.shift) & mask);
+        }
+        key[k] = kk;
+        uint64_t eq = __ballot(kk >= 0);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (kk >> b) & 1;
+            const uint64_t m = __ballot(bit);
+            eq &= bit ? m : ~m;
+        }
+        if (kk >= 0) {
+            const int before = __popcll(eq & lt);
+            const int base = myhist[kk];
+            rank[k] = base + before;
+            if (before == 0) myhist[kk] = base + __popcll(eq);
         }
     }
     __syncthreads();
 
-    // 2. local exclusive scan (each thread a contiguous run of keys) + reservation
+    // 2. per key: wave prefixes, tile offset (block scan) and reservation
     {
         const int per = (nkeys + kMsNT - 1) / kMsNT;
-        const int k0 = min(nkeys, (int)threadIdx.x * per);
+        const int k0 = min(nkeys, tt * per);
         const int k1 = min(nkeys, k0 + per);
         int s = 0;
-        for (int x = k0; x < k1; ++x) s += hist[x];
+        for (int x = k0; x < k1; ++x) {
+            int run = 0;
+            for (int ww = 0; ww < NW; ++ww) {
+                int c = whist[ww * nkeys + x];
+                whist[ww * nkeys + x] = run;
+                run += c;
+            }
+            loff[x] = run;  // total for now
+            s += run;
+        }
         int tot;
         int pre = block_exclusive_scan<kMsNT>(s, scan_sh, &tot);
         for (int x = k0; x < k1; ++x) {
-            int v = hist[x];
+            const int v = loff[x];
             loff[x] = pre;
-            pre += v;
             if (v) {
-                int64_t nat = (r0 + x / g.nch) * g.nch + (x & mask);
-                int p = pos_of[nat];
-                gbase[x] = (int64_t)atomicAdd(&cursor[p], (unsigned long long)v);
+                const int64_t nat = (r0 + x / g.nch) * g.nch + (x & mask);
+                const int p = pos_of[nat];
+                delta[x] = (int64_t)atomicAdd(&cursor[p], (unsigned long long)v) - pre;
             }
+            pre += v;
         }
-        if (threadIdx.x == 0) loff[nkeys] = tot;
+        if (tt == 0) loff[nkeys] = tot;
     }
     __syncthreads();
 
     // 3. permute into LDS
 #pragma unroll
     for (int k = 0; k < kMsK; ++k) {
-        if (key[k] >= 0) {
-            int d = loff[key[k]] + rank[k];
+        const int kk = key[k];
+        if (kk >= 0) {
+            const int d = loff[kk] + myhist[kk] + rank[k];
             colbuf[d] = col[k];
+            keybuf[d] = (uint16_t)kk;
             if constexpr (NUM) valbuf[d] = val[k];
         }
     }
     __syncthreads();
 
-    // 4. ordered write: slot d's local row is found from the row starts in loff
-    lr = 0;
-    for (int d = threadIdx.x; d < n_wg; d += kMsNT) {
-        while (lr + 1 < nr_max && d >= loff[(lr + 1) * g.nch]) ++lr;
-        int32_t c = colbuf[d];
-        int kk = lr * g.nch + ((c >> g.shift) & mask);
-        int64_t ga = gbase[kk] + (d - loff[kk]);
-        out_col[ga] = c;
+    // 4. ordered write
+    for (int d = tt; d < n_wg; d += kMsNT) {
+        const int64_t ga = delta[keybuf[d]] + d;
+        out_col[ga] = colbuf[d];
         if constexpr (NUM) out_val[ga] = valbuf[d];
     }
 }
 
-static size_t ms_lds(int64_t epb, int nr_max, int nch, bool num) {
+static size_t ms_lds(int64_t epb, int nr_max, int nch, bool num, int nw) {
     size_t nkeys = (size_t)nr_max * nch;
-    return nkeys * 8 + (size_t)(nr_max + 1) * 8 + (num ? (size_t)epb * 8 : 0) + nkeys * 4 +
-           (nkeys + 1) * 4 + (size_t)epb * 4;
+    return nkeys * 8 + (size_t)(nr_max + 1) * 8 + (num ? (size_t)epb * 8 : 0) +
+           (size_t)nw * nkeys * 4 + (nkeys + 1) * 4 + (size_t)epb * 4 + (size_t)epb * 2 + 8;
 }
 
-void multisplit(const LevelGeom& g, const int32_t* in_col, const double* in_val,
-                const int32_t* pos_of, int64_t* cursor, int32_t* out_col, double* out_val,
-                hipStream_t st) {
-    if (g.total <= 0) return;
+template <int NT, int K>
+static void ms_launch(const LevelGeom& g, const int32_t* in_col, const double* in_val,
+                      const int32_t* pos_of, int64_t* cursor, int32_t* out_col, double* out_val,
+                      Arena& ar, hipStream_t st) {
     bool num = out_val != nullptr;
-    // Elements per work group: the full register tile unless the local
-    // histogram (rows per range x chunks) pushes LDS past 64 KiB.
-    int64_t epb = kMsEPB;
+    int64_t epb = (int64_t)NT * K;
     int nr_max = rows_per_range(epb, g.tau);
-    while (epb > 64 && ms_lds(epb, nr_max, g.nch, num) > 65536) {
+    while (epb > 64 && ms_lds(epb, nr_max, g.nch, num, NT / kWave) > 65536) {
         epb /= 2;
         nr_max = rows_per_range(epb, g.tau);
     }
-    size_t lds = ms_lds(epb, nr_max, g.nch, num);
+    if ((int64_t)nr_max * g.nch > 65535) throw OverflowError("multisplit keys exceed 16 bits");
+    size_t lds = ms_lds(epb, nr_max, g.nch, num, NT / kWave);
     if (lds > 160 * 1024) throw OverflowError("multisplit local histogram exceeds LDS");
     int64_t blocks = ceil_div(g.total, epb);
+    int64_t* tile_r0 = ar.get<int64_t>("ms_tile_r0", (size_t)blocks + 1);
+    tile_starts(g.rp, g.nrows, epb, blocks, tile_r0, st);
     if (num) {
-        SG_HIP(hipFuncSetAttribute((const void*)k_multisplit<true>,
+        SG_HIP(hipFuncSetAttribute((const void*)k_multisplit<true, NT, K>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-        hipLaunchKernelGGL(k_multisplit<true>, dim3(grid_1d(blocks)), dim3(kMsNT), lds, st, g,
-                           in_col, in_val, pos_of, (unsigned long long*)cursor, out_col, out_val,
-                           epb, nr_max);
+        hipLaunchKernelGGL((k_multisplit<true, NT, K>), dim3(grid_1d(blocks)), dim3(NT), lds, st,
+                           g, in_col, in_val, pos_of, (unsigned long long*)cursor, out_col,
+                           out_val, tile_r0, epb, nr_max);
     } else {
-        SG_HIP(hipFuncSetAttribute((const void*)k_multisplit<false>,
+        SG_HIP(hipFuncSetAttribute((const void*)k_multisplit<false, NT, K>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-        hipLaunchKernelGGL(k_multisplit<false>, dim3(grid_1d(blocks)), dim3(kMsNT), lds, st, g,
-                           in_col, in_val, pos_of, (unsigned long long*)cursor, out_col,
-                           (double*)nullptr, epb, nr_max);
+        hipLaunchKernelGGL((k_multisplit<false, NT, K>), dim3(grid_1d(blocks)), dim3(NT), lds, st,
+                           g, in_col, in_val, pos_of, (unsigned long long*)cursor, out_col,
+                           (double*)nullptr, tile_r0, epb, nr_max);
     }
     SG_LAUNCH_CHECK();
+}
+
+// 256 threads x 8 elements (2048 per group, about 25 KiB of LDS with values)
+// measured fastest on MI355X among 128..1024 threads x 4..16 elements.
+constexpr int kMsNT = 256;
+constexpr int kMsK = 8;
+
+void multisplit(const LevelGeom& g, const int32_t* in_col, const double* in_val,
+                const int32_t* pos_of, int64_t* cursor, int32_t* out_col, double* out_val,
+                Arena& ar, hipStream_t st) {
+    if (g.total <= 0) return;
+    ms_launch<kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, out_val, ar, st);
 }
 
 // ---------------------------------------------------------------- fused symbolic
@@ -486,6 +597,7 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     const int64_t h = blockIdx.x;
     for (int i = tt; i < nwords; i += kHsymNT) bits[i] = 0u;
     for (int i = tt; i < req; i += kHsymNT) dsl[i] = 0;
+    __syncthreads();
     const int32_t r = hrows[h];
     const int64_t a0 = arp[r], a1 = arp[r + 1];
     for (int64_t ew = a0; ew < a1; ew += kHsymEW) {
@@ -504,14 +616,23 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
         if (tt < ne) ppre[tt] = pre;
         if (tt == 0) ppre[ne] = tot;
         __syncthreads();
+        constexpr int U = 8;  // pieces in flight per wave
         int j = 0;
-        for (int piece = w; piece < tot; piece += NW) {
-            while (ppre[j + 1] <= piece) ++j;
-            int off = (piece - ppre[j]) * kWave + lane;
-            if (off < nbv[j]) {
-                uint32_t c = (uint32_t)bcol[bst[j] + off];
-                atomicOr(&bits[c >> 5], 1u << (c & 31));
+        for (int piece = w; piece < tot; piece += NW * U) {
+            uint32_t c[U];
+#pragma unroll
+            for (int uu = 0; uu < U; ++uu) {
+                const int pu = piece + uu * NW;
+                c[uu] = 0xffffffffu;
+                if (pu < tot) {
+                    while (ppre[j + 1] <= pu) ++j;
+                    const int off = (pu - ppre[j]) * kWave + lane;
+                    if (off < nbv[j]) c[uu] = (uint32_t)bcol[bst[j] + off];
+                }
             }
+#pragma unroll
+            for (int uu = 0; uu < U; ++uu)
+                if (c[uu] != 0xffffffffu) atomicOr(&bits[c[uu] >> 5], 1u << (c[uu] & 31));
         }
         __syncthreads();
     }

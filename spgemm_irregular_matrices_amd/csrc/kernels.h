@@ -75,11 +75,14 @@ void heavy_rowptr(const DevCSR& A, const int64_t* S, const int32_t* hrows, int64
 
 // Masked CSR-to-CSC of A[heavy rows, :], keeping only entries whose B row
 // is nonempty. ent_k = column of A (the slice), ent_q = A entry index,
-// ent_dest = position in C-hat of the entry's first product; P = flattened
-// slice offsets (exclusive scan of nnz(B[ent_k,:])). Returns the entry count.
+// ent_dest = position in C-hat of the entry's first product; P = exclusive
+// scan of the entries' piece counts ceil(nnz(B[ent_k,:]) / 64), the
+// flattened slice offsets in units of 64-product pieces. Returns the entry
+// count.
 int64_t masked_csr2csc(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
                        int64_t H, const int64_t* chat_rp, int32_t** ent_k, int64_t** ent_q,
-                       int64_t** ent_dest, int64_t** P, Arena& ar, hipStream_t st);
+                       int64_t** ent_dest, int64_t** P, int64_t* total_pieces, Arena& ar,
+                       hipStream_t st);
 
 struct ExpandArgs {
     const int32_t* ent_k;
@@ -93,10 +96,16 @@ struct ExpandArgs {
     const double* Bval;
     int32_t* out_col;
     double* out_val;  // null: columns only
+    int64_t total_pieces;    // P[ne]
+    const int64_t* tile_e0;  // first entry of every tile (expand_tile_starts)
 };
+// Number of expand tiles, and their first entries (cached between calls).
+int64_t expand_tiles(int64_t total_pieces);
+void expand_tile_starts(const int64_t* P, int64_t ne, int64_t total_pieces, int64_t* tile_e0,
+                        hipStream_t st);
 // OuterProduct (Algorithm 4): every (a, B-row) pair of every slice written
-// to its C-hat position. Returns the number of launches (1).
-void expand(const ExpandArgs& a, int64_t total, hipStream_t st);
+// to its C-hat position.
+void expand(const ExpandArgs& a, hipStream_t st);
 
 struct LevelGeom {
     const int64_t* rp;  // input row pointers, nrows+1
@@ -108,7 +117,8 @@ struct LevelGeom {
 };
 
 // Histogram (Section III-C): counts[r*nch + c] += elements of row r in chunk c.
-void histogram(const LevelGeom& g, const int32_t* in_col, int64_t* counts, hipStream_t st);
+void histogram(const LevelGeom& g, const int32_t* in_col, int64_t* counts, Arena& ar,
+               hipStream_t st);
 
 // Classify the level's chunks and partition them (CB_* order). inv[pos] =
 // natural chunk index, pos_of[natural] = pos. bin_start has CB_COUNT+1.
@@ -124,7 +134,7 @@ void reord_rowptr(const int64_t* counts, const int32_t* inv, int64_t npos, int64
 // cursor[pos] starts at rp_out[pos] and is advanced by reservations.
 void multisplit(const LevelGeom& g, const int32_t* in_col, const double* in_val,
                 const int32_t* pos_of, int64_t* cursor, int32_t* out_col, double* out_val,
-                hipStream_t st);
+                Arena& ar, hipStream_t st);
 
 // Fused symbolic pass over the heavy rows (one work group per row): per
 // finest chunk slot of width wfin, the element count and the number of

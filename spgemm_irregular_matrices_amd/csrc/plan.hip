@@ -62,7 +62,7 @@ struct spgemm_plan_s {
     int64_t An = 0, Am = 0, Annz = 0, Bn = 0, Bm = 0, Bnnz = 0, Cnnz = 0;
     Params prm;
     int64_t row_bins[RB_COUNT + 1] = {};
-    int64_t H = 0, Nh = 0, ne = 0;
+    int64_t H = 0, Nh = 0, ne = 0, npieces = 0;
     int L = 0;
     LevelState lv[kMaxLevels];
     spgemm_stats stats{};
@@ -233,9 +233,10 @@ void heavy_symbolic_multisplit(spgemm_plan p, const DevCSR& A, const DevCSR& B,
     int32_t* buf0c = ar.get<int32_t>("buf0c", (size_t)p->Nh);
     {
         ExpandArgs ea{ent_k, ent_q, ent_dest, P, p->ne, A.val, B.rp, B.col, B.val, buf0c,
-                      nullptr};
+                      nullptr, p->npieces,
+                      ar.get<int64_t>("expand_tiles", (size_t)expand_tiles(p->npieces) + 1)};
         PhaseScope ps(p, 0, SPGEMM_PHASE_OUTER_PROD, st);
-        expand(ea, p->Nh, st);
+        expand(ea, st);
         add_bytes(p, 0, SPGEMM_PHASE_OUTER_PROD, 4.0 * p->Nh + 20.0 * p->ne);
     }
     if (p->opt.debug_dump) debug_copy_chat(p, chat_rp, buf0c, nullptr, hrows, st);
@@ -274,7 +275,7 @@ void heavy_symbolic_multisplit(spgemm_plan p, const DevCSR& A, const DevCSR& B,
             {
                 PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
                 fill<int64_t>(counts, S_l.nnat, 0, st);
-                histogram(g, bufc[l & 1], counts, st);
+                histogram(g, bufc[l & 1], counts, ar, st);
                 classify_chunks(counts, S_l.nnat, q.tau, last, inv, pos, bins, ar, st);
                 add_bytes(p, 0, SPGEMM_PHASE_HISTO,
                           4.0 * total + 8.0 * (R + 1) + 8.0 * S_l.nnat);
@@ -292,7 +293,7 @@ void heavy_symbolic_multisplit(spgemm_plan p, const DevCSR& A, const DevCSR& B,
             int32_t* out = bufc[(l + 1) & 1];
             {
                 PhaseScope ps(p, 0, SPGEMM_PHASE_MULTISPLIT, st);
-                multisplit(g, bufc[l & 1], nullptr, pos, cursor, out, nullptr, st);
+                multisplit(g, bufc[l & 1], nullptr, pos, cursor, out, nullptr, ar, st);
                 add_bytes(p, 0, SPGEMM_PHASE_MULTISPLIT, 8.0 * total + 8.0 * (R + 1));
             }
             if (p->opt.debug_dump) debug_copy_level(p, l, rp, S_l.npos, out, nullptr, inv, st);
@@ -516,7 +517,10 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             PhaseScope ps(p, 0, SPGEMM_PHASE_CSR_TO_CSC, st);
             heavy_rowptr(A, S, hrows, p->H, chat_rp, ar, st);
             p->ne = masked_csr2csc(A, B, S, hrows, p->H, chat_rp, &ent_k, &ent_q, &ent_dest, &P,
-                                   ar, st);
+                                   &p->npieces, ar, st);
+            expand_tile_starts(P, p->ne, p->npieces,
+                               ar.get<int64_t>("expand_tiles", (size_t)expand_tiles(p->npieces) + 1),
+                               st);
             add_bytes(p, 0, SPGEMM_PHASE_CSR_TO_CSC, 36.0 * p->ne);
         }
         p->stats.chat_bytes = 12 * p->Nh + 8 * (p->H + 1);
@@ -615,9 +619,10 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
     double* bufv[2] = {ar.get<double>("buf0v", (size_t)p->Nh), nullptr};
     {
         ExpandArgs ea{ent_k, ent_q, ent_dest, P, p->ne, A.val, B.rp, B.col, B.val, bufc[0],
-                      bufv[0]};
+                      bufv[0], p->npieces,
+                      ar.get<int64_t>("expand_tiles", (size_t)expand_tiles(p->npieces) + 1)};
         PhaseScope ps(p, 1, SPGEMM_PHASE_OUTER_PROD, st);
-        expand(ea, p->Nh, st);
+        expand(ea, st);
         add_bytes(p, 1, SPGEMM_PHASE_OUTER_PROD, 12.0 * p->Nh + 28.0 * p->ne);
     }
     if (p->opt.debug_dump) debug_copy_chat(p, chat_rp, bufc[0], bufv[0], hrows, st);
@@ -653,7 +658,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         const int in = l & 1, outb = (l + 1) & 1;
         {
             PhaseScope ps(p, 1, SPGEMM_PHASE_MULTISPLIT, st);
-            multisplit(g, bufc[in], bufv[in], pos, cursor, bufc[outb], bufv[outb], st);
+            multisplit(g, bufc[in], bufv[in], pos, cursor, bufc[outb], bufv[outb], ar, st);
             add_bytes(p, 1, SPGEMM_PHASE_MULTISPLIT, 24.0 * S_l.total_in + 8.0 * (S_l.R + 1));
         }
         if (p->opt.debug_dump) debug_copy_level(p, l, rp, S_l.npos, bufc[outb], bufv[outb], inv, st);

@@ -115,6 +115,22 @@ void scan_exclusive(F f, int64_t n, int64_t* out, Arena& ar, hipStream_t st, int
     SG_LAUNCH_CHECK();
 }
 
+// ---------------------------------------------------------------- tile starts
+// out[g] = largest j in [0, n) with a[j] <= g*step, for g in [0, ntiles): the
+// first row (or entry) of every static tile of a flattened range. One
+// independent search per thread, so the search latency is paid in parallel
+// instead of at the start of every tile.
+__global__ void k_tile_starts(const int64_t* a, int64_t n, int64_t step, int64_t ntiles,
+                              int64_t* out);
+
+inline void tile_starts(const int64_t* a, int64_t n, int64_t step, int64_t ntiles, int64_t* out,
+                        hipStream_t st) {
+    if (ntiles <= 0) return;
+    hipLaunchKernelGGL(k_tile_starts, dim3(grid_1d(ceil_div(ntiles, 256))), dim3(256), 0, st, a, n,
+                       step, ntiles, out);
+    SG_LAUNCH_CHECK();
+}
+
 // ---------------------------------------------------------------- partition
 // Stable partition of items [0, n) into bins 0..nb-1 (bin order, then item
 // order). perm[pos] = item, pos_of[item] = pos (pos_of may be null),

@@ -13,6 +13,12 @@ __global__ void k_part_bin_starts(const int64_t* offs, int nb, int64_t nblocks, 
     if (b == nb) bin_start[nb] = n;
 }
 
+__global__ void k_tile_starts(const int64_t* a, int64_t n, int64_t step, int64_t ntiles,
+                              int64_t* out) {
+    int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g < ntiles) out[g] = upper_index(a, int64_t(0), n, g * step);
+}
+
 // ---------------------------------------------------------------- validation
 __global__ void k_validate_rowptr(const int64_t* rp, int64_t n, int64_t nnz, int* flag) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
