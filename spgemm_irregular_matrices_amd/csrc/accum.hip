@@ -252,6 +252,7 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
     double* vals = (double*)lds_r;                                // TW*KPT (NUM)
     uint32_t* bits = (uint32_t*)(vals + (NUM ? TW * KPT : 0));    // NWD
     int* wpre = (int*)(bits + NWD);                               // NWD (NUM)
+    int32_t* scol = (int32_t*)(wpre + NWD);                       // TW*KPT (NUM)
     __shared__ int red_sh[TW / kWave + 1];
     __shared__ int32_t lo_sh;
     const int tt = threadIdx.x;
@@ -303,23 +304,21 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
                 atomicAdd(&vals[rank], v[k]);
             }
         }
+        // the column of every rank, scattered into LDS from the bitmap words
+        // (each thread walks the set bits of its own words), then streamed out
+        for (int w = w0; w < w1; ++w) {
+            uint32_t x = bits[w];
+            int r = wpre[w];
+            while (x) {
+                const int b = __ffs(x) - 1;
+                x &= x - 1;
+                scol[r++] = lo + w * 32 + b;
+            }
+        }
         __syncthreads();
         const int64_t off = ci.off[out];
         for (int r = tt; r < tot; r += TW) {
-            int w = (int)upper_index(wpre, int64_t(0), int64_t(NWD), r);
-            int j = r - wpre[w];
-            uint32_t x = bits[w];
-            int pos = 0;
-#pragma unroll
-            for (int sh = 16; sh > 0; sh >>= 1) {
-                int c = __popc(x & ((1u << sh) - 1u));
-                if (j >= c) {
-                    j -= c;
-                    x >>= sh;
-                    pos += sh;
-                }
-            }
-            ci.Ccol[off + r] = lo + w * 32 + pos;
+            ci.Ccol[off + r] = scol[r];
             ci.Cval[off + r] = vals[r];
         }
     }
@@ -435,7 +434,7 @@ static void launch_hash(const RowItems& ri, const ChunkItems& ci, int64_t p0, in
 template <bool NUM, int TW, int KPT>
 static void launch_rank(const ChunkItems& ci, int64_t p0, int64_t n, hipStream_t st) {
     const int64_t W = ci.width;
-    size_t lds = (NUM ? (size_t)TW * KPT * 8 : 0) + (size_t)(W / 32) * 4 * (NUM ? 2 : 1);
+    size_t lds = (NUM ? (size_t)TW * KPT * 12 : 0) + (size_t)(W / 32) * 4 * (NUM ? 2 : 1);
     auto kern = k_acc_rank<NUM, TW, KPT>;
     SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds));

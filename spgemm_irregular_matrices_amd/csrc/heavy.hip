@@ -46,14 +46,14 @@ __global__ __launch_bounds__(256) void k_csc_count(const int64_t* arp, const int
 __global__ __launch_bounds__(256) void k_csc_fill(const int64_t* arp, const int32_t* acol,
                                                   const int64_t* brp, const int32_t* hrows,
                                                   int64_t H, const int64_t* S,
-                                                  const int64_t* chat_rp,
+                                                  const int64_t* chat_rp, int64_t dest_base,
                                                   unsigned long long* cursor, int32_t* ent_k,
                                                   int64_t* ent_q, int64_t* ent_dest) {
     int64_t h = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
     if (h >= H) return;
     int32_t r = hrows[h];
     int64_t a0 = arp[r];
-    int64_t base = chat_rp[h] - S[a0];
+    int64_t base = chat_rp[h] - dest_base - S[a0];
     for (int64_t q = a0 + lane_id(); q < arp[r + 1]; q += kWave) {
         int32_t k = acol[q];
         if (brp[k + 1] > brp[k]) {
@@ -80,9 +80,9 @@ struct SlicePieces {
 };
 
 int64_t masked_csr2csc(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
-                       int64_t H, const int64_t* chat_rp, int32_t** ent_k, int64_t** ent_q,
-                       int64_t** ent_dest, int64_t** P, int64_t* total_pieces, Arena& ar,
-                       hipStream_t st) {
+                       int64_t H, const int64_t* chat_rp, int64_t dest_base, int32_t* ent_k,
+                       int64_t* ent_q, int64_t* ent_dest, int64_t ent_capacity, int64_t* P,
+                       int64_t* total_pieces, Arena& ar, hipStream_t st) {
     int32_t* colcnt = ar.get<int32_t>("csc_colcnt", (size_t)A.m + 1);
     int64_t* colptr = ar.get<int64_t>("csc_colptr", (size_t)A.m + 1);
     fill<int32_t>(colcnt, A.m, 0, st);
@@ -94,19 +94,29 @@ int64_t masked_csr2csc(const DevCSR& A, const DevCSR& B, const int64_t* S, const
     int64_t ne = 0;
     SG_HIP(hipMemcpyAsync(&ne, colptr + A.m, sizeof(int64_t), hipMemcpyDeviceToHost, st));
     SG_HIP(hipStreamSynchronize(st));
-    *ent_k = ar.get<int32_t>("csc_ent_k", (size_t)ne);
-    *ent_q = ar.get<int64_t>("csc_ent_q", (size_t)ne);
-    *ent_dest = ar.get<int64_t>("csc_ent_dest", (size_t)ne);
-    *P = ar.get<int64_t>("csc_slice_off", (size_t)ne + 1);
+    if (ne > ent_capacity) throw std::logic_error("CSC entry capacity exceeded");
     unsigned long long* cursor = ar.get<unsigned long long>("csc_cursor", (size_t)A.m + 1);
     copy<int64_t>((int64_t*)cursor, colptr, A.m, st);
     hipLaunchKernelGGL(k_csc_fill, dim3(grid_1d(blocks)), dim3(256), 0, st, A.rp, A.col, B.rp,
-                       hrows, H, S, chat_rp, cursor, *ent_k, *ent_q, *ent_dest);
+                       hrows, H, S, chat_rp, dest_base, cursor, ent_k, ent_q, ent_dest);
     SG_LAUNCH_CHECK();
-    scan_exclusive(SlicePieces{*ent_k, B.rp}, ne, *P, ar, st);
-    SG_HIP(hipMemcpyAsync(total_pieces, *P + ne, sizeof(int64_t), hipMemcpyDeviceToHost, st));
+    scan_exclusive(SlicePieces{ent_k, B.rp}, ne, P, ar, st);
+    SG_HIP(hipMemcpyAsync(total_pieces, P + ne, sizeof(int64_t), hipMemcpyDeviceToHost, st));
     SG_HIP(hipStreamSynchronize(st));
     return ne;
+}
+
+// C-hat row pointers of one batch, relative to the batch's first element.
+__global__ void k_sub_base(const int64_t* a, int64_t n, int64_t base, int64_t* out) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = a[i] - base;
+}
+
+void rebase(const int64_t* a, int64_t n, int64_t base, int64_t* out, hipStream_t st) {
+    if (n <= 0) return;
+    hipLaunchKernelGGL(k_sub_base, dim3(grid_1d(ceil_div(n, 256))), dim3(256), 0, st, a, n, base,
+                       out);
+    SG_LAUNCH_CHECK();
 }
 
 // ---------------------------------------------------------------- outer product

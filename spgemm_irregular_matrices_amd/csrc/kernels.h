@@ -73,16 +73,20 @@ void classify_rows(const DevCSR& A, const int64_t* S, const int32_t* bmin, const
 void heavy_rowptr(const DevCSR& A, const int64_t* S, const int32_t* hrows, int64_t H,
                   int64_t* chat_rp, Arena& ar, hipStream_t st);
 
-// Masked CSR-to-CSC of A[heavy rows, :], keeping only entries whose B row
-// is nonempty. ent_k = column of A (the slice), ent_q = A entry index,
-// ent_dest = position in C-hat of the entry's first product; P = exclusive
-// scan of the entries' piece counts ceil(nnz(B[ent_k,:]) / 64), the
-// flattened slice offsets in units of 64-product pieces. Returns the entry
-// count.
+// Masked CSR-to-CSC of A[heavy rows, :] for the heavy rows hrows[0..H) of
+// one batch, keeping only entries whose B row is nonempty. ent_k = column of
+// A (the slice), ent_q = A entry index, ent_dest = position, relative to
+// dest_base, of the entry's first product in C-hat (chat_rp holds the
+// batch's C-hat row starts); P = exclusive scan of the entries' piece counts
+// ceil(nnz(B[ent_k,:]) / 64), the flattened slice offsets in units of
+// 64-product pieces. Outputs go to caller buffers of ent_capacity entries
+// (P: one more). Returns the entry count.
 int64_t masked_csr2csc(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
-                       int64_t H, const int64_t* chat_rp, int32_t** ent_k, int64_t** ent_q,
-                       int64_t** ent_dest, int64_t** P, int64_t* total_pieces, Arena& ar,
-                       hipStream_t st);
+                       int64_t H, const int64_t* chat_rp, int64_t dest_base, int32_t* ent_k,
+                       int64_t* ent_q, int64_t* ent_dest, int64_t ent_capacity, int64_t* P,
+                       int64_t* total_pieces, Arena& ar, hipStream_t st);
+// out[i] = a[i] - base for i < n.
+void rebase(const int64_t* a, int64_t n, int64_t base, int64_t* out, hipStream_t st);
 
 struct ExpandArgs {
     const int32_t* ent_k;

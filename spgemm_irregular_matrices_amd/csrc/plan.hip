@@ -1,11 +1,16 @@
 // Host orchestration and the C ABI (include/spgemm.h).
 //
 // spgemm_symbolic runs Algorithm 3 of the gMAGNUS page up to the prefix sum
-// of C.rowPtr (lines 1-25) with columns only; spgemm_numeric reruns the
-// heavy path with values and accumulates (lines 26-27). The structure the
-// symbolic pass finds (row bins, C-hat and C-hat-reord row pointers, chunk
-// partitions and chunk output offsets) is kept in the plan, so the numeric
+// of C.rowPtr (lines 1-25); spgemm_numeric runs the heavy path with values
+// and accumulates (lines 26-27). The structure the symbolic pass finds (row
+// bins, the masked CSC, every level's chunk partition, C-hat-reord row
+// pointers and chunk output offsets) is kept in the plan, so the numeric
 // pass does no histogramming, partitioning or blocking host reads.
+//
+// Heavy rows are processed in batches of consecutive heavy rows whose
+// intermediate products fit a budget (max_batch_products; one batch by
+// default). Each batch has its own masked CSC, C-hat, levels and chunk
+// partitions, so C-hat and C-hat-reord need buffers of one batch's size.
 #include <string.h>
 
 #include <algorithm>
@@ -37,6 +42,10 @@ struct Params {
     int hash_top_logS = 13;  // slots of the largest light hash table (log2)
 };
 
+// One multisplit level of one batch. Natural chunk indices of the level are
+// local to the batch (parent * nch + chunk); the level's arrays hold every
+// batch, the batch's part starting at nat_off (and its C-hat-reord row
+// pointers at rp_off).
 struct LevelState {
     int64_t R = 0;         // input rows (C-hat rows or the previous level's heavy chunks)
     int64_t total_in = 0;  // input elements
@@ -45,8 +54,24 @@ struct LevelState {
     int64_t nnat = 0;      // R * nch
     int64_t npos = 0;      // nonempty chunks
     int64_t bins[CB_COUNT + 1] = {};
-    int in_buf = 0;        // which double buffer holds the input
     int64_t final_elems = 0;  // elements of this level's accumulated (non-split) chunks
+    int64_t nat_off = 0;
+    int64_t rp_off = 0;
+    int64_t nheavy() const { return bins[CB_NEXT + 1] - bins[CB_NEXT]; }
+};
+
+// A run of consecutive heavy rows [h0, h1) processed together.
+struct BatchState {
+    int64_t h0 = 0, h1 = 0;
+    int64_t N = 0;          // intermediate products (C-hat elements)
+    int64_t chat_base = 0;  // C-hat offset of the batch's first row
+    int64_t ent0 = 0, ne = 0;   // masked CSC entries
+    int64_t P0 = 0;             // offset of the batch's piece prefix (ne + 1 values)
+    int64_t npieces = 0;
+    int64_t tile0 = 0;          // offset of the batch's expand tile starts
+    int64_t crp0 = 0;           // offset of the batch's rebased C-hat row pointers (R + 1)
+    int L = 0;
+    LevelState lv[kMaxLevels];
 };
 
 }  // namespace
@@ -62,9 +87,12 @@ struct spgemm_plan_s {
     int64_t An = 0, Am = 0, Annz = 0, Bn = 0, Bm = 0, Bnnz = 0, Cnnz = 0;
     Params prm;
     int64_t row_bins[RB_COUNT + 1] = {};
-    int64_t H = 0, Nh = 0, ne = 0, npieces = 0;
-    int L = 0;
-    LevelState lv[kMaxLevels];
+    int64_t H = 0, Nh = 0;
+    int L = 0;  // deepest level used by any batch
+    std::vector<BatchState> batches;
+    int64_t maxN = 0;                         // largest batch (C-hat buffer size)
+    int64_t cap_nat[kMaxLevels] = {}, cap_rp[kMaxLevels] = {};
+    int64_t cap_ent = 0, cap_P = 0, cap_tiles = 0, cap_crp = 0;
     spgemm_stats stats{};
     // timing
     struct Ev {
@@ -74,11 +102,10 @@ struct spgemm_plan_s {
     std::vector<hipEvent_t> evpool;
     size_t evnext = 0;
     std::vector<Ev> evs;
-    // debug dumps
     bool fused_sym = false;
+    // debug dumps (kept for single-batch products)
     bool dbg_valid = false;
     bool dbg_has_val = false;
-    int dbg_levels = 0;
 };
 
 namespace {
@@ -211,222 +238,327 @@ int check_csr(const spgemm_csr* M, bool need_val) {
 
 std::string lvname(const char* what, int l) { return std::string("lv") + std::to_string(l) + what; }
 
-void debug_copy_chat(spgemm_plan p, const int64_t* chat_rp, const int32_t* col, const double* val,
-                     const int32_t* hrows, hipStream_t st);
-void debug_copy_level(spgemm_plan p, int l, const int64_t* rp, int64_t npos, const int32_t* col,
-                      const double* val, const int32_t* inv, hipStream_t st);
+// A level's array of natural-chunk values (every batch), or of row pointers.
+template <class T>
+T* lvarr(spgemm_plan p, int l, const char* what, bool rowptrs = false) {
+    const int64_t cap = rowptrs ? p->cap_rp[l] : p->cap_nat[l];
+    return p->ar.get<T>(lvname(what, l), (size_t)cap + 1);
+}
 
 __global__ void k_i32_to_i64(const int32_t* a, int64_t n, int64_t* b) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) b[i] = a[i];
 }
 
-// Symbolic pass of the heavy rows the way Algorithm 3 lays it out: expand
-// C-hat (columns only), then per level Histogram, ThreshPartition and
-// Multisplit, and count distinct columns of every final chunk.
-void heavy_symbolic_multisplit(spgemm_plan p, const DevCSR& A, const DevCSR& B,
-                               const int64_t* chat_rp, const int32_t* ent_k, const int64_t* ent_q,
-                               const int64_t* ent_dest, const int64_t* P, const int32_t* hrows,
-                               int64_t* cnt_row, hipStream_t st) {
+void debug_copy_chat(spgemm_plan p, const BatchState& bt, const int64_t* crp, const int32_t* col,
+                     const double* val, const int32_t* hrows, hipStream_t st) {
+    Arena& ar = p->ar;
+    const int64_t R = bt.h1 - bt.h0;
+    copy<int64_t>(ar.get<int64_t>("dbg_m1_rp", (size_t)R + 1), crp, R + 1, st);
+    copy<int32_t>(ar.get<int32_t>("dbg_m1_col", (size_t)bt.N), col, bt.N, st);
+    if (val) copy<double>(ar.get<double>("dbg_m1_val", (size_t)bt.N), val, bt.N, st);
+    int64_t* key = ar.get<int64_t>("dbg_m1_key", (size_t)R + 1);
+    hipLaunchKernelGGL(k_i32_to_i64, dim3(grid_1d(ceil_div(R, 256))), dim3(256), 0, st, hrows, R,
+                       key);
+    SG_LAUNCH_CHECK();
+    p->dbg_valid = true;
+    p->dbg_has_val = val != nullptr;
+}
+
+void debug_copy_level(spgemm_plan p, int l, const LevelState& S_l, const int64_t* rp,
+                      const int32_t* col, const double* val, const int32_t* inv, hipStream_t st) {
+    Arena& ar = p->ar;
+    int64_t nnz = d2h(p, rp + S_l.npos, 1, st)[0];
+    std::string b = "dbg_l" + std::to_string(l);
+    copy<int64_t>(ar.get<int64_t>(b + "_rp", (size_t)S_l.npos + 1), rp, S_l.npos + 1, st);
+    copy<int32_t>(ar.get<int32_t>(b + "_col", (size_t)nnz), col, nnz, st);
+    if (val) copy<double>(ar.get<double>(b + "_val", (size_t)nnz), val, nnz, st);
+    int64_t* key = ar.get<int64_t>(b + "_key", (size_t)S_l.npos + 1);
+    if (S_l.npos > 0) {
+        hipLaunchKernelGGL(k_i32_to_i64, dim3(grid_1d(ceil_div(S_l.npos, 256))), dim3(256), 0, st,
+                           inv, S_l.npos, key);
+        SG_LAUNCH_CHECK();
+    }
+}
+
+// ---------------------------------------------------------------- batches
+// Consecutive heavy rows whose products fit max_batch_products (a row larger
+// than the budget is a batch of its own); one batch when there is no budget.
+void plan_batches(spgemm_plan p, const int64_t* chat_rp, hipStream_t st) {
+    p->batches.clear();
+    const int64_t budget = p->opt.max_batch_products;
+    if (budget <= 0 || p->Nh <= budget) {
+        BatchState b;
+        b.h0 = 0;
+        b.h1 = p->H;
+        b.N = p->Nh;
+        p->batches.push_back(b);
+    } else {
+        std::vector<int64_t> h((size_t)p->H + 1);
+        SG_HIP(hipMemcpyAsync(h.data(), chat_rp, h.size() * sizeof(int64_t),
+                              hipMemcpyDeviceToHost, st));
+        SG_HIP(hipStreamSynchronize(st));
+        int64_t h0 = 0;
+        while (h0 < p->H) {
+            int64_t h1 = h0 + 1;
+            while (h1 < p->H && h[h1 + 1] - h[h0] <= budget) ++h1;
+            BatchState b;
+            b.h0 = h0;
+            b.h1 = h1;
+            b.N = h[h1] - h[h0];
+            b.chat_base = h[h0];
+            p->batches.push_back(b);
+            h0 = h1;
+        }
+    }
+    p->maxN = 0;
+    for (auto& b : p->batches) p->maxN = std::max(p->maxN, b.N);
+}
+
+// Upper bounds of the arrays that hold every batch: a batch's level-l input
+// rows (l >= 1) each hold more than tau elements, so their number is at
+// most N_b / (tau + 1).
+void plan_capacities(spgemm_plan p, const DevCSR& A) {
+    const Params& q = p->prm;
+    const int64_t nb = (int64_t)p->batches.size();
+    for (int l = 0; l < kMaxLevels; ++l) p->cap_nat[l] = p->cap_rp[l] = 0;
+    for (int l = 0; l < q.nlevels; ++l) {
+        const int64_t rows = l == 0 ? p->H : p->Nh / (q.tau + 1);
+        p->cap_nat[l] = rows * q.vchunks[l];
+        p->cap_rp[l] = p->cap_nat[l] + nb;
+        if (p->cap_nat[l] >= (int64_t(1) << 31)) throw OverflowError("too many chunks in a level");
+    }
+    p->cap_ent = A.nnz;
+    p->cap_P = A.nnz + nb;
+    p->cap_tiles = (A.nnz + p->Nh / 64 + nb) / 128 + 2 * nb + 2;
+    p->cap_crp = p->H + nb;
+}
+
+struct CscBufs {
+    int32_t* ent_k;
+    int64_t* ent_q;
+    int64_t* ent_dest;
+    int64_t* P;
+    int64_t* tiles;
+    int64_t* crp;
+};
+
+CscBufs csc_bufs(spgemm_plan p) {
+    Arena& ar = p->ar;
+    return {ar.get<int32_t>("csc_ent_k", (size_t)p->cap_ent + 1),
+            ar.get<int64_t>("csc_ent_q", (size_t)p->cap_ent + 1),
+            ar.get<int64_t>("csc_ent_dest", (size_t)p->cap_ent + 1),
+            ar.get<int64_t>("csc_slice_off", (size_t)p->cap_P + 1),
+            ar.get<int64_t>("expand_tiles", (size_t)p->cap_tiles + 1),
+            ar.get<int64_t>("chat_rp_local", (size_t)p->cap_crp + 1)};
+}
+
+ExpandArgs expand_args(spgemm_plan p, const BatchState& bt, const DevCSR& A, const DevCSR& B,
+                       int32_t* out_col, double* out_val) {
+    CscBufs c = csc_bufs(p);
+    return ExpandArgs{c.ent_k + bt.ent0, c.ent_q + bt.ent0, c.ent_dest + bt.ent0, c.P + bt.P0,
+                      bt.ne, A.val, B.rp, B.col, B.val, out_col, out_val, bt.npieces,
+                      c.tiles + bt.tile0};
+}
+
+// ---------------------------------------------------------------- symbolic, heavy rows
+// Symbolic pass of one batch the way Algorithm 3 lays it out: expand C-hat
+// (columns only), then per level Histogram, ThreshPartition and Multisplit,
+// and count distinct columns of every final chunk.
+void symbolic_batch_multisplit(spgemm_plan p, BatchState& bt, const DevCSR& A, const DevCSR& B,
+                               const int32_t* hrows, int64_t* cnt_row, int64_t* nat_cur,
+                               int64_t* rp_cur, hipStream_t st) {
     Arena& ar = p->ar;
     const Params& q = p->prm;
-    int32_t* buf0c = ar.get<int32_t>("buf0c", (size_t)p->Nh);
+    const int64_t R0 = bt.h1 - bt.h0;
+    CscBufs c = csc_bufs(p);
+    int32_t* buf0c = ar.get<int32_t>("buf0c", (size_t)p->maxN);
     {
-        ExpandArgs ea{ent_k, ent_q, ent_dest, P, p->ne, A.val, B.rp, B.col, B.val, buf0c,
-                      nullptr, p->npieces,
-                      ar.get<int64_t>("expand_tiles", (size_t)expand_tiles(p->npieces) + 1)};
         PhaseScope ps(p, 0, SPGEMM_PHASE_OUTER_PROD, st);
-        expand(ea, st);
-        add_bytes(p, 0, SPGEMM_PHASE_OUTER_PROD, 4.0 * p->Nh + 20.0 * p->ne);
+        expand(expand_args(p, bt, A, B, buf0c, nullptr), st);
+        add_bytes(p, 0, SPGEMM_PHASE_OUTER_PROD, 4.0 * bt.N + 20.0 * bt.ne);
     }
-    if (p->opt.debug_dump) debug_copy_chat(p, chat_rp, buf0c, nullptr, hrows, st);
-
+    const bool dump = p->opt.debug_dump && p->batches.size() == 1;
+    if (dump) debug_copy_chat(p, bt, c.crp + bt.crp0, buf0c, nullptr, hrows + bt.h0, st);
     if (q.nlevels == 0) {
         ChunkItems ci{};
-            ci.hash_top_logS = p->prm.hash_top_logS;
-        ci.rp = chat_rp;
-        ci.map = hrows;
+        ci.hash_top_logS = q.hash_top_logS;
+        ci.rp = c.crp + bt.crp0;
+        ci.map = hrows + bt.h0;
         ci.bcol = buf0c;
         ci.cnt = cnt_row;
         ci.width = q.final_width;
         PhaseScope ps(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, st);
-        accumulate_chunks(ci, CB_DENSE, 0, p->H, false, st);
-        add_bytes(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, 4.0 * p->Nh);
-    } else {
-        int32_t* bufc[2] = {buf0c, ar.get<int32_t>("buf1c", (size_t)p->Nh)};
-        const int64_t* rp_in = chat_rp;
-        int64_t R = p->H, total = p->Nh;
-        int L = 0;
-        for (int l = 0; l < q.nlevels; ++l) {
-            const bool last = (l == q.nlevels - 1);
-            LevelState& S_l = p->lv[l];
-            S_l.R = R;
-            S_l.total_in = total;
-            S_l.nch = q.vchunks[l];
-            S_l.shift = ilog2(q.width[l]);
-            S_l.nnat = R * S_l.nch;
-            S_l.in_buf = l & 1;
-            if (S_l.nnat >= (int64_t(1) << 31)) throw OverflowError("too many chunks in a level");
-            int64_t* counts = ar.get<int64_t>(lvname("_counts", l), (size_t)S_l.nnat);
-            int32_t* inv = ar.get<int32_t>(lvname("_inv", l), (size_t)S_l.nnat);
-            int32_t* pos = ar.get<int32_t>(lvname("_pos", l), (size_t)S_l.nnat);
-            int64_t* bins = ar.get<int64_t>(lvname("_bins", l), CB_COUNT + 1);
-            LevelGeom g{rp_in, R, total, S_l.shift, S_l.nch, q.tau};
-            {
-                PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
-                fill<int64_t>(counts, S_l.nnat, 0, st);
-                histogram(g, bufc[l & 1], counts, ar, st);
-                classify_chunks(counts, S_l.nnat, q.tau, last, inv, pos, bins, ar, st);
-                add_bytes(p, 0, SPGEMM_PHASE_HISTO,
-                          4.0 * total + 8.0 * (R + 1) + 8.0 * S_l.nnat);
-            }
-            int64_t* hb = d2h(p, bins, CB_COUNT + 1, st);
-            for (int b = 0; b <= CB_COUNT; ++b) S_l.bins[b] = hb[b];
-            S_l.npos = S_l.bins[CB_EMPTY];
-            int64_t* rp = ar.get<int64_t>(lvname("_rp", l), (size_t)S_l.npos + 1);
-            int64_t* cursor = ar.get<int64_t>("cursor", (size_t)S_l.npos + 1);
-            {
-                PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
-                reord_rowptr(counts, inv, S_l.npos, rp, ar, st);
-                copy<int64_t>(cursor, rp, S_l.npos, st);
-            }
-            int32_t* out = bufc[(l + 1) & 1];
-            {
-                PhaseScope ps(p, 0, SPGEMM_PHASE_MULTISPLIT, st);
-                multisplit(g, bufc[l & 1], nullptr, pos, cursor, out, nullptr, ar, st);
-                add_bytes(p, 0, SPGEMM_PHASE_MULTISPLIT, 8.0 * total + 8.0 * (R + 1));
-            }
-            if (p->opt.debug_dump) debug_copy_level(p, l, rp, S_l.npos, out, nullptr, inv, st);
-            int64_t* nnz_l = ar.get<int64_t>(lvname("_nnz", l), (size_t)S_l.nnat);
-            fill<int64_t>(nnz_l, S_l.nnat, 0, st);
-            const int64_t nheavy = S_l.bins[CB_NEXT + 1] - S_l.bins[CB_NEXT];
-            {
-                ChunkItems ci{};
-            ci.hash_top_logS = p->prm.hash_top_logS;
-                ci.rp = rp;
-                ci.map = inv;
-                ci.bcol = out;
-                ci.cnt = nnz_l;
-                ci.width = q.width[l];
-                PhaseScope ps(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, st);
-                for (int b = CB_DENSE; b <= CB_H8192; ++b)
-                    accumulate_chunks(ci, b, S_l.bins[b], S_l.bins[b + 1] - S_l.bins[b], false,
-                                      st);
-            }
-            p->stats.vchunks[l] = S_l.nch;
-            p->stats.level_in_elems[l] = total;
-            p->stats.level_heavy_chunks[l] = nheavy;
-            p->stats.level_final_chunks[l] = S_l.bins[CB_EMPTY] - S_l.bins[CB_DENSE];
-            L = l + 1;
-            if (nheavy == 0) {
-                S_l.final_elems = total;
-                add_bytes(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, 4.0 * total);
-                break;
-            }
-            int64_t elems_heavy = d2h(p, rp + nheavy, 1, st)[0];
-            S_l.final_elems = total - elems_heavy;
-            add_bytes(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, 4.0 * S_l.final_elems);
-            rp_in = rp;
-            R = nheavy;
-            total = elems_heavy;
-        }
-        p->L = L;
-        // bottom-up: a heavy chunk's count is the sum of its sub-chunks' counts
-        {
-            PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
-            for (int l = L - 2; l >= 0; --l) {
-                LevelState& a = p->lv[l];
-                const int64_t nheavy = a.bins[CB_NEXT + 1] - a.bins[CB_NEXT];
-                reduce_children(ar.get<int64_t>(lvname("_nnz", l + 1), 1), p->lv[l + 1].nch,
-                                nheavy, ar.get<int32_t>(lvname("_inv", l), 1),
-                                ar.get<int64_t>(lvname("_nnz", l), 1), st);
-            }
-            reduce_children(ar.get<int64_t>(lvname("_nnz", 0), 1), p->lv[0].nch, p->H, hrows,
-                            cnt_row, st);
-        }
-    }
-}
-
-// Symbolic pass of the heavy rows without C-hat: per finest chunk slot, the
-// element and distinct-column counts from one bitmap pass per heavy row;
-// every level's chunk counts (the Histogram of Algorithm 3) and distinct
-// counts (its Symbolic) are sums over slots. ThreshPartition then orders
-// each level's chunks exactly as the multisplit path would.
-void heavy_symbolic_fused(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t* S,
-                          const int32_t* hrows, int64_t* cnt_row, hipStream_t st) {
-    Arena& ar = p->ar;
-    const Params& q = p->prm;
-    const int64_t req = q.nlevels == 0 ? 1 : q.nchunks_required;
-    const int64_t wfin = q.nlevels == 0 ? q.ppow : q.final_width;
-    int64_t* elem_fin = ar.get<int64_t>("elem_fin", (size_t)(p->H * req));
-    int64_t* dist_fin = ar.get<int64_t>("dist_fin", (size_t)(p->H * req));
-    {
-        PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
-        int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
-        heavy_symbolic(A, B, hrows, p->H, q.ppow, wfin, bslot, elem_fin, dist_fin, st);
-        add_bytes(p, 0, SPGEMM_PHASE_HISTO, 4.0 * p->Nh + 16.0 * p->H * req);
-    }
-    if (q.nlevels == 0) {
-        PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
-        reduce_children(dist_fin, 1, p->H, hrows, cnt_row, st);
+        accumulate_chunks(ci, CB_DENSE, 0, R0, false, st);
+        add_bytes(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, 4.0 * bt.N);
         return;
     }
-    const int64_t* parent_slot0 = nullptr;
-    const int32_t* parent_inv = nullptr;
-    int64_t R = p->H, total = p->Nh;
-    int64_t slots_per_chunk = req;
-    int L = 0;
+    int32_t* bufc[2] = {buf0c, ar.get<int32_t>("buf1c", (size_t)p->maxN)};
+    const int64_t* rp_in = c.crp + bt.crp0;
+    int64_t R = R0, total = bt.N;
     for (int l = 0; l < q.nlevels; ++l) {
         const bool last = (l == q.nlevels - 1);
-        LevelState& S_l = p->lv[l];
+        LevelState& S_l = bt.lv[l];
         S_l.R = R;
         S_l.total_in = total;
         S_l.nch = q.vchunks[l];
         S_l.shift = ilog2(q.width[l]);
         S_l.nnat = R * S_l.nch;
-        S_l.in_buf = l & 1;
-        if (S_l.nnat >= (int64_t(1) << 31)) throw OverflowError("too many chunks in a level");
+        S_l.nat_off = nat_cur[l];
+        S_l.rp_off = rp_cur[l];
+        if (S_l.nat_off + S_l.nnat > p->cap_nat[l]) throw std::logic_error("level capacity");
+        int64_t* counts = lvarr<int64_t>(p, l, "_counts") + S_l.nat_off;
+        int32_t* inv = lvarr<int32_t>(p, l, "_inv") + S_l.nat_off;
+        int32_t* pos = lvarr<int32_t>(p, l, "_pos") + S_l.nat_off;
+        int64_t* nnz_l = lvarr<int64_t>(p, l, "_nnz") + S_l.nat_off;
+        int64_t* bins = ar.get<int64_t>("chunk_bins", CB_COUNT + 1);
+        LevelGeom g{rp_in, R, total, S_l.shift, S_l.nch, q.tau};
+        {
+            PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
+            fill<int64_t>(counts, S_l.nnat, 0, st);
+            histogram(g, bufc[l & 1], counts, ar, st);
+            classify_chunks(counts, S_l.nnat, q.tau, last, inv, pos, bins, ar, st);
+            add_bytes(p, 0, SPGEMM_PHASE_HISTO, 4.0 * total + 8.0 * (R + 1) + 8.0 * S_l.nnat);
+        }
+        int64_t* hb = d2h(p, bins, CB_COUNT + 1, st);
+        for (int b = 0; b <= CB_COUNT; ++b) S_l.bins[b] = hb[b];
+        S_l.npos = S_l.bins[CB_EMPTY];
+        int64_t* rp = lvarr<int64_t>(p, l, "_rp", true) + S_l.rp_off;
+        int64_t* cursor = ar.get<int64_t>("cursor", (size_t)p->cap_rp[l] + 1);
+        {
+            PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
+            reord_rowptr(counts, inv, S_l.npos, rp, ar, st);
+            copy<int64_t>(cursor, rp, S_l.npos, st);
+        }
+        int32_t* out = bufc[(l + 1) & 1];
+        {
+            PhaseScope ps(p, 0, SPGEMM_PHASE_MULTISPLIT, st);
+            multisplit(g, bufc[l & 1], nullptr, pos, cursor, out, nullptr, ar, st);
+            add_bytes(p, 0, SPGEMM_PHASE_MULTISPLIT, 8.0 * total + 8.0 * (R + 1));
+        }
+        if (dump) debug_copy_level(p, l, S_l, rp, out, nullptr, inv, st);
+        fill<int64_t>(nnz_l, S_l.nnat, 0, st);
+        {
+            ChunkItems ci{};
+            ci.hash_top_logS = q.hash_top_logS;
+            ci.rp = rp;
+            ci.map = inv;
+            ci.bcol = out;
+            ci.cnt = nnz_l;
+            ci.width = q.width[l];
+            PhaseScope ps(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, st);
+            for (int b = CB_DENSE; b <= CB_H8192; ++b)
+                accumulate_chunks(ci, b, S_l.bins[b], S_l.bins[b + 1] - S_l.bins[b], false, st);
+        }
+        nat_cur[l] += S_l.nnat;
+        rp_cur[l] += S_l.npos + 1;
+        bt.L = l + 1;
+        const int64_t nheavy = S_l.nheavy();
+        if (nheavy == 0) {
+            S_l.final_elems = total;
+            add_bytes(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, 4.0 * total);
+            break;
+        }
+        const int64_t elems_heavy = d2h(p, rp + nheavy, 1, st)[0];
+        S_l.final_elems = total - elems_heavy;
+        add_bytes(p, 0, SPGEMM_PHASE_HEAVY_ACCUM, 4.0 * S_l.final_elems);
+        rp_in = rp;
+        R = nheavy;
+        total = elems_heavy;
+    }
+    // bottom-up: a heavy chunk's count is the sum of its sub-chunks' counts
+    PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
+    for (int l = bt.L - 2; l >= 0; --l) {
+        const LevelState& a = bt.lv[l];
+        const LevelState& c1 = bt.lv[l + 1];
+        reduce_children(lvarr<int64_t>(p, l + 1, "_nnz") + c1.nat_off, c1.nch, a.nheavy(),
+                        lvarr<int32_t>(p, l, "_inv") + a.nat_off,
+                        lvarr<int64_t>(p, l, "_nnz") + a.nat_off, st);
+    }
+}
+
+// Symbolic pass of one batch without C-hat: every level's chunk counts (the
+// Histogram of Algorithm 3) and distinct counts (its Symbolic) are sums of
+// the finest-slot counts of one bitmap pass per heavy row; ThreshPartition
+// then orders each level's chunks exactly as the multisplit path would.
+void symbolic_batch_fused(spgemm_plan p, BatchState& bt, const int64_t* elem_fin,
+                          const int64_t* dist_fin, int64_t* nat_cur, int64_t* rp_cur,
+                          hipStream_t st) {
+    Arena& ar = p->ar;
+    const Params& q = p->prm;
+    const int64_t req = q.nchunks_required;
+    const int64_t* elem = elem_fin + bt.h0 * req;
+    const int64_t* dist = dist_fin + bt.h0 * req;
+    const int64_t* parent_slot0 = nullptr;
+    const int32_t* parent_inv = nullptr;
+    int64_t R = bt.h1 - bt.h0, total = bt.N;
+    int64_t slots_per_chunk = req;
+    for (int l = 0; l < q.nlevels; ++l) {
+        const bool last = (l == q.nlevels - 1);
+        LevelState& S_l = bt.lv[l];
+        S_l.R = R;
+        S_l.total_in = total;
+        S_l.nch = q.vchunks[l];
+        S_l.shift = ilog2(q.width[l]);
+        S_l.nnat = R * S_l.nch;
+        S_l.nat_off = nat_cur[l];
+        S_l.rp_off = rp_cur[l];
+        if (S_l.nat_off + S_l.nnat > p->cap_nat[l]) throw std::logic_error("level capacity");
         slots_per_chunk /= S_l.nch;
-        int64_t* counts = ar.get<int64_t>(lvname("_counts", l), (size_t)S_l.nnat);
-        int64_t* nnz_l = ar.get<int64_t>(lvname("_nnz", l), (size_t)S_l.nnat);
-        int64_t* slot0 = ar.get<int64_t>(lvname("_slot0", l), (size_t)S_l.nnat);
-        int32_t* inv = ar.get<int32_t>(lvname("_inv", l), (size_t)S_l.nnat);
-        int32_t* pos = ar.get<int32_t>(lvname("_pos", l), (size_t)S_l.nnat);
-        int64_t* bins = ar.get<int64_t>(lvname("_bins", l), CB_COUNT + 1);
+        int64_t* counts = lvarr<int64_t>(p, l, "_counts") + S_l.nat_off;
+        int64_t* nnz_l = lvarr<int64_t>(p, l, "_nnz") + S_l.nat_off;
+        int64_t* slot0 = lvarr<int64_t>(p, l, "_slot0") + S_l.nat_off;
+        int32_t* inv = lvarr<int32_t>(p, l, "_inv") + S_l.nat_off;
+        int32_t* pos = lvarr<int32_t>(p, l, "_pos") + S_l.nat_off;
+        int64_t* bins = ar.get<int64_t>("chunk_bins", CB_COUNT + 1);
         {
             PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
             level_from_slots(parent_slot0, parent_inv, R, S_l.nch, (int)slots_per_chunk, req,
-                             elem_fin, dist_fin, counts, nnz_l, slot0, st);
+                             elem, dist, counts, nnz_l, slot0, st);
             classify_chunks(counts, S_l.nnat, q.tau, last, inv, pos, bins, ar, st);
         }
         int64_t* hb = d2h(p, bins, CB_COUNT + 1, st);
         for (int b = 0; b <= CB_COUNT; ++b) S_l.bins[b] = hb[b];
         S_l.npos = S_l.bins[CB_EMPTY];
-        int64_t* rp = ar.get<int64_t>(lvname("_rp", l), (size_t)S_l.npos + 1);
+        int64_t* rp = lvarr<int64_t>(p, l, "_rp", true) + S_l.rp_off;
         {
             PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
             reord_rowptr(counts, inv, S_l.npos, rp, ar, st);
         }
-        const int64_t nheavy = S_l.bins[CB_NEXT + 1] - S_l.bins[CB_NEXT];
-        p->stats.vchunks[l] = S_l.nch;
-        p->stats.level_in_elems[l] = total;
-        p->stats.level_heavy_chunks[l] = nheavy;
-        p->stats.level_final_chunks[l] = S_l.bins[CB_EMPTY] - S_l.bins[CB_DENSE];
-        L = l + 1;
+        nat_cur[l] += S_l.nnat;
+        rp_cur[l] += S_l.npos + 1;
+        bt.L = l + 1;
+        const int64_t nheavy = S_l.nheavy();
         if (nheavy == 0) {
             S_l.final_elems = total;
             break;
         }
-        int64_t elems_heavy = d2h(p, rp + nheavy, 1, st)[0];
+        const int64_t elems_heavy = d2h(p, rp + nheavy, 1, st)[0];
         S_l.final_elems = total - elems_heavy;
         parent_slot0 = slot0;
         parent_inv = inv;
         R = nheavy;
         total = elems_heavy;
     }
-    p->L = L;
+}
+
+// Chunk output offsets, top-down: level 0 from C.rowPtr of the heavy rows,
+// every deeper level from its parent chunk's offset.
+void heavy_offsets(spgemm_plan p, const int32_t* hrows, const int64_t* C_rp, hipStream_t st) {
+    if (p->prm.nlevels == 0 || p->H == 0) return;
     PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
-    reduce_children(ar.get<int64_t>(lvname("_nnz", 0), 1), p->lv[0].nch, p->H, hrows, cnt_row, st);
+    child_offsets(lvarr<int64_t>(p, 0, "_nnz"), p->prm.vchunks[0], p->H, hrows, C_rp,
+                  lvarr<int64_t>(p, 0, "_off"), st);
+    for (const BatchState& bt : p->batches) {
+        for (int l = 0; l + 1 < bt.L; ++l) {
+            const LevelState& a = bt.lv[l];
+            const LevelState& c1 = bt.lv[l + 1];
+            child_offsets(lvarr<int64_t>(p, l + 1, "_nnz") + c1.nat_off, c1.nch, a.nheavy(),
+                          lvarr<int32_t>(p, l, "_inv") + a.nat_off,
+                          lvarr<int64_t>(p, l, "_off") + a.nat_off,
+                          lvarr<int64_t>(p, l + 1, "_off") + c1.nat_off, st);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- symbolic
@@ -507,22 +639,17 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             accumulate_rows(ri, b, p->row_bins[b], p->row_bins[b + 1] - p->row_bins[b], false, st);
     }
 
-    // heavy rows (Algorithm 3 lines 6-21)
+    // heavy rows (Algorithm 3 lines 6-21), batch by batch
     p->L = 0;
+    p->batches.clear();
     if (p->H > 0) {
         int64_t* chat_rp = ar.get<int64_t>("chat_rp", (size_t)p->H + 1);
-        int32_t *ent_k = nullptr;
-        int64_t *ent_q = nullptr, *ent_dest = nullptr, *P = nullptr;
         {
             PhaseScope ps(p, 0, SPGEMM_PHASE_CSR_TO_CSC, st);
             heavy_rowptr(A, S, hrows, p->H, chat_rp, ar, st);
-            p->ne = masked_csr2csc(A, B, S, hrows, p->H, chat_rp, &ent_k, &ent_q, &ent_dest, &P,
-                                   &p->npieces, ar, st);
-            expand_tile_starts(P, p->ne, p->npieces,
-                               ar.get<int64_t>("expand_tiles", (size_t)expand_tiles(p->npieces) + 1),
-                               st);
-            add_bytes(p, 0, SPGEMM_PHASE_CSR_TO_CSC, 36.0 * p->ne);
         }
+        plan_batches(p, chat_rp, st);
+        plan_capacities(p, A);
         p->stats.chat_bytes = 12 * p->Nh + 8 * (p->H + 1);
         const int64_t req = q.nlevels == 0 ? 1 : q.nchunks_required;
         // the fused pass needs the row's bitmap in LDS and a per-B-row slot
@@ -532,45 +659,83 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
         p->fused_sym = p->opt.symbolic_mode == 1 || (p->opt.symbolic_mode == 0 && fused_fits);
         if (p->fused_sym && !fused_fits)
             throw OverflowError("fused symbolic pass needs more LDS than the device has");
-        if (p->fused_sym)
-            heavy_symbolic_fused(p, A, B, S, hrows, cnt_row, st);
-        else
-            heavy_symbolic_multisplit(p, A, B, chat_rp, ent_k, ent_q, ent_dest, P, hrows, cnt_row,
-                                      st);
+        int64_t* elem_fin = nullptr;
+        int64_t* dist_fin = nullptr;
+        if (p->fused_sym) {
+            const int64_t wfin = q.nlevels == 0 ? q.ppow : q.final_width;
+            elem_fin = ar.get<int64_t>("elem_fin", (size_t)(p->H * req));
+            dist_fin = ar.get<int64_t>("dist_fin", (size_t)(p->H * req));
+            PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
+            int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
+            heavy_symbolic(A, B, hrows, p->H, q.ppow, wfin, bslot, elem_fin, dist_fin, st);
+            add_bytes(p, 0, SPGEMM_PHASE_HISTO, 4.0 * p->Nh + 16.0 * p->H * req);
+        }
+        CscBufs c = csc_bufs(p);
+        int64_t ent_cur = 0, P_cur = 0, tile_cur = 0, crp_cur = 0;
+        int64_t nat_cur[kMaxLevels] = {}, rp_cur[kMaxLevels] = {};
+        for (BatchState& bt : p->batches) {
+            const int64_t R0 = bt.h1 - bt.h0;
+            {
+                PhaseScope ps(p, 0, SPGEMM_PHASE_CSR_TO_CSC, st);
+                bt.ent0 = ent_cur;
+                bt.P0 = P_cur;
+                bt.ne = masked_csr2csc(A, B, S, hrows + bt.h0, R0, chat_rp + bt.h0, bt.chat_base,
+                                       c.ent_k + ent_cur, c.ent_q + ent_cur, c.ent_dest + ent_cur,
+                                       p->cap_ent - ent_cur, c.P + P_cur, &bt.npieces, ar, st);
+                ent_cur += bt.ne;
+                P_cur += bt.ne + 1;
+                bt.tile0 = tile_cur;
+                if (tile_cur + expand_tiles(bt.npieces) + 1 > p->cap_tiles)
+                    throw std::logic_error("expand tile capacity");
+                expand_tile_starts(c.P + bt.P0, bt.ne, bt.npieces, c.tiles + bt.tile0, st);
+                tile_cur += expand_tiles(bt.npieces) + 1;
+                bt.crp0 = crp_cur;
+                rebase(chat_rp + bt.h0, R0 + 1, bt.chat_base, c.crp + bt.crp0, st);
+                crp_cur += R0 + 1;
+                add_bytes(p, 0, SPGEMM_PHASE_CSR_TO_CSC, 36.0 * bt.ne);
+            }
+            if (p->fused_sym) {
+                if (q.nlevels > 0)
+                    symbolic_batch_fused(p, bt, elem_fin, dist_fin, nat_cur, rp_cur, st);
+            } else {
+                symbolic_batch_multisplit(p, bt, A, B, hrows, cnt_row, nat_cur, rp_cur, st);
+            }
+            p->L = std::max(p->L, bt.L);
+            for (int l = 0; l < bt.L; ++l) {
+                const LevelState& S_l = bt.lv[l];
+                p->stats.vchunks[l] = S_l.nch;
+                p->stats.level_in_elems[l] += S_l.total_in;
+                p->stats.level_heavy_chunks[l] += S_l.nheavy();
+                p->stats.level_final_chunks[l] += S_l.bins[CB_EMPTY] - S_l.bins[CB_DENSE];
+            }
+        }
+        // row counts of the heavy rows
+        PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
+        if (q.nlevels == 0) {
+            if (p->fused_sym) reduce_children(dist_fin, 1, p->H, hrows, cnt_row, st);
+        } else {
+            reduce_children(lvarr<int64_t>(p, 0, "_nnz"), q.vchunks[0], p->H, hrows, cnt_row, st);
+        }
     }
 
     // C.rowPtr (Algorithm 3 lines 23-25)
-    int64_t nnz_c;
     {
         PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
         scan_exclusive(LoadI64{cnt_row}, n, C_rp, ar, st);
         add_bytes(p, 0, SPGEMM_PHASE_PREFIX_SUM, 16.0 * n);
     }
-    nnz_c = d2h(p, C_rp + n, 1, st)[0];
-    // chunk output offsets, top-down
-    if (p->H > 0 && p->L > 0) {
-        PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
-        child_offsets(ar.get<int64_t>(lvname("_nnz", 0), 1), p->lv[0].nch, p->H, hrows, C_rp,
-                      ar.get<int64_t>(lvname("_off", 0), (size_t)p->lv[0].nnat), st);
-        for (int l = 0; l + 1 < p->L; ++l) {
-            const int64_t nheavy = p->lv[l].bins[CB_NEXT + 1] - p->lv[l].bins[CB_NEXT];
-            child_offsets(ar.get<int64_t>(lvname("_nnz", l + 1), 1), p->lv[l + 1].nch, nheavy,
-                          ar.get<int32_t>(lvname("_inv", l), 1),
-                          ar.get<int64_t>(lvname("_off", l), 1),
-                          ar.get<int64_t>(lvname("_off", l + 1), (size_t)p->lv[l + 1].nnat), st);
-        }
-    }
+    const int64_t nnz_c = d2h(p, C_rp + n, 1, st)[0];
+    heavy_offsets(p, hrows, C_rp, st);
     p->stats.nrows = n;
     p->stats.ncols_c = B.m;
     p->stats.nnz_c = nnz_c;
     p->stats.tau = q.tau;
     p->stats.final_chunk_width = q.final_width;
     p->stats.nlevels = p->L;
-    p->stats.nbatches = p->H > 0 ? 1 : 0;
+    p->stats.nbatches = (int32_t)p->batches.size();
     p->stats.lds_bytes = q.slm;
     p->stats.light_rows = p->row_bins[RB_EMPTY] - p->row_bins[RB_WIN64];
     p->stats.light_products = p->stats.sum_products - p->stats.heavy_products;
-    if (p->H > 0 && q.nlevels == 0) p->stats.nlevels = 0;
     return nnz_c;
 }
 
@@ -610,108 +775,74 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
     }
     if (p->H == 0) return;
 
-    int64_t* chat_rp = ar.get<int64_t>("chat_rp", (size_t)p->H + 1);
-    int32_t* ent_k = ar.get<int32_t>("csc_ent_k", (size_t)p->ne);
-    int64_t* ent_q = ar.get<int64_t>("csc_ent_q", (size_t)p->ne);
-    int64_t* ent_dest = ar.get<int64_t>("csc_ent_dest", (size_t)p->ne);
-    int64_t* P = ar.get<int64_t>("csc_slice_off", (size_t)p->ne + 1);
-    int32_t* bufc[2] = {ar.get<int32_t>("buf0c", (size_t)p->Nh), nullptr};
-    double* bufv[2] = {ar.get<double>("buf0v", (size_t)p->Nh), nullptr};
-    {
-        ExpandArgs ea{ent_k, ent_q, ent_dest, P, p->ne, A.val, B.rp, B.col, B.val, bufc[0],
-                      bufv[0], p->npieces,
-                      ar.get<int64_t>("expand_tiles", (size_t)expand_tiles(p->npieces) + 1)};
-        PhaseScope ps(p, 1, SPGEMM_PHASE_OUTER_PROD, st);
-        expand(ea, st);
-        add_bytes(p, 1, SPGEMM_PHASE_OUTER_PROD, 12.0 * p->Nh + 28.0 * p->ne);
+    CscBufs c = csc_bufs(p);
+    int32_t* bufc[2] = {ar.get<int32_t>("buf0c", (size_t)p->maxN), nullptr};
+    double* bufv[2] = {ar.get<double>("buf0v", (size_t)p->maxN), nullptr};
+    if (q.nlevels > 0) {
+        bufc[1] = ar.get<int32_t>("buf1c", (size_t)p->maxN);
+        bufv[1] = ar.get<double>("buf1v", (size_t)p->maxN);
     }
-    if (p->opt.debug_dump) debug_copy_chat(p, chat_rp, bufc[0], bufv[0], hrows, st);
-
-    if (q.nlevels == 0) {
-        ChunkItems ci{};
-            ci.hash_top_logS = p->prm.hash_top_logS;
-        ci.rp = chat_rp;
-        ci.map = hrows;
-        ci.bcol = bufc[0];
-        ci.bval = bufv[0];
-        ci.off = C_rp;
-        ci.Ccol = C_col;
-        ci.Cval = C_val;
-        ci.width = q.final_width;
-        PhaseScope ps(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, st);
-        accumulate_chunks(ci, CB_DENSE, 0, p->H, true, st);
-        add_bytes(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, 12.0 * p->Nh);
-        return;
-    }
-    bufc[1] = ar.get<int32_t>("buf1c", (size_t)p->Nh);
-    bufv[1] = ar.get<double>("buf1v", (size_t)p->Nh);
-    const int64_t* rp_in = chat_rp;
-    for (int l = 0; l < p->L; ++l) {
-        LevelState& S_l = p->lv[l];
-        int32_t* inv = ar.get<int32_t>(lvname("_inv", l), (size_t)S_l.nnat);
-        int32_t* pos = ar.get<int32_t>(lvname("_pos", l), (size_t)S_l.nnat);
-        int64_t* rp = ar.get<int64_t>(lvname("_rp", l), (size_t)S_l.npos + 1);
-        int64_t* off = ar.get<int64_t>(lvname("_off", l), (size_t)S_l.nnat);
-        int64_t* cursor = ar.get<int64_t>("cursor", (size_t)S_l.npos + 1);
-        copy<int64_t>(cursor, rp, S_l.npos, st);
-        LevelGeom g{rp_in, S_l.R, S_l.total_in, S_l.shift, S_l.nch, q.tau};
-        const int in = l & 1, outb = (l + 1) & 1;
+    const bool dump = p->opt.debug_dump && p->batches.size() == 1;
+    for (const BatchState& bt : p->batches) {
+        const int64_t R0 = bt.h1 - bt.h0;
         {
-            PhaseScope ps(p, 1, SPGEMM_PHASE_MULTISPLIT, st);
-            multisplit(g, bufc[in], bufv[in], pos, cursor, bufc[outb], bufv[outb], ar, st);
-            add_bytes(p, 1, SPGEMM_PHASE_MULTISPLIT, 24.0 * S_l.total_in + 8.0 * (S_l.R + 1));
+            PhaseScope ps(p, 1, SPGEMM_PHASE_OUTER_PROD, st);
+            expand(expand_args(p, bt, A, B, bufc[0], bufv[0]), st);
+            add_bytes(p, 1, SPGEMM_PHASE_OUTER_PROD, 12.0 * bt.N + 28.0 * bt.ne);
         }
-        if (p->opt.debug_dump) debug_copy_level(p, l, rp, S_l.npos, bufc[outb], bufv[outb], inv, st);
-        {
+        if (dump) debug_copy_chat(p, bt, c.crp + bt.crp0, bufc[0], bufv[0], hrows + bt.h0, st);
+        if (q.nlevels == 0) {
             ChunkItems ci{};
-            ci.hash_top_logS = p->prm.hash_top_logS;
-            ci.rp = rp;
-            ci.map = inv;
-            ci.bcol = bufc[outb];
-            ci.bval = bufv[outb];
-            ci.off = off;
+            ci.hash_top_logS = q.hash_top_logS;
+            ci.rp = c.crp + bt.crp0;
+            ci.map = hrows + bt.h0;
+            ci.bcol = bufc[0];
+            ci.bval = bufv[0];
+            ci.off = C_rp;
             ci.Ccol = C_col;
             ci.Cval = C_val;
-            ci.width = p->prm.width[l];
+            ci.width = q.final_width;
             PhaseScope ps(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, st);
-            for (int b = CB_DENSE; b <= CB_H8192; ++b)
-                accumulate_chunks(ci, b, S_l.bins[b], S_l.bins[b + 1] - S_l.bins[b], true, st);
-            add_bytes(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, 12.0 * S_l.final_elems);
+            accumulate_chunks(ci, CB_DENSE, 0, R0, true, st);
+            add_bytes(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, 12.0 * bt.N);
+            continue;
         }
-        rp_in = rp;
+        const int64_t* rp_in = c.crp + bt.crp0;
+        for (int l = 0; l < bt.L; ++l) {
+            const LevelState& S_l = bt.lv[l];
+            int32_t* inv = lvarr<int32_t>(p, l, "_inv") + S_l.nat_off;
+            int32_t* pos = lvarr<int32_t>(p, l, "_pos") + S_l.nat_off;
+            int64_t* off = lvarr<int64_t>(p, l, "_off") + S_l.nat_off;
+            int64_t* rp = lvarr<int64_t>(p, l, "_rp", true) + S_l.rp_off;
+            int64_t* cursor = ar.get<int64_t>("cursor", (size_t)p->cap_rp[l] + 1);
+            copy<int64_t>(cursor, rp, S_l.npos, st);
+            LevelGeom g{rp_in, S_l.R, S_l.total_in, S_l.shift, S_l.nch, q.tau};
+            const int in = l & 1, outb = (l + 1) & 1;
+            {
+                PhaseScope ps(p, 1, SPGEMM_PHASE_MULTISPLIT, st);
+                multisplit(g, bufc[in], bufv[in], pos, cursor, bufc[outb], bufv[outb], ar, st);
+                add_bytes(p, 1, SPGEMM_PHASE_MULTISPLIT, 24.0 * S_l.total_in + 8.0 * (S_l.R + 1));
+            }
+            if (dump) debug_copy_level(p, l, S_l, rp, bufc[outb], bufv[outb], inv, st);
+            {
+                ChunkItems ci{};
+                ci.hash_top_logS = q.hash_top_logS;
+                ci.rp = rp;
+                ci.map = inv;
+                ci.bcol = bufc[outb];
+                ci.bval = bufv[outb];
+                ci.off = off;
+                ci.Ccol = C_col;
+                ci.Cval = C_val;
+                ci.width = q.width[l];
+                PhaseScope ps(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, st);
+                for (int b = CB_DENSE; b <= CB_H8192; ++b)
+                    accumulate_chunks(ci, b, S_l.bins[b], S_l.bins[b + 1] - S_l.bins[b], true, st);
+                add_bytes(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, 12.0 * S_l.final_elems);
+            }
+            rp_in = rp;
+        }
     }
-}
-
-// ---------------------------------------------------------------- debug dumps
-void debug_copy_chat(spgemm_plan p, const int64_t* chat_rp, const int32_t* col, const double* val,
-                     const int32_t* hrows, hipStream_t st) {
-    Arena& ar = p->ar;
-    copy<int64_t>(ar.get<int64_t>("dbg_m1_rp", (size_t)p->H + 1), chat_rp, p->H + 1, st);
-    copy<int32_t>(ar.get<int32_t>("dbg_m1_col", (size_t)p->Nh), col, p->Nh, st);
-    if (val) copy<double>(ar.get<double>("dbg_m1_val", (size_t)p->Nh), val, p->Nh, st);
-    int64_t* key = ar.get<int64_t>("dbg_m1_key", (size_t)p->H + 1);
-    hipLaunchKernelGGL(k_i32_to_i64, dim3(grid_1d(ceil_div(p->H, 256))), dim3(256), 0, st, hrows,
-                       p->H, key);
-    SG_LAUNCH_CHECK();
-    p->dbg_valid = true;
-    p->dbg_has_val = val != nullptr;
-}
-
-void debug_copy_level(spgemm_plan p, int l, const int64_t* rp, int64_t npos, const int32_t* col,
-                      const double* val, const int32_t* inv, hipStream_t st) {
-    Arena& ar = p->ar;
-    int64_t nnz = d2h(p, rp + npos, 1, st)[0];
-    std::string b = "dbg_l" + std::to_string(l);
-    copy<int64_t>(ar.get<int64_t>(b + "_rp", (size_t)npos + 1), rp, npos + 1, st);
-    copy<int32_t>(ar.get<int32_t>(b + "_col", (size_t)nnz), col, nnz, st);
-    if (val) copy<double>(ar.get<double>(b + "_val", (size_t)nnz), val, nnz, st);
-    int64_t* key = ar.get<int64_t>(b + "_key", (size_t)npos + 1);
-    if (npos > 0) {
-        hipLaunchKernelGGL(k_i32_to_i64, dim3(grid_1d(ceil_div(npos, 256))), dim3(256), 0, st,
-                           inv, npos, key);
-        SG_LAUNCH_CHECK();
-    }
-    p->dbg_levels = std::max(p->dbg_levels, l + 1);
 }
 
 template <class F>
@@ -859,22 +990,25 @@ SPGEMM_API int spgemm_plan_stats(spgemm_plan p, spgemm_stats* out) {
 }
 
 SPGEMM_API int spgemm_plan_debug(spgemm_plan p, int which, spgemm_debug_matrix* out) {
-    if (!p || !out || !p->opt.debug_dump || !p->dbg_valid) return SPGEMM_ERR_INVALID_ARG;
+    if (!p || !out || !p->opt.debug_dump || !p->dbg_valid || p->batches.size() != 1)
+        return SPGEMM_ERR_INVALID_ARG;
     return guarded([&]() -> int {
         Arena& ar = p->ar;
+        const BatchState& bt = p->batches[0];
         memset(out, 0, sizeof(*out));
         if (which == -1) {
-            out->nrows = p->H;
-            out->nnz = p->Nh;
-            out->rowptr = ar.get<int64_t>("dbg_m1_rp", (size_t)p->H + 1);
-            out->col = ar.get<int32_t>("dbg_m1_col", (size_t)p->Nh);
-            out->val = p->dbg_has_val ? ar.get<double>("dbg_m1_val", (size_t)p->Nh) : nullptr;
-            out->row_key = ar.get<int64_t>("dbg_m1_key", (size_t)p->H + 1);
+            const int64_t R = bt.h1 - bt.h0;
+            out->nrows = R;
+            out->nnz = bt.N;
+            out->rowptr = ar.get<int64_t>("dbg_m1_rp", (size_t)R + 1);
+            out->col = ar.get<int32_t>("dbg_m1_col", (size_t)bt.N);
+            out->val = p->dbg_has_val ? ar.get<double>("dbg_m1_val", (size_t)bt.N) : nullptr;
+            out->row_key = ar.get<int64_t>("dbg_m1_key", (size_t)R + 1);
             out->chunk_width = p->prm.ppow;
             return SPGEMM_OK;
         }
-        if (which < 0 || which >= p->L) return SPGEMM_ERR_INVALID_ARG;
-        const LevelState& S_l = p->lv[which];
+        if (which < 0 || which >= bt.L) return SPGEMM_ERR_INVALID_ARG;
+        const LevelState& S_l = bt.lv[which];
         std::string b = "dbg_l" + std::to_string(which);
         SG_HIP(hipDeviceSynchronize());
         int64_t* rp = ar.get<int64_t>(b + "_rp", (size_t)S_l.npos + 1);

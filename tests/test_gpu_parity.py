@@ -181,6 +181,17 @@ def test_random_skewed_paths(tau, seed, mode):
     compare(A, B, rp, col, val)
 
 
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("budget,width,cap", [(1, 64, 4), (700, 64, 4), (5000, 32, 2), (20000, 0, 0)])
+def test_row_batches(budget, width, cap, mode):
+    """Heavy rows processed in batches of bounded products (one row per batch at budget 1)."""
+    A = synth.rmat(11, 8, seed=121, value_seed=122)
+    rp, col, val, st = run_gpu(A, A, tau_override=64, chunk_width_override=width, nchunks_cap=cap,
+                               max_batch_products=budget, symbolic_mode=mode)
+    assert st["nbatches"] > 1
+    compare(A, A, rp, col, val)
+
+
 def test_small_integer_values_exact():
     A = synth.rmat(11, 8, seed=61, value_seed=62, values="int")
     for mode in (1, 2):

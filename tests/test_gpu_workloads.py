@@ -29,12 +29,12 @@ def _gpu():
     binding.load()
 
 
-def _multiply(A, B):
+def _multiply(A, B, **plan_kwargs):
     import torch
     from spgemm_irregular_matrices_amd import binding
     dA = binding.DeviceCSR.from_host(A)
     dB = dA if B is A else binding.DeviceCSR.from_host(B)
-    with binding.Plan() as p:
+    with binding.Plan(**plan_kwargs) as p:
         C = p.multiply(dA, dB)
         torch.cuda.synchronize()
         st = p.stats()
@@ -131,11 +131,14 @@ def test_banded_1M_all_rows():
     compare(A, B, rp, C.col.cpu().numpy(), C.val.cpu().numpy())
 
 
-@pytest.mark.parametrize("name", ["rmat18_ef16", "rmat20_ef8", "rect_zipf2.1_x_uniform16"])
-def test_large_sampled_rows_and_properties(name):
+@pytest.mark.parametrize("name,batch", [("rmat18_ef16", 0), ("rmat20_ef8", 0),
+                                        ("rect_zipf2.1_x_uniform16", 0), ("rmat20_ef8", 1 << 31)])
+def test_large_sampled_rows_and_properties(name, batch):
     import torch
     A, B = synth.workload(name)
-    C, st = _multiply(A, B)
+    C, st = _multiply(A, B, max_batch_products=batch)
+    if batch:
+        assert st["nbatches"] >= 3
     rows, u = sample_rows(A, B, n_heavy=6, n_random=300, seed=7, tau=st["tau"])
     assert st["heavy_rows"] > 0 and st["nlevels"] >= 1
     assert st["sum_products"] == int(u.sum())
