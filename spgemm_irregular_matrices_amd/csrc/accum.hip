@@ -60,7 +60,7 @@ __device__ __forceinline__ ItemHdr load_item(const RowItems& ri, const ChunkItem
 template <int MODE, bool NUM>
 __device__ __forceinline__ void load_elem(const RowItems& ri, const ChunkItems& ci,
                                           const ItemHdr& h, int64_t t, int64_t& cur,
-                                          int32_t& col, double& val) {
+                                          int32_t lo, int32_t& col, double& val) {
     if constexpr (MODE == MODE_ROW) {
         int64_t target = h.s0 + t;
         int64_t q = upper_index(ri.S, cur, h.a1, target);
@@ -70,9 +70,17 @@ __device__ __forceinline__ void load_elem(const RowItems& ri, const ChunkItems& 
         col = ri.B.col[b];
         if constexpr (NUM) val = ri.A.val[q] * ri.B.val[b];
     } else {
-        col = ci.bcol[h.start + t];
+        col = ci.bcol16 ? lo + (int32_t)ci.bcol16[h.start + t] : ci.bcol[h.start + t];
         if constexpr (NUM) val = ci.bval[h.start + t];
     }
+}
+
+// First column of a chunk's window: from the per-chunk base when columns are
+// stored as 16-bit offsets, else from the chunk's first column rounded down
+// to the chunk width.
+__device__ __forceinline__ int32_t chunk_lo(const ChunkItems& ci, int64_t start, int64_t out,
+                                            int64_t W) {
+    return ci.bcol16 ? ci.colbase[out] : (int32_t)(ci.bcol[start] & ~(int32_t)(W - 1));
 }
 
 template <int MODE>
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(TW) void k_acc_hash(RowItems ri, ChunkItems ci, int
         for (int64_t t = tt; t < h.count; t += TW) {
             int32_t c;
             double v = 0.0;
-            load_elem<MODE, NUM>(ri, ci, h, t, cur, c, v);
+            load_elem<MODE, NUM>(ri, ci, h, t, cur, 0, c, v);
             uint32_t key = (uint32_t)c;
             uint32_t slot = (key * 2654435769u) >> (32 - LOGS);
             for (;;) {
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
     const int count = (int)(ci.rp[p0 + item + 1] - start);
     const int64_t out = ci.map[p0 + item];
     for (int w = tt; w < NWD; w += TW) bits[w] = 0u;
-    if (tt == 0) lo_sh = (int32_t)(ci.bcol[start] & ~(int32_t)(W - 1));
+    if (tt == 0) lo_sh = chunk_lo(ci, start, out, W);
     __syncthreads();
     const int32_t lo = lo_sh;
     uint32_t idx[KPT];
@@ -272,7 +280,8 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
         int t = tt + k * TW;
         idx[k] = 0xffffffffu;
         if (t < count) {
-            idx[k] = (uint32_t)(ci.bcol[start + t] - lo);
+            idx[k] = ci.bcol16 ? (uint32_t)ci.bcol16[start + t]
+                               : (uint32_t)(ci.bcol[start + t] - lo);
             if constexpr (NUM) v[k] = ci.bval[start + t];
         }
     }
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, ChunkItems c
         if constexpr (MODE == MODE_ROW) {
             lo_sh[team] = ri.rowlo[h.out];
         } else {
-            lo_sh[team] = (int32_t)(ci.bcol[h.start] & ~(int32_t)(ci.width - 1));
+            lo_sh[team] = chunk_lo(ci, h.start, h.out, ci.width);
         }
     }
     __syncthreads();
@@ -369,7 +378,7 @@ __global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, ChunkItems c
                 const int64_t t = t0 + (int64_t)uu * TW;
                 c[uu] = lo - 1;  // out of the window: skipped below
                 v[uu] = 0.0;
-                if (t < h.count) load_elem<MODE, NUM>(ri, ci, h, t, cur, c[uu], v[uu]);
+                if (t < h.count) load_elem<MODE, NUM>(ri, ci, h, t, cur, lo, c[uu], v[uu]);
             }
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
@@ -520,9 +529,11 @@ static void chunks_impl(const ChunkItems& it, int bin, int64_t p0, int64_t n, hi
         case CB_H8192:
             if (it.width <= kRankMaxWidth)
                 launch_rank_bin<NUM>(bin - CB_H128, it, p0, n, st);
-            else
+            else if (!it.bcol16)
                 launch_hash_bin<MODE_CHUNK, NUM>(bin - CB_H128, it.hash_top_logS, none, it, p0, n,
                                                  st);
+            else
+                throw std::logic_error("16-bit chunk columns need chunks at most 2^16 wide");
             break;
         default: throw std::logic_error("not an accumulated chunk bin");
     }

@@ -350,7 +350,7 @@ void reord_rowptr(const int64_t* counts, const int32_t* inv, int64_t npos, int64
 //     Algorithm 5).
 // Inside a tile, elements keep their input order within each chunk; across
 // tiles the order follows the reservations.
-template <bool NUM, int kMsNT, int kMsK>
+template <bool NUM, bool OUT16, int kMsNT, int kMsK>
 __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t* in_col,
                                                       const double* in_val,
                                                       const int32_t* pos_of,
@@ -427,7 +427,12 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
     }
     __syncthreads();
 
-    // 2. per key: wave prefixes, tile offset (block scan) and reservation
+    // 2. per key: wave prefixes, tile offset (block scan) and reservation.
+    // The reservation atomic of a thread's first key is only waited for
+    // after the LDS permute, so its latency overlaps the permute (with
+    // nkeys <= threads every key is such a first key).
+    int64_t pend_v = 0;
+    int pend_x = -1;
     {
         const int per = (nkeys + kMsNT - 1) / kMsNT;
         const int k0 = min(nkeys, tt * per);
@@ -451,7 +456,13 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
             if (v) {
                 const int64_t nat = (r0 + x / g.nch) * g.nch + (x & mask);
                 const int p = pos_of[nat];
-                delta[x] = (int64_t)atomicAdd(&cursor[p], (unsigned long long)v) - pre;
+                const int64_t got = (int64_t)atomicAdd(&cursor[p], (unsigned long long)v) - pre;
+                if (x == k0) {
+                    pend_v = got;
+                    pend_x = x;
+                } else {
+                    delta[x] = got;
+                }
             }
             pre += v;
         }
@@ -470,12 +481,16 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
             if constexpr (NUM) valbuf[d] = val[k];
         }
     }
+    if (pend_x >= 0) delta[pend_x] = pend_v;
     __syncthreads();
 
-    // 4. ordered write
+    // 4. ordered write; at the last level the column is stored as its
+    // 16-bit offset inside the chunk (chunks there are at most 2^16 wide)
+    const int32_t lmask = (1 << g.shift) - 1;
     for (int d = tt; d < n_wg; d += kMsNT) {
         const int64_t ga = delta[keybuf[d]] + d;
-        out_col[ga] = colbuf[d];
+        if constexpr (OUT16) ((uint16_t*)out_col)[ga] = (uint16_t)(colbuf[d] & lmask);
+        else out_col[ga] = colbuf[d];
         if constexpr (NUM) out_val[ga] = valbuf[d];
     }
 }
@@ -486,36 +501,27 @@ static size_t ms_lds(int64_t epb, int nr_max, int nch, bool num, int nw) {
            (size_t)nw * nkeys * 4 + (nkeys + 1) * 4 + (size_t)epb * 4 + (size_t)epb * 2 + 8;
 }
 
-template <int NT, int K>
+template <bool NUM, bool OUT16, int NT, int K>
 static void ms_launch(const LevelGeom& g, const int32_t* in_col, const double* in_val,
                       const int32_t* pos_of, int64_t* cursor, int32_t* out_col, double* out_val,
                       Arena& ar, hipStream_t st) {
-    bool num = out_val != nullptr;
     int64_t epb = (int64_t)NT * K;
     int nr_max = rows_per_range(epb, g.tau);
-    while (epb > 64 && ms_lds(epb, nr_max, g.nch, num, NT / kWave) > 65536) {
+    while (epb > 64 && ms_lds(epb, nr_max, g.nch, NUM, NT / kWave) > 65536) {
         epb /= 2;
         nr_max = rows_per_range(epb, g.tau);
     }
     if ((int64_t)nr_max * g.nch > 65535) throw OverflowError("multisplit keys exceed 16 bits");
-    size_t lds = ms_lds(epb, nr_max, g.nch, num, NT / kWave);
+    size_t lds = ms_lds(epb, nr_max, g.nch, NUM, NT / kWave);
     if (lds > 160 * 1024) throw OverflowError("multisplit local histogram exceeds LDS");
     int64_t blocks = ceil_div(g.total, epb);
     int64_t* tile_r0 = ar.get<int64_t>("ms_tile_r0", (size_t)blocks + 1);
     tile_starts(g.rp, g.nrows, epb, blocks, tile_r0, st);
-    if (num) {
-        SG_HIP(hipFuncSetAttribute((const void*)k_multisplit<true, NT, K>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-        hipLaunchKernelGGL((k_multisplit<true, NT, K>), dim3(grid_1d(blocks)), dim3(NT), lds, st,
-                           g, in_col, in_val, pos_of, (unsigned long long*)cursor, out_col,
-                           out_val, tile_r0, epb, nr_max);
-    } else {
-        SG_HIP(hipFuncSetAttribute((const void*)k_multisplit<false, NT, K>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-        hipLaunchKernelGGL((k_multisplit<false, NT, K>), dim3(grid_1d(blocks)), dim3(NT), lds, st,
-                           g, in_col, in_val, pos_of, (unsigned long long*)cursor, out_col,
-                           (double*)nullptr, tile_r0, epb, nr_max);
-    }
+    auto kern = k_multisplit<NUM, OUT16, NT, K>;
+    SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds));
+    hipLaunchKernelGGL(kern, dim3(grid_1d(blocks)), dim3(NT), lds, st, g, in_col, in_val, pos_of,
+                       (unsigned long long*)cursor, out_col, out_val, tile_r0, epb, nr_max);
     SG_LAUNCH_CHECK();
 }
 
@@ -526,9 +532,37 @@ constexpr int kMsK = 8;
 
 void multisplit(const LevelGeom& g, const int32_t* in_col, const double* in_val,
                 const int32_t* pos_of, int64_t* cursor, int32_t* out_col, double* out_val,
-                Arena& ar, hipStream_t st) {
+                bool out16, Arena& ar, hipStream_t st) {
     if (g.total <= 0) return;
-    ms_launch<kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, out_val, ar, st);
+    if (out16 && g.shift > 16) throw std::logic_error("16-bit columns need chunks <= 2^16 wide");
+    if (out_val) {
+        if (out16) ms_launch<true, true, kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, out_val, ar, st);
+        else ms_launch<true, false, kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, out_val, ar, st);
+    } else {
+        if (out16) ms_launch<false, true, kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, nullptr, ar, st);
+        else ms_launch<false, false, kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, nullptr, ar, st);
+    }
+}
+
+// First column of every chunk of a level: level 0 chunk c of a row starts at
+// c*W; a deeper chunk c of parent p starts at parent's start + c*W.
+__global__ void k_chunk_colbase(int64_t nparents, int nch, int64_t width, const int32_t* parent_inv,
+                                const int32_t* parent_base, int32_t* out) {
+    int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= nparents * nch) return;
+    int64_t p = x / nch;
+    int c = (int)(x - p * nch);
+    int64_t b = parent_inv ? parent_base[parent_inv[p]] : 0;
+    out[x] = (int32_t)(b + c * width);
+}
+
+void chunk_colbase(int64_t nparents, int nch, int64_t width, const int32_t* parent_inv,
+                   const int32_t* parent_base, int32_t* out, hipStream_t st) {
+    int64_t n = nparents * nch;
+    if (n <= 0) return;
+    hipLaunchKernelGGL(k_chunk_colbase, dim3(grid_1d(ceil_div(n, 256))), dim3(256), 0, st,
+                       nparents, nch, width, parent_inv, parent_base, out);
+    SG_LAUNCH_CHECK();
 }
 
 // ---------------------------------------------------------------- fused symbolic

@@ -136,9 +136,15 @@ void reord_rowptr(const int64_t* counts, const int32_t* inv, int64_t npos, int64
 
 // Multisplit (Algorithm 5): permute the level's input into C-hat-reord.
 // cursor[pos] starts at rp_out[pos] and is advanced by reservations.
+// With out16 the output columns are 16-bit offsets inside each chunk
+// (written to out_col's memory as uint16), for levels whose chunks are at
+// most 2^16 columns wide.
 void multisplit(const LevelGeom& g, const int32_t* in_col, const double* in_val,
                 const int32_t* pos_of, int64_t* cursor, int32_t* out_col, double* out_val,
-                Arena& ar, hipStream_t st);
+                bool out16, Arena& ar, hipStream_t st);
+// out[p*nch + c] = (parent_inv ? parent_base[parent_inv[p]] : 0) + c*width.
+void chunk_colbase(int64_t nparents, int nch, int64_t width, const int32_t* parent_inv,
+                   const int32_t* parent_base, int32_t* out, hipStream_t st);
 
 // Fused symbolic pass over the heavy rows (one work group per row): per
 // finest chunk slot of width wfin, the element count and the number of
@@ -190,6 +196,8 @@ struct ChunkItems {
     double* Cval;
     int64_t width;         // column width of every chunk (power of two)
     int hash_top_logS;     // slots (log2) of the largest light hash table
+    const uint16_t* bcol16;  // if set: columns as 16-bit offsets from colbase[map[p]]
+    const int32_t* colbase;
 };
 void accumulate_chunks(const ChunkItems& it, int bin, int64_t p0, int64_t n, bool numeric,
                        hipStream_t st);

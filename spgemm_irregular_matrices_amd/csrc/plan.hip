@@ -433,7 +433,7 @@ void symbolic_batch_multisplit(spgemm_plan p, BatchState& bt, const DevCSR& A, c
         int32_t* out = bufc[(l + 1) & 1];
         {
             PhaseScope ps(p, 0, SPGEMM_PHASE_MULTISPLIT, st);
-            multisplit(g, bufc[l & 1], nullptr, pos, cursor, out, nullptr, ar, st);
+            multisplit(g, bufc[l & 1], nullptr, pos, cursor, out, nullptr, false, ar, st);
             add_bytes(p, 0, SPGEMM_PHASE_MULTISPLIT, 8.0 * total + 8.0 * (R + 1));
         }
         if (dump) debug_copy_level(p, l, S_l, rp, out, nullptr, inv, st);
@@ -549,6 +549,10 @@ void heavy_offsets(spgemm_plan p, const int32_t* hrows, const int64_t* C_rp, hip
     PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
     child_offsets(lvarr<int64_t>(p, 0, "_nnz"), p->prm.vchunks[0], p->H, hrows, C_rp,
                   lvarr<int64_t>(p, 0, "_off"), st);
+    // first column of every chunk, for levels whose columns are stored as
+    // 16-bit offsets inside the chunk
+    chunk_colbase(p->H, p->prm.vchunks[0], p->prm.width[0], nullptr, nullptr,
+                  lvarr<int32_t>(p, 0, "_cb"), st);
     for (const BatchState& bt : p->batches) {
         for (int l = 0; l + 1 < bt.L; ++l) {
             const LevelState& a = bt.lv[l];
@@ -557,6 +561,10 @@ void heavy_offsets(spgemm_plan p, const int32_t* hrows, const int64_t* C_rp, hip
                           lvarr<int32_t>(p, l, "_inv") + a.nat_off,
                           lvarr<int64_t>(p, l, "_off") + a.nat_off,
                           lvarr<int64_t>(p, l + 1, "_off") + c1.nat_off, st);
+            chunk_colbase(a.nheavy(), c1.nch, p->prm.width[l + 1],
+                          lvarr<int32_t>(p, l, "_inv") + a.nat_off,
+                          lvarr<int32_t>(p, l, "_cb") + a.nat_off,
+                          lvarr<int32_t>(p, l + 1, "_cb") + c1.nat_off, st);
         }
     }
 }
@@ -818,10 +826,14 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
             copy<int64_t>(cursor, rp, S_l.npos, st);
             LevelGeom g{rp_in, S_l.R, S_l.total_in, S_l.shift, S_l.nch, q.tau};
             const int in = l & 1, outb = (l + 1) & 1;
+            // A level with no chunk for a further level feeds only the
+            // accumulators: its columns go out as 16-bit offsets in the chunk.
+            const bool c16 = !dump && S_l.nheavy() == 0 && q.width[l] <= (int64_t(1) << 16);
             {
                 PhaseScope ps(p, 1, SPGEMM_PHASE_MULTISPLIT, st);
-                multisplit(g, bufc[in], bufv[in], pos, cursor, bufc[outb], bufv[outb], ar, st);
-                add_bytes(p, 1, SPGEMM_PHASE_MULTISPLIT, 24.0 * S_l.total_in + 8.0 * (S_l.R + 1));
+                multisplit(g, bufc[in], bufv[in], pos, cursor, bufc[outb], bufv[outb], c16, ar, st);
+                add_bytes(p, 1, SPGEMM_PHASE_MULTISPLIT,
+                          (c16 ? 22.0 : 24.0) * S_l.total_in + 8.0 * (S_l.R + 1));
             }
             if (dump) debug_copy_level(p, l, S_l, rp, bufc[outb], bufv[outb], inv, st);
             {
@@ -830,6 +842,10 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
                 ci.rp = rp;
                 ci.map = inv;
                 ci.bcol = bufc[outb];
+                if (c16) {
+                    ci.bcol16 = (const uint16_t*)bufc[outb];
+                    ci.colbase = lvarr<int32_t>(p, l, "_cb") + S_l.nat_off;
+                }
                 ci.bval = bufv[outb];
                 ci.off = off;
                 ci.Ccol = C_col;
@@ -838,7 +854,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
                 PhaseScope ps(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, st);
                 for (int b = CB_DENSE; b <= CB_H8192; ++b)
                     accumulate_chunks(ci, b, S_l.bins[b], S_l.bins[b + 1] - S_l.bins[b], true, st);
-                add_bytes(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, 12.0 * S_l.final_elems);
+                add_bytes(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, (c16 ? 10.0 : 12.0) * S_l.final_elems);
             }
             rp_in = rp;
         }
