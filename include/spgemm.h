@@ -79,7 +79,11 @@ typedef struct {
     int64_t max_batch_products;   /* heavy products per row batch; 0 = one batch          */
     int32_t symbolic_mode;        /* heavy-row symbolic pass: 0 = auto, 1 = fused per-row
                                      bitmap pass, 2 = multisplit of column-only C-hat      */
-    int32_t reserved;
+    int32_t numeric_mode;         /* heavy-row numeric pass: 0 = auto (1, or 2 when
+                                     debug_dump is set, so that C-hat can be dumped),
+                                     1 = products formed inside the first multisplit level
+                                     (C-hat is never written), 2 = outer product into C-hat
+                                     then multisplit                                       */
 } spgemm_options;
 
 /* Phases, named after the gMAGNUS page's phase breakdown (Section IV-C,

@@ -350,14 +350,36 @@ void reord_rowptr(const int64_t* counts, const int32_t* inv, int64_t npos, int64
 //     Algorithm 5).
 // Inside a tile, elements keep their input order within each chunk; across
 // tiles the order follows the reservations.
-template <bool NUM, bool OUT16, int kMsNT, int kMsK>
+// With FUSED, level 0 of the numeric pass takes its input straight from A
+// and B instead of from C-hat: every thread forms the products of its own
+// elements of the tile (the same C-hat range a plain multisplit tile would
+// read). The tile's A entries are staged in LDS in rounds of kMsNT; an
+// element's entry is found by a search over the staged product offsets,
+// and its B entry is the entry's B row start plus the element's distance
+// from the entry's first product. All loads of a round are issued together.
+struct FusedSrc {
+    const int64_t* hq0 = nullptr;   // per C-hat row: first A entry of its heavy row
+    const int64_t* hq1 = nullptr;   // ... one past its last A entry
+    const int64_t* hs0 = nullptr;   // ... InterOffsets at its first entry
+    const int64_t* S = nullptr;     // InterOffsets over A's entries
+    const int64_t* ebo = nullptr;   // per A entry: first entry of its B row
+    const double* Aval = nullptr;
+    const int32_t* Bcol = nullptr;
+    const double* Bval = nullptr;
+    const int64_t* tile_q0 = nullptr; // entry holding each tile's first product
+    const int64_t* tile_r0 = nullptr; // C-hat row holding each tile's first product
+    int64_t nblocks = 0;
+};
+
+template <bool NUM, bool OUT16, bool FUSED, int kMsNT, int kMsK>
 __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t* in_col,
                                                       const double* in_val,
                                                       const int32_t* pos_of,
                                                       unsigned long long* cursor,
                                                       int32_t* out_col, double* out_val,
                                                       const int64_t* tile_r0, int64_t epb,
-                                                      int nr_max) {
+                                                      int nr_max, FusedSrc fs) {
+    static_assert(!FUSED || NUM, "the fused tile forms values");
     constexpr int NW = kMsNT / kWave;
     extern __shared__ int64_t lds_m[];
     const int nkeys = nr_max * g.nch;
@@ -368,6 +390,7 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
     int* loff = whist + NW * nkeys;                  // nkeys + 1
     int* colbuf = loff + nkeys + 1;                  // epb
     uint16_t* keybuf = (uint16_t*)(colbuf + epb);    // epb
+    int* pos_sh = (int*)(keybuf + epb + (epb & 1));  // nkeys
     __shared__ int64_t r0_sh;
     __shared__ int scan_sh[NW + 1];
 
@@ -384,20 +407,129 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
         rb[j] = (r0 + j <= g.nrows) ? g.rp[r0 + j] : INT64_MAX;
     __syncthreads();
 
+    // positions of this tile's (row, chunk) keys in the level's partition,
+    // loaded now so that the reservations below wait on one load less
+    for (int x = tt; x < nkeys; x += kMsNT) {
+        const int64_t r = r0 + x / g.nch;
+        pos_sh[x] = r < g.nrows ? pos_of[r * g.nch + (x & mask)] : -1;
+    }
+
+    int32_t col[kMsK];
+    double val[kMsK];
+    if constexpr (FUSED) {
+        // 0. form the tile's products in registers, in the layout phase 1
+        // reads: element t of the tile (C-hat order) lies in the last A
+        // entry whose product range starts at or before t.
+        // (offsets from the LDS base keep the pointers in the LDS address space)
+        const int rq_off = (int)(((char*)(pos_sh + nkeys) - (char*)lds_m + 7) & ~7);
+        int64_t* rq0 = (int64_t*)((char*)lds_m + rq_off);                               // nr_max
+        int64_t* rpre = rq0 + nr_max;                                                  // nr_max + 1
+        int64_t* rrel = rpre + nr_max + 1;                                             // nr_max
+        __shared__ int s_rel[kMsNT + 1];
+        __shared__ int64_t s_bo[kMsNT + 1];  // the extra slot keeps the staging branch-free
+        __shared__ double s_a[kMsNT + 1];
+        // per row of the tile: first entry, entry count, and the tile-relative
+        // position of the row's InterOffsets origin
+        for (int j = tt; j < nr_max; j += kMsNT) {
+            const int64_t r = r0 + j;
+            int64_t cnt = 0, qs = 0, rel = 0;
+            if (r < g.nrows && rb[j] < g1) {
+                qs = (j == 0) ? fs.tile_q0[blockIdx.x] : fs.hq0[r];
+                int64_t qe = fs.hq1[r];
+                if (blockIdx.x + 1 < fs.nblocks && fs.tile_r0[blockIdx.x + 1] == r)
+                    qe = fs.tile_q0[blockIdx.x + 1] + 1;
+                cnt = qe > qs ? qe - qs : 0;
+                rel = rb[j] - g0 - fs.hs0[r];
+            }
+            rq0[j] = qs;
+            rpre[j + 1] = cnt;  // prefix formed below
+            rrel[j] = rel;
+        }
+        __syncthreads();
+        if (tt == 0) {
+            rpre[0] = 0;
+            for (int j = 0; j < nr_max; ++j) rpre[j + 1] += rpre[j];
+        }
+        __syncthreads();
+        const int64_t E = rpre[nr_max];
+        // entries in rounds of kMsNT; a round covers the elements from its
+        // first entry's start to the next round's first entry's start
+        for (int64_t eb = 0; eb < E; eb += kMsNT) {
+            for (int x = tt; x <= kMsNT; x += kMsNT) {
+                const int64_t e = eb + x;
+                int cs = n_wg;
+                if (e < E) {
+                    int j = 0;
+                    while (rpre[j + 1] <= e) ++j;
+                    const int64_t q = rq0[j] + (e - rpre[j]);
+                    // the three loads depend on q only: issue them together
+                    const int64_t sq = fs.S[q];
+                    const int64_t eq = fs.ebo[q];
+                    const double aq = fs.Aval[q];
+                    const int64_t rs = rrel[j] + sq;
+                    cs = (int)(rs < 0 ? 0 : (rs > n_wg ? n_wg : rs));
+                    s_bo[x] = eq + (cs - rs);
+                    s_a[x] = aq;
+                }
+                s_rel[x] = cs;
+            }
+            __syncthreads();
+            const int nst = (int)min((int64_t)kMsNT, E - eb);
+            const int lo = s_rel[0], hi = s_rel[kMsNT];
+            // B indices of this round's elements from LDS first, then every
+            // load at once, then the products (a load per element waited on
+            // in turn would serialise the round's latency kMsK times)
+            int64_t bi[kMsK];
+            double av[kMsK];
+            int j = 0;
+#pragma unroll
+            for (int k = 0; k < kMsK; ++k) {
+                const int t = k * kMsNT + tt;
+                bi[k] = -1;
+                if (t >= lo && t < hi) {
+                    int jh = nst;  // largest j with s_rel[j] <= t, searched in [j, jh)
+                    while (jh - j > 1) {
+                        const int mid = (j + jh) >> 1;
+                        if (s_rel[mid] <= t) j = mid; else jh = mid;
+                    }
+                    bi[k] = s_bo[j] + (t - s_rel[j]);
+                    av[k] = s_a[j];
+                }
+            }
+            int32_t bc[kMsK];
+            double bv[kMsK];
+#pragma unroll
+            for (int k = 0; k < kMsK; ++k) {
+                if (bi[k] >= 0) {
+                    bc[k] = fs.Bcol[bi[k]];
+                    bv[k] = fs.Bval[bi[k]];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kMsK; ++k) {
+                if (bi[k] >= 0) {
+                    col[k] = bc[k];
+                    val[k] = av[k] * bv[k];
+                }
+            }
+            __syncthreads();
+        }
+    }
+
     // 1. load, key, rank within the wave by ballot matching
     int nbits = 0;
     while ((1 << nbits) < nkeys) ++nbits;
-    int32_t col[kMsK];
-    double val[kMsK];
     int key[kMsK];
     int rank[kMsK];
 #pragma unroll
     for (int k = 0; k < kMsK; ++k) {
         int64_t t = g0 + (int64_t)k * kMsNT + tt;
         key[k] = -1;
-        if (t < g1) {
-            col[k] = in_col[t];
-            if constexpr (NUM) val[k] = in_val[t];
+        if constexpr (!FUSED) {
+            if (t < g1) {
+                col[k] = in_col[t];
+                if constexpr (NUM) val[k] = in_val[t];
+            }
         }
     }
     int lr = 0;
@@ -454,8 +586,7 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
             const int v = loff[x];
             loff[x] = pre;
             if (v) {
-                const int64_t nat = (r0 + x / g.nch) * g.nch + (x & mask);
-                const int p = pos_of[nat];
+                const int p = pos_sh[x];
                 const int64_t got = (int64_t)atomicAdd(&cursor[p], (unsigned long long)v) - pre;
                 if (x == k0) {
                     pend_v = got;
@@ -495,33 +626,94 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
     }
 }
 
-static size_t ms_lds(int64_t epb, int nr_max, int nch, bool num, int nw) {
+static size_t ms_lds(int64_t epb, int nr_max, int nch, bool num, int nw, bool fused) {
     size_t nkeys = (size_t)nr_max * nch;
-    return nkeys * 8 + (size_t)(nr_max + 1) * 8 + (num ? (size_t)epb * 8 : 0) +
-           (size_t)nw * nkeys * 4 + (nkeys + 1) * 4 + (size_t)epb * 4 + (size_t)epb * 2 + 8;
+    size_t b = nkeys * 8 + (size_t)(nr_max + 1) * 8 + (num ? (size_t)epb * 8 : 0) +
+               (size_t)nw * nkeys * 4 + (nkeys + 1) * 4 + (size_t)epb * 4 + (size_t)epb * 2 + 8;
+    b += nkeys * 4 + 4;                                // key positions (+ pad)
+    if (fused) b += 8 + (size_t)(3 * nr_max + 1) * 8;  // pad + per-row entry ranges
+    return b;
 }
 
-template <bool NUM, bool OUT16, int NT, int K>
+// C-hat entry holding every tile's first product: the tile's first row is
+// tile_r0[t]; inside the row the entry is found from InterOffsets.
+__global__ void k_fused_tile_entries(const int64_t* chat_rp, const int64_t* hq0,
+                                     const int64_t* hq1, const int64_t* hs0, const int64_t* S,
+                                     const int64_t* tile_r0, int64_t epb, int64_t nblocks,
+                                     int64_t* tile_q0) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nblocks) return;
+    const int64_t r = tile_r0[t];
+    const int64_t target = hs0[r] + (t * epb - chat_rp[r]);
+    tile_q0[t] = upper_index(S, hq0[r], hq1[r], target);
+}
+
+// Per heavy row: its A entry range and InterOffsets at its first entry.
+__global__ void k_heavy_row_info(const int64_t* Arp, const int64_t* S, const int32_t* hrows,
+                                 int64_t H, int64_t* hq0, int64_t* hq1, int64_t* hs0) {
+    const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (h >= H) return;
+    const int32_t i = hrows[h];
+    const int64_t a0 = Arp[i];
+    hq0[h] = a0;
+    hq1[h] = Arp[i + 1];
+    hs0[h] = S[a0];
+}
+
+// Per A entry: the first entry of the B row it multiplies.
+__global__ void k_entry_bstart(const int32_t* Acol, const int64_t* Brp, int64_t nnz,
+                               int64_t* ebo) {
+    int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (; q < nnz; q += stride) ebo[q] = Brp[Acol[q]];
+}
+
+void fused_setup(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
+                 int64_t H, int64_t* hq0, int64_t* hq1, int64_t* hs0, int64_t* ebo,
+                 hipStream_t st) {
+    if (H > 0) {
+        hipLaunchKernelGGL(k_heavy_row_info, dim3(grid_1d(ceil_div(H, 256))), dim3(256), 0, st,
+                           A.rp, S, hrows, H, hq0, hq1, hs0);
+        SG_LAUNCH_CHECK();
+    }
+    if (A.nnz > 0) {
+        int64_t blocks = std::min<int64_t>(ceil_div(A.nnz, 256), 8192);
+        hipLaunchKernelGGL(k_entry_bstart, dim3(grid_1d(blocks)), dim3(256), 0, st, A.col, B.rp,
+                           A.nnz, ebo);
+        SG_LAUNCH_CHECK();
+    }
+}
+
+template <bool NUM, bool OUT16, bool FUSED, int NT, int K>
 static void ms_launch(const LevelGeom& g, const int32_t* in_col, const double* in_val,
                       const int32_t* pos_of, int64_t* cursor, int32_t* out_col, double* out_val,
-                      Arena& ar, hipStream_t st) {
+                      FusedSrc fs, Arena& ar, hipStream_t st) {
     int64_t epb = (int64_t)NT * K;
     int nr_max = rows_per_range(epb, g.tau);
-    while (epb > 64 && ms_lds(epb, nr_max, g.nch, NUM, NT / kWave) > 65536) {
+    while (epb > 64 && ms_lds(epb, nr_max, g.nch, NUM, NT / kWave, FUSED) > 65536) {
         epb /= 2;
         nr_max = rows_per_range(epb, g.tau);
     }
     if ((int64_t)nr_max * g.nch > 65535) throw OverflowError("multisplit keys exceed 16 bits");
-    size_t lds = ms_lds(epb, nr_max, g.nch, NUM, NT / kWave);
+    size_t lds = ms_lds(epb, nr_max, g.nch, NUM, NT / kWave, FUSED);
     if (lds > 160 * 1024) throw OverflowError("multisplit local histogram exceeds LDS");
     int64_t blocks = ceil_div(g.total, epb);
     int64_t* tile_r0 = ar.get<int64_t>("ms_tile_r0", (size_t)blocks + 1);
     tile_starts(g.rp, g.nrows, epb, blocks, tile_r0, st);
-    auto kern = k_multisplit<NUM, OUT16, NT, K>;
+    if constexpr (FUSED) {
+        int64_t* tile_q0 = ar.get<int64_t>("ms_tile_q0", (size_t)blocks + 1);
+        hipLaunchKernelGGL(k_fused_tile_entries, dim3(grid_1d(ceil_div(blocks, 256))), dim3(256), 0,
+                           st, g.rp, fs.hq0, fs.hq1, fs.hs0, fs.S, tile_r0, epb, blocks, tile_q0);
+        SG_LAUNCH_CHECK();
+        fs.tile_q0 = tile_q0;
+        fs.tile_r0 = tile_r0;
+        fs.nblocks = blocks;
+    }
+    auto kern = k_multisplit<NUM, OUT16, FUSED, NT, K>;
     SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds));
     hipLaunchKernelGGL(kern, dim3(grid_1d(blocks)), dim3(NT), lds, st, g, in_col, in_val, pos_of,
-                       (unsigned long long*)cursor, out_col, out_val, tile_r0, epb, nr_max);
+                       (unsigned long long*)cursor, out_col, out_val, tile_r0, epb, nr_max, fs);
     SG_LAUNCH_CHECK();
 }
 
@@ -535,13 +727,32 @@ void multisplit(const LevelGeom& g, const int32_t* in_col, const double* in_val,
                 bool out16, Arena& ar, hipStream_t st) {
     if (g.total <= 0) return;
     if (out16 && g.shift > 16) throw std::logic_error("16-bit columns need chunks <= 2^16 wide");
+    FusedSrc none{};
     if (out_val) {
-        if (out16) ms_launch<true, true, kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, out_val, ar, st);
-        else ms_launch<true, false, kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, out_val, ar, st);
+        if (out16) ms_launch<true, true, false, kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, out_val, none, ar, st);
+        else ms_launch<true, false, false, kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, out_val, none, ar, st);
     } else {
-        if (out16) ms_launch<false, true, kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, nullptr, ar, st);
-        else ms_launch<false, false, kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, nullptr, ar, st);
+        if (out16) ms_launch<false, true, false, kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, nullptr, none, ar, st);
+        else ms_launch<false, false, false, kMsNT, kMsK>(g, in_col, in_val, pos_of, cursor, out_col, nullptr, none, ar, st);
     }
+}
+
+void expand_multisplit(const LevelGeom& g, const FusedRows& fr, const DevCSR& A, const DevCSR& B,
+                       const int64_t* S, const int32_t* pos_of, int64_t* cursor, int32_t* out_col,
+                       double* out_val, bool out16, Arena& ar, hipStream_t st) {
+    if (g.total <= 0) return;
+    if (out16 && g.shift > 16) throw std::logic_error("16-bit columns need chunks <= 2^16 wide");
+    FusedSrc fs{};
+    fs.hq0 = fr.hq0;
+    fs.hq1 = fr.hq1;
+    fs.hs0 = fr.hs0;
+    fs.ebo = fr.ebo;
+    fs.S = S;
+    fs.Aval = A.val;
+    fs.Bcol = B.col;
+    fs.Bval = B.val;
+    if (out16) ms_launch<true, true, true, kMsNT, kMsK>(g, nullptr, nullptr, pos_of, cursor, out_col, out_val, fs, ar, st);
+    else ms_launch<true, false, true, kMsNT, kMsK>(g, nullptr, nullptr, pos_of, cursor, out_col, out_val, fs, ar, st);
 }
 
 // First column of every chunk of a level: level 0 chunk c of a row starts at

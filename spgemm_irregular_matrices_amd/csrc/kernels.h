@@ -142,6 +142,21 @@ void reord_rowptr(const int64_t* counts, const int32_t* inv, int64_t npos, int64
 void multisplit(const LevelGeom& g, const int32_t* in_col, const double* in_val,
                 const int32_t* pos_of, int64_t* cursor, int32_t* out_col, double* out_val,
                 bool out16, Arena& ar, hipStream_t st);
+// Outer product and first multisplit level in one pass (numeric): the
+// products of the C-hat rows g.rp are formed from A, B and InterOffsets S
+// tile by tile and multisplit as they are formed, without writing C-hat.
+struct FusedRows {
+    const int64_t* hq0;  // per C-hat row of the batch: first A entry
+    const int64_t* hq1;  // one past the last A entry
+    const int64_t* hs0;  // InterOffsets at the first entry
+    const int64_t* ebo;  // per A entry (all of A): first entry of its B row
+};
+void fused_setup(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
+                 int64_t H, int64_t* hq0, int64_t* hq1, int64_t* hs0, int64_t* ebo,
+                 hipStream_t st);
+void expand_multisplit(const LevelGeom& g, const FusedRows& fr, const DevCSR& A, const DevCSR& B,
+                       const int64_t* S, const int32_t* pos_of, int64_t* cursor, int32_t* out_col,
+                       double* out_val, bool out16, Arena& ar, hipStream_t st);
 // out[p*nch + c] = (parent_inv ? parent_base[parent_inv[p]] : 0) + c*width.
 void chunk_colbase(int64_t nparents, int nch, int64_t width, const int32_t* parent_inv,
                    const int32_t* parent_base, int32_t* out, hipStream_t st);

@@ -103,9 +103,12 @@ struct spgemm_plan_s {
     size_t evnext = 0;
     std::vector<Ev> evs;
     bool fused_sym = false;
+    bool fused_num = false;  // numeric level 0 forms its products itself (no C-hat)
     // debug dumps (kept for single-batch products)
     bool dbg_valid = false;
-    bool dbg_has_val = false;
+    bool dbg_chat = false;  // C-hat was dumped (separate outer product only)
+    bool dbg_has_val = false;       // levels were dumped with values
+    bool dbg_chat_val = false;      // C-hat was dumped with values
 };
 
 namespace {
@@ -262,7 +265,8 @@ void debug_copy_chat(spgemm_plan p, const BatchState& bt, const int64_t* crp, co
                        key);
     SG_LAUNCH_CHECK();
     p->dbg_valid = true;
-    p->dbg_has_val = val != nullptr;
+    p->dbg_chat = true;
+    p->dbg_chat_val = val != nullptr;
 }
 
 void debug_copy_level(spgemm_plan p, int l, const LevelState& S_l, const int64_t* rp,
@@ -274,6 +278,8 @@ void debug_copy_level(spgemm_plan p, int l, const LevelState& S_l, const int64_t
     copy<int32_t>(ar.get<int32_t>(b + "_col", (size_t)nnz), col, nnz, st);
     if (val) copy<double>(ar.get<double>(b + "_val", (size_t)nnz), val, nnz, st);
     int64_t* key = ar.get<int64_t>(b + "_key", (size_t)S_l.npos + 1);
+    p->dbg_valid = true;
+    p->dbg_has_val = val != nullptr;
     if (S_l.npos > 0) {
         hipLaunchKernelGGL(k_i32_to_i64, dim3(grid_1d(ceil_div(S_l.npos, 256))), dim3(256), 0, st,
                            inv, S_l.npos, key);
@@ -575,6 +581,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     Arena& ar = p->ar;
     p->ready = false;
     p->dbg_valid = false;
+    p->dbg_chat = false;
     p->evnext = 0;
     p->evs.clear();
     memset(&p->stats, 0, sizeof(p->stats));
@@ -665,6 +672,17 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
         const bool fused_fits = heavy_symbolic_lds(q.ppow, req) <= (size_t)p->dev_lds &&
                                 B.n * req <= (int64_t(1) << 28);
         p->fused_sym = p->opt.symbolic_mode == 1 || (p->opt.symbolic_mode == 0 && fused_fits);
+        p->fused_num = q.nlevels > 0 && (p->opt.numeric_mode == 1 ||
+                                         (p->opt.numeric_mode == 0 && !p->opt.debug_dump));
+        // the masked CSC feeds the separate outer product only
+        const bool need_csc = !p->fused_num || !p->fused_sym;
+        if (p->fused_num) {
+            PhaseScope ps(p, 0, SPGEMM_PHASE_CSR_TO_CSC, st);
+            fused_setup(A, B, S, hrows, p->H, ar.get<int64_t>("h_q0", (size_t)p->H),
+                        ar.get<int64_t>("h_q1", (size_t)p->H), ar.get<int64_t>("h_s0", (size_t)p->H),
+                        ar.get<int64_t>("ebo", (size_t)A.nnz + 1), st);
+            add_bytes(p, 0, SPGEMM_PHASE_CSR_TO_CSC, 28.0 * p->H + 20.0 * A.nnz);
+        }
         if (p->fused_sym && !fused_fits)
             throw OverflowError("fused symbolic pass needs more LDS than the device has");
         int64_t* elem_fin = nullptr;
@@ -687,20 +705,25 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
                 PhaseScope ps(p, 0, SPGEMM_PHASE_CSR_TO_CSC, st);
                 bt.ent0 = ent_cur;
                 bt.P0 = P_cur;
-                bt.ne = masked_csr2csc(A, B, S, hrows + bt.h0, R0, chat_rp + bt.h0, bt.chat_base,
-                                       c.ent_k + ent_cur, c.ent_q + ent_cur, c.ent_dest + ent_cur,
-                                       p->cap_ent - ent_cur, c.P + P_cur, &bt.npieces, ar, st);
-                ent_cur += bt.ne;
-                P_cur += bt.ne + 1;
                 bt.tile0 = tile_cur;
-                if (tile_cur + expand_tiles(bt.npieces) + 1 > p->cap_tiles)
-                    throw std::logic_error("expand tile capacity");
-                expand_tile_starts(c.P + bt.P0, bt.ne, bt.npieces, c.tiles + bt.tile0, st);
-                tile_cur += expand_tiles(bt.npieces) + 1;
+                bt.ne = 0;
+                bt.npieces = 0;
+                if (need_csc) {
+                    bt.ne = masked_csr2csc(A, B, S, hrows + bt.h0, R0, chat_rp + bt.h0,
+                                           bt.chat_base, c.ent_k + ent_cur, c.ent_q + ent_cur,
+                                           c.ent_dest + ent_cur, p->cap_ent - ent_cur,
+                                           c.P + P_cur, &bt.npieces, ar, st);
+                    ent_cur += bt.ne;
+                    P_cur += bt.ne + 1;
+                    if (tile_cur + expand_tiles(bt.npieces) + 1 > p->cap_tiles)
+                        throw std::logic_error("expand tile capacity");
+                    expand_tile_starts(c.P + bt.P0, bt.ne, bt.npieces, c.tiles + bt.tile0, st);
+                    tile_cur += expand_tiles(bt.npieces) + 1;
+                    add_bytes(p, 0, SPGEMM_PHASE_CSR_TO_CSC, 36.0 * bt.ne);
+                }
                 bt.crp0 = crp_cur;
                 rebase(chat_rp + bt.h0, R0 + 1, bt.chat_base, c.crp + bt.crp0, st);
                 crp_cur += R0 + 1;
-                add_bytes(p, 0, SPGEMM_PHASE_CSR_TO_CSC, 36.0 * bt.ne);
             }
             if (p->fused_sym) {
                 if (q.nlevels > 0)
@@ -784,8 +807,14 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
     if (p->H == 0) return;
 
     CscBufs c = csc_bufs(p);
-    int32_t* bufc[2] = {ar.get<int32_t>("buf0c", (size_t)p->maxN), nullptr};
-    double* bufv[2] = {ar.get<double>("buf0v", (size_t)p->maxN), nullptr};
+    // C-hat (buffer 0) is written only by the separate outer product; with
+    // the fused first level, buffer 0 holds level 1's output if there is one
+    int32_t* bufc[2] = {nullptr, nullptr};
+    double* bufv[2] = {nullptr, nullptr};
+    if (!p->fused_num || p->L > 1) {
+        bufc[0] = ar.get<int32_t>("buf0c", (size_t)p->maxN);
+        bufv[0] = ar.get<double>("buf0v", (size_t)p->maxN);
+    }
     if (q.nlevels > 0) {
         bufc[1] = ar.get<int32_t>("buf1c", (size_t)p->maxN);
         bufv[1] = ar.get<double>("buf1v", (size_t)p->maxN);
@@ -793,12 +822,14 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
     const bool dump = p->opt.debug_dump && p->batches.size() == 1;
     for (const BatchState& bt : p->batches) {
         const int64_t R0 = bt.h1 - bt.h0;
-        {
-            PhaseScope ps(p, 1, SPGEMM_PHASE_OUTER_PROD, st);
-            expand(expand_args(p, bt, A, B, bufc[0], bufv[0]), st);
-            add_bytes(p, 1, SPGEMM_PHASE_OUTER_PROD, 12.0 * bt.N + 28.0 * bt.ne);
+        if (!p->fused_num) {
+            {
+                PhaseScope ps(p, 1, SPGEMM_PHASE_OUTER_PROD, st);
+                expand(expand_args(p, bt, A, B, bufc[0], bufv[0]), st);
+                add_bytes(p, 1, SPGEMM_PHASE_OUTER_PROD, 12.0 * bt.N + 28.0 * bt.ne);
+            }
+            if (dump) debug_copy_chat(p, bt, c.crp + bt.crp0, bufc[0], bufv[0], hrows + bt.h0, st);
         }
-        if (dump) debug_copy_chat(p, bt, c.crp + bt.crp0, bufc[0], bufv[0], hrows + bt.h0, st);
         if (q.nlevels == 0) {
             ChunkItems ci{};
             ci.hash_top_logS = q.hash_top_logS;
@@ -831,9 +862,24 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
             const bool c16 = !dump && S_l.nheavy() == 0 && q.width[l] <= (int64_t(1) << 16);
             {
                 PhaseScope ps(p, 1, SPGEMM_PHASE_MULTISPLIT, st);
-                multisplit(g, bufc[in], bufv[in], pos, cursor, bufc[outb], bufv[outb], c16, ar, st);
-                add_bytes(p, 1, SPGEMM_PHASE_MULTISPLIT,
-                          (c16 ? 22.0 : 24.0) * S_l.total_in + 8.0 * (S_l.R + 1));
+                if (l == 0 && p->fused_num) {
+                    // products formed in the tile: the Ĉreord write, one read
+                    // of the B rows and the row pointers are the minimum
+                    FusedRows fr{ar.get<int64_t>("h_q0", (size_t)p->H) + bt.h0,
+                                 ar.get<int64_t>("h_q1", (size_t)p->H) + bt.h0,
+                                 ar.get<int64_t>("h_s0", (size_t)p->H) + bt.h0,
+                                 ar.get<int64_t>("ebo", (size_t)A.nnz + 1)};
+                    expand_multisplit(g, fr, A, B, S, pos, cursor, bufc[outb], bufv[outb], c16,
+                                      ar, st);
+                    add_bytes(p, 1, SPGEMM_PHASE_MULTISPLIT,
+                              (c16 ? 10.0 : 12.0) * S_l.total_in + 12.0 * B.nnz +
+                                  8.0 * (S_l.R + 1));
+                } else {
+                    multisplit(g, bufc[in], bufv[in], pos, cursor, bufc[outb], bufv[outb], c16,
+                               ar, st);
+                    add_bytes(p, 1, SPGEMM_PHASE_MULTISPLIT,
+                              (c16 ? 22.0 : 24.0) * S_l.total_in + 8.0 * (S_l.R + 1));
+                }
             }
             if (dump) debug_copy_level(p, l, S_l, rp, bufc[outb], bufv[outb], inv, st);
             {
@@ -900,6 +946,8 @@ SPGEMM_API int spgemm_plan_create(spgemm_plan* out, const spgemm_options* opt) {
     if (opt) o = *opt;
     if (o.lds_budget_bytes < 0 || o.tau_override < 0 || o.chunk_width_override < 0 ||
         o.nchunks_cap < 0 || o.max_batch_products < 0)
+        return SPGEMM_ERR_INVALID_ARG;
+    if (o.symbolic_mode < 0 || o.symbolic_mode > 2 || o.numeric_mode < 0 || o.numeric_mode > 2)
         return SPGEMM_ERR_INVALID_ARG;
     if (o.chunk_width_override > 0 &&
         (o.chunk_width_override < 32 || (o.chunk_width_override & (o.chunk_width_override - 1))))
@@ -1013,12 +1061,13 @@ SPGEMM_API int spgemm_plan_debug(spgemm_plan p, int which, spgemm_debug_matrix* 
         const BatchState& bt = p->batches[0];
         memset(out, 0, sizeof(*out));
         if (which == -1) {
+            if (!p->dbg_chat) return SPGEMM_ERR_INVALID_ARG;
             const int64_t R = bt.h1 - bt.h0;
             out->nrows = R;
             out->nnz = bt.N;
             out->rowptr = ar.get<int64_t>("dbg_m1_rp", (size_t)R + 1);
             out->col = ar.get<int32_t>("dbg_m1_col", (size_t)bt.N);
-            out->val = p->dbg_has_val ? ar.get<double>("dbg_m1_val", (size_t)bt.N) : nullptr;
+            out->val = p->dbg_chat_val ? ar.get<double>("dbg_m1_val", (size_t)bt.N) : nullptr;
             out->row_key = ar.get<int64_t>("dbg_m1_key", (size_t)R + 1);
             out->chunk_width = p->prm.ppow;
             return SPGEMM_OK;

@@ -42,8 +42,9 @@ def test_struct_layout_matches_header(tmp_path):
 int main(void) {
   printf("%zu %zu %zu %zu\n", sizeof(spgemm_csr), sizeof(spgemm_options),
          sizeof(spgemm_stats), sizeof(spgemm_debug_matrix));
-  printf("%zu %zu %zu %zu\n", offsetof(spgemm_stats, phase_ms), offsetof(spgemm_stats, lds_bytes),
-         offsetof(spgemm_options, max_batch_products), offsetof(spgemm_options, symbolic_mode));
+  printf("%zu %zu %zu %zu %zu\n", offsetof(spgemm_stats, phase_ms), offsetof(spgemm_stats, lds_bytes),
+         offsetof(spgemm_options, max_batch_products), offsetof(spgemm_options, symbolic_mode),
+         offsetof(spgemm_options, numeric_mode));
   return 0;
 }''')
     exe = tmp_path / "layout"
@@ -58,6 +59,7 @@ int main(void) {
     assert sizes[5] == binding.Stats.lds_bytes.offset
     assert sizes[6] == binding.Options.max_batch_products.offset
     assert sizes[7] == binding.Options.symbolic_mode.offset
+    assert sizes[8] == binding.Options.numeric_mode.offset
 
 
 def test_no_gpu_call_fails_loudly():

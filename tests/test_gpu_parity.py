@@ -45,7 +45,12 @@ def test_rmat10_default_and_all_light():
     compare(A, A, rp, col, val)
 
 
-@pytest.mark.parametrize("mode", [1, 2])  # fused bitmap symbolic / multisplit symbolic
+# (symbolic, numeric) modes: fused bitmap symbolic or multisplit symbolic;
+# products formed inside the first multisplit level or a separate C-hat
+MODES = [(1, 1), (2, 2), (1, 2)]
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("tau,width,cap,levels", [
     (64, 0, 0, 0),        # heavy rows accumulate densely without any multisplit
     (64, 256, 32, 1),     # one level of 4 chunks
@@ -56,7 +61,7 @@ def test_rmat10_default_and_all_light():
 def test_rmat10_forced_heavy(tau, width, cap, levels, mode):
     A = _rmat10()
     rp, col, val, st = run_gpu(A, A, tau_override=tau, chunk_width_override=width,
-                               nchunks_cap=cap, symbolic_mode=mode)
+                               nchunks_cap=cap, symbolic_mode=mode[0], numeric_mode=mode[1])
     assert st["heavy_rows"] > 0
     assert st["nlevels"] == levels, st
     compare(A, A, rp, col, val)
@@ -135,28 +140,42 @@ def test_fig1_chunks_on_wider_columns():
     compare(A, B, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy())
 
 
-def test_chat_stage_matches_oracle():
-    """C-hat rows are bit-exact against the oracle's expansion, in Gustavson order."""
+@pytest.mark.parametrize("numeric_mode", [2, 1])
+def test_chat_stage_matches_oracle(numeric_mode):
+    """C-hat rows are bit-exact against the oracle's expansion, in Gustavson order,
+    and level 0 holds each heavy row's products split by column range.
+
+    With the products formed inside the first multisplit level (numeric
+    mode 1) C-hat is never written: its columns come from the multisplit
+    symbolic pass and carry no values.
+    """
     A = synth.random_csr(400, 300, seed=41, value_seed=42, mean_len=10, skew=1.2)
     B = synth.random_csr(300, 500, seed=43, value_seed=44, mean_len=8, skew=1.2)
     import torch
     from spgemm_irregular_matrices_amd import binding
     dA, dB = binding.DeviceCSR.from_host(A), binding.DeviceCSR.from_host(B)
-    with binding.Plan(tau_override=40, chunk_width_override=64, nchunks_cap=2,
-                      debug_dump=True, symbolic_mode=2) as p:
+    tau = 40
+    with binding.Plan(tau_override=tau, chunk_width_override=64, nchunks_cap=2,
+                      debug_dump=True, symbolic_mode=2, numeric_mode=numeric_mode) as p:
         C = p.multiply(dA, dB)
         torch.cuda.synchronize()
-        chat = p.debug(-1)
         levels = [p.debug(l) for l in range(p.stats()["nlevels"])]
-    rows = chat["row_key"]
+        chat = p.debug(-1)
+    u = oracle.row_products(A, B)
+    rows = np.nonzero(u > tau)[0]
     rp, col, val = stages.expand(A, B, rows)
+    assert np.array_equal(chat["row_key"], rows)
     assert np.array_equal(chat["rowptr"], rp)
     assert np.array_equal(chat["col"], col)
-    assert np.array_equal(chat["val"], val)
+    if numeric_mode == 2:
+        assert np.array_equal(chat["val"], val)
+    else:
+        assert chat["val"] is None
     # level 0: each chunk is its parent row's entries in that column range
     l0 = levels[0]
     W = l0["chunk_width"]
     nch = 512 // W  # B.ncols=500 rounds up to 512
+    seen = 0
     for r in range(l0["rowptr"].size - 1):
         key = int(l0["row_key"][r])
         h, c = divmod(key, nch)
@@ -165,10 +184,12 @@ def test_chat_stage_matches_oracle():
         exp = sorted(zip(col[s:e][m].tolist(), val[s:e][m].tolist()))
         a, b = l0["rowptr"][r], l0["rowptr"][r + 1]
         assert sorted(zip(l0["col"][a:b].tolist(), l0["val"][a:b].tolist())) == exp
+        seen += b - a
+    assert seen == rp[-1]
     compare(A, B, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy())
 
 
-@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("tau", [6826, 1, 20, 300])
 @pytest.mark.parametrize("seed", [1, 2])
 def test_random_skewed_paths(tau, seed, mode):
@@ -177,26 +198,27 @@ def test_random_skewed_paths(tau, seed, mode):
     B = synth.random_csr(500, 700, seed=seed + 20, value_seed=seed + 30, mean_len=9, skew=1.1,
                          empty_frac=0.05)
     rp, col, val, st = run_gpu(A, B, tau_override=tau, chunk_width_override=32, nchunks_cap=4,
-                               symbolic_mode=mode)
+                               symbolic_mode=mode[0], numeric_mode=mode[1])
     compare(A, B, rp, col, val)
 
 
-@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("budget,width,cap", [(1, 64, 4), (700, 64, 4), (5000, 32, 2), (20000, 0, 0)])
 def test_row_batches(budget, width, cap, mode):
     """Heavy rows processed in batches of bounded products (one row per batch at budget 1)."""
     A = synth.rmat(11, 8, seed=121, value_seed=122)
     rp, col, val, st = run_gpu(A, A, tau_override=64, chunk_width_override=width, nchunks_cap=cap,
-                               max_batch_products=budget, symbolic_mode=mode)
+                               max_batch_products=budget, symbolic_mode=mode[0],
+                               numeric_mode=mode[1])
     assert st["nbatches"] > 1
     compare(A, A, rp, col, val)
 
 
 def test_small_integer_values_exact():
     A = synth.rmat(11, 8, seed=61, value_seed=62, values="int")
-    for mode in (1, 2):
+    for mode in MODES:
         rp, col, val, st = run_gpu(A, A, tau_override=100, chunk_width_override=64, nchunks_cap=4,
-                                   symbolic_mode=mode)
+                                   symbolic_mode=mode[0], numeric_mode=mode[1])
         assert st["heavy_rows"] > 0 and st["nlevels"] >= 2
         compare(A, A, rp, col, val, exact_values=True)
     rp, col, val, st = run_gpu(A, A)
@@ -342,6 +364,7 @@ def test_error_paths():
         with pytest.raises(binding.SpgemmError) as e:
             p.numeric(A51, dBg, C.rowptr, C.col, C.val)
         assert e.value.code == -6
-    with pytest.raises(binding.SpgemmError) as e:
-        binding.Plan(chunk_width_override=48)
-    assert e.value.code == -1
+    for kw in ({"chunk_width_override": 48}, {"numeric_mode": 3}, {"symbolic_mode": -1}):
+        with pytest.raises(binding.SpgemmError) as e:
+            binding.Plan(**kw)
+        assert e.value.code == -1
