@@ -79,11 +79,15 @@ typedef struct {
     int64_t max_batch_products;   /* heavy products per row batch; 0 = one batch          */
     int32_t symbolic_mode;        /* heavy-row symbolic pass: 0 = auto, 1 = fused per-row
                                      bitmap pass, 2 = multisplit of column-only C-hat      */
-    int32_t numeric_mode;         /* heavy-row numeric pass: 0 = auto (1, or 2 when
-                                     debug_dump is set, so that C-hat can be dumped),
+    int32_t numeric_mode;         /* heavy-row numeric pass: 0 = auto (3 where it applies,
+                                     else 1; 2 when debug_dump is set, so that C-hat and
+                                     the levels can be dumped),
                                      1 = products formed inside the first multisplit level
                                      (C-hat is never written), 2 = outer product into C-hat
-                                     then multisplit                                       */
+                                     then multisplit, 3 = direct: B's rows split into the
+                                     final chunks once, and every (heavy row, chunk) item
+                                     accumulated straight from A and the split B (needs
+                                     the fused symbolic pass; else 1 runs)                 */
 } spgemm_options;
 
 /* Phases, named after the gMAGNUS page's phase breakdown (Section IV-C,
@@ -131,6 +135,10 @@ typedef struct {
     int64_t lds_bytes;            /* s_LM used                                    */
     int64_t light_rows;           /* rows with 0 < u(i) <= tau                    */
     int64_t light_products;
+    int32_t numeric_path;         /* heavy rows' numeric pass that ran: 0 = none,
+                                     1 = first level formed in the multisplit tiles,
+                                     2 = outer product into C-hat, 3 = direct          */
+    int32_t reserved_stats;
 } spgemm_stats;
 
 /* One intermediate matrix kept by a plan with debug_dump = 1. */

@@ -67,7 +67,8 @@ class Stats(ctypes.Structure):
                 ("phase_launches", (ctypes.c_int64 * NPH) * 2),
                 ("phase_bytes", (ctypes.c_double * NPH) * 2),
                 ("lds_bytes", ctypes.c_int64), ("light_rows", ctypes.c_int64),
-                ("light_products", ctypes.c_int64)]
+                ("light_products", ctypes.c_int64), ("numeric_path", ctypes.c_int32),
+                ("reserved_stats", ctypes.c_int32)]
 
 
 class DebugMatrix(ctypes.Structure):
@@ -236,7 +237,8 @@ class Plan:
         d = {k: getattr(s, k) for k in ("nrows", "ncols_c", "nnz_c", "sum_products",
                                          "max_products", "heavy_rows", "heavy_products", "tau",
                                          "final_chunk_width", "nlevels", "nbatches", "chat_bytes",
-                                         "lds_bytes", "light_rows", "light_products")}
+                                         "lds_bytes", "light_rows", "light_products",
+                                         "numeric_path")}
         d["vchunks"] = [int(s.vchunks[i]) for i in range(L)]
         d["level_in_elems"] = [int(s.level_in_elems[i]) for i in range(L)]
         d["level_heavy_chunks"] = [int(s.level_heavy_chunks[i]) for i in range(L)]

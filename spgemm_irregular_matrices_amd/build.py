@@ -13,7 +13,7 @@ OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libspgemm.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["setup.hip", "heavy.hip", "accum.hip", "plan.hip"]
+SOURCES = ["setup.hip", "heavy.hip", "accum.hip", "direct.hip", "plan.hip"]
 ARCH = os.environ.get("SPGEMM_OFFLOAD_ARCH", "gfx950")
 
 

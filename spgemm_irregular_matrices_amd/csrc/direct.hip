@@ -1,0 +1,457 @@
+// Direct accumulation of the heavy rows (numeric pass).
+//
+// The chunk of a product a_ik * b_kj is fixed by j alone, so the
+// column-range split that the gMAGNUS page applies to C-hat (Section III-C,
+// hierarchical multisplit) can be applied to B instead: every B row is
+// partitioned once, stably, into the final chunks (slots of width W), and
+// bsplit[k][s] records where slot s starts inside row k. The products of
+// heavy row i that fall into chunk s are then the slices [bsplit[k][s],
+// bsplit[k][s+1]) of the B rows k of row i's entries, each scaled by its
+// a_ik. One work group per (heavy row, chunk) item forms exactly those
+// products and accumulates them in LDS with the page's accumulators
+// (Section III-E): the bitmap-rank accumulator for items of at most
+// kDirectDense products, the dense window above that. C-hat and
+// C-hat-reord are never written; the per-item product and distinct-column
+// counts come from the fused symbolic pass.
+#include "accum_util.h"
+#include "kernels.h"
+#include "primitives.h"
+
+namespace sg {
+
+// ---------------------------------------------------------------- B split
+// bsplit[k*(req+1) + s] = entries of B row k in slots before s (so
+// bsplit[k*(req+1) + req] is the row length).
+__global__ void k_bsplit_prefix(const int32_t* bslot, int64_t nb, int req, int32_t* bsplit) {
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= nb) return;
+    const int32_t* src = bslot + k * req;
+    int32_t* dst = bsplit + k * (req + 1);
+    int32_t run = 0;
+    for (int s = 0; s < req; ++s) {
+        dst[s] = run;
+        run += src[s];
+    }
+    dst[req] = run;
+}
+
+// One wavefront per B row: entries are placed slot by slot, in row order
+// within a slot. The wave ranks each batch of 64 entries by peeling one
+// distinct slot at a time (ballot of the lanes holding the first remaining
+// lane's slot); running slot offsets live in the wave's LDS.
+constexpr int kBpartNT = 256;
+
+__global__ __launch_bounds__(kBpartNT) void k_bpartition(const int64_t* brp, const int32_t* bcol,
+                                                         int64_t nb, int logW, int req,
+                                                         const int32_t* bsplit, int64_t* bperm,
+                                                         uint16_t* bcol16) {
+    extern __shared__ int lds_b[];
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    int* run = lds_b + w * req;
+    const int64_t k = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    if (k >= nb) return;  // whole waves leave together; no block barrier below
+    const int32_t* bs = bsplit + k * (req + 1);
+    for (int s = lane; s < req; s += kWave) run[s] = bs[s];
+    const int64_t e0 = brp[k], e1 = brp[k + 1];
+    const uint32_t wmask = (1u << logW) - 1u;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    for (int64_t eb = e0; eb < e1; eb += kWave) {
+        const int64_t e = eb + lane;
+        int32_t c = 0;
+        int s = -1;
+        if (e < e1) {
+            c = bcol[e];
+            s = (int)((uint32_t)c >> logW);
+        }
+        uint64_t act = __ballot(s >= 0);
+        while (act) {
+            const int leader = __builtin_ctzll(act);
+            const int ls = __builtin_amdgcn_readlane(s, leader);
+            const uint64_t m = __ballot(s == ls);
+            const int base = run[ls];
+            if (s == ls) {
+                const int64_t pos = e0 + base + __popcll(m & lt);
+                bperm[pos] = e;
+                bcol16[pos] = (uint16_t)((uint32_t)c & wmask);
+            }
+            if (lane == leader) run[ls] = base + __popcll(m);
+            act &= ~m;
+        }
+    }
+}
+
+void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int32_t* bsplit,
+                    int64_t* bperm, uint16_t* bcol16, hipStream_t st) {
+    if (B.n <= 0) return;
+    if (W > 65536 || req > kDirectMaxSlots) throw std::logic_error("direct split limits");
+    hipLaunchKernelGGL(k_bsplit_prefix, dim3(grid_1d(ceil_div(B.n, 256))), dim3(256), 0, st, bslot,
+                       B.n, req, bsplit);
+    SG_LAUNCH_CHECK();
+    if (B.nnz <= 0) return;
+    const size_t lds = (size_t)(kBpartNT / kWave) * req * 4;
+    SG_HIP(hipFuncSetAttribute((const void*)k_bpartition,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    hipLaunchKernelGGL(k_bpartition, dim3(grid_1d(ceil_div(B.n * kWave, kBpartNT))),
+                       dim3(kBpartNT), lds, st, B.rp, B.col, B.n, ilog2(W), req, bsplit, bperm,
+                       bcol16);
+    SG_LAUNCH_CHECK();
+}
+
+// ---------------------------------------------------------------- offsets
+// off[h*req + s] = C.rowPtr of heavy row h + distinct columns of the row in
+// slots before s (slots are in column order, so this is the item's place in
+// the sorted output row).
+__global__ void k_direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int req,
+                                 const int64_t* dist_fin, int64_t* off) {
+    const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (h >= H) return;
+    int64_t run = C_rp[hrows[h]];
+    for (int s = 0; s < req; ++s) {
+        off[h * req + s] = run;
+        run += dist_fin[h * req + s];
+    }
+}
+
+void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int req,
+                    const int64_t* dist_fin, int64_t* off, hipStream_t st) {
+    if (H <= 0) return;
+    hipLaunchKernelGGL(k_direct_offsets, dim3(grid_1d(ceil_div(H, 256))), dim3(256), 0, st, C_rp,
+                       hrows, H, req, dist_fin, off);
+    SG_LAUNCH_CHECK();
+}
+
+// ---------------------------------------------------------------- item classes
+struct DirectBinOf {
+    const int64_t* elem;
+    __device__ int operator()(int64_t x) const {
+        const int64_t c = elem[x];
+        if (c == 0) return CB_EMPTY;
+        if (c > kDirectDense) return CB_DENSE;
+        if (c <= kHashMaxItems[0]) return CB_H128;
+        if (c <= kHashMaxItems[1]) return CB_H512;
+        if (c <= kHashMaxItems[2]) return CB_H2048;
+        return CB_H8192;
+    }
+};
+
+void direct_classify(const int64_t* elem_fin, int64_t nitems, int32_t* items, int64_t* bins,
+                     Arena& ar, hipStream_t st) {
+    partition(DirectBinOf{elem_fin}, nitems, CB_COUNT, items, (int32_t*)nullptr, bins, ar, st);
+}
+
+// ---------------------------------------------------------------- numeric
+__global__ void k_gather_bval(const int64_t* bperm, const double* bval, int64_t nnz,
+                              double* out) {
+    int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (; j < nnz; j += stride) out[j] = bval[bperm[j]];
+}
+
+void direct_gather_values(const int64_t* bperm, const double* bval, int64_t nnz, double* out,
+                          hipStream_t st) {
+    if (nnz <= 0) return;
+    const int64_t blocks = std::min<int64_t>(ceil_div(nnz, 256), 8192);
+    hipLaunchKernelGGL(k_gather_bval, dim3(grid_1d(blocks)), dim3(256), 0, st, bperm, bval, nnz,
+                       out);
+    SG_LAUNCH_CHECK();
+}
+
+// Staging of one round of an item's A entries (at most NE of them, taken by
+// threads tt < NE): each entry's slice of the item's chunk (its start in the
+// partitioned B and its a value) and the exclusive prefix of slice lengths.
+// Returns the products of the round. Threads past the item's entries add 0.
+template <int TW, int NE>
+__device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int64_t q1, int s,
+                                            int* s_pre, int64_t* s_bo, double* s_a, int* red_sh) {
+    const int tt = threadIdx.x;
+    int len = 0;
+    if (tt < NE && q < q1) {
+        const int32_t k = d.Acol[q];
+        const int64_t eb = d.ebo[q];
+        const double a = d.Aval[q];
+        const int32_t* bs = d.bsplit + (int64_t)k * (d.req + 1) + s;
+        const int32_t lo = bs[0];
+        len = bs[1] - lo;
+        s_bo[tt] = eb + lo;
+        s_a[tt] = a;
+    }
+    int tot;
+    const int pre = team_exclusive_scan<TW>(len, red_sh, &tot);
+    if (tt < NE) s_pre[tt] = pre;
+    __syncthreads();
+    return tot;
+}
+
+// Entry of product p of a round: the last staged entry whose prefix is <= p,
+// searched from `j` up (products are visited in increasing order per thread).
+__device__ __forceinline__ int direct_find(const int* s_pre, int ne, int p, int j) {
+    int jh = ne;
+    while (jh - j > 1) {
+        const int mid = (j + jh) >> 1;
+        if (s_pre[mid] <= p) j = mid; else jh = mid;
+    }
+    return j;
+}
+
+// Bitmap-rank accumulation of items with at most TW*KPT products: the
+// products are formed into registers, then accumulated as in the chunk
+// accumulator (bitmap of the chunk's columns, word-popcount prefix for the
+// ranks, values summed at their rank) and written sorted.
+template <int TW, int KPT>
+__global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, int64_t nitems) {
+    extern __shared__ int64_t lds_r[];
+    const int W = 1 << d.logW;
+    const int NWD = W >> 5;
+    double* vals = (double*)lds_r;                  // TW*KPT
+    uint32_t* bits = (uint32_t*)(vals + TW * KPT);  // NWD
+    int* wpre = (int*)(bits + NWD);                 // NWD
+    int32_t* scol = (int32_t*)(wpre + NWD);         // TW*KPT
+    __shared__ int s_pre[TW];
+    __shared__ int64_t s_bo[TW];
+    __shared__ double s_a[TW];
+    __shared__ int red_sh[TW / kWave + 1];
+    const int tt = threadIdx.x;
+    const int64_t item = blockIdx.x;
+    if (item >= nitems) return;
+    const int32_t x = d.items[p0 + item];
+    const int64_t h = x / d.req;
+    const int s = (int)(x - h * d.req);
+    const int64_t q0 = d.hq0[h], q1 = d.hq1[h];
+    for (int wd = tt; wd < NWD; wd += TW) bits[wd] = 0u;
+
+    uint32_t idx[KPT];
+    double v[KPT];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) idx[k] = 0xffffffffu;
+    int done = 0;
+    for (int64_t qb = q0; qb < q1; qb += TW) {
+        const int tot = direct_stage<TW, TW>(d, qb + tt, q1, s, s_pre, s_bo, s_a, red_sh);
+        const int ne = (int)min((int64_t)TW, q1 - qb);
+        int64_t bi[KPT];
+        double av[KPT];
+        int j = 0;
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const int p = k * TW + tt - done;
+            bi[k] = -1;
+            if (p >= 0 && p < tot) {
+                j = direct_find(s_pre, ne, p, j);
+                bi[k] = s_bo[j] + (p - s_pre[j]);
+                av[k] = s_a[j];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            if (bi[k] >= 0) {
+                idx[k] = d.bcol16[bi[k]];
+                v[k] = av[k] * d.bval[bi[k]];
+            }
+        }
+        done += tot;
+        __syncthreads();  // the next round restages
+    }
+#pragma unroll
+    for (int k = 0; k < KPT; ++k)
+        if (idx[k] < (uint32_t)W) atomicOr(&bits[idx[k] >> 5], 1u << (idx[k] & 31));
+    __syncthreads();
+    const int per = (NWD + TW - 1) / TW;
+    const int w0 = min(NWD, tt * per), w1 = min(NWD, w0 + per);
+    int pc = 0;
+    for (int wd = w0; wd < w1; ++wd) pc += __popc(bits[wd]);
+    int tot;
+    int pre = team_exclusive_scan<TW>(pc, red_sh, &tot);
+    for (int wd = w0; wd < w1; ++wd) {
+        wpre[wd] = pre;
+        pre += __popc(bits[wd]);
+    }
+    for (int r = tt; r < tot; r += TW) vals[r] = 0.0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+        if (idx[k] < (uint32_t)W) {
+            const uint32_t wd = idx[k] >> 5;
+            const int rank = wpre[wd] + __popc(bits[wd] & ((1u << (idx[k] & 31)) - 1u));
+            atomicAdd(&vals[rank], v[k]);
+        }
+    }
+    const int32_t lo = s << d.logW;
+    for (int wd = w0; wd < w1; ++wd) {
+        uint32_t bw = bits[wd];
+        int r = wpre[wd];
+        while (bw) {
+            const int b = __ffs(bw) - 1;
+            bw &= bw - 1;
+            scol[r++] = lo + wd * 32 + b;
+        }
+    }
+    __syncthreads();
+    const int64_t off = d.off[x];
+    for (int r = tt; r < tot; r += TW) {
+        d.Ccol[off + r] = scol[r];
+        d.Cval[off + r] = vals[r];
+    }
+}
+
+// Dense window accumulation of the large items: the item's entries are
+// staged kDirectNE at a time and their products streamed through an LDS
+// array over the chunk's W columns (fp64 atomics) with one-byte presence
+// flags; the flags then give every present column its rank in the sorted
+// output, as in the chunk window accumulator.
+constexpr int kDirectWinNT = 1024;
+constexpr int kDirectNE = 128;
+constexpr int kDirectU = 4;  // products in flight per thread
+
+__global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, int64_t p0,
+                                                               int64_t nitems) {
+    constexpr int TW = kDirectWinNT;
+    extern __shared__ int64_t lds_w[];
+    const int W = 1 << d.logW;
+    const int NWD = W >> 5;
+    double* acc = (double*)lds_w;                    // W
+    uint32_t* flags = (uint32_t*)(acc + W);          // W bytes
+    uint32_t* bits = flags + NWD * 8;                // NWD
+    int* wpre = (int*)(bits + NWD);                  // NWD
+    __shared__ int s_pre[kDirectNE];
+    __shared__ int64_t s_bo[kDirectNE];
+    __shared__ double s_a[kDirectNE];
+    __shared__ int red_sh[TW / kWave + 1];
+    const int tt = threadIdx.x;
+    const int64_t item = blockIdx.x;
+    if (item >= nitems) return;
+    const int32_t x = d.items[p0 + item];
+    const int64_t h = x / d.req;
+    const int s = (int)(x - h * d.req);
+    const int64_t q0 = d.hq0[h], q1 = d.hq1[h];
+    for (int i = tt; i < NWD * 8; i += TW) flags[i] = 0u;
+    for (int i = tt; i < W; i += TW) acc[i] = 0.0;
+    uint8_t* fb = (uint8_t*)flags;
+    for (int64_t qb = q0; qb < q1; qb += kDirectNE) {
+        __syncthreads();  // zeroing done / previous round's staging consumed
+        const int tot = direct_stage<TW, kDirectNE>(d, qb + tt, q1, s, s_pre, s_bo, s_a, red_sh);
+        const int ne = (int)min((int64_t)kDirectNE, q1 - qb);
+        int j = 0;
+        for (int pb = tt; pb < tot; pb += TW * kDirectU) {
+            int64_t bi[kDirectU];
+            double av[kDirectU];
+#pragma unroll
+            for (int u = 0; u < kDirectU; ++u) {
+                const int p = pb + u * TW;
+                bi[u] = -1;
+                if (p < tot) {
+                    j = direct_find(s_pre, ne, p, j);
+                    bi[u] = s_bo[j] + (p - s_pre[j]);
+                    av[u] = s_a[j];
+                }
+            }
+            uint32_t c[kDirectU];
+            double bv[kDirectU];
+#pragma unroll
+            for (int u = 0; u < kDirectU; ++u) {
+                if (bi[u] >= 0) {
+                    c[u] = d.bcol16[bi[u]];
+                    bv[u] = d.bval[bi[u]];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kDirectU; ++u) {
+                if (bi[u] >= 0) {
+                    fb[c[u]] = 1;
+                    atomicAdd(&acc[c[u]], av[u] * bv[u]);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int per = (NWD + TW - 1) / TW;
+    const int w0 = min(NWD, tt * per), w1 = min(NWD, w0 + per);
+    int pc = 0;
+    for (int wd = w0; wd < w1; ++wd) {
+        const uint32_t m = pack_flags32(flags + wd * 8);
+        bits[wd] = m;
+        pc += __popc(m);
+    }
+    int tot;
+    int pre = team_exclusive_scan<TW>(pc, red_sh, &tot);
+    for (int wd = w0; wd < w1; ++wd) {
+        wpre[wd] = pre;
+        pre += __popc(bits[wd]);
+    }
+    __syncthreads();
+    const int64_t off = d.off[x];
+    const int32_t lo = s << d.logW;
+    for (int i = tt; i < W; i += TW) {
+        const uint32_t word = bits[i >> 5];
+        const uint32_t bit = 1u << (i & 31);
+        if (word & bit) {
+            const int rank = wpre[i >> 5] + __popc(word & (bit - 1));
+            d.Ccol[off + rank] = lo + i;
+            d.Cval[off + rank] = acc[i];
+        }
+    }
+}
+
+// Heavy A entries and heavy output entries, for the algorithmic byte count:
+// one work group per 256 heavy rows, one atomic pair per group.
+__global__ __launch_bounds__(256) void k_direct_totals(const int64_t* hq0, const int64_t* hq1,
+                                                      int64_t H, int req,
+                                                      const int64_t* dist_fin,
+                                                      unsigned long long* out) {
+    __shared__ int64_t sh[256 / kWave + 1];
+    const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t ne = 0, no = 0;
+    if (h < H) {
+        ne = hq1[h] - hq0[h];
+        for (int s = 0; s < req; ++s) no += dist_fin[h * req + s];
+    }
+    ne = block_reduce_sum<256>(ne, sh);
+    no = block_reduce_sum<256>(no, sh);
+    if (threadIdx.x == 0) {
+        atomicAdd(&out[0], (unsigned long long)ne);
+        atomicAdd(&out[1], (unsigned long long)no);
+    }
+}
+
+void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
+                   const int64_t* dist_fin, int64_t* out2, hipStream_t st) {
+    fill<int64_t>(out2, 2, 0, st);
+    if (H <= 0) return;
+    hipLaunchKernelGGL(k_direct_totals, dim3(grid_1d(ceil_div(H, 256))), dim3(256), 0, st, hq0,
+                       hq1, H, req, dist_fin, (unsigned long long*)out2);
+    SG_LAUNCH_CHECK();
+}
+
+template <int TW, int KPT>
+static void launch_direct_rank(const DirectArgs& d, int64_t p0, int64_t n, hipStream_t st) {
+    const int64_t W = int64_t(1) << d.logW;
+    const size_t lds = (size_t)TW * KPT * 12 + (size_t)(W / 32) * 8;
+    auto kern = k_direct_rank<TW, KPT>;
+    SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds));
+    hipLaunchKernelGGL(kern, dim3(grid_1d(n)), dim3(TW), lds, st, d, p0, n);
+    SG_LAUNCH_CHECK();
+}
+
+size_t direct_window_lds(int64_t W) { return (size_t)W * 9 + (size_t)(W / 32) * 8; }
+
+void direct_accumulate(const DirectArgs& d, int bin, int64_t p0, int64_t n, hipStream_t st) {
+    if (n <= 0) return;
+    switch (bin) {
+        case CB_DENSE: {
+            const int64_t W = int64_t(1) << d.logW;
+            const size_t lds = direct_window_lds(W);
+            SG_HIP(hipFuncSetAttribute((const void*)k_direct_window,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+            hipLaunchKernelGGL(k_direct_window, dim3(grid_1d(n)), dim3(kDirectWinNT), lds, st, d,
+                               p0, n);
+            SG_LAUNCH_CHECK();
+            break;
+        }
+        case CB_H128: launch_direct_rank<64, 1>(d, p0, n, st); break;
+        case CB_H512: launch_direct_rank<64, 4>(d, p0, n, st); break;
+        case CB_H2048: launch_direct_rank<128, 8>(d, p0, n, st); break;
+        case CB_H8192: launch_direct_rank<256, 8>(d, p0, n, st); break;
+        default: throw std::logic_error("not a direct item class");
+    }
+}
+
+}  // namespace sg

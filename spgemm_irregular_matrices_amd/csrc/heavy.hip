@@ -391,6 +391,7 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
     int* colbuf = loff + nkeys + 1;                  // epb
     uint16_t* keybuf = (uint16_t*)(colbuf + epb);    // epb
     int* pos_sh = (int*)(keybuf + epb + (epb & 1));  // nkeys
+    int* rbr = pos_sh + nkeys;                       // nr_max + 1: tile-relative row starts
     __shared__ int64_t r0_sh;
     __shared__ int scan_sh[NW + 1];
 
@@ -403,8 +404,15 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
     for (int x = tt; x < NW * nkeys; x += kMsNT) whist[x] = 0;
     __syncthreads();
     const int64_t r0 = r0_sh;
-    for (int j = tt; j <= nr_max; j += kMsNT)
-        rb[j] = (r0 + j <= g.nrows) ? g.rp[r0 + j] : INT64_MAX;
+    for (int j = tt; j <= nr_max; j += kMsNT) {
+        const int64_t v = (r0 + j <= g.nrows) ? g.rp[r0 + j] : INT64_MAX;
+        rb[j] = v;
+        // 32-bit copy relative to the tile, with a sentinel that ends the
+        // row search at the last row slot
+        rbr[j] = (j == nr_max || v - g0 >= (int64_t)INT32_MAX)
+                     ? INT32_MAX
+                     : (int)(v > g0 ? v - g0 : 0);
+    }
     __syncthreads();
 
     // positions of this tile's (row, chunk) keys in the level's partition,
@@ -421,7 +429,7 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
         // reads: element t of the tile (C-hat order) lies in the last A
         // entry whose product range starts at or before t.
         // (offsets from the LDS base keep the pointers in the LDS address space)
-        const int rq_off = (int)(((char*)(pos_sh + nkeys) - (char*)lds_m + 7) & ~7);
+        const int rq_off = (int)(((char*)(rbr + nr_max + 1) - (char*)lds_m + 7) & ~7);
         int64_t* rq0 = (int64_t*)((char*)lds_m + rq_off);                               // nr_max
         int64_t* rpre = rq0 + nr_max;                                                  // nr_max + 1
         int64_t* rrel = rpre + nr_max + 1;                                             // nr_max
@@ -516,46 +524,49 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
         }
     }
 
-    // 1. load, key, rank within the wave by ballot matching
-    int nbits = 0;
-    while ((1 << nbits) < nkeys) ++nbits;
+    // 1. load, key, rank within the wave. Keys of a wave's 64 elements are
+    // few and clustered (consecutive products share a row and mostly a
+    // chunk), so the wave peels them one distinct key at a time: the first
+    // remaining lane's key is broadcast, a ballot finds the lanes holding it,
+    // and each takes the wave's running count of the key plus its place
+    // among those lanes.
     int key[kMsK];
     int rank[kMsK];
+    if constexpr (!FUSED) {
 #pragma unroll
-    for (int k = 0; k < kMsK; ++k) {
-        int64_t t = g0 + (int64_t)k * kMsNT + tt;
-        key[k] = -1;
-        if constexpr (!FUSED) {
-            if (t < g1) {
-                col[k] = in_col[t];
-                if constexpr (NUM) val[k] = in_val[t];
+        for (int k = 0; k < kMsK; ++k) {
+            const int t = k * kMsNT + tt;
+            if (t < n_wg) {
+                col[k] = in_col[g0 + t];
+                if constexpr (NUM) val[k] = in_val[g0 + t];
             }
         }
     }
     int lr = 0;
     int* myhist = whist + w * nkeys;
-    const uint64_t lt = (lane_id() == 0) ? 0ull : (~0ull >> (kWave - lane_id()));
+    const int lane = lane_id();
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 #pragma unroll
     for (int k = 0; k < kMsK; ++k) {
-        int64_t t = g0 + (int64_t)k * kMsNT + tt;
+        const int t = k * kMsNT + tt;
         int kk = -1;
-        if (t < g1) {
-            while (lr + 1 < nr_max && t >= rb[lr + 1]) ++lr;
+        if (t < n_wg) {
+            while (t >= rbr[lr + 1]) ++lr;
             kk = lr * g.nch + ((col[k] >> g.shift) & mask);
         }
         key[k] = kk;
-        uint64_t eq = __ballot(kk >= 0);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (kk >> b) & 1;
-            const uint64_t m = __ballot(bit);
-            eq &= bit ? m : ~m;
+        int r = 0;
+        uint64_t act = __ballot(kk >= 0);
+        while (act) {
+            const int leader = __builtin_ctzll(act);
+            const int lk = __builtin_amdgcn_readlane(kk, leader);
+            const uint64_t m = __ballot(kk == lk);
+            const int base = myhist[lk];
+            if (kk == lk) r = base + __popcll(m & lt);
+            if (lane == leader) myhist[lk] = base + __popcll(m);
+            act &= ~m;
         }
-        if (kk >= 0) {
-            const int before = __popcll(eq & lt);
-            const int base = myhist[kk];
-            rank[k] = base + before;
-            if (before == 0) myhist[kk] = base + __popcll(eq);
-        }
+        rank[k] = r;
     }
     __syncthreads();
 
@@ -584,8 +595,10 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
         int pre = block_exclusive_scan<kMsNT>(s, scan_sh, &tot);
         for (int x = k0; x < k1; ++x) {
             const int v = loff[x];
-            loff[x] = pre;
             if (v) {
+                // each wave's slot base for the key now includes the key's
+                // offset in the tile
+                for (int ww = 0; ww < NW; ++ww) whist[ww * nkeys + x] += pre;
                 const int p = pos_sh[x];
                 const int64_t got = (int64_t)atomicAdd(&cursor[p], (unsigned long long)v) - pre;
                 if (x == k0) {
@@ -597,7 +610,6 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
             }
             pre += v;
         }
-        if (tt == 0) loff[nkeys] = tot;
     }
     __syncthreads();
 
@@ -606,7 +618,7 @@ __global__ __launch_bounds__(kMsNT) void k_multisplit(LevelGeom g, const int32_t
     for (int k = 0; k < kMsK; ++k) {
         const int kk = key[k];
         if (kk >= 0) {
-            const int d = loff[kk] + myhist[kk] + rank[k];
+            const int d = myhist[kk] + rank[k];
             colbuf[d] = col[k];
             keybuf[d] = (uint16_t)kk;
             if constexpr (NUM) valbuf[d] = val[k];
@@ -630,7 +642,7 @@ static size_t ms_lds(int64_t epb, int nr_max, int nch, bool num, int nw, bool fu
     size_t nkeys = (size_t)nr_max * nch;
     size_t b = nkeys * 8 + (size_t)(nr_max + 1) * 8 + (num ? (size_t)epb * 8 : 0) +
                (size_t)nw * nkeys * 4 + (nkeys + 1) * 4 + (size_t)epb * 4 + (size_t)epb * 2 + 8;
-    b += nkeys * 4 + 4;                                // key positions (+ pad)
+    b += nkeys * 4 + 4 + (size_t)(nr_max + 1) * 4;     // key positions (+ pad), row starts
     if (fused) b += 8 + (size_t)(3 * nr_max + 1) * 8;  // pad + per-row entry ranges
     return b;
 }

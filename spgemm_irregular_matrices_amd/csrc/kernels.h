@@ -217,4 +217,46 @@ struct ChunkItems {
 void accumulate_chunks(const ChunkItems& it, int bin, int64_t p0, int64_t n, bool numeric,
                        hipStream_t st);
 
+// ---------------------------------------------------------------- direct
+// Heavy rows accumulated per (heavy row, final chunk) item straight from A
+// and a chunk-partitioned copy of B (no C-hat): items of more than
+// kDirectDense products use the dense window, smaller ones the bitmap-rank
+// accumulator. Slots per row are bounded so that every wave of the B
+// partition keeps its slot offsets in LDS.
+constexpr int64_t kDirectDense = 2048;
+constexpr int kDirectMaxSlots = 4096;
+struct DirectArgs {
+    const int32_t* items;   // item ids h*req + s, in class order
+    int req;                // final chunks (slots) per row
+    int logW;               // log2 of the slot width
+    const int64_t* hq0;     // per heavy row: first A entry
+    const int64_t* hq1;     // one past its last A entry
+    const int32_t* Acol;
+    const double* Aval;
+    const int64_t* ebo;     // per A entry: start of its B row
+    const int32_t* bsplit;  // B.nrows x (req+1): slot starts inside each B row
+    const uint16_t* bcol16; // partitioned B: column offset inside the slot
+    const double* bval;     // partitioned B: values
+    const int64_t* off;     // per item: output offset in C
+    int32_t* Ccol;
+    double* Cval;
+};
+// bsplit from the per-row slot counts bslot; bperm[p] = B entry placed at p
+// (rows keep their extents), bcol16[p] its column inside its slot.
+void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int32_t* bsplit,
+                    int64_t* bperm, uint16_t* bcol16, hipStream_t st);
+void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int req,
+                    const int64_t* dist_fin, int64_t* off, hipStream_t st);
+// Stable partition of the items x in [0, nitems) by class (CB_* bins, from
+// the exact product count elem_fin[x]).
+void direct_classify(const int64_t* elem_fin, int64_t nitems, int32_t* items, int64_t* bins,
+                     Arena& ar, hipStream_t st);
+void direct_gather_values(const int64_t* bperm, const double* bval, int64_t nnz, double* out,
+                          hipStream_t st);
+// out2[0] = A entries of the heavy rows, out2[1] = their output entries.
+void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
+                   const int64_t* dist_fin, int64_t* out2, hipStream_t st);
+size_t direct_window_lds(int64_t W);
+void direct_accumulate(const DirectArgs& d, int bin, int64_t p0, int64_t n, hipStream_t st);
+
 }  // namespace sg

@@ -104,6 +104,11 @@ struct spgemm_plan_s {
     std::vector<Ev> evs;
     bool fused_sym = false;
     bool fused_num = false;  // numeric level 0 forms its products itself (no C-hat)
+    bool direct = false;     // heavy rows accumulated per (row, final chunk) from A and split B
+    int direct_req = 0;      // final chunks per heavy row on the direct path
+    int64_t direct_W = 0;    // their width
+    int64_t dir_bins[CB_COUNT + 1] = {};
+    int64_t dir_heavy_entries = 0, dir_heavy_outputs = 0;
     // debug dumps (kept for single-batch products)
     bool dbg_valid = false;
     bool dbg_chat = false;  // C-hat was dumped (separate outer product only)
@@ -672,11 +677,22 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
         const bool fused_fits = heavy_symbolic_lds(q.ppow, req) <= (size_t)p->dev_lds &&
                                 B.n * req <= (int64_t(1) << 28);
         p->fused_sym = p->opt.symbolic_mode == 1 || (p->opt.symbolic_mode == 0 && fused_fits);
-        p->fused_num = q.nlevels > 0 && (p->opt.numeric_mode == 1 ||
-                                         (p->opt.numeric_mode == 0 && !p->opt.debug_dump));
+        // the direct path needs the fused pass's per-slot counts, 16-bit
+        // columns inside a slot and a dense window of one slot in LDS
+        const int64_t wfin_d = q.nlevels == 0 ? q.ppow : q.final_width;
+        const bool direct_ok = p->fused_sym && wfin_d <= 65536 && req <= kDirectMaxSlots &&
+                               direct_window_lds(wfin_d) + 8192 <= (size_t)p->dev_lds &&
+                               p->H * req < (int64_t(1) << 31);
+        p->direct = direct_ok && (p->opt.numeric_mode == 3 ||
+                                  (p->opt.numeric_mode == 0 && !p->opt.debug_dump));
+        p->direct_req = (int)req;
+        p->direct_W = wfin_d;
+        p->fused_num = !p->direct && q.nlevels > 0 &&
+                       (p->opt.numeric_mode == 1 || p->opt.numeric_mode == 3 ||
+                        (p->opt.numeric_mode == 0 && !p->opt.debug_dump));
         // the masked CSC feeds the separate outer product only
-        const bool need_csc = !p->fused_num || !p->fused_sym;
-        if (p->fused_num) {
+        const bool need_csc = !(p->fused_num || p->direct) || !p->fused_sym;
+        if (p->fused_num || p->direct) {
             PhaseScope ps(p, 0, SPGEMM_PHASE_CSR_TO_CSC, st);
             fused_setup(A, B, S, hrows, p->H, ar.get<int64_t>("h_q0", (size_t)p->H),
                         ar.get<int64_t>("h_q1", (size_t)p->H), ar.get<int64_t>("h_s0", (size_t)p->H),
@@ -695,6 +711,29 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
             heavy_symbolic(A, B, hrows, p->H, q.ppow, wfin, bslot, elem_fin, dist_fin, st);
             add_bytes(p, 0, SPGEMM_PHASE_HISTO, 4.0 * p->Nh + 16.0 * p->H * req);
+        }
+        if (p->direct) {
+            // B partitioned into the final chunks (the column-range split
+            // applied to B rather than to C-hat), and the items by class
+            PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
+            int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
+            direct_split_b(B, bslot, (int)req, wfin_d,
+                           ar.get<int32_t>("bsplit", (size_t)(B.n * (req + 1) + 1)),
+                           ar.get<int64_t>("bperm", (size_t)B.nnz + 1),
+                           ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1), st);
+            int64_t* bins = ar.get<int64_t>("dbins", CB_COUNT + 1);
+            direct_classify(elem_fin, p->H * req, ar.get<int32_t>("ditems", (size_t)(p->H * req)),
+                            bins, ar, st);
+            int64_t* tot2 = ar.get<int64_t>("dtot", 2);
+            direct_totals(ar.get<int64_t>("h_q0", (size_t)p->H), ar.get<int64_t>("h_q1", (size_t)p->H),
+                          p->H, (int)req, dist_fin, tot2, st);
+            int64_t* hb = d2h(p, bins, CB_COUNT + 1, st);
+            for (int b = 0; b <= CB_COUNT; ++b) p->dir_bins[b] = hb[b];
+            int64_t* ht = d2h(p, tot2, 2, st);
+            p->dir_heavy_entries = ht[0];
+            p->dir_heavy_outputs = ht[1];
+            add_bytes(p, 0, SPGEMM_PHASE_HISTO, 20.0 * B.nnz + 4.0 * B.n * (req + 1) +
+                                                    8.0 * p->H * req);
         }
         CscBufs c = csc_bufs(p);
         int64_t ent_cur = 0, P_cur = 0, tile_cur = 0, crp_cur = 0;
@@ -757,6 +796,13 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     }
     const int64_t nnz_c = d2h(p, C_rp + n, 1, st)[0];
     heavy_offsets(p, hrows, C_rp, st);
+    if (p->direct) {
+        PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
+        direct_offsets(C_rp, hrows, p->H, p->direct_req,
+                       ar.get<int64_t>("dist_fin", (size_t)(p->H * p->direct_req)),
+                       ar.get<int64_t>("doff", (size_t)(p->H * p->direct_req)), st);
+    }
+    p->stats.numeric_path = p->H == 0 ? 0 : (p->direct ? 3 : (p->fused_num ? 1 : 2));
     p->stats.nrows = n;
     p->stats.ncols_c = B.m;
     p->stats.nnz_c = nnz_c;
@@ -805,6 +851,36 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
             accumulate_rows(ri, b, p->row_bins[b], p->row_bins[b + 1] - p->row_bins[b], true, st);
     }
     if (p->H == 0) return;
+
+    if (p->direct) {
+        const int req = p->direct_req;
+        double* bpval = ar.get<double>("bpval", (size_t)B.nnz + 1);
+        DirectArgs d{};
+        d.items = ar.get<int32_t>("ditems", (size_t)(p->H * req));
+        d.req = req;
+        d.logW = ilog2(p->direct_W);
+        d.hq0 = ar.get<int64_t>("h_q0", (size_t)p->H);
+        d.hq1 = ar.get<int64_t>("h_q1", (size_t)p->H);
+        d.Acol = A.col;
+        d.Aval = A.val;
+        d.ebo = ar.get<int64_t>("ebo", (size_t)A.nnz + 1);
+        d.bsplit = ar.get<int32_t>("bsplit", (size_t)(B.n * (req + 1) + 1));
+        d.bcol16 = ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1);
+        d.bval = bpval;
+        d.off = ar.get<int64_t>("doff", (size_t)(p->H * req));
+        d.Ccol = C_col;
+        d.Cval = C_val;
+        PhaseScope ps(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, st);
+        // B's values in the partitioned order (values may change between
+        // numeric calls; the structure may not)
+        direct_gather_values(ar.get<int64_t>("bperm", (size_t)B.nnz + 1), B.val, B.nnz, bpval, st);
+        for (int b = CB_DENSE; b <= CB_H8192; ++b)
+            direct_accumulate(d, b, p->dir_bins[b], p->dir_bins[b + 1] - p->dir_bins[b], st);
+        // minimum: A's heavy entries and B once, C's heavy entries once
+        add_bytes(p, 1, SPGEMM_PHASE_HEAVY_ACCUM,
+                  12.0 * p->dir_heavy_entries + 12.0 * B.nnz + 12.0 * p->dir_heavy_outputs);
+        return;
+    }
 
     CscBufs c = csc_bufs(p);
     // C-hat (buffer 0) is written only by the separate outer product; with
@@ -947,7 +1023,7 @@ SPGEMM_API int spgemm_plan_create(spgemm_plan* out, const spgemm_options* opt) {
     if (o.lds_budget_bytes < 0 || o.tau_override < 0 || o.chunk_width_override < 0 ||
         o.nchunks_cap < 0 || o.max_batch_products < 0)
         return SPGEMM_ERR_INVALID_ARG;
-    if (o.symbolic_mode < 0 || o.symbolic_mode > 2 || o.numeric_mode < 0 || o.numeric_mode > 2)
+    if (o.symbolic_mode < 0 || o.symbolic_mode > 2 || o.numeric_mode < 0 || o.numeric_mode > 3)
         return SPGEMM_ERR_INVALID_ARG;
     if (o.chunk_width_override > 0 &&
         (o.chunk_width_override < 32 || (o.chunk_width_override & (o.chunk_width_override - 1))))

@@ -45,6 +45,7 @@ int main(void) {
   printf("%zu %zu %zu %zu %zu\n", offsetof(spgemm_stats, phase_ms), offsetof(spgemm_stats, lds_bytes),
          offsetof(spgemm_options, max_batch_products), offsetof(spgemm_options, symbolic_mode),
          offsetof(spgemm_options, numeric_mode));
+  printf("%zu\n", offsetof(spgemm_stats, numeric_path));
   return 0;
 }''')
     exe = tmp_path / "layout"
@@ -60,6 +61,7 @@ int main(void) {
     assert sizes[6] == binding.Options.max_batch_products.offset
     assert sizes[7] == binding.Options.symbolic_mode.offset
     assert sizes[8] == binding.Options.numeric_mode.offset
+    assert sizes[9] == binding.Stats.numeric_path.offset
 
 
 def test_no_gpu_call_fails_loudly():

@@ -46,8 +46,15 @@ def test_rmat10_default_and_all_light():
 
 
 # (symbolic, numeric) modes: fused bitmap symbolic or multisplit symbolic;
-# products formed inside the first multisplit level or a separate C-hat
-MODES = [(1, 1), (2, 2), (1, 2)]
+# products formed inside the first multisplit level, a separate C-hat, or
+# direct accumulation from A and the chunk-split B
+MODES = [(1, 1), (2, 2), (1, 2), (1, 3)]
+
+
+def _expected_path(mode, nlevels):
+    if mode[1] == 3:
+        return 3
+    return 1 if mode[1] == 1 and nlevels > 0 else 2
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -64,6 +71,7 @@ def test_rmat10_forced_heavy(tau, width, cap, levels, mode):
                                nchunks_cap=cap, symbolic_mode=mode[0], numeric_mode=mode[1])
     assert st["heavy_rows"] > 0
     assert st["nlevels"] == levels, st
+    assert st["numeric_path"] == _expected_path(mode, levels)
     compare(A, A, rp, col, val)
 
 
@@ -364,7 +372,7 @@ def test_error_paths():
         with pytest.raises(binding.SpgemmError) as e:
             p.numeric(A51, dBg, C.rowptr, C.col, C.val)
         assert e.value.code == -6
-    for kw in ({"chunk_width_override": 48}, {"numeric_mode": 3}, {"symbolic_mode": -1}):
+    for kw in ({"chunk_width_override": 48}, {"numeric_mode": 4}, {"symbolic_mode": -1}):
         with pytest.raises(binding.SpgemmError) as e:
             binding.Plan(**kw)
         assert e.value.code == -1

@@ -141,6 +141,7 @@ def test_large_sampled_rows_and_properties(name, batch):
         assert st["nbatches"] >= 3
     rows, u = sample_rows(A, B, n_heavy=6, n_random=300, seed=7, tau=st["tau"])
     assert st["heavy_rows"] > 0 and st["nlevels"] >= 1
+    assert st["numeric_path"] == 3  # the default heavy numeric pass, as benchmarked
     assert st["sum_products"] == int(u.sum())
     assert st["heavy_products"] == int(u[u > st["tau"]].sum())
     rp, fake_rp, col, val = _rows_to_host(C, rows)
