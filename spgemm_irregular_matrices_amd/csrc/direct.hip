@@ -81,12 +81,14 @@ __global__ __launch_bounds__(kBpartNT) void k_bpartition(const int64_t* brp, con
 }
 
 void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int32_t* bsplit,
-                    int64_t* bperm, uint16_t* bcol16, hipStream_t st) {
+                    bool bsplit_done, int64_t* bperm, uint16_t* bcol16, hipStream_t st) {
     if (B.n <= 0) return;
     if (W > 65536 || req > kDirectMaxSlots) throw std::logic_error("direct split limits");
-    hipLaunchKernelGGL(k_bsplit_prefix, dim3(grid_1d(ceil_div(B.n, 256))), dim3(256), 0, st, bslot,
-                       B.n, req, bsplit);
-    SG_LAUNCH_CHECK();
+    if (!bsplit_done) {
+        hipLaunchKernelGGL(k_bsplit_prefix, dim3(grid_1d(ceil_div(B.n, 256))), dim3(256), 0, st,
+                           bslot, B.n, req, bsplit);
+        SG_LAUNCH_CHECK();
+    }
     if (B.nnz <= 0) return;
     const size_t lds = (size_t)(kBpartNT / kWave) * req * 4;
     SG_HIP(hipFuncSetAttribute((const void*)k_bpartition,

@@ -807,6 +807,50 @@ __global__ void k_bslot_counts(const int64_t* brp, const int32_t* bcol, int64_t 
         atomicAdd(&bslot[k * req + (bcol[e] >> logW)], 1);
 }
 
+// The same counts without global atomics: one wavefront per B row counts
+// its slots in LDS, peeling one distinct slot of each 64-entry batch at a
+// time (B rows are mostly sorted, so a batch holds few slots), then writes
+// the row's counts and, when asked, their exclusive prefix (the row's slot
+// starts, with the row length last).
+constexpr int kBslotNT = 256;
+constexpr int kBslotMaxReq = 4096;
+
+__global__ __launch_bounds__(kBslotNT) void k_bslot_rows(const int64_t* brp, const int32_t* bcol,
+                                                         int64_t nb, int logW, int req,
+                                                         int32_t* bslot, int32_t* bsplit) {
+    extern __shared__ int lds_c[];
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    int* cnt = lds_c + w * req;
+    const int64_t k = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    if (k >= nb) return;  // whole waves leave together; no block barrier below
+    for (int s = lane; s < req; s += kWave) cnt[s] = 0;
+    const int64_t e0 = brp[k], e1 = brp[k + 1];
+    for (int64_t eb = e0; eb < e1; eb += kWave) {
+        const int64_t e = eb + lane;
+        const int s = e < e1 ? (int)((uint32_t)bcol[e] >> logW) : -1;
+        uint64_t act = __ballot(s >= 0);
+        while (act) {
+            const int leader = __builtin_ctzll(act);
+            const int ls = __builtin_amdgcn_readlane(s, leader);
+            const uint64_t m = __ballot(s == ls);
+            if (lane == leader) cnt[ls] += __popcll(m);
+            act &= ~m;
+        }
+    }
+    int run = 0;
+    for (int sb = 0; sb < req; sb += kWave) {
+        const int s = sb + lane;
+        const int c = s < req ? cnt[s] : 0;
+        if (s < req) bslot[k * req + s] = c;
+        if (bsplit) {
+            const int inc = wave_inclusive_scan(c);
+            if (s < req) bsplit[k * (req + 1) + s] = run + inc - c;
+            run += __shfl(inc, kWave - 1, kWave);
+        }
+    }
+    if (bsplit && lane == 0) bsplit[k * (req + 1) + req] = run;
+}
+
 // One work group per heavy row; thread tt owns slot tt % req and sums the
 // B-row vectors of every (TW/req)-th entry of the row.
 constexpr int kElemNT = 256;
@@ -925,17 +969,31 @@ size_t heavy_symbolic_lds(int64_t ppow, int64_t req) {
            (size_t)req * 4 + (size_t)(ppow / 32) * 4;
 }
 
-void heavy_symbolic(const DevCSR& A, const DevCSR& B, const int32_t* hrows, int64_t H,
-                    int64_t ppow, int64_t wfin, int32_t* bslot, int64_t* elem_fin,
-                    int64_t* dist_fin, hipStream_t st) {
-    if (H <= 0) return;
+bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int32_t* hrows, int64_t H,
+                    int64_t ppow, int64_t wfin, int32_t* bslot, int32_t* bsplit,
+                    int64_t* elem_fin, int64_t* dist_fin, hipStream_t st) {
+    if (H <= 0) return false;
     const int64_t req = ppow / wfin;
     const int logW = ilog2(wfin);
-    fill<int32_t>(bslot, B.n * req, 0, st);
-    if (B.n > 0) {
-        hipLaunchKernelGGL(k_bslot_counts, dim3(grid_1d(ceil_div(B.n * kWave, 256))), dim3(256),
-                           0, st, B.rp, B.col, B.n, logW, (int)req, bslot);
-        SG_LAUNCH_CHECK();
+    bool split_done = false;
+    if (req <= kBslotMaxReq) {
+        if (B.n > 0) {
+            const size_t lds = (size_t)(kBslotNT / kWave) * req * 4;
+            SG_HIP(hipFuncSetAttribute((const void*)k_bslot_rows,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+            hipLaunchKernelGGL(k_bslot_rows, dim3(grid_1d(ceil_div(B.n * kWave, kBslotNT))),
+                               dim3(kBslotNT), lds, st, B.rp, B.col, B.n, logW, (int)req, bslot,
+                               bsplit);
+            SG_LAUNCH_CHECK();
+        }
+        split_done = bsplit != nullptr;
+    } else {
+        fill<int32_t>(bslot, B.n * req, 0, st);
+        if (B.n > 0) {
+            hipLaunchKernelGGL(k_bslot_counts, dim3(grid_1d(ceil_div(B.n * kWave, 256))),
+                               dim3(256), 0, st, B.rp, B.col, B.n, logW, (int)req, bslot);
+            SG_LAUNCH_CHECK();
+        }
     }
     const size_t elds = (size_t)req * 8;
     SG_HIP(hipFuncSetAttribute((const void*)k_heavy_elem_counts,
@@ -949,6 +1007,7 @@ void heavy_symbolic(const DevCSR& A, const DevCSR& B, const int32_t* hrows, int6
     hipLaunchKernelGGL(k_heavy_symbolic, dim3(grid_1d(H)), dim3(kHsymNT), lds, st, A.rp, A.col,
                        B.rp, B.col, hrows, (int)req, (int)(ppow / 32), dist_fin);
     SG_LAUNCH_CHECK();
+    return split_done;
 }
 
 // Per natural chunk of a level: its first finest slot, and its element and

@@ -165,10 +165,12 @@ void chunk_colbase(int64_t nparents, int nch, int64_t width, const int32_t* pare
 // finest chunk slot of width wfin, the element count and the number of
 // distinct columns. Needs heavy_symbolic_lds(ppow, ppow/wfin) bytes of LDS.
 size_t heavy_symbolic_lds(int64_t ppow, int64_t req);
-// bslot is scratch of B.n * (ppow/wfin) int32.
-void heavy_symbolic(const DevCSR& A, const DevCSR& B, const int32_t* hrows, int64_t H,
-                    int64_t ppow, int64_t wfin, int32_t* bslot, int64_t* elem_fin,
-                    int64_t* dist_fin, hipStream_t st);
+// bslot (B.n * (ppow/wfin) int32) receives every B row's entries per slot.
+// If bsplit (B.n * (ppow/wfin + 1) int32) is given it may also receive the
+// rows' slot starts (their exclusive prefix); returns whether it did.
+bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int32_t* hrows, int64_t H,
+                    int64_t ppow, int64_t wfin, int32_t* bslot, int32_t* bsplit,
+                    int64_t* elem_fin, int64_t* dist_fin, hipStream_t st);
 // Counts, distinct counts and first finest slot of every natural chunk of a
 // level, summed from the finest slots (g slots per chunk).
 void level_from_slots(const int64_t* parent_slot0, const int32_t* parent_inv, int64_t nparents,
@@ -244,7 +246,7 @@ struct DirectArgs {
 // bsplit from the per-row slot counts bslot; bperm[p] = B entry placed at p
 // (rows keep their extents), bcol16[p] its column inside its slot.
 void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int32_t* bsplit,
-                    int64_t* bperm, uint16_t* bcol16, hipStream_t st);
+                    bool bsplit_done, int64_t* bperm, uint16_t* bcol16, hipStream_t st);
 void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int req,
                     const int64_t* dist_fin, int64_t* off, hipStream_t st);
 // Stable partition of the items x in [0, nitems) by class (CB_* bins, from

@@ -703,13 +703,17 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             throw OverflowError("fused symbolic pass needs more LDS than the device has");
         int64_t* elem_fin = nullptr;
         int64_t* dist_fin = nullptr;
+        bool bsplit_done = false;
         if (p->fused_sym) {
             const int64_t wfin = q.nlevels == 0 ? q.ppow : q.final_width;
             elem_fin = ar.get<int64_t>("elem_fin", (size_t)(p->H * req));
             dist_fin = ar.get<int64_t>("dist_fin", (size_t)(p->H * req));
             PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
             int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
-            heavy_symbolic(A, B, hrows, p->H, q.ppow, wfin, bslot, elem_fin, dist_fin, st);
+            bsplit_done = heavy_symbolic(
+                A, B, hrows, p->H, q.ppow, wfin, bslot,
+                p->direct ? ar.get<int32_t>("bsplit", (size_t)(B.n * (req + 1) + 1)) : nullptr,
+                elem_fin, dist_fin, st);
             add_bytes(p, 0, SPGEMM_PHASE_HISTO, 4.0 * p->Nh + 16.0 * p->H * req);
         }
         if (p->direct) {
@@ -718,7 +722,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
             int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
             direct_split_b(B, bslot, (int)req, wfin_d,
-                           ar.get<int32_t>("bsplit", (size_t)(B.n * (req + 1) + 1)),
+                           ar.get<int32_t>("bsplit", (size_t)(B.n * (req + 1) + 1)), bsplit_done,
                            ar.get<int64_t>("bperm", (size_t)B.nnz + 1),
                            ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1), st);
             int64_t* bins = ar.get<int64_t>("dbins", CB_COUNT + 1);
