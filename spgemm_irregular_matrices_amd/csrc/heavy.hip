@@ -851,41 +851,9 @@ __global__ __launch_bounds__(kBslotNT) void k_bslot_rows(const int64_t* brp, con
     if (bsplit && lane == 0) bsplit[k * (req + 1) + req] = run;
 }
 
-// One work group per heavy row; thread tt owns slot tt % req and sums the
-// B-row vectors of every (TW/req)-th entry of the row.
-constexpr int kElemNT = 256;
-__global__ __launch_bounds__(kElemNT) void k_heavy_elem_counts(const int64_t* arp,
-                                                               const int32_t* acol,
-                                                               const int32_t* hrows, int req,
-                                                               const int32_t* bslot,
-                                                               int64_t* elem_fin) {
-    extern __shared__ int64_t lds_e[];
-    unsigned long long* acc = (unsigned long long*)lds_e;  // req
-    const int tt = threadIdx.x;
-    const int64_t h = blockIdx.x;
-    for (int s = tt; s < req; s += kElemNT) acc[s] = 0ull;
-    __syncthreads();
-    const int32_t r = hrows[h];
-    const int64_t a0 = arp[r], a1 = arp[r + 1];
-    if (req <= kElemNT) {
-        const int s = tt % req;
-        const int jstep = kElemNT / req;
-        int64_t sum = 0;
-        for (int64_t q = a0 + tt / req; q < a1; q += jstep) sum += bslot[(int64_t)acol[q] * req + s];
-        if (tt < jstep * req && sum) atomicAdd(&acc[s], (unsigned long long)sum);
-    } else {
-        for (int s = tt; s < req; s += kElemNT) {
-            int64_t sum = 0;
-            for (int64_t q = a0; q < a1; ++q) sum += bslot[(int64_t)acol[q] * req + s];
-            acc[s] += (unsigned long long)sum;
-        }
-    }
-    __syncthreads();
-    for (int s = tt; s < req; s += kElemNT) elem_fin[h * req + s] = (int64_t)acc[s];
-}
-
 // Distinct columns: one work group per heavy row keeps a one-bit-per-column
-// bitmap of the row's column range in LDS. The row's A entries are taken in
+// bitmap of the row's column range in LDS; the row's element counts per slot
+// are the sums of its entries' B-row slot vectors. The row's A entries are taken in
 // windows staged in LDS; each entry's B row is cut into pieces of 64
 // products and the waves take pieces in turn, one product per lane, so the
 // reads of B are coalesced and no product needs a search.
@@ -894,20 +862,26 @@ constexpr int kHsymEW = 1024;  // entries per staged window
 
 __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     const int64_t* arp, const int32_t* acol, const int64_t* brp, const int32_t* bcol,
-    const int32_t* hrows, int req, int nwords, int64_t* dist_fin) {
+    const int32_t* hrows, int req, int nwords, const int32_t* bslot, int64_t* elem_fin,
+    int64_t* dist_fin) {
     extern __shared__ int64_t lds_s[];
     constexpr int NW = kHsymNT / kWave;
-    int64_t* bst = lds_s;                          // kHsymEW B row starts
-    int* nbv = (int*)(bst + kHsymEW);              // kHsymEW B row lengths
-    int* ppre = nbv + kHsymEW;                     // kHsymEW + 1 piece prefix
-    int* dsl = ppre + kHsymEW + 1;                 // req distinct counts
-    uint32_t* bits = (uint32_t*)(dsl + req);       // nwords
+    int64_t* bst = lds_s;                                   // kHsymEW B row starts
+    unsigned long long* esl = (unsigned long long*)(bst + kHsymEW);  // req element counts
+    int* nbv = (int*)(esl + req);                           // kHsymEW B row lengths
+    int* kst = nbv + kHsymEW;                               // kHsymEW B rows
+    int* ppre = kst + kHsymEW;                              // kHsymEW + 1 piece prefix
+    int* dsl = ppre + kHsymEW + 1;                          // req distinct counts
+    uint32_t* bits = (uint32_t*)(dsl + req);                // nwords
     __shared__ int scan_sh[NW + 1];
     const int tt = threadIdx.x;
     const int w = tt / kWave, lane = lane_id();
     const int64_t h = blockIdx.x;
     for (int i = tt; i < nwords; i += kHsymNT) bits[i] = 0u;
-    for (int i = tt; i < req; i += kHsymNT) dsl[i] = 0;
+    for (int i = tt; i < req; i += kHsymNT) {
+        dsl[i] = 0;
+        esl[i] = 0ull;
+    }
     __syncthreads();
     const int32_t r = hrows[h];
     const int64_t a0 = arp[r], a1 = arp[r + 1];
@@ -920,6 +894,7 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
             int nb = (int)(brp[k + 1] - b0);
             bst[tt] = b0;
             nbv[tt] = nb;
+            kst[tt] = k;
             pc = (nb + kWave - 1) / kWave;
         }
         int tot;
@@ -945,6 +920,20 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
             for (int uu = 0; uu < U; ++uu)
                 if (c[uu] != 0xffffffffu) atomicOr(&bits[c[uu] >> 5], 1u << (c[uu] & 31));
         }
+        // element counts per slot: the sum of the window's B-row slot vectors
+        if (req <= kHsymNT) {
+            const int sl = tt % req, step = kHsymNT / req;
+            int64_t sum = 0;
+            if (tt < step * req)
+                for (int e = tt / req; e < ne; e += step) sum += bslot[(int64_t)kst[e] * req + sl];
+            if (sum) atomicAdd(&esl[sl], (unsigned long long)sum);
+        } else {
+            for (int sl = tt; sl < req; sl += kHsymNT) {
+                int64_t sum = 0;
+                for (int e = 0; e < ne; ++e) sum += bslot[(int64_t)kst[e] * req + sl];
+                esl[sl] += (unsigned long long)sum;
+            }
+        }
         __syncthreads();
     }
     // distinct columns per finest slot: popcounts of the slot's words
@@ -961,12 +950,15 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
         }
     }
     __syncthreads();
-    for (int sl = tt; sl < req; sl += kHsymNT) dist_fin[h * req + sl] = dsl[sl];
+    for (int sl = tt; sl < req; sl += kHsymNT) {
+        dist_fin[h * req + sl] = dsl[sl];
+        elem_fin[h * req + sl] = (int64_t)esl[sl];
+    }
 }
 
 size_t heavy_symbolic_lds(int64_t ppow, int64_t req) {
-    return (size_t)kHsymEW * 8 + (size_t)kHsymEW * 4 + (size_t)(kHsymEW + 1) * 4 +
-           (size_t)req * 4 + (size_t)(ppow / 32) * 4;
+    return (size_t)kHsymEW * 8 + (size_t)req * 8 + (size_t)kHsymEW * 4 * 2 +
+           (size_t)(kHsymEW + 1) * 4 + (size_t)req * 4 + (size_t)(ppow / 32) * 4;
 }
 
 bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int32_t* hrows, int64_t H,
@@ -995,17 +987,11 @@ bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int32_t* hrows, int6
             SG_LAUNCH_CHECK();
         }
     }
-    const size_t elds = (size_t)req * 8;
-    SG_HIP(hipFuncSetAttribute((const void*)k_heavy_elem_counts,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)elds));
-    hipLaunchKernelGGL(k_heavy_elem_counts, dim3(grid_1d(H)), dim3(kElemNT), elds, st, A.rp,
-                       A.col, hrows, (int)req, bslot, elem_fin);
-    SG_LAUNCH_CHECK();
     const size_t lds = heavy_symbolic_lds(ppow, req);
     SG_HIP(hipFuncSetAttribute((const void*)k_heavy_symbolic,
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     hipLaunchKernelGGL(k_heavy_symbolic, dim3(grid_1d(H)), dim3(kHsymNT), lds, st, A.rp, A.col,
-                       B.rp, B.col, hrows, (int)req, (int)(ppow / 32), dist_fin);
+                       B.rp, B.col, hrows, (int)req, (int)(ppow / 32), bslot, elem_fin, dist_fin);
     SG_LAUNCH_CHECK();
     return split_done;
 }
