@@ -1,10 +1,15 @@
 """Benchmark: C = A*A for R-MAT scale 18, edge factor 16 (262,144 x 262,144).
 
 One step is the whole hot path: spgemm_symbolic + spgemm_numeric (setup,
-light rows, outer product, multisplit levels, accumulation, prefix sums),
-on inputs already resident in HBM. Protocol after the gMAGNUS page
-(Section IV-A): warmup runs, then timed runs, mean reported. Prints one
-JSON line.
+InterOffsets, binning, the heavy rows' chunk counts and split, light rows,
+accumulation of every (heavy row, chunk), prefix sums), on inputs already
+resident in HBM, with the library's default options. Protocol after the
+gMAGNUS page (Section IV-A): warmup runs, then timed runs, mean reported.
+Prints one JSON line.
+
+paths = the same product with the page's own numeric dataflows (outer
+        product into C-hat then multisplit; the first multisplit level
+        formed in its tiles), a few steps each, for context
 
 value  = intermediate products per second (sum of u(i) over all rows / step time)
 roofline = the dominant kernel's algorithmic bytes per launch / its mean
@@ -35,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="rmat18_ef16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-paths", action="store_true",
+                    help="skip timing the other numeric paths (separate C-hat, fused first level)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--tau", type=int, default=0)
     ap.add_argument("--width", type=int, default=0)
@@ -76,7 +83,10 @@ PHASE_KERNELS = {
     "numeric:multisplit": ["k_multisplit<true,"],
     "numeric:outer_prod": ["k_expand<true>"],
     "numeric:heavy_accum": ["k_acc_window<1,true,", "k_acc_rank<true,", "k_acc_hash<1,true,"],
+    "numeric:direct_dense": ["k_direct_window"],
+    "numeric:direct_rank": ["k_direct_rank<", "k_gather_bval"],
 }
+HEAVY_PHASES = ("outer_prod", "multisplit", "heavy_accum", "histo", "direct_dense", "direct_rank")
 
 
 def measured_traffic(workload: str, phase: str):
@@ -105,6 +115,36 @@ def measured_traffic(workload: str, phase: str):
         total += int(fetch) + int(write)
         found = True
     return total if found else None
+
+
+def time_numeric_path(dA, dB, numeric_mode: int, steps: int) -> dict:
+    """Mean step time of the same product with another heavy numeric path (context)."""
+    import torch
+    from spgemm_irregular_matrices_amd import binding
+    with binding.Plan(timing=True, numeric_mode=numeric_mode) as plan:
+        def step():
+            rp, nnz = plan.symbolic(dA, dB)
+            col = torch.empty(nnz, dtype=torch.int32, device="cuda")
+            val = torch.empty(nnz, dtype=torch.float64, device="cuda")
+            plan.numeric(dA, dB, rp, col, val)
+        step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        phases = {}
+        for _ in range(steps):
+            step()
+            st = plan.stats()
+            for pn in ("symbolic", "numeric"):
+                for ph, rec in st[pn].items():
+                    if rec["launches"]:
+                        key = f"{pn}:{ph}"
+                        phases[key] = phases.get(key, 0.0) + rec["ms"] / steps
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        path = st["numeric_path"]
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "numeric_path": path,
+            "phase_ms_per_step": {k: round(v, 3) for k, v in phases.items() if v >= 0.05}}
 
 
 def cpu_baseline(A, B, target_s: float):
@@ -194,8 +234,7 @@ def main():
     value = products * args.steps / elapsed
 
     # dominant kernel of the heavy path by measured time
-    cands = [k for k in per_phase if k[1] in ("outer_prod", "multisplit", "heavy_accum",
-                                               "histo", "light_accum")]
+    cands = [k for k in per_phase if k[1] in HEAVY_PHASES + ("light_accum",)]
     dom = max(cands, key=lambda k: per_phase[k]["ms"])
     d = per_phase[dom]
     launch_ms = d["ms"] / max(d["launches"], 1)
@@ -206,10 +245,16 @@ def main():
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "kernel": f"{dom[0]}:{dom[1]}", "launch_ms": launch_ms,
                 "bytes_per_launch": bytes_per_launch}
-    heavy_bytes = sum(v["bytes"] for k, v in per_phase.items()
-                      if k[1] in ("outer_prod", "multisplit", "heavy_accum", "histo"))
-    heavy_ms = sum(v["ms"] for k, v in per_phase.items()
-                   if k[1] in ("outer_prod", "multisplit", "heavy_accum", "histo"))
+    heavy_bytes = sum(v["bytes"] for k, v in per_phase.items() if k[1] in HEAVY_PHASES)
+    heavy_ms = sum(v["ms"] for k, v in per_phase.items() if k[1] in HEAVY_PHASES)
+
+    plan.close()
+    paths = None
+    if not args.no_paths:
+        # the page's dataflows on the same product, for context: outer product
+        # into C-hat then multisplit, and the first level formed in the tiles
+        paths = {"separate_chat": time_numeric_path(dA, dB, 2, 3),
+                 "fused_first_level": time_numeric_path(dA, dB, 1, 3)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -224,7 +269,9 @@ def main():
                    "nrows": A.nrows, "nnz_A": A.nnz, "sum_products": products,
                    "nnz_C": st["nnz_c"], "heavy_rows": st["heavy_rows"],
                    "heavy_products": st["heavy_products"], "tau": st["tau"],
-                   "vchunks": st["vchunks"], "final_chunk_width": st["final_chunk_width"]},
+                   "vchunks": st["vchunks"], "final_chunk_width": st["final_chunk_width"],
+                   "numeric_path": {0: "none", 1: "fused first level", 2: "separate C-hat",
+                                    3: "direct"}[st["numeric_path"]]},
         "gflops": 2.0 * value / 1e9,
         "roofline": roofline,
         "heavy_path": {"ms_per_step": heavy_ms / args.steps,
@@ -234,8 +281,8 @@ def main():
                               if v["launches"]},
         "step_ms_min_max": [min(step_ms), max(step_ms)],
         "cpu_baseline": cpu,
+        "paths": paths,
     }
-    plan.close()
     print(json.dumps(line))
 
 

@@ -103,6 +103,9 @@ typedef enum {
     SPGEMM_PHASE_HEAVY_ACCUM,     /* dense / hash accumulation of chunks           */
     SPGEMM_PHASE_LIGHT_ACCUM,     /* accumulation of light rows                    */
     SPGEMM_PHASE_PREFIX_SUM,      /* C.rowPtr prefix sum and chunk offsets         */
+    SPGEMM_PHASE_DIRECT_DENSE,    /* direct numeric path: dense-window items       */
+    SPGEMM_PHASE_DIRECT_RANK,     /* direct numeric path: bitmap-rank items and
+                                     B's values in split order                     */
     SPGEMM_NUM_PHASES
 } spgemm_phase;
 

@@ -23,7 +23,7 @@ STATUS = {
     -6: "SPGEMM_ERR_PLAN_MISMATCH", -7: "SPGEMM_ERR_HIP", -8: "SPGEMM_ERR_NOT_READY",
 }
 PHASES = ["validate", "inter_prod_size", "binning", "csr_to_csc", "outer_prod", "histo",
-          "multisplit", "heavy_accum", "light_accum", "prefix_sum"]
+          "multisplit", "heavy_accum", "light_accum", "prefix_sum", "direct_dense", "direct_rank"]
 MAX_LEVELS = 8
 EXPORTS = ["spgemm_options_default", "spgemm_plan_create", "spgemm_plan_destroy",
            "spgemm_symbolic", "spgemm_numeric", "spgemm_plan_stats", "spgemm_plan_debug",
