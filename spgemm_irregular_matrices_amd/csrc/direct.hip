@@ -392,33 +392,44 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     }
 }
 
-// Heavy A entries and heavy output entries, for the algorithmic byte count:
-// one work group per 256 heavy rows, one atomic pair per group.
+// Per class of items (dense window / bitmap rank): products, output
+// entries, and A entries read (an item reads all of its row's entries), for
+// the algorithmic byte counts. out6 = {dense: products, outputs, entries,
+// rank: products, outputs, entries}.
 __global__ __launch_bounds__(256) void k_direct_totals(const int64_t* hq0, const int64_t* hq1,
-                                                      int64_t H, int req,
+                                                      int64_t nitems, int req,
+                                                      const int64_t* elem_fin,
                                                       const int64_t* dist_fin,
-                                                      unsigned long long* out) {
+                                                      unsigned long long* out6) {
     __shared__ int64_t sh[256 / kWave + 1];
-    const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    int64_t ne = 0, no = 0;
-    if (h < H) {
-        ne = hq1[h] - hq0[h];
-        for (int s = 0; s < req; ++s) no += dist_fin[h * req + s];
+    int64_t v[6] = {0, 0, 0, 0, 0, 0};
+    int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (; x < nitems; x += stride) {
+        const int64_t e = elem_fin[x];
+        if (e == 0) continue;
+        const int64_t h = x / req;
+        const int c = e > kDirectDense ? 0 : 3;
+        v[c] += e;
+        v[c + 1] += dist_fin[x];
+        v[c + 2] += hq1[h] - hq0[h];
     }
-    ne = block_reduce_sum<256>(ne, sh);
-    no = block_reduce_sum<256>(no, sh);
-    if (threadIdx.x == 0) {
-        atomicAdd(&out[0], (unsigned long long)ne);
-        atomicAdd(&out[1], (unsigned long long)no);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+        const int64_t r = block_reduce_sum<256>(v[i], sh);
+        if (threadIdx.x == 0 && r) atomicAdd(&out6[i], (unsigned long long)r);
     }
 }
 
 void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
-                   const int64_t* dist_fin, int64_t* out2, hipStream_t st) {
-    fill<int64_t>(out2, 2, 0, st);
-    if (H <= 0) return;
-    hipLaunchKernelGGL(k_direct_totals, dim3(grid_1d(ceil_div(H, 256))), dim3(256), 0, st, hq0,
-                       hq1, H, req, dist_fin, (unsigned long long*)out2);
+                   const int64_t* elem_fin, const int64_t* dist_fin, int64_t* out6,
+                   hipStream_t st) {
+    fill<int64_t>(out6, 6, 0, st);
+    const int64_t n = H * req;
+    if (n <= 0) return;
+    const int64_t blocks = std::min<int64_t>(ceil_div(n, 256), 4096);
+    hipLaunchKernelGGL(k_direct_totals, dim3(grid_1d(blocks)), dim3(256), 0, st, hq0, hq1, n, req,
+                       elem_fin, dist_fin, (unsigned long long*)out6);
     SG_LAUNCH_CHECK();
 }
 

@@ -255,9 +255,10 @@ void direct_classify(const int64_t* elem_fin, int64_t nitems, int32_t* items, in
                      Arena& ar, hipStream_t st);
 void direct_gather_values(const int64_t* bperm, const double* bval, int64_t nnz, double* out,
                           hipStream_t st);
-// out2[0] = A entries of the heavy rows, out2[1] = their output entries.
+// out6 = {dense items: products, outputs, A entries read; rank items: the same}.
 void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
-                   const int64_t* dist_fin, int64_t* out2, hipStream_t st);
+                   const int64_t* elem_fin, const int64_t* dist_fin, int64_t* out6,
+                   hipStream_t st);
 size_t direct_window_lds(int64_t W);
 void direct_accumulate(const DirectArgs& d, int bin, int64_t p0, int64_t n, hipStream_t st);
 

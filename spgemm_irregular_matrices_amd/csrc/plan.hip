@@ -108,7 +108,7 @@ struct spgemm_plan_s {
     int direct_req = 0;      // final chunks per heavy row on the direct path
     int64_t direct_W = 0;    // their width
     int64_t dir_bins[CB_COUNT + 1] = {};
-    int64_t dir_heavy_entries = 0, dir_heavy_outputs = 0;
+    int64_t dir_tot[6] = {};  // dense / rank items: products, outputs, A entries read
     // debug dumps (kept for single-batch products)
     bool dbg_valid = false;
     bool dbg_chat = false;  // C-hat was dumped (separate outer product only)
@@ -728,14 +728,13 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             int64_t* bins = ar.get<int64_t>("dbins", CB_COUNT + 1);
             direct_classify(elem_fin, p->H * req, ar.get<int32_t>("ditems", (size_t)(p->H * req)),
                             bins, ar, st);
-            int64_t* tot2 = ar.get<int64_t>("dtot", 2);
+            int64_t* tot6 = ar.get<int64_t>("dtot", 6);
             direct_totals(ar.get<int64_t>("h_q0", (size_t)p->H), ar.get<int64_t>("h_q1", (size_t)p->H),
-                          p->H, (int)req, dist_fin, tot2, st);
+                          p->H, (int)req, elem_fin, dist_fin, tot6, st);
             int64_t* hb = d2h(p, bins, CB_COUNT + 1, st);
             for (int b = 0; b <= CB_COUNT; ++b) p->dir_bins[b] = hb[b];
-            int64_t* ht = d2h(p, tot2, 2, st);
-            p->dir_heavy_entries = ht[0];
-            p->dir_heavy_outputs = ht[1];
+            int64_t* ht = d2h(p, tot6, 6, st);
+            for (int i = 0; i < 6; ++i) p->dir_tot[i] = ht[i];
             add_bytes(p, 0, SPGEMM_PHASE_HISTO, 20.0 * B.nnz + 4.0 * B.n * (req + 1) +
                                                     8.0 * p->H * req);
         }
@@ -874,15 +873,28 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         d.off = ar.get<int64_t>("doff", (size_t)(p->H * req));
         d.Ccol = C_col;
         d.Cval = C_val;
-        PhaseScope ps(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, st);
-        // B's values in the partitioned order (values may change between
-        // numeric calls; the structure may not)
-        direct_gather_values(ar.get<int64_t>("bperm", (size_t)B.nnz + 1), B.val, B.nnz, bpval, st);
-        for (int b = CB_DENSE; b <= CB_H8192; ++b)
-            direct_accumulate(d, b, p->dir_bins[b], p->dir_bins[b + 1] - p->dir_bins[b], st);
-        // minimum: A's heavy entries and B once, C's heavy entries once
-        add_bytes(p, 1, SPGEMM_PHASE_HEAVY_ACCUM,
-                  12.0 * p->dir_heavy_entries + 12.0 * B.nnz + 12.0 * p->dir_heavy_outputs);
+        // Bytes per class: every product's B operand (16-bit column and
+        // value, read once), every output entry written once, and each item's
+        // reads of its row's entries (column, B row start, value, slice bounds).
+        {
+            PhaseScope ps(p, 1, SPGEMM_PHASE_DIRECT_RANK, st);
+            // B's values in the split order (values may change between
+            // numeric calls; the structure may not)
+            direct_gather_values(ar.get<int64_t>("bperm", (size_t)B.nnz + 1), B.val, B.nnz, bpval,
+                                 st);
+            for (int b = CB_H128; b <= CB_H8192; ++b)
+                direct_accumulate(d, b, p->dir_bins[b], p->dir_bins[b + 1] - p->dir_bins[b], st);
+            add_bytes(p, 1, SPGEMM_PHASE_DIRECT_RANK,
+                      24.0 * B.nnz + 10.0 * p->dir_tot[3] + 12.0 * p->dir_tot[4] +
+                          28.0 * p->dir_tot[5]);
+        }
+        {
+            PhaseScope ps(p, 1, SPGEMM_PHASE_DIRECT_DENSE, st);
+            direct_accumulate(d, CB_DENSE, p->dir_bins[CB_DENSE],
+                              p->dir_bins[CB_DENSE + 1] - p->dir_bins[CB_DENSE], st);
+            add_bytes(p, 1, SPGEMM_PHASE_DIRECT_DENSE,
+                      10.0 * p->dir_tot[0] + 12.0 * p->dir_tot[1] + 28.0 * p->dir_tot[2]);
+        }
         return;
     }
 
