@@ -300,7 +300,7 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
 // flags; the flags then give every present column its rank in the sorted
 // output, as in the chunk window accumulator.
 constexpr int kDirectWinNT = 1024;
-constexpr int kDirectNE = 128;
+constexpr int kDirectNE = 256;
 constexpr int kDirectU = 4;  // products in flight per thread
 
 __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, int64_t p0,
