@@ -301,6 +301,8 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
 // output, as in the chunk window accumulator.
 constexpr int kDirectWinNT = 1024;
 constexpr int kDirectNE = 256;
+// one thread stages each entry of a round
+static_assert(kDirectNE <= kDirectWinNT, "a staged round holds at most one entry per thread");
 constexpr int kDirectU = 4;  // products in flight per thread
 
 __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, int64_t p0,

@@ -859,6 +859,8 @@ __global__ __launch_bounds__(kBslotNT) void k_bslot_rows(const int64_t* brp, con
 // reads of B are coalesced and no product needs a search.
 constexpr int kHsymNT = 1024;
 constexpr int kHsymEW = 1024;  // entries per staged window
+// one thread stages each entry of a window
+static_assert(kHsymEW <= kHsymNT, "a staged window holds at most one entry per thread");
 
 __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     const int64_t* arp, const int32_t* acol, const int64_t* brp, const int32_t* bcol,
