@@ -905,19 +905,33 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
         if (tt == 0) ppre[ne] = tot;
         __syncthreads();
         constexpr int U = 8;  // pieces in flight per wave
-        int j = 0;
+        int j0 = 0;  // entry of the wave's last piece (pieces rise per wave)
         for (int piece = w; piece < tot; piece += NW * U) {
+            // The entries of this iteration's pieces from one LDS read: lane l
+            // holds the piece prefix of entry j0+1+l, and a ballot counts the
+            // entries that start at or before a piece (prefixes rise). Only
+            // if all 64 do is the rest walked one entry at a time.
+            const int win = j0 + 1 + lane;
+            const int pw = win <= ne ? ppre[win] : INT_MAX;
             uint32_t c[U];
+            int jl = j0;
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
                 const int pu = piece + uu * NW;
                 c[uu] = 0xffffffffu;
                 if (pu < tot) {
-                    while (ppre[j + 1] <= pu) ++j;
+                    const int cnt = __popcll(__ballot(pw <= pu));
+                    int j = j0 + cnt;
+                    if (cnt == kWave) {
+                        j = jl > j ? jl : j;
+                        while (ppre[j + 1] <= pu) ++j;
+                    }
+                    jl = j;
                     const int off = (pu - ppre[j]) * kWave + lane;
                     if (off < nbv[j]) c[uu] = (uint32_t)bcol[bst[j] + off];
                 }
             }
+            j0 = jl;
 #pragma unroll
             for (int uu = 0; uu < U; ++uu)
                 if (c[uu] != 0xffffffffu) atomicOr(&bits[c[uu] >> 5], 1u << (c[uu] & 31));
