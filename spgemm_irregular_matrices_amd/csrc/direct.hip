@@ -136,9 +136,27 @@ struct DirectBinOf {
     }
 };
 
-void direct_classify(const int64_t* elem_fin, int64_t nitems, int32_t* items, int64_t* bins,
-                     Arena& ar, hipStream_t st) {
+// Per position of the class-ordered item list: the item's row's first A
+// entry and entry count, so that an item's kernel reads its header in one
+// step instead of item -> row -> entries.
+__global__ void k_item_heads(const int32_t* items, int64_t n, int req, const int64_t* hq0,
+                             const int64_t* hq1, int64_t* iq0, int32_t* ine) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= n) return;
+    const int64_t h = items[p] / req;
+    const int64_t q0 = hq0[h];
+    iq0[p] = q0;
+    ine[p] = (int32_t)(hq1[h] - q0);
+}
+
+void direct_classify(const int64_t* elem_fin, int64_t nitems, int req, const int64_t* hq0,
+                     const int64_t* hq1, int32_t* items, int64_t* iq0, int32_t* ine,
+                     int64_t* bins, Arena& ar, hipStream_t st) {
     partition(DirectBinOf{elem_fin}, nitems, CB_COUNT, items, (int32_t*)nullptr, bins, ar, st);
+    if (nitems <= 0) return;
+    hipLaunchKernelGGL(k_item_heads, dim3(grid_1d(ceil_div(nitems, 256))), dim3(256), 0, st, items,
+                       nitems, req, hq0, hq1, iq0, ine);
+    SG_LAUNCH_CHECK();
 }
 
 // ---------------------------------------------------------------- numeric
@@ -216,9 +234,10 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
     const int64_t item = blockIdx.x;
     if (item >= nitems) return;
     const int32_t x = d.items[p0 + item];
+    const int64_t q0 = d.iq0[p0 + item];
+    const int64_t q1 = q0 + d.ine[p0 + item];
     const int64_t h = x / d.req;
     const int s = (int)(x - h * d.req);
-    const int64_t q0 = d.hq0[h], q1 = d.hq1[h];
     for (int wd = tt; wd < NWD; wd += TW) bits[wd] = 0u;
 
     uint32_t idx[KPT];
@@ -323,9 +342,10 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     const int64_t item = blockIdx.x;
     if (item >= nitems) return;
     const int32_t x = d.items[p0 + item];
+    const int64_t q0 = d.iq0[p0 + item];
+    const int64_t q1 = q0 + d.ine[p0 + item];
     const int64_t h = x / d.req;
     const int s = (int)(x - h * d.req);
-    const int64_t q0 = d.hq0[h], q1 = d.hq1[h];
     for (int i = tt; i < NWD * 8; i += TW) flags[i] = 0u;
     for (int i = tt; i < W; i += TW) acc[i] = 0.0;
     uint8_t* fb = (uint8_t*)flags;
@@ -404,18 +424,25 @@ __global__ __launch_bounds__(256) void k_direct_totals(const int64_t* hq0, const
                                                       const int64_t* dist_fin,
                                                       unsigned long long* out6) {
     __shared__ int64_t sh[256 / kWave + 1];
-    int64_t v[6] = {0, 0, 0, 0, 0, 0};
+    int64_t dp = 0, dout = 0, de = 0, rp = 0, rout = 0, re = 0;
     int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (; x < nitems; x += stride) {
         const int64_t e = elem_fin[x];
         if (e == 0) continue;
         const int64_t h = x / req;
-        const int c = e > kDirectDense ? 0 : 3;
-        v[c] += e;
-        v[c + 1] += dist_fin[x];
-        v[c + 2] += hq1[h] - hq0[h];
+        const int64_t o = dist_fin[x], ne = hq1[h] - hq0[h];
+        if (e > kDirectDense) {
+            dp += e;
+            dout += o;
+            de += ne;
+        } else {
+            rp += e;
+            rout += o;
+            re += ne;
+        }
     }
+    const int64_t v[6] = {dp, dout, de, rp, rout, re};
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
         const int64_t r = block_reduce_sum<256>(v[i], sh);

@@ -233,6 +233,8 @@ struct DirectArgs {
     int logW;               // log2 of the slot width
     const int64_t* hq0;     // per heavy row: first A entry
     const int64_t* hq1;     // one past its last A entry
+    const int64_t* iq0;     // per position of items: its row's first A entry
+    const int32_t* ine;     // per position of items: its row's A entries
     const int32_t* Acol;
     const double* Aval;
     const int64_t* ebo;     // per A entry: start of its B row
@@ -251,8 +253,11 @@ void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int re
                     const int64_t* dist_fin, int64_t* off, hipStream_t st);
 // Stable partition of the items x in [0, nitems) by class (CB_* bins, from
 // the exact product count elem_fin[x]).
-void direct_classify(const int64_t* elem_fin, int64_t nitems, int32_t* items, int64_t* bins,
-                     Arena& ar, hipStream_t st);
+// Also writes, per position, the item's row's first A entry (iq0) and entry
+// count (ine).
+void direct_classify(const int64_t* elem_fin, int64_t nitems, int req, const int64_t* hq0,
+                     const int64_t* hq1, int32_t* items, int64_t* iq0, int32_t* ine,
+                     int64_t* bins, Arena& ar, hipStream_t st);
 void direct_gather_values(const int64_t* bperm, const double* bval, int64_t nnz, double* out,
                           hipStream_t st);
 // out6 = {dense items: products, outputs, A entries read; rank items: the same}.

@@ -726,8 +726,11 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
                            ar.get<int64_t>("bperm", (size_t)B.nnz + 1),
                            ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1), st);
             int64_t* bins = ar.get<int64_t>("dbins", CB_COUNT + 1);
-            direct_classify(elem_fin, p->H * req, ar.get<int32_t>("ditems", (size_t)(p->H * req)),
-                            bins, ar, st);
+            direct_classify(elem_fin, p->H * req, (int)req, ar.get<int64_t>("h_q0", (size_t)p->H),
+                            ar.get<int64_t>("h_q1", (size_t)p->H),
+                            ar.get<int32_t>("ditems", (size_t)(p->H * req)),
+                            ar.get<int64_t>("diq0", (size_t)(p->H * req)),
+                            ar.get<int32_t>("dine", (size_t)(p->H * req)), bins, ar, st);
             int64_t* tot6 = ar.get<int64_t>("dtot", 6);
             direct_totals(ar.get<int64_t>("h_q0", (size_t)p->H), ar.get<int64_t>("h_q1", (size_t)p->H),
                           p->H, (int)req, elem_fin, dist_fin, tot6, st);
@@ -864,6 +867,8 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         d.logW = ilog2(p->direct_W);
         d.hq0 = ar.get<int64_t>("h_q0", (size_t)p->H);
         d.hq1 = ar.get<int64_t>("h_q1", (size_t)p->H);
+        d.iq0 = ar.get<int64_t>("diq0", (size_t)(p->H * req));
+        d.ine = ar.get<int32_t>("dine", (size_t)(p->H * req));
         d.Acol = A.col;
         d.Aval = A.val;
         d.ebo = ar.get<int64_t>("ebo", (size_t)A.nnz + 1);
