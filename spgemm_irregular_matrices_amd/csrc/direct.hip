@@ -139,11 +139,11 @@ struct DirectBinOf {
 // Per position of the class-ordered item list: the item's row's first A
 // entry and entry count, so that an item's kernel reads its header in one
 // step instead of item -> row -> entries.
-__global__ void k_item_heads(const int32_t* items, int64_t n, int req, const int64_t* hq0,
+__global__ void k_item_heads(const int32_t* items, int64_t n, int logreq, const int64_t* hq0,
                              const int64_t* hq1, int64_t* iq0, int32_t* ine) {
     const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= n) return;
-    const int64_t h = items[p] / req;
+    const int64_t h = items[p] >> logreq;  // req is a power of two
     const int64_t q0 = hq0[h];
     iq0[p] = q0;
     ine[p] = (int32_t)(hq1[h] - q0);
@@ -155,7 +155,7 @@ void direct_classify(const int64_t* elem_fin, int64_t nitems, int req, const int
     partition(DirectBinOf{elem_fin}, nitems, CB_COUNT, items, (int32_t*)nullptr, bins, ar, st);
     if (nitems <= 0) return;
     hipLaunchKernelGGL(k_item_heads, dim3(grid_1d(ceil_div(nitems, 256))), dim3(256), 0, st, items,
-                       nitems, req, hq0, hq1, iq0, ine);
+                       nitems, ilog2(req), hq0, hq1, iq0, ine);
     SG_LAUNCH_CHECK();
 }
 
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
 // the algorithmic byte counts. out6 = {dense: products, outputs, entries,
 // rank: products, outputs, entries}.
 __global__ __launch_bounds__(256) void k_direct_totals(const int64_t* hq0, const int64_t* hq1,
-                                                      int64_t nitems, int req,
+                                                      int64_t nitems, int logreq,
                                                       const int64_t* elem_fin,
                                                       const int64_t* dist_fin,
                                                       unsigned long long* out6) {
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(256) void k_direct_totals(const int64_t* hq0, const
     for (; x < nitems; x += stride) {
         const int64_t e = elem_fin[x];
         if (e == 0) continue;
-        const int64_t h = x / req;
+        const int64_t h = x >> logreq;  // req is a power of two
         const int64_t o = dist_fin[x], ne = hq1[h] - hq0[h];
         if (e > kDirectDense) {
             dp += e;
@@ -457,8 +457,8 @@ void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
     const int64_t n = H * req;
     if (n <= 0) return;
     const int64_t blocks = std::min<int64_t>(ceil_div(n, 256), 4096);
-    hipLaunchKernelGGL(k_direct_totals, dim3(grid_1d(blocks)), dim3(256), 0, st, hq0, hq1, n, req,
-                       elem_fin, dist_fin, (unsigned long long*)out6);
+    hipLaunchKernelGGL(k_direct_totals, dim3(grid_1d(blocks)), dim3(256), 0, st, hq0, hq1, n,
+                       ilog2(req), elem_fin, dist_fin, (unsigned long long*)out6);
     SG_LAUNCH_CHECK();
 }
 

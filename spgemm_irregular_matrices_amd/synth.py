@@ -271,6 +271,16 @@ def from_rows(nrows: int, ncols: int, rows: list, vals: list | None = None) -> C
     return CSR(nrows, ncols, rowptr, col, val).check()
 
 
+def transpose(M: CSR) -> CSR:
+    """The transpose of M; each of its rows lists entries in ascending column order."""
+    rows = np.repeat(np.arange(M.nrows, dtype=np.int64), np.diff(M.rowptr))
+    order = np.argsort(M.col.astype(np.int64) * max(M.nrows, 1) + rows, kind="stable")
+    rowptr = np.zeros(M.ncols + 1, dtype=np.int64)
+    np.cumsum(np.bincount(M.col, minlength=M.ncols), out=rowptr[1:])
+    return CSR(M.ncols, M.nrows, rowptr, rows[order].astype(np.int32),
+               M.val[order].copy()).check()
+
+
 def identity(n: int) -> CSR:
     return CSR(n, n, np.arange(n + 1, dtype=np.int64), np.arange(n, dtype=np.int32),
                np.ones(n, dtype=np.float64))
