@@ -142,6 +142,15 @@ typedef struct {
                                      1 = first level formed in the multisplit tiles,
                                      2 = outer product into C-hat, 3 = direct          */
     int32_t reserved_stats;
+    /* Structural statistics of the product over all rows of A (the operator
+     * features of the SparseDitto page, Section 3.1, Eqs. 5 and 6): */
+    int64_t u_p95;                /* 95th percentile of u(i), as the upper end of the
+                                     histogram bucket that holds it: exact below 64,
+                                     then buckets 1/64 of an octave wide             */
+    double u_cv;                  /* coefficient of variation of u(i)             */
+    double f_u_le[3];             /* F_h: fraction of rows with u(i) <= h for
+                                     h = 512, 4096, 32768                         */
+    double gamma;                 /* sum of u(i) / nnz(C): products per output    */
 } spgemm_stats;
 
 /* One intermediate matrix kept by a plan with debug_dump = 1. */
@@ -169,7 +178,8 @@ SPGEMM_API int spgemm_plan_create(spgemm_plan* out, const spgemm_options* opt);
 /* Free the plan and every device buffer it holds. NULL is a no-op. */
 SPGEMM_API void spgemm_plan_destroy(spgemm_plan plan);
 
-/* Symbolic phase (gMAGNUS page, Section II-B and Algorithm 3 lines 1-25):
+/* Symbolic phase (gMAGNUS page, Section II-B and Algorithm 3 up to the
+ * PrefixSum of C.rowPtr):
  * computes C_rowptr (device, A.nrows+1 int64, caller-allocated) and the
  * total C_nnz (host out). The structure is the symbolic product: every
  * (i, j) reachable through a stored A[i,k] and a stored B[k,j], including
@@ -180,8 +190,8 @@ SPGEMM_API void spgemm_plan_destroy(spgemm_plan plan);
 SPGEMM_API int spgemm_symbolic(spgemm_plan plan, const spgemm_csr* A, const spgemm_csr* B,
                                int64_t* C_rowptr, int64_t* C_nnz, void* stream);
 
-/* Numeric phase (gMAGNUS page, Algorithm 1 outputs; Algorithm 3 lines
- * 26-27): fills C_col (int32) and C_val (fp64), C_nnz entries each,
+/* Numeric phase (gMAGNUS page, Algorithm 1 outputs; the numeric steps
+ * that close Algorithm 3): fills C_col (int32) and C_val (fp64), C_nnz entries each,
  * caller-allocated device buffers, given the C_rowptr that
  * spgemm_symbolic produced for the same A and B structure. Columns come out
  * strictly ascending within each row. Values are recomputed from A.val and

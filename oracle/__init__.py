@@ -131,3 +131,30 @@ def spgemm(A, B, nthreads: int | None = None):
     """All of C = A*B as (rowptr int64, col int32, val f64, abssum f64)."""
     r = spgemm_rows(A, B, None, nthreads)
     return r.rowptr, r.col, r.val, r.abssum
+
+
+def structural_stats(u: np.ndarray, nnz_c: int) -> dict:
+    """The operator-induced features of the SparseDitto page (Section 3.1):
+    total, maximum, 95th percentile and coefficient of variation of u(i), the
+    accumulator-fit fractions F_h = (1/m) * #{i : u(i) <= h} for h = 512, 4K
+    and 32K (Eq. 5), and gamma = sum_i u(i) / nnz(C) (Eq. 6). m counts every
+    row of A. The percentile is the nearest-rank one: the smallest value v
+    with at least 95% of the rows at u(i) <= v. The CV is the population
+    standard deviation over the mean (0 when the mean is 0).
+    """
+    u = np.asarray(u, dtype=np.int64)
+    m = u.size
+    total = int(u.sum())
+    out = {"sum": total, "max": int(u.max()) if m else 0}
+    if m == 0:
+        out.update(p95=0, cv=0.0, f=[0.0, 0.0, 0.0], gamma=0.0)
+        return out
+    srt = np.sort(u)
+    rank = -(-95 * m // 100)  # ceil(0.95 m), 1-based
+    out["p95"] = int(srt[rank - 1])
+    mean = total / m
+    dev = u.astype(np.float64) - mean
+    out["cv"] = float(np.sqrt(np.mean(dev * dev)) / mean) if mean > 0 else 0.0
+    out["f"] = [float(np.count_nonzero(u <= h)) / m for h in (512, 4096, 32768)]
+    out["gamma"] = total / nnz_c if nnz_c > 0 else 0.0
+    return out

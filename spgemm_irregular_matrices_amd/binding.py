@@ -68,7 +68,9 @@ class Stats(ctypes.Structure):
                 ("phase_bytes", (ctypes.c_double * NPH) * 2),
                 ("lds_bytes", ctypes.c_int64), ("light_rows", ctypes.c_int64),
                 ("light_products", ctypes.c_int64), ("numeric_path", ctypes.c_int32),
-                ("reserved_stats", ctypes.c_int32)]
+                ("reserved_stats", ctypes.c_int32), ("u_p95", ctypes.c_int64),
+                ("u_cv", ctypes.c_double), ("f_u_le", ctypes.c_double * 3),
+                ("gamma", ctypes.c_double)]
 
 
 class DebugMatrix(ctypes.Structure):
@@ -238,7 +240,8 @@ class Plan:
                                          "max_products", "heavy_rows", "heavy_products", "tau",
                                          "final_chunk_width", "nlevels", "nbatches", "chat_bytes",
                                          "lds_bytes", "light_rows", "light_products",
-                                         "numeric_path")}
+                                         "numeric_path", "u_p95", "u_cv", "gamma")}
+        d["f_u_le"] = [float(s.f_u_le[i]) for i in range(3)]
         d["vchunks"] = [int(s.vchunks[i]) for i in range(L)]
         d["level_in_elems"] = [int(s.level_in_elems[i]) for i in range(L)]
         d["level_heavy_chunks"] = [int(s.level_heavy_chunks[i]) for i in range(L)]

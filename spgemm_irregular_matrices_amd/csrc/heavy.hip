@@ -1,4 +1,4 @@
-// Heavy-row path of the gMAGNUS page (Algorithm 3 lines 6-20):
+// Heavy-row path of the gMAGNUS page (the heavy branch of Algorithm 3):
 // masked CSR-to-CSC of the heavy rows, the outer product into C-hat
 // (Section III-B, Algorithm 4), and the hierarchical multisplit that
 // reorders every heavy row into column-range chunks (Section III-C,

@@ -56,17 +56,20 @@ constexpr int kWinLarge = 1024;
 void launch_validate(const DevCSR& M, int* flag, hipStream_t st);
 
 // S[q] = sum_{q' < q} nnz(B[A.col[q'],:]) for q in [0, A.nnz] (InterOffsets,
-// Algorithm 3 line 3, at entry granularity: u(i) = S[rp[i+1]] - S[rp[i]]).
+// Algorithm 3, at entry granularity: u(i) = S[rp[i+1]] - S[rp[i]]).
 void entry_prefix(const DevCSR& A, const DevCSR& B, int64_t* S, Arena& ar, hipStream_t st);
 
 // Per B row: smallest and largest column (INT32_MAX / -1 for empty rows).
 void brow_minmax(const DevCSR& B, int32_t* bmin, int32_t* bmax, hipStream_t st);
 
 // Row classification and stable partition into RowBins.
-// stats[0]=sum u, [1]=max u, [2]=heavy rows, [3]=heavy products.
+// stats[0]=sum u, [1]=max u, [2]=heavy rows, [3]=heavy products, [4..6]=rows
+// with u <= 512, 4096, 32768, [7]=sum of u^2 (a double); uhist counts the
+// rows per u bucket (kUHistBuckets: u < 64 exactly, then 64 per octave).
+constexpr int kUHistBuckets = 4096;
 void classify_rows(const DevCSR& A, const int64_t* S, const int32_t* bmin, const int32_t* bmax,
                    int64_t tau, int32_t* rowlo, int32_t* perm, int64_t* bin_start,
-                   int64_t* stats, Arena& ar, hipStream_t st);
+                   int64_t* stats, int32_t* uhist, Arena& ar, hipStream_t st);
 
 // ---------------------------------------------------------------- heavy path
 // C-hat row pointers: exclusive scan of u over the heavy rows perm[0..H).

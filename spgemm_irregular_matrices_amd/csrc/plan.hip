@@ -1,8 +1,8 @@
 // Host orchestration and the C ABI (include/spgemm.h).
 //
-// spgemm_symbolic runs Algorithm 3 of the gMAGNUS page up to the prefix sum
-// of C.rowPtr (lines 1-25); spgemm_numeric runs the heavy path with values
-// and accumulates (lines 26-27). The structure the symbolic pass finds (row
+// spgemm_symbolic runs Algorithm 3 of the gMAGNUS page up to and including
+// the prefix sum of C.rowPtr; spgemm_numeric runs the heavy path with values
+// and then the accumulation steps. The structure the symbolic pass finds (row
 // bins, the masked CSC, every level's chunk partition, C-hat-reord row
 // pointers and chunk output offsets) is kept in the plan, so the numeric
 // pass does no histogramming, partitioning or blocking host reads.
@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <string>
 #include <vector>
+#include <cmath>
 
 #include "../../include/spgemm.h"
 #include "kernels.h"
@@ -76,12 +77,15 @@ struct BatchState {
 
 }  // namespace
 
+// Pinned host words: 64 for small scalars, then the u histogram (int32).
+constexpr int kHostWords = 64 + sg::kUHistBuckets / 2;
+
 struct spgemm_plan_s {
     spgemm_options opt{};
     Arena ar;
     int device = 0;
     int64_t dev_lds = 0;
-    int64_t* host = nullptr;  // pinned staging for small device-to-host reads
+    int64_t* host = nullptr;  // pinned staging for small device-to-host reads (kHostWords)
     // state of the last successful symbolic call
     bool ready = false;
     int64_t An = 0, Am = 0, Annz = 0, Bn = 0, Bm = 0, Bnnz = 0, Cnnz = 0;
@@ -580,6 +584,37 @@ void heavy_offsets(spgemm_plan p, const int32_t* hrows, const int64_t* C_rp, hip
     }
 }
 
+// ---------------------------------------------------------------- row statistics
+// The structural statistics of the products the SparseDitto page uses as
+// operator features (Section 3.1, Eqs. 5 and 6): p95 and coefficient of
+// variation of u(i), the fractions F_h of rows with u(i) <= h for h = 512,
+// 4K, 32K; gamma (sum u / nnz(C)) is set once nnz(C) is known.
+static void row_statistics(spgemm_plan p, int64_t n, const int32_t* hist) {
+    spgemm_stats& S = p->stats;
+    double u2;
+    memcpy(&u2, &p->host[23], sizeof(double));
+    const double mean = n > 0 ? (double)S.sum_products / (double)n : 0.0;
+    const double var = n > 0 ? u2 / (double)n - mean * mean : 0.0;
+    S.u_cv = mean > 0 ? std::sqrt(var > 0 ? var : 0.0) / mean : 0.0;
+    for (int k = 0; k < 3; ++k) S.f_u_le[k] = n > 0 ? (double)p->host[20 + k] / (double)n : 0.0;
+    // p95: the upper end of the first bucket at which 95% of the rows are reached
+    const int64_t need = (n * 95 + 99) / 100;
+    int64_t run = 0;
+    S.u_p95 = 0;
+    for (int b = 0; b < kUHistBuckets && n > 0; ++b) {
+        run += hist[b];
+        if (run >= need) {
+            if (b < 64) {
+                S.u_p95 = b;
+            } else {
+                const int e = (b - 64) / 64 + 6, f = (b - 64) % 64;
+                S.u_p95 = ((int64_t)(64 + f + 1) << (e - 6)) - 1;
+            }
+            break;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- symbolic
 int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* C_rp,
                       hipStream_t st) {
@@ -616,26 +651,31 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     int32_t* rowlo = ar.get<int32_t>("rowlo", (size_t)n + 1);
     int32_t* rowperm = ar.get<int32_t>("rowperm", (size_t)n + 1);
     int64_t* rowbins = ar.get<int64_t>("rowbins", RB_COUNT + 1);
-    int64_t* st4 = ar.get<int64_t>("stats4", 4);
+    int64_t* st4 = ar.get<int64_t>("stats4", 8);
+    int32_t* uhist = ar.get<int32_t>("uhist", kUHistBuckets);
     {
         PhaseScope ps(p, 0, SPGEMM_PHASE_BINNING, st);
         int32_t* bmin = ar.get<int32_t>("bmin", (size_t)B.n + 1);
         int32_t* bmax = ar.get<int32_t>("bmax", (size_t)B.n + 1);
         brow_minmax(B, bmin, bmax, st);
-        classify_rows(A, S, bmin, bmax, q.tau, rowlo, rowperm, rowbins, st4, ar, st);
+        classify_rows(A, S, bmin, bmax, q.tau, rowlo, rowperm, rowbins, st4, uhist, ar, st);
         add_bytes(p, 0, SPGEMM_PHASE_BINNING, 8.0 * (n + 1) + 8.0 * n + 4.0 * n);
     }
-    // Synchronize() of Algorithm 3 line 5: workspace is sized from these
+    // the Synchronize() after ThreshPartition in Algorithm 3: workspace is sized from these
     {
         SG_HIP(hipMemcpyAsync(p->host, rowbins, (RB_COUNT + 1) * sizeof(int64_t),
                               hipMemcpyDeviceToHost, st));
-        SG_HIP(hipMemcpyAsync(p->host + 16, st4, 4 * sizeof(int64_t), hipMemcpyDeviceToHost, st));
+        SG_HIP(hipMemcpyAsync(p->host + 16, st4, 8 * sizeof(int64_t), hipMemcpyDeviceToHost, st));
+        int32_t* hist = (int32_t*)(p->host + 64);
+        SG_HIP(hipMemcpyAsync(hist, uhist, kUHistBuckets * sizeof(int32_t),
+                              hipMemcpyDeviceToHost, st));
         SG_HIP(hipStreamSynchronize(st));
         for (int b = 0; b <= RB_COUNT; ++b) p->row_bins[b] = p->host[b];
         p->stats.sum_products = p->host[16];
         p->stats.max_products = p->host[17];
         p->stats.heavy_rows = p->host[18];
         p->stats.heavy_products = p->host[19];
+        row_statistics(p, n, hist);
     }
     p->H = p->row_bins[RB_HEAVY + 1] - p->row_bins[RB_HEAVY];
     p->Nh = p->stats.heavy_products;
@@ -644,7 +684,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     int64_t* cnt_row = ar.get<int64_t>("cnt_row", (size_t)n + 1);
     fill<int64_t>(cnt_row, n, 0, st);
 
-    // light rows (Algorithm 3 line 22)
+    // light rows (Algorithm 3, the light-row symbolic step)
     RowItems ri{};
     ri.A = A;
     ri.B = B;
@@ -659,7 +699,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             accumulate_rows(ri, b, p->row_bins[b], p->row_bins[b + 1] - p->row_bins[b], false, st);
     }
 
-    // heavy rows (Algorithm 3 lines 6-21), batch by batch
+    // heavy rows (Algorithm 3, the heavy-row branch), batch by batch
     p->L = 0;
     p->batches.clear();
     if (p->H > 0) {
@@ -794,7 +834,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
         }
     }
 
-    // C.rowPtr (Algorithm 3 lines 23-25)
+    // C.rowPtr (Algorithm 3, the closing PrefixSum)
     {
         PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
         scan_exclusive(LoadI64{cnt_row}, n, C_rp, ar, st);
@@ -819,6 +859,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     p->stats.lds_bytes = q.slm;
     p->stats.light_rows = p->row_bins[RB_EMPTY] - p->row_bins[RB_WIN64];
     p->stats.light_products = p->stats.sum_products - p->stats.heavy_products;
+    p->stats.gamma = nnz_c > 0 ? (double)p->stats.sum_products / (double)nnz_c : 0.0;
     return nnz_c;
 }
 
@@ -1064,7 +1105,7 @@ SPGEMM_API int spgemm_plan_create(spgemm_plan* out, const spgemm_options* opt) {
             return SPGEMM_ERR_HIP;
         }
         p->dev_lds = (int64_t)prop.sharedMemPerBlock;
-        if (hipHostMalloc((void**)&p->host, 64 * sizeof(int64_t), hipHostMallocDefault) !=
+        if (hipHostMalloc((void**)&p->host, kHostWords * sizeof(int64_t), hipHostMallocDefault) !=
             hipSuccess) {
             delete p;
             return SPGEMM_ERR_HIP;

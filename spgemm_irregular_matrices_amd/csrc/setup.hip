@@ -105,12 +105,23 @@ void brow_minmax(const DevCSR& B, int32_t* bmin, int32_t* bmax, hipStream_t st) 
 // Per row: u(i), the row's output column span (from the B rows' spans), and
 // its bin. Heavy rows (u > tau) are the rows whose intermediate products
 // would overflow a local-memory accumulator (Section II-B, Eq. 4).
+// Histogram bucket of u >= 0 for the p95 statistic: u < 64 exactly, above
+// that 64 buckets per octave (the 6 bits below the leading one).
+__device__ __forceinline__ int u_bucket(int64_t u) {
+    if (u < 64) return (int)u;
+    const int e = 63 - __clzll((unsigned long long)u);
+    return 64 + (e - 6) * 64 + (int)((u >> (e - 6)) & 63);
+}
+
 __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const int32_t* acol,
                                                        int64_t n, const int64_t* S,
                                                        const int32_t* bmin, const int32_t* bmax,
                                                        int64_t tau, uint8_t* bin, int32_t* rowlo,
-                                                       int64_t* stats) {
+                                                       int64_t* stats, int32_t* uhist) {
     __shared__ int64_t sh[8];
+    __shared__ double shd[8];
+    __shared__ int hsmall[64];  // the exact buckets u < 64, gathered per block
+    if (threadIdx.x < 64) hsmall[threadIdx.x] = 0;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     int64_t u = 0, heavy = 0, hprod = 0;
     if (i < n) {
@@ -151,6 +162,19 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
     int64_t su = block_reduce_sum<256>(u, sh);
     int64_t sh_heavy = block_reduce_sum<256>(heavy, sh);
     int64_t sh_hprod = block_reduce_sum<256>(hprod, sh);
+    // the structural statistics of the rows' products: F_h counts, sum of
+    // squares (for the coefficient of variation) and the u histogram
+    const bool in = i < n;
+    const int64_t c512 = block_reduce_sum<256>((int64_t)(in && u <= 512), sh);
+    const int64_t c4k = block_reduce_sum<256>((int64_t)(in && u <= 4096), sh);
+    const int64_t c32k = block_reduce_sum<256>((int64_t)(in && u <= 32768), sh);
+    const double u2 = block_reduce_sum<256>(in ? (double)u * (double)u : 0.0, shd);
+    if (in) {
+        if (u < 64) atomicAdd(&hsmall[u], 1);
+        else atomicAdd(&uhist[u_bucket(u)], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64 && hsmall[threadIdx.x]) atomicAdd(&uhist[threadIdx.x], hsmall[threadIdx.x]);
     // max via wave shuffles, then one atomic per wave
     int64_t mu = u;
 #pragma unroll
@@ -164,6 +188,10 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
         atomicAdd((unsigned long long*)&stats[0], (unsigned long long)su);
         atomicAdd((unsigned long long*)&stats[2], (unsigned long long)sh_heavy);
         atomicAdd((unsigned long long*)&stats[3], (unsigned long long)sh_hprod);
+        atomicAdd((unsigned long long*)&stats[4], (unsigned long long)c512);
+        atomicAdd((unsigned long long*)&stats[5], (unsigned long long)c4k);
+        atomicAdd((unsigned long long*)&stats[6], (unsigned long long)c32k);
+        atomicAdd((double*)&stats[7], u2);
     }
 }
 
@@ -174,12 +202,13 @@ struct RowBinOf {
 
 void classify_rows(const DevCSR& A, const int64_t* S, const int32_t* bmin, const int32_t* bmax,
                    int64_t tau, int32_t* rowlo, int32_t* perm, int64_t* bin_start,
-                   int64_t* stats, Arena& ar, hipStream_t st) {
+                   int64_t* stats, int32_t* uhist, Arena& ar, hipStream_t st) {
     uint8_t* bin = ar.get<uint8_t>("row_bin", (size_t)A.n + 1);
-    fill<int64_t>(stats, 4, 0, st);
+    fill<int64_t>(stats, 8, 0, st);
+    fill<int32_t>(uhist, kUHistBuckets, 0, st);
     if (A.n > 0) {
         hipLaunchKernelGGL(k_classify_rows, dim3(grid_1d(ceil_div(A.n, 256))), dim3(256), 0, st,
-                           A.rp, A.col, A.n, S, bmin, bmax, tau, bin, rowlo, stats);
+                           A.rp, A.col, A.n, S, bmin, bmax, tau, bin, rowlo, stats, uhist);
         SG_LAUNCH_CHECK();
     }
     partition(RowBinOf{bin}, A.n, RB_COUNT, perm, (int32_t*)nullptr, bin_start, ar, st);

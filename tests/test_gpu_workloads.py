@@ -112,10 +112,31 @@ def _check_properties(A, B, C, u):
     torch.cuda.empty_cache()
 
 
+def _bucket_upper(v: int) -> int:
+    """Upper end of the stats record's u-histogram bucket holding v: exact
+    below 64, then 64 buckets per octave."""
+    if v < 64:
+        return v
+    e = v.bit_length() - 1
+    f = (v >> (e - 6)) & 63
+    return ((64 + f + 1) << (e - 6)) - 1
+
+
+def _check_structural_stats(st, u):
+    """The stats record's structural statistics against the oracle's, on all rows."""
+    ref = oracle.structural_stats(u, st["nnz_c"])
+    assert st["sum_products"] == ref["sum"] and st["max_products"] == ref["max"]
+    assert st["u_p95"] == _bucket_upper(ref["p95"])
+    assert st["u_cv"] == pytest.approx(ref["cv"], rel=1e-9, abs=1e-12)
+    assert st["f_u_le"] == ref["f"]
+    assert st["gamma"] == ref["gamma"]
+
+
 def test_rmat10_all_rows():
     A, B = synth.workload("rmat10_ef8")
     C, st = _multiply(A, B)
     compare(A, B, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy())
+    _check_structural_stats(st, oracle.row_products(A, B))
 
 
 def test_banded_1M_all_rows():
@@ -129,6 +150,7 @@ def test_banded_1M_all_rows():
     exp = np.minimum(n - 1, i + 16) - np.maximum(0, i - 16) + 1
     assert np.array_equal(np.diff(rp), exp)
     compare(A, B, rp, C.col.cpu().numpy(), C.val.cpu().numpy())
+    _check_structural_stats(st, oracle.row_products(A, B))
 
 
 @pytest.mark.parametrize("name,batch", [("rmat18_ef16", 0), ("rmat20_ef8", 0),
@@ -148,5 +170,6 @@ def test_large_sampled_rows_and_properties(name, batch):
     assert rp[-1] == st["nnz_c"]
     compare(A, B, fake_rp, col, val, rows=rows, check_all_rowptr=False)
     _check_properties(A, B, C, u)
+    _check_structural_stats(st, u)
     del C
     torch.cuda.empty_cache()

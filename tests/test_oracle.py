@@ -9,7 +9,9 @@ The oracle (``oracle/``) is checked against
 * the closed form of the all-ones banded square;
 * the row-sum identity C*1 = A*(B*1);
 * scipy.sparse's product;
-* brute-force u(i) = sum of nnz(B[k,:]) over row i of A.
+* brute-force u(i) = sum of nnz(B[k,:]) over row i of A;
+* closed forms of the structural statistics (SparseDitto page, Section 3.1,
+  Eqs. 5 and 6) on a staircase product whose u(i) = i * L is known.
 A plausible mistake (a dropped term, a wrong index, a transposed operand,
 an unsorted or merged-away column) breaks at least one of these.
 """
@@ -338,3 +340,46 @@ def test_stage_chunks_partition_rows():
         assert dist.sum() == c.size
         assert np.array_equal(stages.chunk_counts(cols, W, 0, nch),
                               np.bincount(cols // W, minlength=nch))
+
+
+# ---------------------------------------------------------------- structural statistics
+def _staircase(L):
+    """Row i of A (100 rows) holds columns 0..i-1; every row of B holds columns
+    0..L-1. So u(i) = i*L, C's row i has L entries for i > 0, nnz(C) = 99*L."""
+    m = 100
+    lens = np.arange(m, dtype=np.int64)
+    arp = np.zeros(m + 1, dtype=np.int64)
+    np.cumsum(lens, out=arp[1:])
+    acol = np.concatenate([np.arange(i, dtype=np.int32) for i in range(m)])
+    A = synth.CSR(m, m, arp, acol, np.ones(acol.size))
+    brp = np.arange(m + 1, dtype=np.int64) * L
+    bcol = np.tile(np.arange(L, dtype=np.int32), m)
+    B = synth.CSR(m, L, brp, bcol, np.ones(bcol.size))
+    return A, B
+
+
+@pytest.mark.parametrize("L", [32, 512])
+def test_structural_stats_closed_form(L):
+    A, B = _staircase(L)
+    u = oracle.row_products(A, B)
+    assert np.array_equal(u, np.arange(100) * L)
+    rp, _, _, _ = oracle.spgemm(A, B)
+    assert rp[-1] == 99 * L
+    st = oracle.structural_stats(u, int(rp[-1]))
+    assert st["sum"] == 4950 * L and st["max"] == 99 * L
+    # nearest rank: the 95th smallest of 0, L, ..., 99L is 94L
+    assert st["p95"] == 94 * L
+    # mean 49.5 L, population variance (100^2 - 1)/12 * L^2
+    assert st["cv"] == pytest.approx(math.sqrt(9999 / 12) / 49.5, rel=1e-14)
+    # F_h counts rows with i*L <= h, the bound included
+    exp = [(min(h // L, 99) + 1) / 100 for h in (512, 4096, 32768)]
+    assert st["f"] == exp
+    assert exp[0] == (0.17 if L == 32 else 0.02)
+    assert st["gamma"] == 50.0
+
+
+def test_structural_stats_degenerate():
+    st = oracle.structural_stats(np.zeros(0, dtype=np.int64), 0)
+    assert st == {"sum": 0, "max": 0, "p95": 0, "cv": 0.0, "f": [0.0, 0.0, 0.0], "gamma": 0.0}
+    st = oracle.structural_stats(np.full(20, 7), 140)
+    assert st["p95"] == 7 and st["cv"] == 0.0 and st["f"] == [1.0, 1.0, 1.0] and st["gamma"] == 1.0
