@@ -853,7 +853,11 @@ __global__ __launch_bounds__(kBslotNT) void k_bslot_rows(const int64_t* brp, con
 
 // Distinct columns: one work group per heavy row keeps a one-bit-per-column
 // bitmap of the row's column range in LDS; the row's element counts per slot
-// are the sums of its entries' B-row slot vectors. The row's A entries are taken in
+// are the sums of its entries' B-row slot vectors. A row with far more
+// products than a work group's share of the pass (power-law rows) is split
+// by its product range over several work groups, which OR their bitmaps
+// into a global one and add their element counts; a last pass counts the
+// bits of the split rows. The row's A entries are taken in
 // windows staged in LDS; each entry's B row is cut into pieces of 64
 // products and the waves take pieces in turn, one product per lane, so the
 // reads of B are coalesced and no product needs a search.
@@ -862,10 +866,65 @@ constexpr int kHsymEW = 1024;  // entries per staged window
 // one thread stages each entry of a window
 static_assert(kHsymEW <= kHsymNT, "a staged window holds at most one entry per thread");
 
+constexpr int kHsymMaxSplit = 64;      // work groups per row at most
+constexpr int64_t kHsymSplitMin = 16384;  // products per work group at least
+
+// Per heavy row: (work groups) | (1 if split) << 32, for the exclusive scan
+// that gives each row its first work group and its split-row index.
+struct HsymSplitOf {
+    const int64_t* arp;
+    const int64_t* S;
+    const int32_t* hrows;
+    int64_t T;
+    __device__ int64_t operator()(int64_t h) const {
+        const int32_t r = hrows[h];
+        const int64_t a0 = arp[r], a1 = arp[r + 1];
+        const int64_t u = S[a1] - S[a0];
+        int64_t ns = u > T ? (u + T - 1) / T : 1;
+        ns = min(ns, (int64_t)kHsymMaxSplit);
+        ns = max((int64_t)1, min(ns, a1 - a0));
+        return ns | (ns > 1 ? (int64_t(1) << 32) : 0);
+    }
+};
+
+__device__ __forceinline__ int64_t hsym_blocks(int64_t packed) { return packed & 0xffffffffLL; }
+__device__ __forceinline__ int64_t hsym_split(int64_t packed) { return packed >> 32; }
+
+// Work group -> heavy row map, split row -> heavy row map, and the split
+// rows' element counts cleared (their work groups add into them).
+__global__ void k_hsym_map(const int64_t* off, int64_t H, int req, int32_t* bmap, int32_t* smap,
+                           int64_t* elem_fin) {
+    const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (h >= H) return;
+    const int64_t b0 = hsym_blocks(off[h]), b1 = hsym_blocks(off[h + 1]);
+    for (int64_t b = b0; b < b1; ++b) bmap[b] = (int32_t)h;
+    if (b1 - b0 > 1) {
+        smap[hsym_split(off[h])] = (int32_t)h;
+        for (int sl = 0; sl < req; ++sl) elem_fin[h * req + sl] = 0;
+    }
+}
+
+// First entry e in [lo, hi] with S[e] >= x (S rises over a row's entries).
+__device__ __forceinline__ int64_t first_at_or_above(const int64_t* S, int64_t lo, int64_t hi,
+                                                     int64_t x) {
+    while (lo < hi) {
+        const int64_t mid = lo + ((hi - lo) >> 1);
+        if (S[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+struct HsymSplitArgs {
+    const int64_t* S;      // entry product prefix
+    const int64_t* off;    // packed scan of HsymSplitOf (H + 1), or null: no split
+    const int32_t* bmap;   // work group -> heavy row
+    uint32_t* gbits;       // split rows' bitmaps (split index * nwords)
+};
+
 __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     const int64_t* arp, const int32_t* acol, const int64_t* brp, const int32_t* bcol,
     const int32_t* hrows, int req, int nwords, const int32_t* bslot, int64_t* elem_fin,
-    int64_t* dist_fin) {
+    int64_t* dist_fin, HsymSplitArgs sp, int64_t H) {
     extern __shared__ int64_t lds_s[];
     constexpr int NW = kHsymNT / kWave;
     int64_t* bst = lds_s;                                   // kHsymEW B row starts
@@ -876,9 +935,18 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     int* dsl = ppre + kHsymEW + 1;                          // req distinct counts
     uint32_t* bits = (uint32_t*)(dsl + req);                // nwords
     __shared__ int scan_sh[NW + 1];
+    __shared__ int64_t range_sh[2];
     const int tt = threadIdx.x;
     const int w = tt / kWave, lane = lane_id();
-    const int64_t h = blockIdx.x;
+    int64_t h = blockIdx.x, ns = 1, sidx = 0;
+    if (sp.off) {
+        // the whole work group leaves together when the grid's bound exceeds the split count
+        if ((int64_t)blockIdx.x >= hsym_blocks(sp.off[H])) return;
+        h = sp.bmap[blockIdx.x];
+        const int64_t o = sp.off[h];
+        ns = hsym_blocks(sp.off[h + 1]) - hsym_blocks(o);
+        sidx = hsym_split(o);
+    }
     for (int i = tt; i < nwords; i += kHsymNT) bits[i] = 0u;
     for (int i = tt; i < req; i += kHsymNT) {
         dsl[i] = 0;
@@ -886,7 +954,21 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     }
     __syncthreads();
     const int32_t r = hrows[h];
-    const int64_t a0 = arp[r], a1 = arp[r + 1];
+    int64_t a0 = arp[r], a1 = arp[r + 1];
+    if (ns > 1) {
+        // this work group's part: the entries whose products start in its
+        // 1/ns of the row's product range
+        if (tt == 0) {
+            const int64_t part = (int64_t)blockIdx.x - hsym_blocks(sp.off[h]);
+            const int64_t s0 = sp.S[a0], u = sp.S[a1] - s0;
+            const int64_t lo = s0 + u * part / ns, hi = s0 + u * (part + 1) / ns;
+            range_sh[0] = first_at_or_above(sp.S, a0, a1, lo);
+            range_sh[1] = part == ns - 1 ? a1 : first_at_or_above(sp.S, a0, a1, hi);
+        }
+        __syncthreads();
+        a0 = range_sh[0];
+        a1 = range_sh[1];
+    }
     for (int64_t ew = a0; ew < a1; ew += kHsymEW) {
         const int ne = (int)min((int64_t)kHsymEW, a1 - ew);
         int pc = 0;
@@ -952,6 +1034,16 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
         }
         __syncthreads();
     }
+    if (ns > 1) {
+        // a part of a split row: add into the row's global counts and bitmap
+        uint32_t* g = sp.gbits + sidx * (int64_t)nwords;
+        for (int i = tt; i < nwords; i += kHsymNT)
+            if (bits[i]) atomicOr(&g[i], bits[i]);
+        for (int sl = tt; sl < req; sl += kHsymNT)
+            if (esl[sl])
+                atomicAdd((unsigned long long*)&elem_fin[h * req + sl], esl[sl]);
+        return;
+    }
     // distinct columns per finest slot: popcounts of the slot's words
     const int wps = nwords / req;  // words per slot (>= 1)
     for (int i = tt; i < nwords; i += kHsymNT) {
@@ -972,14 +1064,42 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     }
 }
 
+// Distinct columns of the split rows: popcounts of their global bitmaps.
+__global__ __launch_bounds__(kHsymNT) void k_hsym_finalize(const int64_t* off, int64_t H,
+                                                          const int32_t* smap,
+                                                          const uint32_t* gbits, int req,
+                                                          int nwords, int64_t* dist_fin) {
+    extern __shared__ int dsl_f[];
+    const int64_t b = blockIdx.x;
+    if (b >= hsym_split(off[H])) return;
+    const int tt = threadIdx.x, lane = lane_id();
+    const int64_t h = smap[b];
+    for (int i = tt; i < req; i += kHsymNT) dsl_f[i] = 0;
+    __syncthreads();
+    const uint32_t* g = gbits + b * (int64_t)nwords;
+    const int wps = nwords / req;
+    for (int i = tt; i < nwords; i += kHsymNT) {
+        int pc = __popc(g[i]);
+        if (wps >= kWave) {
+            pc = wave_reduce_sum(pc);
+            if (lane == 0 && pc) atomicAdd(&dsl_f[i / wps], pc);
+        } else if (pc) {
+            atomicAdd(&dsl_f[i / wps], pc);
+        }
+    }
+    __syncthreads();
+    for (int sl = tt; sl < req; sl += kHsymNT) dist_fin[h * req + sl] = dsl_f[sl];
+}
+
 size_t heavy_symbolic_lds(int64_t ppow, int64_t req) {
     return (size_t)kHsymEW * 8 + (size_t)req * 8 + (size_t)kHsymEW * 4 * 2 +
            (size_t)(kHsymEW + 1) * 4 + (size_t)req * 4 + (size_t)(ppow / 32) * 4;
 }
 
-bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int32_t* hrows, int64_t H,
-                    int64_t ppow, int64_t wfin, int32_t* bslot, int32_t* bsplit,
-                    int64_t* elem_fin, int64_t* dist_fin, hipStream_t st) {
+bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
+                    int64_t H, int64_t Nh, int64_t max_u, int ncu, int64_t dev_lds, int64_t ppow,
+                    int64_t wfin, int32_t* bslot, int32_t* bsplit, int64_t* elem_fin,
+                    int64_t* dist_fin, Arena& ar, hipStream_t st) {
     if (H <= 0) return false;
     const int64_t req = ppow / wfin;
     const int logW = ilog2(wfin);
@@ -1004,11 +1124,40 @@ bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int32_t* hrows, int6
         }
     }
     const size_t lds = heavy_symbolic_lds(ppow, req);
+    const int nwords = (int)(ppow / 32);
+    // a work group's share: a quarter of the pass over the work groups the
+    // device holds at once, and at least kHsymSplitMin products
+    const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(2, dev_lds / (int64_t)lds));
+    const int64_t T = std::max<int64_t>(kHsymSplitMin, ceil_div(Nh, 4 * (int64_t)ncu * per_cu));
+    HsymSplitArgs sp{S, nullptr, nullptr, nullptr};
+    int64_t grid = H, nsplit_max = 0;
+    if (max_u > T) {
+        // sum over rows of the work groups is at most H + Nh / T, and every
+        // split row has more than T products
+        nsplit_max = std::min<int64_t>(H, Nh / T);
+        grid = H + Nh / T;
+        int64_t* off = ar.get<int64_t>("hsym_off", (size_t)H + 1);
+        scan_exclusive(HsymSplitOf{A.rp, S, hrows, T}, H, off, ar, st);
+        int32_t* bmap = ar.get<int32_t>("hsym_bmap", (size_t)grid);
+        int32_t* smap = ar.get<int32_t>("hsym_smap", (size_t)nsplit_max + 1);
+        uint32_t* gbits = ar.get<uint32_t>("hsym_gbits", (size_t)nsplit_max * nwords + 1);
+        fill<uint32_t>(gbits, nsplit_max * (int64_t)nwords, 0u, st);
+        hipLaunchKernelGGL(k_hsym_map, dim3(grid_1d(ceil_div(H, 256))), dim3(256), 0, st, off, H,
+                           (int)req, bmap, smap, elem_fin);
+        SG_LAUNCH_CHECK();
+        sp = HsymSplitArgs{S, off, bmap, gbits};
+    }
     SG_HIP(hipFuncSetAttribute((const void*)k_heavy_symbolic,
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-    hipLaunchKernelGGL(k_heavy_symbolic, dim3(grid_1d(H)), dim3(kHsymNT), lds, st, A.rp, A.col,
-                       B.rp, B.col, hrows, (int)req, (int)(ppow / 32), bslot, elem_fin, dist_fin);
+    hipLaunchKernelGGL(k_heavy_symbolic, dim3(grid_1d(grid)), dim3(kHsymNT), lds, st, A.rp, A.col,
+                       B.rp, B.col, hrows, (int)req, nwords, bslot, elem_fin, dist_fin, sp, H);
     SG_LAUNCH_CHECK();
+    if (sp.off && nsplit_max > 0) {
+        hipLaunchKernelGGL(k_hsym_finalize, dim3(grid_1d(nsplit_max)), dim3(kHsymNT),
+                           (size_t)req * 4, st, sp.off, H, (const int32_t*)ar.get<int32_t>("hsym_smap", (size_t)nsplit_max + 1),
+                           (const uint32_t*)sp.gbits, (int)req, nwords, dist_fin);
+        SG_LAUNCH_CHECK();
+    }
     return split_done;
 }
 

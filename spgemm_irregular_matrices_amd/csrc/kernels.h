@@ -164,16 +164,20 @@ void expand_multisplit(const LevelGeom& g, const FusedRows& fr, const DevCSR& A,
 void chunk_colbase(int64_t nparents, int nch, int64_t width, const int32_t* parent_inv,
                    const int32_t* parent_base, int32_t* out, hipStream_t st);
 
-// Fused symbolic pass over the heavy rows (one work group per row): per
-// finest chunk slot of width wfin, the element count and the number of
-// distinct columns. Needs heavy_symbolic_lds(ppow, ppow/wfin) bytes of LDS.
+// Fused symbolic pass over the heavy rows (a work group per row, several for
+// a row far above the average share): per finest chunk slot of width wfin,
+// the element count and the number of distinct columns. Needs
+// heavy_symbolic_lds(ppow, ppow/wfin) bytes of LDS.
 size_t heavy_symbolic_lds(int64_t ppow, int64_t req);
 // bslot (B.n * (ppow/wfin) int32) receives every B row's entries per slot.
 // If bsplit (B.n * (ppow/wfin + 1) int32) is given it may also receive the
 // rows' slot starts (their exclusive prefix); returns whether it did.
-bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int32_t* hrows, int64_t H,
-                    int64_t ppow, int64_t wfin, int32_t* bslot, int32_t* bsplit,
-                    int64_t* elem_fin, int64_t* dist_fin, hipStream_t st);
+// S is the entry product prefix, Nh the heavy rows' products, max_u the
+// largest u(i); ncu and dev_lds size the per-work-group share.
+bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
+                    int64_t H, int64_t Nh, int64_t max_u, int ncu, int64_t dev_lds, int64_t ppow,
+                    int64_t wfin, int32_t* bslot, int32_t* bsplit, int64_t* elem_fin,
+                    int64_t* dist_fin, Arena& ar, hipStream_t st);
 // Counts, distinct counts and first finest slot of every natural chunk of a
 // level, summed from the finest slots (g slots per chunk).
 void level_from_slots(const int64_t* parent_slot0, const int32_t* parent_inv, int64_t nparents,

@@ -85,6 +85,7 @@ struct spgemm_plan_s {
     Arena ar;
     int device = 0;
     int64_t dev_lds = 0;
+    int dev_cus = 1;
     int64_t* host = nullptr;  // pinned staging for small device-to-host reads (kHostWords)
     // state of the last successful symbolic call
     bool ready = false;
@@ -751,9 +752,10 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
             int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
             bsplit_done = heavy_symbolic(
-                A, B, hrows, p->H, q.ppow, wfin, bslot,
+                A, B, S, hrows, p->H, p->Nh, p->stats.max_products, p->dev_cus, p->dev_lds,
+                q.ppow, wfin, bslot,
                 p->direct ? ar.get<int32_t>("bsplit", (size_t)(B.n * (req + 1) + 1)) : nullptr,
-                elem_fin, dist_fin, st);
+                elem_fin, dist_fin, ar, st);
             add_bytes(p, 0, SPGEMM_PHASE_HISTO, 4.0 * p->Nh + 16.0 * p->H * req);
         }
         if (p->direct) {
@@ -1105,6 +1107,7 @@ SPGEMM_API int spgemm_plan_create(spgemm_plan* out, const spgemm_options* opt) {
             return SPGEMM_ERR_HIP;
         }
         p->dev_lds = (int64_t)prop.sharedMemPerBlock;
+        p->dev_cus = std::max(1, prop.multiProcessorCount);
         if (hipHostMalloc((void**)&p->host, kHostWords * sizeof(int64_t), hipHostMallocDefault) !=
             hipSuccess) {
             delete p;

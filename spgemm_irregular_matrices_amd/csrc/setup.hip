@@ -169,9 +169,21 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
     const int64_t c4k = block_reduce_sum<256>((int64_t)(in && u <= 4096), sh);
     const int64_t c32k = block_reduce_sum<256>((int64_t)(in && u <= 32768), sh);
     const double u2 = block_reduce_sum<256>(in ? (double)u * (double)u : 0.0, shd);
-    if (in) {
-        if (u < 64) atomicAdd(&hsmall[u], 1);
-        else atomicAdd(&uhist[u_bucket(u)], 1);
+    // the lanes of a wave that share a bucket add once (a banded matrix puts
+    // nearly every row in one bucket); buckets below 64 gather in LDS first
+    {
+        const int b = in ? u_bucket(u) : -1;
+        uint64_t act = __ballot(b >= 0);
+        while (act) {
+            const int leader = __ffsll((unsigned long long)act) - 1;
+            const int lb = __shfl(b, leader);
+            const uint64_t m = __ballot(b == lb);
+            if (lane_id() == leader) {
+                if (lb < 64) atomicAdd(&hsmall[lb], __popcll(m));
+                else atomicAdd(&uhist[lb], __popcll(m));
+            }
+            act &= ~m;
+        }
     }
     __syncthreads();
     if (threadIdx.x < 64 && hsmall[threadIdx.x]) atomicAdd(&uhist[threadIdx.x], hsmall[threadIdx.x]);

@@ -75,6 +75,31 @@ def test_rmat10_forced_heavy(tau, width, cap, levels, mode):
     compare(A, A, rp, col, val)
 
 
+def _power_law_rows():
+    """Rows far above the symbolic pass's per-work-group share: 128K, 48K and
+    24K products, plus a 3-entry row whose first B row holds 60,000 entries
+    (split into three parts by product range, the middle one empty)."""
+    n, m, p = 3000, 1 << 15, 1 << 17
+    lens = synth.zipf_lengths(n, 2.1, 20, seed=61)
+    lens[:4] = [8000, 3000, 1500, 3]
+    A = synth.distinct_uniform_rows(lens, m, seed=62, value_seed=63)
+    blens = np.full(m, 16, dtype=np.int64)
+    c = A.col[A.rowptr[3]:A.rowptr[4]]
+    blens[c[0]], blens[c[1]], blens[c[2]] = 60000, 1, 1
+    B = synth.distinct_uniform_rows(blens, p, seed=64, value_seed=65)
+    return A, B
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_power_law_rows_split_over_work_groups(mode):
+    A, B = _power_law_rows()
+    u = oracle.row_products(A, B)
+    assert u[0] == 128000 and u[3] == 60002
+    rp, col, val, st = run_gpu(A, B, symbolic_mode=mode[0], numeric_mode=mode[1])
+    assert st["heavy_rows"] >= 4 and st["max_products"] == int(u.max())
+    compare(A, B, rp, col, val)
+
+
 def test_fig1_stages_and_product():
     with open(os.path.join(GOLDEN, "fig1_heavy_rows.json")) as f:
         g = json.load(f)
