@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include <stdexcept>
@@ -69,16 +70,43 @@ __device__ __forceinline__ int lane_prefix(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Inclusive scan of 32-bit integers across the 64 lanes with DPP moves:
+// shifts by 1, 2, 4 and 8 lanes inside each row of 16 (lanes shifted in
+// from outside the row add 0), then row 0's total into row 1 and row 2's
+// into row 3 (row_bcast:15), then lane 31's total into rows 2 and 3
+// (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_scan_i32(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
+}
+
 // Inclusive scan across the 64 lanes of a wavefront.
 template <class T>
 __device__ __forceinline__ T wave_inclusive_scan(T v) {
-    const int l = lane_id();
+    if constexpr (sizeof(T) == 4 && std::is_integral<T>::value) {
+        return (T)wave_inclusive_scan_i32((int)v);
+    } else {
+        const int l = lane_id();
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        T o = __shfl_up(v, d, kWave);
-        if (l >= d) v += o;
+        for (int d = 1; d < kWave; d <<= 1) {
+            T o = __shfl_up(v, d, kWave);
+            if (l >= d) v += o;
+        }
+        return v;
     }
-    return v;
+}
+
+// Orders this wave's LDS accesses around it (a wave's LDS operations run in
+// issue order; this keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <class T>

@@ -213,6 +213,56 @@ __device__ __forceinline__ int direct_find(const int* s_pre, int ne, int p, int 
     return j;
 }
 
+// Entry of product base + lane for a chunk of 64 consecutive products whose
+// first product lies in entry jc: the entries after jc that start inside
+// the chunk are read 64 at a time (lane w holds entry jc+1+w), and each
+// lane keeps the last one starting at or before its product. Entries start
+// in increasing order, so the ballot's bits are taken lowest first.
+__device__ __forceinline__ int chunk_entry(const int* s_pre, int ne, int base, int jc, int lane) {
+    int e = jc;
+    for (int jw = jc;; jw += kWave) {
+        const int win = jw + 1 + lane;
+        const int dw = win < ne ? s_pre[win] - base : kWave;
+        uint64_t m = __ballot(dw < kWave);
+        const bool full = m == ~0ull;
+        while (m) {
+            const int w = __ffsll((unsigned long long)m) - 1;
+            if (lane >= __builtin_amdgcn_readlane(dw, w)) e = jw + 1 + w;
+            m &= m - 1;
+        }
+        if (!full) return e;
+    }
+}
+
+// The same lookup with a per-wave count of entry starts per lane when more
+// than kWalkMax entries start inside the chunk: lane w adds one to the byte
+// of lane d_w in the wave's 16 LDS words `hw` (zero on entry and on exit),
+// and a scan of the counts gives every lane the entries starting at or
+// before it.
+constexpr int kWalkMax = 4;
+__device__ __forceinline__ int chunk_entry_fast(const int* s_pre, int ne, int base, int jc, int lane,
+                                                uint32_t* hw) {
+    const int win = jc + 1 + lane;
+    const int dw = win < ne ? s_pre[win] - base : kWave;
+    uint64_t m = __ballot(dw < kWave);
+    if (m == ~0ull) return chunk_entry(s_pre, ne, base, jc, lane);
+    if (__popcll(m) <= kWalkMax) {
+        int e = jc;
+        while (m) {
+            const int w = __ffsll((unsigned long long)m) - 1;
+            if (lane >= __builtin_amdgcn_readlane(dw, w)) e = jc + 1 + w;
+            m &= m - 1;
+        }
+        return e;
+    }
+    if (dw < kWave) atomicAdd(&hw[dw >> 2], 1u << ((dw & 3) * 8));
+    wave_lds_sync();
+    const int cnt = (int)((hw[lane >> 2] >> ((lane & 3) * 8)) & 0xffu);
+    wave_lds_sync();
+    if (lane < kWave / 4) hw[lane] = 0u;
+    return jc + wave_inclusive_scan_i32(cnt);
+}
+
 // Bitmap-rank accumulation of items with at most TW*KPT products: the
 // products are formed into registers, then accumulated as in the chunk
 // accumulator (bitmap of the chunk's columns, word-popcount prefix for the
@@ -323,6 +373,8 @@ constexpr int kDirectNE = 256;
 // one thread stages each entry of a round
 static_assert(kDirectNE <= kDirectWinNT, "a staged round holds at most one entry per thread");
 constexpr int kDirectU = 4;  // products in flight per thread
+// per-wave entry-start counts: 16 words for each of the block's waves
+constexpr int kWinHistWords = (kDirectWinNT / kWave) * (kWave / 4);
 
 __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, int64_t p0,
                                                                int64_t nitems) {
@@ -334,6 +386,9 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     uint32_t* flags = (uint32_t*)(acc + W);          // W bytes
     uint32_t* bits = flags + NWD * 8;                // NWD
     int* wpre = (int*)(bits + NWD);                  // NWD
+    // while products accumulate, bits and wpre hold the waves' entry-start
+    // counts (kWinHistWords words from bits on; the launch sizes them)
+    uint32_t* hw_all = bits;
     __shared__ int s_pre[kDirectNE];
     __shared__ int64_t s_bo[kDirectNE];
     __shared__ double s_a[kDirectNE];
@@ -348,23 +403,37 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     const int s = (int)(x - h * d.req);
     for (int i = tt; i < NWD * 8; i += TW) flags[i] = 0u;
     for (int i = tt; i < W; i += TW) acc[i] = 0.0;
+    for (int i = tt; i < kWinHistWords; i += TW) hw_all[i] = 0u;
     uint8_t* fb = (uint8_t*)flags;
+    const int wv = tt / kWave, lane = lane_id();
+    uint32_t* hw = hw_all + wv * (kWave / 4);
+    constexpr int NWV = TW / kWave;
     for (int64_t qb = q0; qb < q1; qb += kDirectNE) {
         __syncthreads();  // zeroing done / previous round's staging consumed
         const int tot = direct_stage<TW, kDirectNE>(d, qb + tt, q1, s, s_pre, s_bo, s_a, red_sh);
         const int ne = (int)min((int64_t)kDirectNE, q1 - qb);
-        int j = 0;
-        for (int pb = tt; pb < tot; pb += TW * kDirectU) {
+        // each wave takes a contiguous run of 64-product chunks; lane l of a
+        // chunk takes product base + l
+        const int nch = (tot + kWave - 1) / kWave;
+        const int cpw = (nch + NWV - 1) / NWV;
+        const int c0 = wv * cpw, c1 = min(nch, c0 + cpw);
+        int jc = c0 < c1 ? direct_find(s_pre, ne, c0 * kWave, 0) : 0;
+        for (int cb = c0; cb < c1; cb += kDirectU) {
             int64_t bi[kDirectU];
             double av[kDirectU];
 #pragma unroll
             for (int u = 0; u < kDirectU; ++u) {
-                const int p = pb + u * TW;
                 bi[u] = -1;
-                if (p < tot) {
-                    j = direct_find(s_pre, ne, p, j);
-                    bi[u] = s_bo[j] + (p - s_pre[j]);
-                    av[u] = s_a[j];
+                if (cb + u < c1) {
+                    const int base = (cb + u) * kWave;
+                    int e = chunk_entry_fast(s_pre, ne, base, jc, lane, hw);
+                    // the chunk's last product's entry starts the next chunk
+                    jc = __builtin_amdgcn_readlane(e, kWave - 1);
+                    const int p = base + lane;
+                    if (p < tot) {
+                        bi[u] = s_bo[e] + (p - s_pre[e]);
+                        av[u] = s_a[e];
+                    }
                 }
             }
             uint32_t c[kDirectU];
@@ -473,7 +542,9 @@ static void launch_direct_rank(const DirectArgs& d, int64_t p0, int64_t n, hipSt
     SG_LAUNCH_CHECK();
 }
 
-size_t direct_window_lds(int64_t W) { return (size_t)W * 9 + (size_t)(W / 32) * 8; }
+size_t direct_window_lds(int64_t W) {
+    return (size_t)W * 9 + std::max<size_t>((size_t)(W / 32) * 8, (size_t)kWinHistWords * 4);
+}
 
 void direct_accumulate(const DirectArgs& d, int bin, int64_t p0, int64_t n, hipStream_t st) {
     if (n <= 0) return;

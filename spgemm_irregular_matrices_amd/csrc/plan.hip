@@ -87,6 +87,10 @@ struct spgemm_plan_s {
     int64_t dev_lds = 0;
     int dev_cus = 1;
     int64_t* host = nullptr;  // pinned staging for small device-to-host reads (kHostWords)
+    // the light rows' numeric pass runs on a stream of its own, beside the
+    // heavy rows (the two queues of Algorithm 3), joined before returning
+    hipStream_t lst = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     // state of the last successful symbolic call
     bool ready = false;
     int64_t An = 0, Am = 0, Annz = 0, Bn = 0, Bm = 0, Bnnz = 0, Cnnz = 0;
@@ -894,10 +898,30 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
     ri.Crp = C_rp;
     ri.Ccol = C_col;
     ri.Cval = C_val;
+    // light rows on the plan's second stream when there are heavy rows to
+    // overlap with; the caller's stream waits for them on every way out
+    const bool fork = p->H > 0 && p->row_bins[RB_H8192 + 1] > p->row_bins[RB_WIN64];
+    struct Join {
+        bool on;
+        hipStream_t st;
+        hipEvent_t ev;
+        ~Join() {
+            if (on) (void)hipStreamWaitEvent(st, ev, 0);
+        }
+    } join{false, st, p->ev_join};
+    const hipStream_t lst = fork ? p->lst : st;
+    if (fork) {
+        SG_HIP(hipEventRecord(p->ev_fork, st));
+        SG_HIP(hipStreamWaitEvent(p->lst, p->ev_fork, 0));
+    }
     {
-        PhaseScope ps(p, 1, SPGEMM_PHASE_LIGHT_ACCUM, st);
+        PhaseScope ps(p, 1, SPGEMM_PHASE_LIGHT_ACCUM, lst);
         for (int b = RB_WIN64; b <= RB_H8192; ++b)
-            accumulate_rows(ri, b, p->row_bins[b], p->row_bins[b + 1] - p->row_bins[b], true, st);
+            accumulate_rows(ri, b, p->row_bins[b], p->row_bins[b + 1] - p->row_bins[b], true, lst);
+    }
+    if (fork) {
+        SG_HIP(hipEventRecord(p->ev_join, p->lst));
+        join.on = true;
     }
     if (p->H == 0) return;
 
@@ -1113,6 +1137,12 @@ SPGEMM_API int spgemm_plan_create(spgemm_plan* out, const spgemm_options* opt) {
             delete p;
             return SPGEMM_ERR_HIP;
         }
+        if (hipStreamCreateWithFlags(&p->lst, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming) != hipSuccess) {
+            spgemm_plan_destroy(p);
+            return SPGEMM_ERR_HIP;
+        }
         *out = p;
         return SPGEMM_OK;
     });
@@ -1122,6 +1152,9 @@ SPGEMM_API void spgemm_plan_destroy(spgemm_plan p) {
     if (!p) return;
     (void)hipDeviceSynchronize();
     for (auto e : p->evpool) (void)hipEventDestroy(e);
+    if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
+    if (p->ev_join) (void)hipEventDestroy(p->ev_join);
+    if (p->lst) (void)hipStreamDestroy(p->lst);
     if (p->host) (void)hipHostFree(p->host);
     p->ar.release();
     delete p;
