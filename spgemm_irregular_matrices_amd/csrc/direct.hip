@@ -275,7 +275,6 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
     double* vals = (double*)lds_r;                  // TW*KPT
     uint32_t* bits = (uint32_t*)(vals + TW * KPT);  // NWD
     int* wpre = (int*)(bits + NWD);                 // NWD
-    int32_t* scol = (int32_t*)(wpre + NWD);         // TW*KPT
     __shared__ int s_pre[TW];
     __shared__ int64_t s_bo[TW];
     __shared__ double s_a[TW];
@@ -345,22 +344,20 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
             atomicAdd(&vals[rank], v[k]);
         }
     }
+    // columns straight from the bitmap words, values once all are summed
     const int32_t lo = s << d.logW;
+    const int64_t off = d.off[x];
     for (int wd = w0; wd < w1; ++wd) {
         uint32_t bw = bits[wd];
-        int r = wpre[wd];
+        int64_t r = off + wpre[wd];
         while (bw) {
             const int b = __ffs(bw) - 1;
             bw &= bw - 1;
-            scol[r++] = lo + wd * 32 + b;
+            d.Ccol[r++] = lo + wd * 32 + b;
         }
     }
     __syncthreads();
-    const int64_t off = d.off[x];
-    for (int r = tt; r < tot; r += TW) {
-        d.Ccol[off + r] = scol[r];
-        d.Cval[off + r] = vals[r];
-    }
+    for (int r = tt; r < tot; r += TW) d.Cval[off + r] = vals[r];
 }
 
 // Dense window accumulation of the large items: the item's entries are
@@ -534,7 +531,7 @@ void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
 template <int TW, int KPT>
 static void launch_direct_rank(const DirectArgs& d, int64_t p0, int64_t n, hipStream_t st) {
     const int64_t W = int64_t(1) << d.logW;
-    const size_t lds = (size_t)TW * KPT * 12 + (size_t)(W / 32) * 8;
+    const size_t lds = (size_t)TW * KPT * 8 + (size_t)(W / 32) * 8;
     auto kern = k_direct_rank<TW, KPT>;
     SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds));
