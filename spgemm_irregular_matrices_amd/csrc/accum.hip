@@ -109,6 +109,88 @@ __device__ __forceinline__ double* out_vals(const RowItems& ri, const ChunkItems
     else return ci.Cval;
 }
 
+// ---------------------------------------------------------------- light rows
+// A light row's products are read round by round: up to TW of the row's A
+// entries are staged in the team's LDS (B row start, A value, exclusive
+// prefix of B row lengths), then each thread reads U products at a time,
+// stride TW, each found by a search of the staged prefix, so that a product
+// costs one dependent global read (its B entry) instead of a walk of the
+// entry offsets in global memory.
+template <int TW>
+struct RowStage {
+    int pre[TW + 1];
+    int64_t b0[TW];
+    double a[TW];
+};
+
+// Synchronises a team: one wave, or the whole work group.
+template <int TW>
+__device__ __forceinline__ void team_sync() {
+    if constexpr (TW == kWave) wave_lds_sync();
+    else __syncthreads();
+}
+
+// Last staged entry j in [j, ne) with pre[j] <= t (pre rises; pre[j] <= t).
+__device__ __forceinline__ int stage_find(const int* pre, int ne, int t, int j) {
+    int jh = ne;
+    while (jh - j > 1) {
+        const int mid = (j + jh) >> 1;
+        if (pre[mid] <= t) j = mid; else jh = mid;
+    }
+    return j;
+}
+
+template <int TW, int U, bool NUM, class F>
+__device__ __forceinline__ void row_products(const RowItems& ri, const ItemHdr& h,
+                                             RowStage<TW>& sg_, int* red_sh, int tt, F&& f) {
+    for (int64_t qb = h.a0; qb < h.a1; qb += TW) {
+        const int ne = (int)min((int64_t)TW, h.a1 - qb);
+        team_sync<TW>();  // the previous round's staging is consumed
+        int len = 0;
+        if (tt < ne) {
+            const int64_t q = qb + tt;
+            const int32_t k = ri.A.col[q];
+            const int64_t b0 = ri.B.rp[k];
+            len = (int)(ri.B.rp[k + 1] - b0);
+            sg_.b0[tt] = b0;
+            if constexpr (NUM) sg_.a[tt] = ri.A.val[q];
+        }
+        int tot;
+        const int pre = team_exclusive_scan<TW>(len, red_sh, &tot);
+        sg_.pre[tt] = pre;
+        team_sync<TW>();
+        int j = 0;
+        for (int tb = tt; tb < tot; tb += TW * U) {
+            int64_t bi[U];
+            double av[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int t = tb + u * TW;
+                bi[u] = -1;
+                av[u] = 0.0;
+                if (t < tot) {
+                    j = stage_find(sg_.pre, ne, t, j);
+                    bi[u] = sg_.b0[j] + (t - sg_.pre[j]);
+                    if constexpr (NUM) av[u] = sg_.a[j];
+                }
+            }
+            int32_t c[U];
+            double v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                v[u] = 0.0;
+                if (bi[u] >= 0) {
+                    c[u] = ri.B.col[bi[u]];
+                    if constexpr (NUM) v[u] = av[u] * ri.B.val[bi[u]];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (bi[u] >= 0) f(c[u], v[u]);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- hash
 // One item per work group of TW threads; the table has S = 2^LOGS slots.
 template <int MODE, bool NUM, int TW, int LOGS>
@@ -133,12 +215,8 @@ __global__ __launch_bounds__(TW) void k_acc_hash(RowItems ri, ChunkItems ci, int
 
     int fresh = 0;
     {
-        int64_t cur = h.a0;
         constexpr uint32_t smask = (uint32_t)S - 1;
-        for (int64_t t = tt; t < h.count; t += TW) {
-            int32_t c;
-            double v = 0.0;
-            load_elem<MODE, NUM>(ri, ci, h, t, cur, 0, c, v);
+        auto insert = [&](int32_t c, double v) {
             uint32_t key = (uint32_t)c;
             uint32_t slot = (key * 2654435769u) >> (32 - LOGS);
             for (;;) {
@@ -151,6 +229,18 @@ __global__ __launch_bounds__(TW) void k_acc_hash(RowItems ri, ChunkItems ci, int
                 slot = (slot + 1) & smask;
             }
             if constexpr (NUM) atomicAdd(&vals[slot], v);
+        };
+        if constexpr (MODE == MODE_ROW) {
+            __shared__ RowStage<TW> stage;
+            row_products<TW, 2, NUM>(ri, h, stage, red_sh, tt, insert);
+        } else {
+            int64_t cur = 0;
+            for (int64_t t = tt; t < h.count; t += TW) {
+                int32_t c;
+                double v = 0.0;
+                load_elem<MODE, NUM>(ri, ci, h, t, cur, 0, c, v);
+                insert(c, v);
+            }
         }
     }
     const int nnz = team_sum<TW>(fresh, red_sh);
@@ -339,9 +429,20 @@ __global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, ChunkItems c
     __syncthreads();
     const int32_t lo = active ? lo_sh[team] : 0;
     uint8_t* fb = (uint8_t*)flags;
-    if (active) {
+    if constexpr (MODE == MODE_ROW) {
+        __shared__ RowStage<TW> stages[NI];
+        if (active) {
+            row_products<TW, 4, NUM>(ri, h, stages[team], red_sh, tt, [&](int32_t c, double v) {
+                const uint32_t idx = (uint32_t)(c - lo);
+                if (idx < (uint32_t)W) {
+                    fb[idx] = 1;
+                    if constexpr (NUM) atomicAdd(&acc[idx], v);
+                }
+            });
+        }
+    } else if (active) {
         int64_t cur = h.a0;
-        constexpr int U = (MODE == MODE_CHUNK) ? 4 : 1;  // loads in flight per thread
+        constexpr int U = 4;  // loads in flight per thread
         for (int64_t t0 = tt; t0 < h.count; t0 += (int64_t)TW * U) {
             int32_t c[U];
             double v[U];

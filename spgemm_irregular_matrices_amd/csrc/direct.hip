@@ -214,38 +214,22 @@ __device__ __forceinline__ int direct_find(const int* s_pre, int ne, int p, int 
 }
 
 // Entry of product base + lane for a chunk of 64 consecutive products whose
-// first product lies in entry jc: the entries after jc that start inside
-// the chunk are read 64 at a time (lane w holds entry jc+1+w), and each
-// lane keeps the last one starting at or before its product. Entries start
-// in increasing order, so the ballot's bits are taken lowest first.
-__device__ __forceinline__ int chunk_entry(const int* s_pre, int ne, int base, int jc, int lane) {
-    int e = jc;
-    for (int jw = jc;; jw += kWave) {
-        const int win = jw + 1 + lane;
-        const int dw = win < ne ? s_pre[win] - base : kWave;
-        uint64_t m = __ballot(dw < kWave);
-        const bool full = m == ~0ull;
-        while (m) {
-            const int w = __ffsll((unsigned long long)m) - 1;
-            if (lane >= __builtin_amdgcn_readlane(dw, w)) e = jw + 1 + w;
-            m &= m - 1;
-        }
-        if (!full) return e;
-    }
-}
-
-// The same lookup with a per-wave count of entry starts per lane when more
-// than kWalkMax entries start inside the chunk: lane w adds one to the byte
-// of lane d_w in the wave's 16 LDS words `hw` (zero on entry and on exit),
-// and a scan of the counts gives every lane the entries starting at or
-// before it.
+// first product lies in entry jc. Lane w reads the start of entry jc+1+w;
+// with at most kWalkMax of them inside the chunk, each lane keeps the last
+// one starting at or before its product (the ballot's bits taken lowest
+// first, as starts rise); with more, lane w adds one to the byte of lane d_w
+// in the wave's 16 LDS words `hw` (zero on entry and on exit) and a scan of
+// the counts gives every lane the entries starting at or before it; if all
+// 64 start inside the chunk, each lane searches the staged prefix.
 constexpr int kWalkMax = 4;
 __device__ __forceinline__ int chunk_entry_fast(const int* s_pre, int ne, int base, int jc, int lane,
                                                 uint32_t* hw) {
     const int win = jc + 1 + lane;
     const int dw = win < ne ? s_pre[win] - base : kWave;
     uint64_t m = __ballot(dw < kWave);
-    if (m == ~0ull) return chunk_entry(s_pre, ne, base, jc, lane);
+    // 64 or more entries start inside the chunk (mostly empty slices, as
+    // when B rows are short against the number of slots): a search per lane
+    if (m == ~0ull) return direct_find(s_pre, ne, base + lane, jc);
     if (__popcll(m) <= kWalkMax) {
         int e = jc;
         while (m) {
