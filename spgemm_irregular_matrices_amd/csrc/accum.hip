@@ -191,6 +191,106 @@ __device__ __forceinline__ void row_products(const RowItems& ri, const ItemHdr& 
     }
 }
 
+// ---------------------------------------------------------------- thread-local rows
+// Rows with at most N products (N = 8, 16, 32) take one thread each: the
+// products go into registers in Gustavson order, a bitonic network of
+// compare-exchanges at fixed places sorts them by column (places past u hold
+// an all-ones key and sort last), and runs of equal columns are summed on
+// the way out. Every index is a compile-time constant after unrolling, so
+// the arrays stay in registers.
+template <bool NUM, int N>
+__device__ __forceinline__ void bitonic_regs(uint32_t (&k)[N], double (&v)[N]) {
+#pragma unroll
+    for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int j = i ^ stride;
+                if (j > i) {
+                    const bool up = (i & size) == 0;
+                    const uint32_t ki = k[i], kj = k[j];
+                    const bool sw = up ? (ki > kj) : (ki < kj);
+                    k[i] = sw ? kj : ki;
+                    k[j] = sw ? ki : kj;
+                    if constexpr (NUM) {
+                        const double vi = v[i], vj = v[j];
+                        v[i] = sw ? vj : vi;
+                        v[j] = sw ? vi : vj;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <bool NUM, int N>
+__global__ __launch_bounds__(256) void k_acc_thread(RowItems ri, int64_t p0, int64_t nitems) {
+    constexpr uint32_t kNone = 0xffffffffu;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= nitems) return;
+    const int32_t r = ri.perm[p0 + i];
+    const int64_t a1 = ri.A.rp[r + 1];
+    int64_t q = ri.A.rp[r], b = 0, b1 = 0;
+    double a = 0.0;
+    uint32_t k[N];
+    double v[N];
+#pragma unroll
+    for (int t = 0; t < N; ++t) {
+        k[t] = kNone;
+        v[t] = 0.0;
+        while (b == b1 && q < a1) {  // next entry with products left
+            const int32_t kk = ri.A.col[q];
+            b = ri.B.rp[kk];
+            b1 = ri.B.rp[kk + 1];
+            if constexpr (NUM) a = ri.A.val[q];
+            ++q;
+        }
+        if (b < b1) {
+            k[t] = (uint32_t)ri.B.col[b];
+            if constexpr (NUM) v[t] = a * ri.B.val[b];
+            ++b;
+        }
+    }
+    bitonic_regs<NUM, N>(k, v);
+    if constexpr (!NUM) {
+        int cnt = k[0] != kNone;
+#pragma unroll
+        for (int t = 1; t < N; ++t) cnt += k[t] != kNone && k[t] != k[t - 1];
+        ri.cnt[r] = cnt;
+    } else {
+        const int64_t off = ri.Crp[r];
+        int64_t w = off;
+        uint32_t cur = k[0];
+        double acc = v[0];
+#pragma unroll
+        for (int t = 1; t < N; ++t) {
+            if (k[t] != cur) {
+                if (cur != kNone) {
+                    ri.Ccol[w] = (int32_t)cur;
+                    ri.Cval[w] = acc;
+                    ++w;
+                }
+                cur = k[t];
+                acc = v[t];
+            } else {
+                acc += v[t];
+            }
+        }
+        if (cur != kNone) {
+            ri.Ccol[w] = (int32_t)cur;
+            ri.Cval[w] = acc;
+        }
+    }
+}
+
+template <bool NUM, int N>
+static void launch_thread(const RowItems& ri, int64_t p0, int64_t n, hipStream_t st) {
+    hipLaunchKernelGGL((k_acc_thread<NUM, N>), dim3(grid_1d(ceil_div(n, 256))), dim3(256), 0, st,
+                       ri, p0, n);
+    SG_LAUNCH_CHECK();
+}
+
 // ---------------------------------------------------------------- hash
 // One item per work group of TW threads; the table has S = 2^LOGS slots.
 template <int MODE, bool NUM, int TW, int LOGS>
@@ -570,6 +670,9 @@ template <bool NUM>
 static void rows_impl(const RowItems& it, int bin, int64_t p0, int64_t n, hipStream_t st) {
     ChunkItems none{};
     switch (bin) {
+        case RB_T8: launch_thread<NUM, 8>(it, p0, n, st); break;
+        case RB_T16: launch_thread<NUM, 16>(it, p0, n, st); break;
+        case RB_T32: launch_thread<NUM, 32>(it, p0, n, st); break;
         case RB_WIN64: launch_window<MODE_ROW, NUM, 64, 4>(it, none, p0, n, kWinSmall, st); break;
         case RB_WIN1024:
             launch_window<MODE_ROW, NUM, 256, 1>(it, none, p0, n, kWinLarge, st);

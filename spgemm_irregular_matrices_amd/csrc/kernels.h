@@ -19,6 +19,9 @@ struct DevCSR {
 // bin order, so heavy rows come first.
 enum RowBin : int {
     RB_HEAVY = 0,  // u > tau: outer product + multisplit path
+    RB_T8,         // light, u <= 8: one thread per row, products sorted in registers
+    RB_T16,        // light, u <= 16
+    RB_T32,        // light, u <= 32
     RB_WIN64,      // light, output span <= 64: wave-per-row dense window
     RB_WIN1024,    // light, output span <= 1024: block dense window
     RB_H128,       // light hash bins by u (table slots >= 2u, alpha = 2)
@@ -47,6 +50,8 @@ constexpr int kHashSlots[4] = {128, 512, 2048, 8192};
 constexpr int64_t kHashMaxItems[4] = {64, 256, 1024, 8191};
 // Light chunks no wider than this use the bitmap-rank accumulator.
 constexpr int64_t kRankMaxWidth = 65536;
+// Largest u of each thread-local bin (one thread per row, registers only).
+constexpr int64_t kThreadMaxItems[3] = {8, 16, 32};
 constexpr int kWinSmall = 64;
 constexpr int kWinLarge = 1024;
 

@@ -700,7 +700,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     ri.hash_top_logS = q.hash_top_logS;
     {
         PhaseScope ps(p, 0, SPGEMM_PHASE_LIGHT_ACCUM, st);
-        for (int b = RB_WIN64; b <= RB_H8192; ++b)
+        for (int b = RB_T8; b <= RB_H8192; ++b)
             accumulate_rows(ri, b, p->row_bins[b], p->row_bins[b + 1] - p->row_bins[b], false, st);
     }
 
@@ -863,7 +863,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     p->stats.nlevels = p->L;
     p->stats.nbatches = (int32_t)p->batches.size();
     p->stats.lds_bytes = q.slm;
-    p->stats.light_rows = p->row_bins[RB_EMPTY] - p->row_bins[RB_WIN64];
+    p->stats.light_rows = p->row_bins[RB_EMPTY] - p->row_bins[RB_T8];
     p->stats.light_products = p->stats.sum_products - p->stats.heavy_products;
     p->stats.gamma = nnz_c > 0 ? (double)p->stats.sum_products / (double)nnz_c : 0.0;
     return nnz_c;
@@ -900,7 +900,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
     ri.Cval = C_val;
     // light rows on the plan's second stream when there are heavy rows to
     // overlap with; the caller's stream waits for them on every way out
-    const bool fork = p->H > 0 && p->row_bins[RB_H8192 + 1] > p->row_bins[RB_WIN64];
+    const bool fork = p->H > 0 && p->row_bins[RB_H8192 + 1] > p->row_bins[RB_T8];
     struct Join {
         bool on;
         hipStream_t st;
@@ -916,7 +916,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
     }
     {
         PhaseScope ps(p, 1, SPGEMM_PHASE_LIGHT_ACCUM, lst);
-        for (int b = RB_WIN64; b <= RB_H8192; ++b)
+        for (int b = RB_T8; b <= RB_H8192; ++b)
             accumulate_rows(ri, b, p->row_bins[b], p->row_bins[b + 1] - p->row_bins[b], true, lst);
     }
     if (fork) {

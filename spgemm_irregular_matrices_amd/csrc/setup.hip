@@ -134,6 +134,8 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
             b = RB_HEAVY;
             heavy = 1;
             hprod = u;
+        } else if (u <= kThreadMaxItems[2]) {
+            b = u <= kThreadMaxItems[0] ? RB_T8 : (u <= kThreadMaxItems[1] ? RB_T16 : RB_T32);
         } else {
             int32_t lo = 0x7fffffff, hi = -1;
             for (int64_t q = a0; q < a1; ++q) {
