@@ -100,6 +100,51 @@ def test_power_law_rows_split_over_work_groups(mode):
     compare(A, B, rp, col, val)
 
 
+def _thread_bin_rows():
+    """Rows at and around the thread-local bin bounds (u = 8, 16, 32), with
+    entries on empty B rows, repeated columns across entries, and a row whose
+    products all fall in one column; small integer values, so sums are exact."""
+    m, p = 64, 40
+    rng = np.random.default_rng(71)
+    brows = [[] for _ in range(m)]
+    for k in range(1, m):
+        ln = [1, 3, 5, 8, 16][k % 5]
+        brows[k] = sorted(rng.choice(p, size=ln, replace=False).tolist())
+    brows[7] = []            # another empty B row
+    brows[9] = [5]           # single column 5
+    brows[11] = [5]
+    arows = []
+    for target in (1, 7, 8, 9, 15, 16, 17, 31, 32, 33):
+        row, u = [0], 0      # entry on the empty B row 0 first
+        for k in rng.permutation(np.arange(1, m)):
+            ln = len(brows[k])
+            if ln and u + ln <= target:
+                row.append(int(k))
+                u += ln
+            if u == target:
+                break
+        row.insert(len(row) // 2, 7)
+        arows.append(row)
+    arows.append([9, 7])                       # one product
+    arows.append([9, 0, 11, 7])                # two products in one column, empty rows between
+    A0 = synth.from_rows(len(arows), m, arows)
+    B0 = synth.from_rows(m, p, brows)
+    A = synth.CSR(A0.nrows, m, A0.rowptr, A0.col, synth.small_int_values(72, A0.nnz))
+    B = synth.CSR(m, p, B0.rowptr, B0.col, synth.small_int_values(73, B0.nnz))
+    return A, B
+
+
+def test_thread_local_bins_exact():
+    A, B = _thread_bin_rows()
+    u = oracle.row_products(A, B)
+    assert {8, 9, 16, 17, 32, 33} <= set(u.tolist())
+    rp, col, val, st = run_gpu(A, B)
+    assert st["heavy_rows"] == 0
+    compare(A, B, rp, col, val, exact_values=True)
+    # all products in one column: a single output
+    assert rp[-1] - rp[-2] == 1
+
+
 def test_fig1_stages_and_product():
     with open(os.path.join(GOLDEN, "fig1_heavy_rows.json")) as f:
         g = json.load(f)
