@@ -3,11 +3,13 @@
 // The chunk of a product a_ik * b_kj is fixed by j alone, so the
 // column-range split that the gMAGNUS page applies to C-hat (Section III-C,
 // hierarchical multisplit) can be applied to B instead: every B row is
-// partitioned once, stably, into the final chunks (slots of width W), and
-// bsplit[k][s] records where slot s starts inside row k. The products of
-// heavy row i that fall into chunk s are then the slices [bsplit[k][s],
-// bsplit[k][s+1]) of the B rows k of row i's entries, each scaled by its
-// a_ik. One work group per (heavy row, chunk) item forms exactly those
+// partitioned once into the final chunks (slots of width W), and the split
+// copy of B is laid out slot by slot: all rows' entries of slot 0, then of
+// slot 1, and so on, each slot's entries in row order. spos[s*B.n + k]
+// records where row k's entries of slot s start, so the products of heavy
+// row i that fall into chunk s are the slices [spos[s*B.n + k],
+// spos[s*B.n + k + 1]) for the B rows k of row i's entries, each scaled by
+// its a_ik, and one slot's part of B is contiguous. One work group per (heavy row, chunk) item forms exactly those
 // products and accumulates them in LDS with the page's accumulators
 // (Section III-E): the bitmap-rank accumulator for items of at most
 // kDirectDense products, the dense window above that. C-hat and
@@ -20,57 +22,67 @@
 namespace sg {
 
 // ---------------------------------------------------------------- B split
-// bsplit[k*(req+1) + s] = entries of B row k in slots before s (so
-// bsplit[k*(req+1) + req] is the row length).
-__global__ void k_bsplit_prefix(const int32_t* bslot, int64_t nb, int req, int32_t* bsplit) {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= nb) return;
-    const int32_t* src = bslot + k * req;
-    int32_t* dst = bsplit + k * (req + 1);
-    int32_t run = 0;
-    for (int s = 0; s < req; ++s) {
-        dst[s] = run;
-        run += src[s];
+// bslot (row-major, B.n x req) to slot-major (req x B.n), in 32 x 32 tiles.
+__global__ __launch_bounds__(256) void k_bslot_transpose(const int32_t* bslot, int64_t nb, int req,
+                                                         int32_t* bslotT) {
+    __shared__ int32_t tile[32][33];
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+    const int64_t k0 = (int64_t)blockIdx.x * 32;
+    const int s0 = blockIdx.y * 32;
+    for (int r = ty; r < 32; r += 8) {
+        const int64_t k = k0 + r;
+        const int sl = s0 + tx;
+        tile[r][tx] = (k < nb && sl < req) ? bslot[k * req + sl] : 0;
     }
-    dst[req] = run;
+    __syncthreads();
+    for (int r = ty; r < 32; r += 8) {
+        const int sl = s0 + r;
+        const int64_t k = k0 + tx;
+        if (sl < req && k < nb) bslotT[(int64_t)sl * nb + k] = tile[tx][r];
+    }
 }
 
-// One wavefront per B row: entries are placed slot by slot, in row order
-// within a slot. The wave ranks each batch of 64 entries by peeling one
+struct LoadI32 {
+    const int32_t* a;
+    __device__ int64_t operator()(int64_t i) const { return a[i]; }
+};
+
+// One wavefront per B row: each entry goes to its slot's part of the split
+// copy, at the row's start there plus its rank among the row's entries of
+// that slot. The wave ranks each batch of 64 entries by peeling one
 // distinct slot at a time (ballot of the lanes holding the first remaining
-// lane's slot); running slot offsets live in the wave's LDS.
+// lane's slot); the row's running counts per slot live in the wave's LDS.
 constexpr int kBpartNT = 256;
 
 __global__ __launch_bounds__(kBpartNT) void k_bpartition(const int64_t* brp, const int32_t* bcol,
                                                          int64_t nb, int logW, int req,
-                                                         const int32_t* bsplit, int64_t* bperm,
+                                                         const int64_t* spos, int64_t* bperm,
                                                          uint16_t* bcol16) {
     extern __shared__ int lds_b[];
     const int w = threadIdx.x / kWave, lane = lane_id();
     int* run = lds_b + w * req;
     const int64_t k = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
     if (k >= nb) return;  // whole waves leave together; no block barrier below
-    const int32_t* bs = bsplit + k * (req + 1);
-    for (int s = lane; s < req; s += kWave) run[s] = bs[s];
+    for (int sl = lane; sl < req; sl += kWave) run[sl] = 0;
     const int64_t e0 = brp[k], e1 = brp[k + 1];
     const uint32_t wmask = (1u << logW) - 1u;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
     for (int64_t eb = e0; eb < e1; eb += kWave) {
         const int64_t e = eb + lane;
         int32_t c = 0;
-        int s = -1;
+        int sl = -1;
         if (e < e1) {
             c = bcol[e];
-            s = (int)((uint32_t)c >> logW);
+            sl = (int)((uint32_t)c >> logW);
         }
-        uint64_t act = __ballot(s >= 0);
+        uint64_t act = __ballot(sl >= 0);
         while (act) {
             const int leader = __builtin_ctzll(act);
-            const int ls = __builtin_amdgcn_readlane(s, leader);
-            const uint64_t m = __ballot(s == ls);
+            const int ls = __builtin_amdgcn_readlane(sl, leader);
+            const uint64_t m = __ballot(sl == ls);
             const int base = run[ls];
-            if (s == ls) {
-                const int64_t pos = e0 + base + __popcll(m & lt);
+            if (sl == ls) {
+                const int64_t pos = spos[(int64_t)ls * nb + k] + base + __popcll(m & lt);
                 bperm[pos] = e;
                 bcol16[pos] = (uint16_t)((uint32_t)c & wmask);
             }
@@ -80,21 +92,25 @@ __global__ __launch_bounds__(kBpartNT) void k_bpartition(const int64_t* brp, con
     }
 }
 
-void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int32_t* bsplit,
-                    bool bsplit_done, int64_t* bperm, uint16_t* bcol16, hipStream_t st) {
-    if (B.n <= 0) return;
+void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int64_t* spos,
+                    int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st) {
     if (W > 65536 || req > kDirectMaxSlots) throw std::logic_error("direct split limits");
-    if (!bsplit_done) {
-        hipLaunchKernelGGL(k_bsplit_prefix, dim3(grid_1d(ceil_div(B.n, 256))), dim3(256), 0, st,
-                           bslot, B.n, req, bsplit);
-        SG_LAUNCH_CHECK();
+    const int64_t n = (int64_t)req * B.n;
+    if (B.n <= 0) {
+        fill<int64_t>(spos, 1, 0, st);
+        return;
     }
+    int32_t* bslotT = ar.get<int32_t>("bslotT", (size_t)n);
+    hipLaunchKernelGGL(k_bslot_transpose, dim3(grid_1d(ceil_div(B.n, 32)), ceil_div(req, 32)),
+                       dim3(256), 0, st, bslot, B.n, req, bslotT);
+    SG_LAUNCH_CHECK();
+    scan_exclusive(LoadI32{bslotT}, n, spos, ar, st);
     if (B.nnz <= 0) return;
     const size_t lds = (size_t)(kBpartNT / kWave) * req * 4;
     SG_HIP(hipFuncSetAttribute((const void*)k_bpartition,
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     hipLaunchKernelGGL(k_bpartition, dim3(grid_1d(ceil_div(B.n * kWave, kBpartNT))),
-                       dim3(kBpartNT), lds, st, B.rp, B.col, B.n, ilog2(W), req, bsplit, bperm,
+                       dim3(kBpartNT), lds, st, B.rp, B.col, B.n, ilog2(W), req, spos, bperm,
                        bcol16);
     SG_LAUNCH_CHECK();
 }
@@ -187,12 +203,11 @@ __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int6
     int len = 0;
     if (tt < NE && q < q1) {
         const int32_t k = d.Acol[q];
-        const int64_t eb = d.ebo[q];
         const double a = d.Aval[q];
-        const int32_t* bs = d.bsplit + (int64_t)k * (d.req + 1) + s;
-        const int32_t lo = bs[0];
-        len = bs[1] - lo;
-        s_bo[tt] = eb + lo;
+        const int64_t* sp = d.spos + (int64_t)s * d.nb + k;
+        const int64_t lo = sp[0];
+        len = (int)(sp[1] - lo);
+        s_bo[tt] = lo;
         s_a[tt] = a;
     }
     int tot;

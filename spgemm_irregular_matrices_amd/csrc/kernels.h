@@ -249,18 +249,19 @@ struct DirectArgs {
     const int32_t* ine;     // per position of items: its row's A entries
     const int32_t* Acol;
     const double* Aval;
-    const int64_t* ebo;     // per A entry: start of its B row
-    const int32_t* bsplit;  // B.nrows x (req+1): slot starts inside each B row
+    const int64_t* spos;    // req x B.nrows (+1): where row k's part of slot s starts in split B
+    int64_t nb;             // B.nrows
     const uint16_t* bcol16; // partitioned B: column offset inside the slot
     const double* bval;     // partitioned B: values
     const int64_t* off;     // per item: output offset in C
     int32_t* Ccol;
     double* Cval;
 };
-// bsplit from the per-row slot counts bslot; bperm[p] = B entry placed at p
-// (rows keep their extents), bcol16[p] its column inside its slot.
-void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int32_t* bsplit,
-                    bool bsplit_done, int64_t* bperm, uint16_t* bcol16, hipStream_t st);
+// The split copy of B, slot by slot: spos (req*B.n + 1 int64) from the
+// per-row slot counts bslot; bperm[p] = B entry placed at p, bcol16[p] its
+// column inside its slot.
+void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int64_t* spos,
+                    int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st);
 void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int req,
                     const int64_t* dist_fin, int64_t* off, hipStream_t st);
 // Stable partition of the items x in [0, nitems) by class (CB_* bins, from

@@ -748,18 +748,14 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             throw OverflowError("fused symbolic pass needs more LDS than the device has");
         int64_t* elem_fin = nullptr;
         int64_t* dist_fin = nullptr;
-        bool bsplit_done = false;
         if (p->fused_sym) {
             const int64_t wfin = q.nlevels == 0 ? q.ppow : q.final_width;
             elem_fin = ar.get<int64_t>("elem_fin", (size_t)(p->H * req));
             dist_fin = ar.get<int64_t>("dist_fin", (size_t)(p->H * req));
             PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
             int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
-            bsplit_done = heavy_symbolic(
-                A, B, S, hrows, p->H, p->Nh, p->stats.max_products, p->dev_cus, p->dev_lds,
-                q.ppow, wfin, bslot,
-                p->direct ? ar.get<int32_t>("bsplit", (size_t)(B.n * (req + 1) + 1)) : nullptr,
-                elem_fin, dist_fin, ar, st);
+            heavy_symbolic(A, B, S, hrows, p->H, p->Nh, p->stats.max_products, p->dev_cus,
+                           p->dev_lds, q.ppow, wfin, bslot, nullptr, elem_fin, dist_fin, ar, st);
             add_bytes(p, 0, SPGEMM_PHASE_HISTO, 4.0 * p->Nh + 16.0 * p->H * req);
         }
         if (p->direct) {
@@ -768,9 +764,9 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
             int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
             direct_split_b(B, bslot, (int)req, wfin_d,
-                           ar.get<int32_t>("bsplit", (size_t)(B.n * (req + 1) + 1)), bsplit_done,
+                           ar.get<int64_t>("spos", (size_t)(B.n * req + 1)),
                            ar.get<int64_t>("bperm", (size_t)B.nnz + 1),
-                           ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1), st);
+                           ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1), ar, st);
             int64_t* bins = ar.get<int64_t>("dbins", CB_COUNT + 1);
             direct_classify(elem_fin, p->H * req, (int)req, ar.get<int64_t>("h_q0", (size_t)p->H),
                             ar.get<int64_t>("h_q1", (size_t)p->H),
@@ -938,8 +934,8 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         d.ine = ar.get<int32_t>("dine", (size_t)(p->H * req));
         d.Acol = A.col;
         d.Aval = A.val;
-        d.ebo = ar.get<int64_t>("ebo", (size_t)A.nnz + 1);
-        d.bsplit = ar.get<int32_t>("bsplit", (size_t)(B.n * (req + 1) + 1));
+        d.spos = ar.get<int64_t>("spos", (size_t)(B.n * req + 1));
+        d.nb = B.n;
         d.bcol16 = ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1);
         d.bval = bpval;
         d.off = ar.get<int64_t>("doff", (size_t)(p->H * req));
