@@ -47,7 +47,8 @@ typedef enum {
     SPGEMM_ERR_OUT_OF_MEMORY = -5, /* device workspace could not be allocated       */
     SPGEMM_ERR_PLAN_MISMATCH = -6, /* numeric called with other shapes than symbolic */
     SPGEMM_ERR_HIP = -7,           /* a HIP runtime call failed                     */
-    SPGEMM_ERR_NOT_READY = -8      /* numeric called before a successful symbolic   */
+    SPGEMM_ERR_NOT_READY = -8,     /* numeric called before a successful symbolic   */
+    SPGEMM_ERR_CAPACITY = -9       /* spgemm_multiply: C has more entries than room */
 } spgemm_status;
 
 /* A CSR matrix (gMAGNUS page, Section II-A). `rowptr` has nrows+1 entries
@@ -202,6 +203,19 @@ SPGEMM_API int spgemm_symbolic(spgemm_plan plan, const spgemm_csr* A, const spge
 SPGEMM_API int spgemm_numeric(spgemm_plan plan, const spgemm_csr* A, const spgemm_csr* B,
                               const int64_t* C_rowptr, int32_t* C_col, double* C_val,
                               void* stream);
+
+/* Both phases in one call (gMAGNUS page, Algorithm 3 run through in one
+ * go): the symbolic phase fills C_rowptr and *C_nnz; if *C_nnz <= capacity
+ * (entries of room in the caller's C_col and C_val, device buffers) the
+ * numeric phase fills them as spgemm_numeric would and the call returns OK.
+ * Otherwise it returns CAPACITY with C_rowptr and *C_nnz valid and the plan
+ * ready, so the caller can allocate *C_nnz entries and call spgemm_numeric
+ * for the same A and B. Blocks until *C_nnz is known; the numeric part is
+ * asynchronous on `stream`. Errors: those of spgemm_symbolic and
+ * spgemm_numeric, INVALID_ARG (capacity < 0), CAPACITY. */
+SPGEMM_API int spgemm_multiply(spgemm_plan plan, const spgemm_csr* A, const spgemm_csr* B,
+                               int64_t* C_rowptr, int32_t* C_col, double* C_val,
+                               int64_t capacity, int64_t* C_nnz, void* stream);
 
 /* Copy the statistics of the last symbolic + numeric pair into *out
  * (synchronises on pending timing events). Errors: INVALID_ARG. */

@@ -21,13 +21,15 @@ STATUS = {
     0: "SPGEMM_OK", -1: "SPGEMM_ERR_INVALID_ARG", -2: "SPGEMM_ERR_DIM_MISMATCH",
     -3: "SPGEMM_ERR_INDEX_RANGE", -4: "SPGEMM_ERR_OVERFLOW", -5: "SPGEMM_ERR_OUT_OF_MEMORY",
     -6: "SPGEMM_ERR_PLAN_MISMATCH", -7: "SPGEMM_ERR_HIP", -8: "SPGEMM_ERR_NOT_READY",
+    -9: "SPGEMM_ERR_CAPACITY",
 }
+CAPACITY = -9
 PHASES = ["validate", "inter_prod_size", "binning", "csr_to_csc", "outer_prod", "histo",
           "multisplit", "heavy_accum", "light_accum", "prefix_sum", "direct_dense", "direct_rank"]
 MAX_LEVELS = 8
 EXPORTS = ["spgemm_options_default", "spgemm_plan_create", "spgemm_plan_destroy",
-           "spgemm_symbolic", "spgemm_numeric", "spgemm_plan_stats", "spgemm_plan_debug",
-           "spgemm_status_string"]
+           "spgemm_symbolic", "spgemm_numeric", "spgemm_multiply", "spgemm_plan_stats",
+           "spgemm_plan_debug", "spgemm_status_string"]
 
 
 class SpgemmError(RuntimeError):
@@ -103,6 +105,11 @@ def load():
         lib.spgemm_numeric.argtypes = [P, ctypes.POINTER(CSRStruct), ctypes.POINTER(CSRStruct),
                                        P, P, P, P]
         lib.spgemm_numeric.restype = ctypes.c_int
+        lib.spgemm_multiply.argtypes = [P, ctypes.POINTER(CSRStruct), ctypes.POINTER(CSRStruct),
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
+                                        ctypes.c_void_p]
+        lib.spgemm_multiply.restype = ctypes.c_int
         lib.spgemm_plan_stats.argtypes = [P, ctypes.POINTER(Stats)]
         lib.spgemm_plan_stats.restype = ctypes.c_int
         lib.spgemm_plan_debug.argtypes = [P, ctypes.c_int, ctypes.POINTER(DebugMatrix)]
@@ -231,6 +238,27 @@ class Plan:
         val = torch.empty(nnz, dtype=torch.float64, device=dev)
         self.numeric(A, B, rp, col, val, stream=stream)
         return DeviceCSR(A.nrows, B.ncols, rp, col, val)
+
+    def multiply_once(self, A: DeviceCSR, B: DeviceCSR, capacity: int, stream=None):
+        """Both phases in one library call with `capacity` entries of room for
+        C. Returns (DeviceCSR, True) if C fit, else (DeviceCSR with a valid
+        rowptr and empty col/val of the right size, False): then call numeric()."""
+        import torch
+        dev = A.rowptr.device
+        rp = torch.empty(A.nrows + 1, dtype=torch.int64, device=dev)
+        col = torch.empty(max(capacity, 0), dtype=torch.int32, device=dev)
+        val = torch.empty(max(capacity, 0), dtype=torch.float64, device=dev)
+        nnz = ctypes.c_int64(0)
+        sa, sb = A.struct(), B.struct()
+        rc = self._lib.spgemm_multiply(self._h, ctypes.byref(sa), ctypes.byref(sb),
+                                       rp.data_ptr(), _ptr(col), _ptr(val), capacity,
+                                       ctypes.byref(nnz), _stream_handle(stream))
+        n = int(nnz.value)
+        if rc == CAPACITY:
+            return DeviceCSR(A.nrows, B.ncols, rp, torch.empty(n, dtype=torch.int32, device=dev),
+                             torch.empty(n, dtype=torch.float64, device=dev)), False
+        _check(rc, "spgemm_multiply")
+        return DeviceCSR(A.nrows, B.ncols, rp, col[:n], val[:n]), True
 
     def stats(self) -> dict:
         s = Stats()

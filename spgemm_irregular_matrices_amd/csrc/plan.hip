@@ -1202,6 +1202,16 @@ SPGEMM_API int spgemm_numeric(spgemm_plan p, const spgemm_csr* A, const spgemm_c
     });
 }
 
+SPGEMM_API int spgemm_multiply(spgemm_plan p, const spgemm_csr* A, const spgemm_csr* B,
+                               int64_t* C_rowptr, int32_t* C_col, double* C_val,
+                               int64_t capacity, int64_t* C_nnz, void* stream) {
+    if (!p || !C_nnz || capacity < 0) return SPGEMM_ERR_INVALID_ARG;
+    int rc = spgemm_symbolic(p, A, B, C_rowptr, C_nnz, stream);
+    if (rc != SPGEMM_OK) return rc;
+    if (*C_nnz > capacity) return SPGEMM_ERR_CAPACITY;
+    return spgemm_numeric(p, A, B, C_rowptr, C_col, C_val, stream);
+}
+
 SPGEMM_API int spgemm_plan_stats(spgemm_plan p, spgemm_stats* out) {
     if (!p || !out) return SPGEMM_ERR_INVALID_ARG;
     return guarded([&]() -> int {
@@ -1271,6 +1281,7 @@ SPGEMM_API const char* spgemm_status_string(int status) {
         case SPGEMM_ERR_PLAN_MISMATCH: return "numeric call does not match the symbolic call";
         case SPGEMM_ERR_HIP: return "HIP runtime error";
         case SPGEMM_ERR_NOT_READY: return "numeric called before a successful symbolic";
+        case SPGEMM_ERR_CAPACITY: return "C has more entries than the room given";
         default: return "unknown status";
     }
 }

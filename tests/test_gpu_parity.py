@@ -145,6 +145,31 @@ def test_thread_local_bins_exact():
     assert rp[-1] - rp[-2] == 1
 
 
+def test_multiply_in_one_call():
+    """spgemm_multiply: with room for C, both phases in one call equal the
+    two-call product; with too little room it returns CAPACITY with a valid
+    row pointer and nnz, and a numeric call into right-sized buffers finishes."""
+    import torch
+    from spgemm_irregular_matrices_amd import binding
+    A = synth.workload("rmat10_ef8")[0]
+    dA = binding.DeviceCSR.from_host(A)
+    with binding.Plan(tau_override=200) as p:
+        ref = p.multiply(dA, dA)
+        C, fit = p.multiply_once(dA, dA, capacity=int(ref.col.numel()) + 5)
+        torch.cuda.synchronize()
+        assert fit
+        assert torch.equal(C.rowptr, ref.rowptr) and torch.equal(C.col, ref.col)
+        compare(A, A, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy())
+        C2, fit2 = p.multiply_once(dA, dA, capacity=10)
+        assert not fit2 and C2.col.numel() == ref.col.numel()
+        assert torch.equal(C2.rowptr, ref.rowptr)
+        p.numeric(dA, dA, C2.rowptr, C2.col, C2.val)
+        torch.cuda.synchronize()
+        compare(A, A, C2.rowptr.cpu().numpy(), C2.col.cpu().numpy(), C2.val.cpu().numpy())
+        with pytest.raises(binding.SpgemmError):
+            p.multiply_once(dA, dA, capacity=-1)
+
+
 def test_fig1_stages_and_product():
     with open(os.path.join(GOLDEN, "fig1_heavy_rows.json")) as f:
         g = json.load(f)
