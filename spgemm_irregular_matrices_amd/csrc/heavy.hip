@@ -862,7 +862,7 @@ __global__ __launch_bounds__(kBslotNT) void k_bslot_rows(const int64_t* brp, con
 // products and the waves take pieces in turn, one product per lane, so the
 // reads of B are coalesced and no product needs a search.
 constexpr int kHsymNT = 1024;
-constexpr int kHsymEW = 1024;  // entries per staged window
+constexpr int kHsymEW = 1024;  // entries per staged window (half with column parts)
 // one thread stages each entry of a window
 static_assert(kHsymEW <= kHsymNT, "a staged window holds at most one entry per thread");
 
@@ -921,19 +921,25 @@ struct HsymSplitArgs {
     uint32_t* gbits;       // split rows' bitmaps (split index * nwords)
 };
 
+// The row's column range may be taken in np parts, one launch each (when the
+// whole bitmap would leave one work group per CU): part p keeps bitmap words
+// [wlo, wlo + nwp) and slots [sl0, sl0 + reqp), reads every product of the
+// row and skips those outside its columns.
+template <int EW>
 __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     const int64_t* arp, const int32_t* acol, const int64_t* brp, const int32_t* bcol,
-    const int32_t* hrows, int req, int nwords, const int32_t* bslot, int64_t* elem_fin,
-    int64_t* dist_fin, HsymSplitArgs sp, int64_t H) {
+    const int32_t* hrows, int req, int nwords, int wlo, int nwp, int sl0, int reqp,
+    const int32_t* bslot, int64_t* elem_fin, int64_t* dist_fin, HsymSplitArgs sp, int64_t H) {
+    static_assert(EW <= kHsymNT, "a staged window holds at most one entry per thread");
     extern __shared__ int64_t lds_s[];
     constexpr int NW = kHsymNT / kWave;
-    int64_t* bst = lds_s;                                   // kHsymEW B row starts
-    unsigned long long* esl = (unsigned long long*)(bst + kHsymEW);  // req element counts
-    int* nbv = (int*)(esl + req);                           // kHsymEW B row lengths
-    int* kst = nbv + kHsymEW;                               // kHsymEW B rows
-    int* ppre = kst + kHsymEW;                              // kHsymEW + 1 piece prefix
-    int* dsl = ppre + kHsymEW + 1;                          // req distinct counts
-    uint32_t* bits = (uint32_t*)(dsl + req);                // nwords
+    int64_t* bst = lds_s;                                   // EW B row starts
+    unsigned long long* esl = (unsigned long long*)(bst + EW);  // reqp element counts
+    int* nbv = (int*)(esl + reqp);                          // EW B row lengths
+    int* kst = nbv + EW;                                    // EW B rows
+    int* ppre = kst + EW;                                   // EW + 1 piece prefix
+    int* dsl = ppre + EW + 1;                               // reqp distinct counts
+    uint32_t* bits = (uint32_t*)(dsl + reqp);               // nwp
     __shared__ int scan_sh[NW + 1];
     __shared__ int64_t range_sh[2];
     const int tt = threadIdx.x;
@@ -947,8 +953,8 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
         ns = hsym_blocks(sp.off[h + 1]) - hsym_blocks(o);
         sidx = hsym_split(o);
     }
-    for (int i = tt; i < nwords; i += kHsymNT) bits[i] = 0u;
-    for (int i = tt; i < req; i += kHsymNT) {
+    for (int i = tt; i < nwp; i += kHsymNT) bits[i] = 0u;
+    for (int i = tt; i < reqp; i += kHsymNT) {
         dsl[i] = 0;
         esl[i] = 0ull;
     }
@@ -969,8 +975,8 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
         a0 = range_sh[0];
         a1 = range_sh[1];
     }
-    for (int64_t ew = a0; ew < a1; ew += kHsymEW) {
-        const int ne = (int)min((int64_t)kHsymEW, a1 - ew);
+    for (int64_t ew = a0; ew < a1; ew += EW) {
+        const int ne = (int)min((int64_t)EW, a1 - ew);
         int pc = 0;
         if (tt < ne) {
             int32_t k = acol[ew + tt];
@@ -1015,20 +1021,24 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
             }
             j0 = jl;
 #pragma unroll
-            for (int uu = 0; uu < U; ++uu)
-                if (c[uu] != 0xffffffffu) atomicOr(&bits[c[uu] >> 5], 1u << (c[uu] & 31));
+            for (int uu = 0; uu < U; ++uu) {
+                const uint32_t wd = (c[uu] >> 5) - (uint32_t)wlo;
+                if (c[uu] != 0xffffffffu && wd < (uint32_t)nwp)
+                    atomicOr(&bits[wd], 1u << (c[uu] & 31));
+            }
         }
         // element counts per slot: the sum of the window's B-row slot vectors
-        if (req <= kHsymNT) {
-            const int sl = tt % req, step = kHsymNT / req;
+        if (reqp <= kHsymNT) {
+            const int sl = tt % reqp, step = kHsymNT / reqp;
             int64_t sum = 0;
-            if (tt < step * req)
-                for (int e = tt / req; e < ne; e += step) sum += bslot[(int64_t)kst[e] * req + sl];
+            if (tt < step * reqp)
+                for (int e = tt / reqp; e < ne; e += step)
+                    sum += bslot[(int64_t)kst[e] * req + sl0 + sl];
             if (sum) atomicAdd(&esl[sl], (unsigned long long)sum);
         } else {
-            for (int sl = tt; sl < req; sl += kHsymNT) {
+            for (int sl = tt; sl < reqp; sl += kHsymNT) {
                 int64_t sum = 0;
-                for (int e = 0; e < ne; ++e) sum += bslot[(int64_t)kst[e] * req + sl];
+                for (int e = 0; e < ne; ++e) sum += bslot[(int64_t)kst[e] * req + sl0 + sl];
                 esl[sl] += (unsigned long long)sum;
             }
         }
@@ -1036,17 +1046,17 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     }
     if (ns > 1) {
         // a part of a split row: add into the row's global counts and bitmap
-        uint32_t* g = sp.gbits + sidx * (int64_t)nwords;
-        for (int i = tt; i < nwords; i += kHsymNT)
+        uint32_t* g = sp.gbits + sidx * (int64_t)nwords + wlo;
+        for (int i = tt; i < nwp; i += kHsymNT)
             if (bits[i]) atomicOr(&g[i], bits[i]);
-        for (int sl = tt; sl < req; sl += kHsymNT)
+        for (int sl = tt; sl < reqp; sl += kHsymNT)
             if (esl[sl])
-                atomicAdd((unsigned long long*)&elem_fin[h * req + sl], esl[sl]);
+                atomicAdd((unsigned long long*)&elem_fin[h * req + sl0 + sl], esl[sl]);
         return;
     }
     // distinct columns per finest slot: popcounts of the slot's words
-    const int wps = nwords / req;  // words per slot (>= 1)
-    for (int i = tt; i < nwords; i += kHsymNT) {
+    const int wps = nwp / reqp;  // words per slot (>= 1)
+    for (int i = tt; i < nwp; i += kHsymNT) {
         int pc = __popc(bits[i]);
         const int sl = i / wps;
         // a wave's 64 words lie in one slot when slots hold >= 64 words
@@ -1058,9 +1068,9 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
         }
     }
     __syncthreads();
-    for (int sl = tt; sl < req; sl += kHsymNT) {
-        dist_fin[h * req + sl] = dsl[sl];
-        elem_fin[h * req + sl] = (int64_t)esl[sl];
+    for (int sl = tt; sl < reqp; sl += kHsymNT) {
+        dist_fin[h * req + sl0 + sl] = dsl[sl];
+        elem_fin[h * req + sl0 + sl] = (int64_t)esl[sl];
     }
 }
 
@@ -1091,10 +1101,12 @@ __global__ __launch_bounds__(kHsymNT) void k_hsym_finalize(const int64_t* off, i
     for (int sl = tt; sl < req; sl += kHsymNT) dist_fin[h * req + sl] = dsl_f[sl];
 }
 
-size_t heavy_symbolic_lds(int64_t ppow, int64_t req) {
-    return (size_t)kHsymEW * 8 + (size_t)req * 8 + (size_t)kHsymEW * 4 * 2 +
-           (size_t)(kHsymEW + 1) * 4 + (size_t)req * 4 + (size_t)(ppow / 32) * 4;
+static size_t hsym_lds(int ew, int64_t nwp, int64_t reqp) {
+    return (size_t)ew * 8 + (size_t)reqp * 8 + (size_t)ew * 4 * 2 + (size_t)(ew + 1) * 4 +
+           (size_t)reqp * 4 + (size_t)nwp * 4;
 }
+
+size_t heavy_symbolic_lds(int64_t ppow, int64_t req) { return hsym_lds(kHsymEW, ppow / 32, req); }
 
 bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
                     int64_t H, int64_t Nh, int64_t max_u, int ncu, int64_t dev_lds, int64_t ppow,
@@ -1123,8 +1135,22 @@ bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const in
             SG_LAUNCH_CHECK();
         }
     }
-    const size_t lds = heavy_symbolic_lds(ppow, req);
     const int nwords = (int)(ppow / 32);
+    // the whole bitmap in one launch if two work groups fit a CU; else the
+    // fewest column parts (with half the staging window) that do
+    int np = 1, ew = kHsymEW;
+    size_t lds = hsym_lds(kHsymEW, nwords, req);
+    if (lds > (size_t)dev_lds / 2) {
+        for (int cand = 2; cand <= req && cand <= 64; cand *= 2) {
+            const size_t l = hsym_lds(kHsymEW / 2, nwords / cand, req / cand);
+            if (l <= (size_t)dev_lds / 2) {
+                np = cand;
+                ew = kHsymEW / 2;
+                lds = l;
+                break;
+            }
+        }
+    }
     // a work group's share: a quarter of the pass over the work groups the
     // device holds at once, and at least kHsymSplitMin products
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(2, dev_lds / (int64_t)lds));
@@ -1147,11 +1173,24 @@ bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const in
         SG_LAUNCH_CHECK();
         sp = HsymSplitArgs{S, off, bmap, gbits};
     }
-    SG_HIP(hipFuncSetAttribute((const void*)k_heavy_symbolic,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-    hipLaunchKernelGGL(k_heavy_symbolic, dim3(grid_1d(grid)), dim3(kHsymNT), lds, st, A.rp, A.col,
-                       B.rp, B.col, hrows, (int)req, nwords, bslot, elem_fin, dist_fin, sp, H);
-    SG_LAUNCH_CHECK();
+    const int nwp = nwords / np, reqp = (int)req / np;
+    for (int part = 0; part < np; ++part) {
+        if (ew == kHsymEW) {
+            SG_HIP(hipFuncSetAttribute((const void*)k_heavy_symbolic<kHsymEW>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+            hipLaunchKernelGGL(k_heavy_symbolic<kHsymEW>, dim3(grid_1d(grid)), dim3(kHsymNT), lds,
+                               st, A.rp, A.col, B.rp, B.col, hrows, (int)req, nwords, part * nwp,
+                               nwp, part * reqp, reqp, bslot, elem_fin, dist_fin, sp, H);
+        } else {
+            SG_HIP(hipFuncSetAttribute((const void*)k_heavy_symbolic<kHsymEW / 2>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+            hipLaunchKernelGGL(k_heavy_symbolic<kHsymEW / 2>, dim3(grid_1d(grid)), dim3(kHsymNT),
+                               lds, st, A.rp, A.col, B.rp, B.col, hrows, (int)req, nwords,
+                               part * nwp, nwp, part * reqp, reqp, bslot, elem_fin, dist_fin, sp,
+                               H);
+        }
+        SG_LAUNCH_CHECK();
+    }
     if (sp.off && nsplit_max > 0) {
         hipLaunchKernelGGL(k_hsym_finalize, dim3(grid_1d(nsplit_max)), dim3(kHsymNT),
                            (size_t)req * 4, st, sp.off, H, (const int32_t*)ar.get<int32_t>("hsym_smap", (size_t)nsplit_max + 1),

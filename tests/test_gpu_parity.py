@@ -75,11 +75,13 @@ def test_rmat10_forced_heavy(tau, width, cap, levels, mode):
     compare(A, A, rp, col, val)
 
 
-def _power_law_rows():
+def _power_law_rows(p=1 << 17):
     """Rows far above the symbolic pass's per-work-group share: 128K, 48K and
     24K products, plus a 3-entry row whose first B row holds 60,000 entries
-    (split into three parts by product range, the middle one empty)."""
-    n, m, p = 3000, 1 << 15, 1 << 17
+    (split into three parts by product range, the middle one empty). With
+    p = 2^19 columns the row bitmap no longer lets two work groups share a
+    CU, so the symbolic pass also takes the columns in parts."""
+    n, m = 3000, 1 << 15
     lens = synth.zipf_lengths(n, 2.1, 20, seed=61)
     lens[:4] = [8000, 3000, 1500, 3]
     A = synth.distinct_uniform_rows(lens, m, seed=62, value_seed=63)
@@ -90,9 +92,10 @@ def _power_law_rows():
     return A, B
 
 
+@pytest.mark.parametrize("cols", [1 << 17, 1 << 19])
 @pytest.mark.parametrize("mode", MODES)
-def test_power_law_rows_split_over_work_groups(mode):
-    A, B = _power_law_rows()
+def test_power_law_rows_split_over_work_groups(mode, cols):
+    A, B = _power_law_rows(cols)
     u = oracle.row_products(A, B)
     assert u[0] == 128000 and u[3] == 60002
     rp, col, val, st = run_gpu(A, B, symbolic_mode=mode[0], numeric_mode=mode[1])
