@@ -521,7 +521,8 @@ void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
     fill<int64_t>(out6, 6, 0, st);
     const int64_t n = H * req;
     if (n <= 0) return;
-    const int64_t blocks = std::min<int64_t>(ceil_div(n, 256), 4096);
+    // few work groups: their sums meet at six global counters
+    const int64_t blocks = std::min<int64_t>(ceil_div(n, 256), 256);
     hipLaunchKernelGGL(k_direct_totals, dim3(grid_1d(blocks)), dim3(256), 0, st, hq0, hq1, n,
                        ilog2(req), elem_fin, dist_fin, (unsigned long long*)out6);
     SG_LAUNCH_CHECK();

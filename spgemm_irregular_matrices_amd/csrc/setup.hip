@@ -113,6 +113,10 @@ __device__ __forceinline__ int u_bucket(int64_t u) {
     return 64 + (e - 6) * 64 + (int)((u >> (e - 6)) & 63);
 }
 
+// Grid-stride over rows, so the per-block sums below meet few work groups
+// at the global counters (same-address atomics serialise at the L2).
+constexpr int kClassifyMaxBlocks = 512;
+
 __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const int32_t* acol,
                                                        int64_t n, const int64_t* S,
                                                        const int32_t* bmin, const int32_t* bmax,
@@ -122,64 +126,67 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
     __shared__ double shd[8];
     __shared__ int hsmall[64];  // the exact buckets u < 64, gathered per block
     if (threadIdx.x < 64) hsmall[threadIdx.x] = 0;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    int64_t u = 0, heavy = 0, hprod = 0;
-    if (i < n) {
-        int64_t a0 = arp[i], a1 = arp[i + 1];
-        u = S[a1] - S[a0];
-        int b;
-        if (u == 0) {
-            b = RB_EMPTY;
-        } else if (u > tau) {
-            b = RB_HEAVY;
-            heavy = 1;
-            hprod = u;
-        } else if (u <= kThreadMaxItems[2]) {
-            b = u <= kThreadMaxItems[0] ? RB_T8 : (u <= kThreadMaxItems[1] ? RB_T16 : RB_T32);
-        } else {
-            int32_t lo = 0x7fffffff, hi = -1;
-            for (int64_t q = a0; q < a1; ++q) {
-                int32_t k = acol[q];
-                lo = min(lo, bmin[k]);
-                hi = max(hi, bmax[k]);
-            }
-            int64_t span = (int64_t)hi - lo + 1;
-            rowlo[i] = lo;
-            if (span <= kWinSmall) {
-                b = RB_WIN64;
-            } else if (span <= kWinLarge) {
-                b = RB_WIN1024;
-            } else if (u <= kHashMaxItems[0]) {
-                b = RB_H128;
-            } else if (u <= kHashMaxItems[1]) {
-                b = RB_H512;
-            } else if (u <= kHashMaxItems[2]) {
-                b = RB_H2048;
+    __syncthreads();
+    int64_t su = 0, heavy = 0, hprod = 0, c512 = 0, c4k = 0, c32k = 0, mu = 0;
+    double u2 = 0.0;
+    for (int64_t base = (int64_t)blockIdx.x * 256; base < n; base += (int64_t)gridDim.x * 256) {
+        const int64_t i = base + threadIdx.x;
+        const bool in = i < n;
+        int64_t u = 0;
+        if (in) {
+            const int64_t a0 = arp[i], a1 = arp[i + 1];
+            u = S[a1] - S[a0];
+            int b;
+            if (u == 0) {
+                b = RB_EMPTY;
+            } else if (u > tau) {
+                b = RB_HEAVY;
+                heavy += 1;
+                hprod += u;
+            } else if (u <= kThreadMaxItems[2]) {
+                b = u <= kThreadMaxItems[0] ? RB_T8 : (u <= kThreadMaxItems[1] ? RB_T16 : RB_T32);
             } else {
-                b = RB_H8192;
+                int32_t lo = 0x7fffffff, hi = -1;
+                for (int64_t q = a0; q < a1; ++q) {
+                    const int32_t k = acol[q];
+                    lo = min(lo, bmin[k]);
+                    hi = max(hi, bmax[k]);
+                }
+                const int64_t span = (int64_t)hi - lo + 1;
+                rowlo[i] = lo;
+                if (span <= kWinSmall) {
+                    b = RB_WIN64;
+                } else if (span <= kWinLarge) {
+                    b = RB_WIN1024;
+                } else if (u <= kHashMaxItems[0]) {
+                    b = RB_H128;
+                } else if (u <= kHashMaxItems[1]) {
+                    b = RB_H512;
+                } else if (u <= kHashMaxItems[2]) {
+                    b = RB_H2048;
+                } else {
+                    b = RB_H8192;
+                }
             }
+            bin[i] = (uint8_t)b;
+            // the structural statistics of the rows' products: F_h counts and
+            // the sum of squares (for the coefficient of variation)
+            su += u;
+            c512 += u <= 512;
+            c4k += u <= 4096;
+            c32k += u <= 32768;
+            u2 += (double)u * (double)u;
+            mu = u > mu ? u : mu;
         }
-        bin[i] = (uint8_t)b;
-    }
-    int64_t su = block_reduce_sum<256>(u, sh);
-    int64_t sh_heavy = block_reduce_sum<256>(heavy, sh);
-    int64_t sh_hprod = block_reduce_sum<256>(hprod, sh);
-    // the structural statistics of the rows' products: F_h counts, sum of
-    // squares (for the coefficient of variation) and the u histogram
-    const bool in = i < n;
-    const int64_t c512 = block_reduce_sum<256>((int64_t)(in && u <= 512), sh);
-    const int64_t c4k = block_reduce_sum<256>((int64_t)(in && u <= 4096), sh);
-    const int64_t c32k = block_reduce_sum<256>((int64_t)(in && u <= 32768), sh);
-    const double u2 = block_reduce_sum<256>(in ? (double)u * (double)u : 0.0, shd);
-    // the lanes of a wave that share a bucket add once (a banded matrix puts
-    // nearly every row in one bucket); buckets below 64 gather in LDS first
-    {
-        const int b = in ? u_bucket(u) : -1;
-        uint64_t act = __ballot(b >= 0);
+        // the u histogram: the lanes of a wave that share a bucket add once
+        // (a banded matrix puts nearly every row in one bucket); buckets
+        // below 64 gather in LDS first
+        const int bk = in ? u_bucket(u) : -1;
+        uint64_t act = __ballot(bk >= 0);
         while (act) {
             const int leader = __ffsll((unsigned long long)act) - 1;
-            const int lb = __shfl(b, leader);
-            const uint64_t m = __ballot(b == lb);
+            const int lb = __shfl(bk, leader);
+            const uint64_t m = __ballot(bk == lb);
             if (lane_id() == leader) {
                 if (lb < 64) atomicAdd(&hsmall[lb], __popcll(m));
                 else atomicAdd(&uhist[lb], __popcll(m));
@@ -187,21 +194,26 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
             act &= ~m;
         }
     }
-    __syncthreads();
+    su = block_reduce_sum<256>(su, sh);
+    heavy = block_reduce_sum<256>(heavy, sh);
+    hprod = block_reduce_sum<256>(hprod, sh);
+    c512 = block_reduce_sum<256>(c512, sh);
+    c4k = block_reduce_sum<256>(c4k, sh);
+    c32k = block_reduce_sum<256>(c32k, sh);
+    u2 = block_reduce_sum<256>(u2, shd);
+    // block_reduce_sum ends with a barrier: every wave's LDS histogram adds are in
     if (threadIdx.x < 64 && hsmall[threadIdx.x]) atomicAdd(&uhist[threadIdx.x], hsmall[threadIdx.x]);
-    // max via wave shuffles, then one atomic per wave
-    int64_t mu = u;
 #pragma unroll
     for (int d = kWave / 2; d > 0; d >>= 1) {
-        int64_t o = __shfl_xor(mu, d, kWave);
+        const int64_t o = __shfl_xor(mu, d, kWave);
         mu = mu > o ? mu : o;
     }
     if (lane_id() == 0 && mu > 0)
         atomicMax((unsigned long long*)&stats[1], (unsigned long long)mu);
     if (threadIdx.x == 0) {
         atomicAdd((unsigned long long*)&stats[0], (unsigned long long)su);
-        atomicAdd((unsigned long long*)&stats[2], (unsigned long long)sh_heavy);
-        atomicAdd((unsigned long long*)&stats[3], (unsigned long long)sh_hprod);
+        atomicAdd((unsigned long long*)&stats[2], (unsigned long long)heavy);
+        atomicAdd((unsigned long long*)&stats[3], (unsigned long long)hprod);
         atomicAdd((unsigned long long*)&stats[4], (unsigned long long)c512);
         atomicAdd((unsigned long long*)&stats[5], (unsigned long long)c4k);
         atomicAdd((unsigned long long*)&stats[6], (unsigned long long)c32k);
@@ -221,7 +233,9 @@ void classify_rows(const DevCSR& A, const int64_t* S, const int32_t* bmin, const
     fill<int64_t>(stats, 8, 0, st);
     fill<int32_t>(uhist, kUHistBuckets, 0, st);
     if (A.n > 0) {
-        hipLaunchKernelGGL(k_classify_rows, dim3(grid_1d(ceil_div(A.n, 256))), dim3(256), 0, st,
+        hipLaunchKernelGGL(k_classify_rows,
+                           dim3(grid_1d(std::min<int64_t>(ceil_div(A.n, 256), kClassifyMaxBlocks))),
+                           dim3(256), 0, st,
                            A.rp, A.col, A.n, S, bmin, bmax, tau, bin, rowlo, stats, uhist);
         SG_LAUNCH_CHECK();
     }
