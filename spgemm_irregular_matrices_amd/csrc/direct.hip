@@ -118,23 +118,28 @@ void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, i
 // ---------------------------------------------------------------- offsets
 // off[h*req + s] = C.rowPtr of heavy row h + distinct columns of the row in
 // slots before s (slots are in column order, so this is the item's place in
-// the sorted output row).
-__global__ void k_direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int req,
-                                 const int64_t* dist_fin, int64_t* off) {
-    const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (h >= H) return;
+// the sorted output row). One wavefront per heavy row scans its slots.
+__global__ __launch_bounds__(256) void k_direct_offsets(const int64_t* C_rp, const int32_t* hrows,
+                                                       int64_t H, int req,
+                                                       const int64_t* dist_fin, int64_t* off) {
+    const int64_t h = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    if (h >= H) return;  // whole waves leave together
+    const int lane = lane_id();
     int64_t run = C_rp[hrows[h]];
-    for (int s = 0; s < req; ++s) {
-        off[h * req + s] = run;
-        run += dist_fin[h * req + s];
+    for (int sb = 0; sb < req; sb += kWave) {
+        const int sl = sb + lane;
+        const int64_t c = sl < req ? dist_fin[h * req + sl] : 0;
+        const int64_t inc = wave_inclusive_scan(c);
+        if (sl < req) off[h * req + sl] = run + inc - c;
+        run += __shfl(inc, kWave - 1, kWave);
     }
 }
 
 void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int req,
                     const int64_t* dist_fin, int64_t* off, hipStream_t st) {
     if (H <= 0) return;
-    hipLaunchKernelGGL(k_direct_offsets, dim3(grid_1d(ceil_div(H, 256))), dim3(256), 0, st, C_rp,
-                       hrows, H, req, dist_fin, off);
+    hipLaunchKernelGGL(k_direct_offsets, dim3(grid_1d(ceil_div(H * kWave, 256))), dim3(256), 0, st,
+                       C_rp, hrows, H, req, dist_fin, off);
     SG_LAUNCH_CHECK();
 }
 
@@ -486,8 +491,7 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
 __global__ __launch_bounds__(256) void k_direct_totals(const int64_t* hq0, const int64_t* hq1,
                                                       int64_t nitems, int logreq,
                                                       const int64_t* elem_fin,
-                                                      const int64_t* dist_fin,
-                                                      unsigned long long* out6) {
+                                                      const int64_t* dist_fin, int64_t* part) {
     __shared__ int64_t sh[256 / kWave + 1];
     int64_t dp = 0, dout = 0, de = 0, rp = 0, rout = 0, re = 0;
     int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -511,20 +515,36 @@ __global__ __launch_bounds__(256) void k_direct_totals(const int64_t* hq0, const
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
         const int64_t r = block_reduce_sum<256>(v[i], sh);
-        if (threadIdx.x == 0 && r) atomicAdd(&out6[i], (unsigned long long)r);
+        if (threadIdx.x == 0) part[(int64_t)i * gridDim.x + blockIdx.x] = r;
+    }
+}
+
+// out6[i] = sum of the groups' partial sums i (one work group).
+__global__ __launch_bounds__(256) void k_sum_parts(const int64_t* part, int nparts, int64_t* out6) {
+    __shared__ int64_t sh[256 / kWave + 1];
+    for (int i = 0; i < 6; ++i) {
+        int64_t v = 0;
+        for (int b = threadIdx.x; b < nparts; b += 256) v += part[(int64_t)i * nparts + b];
+        v = block_reduce_sum<256>(v, sh);
+        if (threadIdx.x == 0) out6[i] = v;
     }
 }
 
 void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
-                   const int64_t* elem_fin, const int64_t* dist_fin, int64_t* out6,
+                   const int64_t* elem_fin, const int64_t* dist_fin, int64_t* out6, Arena& ar,
                    hipStream_t st) {
-    fill<int64_t>(out6, 6, 0, st);
     const int64_t n = H * req;
-    if (n <= 0) return;
-    // few work groups: their sums meet at six global counters
-    const int64_t blocks = std::min<int64_t>(ceil_div(n, 256), 256);
-    hipLaunchKernelGGL(k_direct_totals, dim3(grid_1d(blocks)), dim3(256), 0, st, hq0, hq1, n,
-                       ilog2(req), elem_fin, dist_fin, (unsigned long long*)out6);
+    if (n <= 0) {
+        fill<int64_t>(out6, 6, 0, st);
+        return;
+    }
+    // partial sums per group, then one group adds them: no shared counter
+    const int blocks = (int)std::min<int64_t>(ceil_div(n, 256), 2048);
+    int64_t* part = ar.get<int64_t>("dtot_parts", (size_t)6 * blocks);
+    hipLaunchKernelGGL(k_direct_totals, dim3(blocks), dim3(256), 0, st, hq0, hq1, n, ilog2(req),
+                       elem_fin, dist_fin, part);
+    SG_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_sum_parts, dim3(1), dim3(256), 0, st, part, blocks, out6);
     SG_LAUNCH_CHECK();
 }
 

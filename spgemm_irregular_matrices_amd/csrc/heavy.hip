@@ -810,14 +810,13 @@ __global__ void k_bslot_counts(const int64_t* brp, const int32_t* bcol, int64_t 
 // The same counts without global atomics: one wavefront per B row counts
 // its slots in LDS, peeling one distinct slot of each 64-entry batch at a
 // time (B rows are mostly sorted, so a batch holds few slots), then writes
-// the row's counts and, when asked, their exclusive prefix (the row's slot
-// starts, with the row length last).
+// the row's counts.
 constexpr int kBslotNT = 256;
 constexpr int kBslotMaxReq = 4096;
 
 __global__ __launch_bounds__(kBslotNT) void k_bslot_rows(const int64_t* brp, const int32_t* bcol,
                                                          int64_t nb, int logW, int req,
-                                                         int32_t* bslot, int32_t* bsplit) {
+                                                         int32_t* bslot) {
     extern __shared__ int lds_c[];
     const int w = threadIdx.x / kWave, lane = lane_id();
     int* cnt = lds_c + w * req;
@@ -837,18 +836,7 @@ __global__ __launch_bounds__(kBslotNT) void k_bslot_rows(const int64_t* brp, con
             act &= ~m;
         }
     }
-    int run = 0;
-    for (int sb = 0; sb < req; sb += kWave) {
-        const int s = sb + lane;
-        const int c = s < req ? cnt[s] : 0;
-        if (s < req) bslot[k * req + s] = c;
-        if (bsplit) {
-            const int inc = wave_inclusive_scan(c);
-            if (s < req) bsplit[k * (req + 1) + s] = run + inc - c;
-            run += __shfl(inc, kWave - 1, kWave);
-        }
-    }
-    if (bsplit && lane == 0) bsplit[k * (req + 1) + req] = run;
+    for (int s = lane; s < req; s += kWave) bslot[k * req + s] = cnt[s];
 }
 
 // Distinct columns: one work group per heavy row keeps a one-bit-per-column
@@ -1108,25 +1096,22 @@ static size_t hsym_lds(int ew, int64_t nwp, int64_t reqp) {
 
 size_t heavy_symbolic_lds(int64_t ppow, int64_t req) { return hsym_lds(kHsymEW, ppow / 32, req); }
 
-bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
+void heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
                     int64_t H, int64_t Nh, int64_t max_u, int ncu, int64_t dev_lds, int64_t ppow,
-                    int64_t wfin, int32_t* bslot, int32_t* bsplit, int64_t* elem_fin,
-                    int64_t* dist_fin, Arena& ar, hipStream_t st) {
-    if (H <= 0) return false;
+                    int64_t wfin, int32_t* bslot, int64_t* elem_fin, int64_t* dist_fin, Arena& ar,
+                    hipStream_t st) {
+    if (H <= 0) return;
     const int64_t req = ppow / wfin;
     const int logW = ilog2(wfin);
-    bool split_done = false;
     if (req <= kBslotMaxReq) {
         if (B.n > 0) {
             const size_t lds = (size_t)(kBslotNT / kWave) * req * 4;
             SG_HIP(hipFuncSetAttribute((const void*)k_bslot_rows,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
             hipLaunchKernelGGL(k_bslot_rows, dim3(grid_1d(ceil_div(B.n * kWave, kBslotNT))),
-                               dim3(kBslotNT), lds, st, B.rp, B.col, B.n, logW, (int)req, bslot,
-                               bsplit);
+                               dim3(kBslotNT), lds, st, B.rp, B.col, B.n, logW, (int)req, bslot);
             SG_LAUNCH_CHECK();
         }
-        split_done = bsplit != nullptr;
     } else {
         fill<int32_t>(bslot, B.n * req, 0, st);
         if (B.n > 0) {
@@ -1197,7 +1182,6 @@ bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const in
                            (const uint32_t*)sp.gbits, (int)req, nwords, dist_fin);
         SG_LAUNCH_CHECK();
     }
-    return split_done;
 }
 
 // Per natural chunk of a level: its first finest slot, and its element and

@@ -175,14 +175,12 @@ void chunk_colbase(int64_t nparents, int nch, int64_t width, const int32_t* pare
 // heavy_symbolic_lds(ppow, ppow/wfin) bytes of LDS.
 size_t heavy_symbolic_lds(int64_t ppow, int64_t req);
 // bslot (B.n * (ppow/wfin) int32) receives every B row's entries per slot.
-// If bsplit (B.n * (ppow/wfin + 1) int32) is given it may also receive the
-// rows' slot starts (their exclusive prefix); returns whether it did.
 // S is the entry product prefix, Nh the heavy rows' products, max_u the
 // largest u(i); ncu and dev_lds size the per-work-group share.
-bool heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
+void heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
                     int64_t H, int64_t Nh, int64_t max_u, int ncu, int64_t dev_lds, int64_t ppow,
-                    int64_t wfin, int32_t* bslot, int32_t* bsplit, int64_t* elem_fin,
-                    int64_t* dist_fin, Arena& ar, hipStream_t st);
+                    int64_t wfin, int32_t* bslot, int64_t* elem_fin, int64_t* dist_fin, Arena& ar,
+                    hipStream_t st);
 // Counts, distinct counts and first finest slot of every natural chunk of a
 // level, summed from the finest slots (g slots per chunk).
 void level_from_slots(const int64_t* parent_slot0, const int32_t* parent_inv, int64_t nparents,
@@ -275,7 +273,7 @@ void direct_gather_values(const int64_t* bperm, const double* bval, int64_t nnz,
                           hipStream_t st);
 // out6 = {dense items: products, outputs, A entries read; rank items: the same}.
 void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
-                   const int64_t* elem_fin, const int64_t* dist_fin, int64_t* out6,
+                   const int64_t* elem_fin, const int64_t* dist_fin, int64_t* out6, Arena& ar,
                    hipStream_t st);
 size_t direct_window_lds(int64_t W);
 void direct_accumulate(const DirectArgs& d, int bin, int64_t p0, int64_t n, hipStream_t st);

@@ -755,7 +755,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
             int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
             heavy_symbolic(A, B, S, hrows, p->H, p->Nh, p->stats.max_products, p->dev_cus,
-                           p->dev_lds, q.ppow, wfin, bslot, nullptr, elem_fin, dist_fin, ar, st);
+                           p->dev_lds, q.ppow, wfin, bslot, elem_fin, dist_fin, ar, st);
             add_bytes(p, 0, SPGEMM_PHASE_HISTO, 4.0 * p->Nh + 16.0 * p->H * req);
         }
         if (p->direct) {
@@ -775,7 +775,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
                             ar.get<int32_t>("dine", (size_t)(p->H * req)), bins, ar, st);
             int64_t* tot6 = ar.get<int64_t>("dtot", 6);
             direct_totals(ar.get<int64_t>("h_q0", (size_t)p->H), ar.get<int64_t>("h_q1", (size_t)p->H),
-                          p->H, (int)req, elem_fin, dist_fin, tot6, st);
+                          p->H, (int)req, elem_fin, dist_fin, tot6, ar, st);
             int64_t* hb = d2h(p, bins, CB_COUNT + 1, st);
             for (int b = 0; b <= CB_COUNT; ++b) p->dir_bins[b] = hb[b];
             int64_t* ht = d2h(p, tot6, 6, st);
