@@ -182,7 +182,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the product is not sharded across GPUs in this build", file=sys.stderr)
+              "the library runs one product on one GPU", file=sys.stderr)
         sys.exit(2)
     import torch
 
