@@ -983,12 +983,17 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
         constexpr int U = 8;  // pieces in flight per wave
         int j0 = 0;  // entry of the wave's last piece (pieces rise per wave)
         for (int piece = w; piece < tot; piece += NW * U) {
-            // The entries of this iteration's pieces from one LDS read: lane l
-            // holds the piece prefix of entry j0+1+l, and a ballot counts the
-            // entries that start at or before a piece (prefixes rise). Only
-            // if all 64 do is the rest walked one entry at a time.
-            const int win = j0 + 1 + lane;
-            const int pw = win <= ne ? ppre[win] : INT_MAX;
+            // The entries of this iteration's pieces, read once into the
+            // lanes: lane l holds entry j0+l (first piece, length, B start)
+            // and the first piece of entry j0+1+l. A ballot counts the
+            // entries after j0 that start at or before a piece (prefixes
+            // rise), and the piece's entry is read from that lane. Only if
+            // all 64 do is the rest walked one entry at a time.
+            const int wj = j0 + lane;
+            const int pw = wj + 1 <= ne ? ppre[wj + 1] : INT_MAX;
+            const int wp = wj < ne ? ppre[wj] : 0;
+            const int wn = wj < ne ? nbv[wj] : 0;
+            const int64_t wb = wj < ne ? bst[wj] : 0;
             uint32_t c[U];
             int jl = j0;
 #pragma unroll
@@ -997,14 +1002,26 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
                 c[uu] = 0xffffffffu;
                 if (pu < tot) {
                     const int cnt = __popcll(__ballot(pw <= pu));
-                    int j = j0 + cnt;
-                    if (cnt == kWave) {
+                    int pj, nj;
+                    int64_t bj;
+                    if (cnt < kWave) {
+                        jl = j0 + cnt;
+                        pj = __builtin_amdgcn_readlane(wp, cnt);
+                        nj = __builtin_amdgcn_readlane(wn, cnt);
+                        bj = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                            (int)((uint64_t)wb >> 32), cnt) << 32) |
+                                       (uint32_t)__builtin_amdgcn_readlane((int)wb, cnt));
+                    } else {
+                        int j = j0 + cnt;
                         j = jl > j ? jl : j;
                         while (ppre[j + 1] <= pu) ++j;
+                        jl = j;
+                        pj = ppre[j];
+                        nj = nbv[j];
+                        bj = bst[j];
                     }
-                    jl = j;
-                    const int off = (pu - ppre[j]) * kWave + lane;
-                    if (off < nbv[j]) c[uu] = (uint32_t)bcol[bst[j] + off];
+                    const int off = (pu - pj) * kWave + lane;
+                    if (off < nj) c[uu] = (uint32_t)bcol[bj + off];
                 }
             }
             j0 = jl;
