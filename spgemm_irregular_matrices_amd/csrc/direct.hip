@@ -578,8 +578,8 @@ void direct_accumulate(const DirectArgs& d, int bin, int64_t p0, int64_t n, hipS
         }
         case CB_H128: launch_direct_rank<64, 1>(d, p0, n, st); break;
         case CB_H512: launch_direct_rank<64, 4>(d, p0, n, st); break;
-        case CB_H2048: launch_direct_rank<128, 8>(d, p0, n, st); break;
-        case CB_H8192: launch_direct_rank<256, 8>(d, p0, n, st); break;
+        case CB_H2048: launch_direct_rank<256, 4>(d, p0, n, st); break;
+        case CB_H8192: launch_direct_rank<512, 4>(d, p0, n, st); break;
         default: throw std::logic_error("not a direct item class");
     }
 }
