@@ -9,8 +9,9 @@
 // records where row k's entries of slot s start, so the products of heavy
 // row i that fall into chunk s are the slices [spos[s*B.n + k],
 // spos[s*B.n + k + 1]) for the B rows k of row i's entries, each scaled by
-// its a_ik, and one slot's part of B is contiguous. One work group per (heavy row, chunk) item forms exactly those
-// products and accumulates them in LDS with the page's accumulators
+// its a_ik, and one slot's part of B is contiguous. One work group per
+// (heavy row, chunk) item forms exactly those products and accumulates them
+// in LDS with the page's accumulators
 // (Section III-E): the bitmap-rank accumulator for items of at most
 // kDirectDense products, the dense window above that. C-hat and
 // C-hat-reord are never written; the per-item product and distinct-column
