@@ -290,6 +290,9 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
     const int32_t x = d.items[p0 + item];
     const int64_t q0 = d.iq0[p0 + item];
     const int64_t q1 = q0 + d.ine[p0 + item];
+    // the output offset is read now, beside the item's entries, rather
+    // than after the accumulation
+    const int64_t off = d.off[x];
     const int64_t h = x / d.req;
     const int s = (int)(x - h * d.req);
     for (int wd = tt; wd < NWD; wd += TW) bits[wd] = 0u;
@@ -351,7 +354,6 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
     }
     // columns straight from the bitmap words, values once all are summed
     const int32_t lo = s << d.logW;
-    const int64_t off = d.off[x];
     for (int wd = w0; wd < w1; ++wd) {
         uint32_t bw = bits[wd];
         int64_t r = off + wpre[wd];
@@ -401,6 +403,7 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     const int32_t x = d.items[p0 + item];
     const int64_t q0 = d.iq0[p0 + item];
     const int64_t q1 = q0 + d.ine[p0 + item];
+    const int64_t off = d.off[x];
     const int64_t h = x / d.req;
     const int s = (int)(x - h * d.req);
     for (int i = tt; i < NWD * 8; i += TW) flags[i] = 0u;
@@ -472,7 +475,6 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
         pre += __popc(bits[wd]);
     }
     __syncthreads();
-    const int64_t off = d.off[x];
     const int32_t lo = s << d.logW;
     for (int i = tt; i < W; i += TW) {
         const uint32_t word = bits[i >> 5];

@@ -902,12 +902,47 @@ __device__ __forceinline__ int64_t first_at_or_above(const int64_t* S, int64_t l
     return lo;
 }
 
-struct HsymSplitArgs {
-    const int64_t* S;      // entry product prefix
-    const int64_t* off;    // packed scan of HsymSplitOf (H + 1), or null: no split
-    const int32_t* bmap;   // work group -> heavy row
-    uint32_t* gbits;       // split rows' bitmaps (split index * nwords)
+// What one work group of the symbolic pass takes: A entries [a0, a1) of
+// heavy row h, and the row's split index (-1: the row has one work group).
+struct HsymGroup {
+    int64_t a0, a1;
+    int32_t h, sidx;
 };
+
+// One thread per work group, so that the searches of the split rows' entry
+// ranges run side by side here rather than at the start of each group.
+// off: packed scan of HsymSplitOf (H + 1) or null (one work group per row).
+__global__ void k_hsym_groups(const int64_t* arp, const int32_t* hrows, const int64_t* S,
+                              const int64_t* off, const int32_t* bmap, int64_t H,
+                              int64_t ngroups, HsymGroup* grp) {
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= ngroups) return;
+    HsymGroup g{0, 0, -1, -1};
+    if (!off) {
+        const int32_t r = hrows[b];
+        g = HsymGroup{arp[r], arp[r + 1], (int32_t)b, -1};
+    } else if (b < hsym_blocks(off[H])) {
+        const int64_t h = bmap[b];
+        const int64_t o = off[h];
+        const int64_t ns = hsym_blocks(off[h + 1]) - hsym_blocks(o);
+        const int32_t r = hrows[h];
+        int64_t a0 = arp[r], a1 = arp[r + 1];
+        int32_t sidx = -1;
+        if (ns > 1) {
+            // the entries whose products start in this group's 1/ns of the
+            // row's product range
+            const int64_t part = b - hsym_blocks(o);
+            const int64_t s0 = S[a0], u = S[a1] - s0;
+            const int64_t lo = s0 + u * part / ns, hi = s0 + u * (part + 1) / ns;
+            const int64_t e0 = first_at_or_above(S, a0, a1, lo);
+            a1 = part == ns - 1 ? a1 : first_at_or_above(S, a0, a1, hi);
+            a0 = e0;
+            sidx = (int32_t)hsym_split(o);
+        }
+        g = HsymGroup{a0, a1, (int32_t)h, sidx};
+    }
+    grp[b] = g;
+}
 
 // The row's column range may be taken in np parts, one launch each (when the
 // whole bitmap would leave one work group per CU): part p keeps bitmap words
@@ -915,9 +950,9 @@ struct HsymSplitArgs {
 // row and skips those outside its columns.
 template <int EW>
 __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
-    const int64_t* arp, const int32_t* acol, const int64_t* brp, const int32_t* bcol,
-    const int32_t* hrows, int req, int nwords, int wlo, int nwp, int sl0, int reqp,
-    const int32_t* bslot, int64_t* elem_fin, int64_t* dist_fin, HsymSplitArgs sp, int64_t H) {
+    const HsymGroup* grp, const int32_t* acol, const int64_t* brp, const int32_t* bcol, int req,
+    int nwords, int wlo, int nwp, int sl0, int reqp, const int32_t* bslot, int64_t* elem_fin,
+    int64_t* dist_fin, uint32_t* gbits) {
     static_assert(EW <= kHsymNT, "a staged window holds at most one entry per thread");
     extern __shared__ int64_t lds_s[];
     constexpr int NW = kHsymNT / kWave;
@@ -929,40 +964,18 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     int* dsl = ppre + EW + 1;                               // reqp distinct counts
     uint32_t* bits = (uint32_t*)(dsl + reqp);               // nwp
     __shared__ int scan_sh[NW + 1];
-    __shared__ int64_t range_sh[2];
     const int tt = threadIdx.x;
     const int w = tt / kWave, lane = lane_id();
-    int64_t h = blockIdx.x, ns = 1, sidx = 0;
-    if (sp.off) {
-        // the whole work group leaves together when the grid's bound exceeds the split count
-        if ((int64_t)blockIdx.x >= hsym_blocks(sp.off[H])) return;
-        h = sp.bmap[blockIdx.x];
-        const int64_t o = sp.off[h];
-        ns = hsym_blocks(sp.off[h + 1]) - hsym_blocks(o);
-        sidx = hsym_split(o);
-    }
+    const HsymGroup g = grp[blockIdx.x];
+    // the whole work group leaves together when the grid's bound exceeds the groups
+    if (g.h < 0) return;
+    const int64_t h = g.h, a0 = g.a0, a1 = g.a1;
     for (int i = tt; i < nwp; i += kHsymNT) bits[i] = 0u;
     for (int i = tt; i < reqp; i += kHsymNT) {
         dsl[i] = 0;
         esl[i] = 0ull;
     }
     __syncthreads();
-    const int32_t r = hrows[h];
-    int64_t a0 = arp[r], a1 = arp[r + 1];
-    if (ns > 1) {
-        // this work group's part: the entries whose products start in its
-        // 1/ns of the row's product range
-        if (tt == 0) {
-            const int64_t part = (int64_t)blockIdx.x - hsym_blocks(sp.off[h]);
-            const int64_t s0 = sp.S[a0], u = sp.S[a1] - s0;
-            const int64_t lo = s0 + u * part / ns, hi = s0 + u * (part + 1) / ns;
-            range_sh[0] = first_at_or_above(sp.S, a0, a1, lo);
-            range_sh[1] = part == ns - 1 ? a1 : first_at_or_above(sp.S, a0, a1, hi);
-        }
-        __syncthreads();
-        a0 = range_sh[0];
-        a1 = range_sh[1];
-    }
     for (int64_t ew = a0; ew < a1; ew += EW) {
         const int ne = (int)min((int64_t)EW, a1 - ew);
         int pc = 0;
@@ -1049,11 +1062,11 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
         }
         __syncthreads();
     }
-    if (ns > 1) {
+    if (g.sidx >= 0) {
         // a part of a split row: add into the row's global counts and bitmap
-        uint32_t* g = sp.gbits + sidx * (int64_t)nwords + wlo;
+        uint32_t* gb = gbits + g.sidx * (int64_t)nwords + wlo;
         for (int i = tt; i < nwp; i += kHsymNT)
-            if (bits[i]) atomicOr(&g[i], bits[i]);
+            if (bits[i]) atomicOr(&gb[i], bits[i]);
         for (int sl = tt; sl < reqp; sl += kHsymNT)
             if (esl[sl])
                 atomicAdd((unsigned long long*)&elem_fin[h * req + sl0 + sl], esl[sl]);
@@ -1157,46 +1170,52 @@ void heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const in
     // device holds at once, and at least kHsymSplitMin products
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(2, dev_lds / (int64_t)lds));
     const int64_t T = std::max<int64_t>(kHsymSplitMin, ceil_div(Nh, 4 * (int64_t)ncu * per_cu));
-    HsymSplitArgs sp{S, nullptr, nullptr, nullptr};
+    const int64_t* off = nullptr;
+    const int32_t* bmap = nullptr;
+    uint32_t* gbits = nullptr;
     int64_t grid = H, nsplit_max = 0;
     if (max_u > T) {
         // sum over rows of the work groups is at most H + Nh / T, and every
         // split row has more than T products
         nsplit_max = std::min<int64_t>(H, Nh / T);
         grid = H + Nh / T;
-        int64_t* off = ar.get<int64_t>("hsym_off", (size_t)H + 1);
-        scan_exclusive(HsymSplitOf{A.rp, S, hrows, T}, H, off, ar, st);
-        int32_t* bmap = ar.get<int32_t>("hsym_bmap", (size_t)grid);
+        int64_t* offw = ar.get<int64_t>("hsym_off", (size_t)H + 1);
+        scan_exclusive(HsymSplitOf{A.rp, S, hrows, T}, H, offw, ar, st);
+        int32_t* bmapw = ar.get<int32_t>("hsym_bmap", (size_t)grid);
         int32_t* smap = ar.get<int32_t>("hsym_smap", (size_t)nsplit_max + 1);
-        uint32_t* gbits = ar.get<uint32_t>("hsym_gbits", (size_t)nsplit_max * nwords + 1);
+        gbits = ar.get<uint32_t>("hsym_gbits", (size_t)nsplit_max * nwords + 1);
         fill<uint32_t>(gbits, nsplit_max * (int64_t)nwords, 0u, st);
-        hipLaunchKernelGGL(k_hsym_map, dim3(grid_1d(ceil_div(H, 256))), dim3(256), 0, st, off, H,
-                           (int)req, bmap, smap, elem_fin);
+        hipLaunchKernelGGL(k_hsym_map, dim3(grid_1d(ceil_div(H, 256))), dim3(256), 0, st, offw, H,
+                           (int)req, bmapw, smap, elem_fin);
         SG_LAUNCH_CHECK();
-        sp = HsymSplitArgs{S, off, bmap, gbits};
+        off = offw;
+        bmap = bmapw;
     }
+    HsymGroup* grp = ar.get<HsymGroup>("hsym_grp", (size_t)grid);
+    hipLaunchKernelGGL(k_hsym_groups, dim3(grid_1d(ceil_div(grid, 256))), dim3(256), 0, st, A.rp,
+                       hrows, S, off, bmap, H, grid, grp);
+    SG_LAUNCH_CHECK();
     const int nwp = nwords / np, reqp = (int)req / np;
     for (int part = 0; part < np; ++part) {
         if (ew == kHsymEW) {
             SG_HIP(hipFuncSetAttribute((const void*)k_heavy_symbolic<kHsymEW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
             hipLaunchKernelGGL(k_heavy_symbolic<kHsymEW>, dim3(grid_1d(grid)), dim3(kHsymNT), lds,
-                               st, A.rp, A.col, B.rp, B.col, hrows, (int)req, nwords, part * nwp,
-                               nwp, part * reqp, reqp, bslot, elem_fin, dist_fin, sp, H);
+                               st, grp, A.col, B.rp, B.col, (int)req, nwords, part * nwp, nwp,
+                               part * reqp, reqp, bslot, elem_fin, dist_fin, gbits);
         } else {
             SG_HIP(hipFuncSetAttribute((const void*)k_heavy_symbolic<kHsymEW / 2>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
             hipLaunchKernelGGL(k_heavy_symbolic<kHsymEW / 2>, dim3(grid_1d(grid)), dim3(kHsymNT),
-                               lds, st, A.rp, A.col, B.rp, B.col, hrows, (int)req, nwords,
-                               part * nwp, nwp, part * reqp, reqp, bslot, elem_fin, dist_fin, sp,
-                               H);
+                               lds, st, grp, A.col, B.rp, B.col, (int)req, nwords, part * nwp,
+                               nwp, part * reqp, reqp, bslot, elem_fin, dist_fin, gbits);
         }
         SG_LAUNCH_CHECK();
     }
-    if (sp.off && nsplit_max > 0) {
+    if (off && nsplit_max > 0) {
         hipLaunchKernelGGL(k_hsym_finalize, dim3(grid_1d(nsplit_max)), dim3(kHsymNT),
-                           (size_t)req * 4, st, sp.off, H, (const int32_t*)ar.get<int32_t>("hsym_smap", (size_t)nsplit_max + 1),
-                           (const uint32_t*)sp.gbits, (int)req, nwords, dist_fin);
+                           (size_t)req * 4, st, off, H, (const int32_t*)ar.get<int32_t>("hsym_smap", (size_t)nsplit_max + 1),
+                           (const uint32_t*)gbits, (int)req, nwords, dist_fin);
         SG_LAUNCH_CHECK();
     }
 }
