@@ -767,26 +767,33 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
                            ar.get<int64_t>("spos", (size_t)(B.n * req + 1)),
                            ar.get<int64_t>("bperm", (size_t)B.nnz + 1),
                            ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1), ar, st);
-            int64_t* bins = ar.get<int64_t>("dbins", CB_COUNT + 1);
+            // class starts and totals side by side, read back with nnz(C)
+            int64_t* bins = ar.get<int64_t>("dmeta", CB_COUNT + 1 + 6);
             direct_classify(elem_fin, p->H * req, (int)req, ar.get<int64_t>("h_q0", (size_t)p->H),
                             ar.get<int64_t>("h_q1", (size_t)p->H),
                             ar.get<int32_t>("ditems", (size_t)(p->H * req)),
                             ar.get<int64_t>("diq0", (size_t)(p->H * req)),
                             ar.get<int32_t>("dine", (size_t)(p->H * req)), bins, ar, st);
-            int64_t* tot6 = ar.get<int64_t>("dtot", 6);
+            int64_t* tot6 = bins + CB_COUNT + 1;
             direct_totals(ar.get<int64_t>("h_q0", (size_t)p->H), ar.get<int64_t>("h_q1", (size_t)p->H),
                           p->H, (int)req, elem_fin, dist_fin, tot6, ar, st);
-            int64_t* hb = d2h(p, bins, CB_COUNT + 1, st);
-            for (int b = 0; b <= CB_COUNT; ++b) p->dir_bins[b] = hb[b];
-            int64_t* ht = d2h(p, tot6, 6, st);
-            for (int i = 0; i < 6; ++i) p->dir_tot[i] = ht[i];
             add_bytes(p, 0, SPGEMM_PHASE_HISTO, 20.0 * B.nnz + 4.0 * B.n * (req + 1) +
                                                     8.0 * p->H * req);
+        }
+        if (p->direct) {
+            // the items are the final chunks: C-hat's row pointers and the
+            // per-level chunk classes are not needed, and a heavy row's
+            // count is the sum of its items' distinct columns
+            p->L = q.nlevels;
+            for (int l = 0; l < q.nlevels; ++l) p->stats.vchunks[l] = q.vchunks[l];
+            PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
+            reduce_children(dist_fin, (int)req, p->H, hrows, cnt_row, st);
         }
         CscBufs c = csc_bufs(p);
         int64_t ent_cur = 0, P_cur = 0, tile_cur = 0, crp_cur = 0;
         int64_t nat_cur[kMaxLevels] = {}, rp_cur[kMaxLevels] = {};
         for (BatchState& bt : p->batches) {
+            if (p->direct) break;
             const int64_t R0 = bt.h1 - bt.h0;
             {
                 PhaseScope ps(p, 0, SPGEMM_PHASE_CSR_TO_CSC, st);
@@ -828,11 +835,14 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             }
         }
         // row counts of the heavy rows
-        PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
-        if (q.nlevels == 0) {
-            if (p->fused_sym) reduce_children(dist_fin, 1, p->H, hrows, cnt_row, st);
-        } else {
-            reduce_children(lvarr<int64_t>(p, 0, "_nnz"), q.vchunks[0], p->H, hrows, cnt_row, st);
+        if (!p->direct) {
+            PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
+            if (q.nlevels == 0) {
+                if (p->fused_sym) reduce_children(dist_fin, 1, p->H, hrows, cnt_row, st);
+            } else {
+                reduce_children(lvarr<int64_t>(p, 0, "_nnz"), q.vchunks[0], p->H, hrows, cnt_row,
+                                st);
+            }
         }
     }
 
@@ -842,8 +852,20 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
         scan_exclusive(LoadI64{cnt_row}, n, C_rp, ar, st);
         add_bytes(p, 0, SPGEMM_PHASE_PREFIX_SUM, 16.0 * n);
     }
-    const int64_t nnz_c = d2h(p, C_rp + n, 1, st)[0];
-    heavy_offsets(p, hrows, C_rp, st);
+    int64_t nnz_c = 0;
+    if (p->direct) {
+        // nnz(C) and the direct path's class starts and totals in one wait
+        constexpr int kMeta = CB_COUNT + 1 + 6;
+        SG_HIP(hipMemcpyAsync(p->host + 1, ar.get<int64_t>("dmeta", kMeta),
+                              kMeta * sizeof(int64_t), hipMemcpyDeviceToHost, st));
+        const int64_t* h = d2h(p, C_rp + n, 1, st);
+        nnz_c = h[0];
+        for (int b = 0; b <= CB_COUNT; ++b) p->dir_bins[b] = h[1 + b];
+        for (int i = 0; i < 6; ++i) p->dir_tot[i] = h[2 + CB_COUNT + i];
+    } else {
+        nnz_c = d2h(p, C_rp + n, 1, st)[0];
+    }
+    if (!p->direct) heavy_offsets(p, hrows, C_rp, st);
     if (p->direct) {
         PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
         direct_offsets(C_rp, hrows, p->H, p->direct_req,
