@@ -966,6 +966,8 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     __shared__ int scan_sh[NW + 1];
     const int tt = threadIdx.x;
     const int w = tt / kWave, lane = lane_id();
+    // words per slot, and the rotation group of the bitmap words
+    const uint32_t gm = (uint32_t)min(32, nwords / req) - 1u;
     const HsymGroup g = grp[blockIdx.x];
     // the whole work group leaves together when the grid's bound exceeds the groups
     if (g.h < 0) return;
@@ -1038,11 +1040,16 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
                 }
             }
             j0 = jl;
+            // Column c = 32 q + r sets bit r of word q rotated by r inside
+            // its group of gm + 1 words (which never spans two slots), so
+            // that the runs of nearby columns of a B row fall into
+            // different words and banks; only per-slot counts are read.
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
-                const uint32_t wd = (c[uu] >> 5) - (uint32_t)wlo;
+                const uint32_t q = c[uu] >> 5, r = c[uu] & 31;
+                const uint32_t wd = ((q & ~gm) | ((q + r) & gm)) - (uint32_t)wlo;
                 if (c[uu] != 0xffffffffu && wd < (uint32_t)nwp)
-                    atomicOr(&bits[wd], 1u << (c[uu] & 31));
+                    atomicOr(&bits[wd], 1u << r);
             }
         }
         // element counts per slot: the sum of the window's B-row slot vectors
