@@ -145,10 +145,18 @@ void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int re
 }
 
 // ---------------------------------------------------------------- item classes
+// Class of the item at position i of the pass order: row by row (x = i),
+// or slot by slot (x = (i mod H) * req + i / H).
 struct DirectBinOf {
     const int64_t* elem;
-    __device__ int operator()(int64_t x) const {
-        const int64_t c = elem[x];
+    int64_t H;
+    int logreq;
+    bool slot_major;
+    __device__ int64_t item(int64_t i) const {
+        return slot_major ? ((i % H) << logreq) + i / H : i;
+    }
+    __device__ int operator()(int64_t i) const {
+        const int64_t c = elem[item(i)];
         if (c == 0) return CB_EMPTY;
         if (c > kDirectDense) return CB_DENSE;
         if (c <= kHashMaxItems[0]) return CB_H128;
@@ -171,11 +179,36 @@ __global__ void k_item_heads(const int32_t* items, int64_t n, int logreq, const 
     ine[p] = (int32_t)(hq1[h] - q0);
 }
 
+// The bitmap-rank classes in slot order: positions [bins[CB_H128],
+// bins[CB_EMPTY]) of the slot-major partition, as item ids.
+__global__ void k_rank_slot_major(const int32_t* perm_sm, const int64_t* bins, DirectBinOf bf,
+                                  int64_t n, int32_t* items) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= n || p < bins[CB_H128] || p >= bins[CB_EMPTY]) return;
+    items[p] = (int32_t)bf.item(perm_sm[p]);
+}
+
 void direct_classify(const int64_t* elem_fin, int64_t nitems, int req, const int64_t* hq0,
                      const int64_t* hq1, int32_t* items, int64_t* iq0, int32_t* ine,
                      int64_t* bins, Arena& ar, hipStream_t st) {
-    partition(DirectBinOf{elem_fin}, nitems, CB_COUNT, items, (int32_t*)nullptr, bins, ar, st);
+    const int logreq = ilog2(req);
+    const int64_t H = nitems >> logreq;
+    partition(DirectBinOf{elem_fin, H, logreq, false}, nitems, CB_COUNT, items, (int32_t*)nullptr,
+              bins, ar, st);
     if (nitems <= 0) return;
+    if (req > 1) {
+        // the same classes (a stable partition of the same counts), with the
+        // bitmap-rank items taken slot by slot: items of one slot that run
+        // together share that slot's slice starts and B entries in cache
+        // (the dense items keep row order, which measured faster for them)
+        const DirectBinOf sm{elem_fin, H, logreq, true};
+        int32_t* perm_sm = ar.get<int32_t>("ditems_sm", (size_t)nitems);
+        int64_t* bins_sm = ar.get<int64_t>("dbins_sm", CB_COUNT + 1);
+        partition(sm, nitems, CB_COUNT, perm_sm, (int32_t*)nullptr, bins_sm, ar, st);
+        hipLaunchKernelGGL(k_rank_slot_major, dim3(grid_1d(ceil_div(nitems, 256))), dim3(256), 0,
+                           st, perm_sm, bins, sm, nitems, items);
+        SG_LAUNCH_CHECK();
+    }
     hipLaunchKernelGGL(k_item_heads, dim3(grid_1d(ceil_div(nitems, 256))), dim3(256), 0, st, items,
                        nitems, ilog2(req), hq0, hq1, iq0, ine);
     SG_LAUNCH_CHECK();

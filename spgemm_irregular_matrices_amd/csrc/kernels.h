@@ -262,8 +262,9 @@ void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, i
                     int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st);
 void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int req,
                     const int64_t* dist_fin, int64_t* off, hipStream_t st);
-// Stable partition of the items x in [0, nitems) by class (CB_* bins, from
-// the exact product count elem_fin[x]).
+// Partition of the items x in [0, nitems) by class (CB_* bins, from the
+// exact product count elem_fin[x]): the dense class in row order, the
+// bitmap-rank classes in slot order (all rows' items of slot 0 first).
 // Also writes, per position, the item's row's first A entry (iq0) and entry
 // count (ine).
 void direct_classify(const int64_t* elem_fin, int64_t nitems, int req, const int64_t* hq0,
