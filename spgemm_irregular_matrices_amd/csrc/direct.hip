@@ -157,12 +157,12 @@ struct DirectBinOf {
     }
     __device__ int operator()(int64_t i) const {
         const int64_t c = elem[item(i)];
-        if (c == 0) return CB_EMPTY;
-        if (c > kDirectDense) return CB_DENSE;
-        if (c <= kHashMaxItems[0]) return CB_H128;
-        if (c <= kHashMaxItems[1]) return CB_H512;
-        if (c <= kHashMaxItems[2]) return CB_H2048;
-        return CB_H8192;
+        if (c == 0) return DC_EMPTY;
+        if (c > kDirectDense) return DC_DENSE;
+        int r = 0;
+#pragma unroll
+        for (int j = 0; j + 1 < kNumRankClasses; ++j) r += c > kRankClassMax[j];
+        return DC_RANK0 + r;
     }
 };
 
@@ -179,12 +179,12 @@ __global__ void k_item_heads(const int32_t* items, int64_t n, int logreq, const 
     ine[p] = (int32_t)(hq1[h] - q0);
 }
 
-// The bitmap-rank classes in slot order: positions [bins[CB_H128],
-// bins[CB_EMPTY]) of the slot-major partition, as item ids.
+// The bitmap-rank classes in slot order: positions [bins[DC_RANK0],
+// bins[DC_EMPTY]) of the slot-major partition, as item ids.
 __global__ void k_rank_slot_major(const int32_t* perm_sm, const int64_t* bins, DirectBinOf bf,
                                   int64_t n, int32_t* items) {
     const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (p >= n || p < bins[CB_H128] || p >= bins[CB_EMPTY]) return;
+    if (p >= n || p < bins[DC_RANK0] || p >= bins[DC_EMPTY]) return;
     items[p] = (int32_t)bf.item(perm_sm[p]);
 }
 
@@ -193,7 +193,7 @@ void direct_classify(const int64_t* elem_fin, int64_t nitems, int req, const int
                      int64_t* bins, Arena& ar, hipStream_t st) {
     const int logreq = ilog2(req);
     const int64_t H = nitems >> logreq;
-    partition(DirectBinOf{elem_fin, H, logreq, false}, nitems, CB_COUNT, items, (int32_t*)nullptr,
+    partition(DirectBinOf{elem_fin, H, logreq, false}, nitems, DC_COUNT, items, (int32_t*)nullptr,
               bins, ar, st);
     if (nitems <= 0) return;
     if (req > 1) {
@@ -203,8 +203,8 @@ void direct_classify(const int64_t* elem_fin, int64_t nitems, int req, const int
         // (the dense items keep row order, which measured faster for them)
         const DirectBinOf sm{elem_fin, H, logreq, true};
         int32_t* perm_sm = ar.get<int32_t>("ditems_sm", (size_t)nitems);
-        int64_t* bins_sm = ar.get<int64_t>("dbins_sm", CB_COUNT + 1);
-        partition(sm, nitems, CB_COUNT, perm_sm, (int32_t*)nullptr, bins_sm, ar, st);
+        int64_t* bins_sm = ar.get<int64_t>("dbins_sm", DC_COUNT + 1);
+        partition(sm, nitems, DC_COUNT, perm_sm, (int32_t*)nullptr, bins_sm, ar, st);
         hipLaunchKernelGGL(k_rank_slot_major, dim3(grid_1d(ceil_div(nitems, 256))), dim3(256), 0,
                            st, perm_sm, bins, sm, nitems, items);
         SG_LAUNCH_CHECK();
@@ -599,10 +599,16 @@ size_t direct_window_lds(int64_t W) {
     return (size_t)W * 9 + std::max<size_t>((size_t)(W / 32) * 8, (size_t)kWinHistWords * 4);
 }
 
-void direct_accumulate(const DirectArgs& d, int bin, int64_t p0, int64_t n, hipStream_t st) {
+void direct_accumulate(const DirectArgs& d, int cls, int64_t p0, int64_t n, hipStream_t st) {
     if (n <= 0) return;
-    switch (bin) {
-        case CB_DENSE: {
+    // teams of TW threads with KPT products each: TW * KPT is the class's
+    // largest item
+    static_assert(kRankClassMax[0] == 64 * 1 && kRankClassMax[1] == 64 * 2 &&
+                      kRankClassMax[2] == 64 * 4 && kRankClassMax[3] == 128 * 4 &&
+                      kRankClassMax[4] == 256 * 4 && kRankClassMax[5] == 512 * 4,
+                  "rank class table and kernel teams disagree");
+    switch (cls) {
+        case DC_DENSE: {
             const int64_t W = int64_t(1) << d.logW;
             const size_t lds = direct_window_lds(W);
             SG_HIP(hipFuncSetAttribute((const void*)k_direct_window,
@@ -612,10 +618,12 @@ void direct_accumulate(const DirectArgs& d, int bin, int64_t p0, int64_t n, hipS
             SG_LAUNCH_CHECK();
             break;
         }
-        case CB_H128: launch_direct_rank<64, 1>(d, p0, n, st); break;
-        case CB_H512: launch_direct_rank<64, 4>(d, p0, n, st); break;
-        case CB_H2048: launch_direct_rank<256, 4>(d, p0, n, st); break;
-        case CB_H8192: launch_direct_rank<512, 4>(d, p0, n, st); break;
+        case DC_RANK0 + 0: launch_direct_rank<64, 1>(d, p0, n, st); break;
+        case DC_RANK0 + 1: launch_direct_rank<64, 2>(d, p0, n, st); break;
+        case DC_RANK0 + 2: launch_direct_rank<64, 4>(d, p0, n, st); break;
+        case DC_RANK0 + 3: launch_direct_rank<128, 4>(d, p0, n, st); break;
+        case DC_RANK0 + 4: launch_direct_rank<256, 4>(d, p0, n, st); break;
+        case DC_RANK0 + 5: launch_direct_rank<512, 4>(d, p0, n, st); break;
         default: throw std::logic_error("not a direct item class");
     }
 }

@@ -237,6 +237,18 @@ void accumulate_chunks(const ChunkItems& it, int bin, int64_t p0, int64_t n, boo
 // partition keeps its slot offsets in LDS.
 constexpr int64_t kDirectDense = 2048;
 constexpr int kDirectMaxSlots = 4096;
+// Item classes of the direct path: the dense window, then bitmap-rank
+// classes by product count (class r takes items of at most
+// kRankClassMax[r] products), then the empty items.
+constexpr int kNumRankClasses = 6;
+constexpr int64_t kRankClassMax[kNumRankClasses] = {64, 128, 256, 512, 1024, 2048};
+static_assert(kRankClassMax[kNumRankClasses - 1] == kDirectDense, "rank classes end at the window");
+enum DirectClass : int {
+    DC_DENSE = 0,
+    DC_RANK0 = 1,
+    DC_EMPTY = DC_RANK0 + kNumRankClasses,
+    DC_COUNT
+};
 struct DirectArgs {
     const int32_t* items;   // item ids h*req + s, in class order
     int req;                // final chunks (slots) per row
@@ -262,9 +274,10 @@ void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, i
                     int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st);
 void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int req,
                     const int64_t* dist_fin, int64_t* off, hipStream_t st);
-// Partition of the items x in [0, nitems) by class (CB_* bins, from the
-// exact product count elem_fin[x]): the dense class in row order, the
-// bitmap-rank classes in slot order (all rows' items of slot 0 first).
+// Partition of the items x in [0, nitems) by class (DC_* classes, from the
+// exact product count elem_fin[x]; bins has DC_COUNT + 1 starts): the dense
+// class in row order, the bitmap-rank classes in slot order (all rows'
+// items of slot 0 first).
 // Also writes, per position, the item's row's first A entry (iq0) and entry
 // count (ine).
 void direct_classify(const int64_t* elem_fin, int64_t nitems, int req, const int64_t* hq0,
@@ -277,6 +290,6 @@ void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
                    const int64_t* elem_fin, const int64_t* dist_fin, int64_t* out6, Arena& ar,
                    hipStream_t st);
 size_t direct_window_lds(int64_t W);
-void direct_accumulate(const DirectArgs& d, int bin, int64_t p0, int64_t n, hipStream_t st);
+void direct_accumulate(const DirectArgs& d, int cls, int64_t p0, int64_t n, hipStream_t st);
 
 }  // namespace sg

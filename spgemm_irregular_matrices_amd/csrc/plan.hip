@@ -116,7 +116,7 @@ struct spgemm_plan_s {
     bool direct = false;     // heavy rows accumulated per (row, final chunk) from A and split B
     int direct_req = 0;      // final chunks per heavy row on the direct path
     int64_t direct_W = 0;    // their width
-    int64_t dir_bins[CB_COUNT + 1] = {};
+    int64_t dir_bins[DC_COUNT + 1] = {};
     int64_t dir_tot[6] = {};  // dense / rank items: products, outputs, A entries read
     // debug dumps (kept for single-batch products)
     bool dbg_valid = false;
@@ -768,13 +768,13 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
                            ar.get<int64_t>("bperm", (size_t)B.nnz + 1),
                            ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1), ar, st);
             // class starts and totals side by side, read back with nnz(C)
-            int64_t* bins = ar.get<int64_t>("dmeta", CB_COUNT + 1 + 6);
+            int64_t* bins = ar.get<int64_t>("dmeta", DC_COUNT + 1 + 6);
             direct_classify(elem_fin, p->H * req, (int)req, ar.get<int64_t>("h_q0", (size_t)p->H),
                             ar.get<int64_t>("h_q1", (size_t)p->H),
                             ar.get<int32_t>("ditems", (size_t)(p->H * req)),
                             ar.get<int64_t>("diq0", (size_t)(p->H * req)),
                             ar.get<int32_t>("dine", (size_t)(p->H * req)), bins, ar, st);
-            int64_t* tot6 = bins + CB_COUNT + 1;
+            int64_t* tot6 = bins + DC_COUNT + 1;
             direct_totals(ar.get<int64_t>("h_q0", (size_t)p->H), ar.get<int64_t>("h_q1", (size_t)p->H),
                           p->H, (int)req, elem_fin, dist_fin, tot6, ar, st);
             add_bytes(p, 0, SPGEMM_PHASE_HISTO, 20.0 * B.nnz + 4.0 * B.n * (req + 1) +
@@ -855,13 +855,14 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     int64_t nnz_c = 0;
     if (p->direct) {
         // nnz(C) and the direct path's class starts and totals in one wait
-        constexpr int kMeta = CB_COUNT + 1 + 6;
+        constexpr int kMeta = DC_COUNT + 1 + 6;
+        static_assert(1 + kMeta <= 64, "staging buffer");
         SG_HIP(hipMemcpyAsync(p->host + 1, ar.get<int64_t>("dmeta", kMeta),
                               kMeta * sizeof(int64_t), hipMemcpyDeviceToHost, st));
         const int64_t* h = d2h(p, C_rp + n, 1, st);
         nnz_c = h[0];
-        for (int b = 0; b <= CB_COUNT; ++b) p->dir_bins[b] = h[1 + b];
-        for (int i = 0; i < 6; ++i) p->dir_tot[i] = h[2 + CB_COUNT + i];
+        for (int b = 0; b <= DC_COUNT; ++b) p->dir_bins[b] = h[1 + b];
+        for (int i = 0; i < 6; ++i) p->dir_tot[i] = h[2 + DC_COUNT + i];
     } else {
         nnz_c = d2h(p, C_rp + n, 1, st)[0];
     }
@@ -972,7 +973,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
             // numeric calls; the structure may not)
             direct_gather_values(ar.get<int64_t>("bperm", (size_t)B.nnz + 1), B.val, B.nnz, bpval,
                                  st);
-            for (int b = CB_H128; b <= CB_H8192; ++b)
+            for (int b = DC_RANK0; b < DC_EMPTY; ++b)
                 direct_accumulate(d, b, p->dir_bins[b], p->dir_bins[b + 1] - p->dir_bins[b], st);
             add_bytes(p, 1, SPGEMM_PHASE_DIRECT_RANK,
                       24.0 * B.nnz + 10.0 * p->dir_tot[3] + 12.0 * p->dir_tot[4] +
@@ -980,8 +981,8 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         }
         {
             PhaseScope ps(p, 1, SPGEMM_PHASE_DIRECT_DENSE, st);
-            direct_accumulate(d, CB_DENSE, p->dir_bins[CB_DENSE],
-                              p->dir_bins[CB_DENSE + 1] - p->dir_bins[CB_DENSE], st);
+            direct_accumulate(d, DC_DENSE, p->dir_bins[DC_DENSE],
+                              p->dir_bins[DC_DENSE + 1] - p->dir_bins[DC_DENSE], st);
             add_bytes(p, 1, SPGEMM_PHASE_DIRECT_DENSE,
                       10.0 * p->dir_tot[0] + 12.0 * p->dir_tot[1] + 28.0 * p->dir_tot[2]);
         }
