@@ -385,19 +385,25 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
             atomicAdd(&vals[rank], v[k]);
         }
     }
-    // columns straight from the bitmap words, values once all are summed
-    const int32_t lo = s << d.logW;
+    // each column at its rank, in the staging area (free once the products
+    // are formed), so that columns and values are written out coalesced
+    static_assert(KPT * 2 <= 8, "the ranked columns fit the staged B starts");
+    uint16_t* scol = (uint16_t*)s_bo;
     for (int wd = w0; wd < w1; ++wd) {
         uint32_t bw = bits[wd];
-        int64_t r = off + wpre[wd];
+        int r = wpre[wd];
         while (bw) {
             const int b = __ffs(bw) - 1;
             bw &= bw - 1;
-            d.Ccol[r++] = lo + wd * 32 + b;
+            scol[r++] = (uint16_t)(wd * 32 + b);
         }
     }
     __syncthreads();
-    for (int r = tt; r < tot; r += TW) d.Cval[off + r] = vals[r];
+    const int32_t lo = s << d.logW;
+    for (int r = tt; r < tot; r += TW) {
+        d.Ccol[off + r] = lo + scol[r];
+        d.Cval[off + r] = vals[r];
+    }
 }
 
 // Dense window accumulation of the large items: the item's entries are
