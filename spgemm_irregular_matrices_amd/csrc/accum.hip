@@ -375,7 +375,10 @@ __global__ __launch_bounds__(TW) void k_acc_hash(RowItems ri, ChunkItems ci, int
         __syncthreads();
         for (int s = nnz + tt; s < P2; s += TW) keys[s] = 0xffffffffu;
         __syncthreads();
-        // bitonic sort of the next power of two above nnz
+        // bitonic sort of the next power of two above nnz. With distance
+        // j <= 32, the 64 pairs of a wave lie in its own block of 128 keys
+        // (the same blocks in every such step), so two such steps in a row
+        // need only the wave's own LDS ordering, not a work-group barrier.
         for (int k = 2; k <= P2; k <<= 1) {
             for (int j = k >> 1; j > 0; j >>= 1) {
                 for (int pi = tt; pi < (P2 >> 1); pi += TW) {
@@ -391,9 +394,12 @@ __global__ __launch_bounds__(TW) void k_acc_hash(RowItems ri, ChunkItems ci, int
                         vals[ix] = va;
                     }
                 }
-                __syncthreads();
+                const int jn = j > 1 ? (j >> 1) : k;  // the next step's distance
+                if (j <= kWave / 2 && jn <= kWave / 2) wave_lds_sync();
+                else __syncthreads();
             }
         }
+        __syncthreads();
         int64_t off = out_offset<MODE>(ri, ci, h);
         int32_t* oc = out_cols<MODE>(ri, ci);
         double* ov = out_vals<MODE>(ri, ci);
