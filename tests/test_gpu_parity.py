@@ -148,6 +148,44 @@ def test_thread_local_bins_exact():
     assert rp[-1] - rp[-2] == 1
 
 
+def _class_bound_items():
+    """Heavy rows whose (row, slot) items hold product counts at and around
+    every bound of the direct path's item classes (64, 128, 256, 512, 1 K and
+    2 K products, then the dense window): B row j holds targets[j] distinct
+    columns inside slot j mod 8 of a 65,536-column range (eight slots of
+    8192). Row i takes B rows i..i+7 (one per slot, so each item's count is
+    one target); row 24 + i takes three B rows of one slot, whose columns
+    overlap. The last rows take n single-column B rows of slot 0 each (n =
+    100 ... 2100), so that their items stage their entries over several
+    rounds of the teams (and repeat columns)."""
+    W, req = 8192, 8
+    targets = [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513,
+               1023, 1024, 1025, 2047, 2048, 2049, 3000, 4095, 5000, 8192]
+    nt = len(targets)
+    rng = np.random.default_rng(81)
+    brows = [sorted(((j % req) * W + rng.choice(W, size=L, replace=False)).tolist())
+             for j, L in enumerate(targets)]
+    many = (100, 300, 600, 1500, 2100)
+    brows += [[int(c)] for c in rng.integers(0, W, size=max(many))]
+    arows = [[(i + t) % nt for t in range(req)] for i in range(nt)]
+    arows += [sorted({i, (i + req) % nt, (i + 2 * req) % nt}) for i in range(nt)]
+    arows += [list(range(nt, nt + n)) for n in many]
+    nb = len(brows)
+    A0 = synth.from_rows(len(arows), nb, arows)
+    B0 = synth.from_rows(nb, W * req, brows)
+    A = synth.CSR(A0.nrows, nb, A0.rowptr, A0.col, synth.uniform_values(82, A0.nnz))
+    B = synth.CSR(nb, W * req, B0.rowptr, B0.col, synth.uniform_values(83, B0.nnz))
+    return A, B, targets
+
+
+def test_direct_item_class_bounds():
+    A, B, targets = _class_bound_items()
+    rp, col, val, st = run_gpu(A, B, tau_override=16)
+    assert st["numeric_path"] == 3 and st["final_chunk_width"] == 8192, st
+    assert st["heavy_rows"] == A.nrows
+    compare(A, B, rp, col, val)
+
+
 def test_multiply_in_one_call():
     """spgemm_multiply: with room for C, both phases in one call equal the
     two-call product; with too little room it returns CAPACITY with a valid
