@@ -23,9 +23,11 @@
 namespace sg {
 
 // ---------------------------------------------------------------- B split
-// bslot (row-major, B.n x req) to slot-major (req x B.n), in 32 x 32 tiles.
+// bslot (row-major, B.n x req) to slot-major (req x B.n), in 32 x 32 tiles;
+// with bocc, also one bit per (slot, B row) that has entries, slot-major,
+// ceil(B.n / 32) words per slot (a half wave holds 32 rows of one slot).
 __global__ __launch_bounds__(256) void k_bslot_transpose(const int32_t* bslot, int64_t nb, int req,
-                                                         int32_t* bslotT) {
+                                                         int32_t* bslotT, uint32_t* bocc) {
     __shared__ int32_t tile[32][33];
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
     const int64_t k0 = (int64_t)blockIdx.x * 32;
@@ -39,7 +41,14 @@ __global__ __launch_bounds__(256) void k_bslot_transpose(const int32_t* bslot, i
     for (int r = ty; r < 32; r += 8) {
         const int sl = s0 + r;
         const int64_t k = k0 + tx;
-        if (sl < req && k < nb) bslotT[(int64_t)sl * nb + k] = tile[tx][r];
+        const int32_t c = tile[tx][r];
+        if (sl < req && k < nb) bslotT[(int64_t)sl * nb + k] = c;
+        if (bocc) {
+            const uint64_t m = __ballot(c != 0);
+            if (tx == 0 && sl < req)
+                bocc[(int64_t)sl * gridDim.x + blockIdx.x] =
+                    (uint32_t)(threadIdx.x & 32 ? m >> 32 : m);
+        }
     }
 }
 
@@ -94,7 +103,7 @@ __global__ __launch_bounds__(kBpartNT) void k_bpartition(const int64_t* brp, con
 }
 
 void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int64_t* spos,
-                    int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st) {
+                    uint32_t* bocc, int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st) {
     if (W > 65536 || req > kDirectMaxSlots) throw std::logic_error("direct split limits");
     const int64_t n = (int64_t)req * B.n;
     if (B.n <= 0) {
@@ -103,7 +112,7 @@ void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, i
     }
     int32_t* bslotT = ar.get<int32_t>("bslotT", (size_t)n);
     hipLaunchKernelGGL(k_bslot_transpose, dim3(grid_1d(ceil_div(B.n, 32)), ceil_div(req, 32)),
-                       dim3(256), 0, st, bslot, B.n, req, bslotT);
+                       dim3(256), 0, st, bslot, B.n, req, bslotT, bocc);
     SG_LAUNCH_CHECK();
     scan_exclusive(LoadI32{bslotT}, n, spos, ar, st);
     if (B.nnz <= 0) return;
@@ -243,9 +252,13 @@ __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int6
     if (tt < NE && q < q1) {
         const int32_t k = d.Acol[q];
         const double a = d.Aval[q];
-        const int64_t* sp = d.spos + (int64_t)s * d.nb + k;
-        const int64_t lo = sp[0];
-        len = (int)(sp[1] - lo);
+        // with the occupancy bits, an empty (B row, slot) slice reads no bounds
+        int64_t lo = 0;
+        if (!d.bocc || (d.bocc[(int64_t)s * d.nbw + (k >> 5)] >> (k & 31)) & 1u) {
+            const int64_t* sp = d.spos + (int64_t)s * d.nb + k;
+            lo = sp[0];
+            len = (int)(sp[1] - lo);
+        }
         s_bo[tt] = lo;
         s_a[tt] = a;
     }

@@ -63,6 +63,8 @@ void launch_validate(const DevCSR& M, int* flag, hipStream_t st);
 // S[q] = sum_{q' < q} nnz(B[A.col[q'],:]) for q in [0, A.nnz] (InterOffsets,
 // Algorithm 3, at entry granularity: u(i) = S[rp[i+1]] - S[rp[i]]).
 void entry_prefix(const DevCSR& A, const DevCSR& B, int64_t* S, Arena& ar, hipStream_t st);
+// out[0] = sum over A entries q of (S[q+1] - S[q])^2.
+void entry_len_sq(const int64_t* S, int64_t nnz, double* out, hipStream_t st);
 
 // Per B row: smallest and largest column (INT32_MAX / -1 for empty rows).
 void brow_minmax(const DevCSR& B, int32_t* bmin, int32_t* bmax, hipStream_t st);
@@ -261,6 +263,8 @@ struct DirectArgs {
     const double* Aval;
     const int64_t* spos;    // req x B.nrows (+1): where row k's part of slot s starts in split B
     int64_t nb;             // B.nrows
+    const uint32_t* bocc;   // null, or req x nbw words: bit k of slot s set if the slice has entries
+    int64_t nbw;            // ceil(B.nrows / 32)
     const uint16_t* bcol16; // partitioned B: column offset inside the slot
     const double* bval;     // partitioned B: values
     const int64_t* off;     // per item: output offset in C
@@ -270,8 +274,14 @@ struct DirectArgs {
 // The split copy of B, slot by slot: spos (req*B.n + 1 int64) from the
 // per-row slot counts bslot; bperm[p] = B entry placed at p, bcol16[p] its
 // column inside its slot.
+// bocc (optional): the slices' occupancy bits (see DirectArgs).
 void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int64_t* spos,
-                    int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st);
+                    uint32_t* bocc, int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st);
+// Items test the occupancy bits before reading a slice's bounds when the B
+// rows that the products come from average fewer than req / kOccSparse
+// entries (a product-weighted mean), so that most (B row, slot) slices of
+// an item are empty.
+constexpr int kOccSparse = 4;
 void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int req,
                     const int64_t* dist_fin, int64_t* off, hipStream_t st);
 // Partition of the items x in [0, nitems) by class (DC_* classes, from the

@@ -115,6 +115,7 @@ struct spgemm_plan_s {
     bool fused_num = false;  // numeric level 0 forms its products itself (no C-hat)
     bool direct = false;     // heavy rows accumulated per (row, final chunk) from A and split B
     int direct_req = 0;      // final chunks per heavy row on the direct path
+    bool direct_occ = false;  // items test the slices' occupancy bits
     int64_t direct_W = 0;    // their width
     int64_t dir_bins[DC_COUNT + 1] = {};
     int64_t dir_tot[6] = {};  // dense / rank items: products, outputs, A entries read
@@ -765,10 +766,12 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
             direct_split_b(B, bslot, (int)req, wfin_d,
                            ar.get<int64_t>("spos", (size_t)(B.n * req + 1)),
+                           ar.get<uint32_t>("bocc", (size_t)(req * ceil_div(B.n, 32) + 1)),
                            ar.get<int64_t>("bperm", (size_t)B.nnz + 1),
                            ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1), ar, st);
             // class starts and totals side by side, read back with nnz(C)
-            int64_t* bins = ar.get<int64_t>("dmeta", DC_COUNT + 1 + 6);
+            int64_t* bins = ar.get<int64_t>("dmeta", DC_COUNT + 1 + 6 + 1);
+            entry_len_sq(S, A.nnz, (double*)(bins + DC_COUNT + 1 + 6), st);
             direct_classify(elem_fin, p->H * req, (int)req, ar.get<int64_t>("h_q0", (size_t)p->H),
                             ar.get<int64_t>("h_q1", (size_t)p->H),
                             ar.get<int32_t>("ditems", (size_t)(p->H * req)),
@@ -855,7 +858,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     int64_t nnz_c = 0;
     if (p->direct) {
         // nnz(C) and the direct path's class starts and totals in one wait
-        constexpr int kMeta = DC_COUNT + 1 + 6;
+        constexpr int kMeta = DC_COUNT + 1 + 6 + 1;
         static_assert(1 + kMeta <= 64, "staging buffer");
         SG_HIP(hipMemcpyAsync(p->host + 1, ar.get<int64_t>("dmeta", kMeta),
                               kMeta * sizeof(int64_t), hipMemcpyDeviceToHost, st));
@@ -863,6 +866,11 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
         nnz_c = h[0];
         for (int b = 0; b <= DC_COUNT; ++b) p->dir_bins[b] = h[1 + b];
         for (int i = 0; i < 6; ++i) p->dir_tot[i] = h[2 + DC_COUNT + i];
+        double len_sq;
+        memcpy(&len_sq, &h[8 + DC_COUNT], sizeof(double));
+        // the mean B-row length a product sees, against the slots per row
+        const double seen = p->stats.sum_products > 0 ? len_sq / (double)p->stats.sum_products : 0.0;
+        p->direct_occ = seen * kOccSparse < (double)p->direct_req;
     } else {
         nnz_c = d2h(p, C_rp + n, 1, st)[0];
     }
@@ -959,6 +967,8 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         d.Aval = A.val;
         d.spos = ar.get<int64_t>("spos", (size_t)(B.n * req + 1));
         d.nb = B.n;
+        d.nbw = ceil_div(B.n, 32);
+        d.bocc = p->direct_occ ? ar.get<uint32_t>("bocc", (size_t)(req * d.nbw + 1)) : nullptr;
         d.bcol16 = ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1);
         d.bval = bpval;
         d.off = ar.get<int64_t>("doff", (size_t)(p->H * req));

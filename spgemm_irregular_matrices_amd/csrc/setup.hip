@@ -69,6 +69,29 @@ void entry_prefix(const DevCSR& A, const DevCSR& B, int64_t* S, Arena& ar, hipSt
     scan_exclusive(EntryProducts{A.col, B.rp}, A.nnz, S, ar, st);
 }
 
+// Sum over A's entries of the square of the entry's product count (its B
+// row's length): with the products' sum, the mean B-row length that a
+// product sees.
+__global__ __launch_bounds__(256) void k_entry_len_sq(const int64_t* S, int64_t nnz, double* out) {
+    __shared__ double sh[256 / kWave + 1];
+    double acc = 0.0;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < nnz;
+         q += (int64_t)gridDim.x * 256) {
+        const double l = (double)(S[q + 1] - S[q]);
+        acc += l * l;
+    }
+    acc = block_reduce_sum<256>(acc, sh);
+    if (threadIdx.x == 0 && acc != 0.0) atomicAdd(out, acc);
+}
+
+void entry_len_sq(const int64_t* S, int64_t nnz, double* out, hipStream_t st) {
+    fill<double>(out, 1, 0.0, st);
+    if (nnz <= 0) return;
+    hipLaunchKernelGGL(k_entry_len_sq, dim3(grid_1d(std::min<int64_t>(ceil_div(nnz, 256), 512))),
+                       dim3(256), 0, st, S, nnz, out);
+    SG_LAUNCH_CHECK();
+}
+
 // ---------------------------------------------------------------- B row spans
 // One wavefront per B row: smallest and largest column of the row.
 __global__ __launch_bounds__(256) void k_brow_minmax(const int64_t* rp, const int32_t* col,

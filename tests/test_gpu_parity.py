@@ -186,6 +186,20 @@ def test_direct_item_class_bounds():
     compare(A, B, rp, col, val)
 
 
+def test_short_b_rows_over_many_slots():
+    """B rows of 4 entries over 2^18 columns (32 slots): most (B row, slot)
+    slices of a heavy row's items are empty, so the items test the slices'
+    occupancy bits before reading their bounds."""
+    lens = synth.zipf_lengths(3000, 2.1, 1200, seed=91)
+    lens[:3] = [1200, 900, 700]
+    A = synth.distinct_uniform_rows(lens, 4096, seed=92, value_seed=93)
+    B = synth.distinct_uniform_rows(np.full(4096, 4, dtype=np.int64), 1 << 18, seed=94,
+                                    value_seed=95)
+    rp, col, val, st = run_gpu(A, B)
+    assert st["numeric_path"] == 3 and st["heavy_rows"] >= 3, st
+    compare(A, B, rp, col, val)
+
+
 def test_multiply_in_one_call():
     """spgemm_multiply: with room for C, both phases in one call equal the
     two-call product; with too little room it returns CAPACITY with a valid
