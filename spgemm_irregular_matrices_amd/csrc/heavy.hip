@@ -965,7 +965,9 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     uint32_t* bits = (uint32_t*)(dsl + reqp);               // nwp
     __shared__ int scan_sh[NW + 1];
     const int tt = threadIdx.x;
-    const int w = tt / kWave, lane = lane_id();
+    // the wave index and the loop bounds below are uniform per wave: kept in
+    // scalar registers, the piece loop branches on them without exec masks
+    const int w = __builtin_amdgcn_readfirstlane(tt / kWave), lane = lane_id();
     // words per slot, and the rotation group of the bitmap words
     const uint32_t gm = (uint32_t)min(32, nwords / req) - 1u;
     const HsymGroup g = grp[blockIdx.x];
@@ -992,6 +994,7 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
         }
         int tot;
         int pre = block_exclusive_scan<kHsymNT>(pc, scan_sh, &tot);
+        tot = __builtin_amdgcn_readfirstlane(tot);
         if (tt < ne) ppre[tt] = pre;
         if (tt == 0) ppre[ne] = tot;
         __syncthreads();
