@@ -244,7 +244,7 @@ void direct_gather_values(const int64_t* bperm, const double* bval, int64_t nnz,
 // threads tt < NE): each entry's slice of the item's chunk (its start in the
 // partitioned B and its a value) and the exclusive prefix of slice lengths.
 // Returns the products of the round. Threads past the item's entries add 0.
-template <int TW, int NE>
+template <int TW, int NE, bool OCC>
 __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int64_t q1, int s,
                                             int* s_pre, int64_t* s_bo, double* s_a, int* red_sh) {
     const int tt = threadIdx.x;
@@ -254,7 +254,7 @@ __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int6
         const double a = d.Aval[q];
         // with the occupancy bits, an empty (B row, slot) slice reads no bounds
         int64_t lo = 0;
-        if (!d.bocc || (d.bocc[(int64_t)s * d.nbw + (k >> 5)] >> (k & 31)) & 1u) {
+        if (!OCC || (d.bocc[(int64_t)s * d.nbw + (k >> 5)] >> (k & 31)) & 1u) {
             const int64_t* sp = d.spos + (int64_t)s * d.nb + k;
             lo = sp[0];
             len = (int)(sp[1] - lo);
@@ -318,7 +318,7 @@ __device__ __forceinline__ int chunk_entry_fast(const int* s_pre, int ne, int ba
 // products are formed into registers, then accumulated as in the chunk
 // accumulator (bitmap of the chunk's columns, word-popcount prefix for the
 // ranks, values summed at their rank) and written sorted.
-template <int TW, int KPT>
+template <int TW, int KPT, bool OCC>
 __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, int64_t nitems) {
     extern __shared__ int64_t lds_r[];
     const int W = 1 << d.logW;
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
     for (int k = 0; k < KPT; ++k) idx[k] = 0xffffffffu;
     int done = 0;
     for (int64_t qb = q0; qb < q1; qb += TW) {
-        const int tot = direct_stage<TW, TW>(d, qb + tt, q1, s, s_pre, s_bo, s_a, red_sh);
+        const int tot = direct_stage<TW, TW, OCC>(d, qb + tt, q1, s, s_pre, s_bo, s_a, red_sh);
         const int ne = (int)min((int64_t)TW, q1 - qb);
         int64_t bi[KPT];
         double av[KPT];
@@ -432,6 +432,7 @@ constexpr int kDirectU = 4;  // products in flight per thread
 // per-wave entry-start counts: 16 words for each of the block's waves
 constexpr int kWinHistWords = (kDirectWinNT / kWave) * (kWave / 4);
 
+template <bool OCC>
 __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, int64_t p0,
                                                                int64_t nitems) {
     constexpr int TW = kDirectWinNT;
@@ -467,7 +468,7 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     constexpr int NWV = TW / kWave;
     for (int64_t qb = q0; qb < q1; qb += kDirectNE) {
         __syncthreads();  // zeroing done / previous round's staging consumed
-        const int tot = direct_stage<TW, kDirectNE>(d, qb + tt, q1, s, s_pre, s_bo, s_a, red_sh);
+        const int tot = direct_stage<TW, kDirectNE, OCC>(d, qb + tt, q1, s, s_pre, s_bo, s_a, red_sh);
         const int ne = (int)min((int64_t)kDirectNE, q1 - qb);
         // each wave takes a contiguous run of 64-product chunks; lane l of a
         // chunk takes product base + l
@@ -607,7 +608,7 @@ template <int TW, int KPT>
 static void launch_direct_rank(const DirectArgs& d, int64_t p0, int64_t n, hipStream_t st) {
     const int64_t W = int64_t(1) << d.logW;
     const size_t lds = (size_t)TW * KPT * 8 + (size_t)(W / 32) * 8;
-    auto kern = k_direct_rank<TW, KPT>;
+    auto kern = d.bocc ? k_direct_rank<TW, KPT, true> : k_direct_rank<TW, KPT, false>;
     SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds));
     hipLaunchKernelGGL(kern, dim3(grid_1d(n)), dim3(TW), lds, st, d, p0, n);
@@ -630,9 +631,10 @@ void direct_accumulate(const DirectArgs& d, int cls, int64_t p0, int64_t n, hipS
         case DC_DENSE: {
             const int64_t W = int64_t(1) << d.logW;
             const size_t lds = direct_window_lds(W);
-            SG_HIP(hipFuncSetAttribute((const void*)k_direct_window,
+            auto kern = d.bocc ? k_direct_window<true> : k_direct_window<false>;
+            SG_HIP(hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-            hipLaunchKernelGGL(k_direct_window, dim3(grid_1d(n)), dim3(kDirectWinNT), lds, st, d,
+            hipLaunchKernelGGL(kern, dim3(grid_1d(n)), dim3(kDirectWinNT), lds, st, d,
                                p0, n);
             SG_LAUNCH_CHECK();
             break;
