@@ -1034,12 +1034,19 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
                         j = jl > j ? jl : j;
                         while (ppre[j + 1] <= pu) ++j;
                         jl = j;
-                        pj = ppre[j];
-                        nj = nbv[j];
-                        bj = bst[j];
+                        // every lane read the same entry: keep it scalar
+                        pj = __builtin_amdgcn_readfirstlane(ppre[j]);
+                        nj = __builtin_amdgcn_readfirstlane(nbv[j]);
+                        const int64_t b = bst[j];
+                        bj = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(
+                                            (int)((uint64_t)b >> 32)) << 32) |
+                                       (uint32_t)__builtin_amdgcn_readfirstlane((int)b));
                     }
+                    // the piece's B row start is uniform: a scalar base and a
+                    // 32-bit lane offset
+                    const int32_t* rowp = bcol + bj;
                     const int off = (pu - pj) * kWave + lane;
-                    if (off < nj) c[uu] = (uint32_t)bcol[bj + off];
+                    if (off < nj) c[uu] = (uint32_t)rowp[(uint32_t)off];
                 }
             }
             j0 = jl;
@@ -1047,12 +1054,13 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
             // its group of gm + 1 words (which never spans two slots), so
             // that the runs of nearby columns of a B row fall into
             // different words and banks; only per-slot counts are read.
+            // (A lane without a product holds c = ~0: its word lies far past
+            // any bitmap that fits LDS, so the bound test drops it.)
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
                 const uint32_t q = c[uu] >> 5, r = c[uu] & 31;
                 const uint32_t wd = ((q & ~gm) | ((q + r) & gm)) - (uint32_t)wlo;
-                if (c[uu] != 0xffffffffu && wd < (uint32_t)nwp)
-                    atomicOr(&bits[wd], 1u << r);
+                if (wd < (uint32_t)nwp) atomicOr(&bits[wd], 1u << r);
             }
         }
         // element counts per slot: the sum of the window's B-row slot vectors
