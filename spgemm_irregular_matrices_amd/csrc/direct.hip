@@ -463,12 +463,14 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     for (int i = tt; i < W; i += TW) acc[i] = 0.0;
     for (int i = tt; i < kWinHistWords; i += TW) hw_all[i] = 0u;
     uint8_t* fb = (uint8_t*)flags;
-    const int wv = tt / kWave, lane = lane_id();
+    // wave index and chunk bounds are uniform per wave: scalar registers
+    const int wv = __builtin_amdgcn_readfirstlane(tt / kWave), lane = lane_id();
     uint32_t* hw = hw_all + wv * (kWave / 4);
     constexpr int NWV = TW / kWave;
     for (int64_t qb = q0; qb < q1; qb += kDirectNE) {
         __syncthreads();  // zeroing done / previous round's staging consumed
-        const int tot = direct_stage<TW, kDirectNE, OCC>(d, qb + tt, q1, s, s_pre, s_bo, s_a, red_sh);
+        const int tot = __builtin_amdgcn_readfirstlane(
+            direct_stage<TW, kDirectNE, OCC>(d, qb + tt, q1, s, s_pre, s_bo, s_a, red_sh));
         const int ne = (int)min((int64_t)kDirectNE, q1 - qb);
         // each wave takes a contiguous run of 64-product chunks; lane l of a
         // chunk takes product base + l
