@@ -970,6 +970,8 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     const int w = __builtin_amdgcn_readfirstlane(tt / kWave), lane = lane_id();
     // words per slot, and the rotation group of the bitmap words
     const uint32_t gm = (uint32_t)min(32, nwords / req) - 1u;
+    // the full staging window means a single column part (wlo = 0)
+    const uint32_t wl = EW == kHsymEW ? 0u : (uint32_t)wlo;
     const HsymGroup g = grp[blockIdx.x];
     // the whole work group leaves together when the grid's bound exceeds the groups
     if (g.h < 0) return;
@@ -1050,16 +1052,16 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
                 }
             }
             j0 = jl;
-            // Column c = 32 q + r sets bit r of word q rotated by r inside
-            // its group of gm + 1 words (which never spans two slots), so
-            // that the runs of nearby columns of a B row fall into
-            // different words and banks; only per-slot counts are read.
+            // Column c = 32 q + r sets bit r of word q ^ (r & gm), a word of
+            // q's aligned group of gm + 1 words (which never spans two
+            // slots), so that the runs of nearby columns of a B row fall
+            // into different words and banks; only per-slot counts are read.
             // (A lane without a product holds c = ~0: its word lies far past
             // any bitmap that fits LDS, so the bound test drops it.)
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
                 const uint32_t q = c[uu] >> 5, r = c[uu] & 31;
-                const uint32_t wd = ((q & ~gm) | ((q + r) & gm)) - (uint32_t)wlo;
+                const uint32_t wd = (q ^ (r & gm)) - wl;
                 if (wd < (uint32_t)nwp) atomicOr(&bits[wd], 1u << r);
             }
         }
