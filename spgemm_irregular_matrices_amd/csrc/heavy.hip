@@ -947,8 +947,9 @@ __global__ void k_hsym_groups(const int64_t* arp, const int32_t* hrows, const in
 // The row's column range may be taken in np parts, one launch each (when the
 // whole bitmap would leave one work group per CU): part p keeps bitmap words
 // [wlo, wlo + nwp) and slots [sl0, sl0 + reqp), reads every product of the
-// row and skips those outside its columns.
-template <int EW>
+// row and skips those outside its columns. B32: B has fewer than 2^31
+// entries, so B row starts are kept in 32 bits.
+template <int EW, bool B32>
 __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     const HsymGroup* grp, const int32_t* acol, const int64_t* brp, const int32_t* bcol, int req,
     int nwords, int wlo, int nwp, int sl0, int reqp, const int32_t* bslot, int64_t* elem_fin,
@@ -956,7 +957,8 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     static_assert(EW <= kHsymNT, "a staged window holds at most one entry per thread");
     extern __shared__ int64_t lds_s[];
     constexpr int NW = kHsymNT / kWave;
-    int64_t* bst = lds_s;                                   // EW B row starts
+    using BT = typename std::conditional<B32, uint32_t, int64_t>::type;
+    BT* bst = (BT*)lds_s;                                   // EW B row starts
     unsigned long long* esl = (unsigned long long*)(bst + EW);  // reqp element counts
     int* nbv = (int*)(esl + reqp);                          // EW B row lengths
     int* kst = nbv + EW;                                    // EW B rows
@@ -989,7 +991,7 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
             int32_t k = acol[ew + tt];
             int64_t b0 = brp[k];
             int nb = (int)(brp[k + 1] - b0);
-            bst[tt] = b0;
+            bst[tt] = (BT)b0;
             nbv[tt] = nb;
             kst[tt] = k;
             pc = (nb + kWave - 1) / kWave;
@@ -1013,7 +1015,7 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
             const int pw = wj + 1 <= ne ? ppre[wj + 1] : INT_MAX;
             const int wp = wj < ne ? ppre[wj] : 0;
             const int wn = wj < ne ? nbv[wj] : 0;
-            const int64_t wb = wj < ne ? bst[wj] : 0;
+            const BT wb = wj < ne ? bst[wj] : (BT)0;
             uint32_t c[U];
             int jl = j0;
 #pragma unroll
@@ -1028,9 +1030,12 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
                         jl = j0 + cnt;
                         pj = __builtin_amdgcn_readlane(wp, cnt);
                         nj = __builtin_amdgcn_readlane(wn, cnt);
-                        bj = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
-                                            (int)((uint64_t)wb >> 32), cnt) << 32) |
-                                       (uint32_t)__builtin_amdgcn_readlane((int)wb, cnt));
+                        if constexpr (B32)
+                            bj = (uint32_t)__builtin_amdgcn_readlane((int)wb, cnt);
+                        else
+                            bj = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                                (int)((uint64_t)wb >> 32), cnt) << 32) |
+                                           (uint32_t)__builtin_amdgcn_readlane((int)wb, cnt));
                     } else {
                         int j = j0 + cnt;
                         j = jl > j ? jl : j;
@@ -1039,10 +1044,13 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
                         // every lane read the same entry: keep it scalar
                         pj = __builtin_amdgcn_readfirstlane(ppre[j]);
                         nj = __builtin_amdgcn_readfirstlane(nbv[j]);
-                        const int64_t b = bst[j];
-                        bj = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(
-                                            (int)((uint64_t)b >> 32)) << 32) |
-                                       (uint32_t)__builtin_amdgcn_readfirstlane((int)b));
+                        const BT b = bst[j];
+                        if constexpr (B32)
+                            bj = (uint32_t)__builtin_amdgcn_readfirstlane((int)b);
+                        else
+                            bj = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(
+                                                (int)((uint64_t)b >> 32)) << 32) |
+                                           (uint32_t)__builtin_amdgcn_readfirstlane((int)b));
                     }
                     // the piece's B row start is uniform: a scalar base and a
                     // 32-bit lane offset
@@ -1146,6 +1154,20 @@ static size_t hsym_lds(int ew, int64_t nwp, int64_t reqp) {
 
 size_t heavy_symbolic_lds(int64_t ppow, int64_t req) { return hsym_lds(kHsymEW, ppow / 32, req); }
 
+template <int EW, bool B32>
+static void launch_hsym(size_t lds, int64_t grid, hipStream_t st, const HsymGroup* grp,
+                        const DevCSR& A, const DevCSR& B, int64_t req, int nwords, int part,
+                        int nwp, int reqp, const int32_t* bslot, int64_t* elem_fin,
+                        int64_t* dist_fin, uint32_t* gbits) {
+    auto kern = k_heavy_symbolic<EW, B32>;
+    SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds));
+    hipLaunchKernelGGL(kern, dim3(grid_1d(grid)), dim3(kHsymNT), lds, st, grp, A.col, B.rp, B.col,
+                       (int)req, nwords, part * nwp, nwp, part * reqp, reqp, bslot, elem_fin,
+                       dist_fin, gbits);
+    SG_LAUNCH_CHECK();
+}
+
 void heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const int32_t* hrows,
                     int64_t H, int64_t Nh, int64_t max_u, int ncu, int64_t dev_lds, int64_t ppow,
                     int64_t wfin, int32_t* bslot, int64_t* elem_fin, int64_t* dist_fin, Arena& ar,
@@ -1218,19 +1240,20 @@ void heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const in
     const int nwp = nwords / np, reqp = (int)req / np;
     for (int part = 0; part < np; ++part) {
         if (ew == kHsymEW) {
-            SG_HIP(hipFuncSetAttribute((const void*)k_heavy_symbolic<kHsymEW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-            hipLaunchKernelGGL(k_heavy_symbolic<kHsymEW>, dim3(grid_1d(grid)), dim3(kHsymNT), lds,
-                               st, grp, A.col, B.rp, B.col, (int)req, nwords, part * nwp, nwp,
-                               part * reqp, reqp, bslot, elem_fin, dist_fin, gbits);
+            if (B.nnz < (int64_t(1) << 31))
+                launch_hsym<kHsymEW, true>(lds, grid, st, grp, A, B, req, nwords, part, nwp, reqp,
+                                           bslot, elem_fin, dist_fin, gbits);
+            else
+                launch_hsym<kHsymEW, false>(lds, grid, st, grp, A, B, req, nwords, part, nwp, reqp,
+                                            bslot, elem_fin, dist_fin, gbits);
         } else {
-            SG_HIP(hipFuncSetAttribute((const void*)k_heavy_symbolic<kHsymEW / 2>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-            hipLaunchKernelGGL(k_heavy_symbolic<kHsymEW / 2>, dim3(grid_1d(grid)), dim3(kHsymNT),
-                               lds, st, grp, A.col, B.rp, B.col, (int)req, nwords, part * nwp,
-                               nwp, part * reqp, reqp, bslot, elem_fin, dist_fin, gbits);
+            if (B.nnz < (int64_t(1) << 31))
+                launch_hsym<kHsymEW / 2, true>(lds, grid, st, grp, A, B, req, nwords, part, nwp,
+                                               reqp, bslot, elem_fin, dist_fin, gbits);
+            else
+                launch_hsym<kHsymEW / 2, false>(lds, grid, st, grp, A, B, req, nwords, part, nwp,
+                                                reqp, bslot, elem_fin, dist_fin, gbits);
         }
-        SG_LAUNCH_CHECK();
     }
     if (off && nsplit_max > 0) {
         hipLaunchKernelGGL(k_hsym_finalize, dim3(grid_1d(nsplit_max)), dim3(kHsymNT),
