@@ -339,8 +339,7 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
     // the output offset is read now, beside the item's entries, rather
     // than after the accumulation
     const int64_t off = d.off[x];
-    const int64_t h = x / d.req;
-    const int s = (int)(x - h * d.req);
+    const int s = (int)((uint32_t)x & (uint32_t)(d.req - 1));  // req is a power of two
     for (int wd = tt; wd < NWD; wd += TW) bits[wd] = 0u;
 
     uint32_t idx[KPT];
@@ -457,8 +456,7 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     const int64_t q0 = d.iq0[p0 + item];
     const int64_t q1 = q0 + d.ine[p0 + item];
     const int64_t off = d.off[x];
-    const int64_t h = x / d.req;
-    const int s = (int)(x - h * d.req);
+    const int s = (int)((uint32_t)x & (uint32_t)(d.req - 1));  // req is a power of two
     for (int i = tt; i < NWD * 8; i += TW) flags[i] = 0u;
     for (int i = tt; i < W; i += TW) acc[i] = 0.0;
     for (int i = tt; i < kWinHistWords; i += TW) hw_all[i] = 0u;
