@@ -1102,15 +1102,22 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     }
     // distinct columns per finest slot: popcounts of the slot's words
     const int wps = nwp / reqp;  // words per slot (>= 1)
-    for (int i = tt; i < nwp; i += kHsymNT) {
-        int pc = __popc(bits[i]);
-        const int sl = i / wps;
-        // a wave's 64 words lie in one slot when slots hold >= 64 words
-        if (wps >= kWave) {
-            pc = wave_reduce_sum(pc);
-            if (lane == 0 && pc) atomicAdd(&dsl[sl], pc);
-        } else if (pc) {
-            atomicAdd(&dsl[sl], pc);
+    if (wps >= 8) {
+        // eight consecutive words per thread (all in one slot), summed over
+        // the lps lanes that share the slot (the active lanes of a wave are
+        // a prefix of whole slots: nwp and wps are powers of two)
+        const int lps = min(wps / 8, kWave);
+        for (int i0 = tt * 8; i0 < nwp; i0 += kHsymNT * 8) {
+            int pc = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pc += __popc(bits[i0 + j]);
+            for (int dd = 1; dd < lps; dd <<= 1) pc += __shfl_xor(pc, dd, kWave);
+            if ((lane & (lps - 1)) == 0 && pc) atomicAdd(&dsl[i0 / wps], pc);
+        }
+    } else {
+        for (int i = tt; i < nwp; i += kHsymNT) {
+            const int pc = __popc(bits[i]);
+            if (pc) atomicAdd(&dsl[i / wps], pc);
         }
     }
     __syncthreads();
