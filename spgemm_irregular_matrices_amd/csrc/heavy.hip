@@ -955,16 +955,16 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     int nwords, int wlo, int nwp, int sl0, int reqp, const int32_t* bslot, int64_t* elem_fin,
     int64_t* dist_fin, uint32_t* gbits) {
     static_assert(EW <= kHsymNT, "a staged window holds at most one entry per thread");
-    extern __shared__ int64_t lds_s[];
+    extern __shared__ __align__(16) int64_t lds_s[];
     constexpr int NW = kHsymNT / kWave;
     using BT = typename std::conditional<B32, uint32_t, int64_t>::type;
-    BT* bst = (BT*)lds_s;                                   // EW B row starts
+    uint32_t* bits = (uint32_t*)lds_s;                      // nwp, padded to 4 words
+    BT* bst = (BT*)(bits + ((nwp + 3) & ~3));               // EW B row starts
     unsigned long long* esl = (unsigned long long*)(bst + EW);  // reqp element counts
     int* nbv = (int*)(esl + reqp);                          // EW B row lengths
     int* kst = nbv + EW;                                    // EW B rows
     int* ppre = kst + EW;                                   // EW + 1 piece prefix
     int* dsl = ppre + EW + 1;                               // reqp distinct counts
-    uint32_t* bits = (uint32_t*)(dsl + reqp);               // nwp
     __shared__ int scan_sh[NW + 1];
     const int tt = threadIdx.x;
     // the wave index and the loop bounds below are uniform per wave: kept in
@@ -978,7 +978,8 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     // the whole work group leaves together when the grid's bound exceeds the groups
     if (g.h < 0) return;
     const int64_t h = g.h, a0 = g.a0, a1 = g.a1;
-    for (int i = tt; i < nwp; i += kHsymNT) bits[i] = 0u;
+    // the bitmap starts the 16-byte aligned LDS block: cleared 4 words a store
+    for (int i = tt * 4; i < nwp; i += kHsymNT * 4) *(uint4*)&bits[i] = make_uint4(0, 0, 0, 0);
     for (int i = tt; i < reqp; i += kHsymNT) {
         dsl[i] = 0;
         esl[i] = 0ull;
@@ -1108,9 +1109,10 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
         // a prefix of whole slots: nwp and wps are powers of two)
         const int lps = min(wps / 8, kWave);
         for (int i0 = tt * 8; i0 < nwp; i0 += kHsymNT * 8) {
-            int pc = 0;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) pc += __popc(bits[i0 + j]);
+            const uint4 wa = *(const uint4*)&bits[i0];
+            const uint4 wb = *(const uint4*)&bits[i0 + 4];
+            int pc = __popc(wa.x) + __popc(wa.y) + __popc(wa.z) + __popc(wa.w) + __popc(wb.x) +
+                     __popc(wb.y) + __popc(wb.z) + __popc(wb.w);
             for (int dd = 1; dd < lps; dd <<= 1) pc += __shfl_xor(pc, dd, kWave);
             if ((lane & (lps - 1)) == 0 && pc) atomicAdd(&dsl[i0 / wps], pc);
         }
@@ -1156,7 +1158,7 @@ __global__ __launch_bounds__(kHsymNT) void k_hsym_finalize(const int64_t* off, i
 
 static size_t hsym_lds(int ew, int64_t nwp, int64_t reqp) {
     return (size_t)ew * 8 + (size_t)reqp * 8 + (size_t)ew * 4 * 2 + (size_t)(ew + 1) * 4 +
-           (size_t)reqp * 4 + (size_t)nwp * 4;
+           (size_t)reqp * 4 + (size_t)((nwp + 3) & ~int64_t(3)) * 4;
 }
 
 size_t heavy_symbolic_lds(int64_t ppow, int64_t req) { return hsym_lds(kHsymEW, ppow / 32, req); }
