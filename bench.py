@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--tau", type=int, default=0)
     ap.add_argument("--width", type=int, default=0)
     ap.add_argument("--cap", type=int, default=0)
+    ap.add_argument("--numeric-mode", type=int, default=0, choices=(0, 1, 2, 3),
+                    help="heavy numeric dataflow of the timed steps: 0 the library's choice "
+                         "(direct), 1 fused first level, 2 separate C-hat (the page's), 3 direct")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -230,7 +233,7 @@ def main():
     torch.cuda.synchronize()
 
     plan = binding.Plan(timing=True, tau_override=args.tau, chunk_width_override=args.width,
-                        nchunks_cap=args.cap)
+                        nchunks_cap=args.cap, numeric_mode=args.numeric_mode)
 
     def step():
         rp, nnz = plan.symbolic(dA, dB)
@@ -319,6 +322,10 @@ def main():
                        "frac": (heavy_bytes / (heavy_ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if heavy_ms else 0},
         "phase_ms_per_step": {f"{k[0]}:{k[1]}": v["ms"] / args.steps for k, v in per_phase.items()
                               if v["launches"]},
+        # algorithmic bytes of a phase over its measured time (phases that count bytes)
+        "phase_algorithmic_GBps": {f"{k[0]}:{k[1]}": v["bytes"] / (v["ms"] * 1e-3) / 1e9
+                                   for k, v in per_phase.items()
+                                   if v["launches"] and v["bytes"] > 0 and v["ms"] > 0},
         "step_ms_min_max": [min(step_ms), max(step_ms)],
         "cpu_baseline": cpu,
         "paths": paths,
