@@ -269,6 +269,40 @@ __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int6
     return tot;
 }
 
+// The first staging round of an item, loaded into registers so that two
+// items' loads can be in flight together: this thread's entry q (a valid
+// index of the item's row; `valid` is false past the row's entries, whose
+// slice then counts as empty).
+template <bool OCC>
+__device__ __forceinline__ void stage_load(const DirectArgs& d, int64_t q, bool valid, int s,
+                                           double& a, int64_t& lo, int& len) {
+    const int32_t k = d.Acol[q];
+    a = d.Aval[q];
+    lo = 0;
+    len = 0;
+    if (!OCC || (d.bocc[(int64_t)s * d.nbw + (k >> 5)] >> (k & 31)) & 1u) {
+        const int64_t* sp = d.spos + (int64_t)s * d.nb + k;
+        lo = sp[0];
+        len = (int)(sp[1] - lo);
+    }
+    if (!valid) len = 0;
+}
+
+// Puts a round loaded by stage_load into LDS as direct_stage does (one entry
+// per thread of the team); returns the round's products.
+template <int TW>
+__device__ __forceinline__ int stage_commit(double a, int64_t lo, int len, int* s_pre,
+                                            int64_t* s_bo, double* s_a, int* red_sh) {
+    const int tt = threadIdx.x;
+    s_bo[tt] = lo;
+    s_a[tt] = a;
+    int tot;
+    const int pre = team_exclusive_scan<TW>(len, red_sh, &tot);
+    s_pre[tt] = pre;
+    __syncthreads();
+    return tot;
+}
+
 // Entry of product p of a round: the last staged entry whose prefix is <= p,
 // searched from `j` up (products are visited in increasing order per thread).
 __device__ __forceinline__ int direct_find(const int* s_pre, int ne, int p, int j) {
@@ -314,31 +348,19 @@ __device__ __forceinline__ int chunk_entry_fast(const int* s_pre, int ne, int ba
     return jc + wave_inclusive_scan_i32(cnt);
 }
 
-// Bitmap-rank accumulation of items with at most TW*KPT products: the
+// Bitmap-rank accumulation of one item with at most TW*KPT products: the
 // products are formed into registers, then accumulated as in the chunk
 // accumulator (bitmap of the chunk's columns, word-popcount prefix for the
-// ranks, values summed at their rank) and written sorted.
+// ranks, values summed at their rank) and written sorted. The first staging
+// round arrives in registers (a0, lo0, len0: this thread's entry q0 + tt).
 template <int TW, int KPT, bool OCC>
-__global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, int64_t nitems) {
-    extern __shared__ int64_t lds_r[];
+__device__ __forceinline__ void rank_item(const DirectArgs& d, int32_t x, int64_t q0, int64_t q1,
+                                          int64_t off, double a0, int64_t lo0, int len0,
+                                          double* vals, uint32_t* bits, int* wpre, int* s_pre,
+                                          int64_t* s_bo, double* s_a, int* red_sh) {
     const int W = 1 << d.logW;
     const int NWD = W >> 5;
-    double* vals = (double*)lds_r;                  // TW*KPT
-    uint32_t* bits = (uint32_t*)(vals + TW * KPT);  // NWD
-    int* wpre = (int*)(bits + NWD);                 // NWD
-    __shared__ int s_pre[TW];
-    __shared__ int64_t s_bo[TW];
-    __shared__ double s_a[TW];
-    __shared__ int red_sh[TW / kWave + 1];
     const int tt = threadIdx.x;
-    const int64_t item = blockIdx.x;
-    if (item >= nitems) return;
-    const int32_t x = d.items[p0 + item];
-    const int64_t q0 = d.iq0[p0 + item];
-    const int64_t q1 = q0 + d.ine[p0 + item];
-    // the output offset is read now, beside the item's entries, rather
-    // than after the accumulation
-    const int64_t off = d.off[x];
     const int s = (int)((uint32_t)x & (uint32_t)(d.req - 1));  // req is a power of two
     for (int wd = tt; wd < NWD; wd += TW) bits[wd] = 0u;
 
@@ -348,7 +370,9 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
     for (int k = 0; k < KPT; ++k) idx[k] = 0xffffffffu;
     int done = 0;
     for (int64_t qb = q0; qb < q1; qb += TW) {
-        const int tot = direct_stage<TW, TW, OCC>(d, qb + tt, q1, s, s_pre, s_bo, s_a, red_sh);
+        const int tot = qb == q0
+                            ? stage_commit<TW>(a0, lo0, len0, s_pre, s_bo, s_a, red_sh)
+                            : direct_stage<TW, TW, OCC>(d, qb + tt, q1, s, s_pre, s_bo, s_a, red_sh);
         const int ne = (int)min((int64_t)TW, q1 - qb);
         int64_t bi[KPT];
         double av[KPT];
@@ -416,6 +440,66 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
         d.Ccol[off + r] = lo + scol[r];
         d.Cval[off + r] = vals[r];
     }
+}
+
+// Two consecutive items of a class per work group, one after the other:
+// both items' headers, first-round A entries and slice bounds are loaded
+// together before the first item is accumulated, so the second item's
+// dependent-load chain is mostly paid while the first one runs.
+constexpr int kRankItemsPerGroup = 2;
+template <int TW, int KPT, bool OCC>
+__global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, int64_t nitems) {
+    extern __shared__ int64_t lds_r[];
+    const int W = 1 << d.logW;
+    double* vals = (double*)lds_r;                  // TW*KPT
+    uint32_t* bits = (uint32_t*)(vals + TW * KPT);  // W/32
+    int* wpre = (int*)(bits + (W >> 5));            // W/32
+    __shared__ int s_pre[TW];
+    __shared__ int64_t s_bo[TW];
+    __shared__ double s_a[TW];
+    __shared__ int red_sh[TW / kWave + 1];
+    const int tt = threadIdx.x;
+    const int64_t iA = (int64_t)blockIdx.x * kRankItemsPerGroup;
+    if (iA >= nitems) return;
+    const bool hasB = iA + 1 < nitems;  // uniform over the group
+    const int64_t iB = hasB ? iA + 1 : iA;
+    const int32_t xA = d.items[p0 + iA], xB = d.items[p0 + iB];
+    const int64_t q0A = d.iq0[p0 + iA], q0B = d.iq0[p0 + iB];
+    const int64_t neA = d.ine[p0 + iA], neB = d.ine[p0 + iB];
+    // the output offsets are read now, beside the items' entries, rather
+    // than after the accumulation
+    const int64_t offA = d.off[xA], offB = d.off[xB];
+    const int sA = (int)((uint32_t)xA & (uint32_t)(d.req - 1));
+    const int sB = (int)((uint32_t)xB & (uint32_t)(d.req - 1));
+    // A rank item has products, so its row has at least one entry; the
+    // index is clamped into the row so that every thread's loads stay in
+    // bounds. All loads of both items are issued before any is used.
+    double aA, aB;
+    int64_t loA, loB;
+    int lenA, lenB;
+    const int64_t qA = q0A + min((int64_t)tt, neA - 1), qB = q0B + min((int64_t)tt, neB - 1);
+    if constexpr (!OCC) {
+        const int32_t kA = d.Acol[qA], kB = d.Acol[qB];
+        aA = d.Aval[qA];
+        aB = d.Aval[qB];
+        const int64_t* spA = d.spos + (int64_t)sA * d.nb + kA;
+        const int64_t* spB = d.spos + (int64_t)sB * d.nb + kB;
+        loA = spA[0];
+        const int64_t hiA = spA[1];
+        loB = spB[0];
+        const int64_t hiB = spB[1];
+        lenA = tt < neA ? (int)(hiA - loA) : 0;
+        lenB = tt < neB ? (int)(hiB - loB) : 0;
+    } else {
+        stage_load<OCC>(d, qA, tt < neA, sA, aA, loA, lenA);
+        stage_load<OCC>(d, qB, tt < neB, sB, aB, loB, lenB);
+    }
+    rank_item<TW, KPT, OCC>(d, xA, q0A, q0A + neA, offA, aA, loA, lenA, vals, bits, wpre, s_pre,
+                            s_bo, s_a, red_sh);
+    if (!hasB) return;
+    __syncthreads();  // the first item's output has read the staging area and bitmap
+    rank_item<TW, KPT, OCC>(d, xB, q0B, q0B + neB, offB, aB, loB, lenB, vals, bits, wpre, s_pre,
+                            s_bo, s_a, red_sh);
 }
 
 // Dense window accumulation of the large items: the item's entries are
@@ -611,7 +695,8 @@ static void launch_direct_rank(const DirectArgs& d, int64_t p0, int64_t n, hipSt
     auto kern = d.bocc ? k_direct_rank<TW, KPT, true> : k_direct_rank<TW, KPT, false>;
     SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds));
-    hipLaunchKernelGGL(kern, dim3(grid_1d(n)), dim3(TW), lds, st, d, p0, n);
+    hipLaunchKernelGGL(kern, dim3(grid_1d((n + kRankItemsPerGroup - 1) / kRankItemsPerGroup)),
+                       dim3(TW), lds, st, d, p0, n);
     SG_LAUNCH_CHECK();
 }
 
