@@ -442,12 +442,11 @@ __device__ __forceinline__ void rank_item(const DirectArgs& d, int32_t x, int64_
     }
 }
 
-// Two consecutive items of a class per work group, one after the other:
-// both items' headers, first-round A entries and slice bounds are loaded
-// together before the first item is accumulated, so the second item's
-// dependent-load chain is mostly paid while the first one runs.
-constexpr int kRankItemsPerGroup = 2;
-template <int TW, int KPT, bool OCC>
+// IPG consecutive items of a class per work group, one after the other: all
+// their headers, first-round A entries and slice bounds are loaded together
+// before the first item is accumulated, so the later items' dependent-load
+// chains are mostly paid while the first one runs.
+template <int TW, int KPT, bool OCC, int IPG>
 __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, int64_t nitems) {
     extern __shared__ int64_t lds_r[];
     const int W = 1 << d.logW;
@@ -459,47 +458,63 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
     __shared__ double s_a[TW];
     __shared__ int red_sh[TW / kWave + 1];
     const int tt = threadIdx.x;
-    const int64_t iA = (int64_t)blockIdx.x * kRankItemsPerGroup;
-    if (iA >= nitems) return;
-    const bool hasB = iA + 1 < nitems;  // uniform over the group
-    const int64_t iB = hasB ? iA + 1 : iA;
-    const int32_t xA = d.items[p0 + iA], xB = d.items[p0 + iB];
-    const int64_t q0A = d.iq0[p0 + iA], q0B = d.iq0[p0 + iB];
-    const int64_t neA = d.ine[p0 + iA], neB = d.ine[p0 + iB];
+    const int64_t i0 = (int64_t)blockIdx.x * IPG;
+    if (i0 >= nitems) return;
+    const int nown = (int)min((int64_t)IPG, nitems - i0);  // uniform over the group
+    int32_t x[IPG];
+    int64_t q0[IPG], ne[IPG], off[IPG];
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) {
+        const int64_t i = p0 + i0 + min(u, nown - 1);
+        x[u] = d.items[i];
+        q0[u] = d.iq0[i];
+        ne[u] = d.ine[i];
+    }
     // the output offsets are read now, beside the items' entries, rather
     // than after the accumulation
-    const int64_t offA = d.off[xA], offB = d.off[xB];
-    const int sA = (int)((uint32_t)xA & (uint32_t)(d.req - 1));
-    const int sB = (int)((uint32_t)xB & (uint32_t)(d.req - 1));
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) off[u] = d.off[x[u]];
     // A rank item has products, so its row has at least one entry; the
     // index is clamped into the row so that every thread's loads stay in
-    // bounds. All loads of both items are issued before any is used.
-    double aA, aB;
-    int64_t loA, loB;
-    int lenA, lenB;
-    const int64_t qA = q0A + min((int64_t)tt, neA - 1), qB = q0B + min((int64_t)tt, neB - 1);
+    // bounds. All loads of the items are issued before any is used.
+    double a[IPG];
+    int64_t lo[IPG];
+    int len[IPG];
     if constexpr (!OCC) {
-        const int32_t kA = d.Acol[qA], kB = d.Acol[qB];
-        aA = d.Aval[qA];
-        aB = d.Aval[qB];
-        const int64_t* spA = d.spos + (int64_t)sA * d.nb + kA;
-        const int64_t* spB = d.spos + (int64_t)sB * d.nb + kB;
-        loA = spA[0];
-        const int64_t hiA = spA[1];
-        loB = spB[0];
-        const int64_t hiB = spB[1];
-        lenA = tt < neA ? (int)(hiA - loA) : 0;
-        lenB = tt < neB ? (int)(hiB - loB) : 0;
+        int32_t k[IPG];
+#pragma unroll
+        for (int u = 0; u < IPG; ++u) {
+            const int64_t q = q0[u] + min((int64_t)tt, ne[u] - 1);
+            k[u] = d.Acol[q];
+            a[u] = d.Aval[q];
+        }
+        int64_t hi[IPG];
+#pragma unroll
+        for (int u = 0; u < IPG; ++u) {
+            const int s = (int)((uint32_t)x[u] & (uint32_t)(d.req - 1));
+            const int64_t* sp = d.spos + (int64_t)s * d.nb + k[u];
+            lo[u] = sp[0];
+            hi[u] = sp[1];
+        }
+#pragma unroll
+        for (int u = 0; u < IPG; ++u) len[u] = tt < ne[u] ? (int)(hi[u] - lo[u]) : 0;
     } else {
-        stage_load<OCC>(d, qA, tt < neA, sA, aA, loA, lenA);
-        stage_load<OCC>(d, qB, tt < neB, sB, aB, loB, lenB);
+#pragma unroll
+        for (int u = 0; u < IPG; ++u) {
+            const int s = (int)((uint32_t)x[u] & (uint32_t)(d.req - 1));
+            stage_load<OCC>(d, q0[u] + min((int64_t)tt, ne[u] - 1), tt < ne[u], s, a[u], lo[u],
+                            len[u]);
+        }
     }
-    rank_item<TW, KPT, OCC>(d, xA, q0A, q0A + neA, offA, aA, loA, lenA, vals, bits, wpre, s_pre,
-                            s_bo, s_a, red_sh);
-    if (!hasB) return;
-    __syncthreads();  // the first item's output has read the staging area and bitmap
-    rank_item<TW, KPT, OCC>(d, xB, q0B, q0B + neB, offB, aB, loB, lenB, vals, bits, wpre, s_pre,
-                            s_bo, s_a, red_sh);
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) {
+        if (u < nown) {
+            // the previous item's output has read the staging area and bitmap
+            if (u > 0) __syncthreads();
+            rank_item<TW, KPT, OCC>(d, x[u], q0[u], q0[u] + ne[u], off[u], a[u], lo[u], len[u],
+                                    vals, bits, wpre, s_pre, s_bo, s_a, red_sh);
+        }
+    }
 }
 
 // Dense window accumulation of the large items: the item's entries are
@@ -688,15 +703,18 @@ void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
     SG_LAUNCH_CHECK();
 }
 
-template <int TW, int KPT>
+// items per work group of the rank classes: 4 where a thread forms one or
+// two products, 2 where it forms four (their registers allow no more)
+constexpr int RANK_IPG_S = 4, RANK_IPG_L = 2;
+
+template <int TW, int KPT, int IPG>
 static void launch_direct_rank(const DirectArgs& d, int64_t p0, int64_t n, hipStream_t st) {
     const int64_t W = int64_t(1) << d.logW;
     const size_t lds = (size_t)TW * KPT * 8 + (size_t)(W / 32) * 8;
-    auto kern = d.bocc ? k_direct_rank<TW, KPT, true> : k_direct_rank<TW, KPT, false>;
+    auto kern = d.bocc ? k_direct_rank<TW, KPT, true, IPG> : k_direct_rank<TW, KPT, false, IPG>;
     SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds));
-    hipLaunchKernelGGL(kern, dim3(grid_1d((n + kRankItemsPerGroup - 1) / kRankItemsPerGroup)),
-                       dim3(TW), lds, st, d, p0, n);
+    hipLaunchKernelGGL(kern, dim3(grid_1d((n + IPG - 1) / IPG)), dim3(TW), lds, st, d, p0, n);
     SG_LAUNCH_CHECK();
 }
 
@@ -724,12 +742,12 @@ void direct_accumulate(const DirectArgs& d, int cls, int64_t p0, int64_t n, hipS
             SG_LAUNCH_CHECK();
             break;
         }
-        case DC_RANK0 + 0: launch_direct_rank<64, 1>(d, p0, n, st); break;
-        case DC_RANK0 + 1: launch_direct_rank<64, 2>(d, p0, n, st); break;
-        case DC_RANK0 + 2: launch_direct_rank<64, 4>(d, p0, n, st); break;
-        case DC_RANK0 + 3: launch_direct_rank<128, 4>(d, p0, n, st); break;
-        case DC_RANK0 + 4: launch_direct_rank<256, 4>(d, p0, n, st); break;
-        case DC_RANK0 + 5: launch_direct_rank<512, 4>(d, p0, n, st); break;
+        case DC_RANK0 + 0: launch_direct_rank<64, 1, RANK_IPG_S>(d, p0, n, st); break;
+        case DC_RANK0 + 1: launch_direct_rank<64, 2, RANK_IPG_S>(d, p0, n, st); break;
+        case DC_RANK0 + 2: launch_direct_rank<64, 4, RANK_IPG_L>(d, p0, n, st); break;
+        case DC_RANK0 + 3: launch_direct_rank<128, 4, RANK_IPG_L>(d, p0, n, st); break;
+        case DC_RANK0 + 4: launch_direct_rank<256, 4, RANK_IPG_L>(d, p0, n, st); break;
+        case DC_RANK0 + 5: launch_direct_rank<512, 4, RANK_IPG_L>(d, p0, n, st); break;
         default: throw std::logic_error("not a direct item class");
     }
 }
