@@ -534,7 +534,7 @@ template <bool OCC>
 __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, int64_t p0,
                                                                int64_t nitems) {
     constexpr int TW = kDirectWinNT;
-    extern __shared__ int64_t lds_w[];
+    extern __shared__ __align__(16) int64_t lds_w[];
     const int W = 1 << d.logW;
     const int NWD = W >> 5;
     double* acc = (double*)lds_w;                    // W
@@ -556,8 +556,10 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     const int64_t q1 = q0 + d.ine[p0 + item];
     const int64_t off = d.off[x];
     const int s = (int)((uint32_t)x & (uint32_t)(d.req - 1));  // req is a power of two
-    for (int i = tt; i < NWD * 8; i += TW) flags[i] = 0u;
-    for (int i = tt; i < W; i += TW) acc[i] = 0.0;
+    // 16 bytes a store: W is a power of two of at least 32
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tt; i < NWD * 2; i += TW) ((uint4*)flags)[i] = z4;
+    for (int i = tt; i < W / 2; i += TW) ((uint4*)acc)[i] = z4;
     for (int i = tt; i < kWinHistWords; i += TW) hw_all[i] = 0u;
     uint8_t* fb = (uint8_t*)flags;
     // wave index and chunk bounds are uniform per wave: scalar registers

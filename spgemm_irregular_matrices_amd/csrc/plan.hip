@@ -724,9 +724,11 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
                                 B.n * req <= (int64_t(1) << 28);
         p->fused_sym = p->opt.symbolic_mode == 1 || (p->opt.symbolic_mode == 0 && fused_fits);
         // the direct path needs the fused pass's per-slot counts, 16-bit
-        // columns inside a slot and a dense window of one slot in LDS
+        // columns inside a slot and a dense window of one slot in LDS (of
+        // at least one 32-bit bitmap word)
         const int64_t wfin_d = q.nlevels == 0 ? q.ppow : q.final_width;
-        const bool direct_ok = p->fused_sym && wfin_d <= 65536 && req <= kDirectMaxSlots &&
+        const bool direct_ok = p->fused_sym && wfin_d >= 32 && wfin_d <= 65536 &&
+                               req <= kDirectMaxSlots &&
                                direct_window_lds(wfin_d) + 8192 <= (size_t)p->dev_lds &&
                                p->H * req < (int64_t(1) << 31);
         p->direct = direct_ok && (p->opt.numeric_mode == 3 ||
