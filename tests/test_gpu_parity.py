@@ -186,6 +186,33 @@ def test_direct_item_class_bounds():
     compare(A, B, rp, col, val)
 
 
+@pytest.mark.parametrize("counts", [(5, 3, 1, 2, 3, 7), (1, 1, 1, 1, 1, 1), (4, 6, 2, 8, 6, 3)])
+def test_rank_classes_with_partial_groups(counts):
+    """A work group of a rank class takes several consecutive items (four in
+    the two smallest classes, two in the others), so a class whose item count
+    is not a multiple of that ends in a partly filled group. counts[c] heavy
+    rows each hold one item of class c: a single B row of L distinct columns
+    inside one slot (L = 40, 100, 200, 400, 900, 1800, one per class)."""
+    W, req = 8192, 8
+    sizes = (40, 100, 200, 400, 900, 1800)
+    rng = np.random.default_rng(101)
+    brows, arows = [], []
+    for L, n in zip(sizes, counts):
+        for _ in range(n):
+            j = len(brows)
+            brows.append(sorted(((j % req) * W + rng.choice(W, size=L, replace=False)).tolist()))
+            arows.append([j])
+    nb = len(brows)
+    A0 = synth.from_rows(len(arows), nb, arows)
+    B0 = synth.from_rows(nb, W * req, brows)
+    A = synth.CSR(A0.nrows, nb, A0.rowptr, A0.col, synth.uniform_values(102, A0.nnz))
+    B = synth.CSR(nb, W * req, B0.rowptr, B0.col, synth.uniform_values(103, B0.nnz))
+    rp, col, val, st = run_gpu(A, B, tau_override=16)
+    assert st["numeric_path"] == 3 and st["final_chunk_width"] == W, st
+    assert st["heavy_rows"] == A.nrows
+    compare(A, B, rp, col, val)
+
+
 def test_short_b_rows_over_many_slots():
     """B rows of 4 entries over 2^18 columns (32 slots): most (B row, slot)
     slices of a heavy row's items are empty, so the items test the slices'
