@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--tau", type=int, default=0)
     ap.add_argument("--width", type=int, default=0)
     ap.add_argument("--cap", type=int, default=0)
+    ap.add_argument("--max-batch-products", type=int, default=0,
+                    help="heavy products per row batch of the C-hat dataflows (0: one batch)")
     ap.add_argument("--numeric-mode", type=int, default=0, choices=(0, 1, 2, 3),
                     help="heavy numeric dataflow of the timed steps: 0 the library's choice "
                          "(direct), 1 fused first level, 2 separate C-hat (the page's), 3 direct")
@@ -233,7 +235,8 @@ def main():
     torch.cuda.synchronize()
 
     plan = binding.Plan(timing=True, tau_override=args.tau, chunk_width_override=args.width,
-                        nchunks_cap=args.cap, numeric_mode=args.numeric_mode)
+                        nchunks_cap=args.cap, numeric_mode=args.numeric_mode,
+                        max_batch_products=args.max_batch_products)
 
     def step():
         rp, nnz = plan.symbolic(dA, dB)
@@ -313,6 +316,7 @@ def main():
                    "nnz_C": st["nnz_c"], "heavy_rows": st["heavy_rows"],
                    "heavy_products": st["heavy_products"], "tau": st["tau"],
                    "vchunks": st["vchunks"], "final_chunk_width": st["final_chunk_width"],
+                   "row_batches": st["nbatches"],
                    "numeric_path": {0: "none", 1: "fused first level", 2: "separate C-hat",
                                     3: "direct"}[st["numeric_path"]]},
         "gflops": 2.0 * value / 1e9,
