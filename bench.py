@@ -1,4 +1,6 @@
-"""Benchmark: C = A*A for R-MAT scale 18, edge factor 16 (262,144 x 262,144).
+"""Benchmark: C = A*A for R-MAT scale 18, edge factor 16 (262,144 x 262,144),
+with R-MAT scale 20, edge factor 8 (1,048,576 x 1,048,576) as a second full
+record in the same line.
 
 One step is the whole hot path: spgemm_symbolic + spgemm_numeric (setup,
 InterOffsets, binning, the heavy rows' chunk counts and split, light rows,
@@ -9,13 +11,15 @@ Prints one JSON line.
 
 paths = the same product with the page's own numeric dataflows (outer
         product into C-hat then multisplit; the first multisplit level
-        formed in its tiles), a few steps each, for context
+        formed in its tiles), a few steps each, with each phase's
+        algorithmic GB/s and fraction of the HBM peak
 
 value  = intermediate products per second (sum of u(i) over all rows / step time)
 roofline = the dominant kernel's algorithmic bytes per launch / its mean
            launch time (HIP events recorded by the library on the stream the
            kernel runs on), against MI355X's 8 TB/s HBM peak
-cpu_baseline = the CPU oracle on a bounded row sample of the same product
+cpu_baseline = the CPU oracle on a bounded row sample of the same product,
+           plus one-thread oracle rates on the two small workloads
 """
 from __future__ import annotations
 
@@ -39,6 +43,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="rmat18_ef16")
+    ap.add_argument("--also", default="rmat20_ef8",
+                    help="comma-separated workloads timed after the headline one, each a full "
+                         "record under 'workloads' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paths", action="store_true",
                     help="skip timing the other numeric paths (separate C-hat, fused first level)")
@@ -156,11 +163,38 @@ def measured_traffic(workload: str, phase: str):
     return total if found else None
 
 
-def time_numeric_path(dA, dB, numeric_mode: int, steps: int) -> dict:
-    """Mean step time of the same product with another heavy numeric path (context)."""
+def _phase_fracs(per_phase: dict, steps: int) -> dict:
+    """ms per step, algorithmic GB/s and fraction of the HBM peak of every timed phase."""
+    out = {}
+    for k, v in per_phase.items():
+        if not v["launches"]:
+            continue
+        rec = {"ms_per_step": v["ms"] / steps}
+        if v["bytes"] > 0 and v["ms"] > 0:
+            gbps = v["bytes"] / (v["ms"] * 1e-3) / 1e9
+            rec["algorithmic_GBps"] = gbps
+            rec["frac"] = gbps / HBM_PEAK_GBS
+        out[f"{k[0]}:{k[1]}"] = rec
+    return out
+
+
+def _accumulate(per_phase: dict, st: dict):
+    for pn in ("symbolic", "numeric"):
+        for ph, rec in st[pn].items():
+            d = per_phase.setdefault((pn, ph), {"ms": 0.0, "launches": 0, "bytes": 0.0})
+            d["ms"] += rec["ms"]
+            d["launches"] += rec["launches"]
+            d["bytes"] += rec["bytes"]
+
+
+def time_numeric_path(dA, dB, numeric_mode: int, steps: int, max_batch_products: int = 0) -> dict:
+    """Mean step time of the same product with another heavy numeric path, and
+    each phase's algorithmic GB/s (the page's kernels: outer product,
+    histogram, multisplit, accumulation)."""
     import torch
     from spgemm_irregular_matrices_amd import binding
-    with binding.Plan(timing=True, numeric_mode=numeric_mode) as plan:
+    with binding.Plan(timing=True, numeric_mode=numeric_mode,
+                      max_batch_products=max_batch_products) as plan:
         def step():
             rp, nnz = plan.symbolic(dA, dB)
             col = torch.empty(nnz, dtype=torch.int32, device="cuda")
@@ -169,21 +203,35 @@ def time_numeric_path(dA, dB, numeric_mode: int, steps: int) -> dict:
         step()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        phases = {}
+        per_phase = {}
         for _ in range(steps):
             step()
             st = plan.stats()
-            for pn in ("symbolic", "numeric"):
-                for ph, rec in st[pn].items():
-                    if rec["launches"]:
-                        key = f"{pn}:{ph}"
-                        phases[key] = phases.get(key, 0.0) + rec["ms"] / steps
+            _accumulate(per_phase, st)
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) / steps * 1e3
-        path = st["numeric_path"]
     torch.cuda.empty_cache()
-    return {"ms_per_step": ms, "numeric_path": path,
-            "phase_ms_per_step": {k: round(v, 3) for k, v in phases.items() if v >= 0.05}}
+    heavy_bytes = sum(v["bytes"] for k, v in per_phase.items() if k[1] in HEAVY_PHASES)
+    heavy_ms = sum(v["ms"] for k, v in per_phase.items() if k[1] in HEAVY_PHASES)
+    return {"ms_per_step": ms, "numeric_path": st["numeric_path"], "row_batches": st["nbatches"],
+            "vchunks": st["vchunks"],
+            "heavy_path": {"ms_per_step": heavy_ms / steps,
+                           "frac": (heavy_bytes / (heavy_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+                           if heavy_ms else 0},
+            "phases": {k: v for k, v in _phase_fracs(per_phase, steps).items()
+                       if v["ms_per_step"] >= 0.05}}
+
+
+def host_threads():
+    """(threads the oracle uses, cores this process may run on).
+
+    A one-GPU machine gives the process a share of 16 host threads whatever the
+    affinity mask shows, so the oracle uses at most 16."""
+    try:
+        visible = len(os.sched_getaffinity(0))
+    except AttributeError:
+        visible = os.cpu_count() or 1
+    return max(1, min(visible, 16)), visible
 
 
 def cpu_baseline(A, B, target_s: float):
@@ -191,11 +239,7 @@ def cpu_baseline(A, B, target_s: float):
     import oracle
 
     oracle.build(force=False)
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
+    cores, visible = host_threads()
     u = oracle.row_products(A, B)
     total = int(u.sum())
     frac = 1.0 / 4096
@@ -209,27 +253,42 @@ def cpu_baseline(A, B, target_s: float):
         if dt >= target_s * 0.5 or step == 1:
             break
         frac = min(1.0, frac * max(2.0, min(16.0, target_s / max(dt, 1e-3))))
-    return {"value": prods / dt, "unit": "products/s", "cores": cores, "kind": "oracle",
+    return {"value": prods / dt, "unit": "products/s", "cores": cores, "cores_visible": visible,
+            "kind": "oracle",
             "sample": f"one row of C in every {step} ({rows.size} rows, {prods} of {total} products)",
             "seconds": dt, "gflops": 2.0 * prods / dt / 1e9, "cpu_model": cpu_model()}
 
 
-def main():
-    args = parse()
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the library runs one product on one GPU", file=sys.stderr)
-        sys.exit(2)
+def oracle_one_thread():
+    """The oracle on one thread for the two small workloads: every row of the
+    1024^2 R-MAT square (best of 3), one row in 16 of the 2^20 banded square."""
+    import oracle
+    from spgemm_irregular_matrices_amd import synth
+
+    out = {}
+    for name, step, reps in (("rmat10_ef8", 1, 3), ("banded_n1M_17diag", 16, 1)):
+        A, B = synth.workload(name)
+        u = oracle.row_products(A, B)
+        rows = np.arange(0, A.nrows, step, dtype=np.int64)
+        best = None
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.spgemm_rows(A, B, rows, nthreads=1)
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+        prods = int(u[rows].sum())
+        out[name] = {"value": prods / best, "unit": "products/s", "seconds": best,
+                     "sample": "every row, best of 3" if step == 1 else f"one row in {step}"}
+    return out
+
+
+def bench_workload(name: str, args, copy_gbps: float, with_paths: bool, with_cpu: bool) -> dict:
+    """Time `args.steps` steps of one workload; returns its full record."""
     import torch
 
     from spgemm_irregular_matrices_amd import binding, synth
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    binding.load()
-    A, B = synth.workload(args.workload)
+    A, B = synth.workload(name)
     dA = binding.DeviceCSR.from_host(A)
     dB = dA if B is A else binding.DeviceCSR.from_host(B)
     torch.cuda.synchronize()
@@ -259,12 +318,7 @@ def main():
         out = step()
         st = plan.stats()   # waits for this step's events
         step_ms.append((time.perf_counter() - ts) * 1e3)
-        for pn in ("symbolic", "numeric"):
-            for ph, rec in st[pn].items():
-                d = per_phase.setdefault((pn, ph), {"ms": 0.0, "launches": 0, "bytes": 0.0})
-                d["ms"] += rec["ms"]
-                d["launches"] += rec["launches"]
-                d["bytes"] += rec["bytes"]
+        _accumulate(per_phase, st)
         del out
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -284,8 +338,7 @@ def main():
     launch_ms = d["ms"] / max(d["launches"], 1)
     bytes_per_launch = d["bytes"] / max(d["launches"], 1)
     achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9 if launch_ms > 0 else 0.0
-    traffic = measured_traffic(args.workload, f"{dom[0]}:{dom[1]}")
-    copy_gbps = copy_rate_GBps()
+    traffic = measured_traffic(name, f"{dom[0]}:{dom[1]}")
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "kernel": f"{dom[0]}:{dom[1]}", "launch_ms": launch_ms,
@@ -293,25 +346,27 @@ def main():
                 "measured_copy_GBps": copy_gbps, "frac_of_measured_copy": achieved / copy_gbps}
     heavy_bytes = sum(v["bytes"] for k, v in per_phase.items() if k[1] in HEAVY_PHASES)
     heavy_ms = sum(v["ms"] for k, v in per_phase.items() if k[1] in HEAVY_PHASES)
-
     plan.close()
+
     paths = None
-    if not args.no_paths:
-        # the page's dataflows on the same product, for context: outer product
-        # into C-hat then multisplit, and the first level formed in the tiles
+    if with_paths:
+        # the page's dataflows on the same product: outer product into C-hat
+        # then multisplit (in one batch, and in batches of at most 2^31 - 1
+        # products where C-hat holds more), and the first level formed in the
+        # multisplit tiles
         paths = {"separate_chat": time_numeric_path(dA, dB, 2, 3),
                  "fused_first_level": time_numeric_path(dA, dB, 1, 3)}
+        if st["heavy_products"] > (1 << 31) - 1 and name == "rmat20_ef8":
+            paths["separate_chat_batched"] = time_numeric_path(dA, dB, 2, 3, (1 << 31) - 1)
+    del dA, dB
+    torch.cuda.empty_cache()
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(A, B, args.cpu_seconds)
-
-    line = {
-        "metric": "SpGEMM intermediate products/s (GFLOP/s) and HBM GB/s fraction, R-MAT A*A",
-        "value": value, "unit": "products/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
-        "config": {"workload": args.workload, "description": synth.WORKLOADS[args.workload],
+    cpu = cpu_baseline(A, B, args.cpu_seconds) if with_cpu else None
+    phases = _phase_fracs(per_phase, args.steps)
+    return {
+        "value": value, "unit": "products/s", "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms,
+        "config": {"workload": name, "description": synth.WORKLOADS[name],
                    "nrows": A.nrows, "nnz_A": A.nnz, "sum_products": products,
                    "nnz_C": st["nnz_c"], "heavy_rows": st["heavy_rows"],
                    "heavy_products": st["heavy_products"], "tau": st["tau"],
@@ -324,16 +379,53 @@ def main():
         "heavy_path": {"ms_per_step": heavy_ms / args.steps,
                        "algorithmic_GBps": heavy_bytes / (heavy_ms * 1e-3) / 1e9 if heavy_ms else 0,
                        "frac": (heavy_bytes / (heavy_ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if heavy_ms else 0},
-        "phase_ms_per_step": {f"{k[0]}:{k[1]}": v["ms"] / args.steps for k, v in per_phase.items()
-                              if v["launches"]},
+        "phase_ms_per_step": {k: v["ms_per_step"] for k, v in phases.items()},
         # algorithmic bytes of a phase over its measured time (phases that count bytes)
-        "phase_algorithmic_GBps": {f"{k[0]}:{k[1]}": v["bytes"] / (v["ms"] * 1e-3) / 1e9
-                                   for k, v in per_phase.items()
-                                   if v["launches"] and v["bytes"] > 0 and v["ms"] > 0},
+        "phase_algorithmic_GBps": {k: v["algorithmic_GBps"] for k, v in phases.items()
+                                   if "algorithmic_GBps" in v},
+        "phase_frac": {k: v["frac"] for k, v in phases.items() if "frac" in v},
         "step_ms_min_max": [min(step_ms), max(step_ms)],
         "cpu_baseline": cpu,
         "paths": paths,
     }
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the library runs one product on one GPU", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from spgemm_irregular_matrices_amd import binding
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load()
+    copy_gbps = copy_rate_GBps()
+    head = bench_workload(args.workload, args, copy_gbps, not args.no_paths,
+                          not args.no_cpu_baseline)
+    others = {}
+    for name in [w for w in args.also.split(",") if w and w != args.workload]:
+        others[name] = bench_workload(name, args, copy_gbps, not args.no_paths,
+                                      not args.no_cpu_baseline)
+    if head["cpu_baseline"] is not None:
+        head["cpu_baseline"]["one_thread"] = oracle_one_thread()
+
+    line = {
+        "metric": "SpGEMM intermediate products/s (GFLOP/s) and HBM GB/s fraction, R-MAT A*A",
+        "value": head["value"], "unit": "products/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+    }
+    for k, v in head.items():
+        if k not in line:
+            line[k] = v
+    if others:
+        line["workloads"] = others
     print(json.dumps(line))
 
 

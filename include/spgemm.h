@@ -10,11 +10,18 @@
  * phase (C.rowPtr and C.nnz) and a numeric phase (C.col and C.val, given
  * C.rowPtr) that Algorithm 1 takes as its inputs and outputs. Internally the
  * library follows Algorithm 3 of that page: per-row intermediate-product
- * counts, a light/heavy row split at the threshold tau of Eq. (4), an outer
- * product (Algorithm 4) that expands the heavy rows into C-hat, a
- * hierarchical multisplit (Algorithm 5, Section III-C/D) that cuts every
- * heavy row into column-range chunks, and local-memory accumulation of
- * every chunk and light row (Section III-E).
+ * counts, a light/heavy row split at the threshold tau of Eq. (4), the
+ * column-range chunk hierarchy of Section III-D (Eqs. 5-7), and
+ * local-memory accumulation of every chunk and light row (Section III-E).
+ * The heavy rows' numeric pass has three dataflows (spgemm_options
+ * numeric_mode). The page's own: an outer product (Algorithm 4) expands the
+ * heavy rows into C-hat and a hierarchical multisplit (Algorithm 5, Section
+ * III-C) cuts them into chunks; or the same with the first multisplit level
+ * forming its own products, so that C-hat is never written. The default,
+ * where it applies: the column-range split is applied once to B's rows
+ * instead of to C-hat, and every (heavy row, final chunk) is accumulated
+ * straight from A and the split B, so neither C-hat nor its reordered copy
+ * is built; the chunk sets, and so the result, are the same.
  *
  * Conventions for every entry point
  *   - Matrix and output arrays are DEVICE pointers on the current HIP
@@ -89,6 +96,8 @@ typedef struct {
                                      final chunks once, and every (heavy row, chunk) item
                                      accumulated straight from A and the split B (needs
                                      the fused symbolic pass; else 1 runs)                 */
+    int64_t workspace_limit_bytes; /* most device workspace the plan may hold; a call that
+                                     needs more returns OUT_OF_MEMORY (0 = no limit)      */
 } spgemm_options;
 
 /* Phases, named after the gMAGNUS page's phase breakdown (Section IV-C,
@@ -186,8 +195,9 @@ SPGEMM_API void spgemm_plan_destroy(spgemm_plan plan);
  * (i, j) reachable through a stored A[i,k] and a stored B[k,j], including
  * entries whose values later cancel to zero. Reads A and B structure only.
  * Blocks the calling thread until C_nnz is known. Errors: INVALID_ARG,
- * DIM_MISMATCH, INDEX_RANGE (validation on), OVERFLOW (B.ncols > INT32_MAX),
- * OUT_OF_MEMORY, HIP. */
+ * DIM_MISMATCH, INDEX_RANGE (validation on), OVERFLOW (A.ncols or B.ncols
+ * above INT32_MAX, A.nrows of INT32_MAX or more), OUT_OF_MEMORY (device
+ * memory, or the plan's workspace_limit_bytes, exhausted), HIP. */
 SPGEMM_API int spgemm_symbolic(spgemm_plan plan, const spgemm_csr* A, const spgemm_csr* B,
                                int64_t* C_rowptr, int64_t* C_nnz, void* stream);
 

@@ -48,7 +48,8 @@ class Options(ctypes.Structure):
                 ("chunk_width_override", ctypes.c_int64), ("nchunks_cap", ctypes.c_int32),
                 ("validate_inputs", ctypes.c_int32), ("debug_dump", ctypes.c_int32),
                 ("timing", ctypes.c_int32), ("max_batch_products", ctypes.c_int64),
-                ("symbolic_mode", ctypes.c_int32), ("numeric_mode", ctypes.c_int32)]
+                ("symbolic_mode", ctypes.c_int32), ("numeric_mode", ctypes.c_int32),
+                ("workspace_limit_bytes", ctypes.c_int64)]
 
 
 NPH = len(PHASES)
@@ -176,7 +177,7 @@ class Plan:
 
     def __init__(self, tau_override=0, chunk_width_override=0, nchunks_cap=0, lds_budget_bytes=0,
                  validate_inputs=True, debug_dump=False, timing=False, max_batch_products=0,
-                 symbolic_mode=0, numeric_mode=0):
+                 symbolic_mode=0, numeric_mode=0, workspace_limit_bytes=0):
         lib = load()
         o = Options()
         lib.spgemm_options_default(ctypes.byref(o))
@@ -190,6 +191,7 @@ class Plan:
         o.max_batch_products = max_batch_products
         o.symbolic_mode = symbolic_mode
         o.numeric_mode = numeric_mode
+        o.workspace_limit_bytes = workspace_limit_bytes
         h = ctypes.c_void_p()
         _check(lib.spgemm_plan_create(ctypes.byref(h), ctypes.byref(o)), "spgemm_plan_create")
         self._h = h

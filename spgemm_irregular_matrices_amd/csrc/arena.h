@@ -17,6 +17,10 @@ class Arena {
     Arena& operator=(const Arena&) = delete;
     ~Arena() { release(); }
 
+    // Largest total the arena may hold (0 = no limit). A request that would
+    // pass it fails as if the device had no more memory.
+    void set_limit(size_t bytes) { limit_ = bytes; }
+
     // Device buffer `name` with room for at least `bytes`. Growing frees the
     // old buffer (hipFree waits for the device, so no kernel still uses it).
     void* get(const std::string& name, size_t bytes) {
@@ -32,6 +36,10 @@ class Arena {
             size_t extra = bytes / 8;
             if (extra > (size_t(256) << 20)) extra = size_t(256) << 20;
             size_t cap = (bytes + extra + (size_t(2) << 20) - 1) & ~((size_t(2) << 20) - 1);
+            if (limit_ && total_ + cap > limit_) cap = (bytes + 255) & ~size_t(255);
+            if (limit_ && total_ + cap > limit_)
+                throw OomError("device workspace '" + name + "' (" + std::to_string(bytes) +
+                               " bytes) passes the plan's workspace limit");
             void* p = nullptr;
             if (hipMalloc(&p, cap) != hipSuccess) {
                 (void)hipGetLastError();
@@ -71,6 +79,7 @@ class Arena {
     };
     std::unordered_map<std::string, Buf> bufs_;
     size_t total_ = 0;
+    size_t limit_ = 0;
 };
 
 }  // namespace sg

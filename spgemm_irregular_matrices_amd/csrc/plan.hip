@@ -709,13 +709,6 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     p->L = 0;
     p->batches.clear();
     if (p->H > 0) {
-        int64_t* chat_rp = ar.get<int64_t>("chat_rp", (size_t)p->H + 1);
-        {
-            PhaseScope ps(p, 0, SPGEMM_PHASE_CSR_TO_CSC, st);
-            heavy_rowptr(A, S, hrows, p->H, chat_rp, ar, st);
-        }
-        plan_batches(p, chat_rp, st);
-        plan_capacities(p, A);
         p->stats.chat_bytes = 12 * p->Nh + 8 * (p->H + 1);
         const int64_t req = q.nlevels == 0 ? 1 : q.nchunks_required;
         // the fused pass needs the row's bitmap in LDS and a per-B-row slot
@@ -740,6 +733,27 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
                         (p->opt.numeric_mode == 0 && !p->opt.debug_dump));
         // the masked CSC feeds the separate outer product only
         const bool need_csc = !(p->fused_num || p->direct) || !p->fused_sym;
+        // C-hat's row pointers, the row batches and the capacities of the
+        // per-batch arrays serve the paths that build C-hat-reord; the
+        // direct path forms every (row, final chunk) item from A and the
+        // split B in one pass, so it has one batch and none of these arrays
+        int64_t* chat_rp = nullptr;
+        if (p->direct) {
+            BatchState b;
+            b.h0 = 0;
+            b.h1 = p->H;
+            b.N = p->Nh;
+            p->batches.push_back(b);
+            p->maxN = 0;
+        } else {
+            chat_rp = ar.get<int64_t>("chat_rp", (size_t)p->H + 1);
+            {
+                PhaseScope ps(p, 0, SPGEMM_PHASE_CSR_TO_CSC, st);
+                heavy_rowptr(A, S, hrows, p->H, chat_rp, ar, st);
+            }
+            plan_batches(p, chat_rp, st);
+            plan_capacities(p, A);
+        }
         if (p->fused_num || p->direct) {
             PhaseScope ps(p, 0, SPGEMM_PHASE_CSR_TO_CSC, st);
             fused_setup(A, B, S, hrows, p->H, ar.get<int64_t>("h_q0", (size_t)p->H),
@@ -794,7 +808,8 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             PhaseScope ps(p, 0, SPGEMM_PHASE_PREFIX_SUM, st);
             reduce_children(dist_fin, (int)req, p->H, hrows, cnt_row, st);
         }
-        CscBufs c = csc_bufs(p);
+        CscBufs c{};
+        if (!p->direct) c = csc_bufs(p);
         int64_t ent_cur = 0, P_cur = 0, tile_cur = 0, crp_cur = 0;
         int64_t nat_cur[kMaxLevels] = {}, rp_cur[kMaxLevels] = {};
         for (BatchState& bt : p->batches) {
@@ -930,27 +945,27 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
     // light rows on the plan's second stream when there are heavy rows to
     // overlap with; the caller's stream waits for them on every way out
     const bool fork = p->H > 0 && p->row_bins[RB_H8192 + 1] > p->row_bins[RB_T8];
+    // Armed as soon as the side stream has forked: whatever was queued on
+    // it, also when a later launch throws, is waited for by the caller's
+    // stream when this function returns.
     struct Join {
         bool on;
-        hipStream_t st;
+        hipStream_t st, side;
         hipEvent_t ev;
         ~Join() {
-            if (on) (void)hipStreamWaitEvent(st, ev, 0);
+            if (on && hipEventRecord(ev, side) == hipSuccess) (void)hipStreamWaitEvent(st, ev, 0);
         }
-    } join{false, st, p->ev_join};
+    } join{false, st, p->lst, p->ev_join};
     const hipStream_t lst = fork ? p->lst : st;
     if (fork) {
         SG_HIP(hipEventRecord(p->ev_fork, st));
         SG_HIP(hipStreamWaitEvent(p->lst, p->ev_fork, 0));
+        join.on = true;
     }
     {
         PhaseScope ps(p, 1, SPGEMM_PHASE_LIGHT_ACCUM, lst);
         for (int b = RB_T8; b <= RB_H8192; ++b)
             accumulate_rows(ri, b, p->row_bins[b], p->row_bins[b + 1] - p->row_bins[b], true, lst);
-    }
-    if (fork) {
-        SG_HIP(hipEventRecord(p->ev_join, p->lst));
-        join.on = true;
     }
     if (p->H == 0) return;
 
@@ -1120,6 +1135,18 @@ int guarded(F&& f) {
     }
 }
 
+// After OUT_OF_MEMORY the plan gives back all of its workspace (hipFree
+// waits for the device, so no queued kernel still uses it) and needs a new
+// symbolic call: the caller can free memory of its own and retry.
+int release_on_oom(spgemm_plan p, int rc) {
+    if (rc == SPGEMM_ERR_OUT_OF_MEMORY) {
+        p->ready = false;
+        p->dbg_valid = false;
+        p->ar.release();
+    }
+    return rc;
+}
+
 }  // namespace
 
 // ============================================================================
@@ -1140,7 +1167,7 @@ SPGEMM_API int spgemm_plan_create(spgemm_plan* out, const spgemm_options* opt) {
     spgemm_options_default(&o);
     if (opt) o = *opt;
     if (o.lds_budget_bytes < 0 || o.tau_override < 0 || o.chunk_width_override < 0 ||
-        o.nchunks_cap < 0 || o.max_batch_products < 0)
+        o.nchunks_cap < 0 || o.max_batch_products < 0 || o.workspace_limit_bytes < 0)
         return SPGEMM_ERR_INVALID_ARG;
     if (o.symbolic_mode < 0 || o.symbolic_mode > 2 || o.numeric_mode < 0 || o.numeric_mode > 3)
         return SPGEMM_ERR_INVALID_ARG;
@@ -1152,6 +1179,7 @@ SPGEMM_API int spgemm_plan_create(spgemm_plan* out, const spgemm_options* opt) {
     return guarded([&]() -> int {
         auto* p = new spgemm_plan_s();
         p->opt = o;
+        p->ar.set_limit((size_t)o.workspace_limit_bytes);
         if (hipGetDevice(&p->device) != hipSuccess) {
             delete p;
             return SPGEMM_ERR_HIP;
@@ -1201,7 +1229,7 @@ SPGEMM_API int spgemm_symbolic(spgemm_plan p, const spgemm_csr* A, const spgemm_
     if (A->ncols != B->nrows) return SPGEMM_ERR_DIM_MISMATCH;
     p->ready = false;
     hipStream_t st = (hipStream_t)stream;
-    return guarded([&]() -> int {
+    return release_on_oom(p, guarded([&]() -> int {
         int64_t nnz = symbolic_impl(p, to_dev(A), to_dev(B), C_rowptr, st);
         if (nnz < 0) return SPGEMM_ERR_INDEX_RANGE;
         *C_nnz = nnz;
@@ -1214,7 +1242,7 @@ SPGEMM_API int spgemm_symbolic(spgemm_plan p, const spgemm_csr* A, const spgemm_
         p->Cnnz = nnz;
         p->ready = true;
         return SPGEMM_OK;
-    });
+    }));
 }
 
 SPGEMM_API int spgemm_numeric(spgemm_plan p, const spgemm_csr* A, const spgemm_csr* B,
@@ -1231,10 +1259,10 @@ SPGEMM_API int spgemm_numeric(spgemm_plan p, const spgemm_csr* A, const spgemm_c
         return SPGEMM_ERR_PLAN_MISMATCH;
     if (p->Cnnz > 0 && (!C_col || !C_val)) return SPGEMM_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
-    return guarded([&]() -> int {
+    return release_on_oom(p, guarded([&]() -> int {
         numeric_impl(p, to_dev(A), to_dev(B), C_rowptr, C_col, C_val, st);
         return SPGEMM_OK;
-    });
+    }));
 }
 
 SPGEMM_API int spgemm_multiply(spgemm_plan p, const spgemm_csr* A, const spgemm_csr* B,

@@ -45,8 +45,8 @@ int main(void) {
   printf("%zu %zu %zu %zu %zu\n", offsetof(spgemm_stats, phase_ms), offsetof(spgemm_stats, lds_bytes),
          offsetof(spgemm_options, max_batch_products), offsetof(spgemm_options, symbolic_mode),
          offsetof(spgemm_options, numeric_mode));
-  printf("%zu %zu %zu\n", offsetof(spgemm_stats, numeric_path), offsetof(spgemm_stats, f_u_le),
-         offsetof(spgemm_stats, gamma));
+  printf("%zu %zu %zu %zu\n", offsetof(spgemm_stats, numeric_path), offsetof(spgemm_stats, f_u_le),
+         offsetof(spgemm_stats, gamma), offsetof(spgemm_options, workspace_limit_bytes));
   return 0;
 }''')
     exe = tmp_path / "layout"
@@ -65,6 +65,7 @@ int main(void) {
     assert sizes[9] == binding.Stats.numeric_path.offset
     assert sizes[10] == binding.Stats.f_u_le.offset
     assert sizes[11] == binding.Stats.gamma.offset
+    assert sizes[12] == binding.Options.workspace_limit_bytes.offset
 
 
 def test_no_gpu_call_fails_loudly():

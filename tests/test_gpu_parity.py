@@ -390,12 +390,17 @@ def test_random_skewed_paths(tau, seed, mode):
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("budget,width,cap", [(1, 64, 4), (700, 64, 4), (5000, 32, 2), (20000, 0, 0)])
 def test_row_batches(budget, width, cap, mode):
-    """Heavy rows processed in batches of bounded products (one row per batch at budget 1)."""
+    """Heavy rows processed in batches of bounded products (one row per batch at
+    budget 1). The direct path (numeric mode 3) builds no C-hat, so the budget
+    does not apply to it: it runs one batch."""
     A = synth.rmat(11, 8, seed=121, value_seed=122)
     rp, col, val, st = run_gpu(A, A, tau_override=64, chunk_width_override=width, nchunks_cap=cap,
                                max_batch_products=budget, symbolic_mode=mode[0],
                                numeric_mode=mode[1])
-    assert st["nbatches"] > 1
+    if st["numeric_path"] == 3:
+        assert st["nbatches"] == 1
+    else:
+        assert st["nbatches"] > 1
     compare(A, A, rp, col, val)
 
 
@@ -553,3 +558,172 @@ def test_error_paths():
         with pytest.raises(binding.SpgemmError) as e:
             binding.Plan(**kw)
         assert e.value.code == -1
+
+
+def _with_duplicates(M, seed):
+    """M with every stored entry repeated once under a new value, the entries of
+    each row shuffled: a repeated column must act as the sum of its entries."""
+    rows = np.repeat(np.arange(M.nrows), np.diff(M.rowptr))
+    rows2 = np.concatenate([rows, rows])
+    col2 = np.concatenate([M.col, M.col])
+    val2 = np.concatenate([M.val, synth.uniform_values(seed, M.nnz)])
+    keys = synth.splitmix64(seed + 1, np.arange(col2.size, dtype=np.uint64))
+    order = np.lexsort((keys, rows2))
+    rp = np.zeros(M.nrows + 1, dtype=np.int64)
+    rp[1:] = np.cumsum(2 * np.diff(M.rowptr))
+    return synth.CSR(M.nrows, M.ncols, rp, col2[order].astype(np.int32), val2[order].copy())
+
+
+@pytest.mark.parametrize("kw", [
+    {},                                                               # light bins only
+    {"tau_override": 40, "chunk_width_override": 64, "nchunks_cap": 4},  # heavy, path 3
+    {"tau_override": 40, "chunk_width_override": 64, "nchunks_cap": 4,
+     "symbolic_mode": 2, "numeric_mode": 2},                           # the page's dataflow
+    {"tau_override": 40, "chunk_width_override": 64, "nchunks_cap": 4, "numeric_mode": 1},
+])
+def test_duplicate_entries_in_rows(kw):
+    """A and B with every (row, column) stored twice: the oracle sums every
+    stored entry's products, and so must each path."""
+    A = _with_duplicates(synth.rmat(10, 4, seed=131, value_seed=132), 133)
+    B = _with_duplicates(synth.random_csr(1024, 900, seed=134, value_seed=135, mean_len=5,
+                                          skew=1.2), 136)
+    rp, col, val, st = run_gpu(A, B, **kw)
+    if kw:
+        assert st["heavy_rows"] > 0
+    compare(A, B, rp, col, val)
+    Ai = _with_duplicates(synth.rmat(10, 4, seed=137, value_seed=138), 139)
+    Ai.val = synth.small_int_values(140, Ai.nnz)  # every partial sum is an exact integer
+    rp, col, val, st = run_gpu(Ai, Ai, **kw)
+    compare(Ai, Ai, rp, col, val, exact_values=True)
+
+
+def test_overflow_rejected_before_any_kernel():
+    """More than INT32_MAX columns cannot be indexed by int32 columns: OVERFLOW."""
+    import torch
+    from spgemm_irregular_matrices_amd import binding
+    big = (1 << 31)
+    rp5 = torch.zeros(6, dtype=torch.int64, device="cuda")
+    rp4 = torch.zeros(5, dtype=torch.int64, device="cuda")
+    empty_i = torch.zeros(0, dtype=torch.int32, device="cuda")
+    empty_v = torch.zeros(0, dtype=torch.float64, device="cuda")
+    A = binding.DeviceCSR(4, 5, rp4, empty_i, empty_v)
+    B = binding.DeviceCSR(5, big, rp5, empty_i, empty_v)
+    with binding.Plan() as p:
+        with pytest.raises(binding.SpgemmError) as e:
+            p.symbolic(A, B)
+        assert e.value.code == -4
+        # A with more columns than int32 holds, B with as many rows
+        Aw = binding.DeviceCSR(4, big, rp4, empty_i, empty_v)
+        Bw = binding.DeviceCSR(big, 3, torch.zeros(1, dtype=torch.int64, device="cuda"),
+                               empty_i, empty_v)
+        with pytest.raises(binding.SpgemmError) as e:
+            p.symbolic(Aw, Bw)
+        assert e.value.code == -4
+        # the plan still works
+        S = synth.random_csr(40, 40, seed=141, value_seed=142, mean_len=4)
+        dS = binding.DeviceCSR.from_host(S)
+        C = p.multiply(dS, dS)
+        torch.cuda.synchronize()
+        compare(S, S, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy())
+
+
+def test_workspace_limit_gives_out_of_memory():
+    """A plan whose workspace limit is below what a product needs returns
+    OUT_OF_MEMORY, frees its workspace, and can then run a product that fits."""
+    import torch
+    from spgemm_irregular_matrices_amd import binding
+    A = synth.rmat(12, 16, seed=143, value_seed=144)
+    dA = binding.DeviceCSR.from_host(A)
+    tiny = synth.from_rows(2, 2, [[0, 1], [1]], [[2.0, -1.0], [3.0]])
+    dT = binding.DeviceCSR.from_host(tiny)
+    with binding.Plan(workspace_limit_bytes=64 << 10) as p:
+        with pytest.raises(binding.SpgemmError) as e:
+            p.multiply(dA, dA)
+        assert e.value.code == -5
+        # the numeric pass needs a successful symbolic pass again
+        rp = torch.zeros(A.nrows + 1, dtype=torch.int64, device="cuda")
+        with pytest.raises(binding.SpgemmError) as e:
+            p.numeric(dA, dA, rp, None, None)
+        assert e.value.code == -8
+        C = p.multiply(dT, dT)
+        torch.cuda.synchronize()
+        assert C.rowptr.cpu().tolist() == [0, 2, 3]
+        assert C.col.cpu().tolist() == [0, 1, 1]
+        assert C.val.cpu().tolist() == [4.0, -5.0, 9.0]
+    rp, col, val, st = run_gpu(A, A, workspace_limit_bytes=1 << 30)
+    compare(A, A, rp, col, val)
+
+
+def _check_levels_against_oracle(A, B, tau, chat, levels):
+    """Every multisplit level, level by level, against the oracle's C-hat cut
+    by oracle.stages.split_by_width.
+
+    Level l's rows are the nonempty chunks of its input rows (the heavy rows
+    of C-hat at level 0, else the heavy chunks of level l-1, which come first
+    in that level's output); row_key = input row * chunks + chunk. Each row
+    must hold exactly the entries of its parent's column range (a multiset:
+    order inside a chunk is free), and a level's first rows are exactly its
+    chunks with more than tau elements when a further level follows.
+    """
+    u = oracle.row_products(A, B)
+    rows = np.nonzero(u > tau)[0]
+    crp, ccol, cval = stages.expand(A, B, rows)
+    # parents of level 0: the heavy rows of C-hat, covering [0, ppow)
+    par_cols = [ccol[crp[h]:crp[h + 1]] for h in range(rows.size)]
+    par_vals = [cval[crp[h]:crp[h + 1]] for h in range(rows.size)]
+    par_base = [0] * rows.size
+    width_in = chat["chunk_width"]
+    for l, lv in enumerate(levels):
+        W = lv["chunk_width"]
+        nch = width_in // W
+        keys = lv["row_key"]
+        lrp = lv["rowptr"]
+        assert np.unique(keys).size == keys.size
+        by_key = {int(k): r for r, k in enumerate(keys)}
+        nxt_cols, nxt_vals, nxt_base = {}, {}, {}
+        seen = 0
+        for p_idx in range(len(par_cols)):
+            pieces = stages.split_by_width(par_cols[p_idx], par_vals[p_idx], W, par_base[p_idx], nch)
+            for c, (ec, ev) in enumerate(pieces):
+                key = p_idx * nch + c
+                if ec.size == 0:
+                    assert key not in by_key, f"level {l}: empty chunk {key} present"
+                    continue
+                r = by_key[key]
+                a, b = int(lrp[r]), int(lrp[r + 1])
+                got = sorted(zip(lv["col"][a:b].tolist(), lv["val"][a:b].tolist()))
+                assert got == sorted(zip(ec.tolist(), ev.tolist())), f"level {l} chunk {key}"
+                seen += b - a
+                nxt_cols[r], nxt_vals[r], nxt_base[r] = ec, ev, par_base[p_idx] + c * W
+        assert seen == int(lrp[-1]) and len(by_key) == len(nxt_cols)
+        counts = np.diff(lrp)
+        if l + 1 < len(levels):
+            nheavy = int(np.count_nonzero(counts > tau))
+            assert np.all(counts[:nheavy] > tau) and np.all(counts[nheavy:] <= tau)
+            par_cols = [nxt_cols[r] for r in range(nheavy)]
+            par_vals = [nxt_vals[r] for r in range(nheavy)]
+            par_base = [nxt_base[r] for r in range(nheavy)]
+        width_in = W
+
+
+@pytest.mark.parametrize("numeric_mode", [2, 1])
+@pytest.mark.parametrize("width,cap,nlevels", [(64, 2, 3), (32, 4, 2), (32, 2, 4)])
+def test_every_multisplit_level_matches_oracle(numeric_mode, width, cap, nlevels):
+    """Stage parity of every multisplit level (not only the first)."""
+    import torch
+    from spgemm_irregular_matrices_amd import binding
+    A = synth.random_csr(300, 200, seed=151, value_seed=152, mean_len=10, skew=1.3)
+    B = synth.random_csr(200, 500, seed=153, value_seed=154, mean_len=12, skew=1.3)
+    tau = 24
+    dA, dB = binding.DeviceCSR.from_host(A), binding.DeviceCSR.from_host(B)
+    with binding.Plan(tau_override=tau, chunk_width_override=width, nchunks_cap=cap,
+                      debug_dump=True, symbolic_mode=2, numeric_mode=numeric_mode) as p:
+        C = p.multiply(dA, dB)
+        torch.cuda.synchronize()
+        st = p.stats()
+        assert st["nlevels"] == nlevels, st
+        levels = [p.debug(l) for l in range(st["nlevels"])]
+        chat = p.debug(-1)
+    assert all(lv["val"] is not None for lv in levels)
+    _check_levels_against_oracle(A, B, tau, chat, levels)
+    compare(A, B, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy())

@@ -1,22 +1,59 @@
-"""GPU parity at the benchmark workloads' full sizes, in the launch
-configuration bench.py times (default plan options).
+"""GPU parity at the benchmark workloads' full sizes, every row of C.
 
-Where the oracle can compute every row in seconds (the 1024^2 R-MAT square
-and the 2^20 banded square), every row is compared. For the large R-MAT and
-rectangular products, the heaviest rows, rows near the heavy threshold and
-seeded random rows are compared one by one, and properties that hold at any
-size are checked on every row: row pointers consistent with nnz, per-row
-nnz <= u(i), strictly ascending columns, and the row-sum identity
-C*1 = A*(B*1) within the value bound plus the summation error of the check.
+Each workload runs through the C ABI in the launch configuration bench.py
+times (default plan options, numeric path 3), and again with the gMAGNUS
+page's own dataflow (numeric path 2: outer product into C-hat, the
+hierarchical multisplit, dense accumulation of the chunks; Alg. 3-5,
+Sec. III-B/C). The 2^18 R-MAT square runs the page's dataflow in one batch,
+so C-hat positions pass 2^31, and also with the fused first level (path 1);
+the 2^20 R-MAT square runs it in row batches of at most 2^31 - 1 products.
+
+The oracle then computes every row in row blocks balanced by intermediate
+products, and each block is compared with every GPU result: row lengths and
+columns bit for bit, every value within 1e-12 * sum|a*b| of its entry. The
+large workloads are split into several tests so that each one reports within
+a minute or so.
 """
+import concurrent.futures as cf
+import os
+
 import numpy as np
 import pytest
 
 import oracle
 from spgemm_irregular_matrices_amd import synth
-from tests.helpers import compare, sample_rows
+from tests.helpers import BOUND, compare
 
 pytestmark = pytest.mark.gpu
+
+BATCH_2G = (1 << 31) - 1
+
+# workload -> (label, plan options, numeric path that must have run, batches)
+RUNS = {
+    "rmat18_ef16": [
+        ("default", {}, 3, 1),
+        ("page_dataflow_one_batch", {"numeric_mode": 2}, 2, 1),
+        ("fused_first_level", {"numeric_mode": 1}, 1, 1),
+    ],
+    "rmat20_ef8": [
+        ("default", {}, 3, 1),
+        ("page_dataflow_batched", {"numeric_mode": 2, "max_batch_products": BATCH_2G}, 2, 3),
+    ],
+    "rect_zipf2.1_x_uniform16": [
+        ("default", {}, 3, 1),
+        ("page_dataflow_one_batch", {"numeric_mode": 2}, 2, 1),
+    ],
+}
+PARTS = {"rmat18_ef16": 4, "rmat20_ef8": 8, "rect_zipf2.1_x_uniform16": 1}
+BLOCK_PRODUCTS = 1 << 27  # oracle work per row block
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -40,76 +77,6 @@ def _multiply(A, B, **plan_kwargs):
         st = p.stats()
     del dA, dB
     return C, st
-
-
-def _rows_to_host(C, rows):
-    """Host CSR arrays holding only the sampled rows (zero-length elsewhere)."""
-    import torch
-    rp = C.rowptr.cpu().numpy()
-    starts = rp[rows]
-    lens = rp[rows + 1] - starts
-    from tests.helpers import gather_ranges
-    idx = torch.from_numpy(gather_ranges(starts, lens)).to(C.col.device)
-    col = C.col[idx].cpu().numpy()
-    val = C.val[idx].cpu().numpy()
-    # rebuild a full-height rowptr whose sampled rows point into col/val
-    n = rp.size - 1
-    fake_rp = np.zeros(n + 1, dtype=np.int64)
-    lens_full = np.zeros(n, dtype=np.int64)
-    lens_full[rows] = lens
-    np.cumsum(lens_full, out=fake_rp[1:])
-    return rp, fake_rp, col, val
-
-
-def _segment_sums_ld(vals, rowptr):
-    """Per-row sums in long double (64-bit significand), empty rows give 0."""
-    n = rowptr.size - 1
-    out = np.zeros(n, dtype=np.longdouble)
-    lens = np.diff(rowptr)
-    nz = lens > 0
-    if vals.size:
-        out[nz] = np.add.reduceat(vals.astype(np.longdouble), rowptr[:-1][nz])
-    return out
-
-
-def _check_properties(A, B, C, u):
-    """Row pointers, per-row bounds, sorted columns and C*1 = A*(B*1), in row blocks.
-
-    Both sides are summed in long double, so the check's own rounding is far
-    below the 1e-12 * sum_k |a_ik| * sum_j |b_kj| the product is allowed.
-    """
-    import torch
-    rp = C.rowptr.cpu().numpy()
-    n = A.nrows
-    assert rp[0] == 0 and np.all(np.diff(rp) >= 0)
-    assert np.all(np.diff(rp) <= u)
-    bsum = _segment_sums_ld(B.val, B.rowptr)
-    babs = _segment_sums_ld(np.abs(B.val), B.rowptr)
-    ld = np.longdouble
-    rhs = _segment_sums_ld(np.zeros(0), A.rowptr)
-    bound = np.zeros(n, dtype=ld)
-    if A.nnz:
-        rhs = _segment_sums_ld(A.val.astype(ld) * bsum[A.col], A.rowptr)
-        bound = _segment_sums_ld(np.abs(A.val).astype(ld) * babs[A.col], A.rowptr)
-    step = 1 << 13
-    for r0 in range(0, n, step):
-        r1 = min(n, r0 + step)
-        s, e = int(rp[r0]), int(rp[r1])
-        col = C.col[s:e].cpu().numpy()
-        val = C.val[s:e].cpu().numpy()
-        lrp = rp[r0:r1 + 1] - s
-        lens = np.diff(lrp)
-        # strictly ascending columns inside every row
-        d = np.diff(col.astype(np.int64))
-        row_start = np.zeros(col.size, dtype=bool)
-        row_start[lrp[:-1][lens > 0]] = True
-        assert np.all((d > 0) | row_start[1:]), f"unsorted row in block {r0}"
-        sums = _segment_sums_ld(val, lrp)
-        tol = (1e-12 + 1e-15) * bound[r0:r1]
-        bad = np.nonzero(np.abs(sums - rhs[r0:r1]) > tol)[0]
-        assert bad.size == 0, f"row-sum identity fails at rows {r0 + bad[:5]}"
-        del col, val
-    torch.cuda.empty_cache()
 
 
 def _bucket_upper(v: int) -> int:
@@ -149,27 +116,131 @@ def test_banded_1M_all_rows():
     i = np.arange(n)
     exp = np.minimum(n - 1, i + 16) - np.maximum(0, i - 16) + 1
     assert np.array_equal(np.diff(rp), exp)
-    compare(A, B, rp, C.col.cpu().numpy(), C.val.cpu().numpy())
+    compare(A, B, rp, C.col.cpu().numpy(), C.val.cpu().numpy(), nthreads=_threads())
     _check_structural_stats(st, oracle.row_products(A, B))
 
 
-@pytest.mark.parametrize("name,batch", [("rmat18_ef16", 0), ("rmat20_ef8", 0),
-                                        ("rect_zipf2.1_x_uniform16", 0), ("rmat20_ef8", 1 << 31)])
-def test_large_sampled_rows_and_properties(name, batch):
+# ---------------------------------------------------------------- large workloads
+_cache: dict = {}
+
+
+def _workload_results(name):
+    """Inputs, u(i) and every GPU result of one workload (kept while its parts run)."""
     import torch
-    A, B = synth.workload(name)
-    C, st = _multiply(A, B, max_batch_products=batch)
-    if batch:
-        assert st["nbatches"] >= 3
-    rows, u = sample_rows(A, B, n_heavy=6, n_random=300, seed=7, tau=st["tau"])
-    assert st["heavy_rows"] > 0 and st["nlevels"] >= 1
-    assert st["numeric_path"] == 3  # the default heavy numeric pass, as benchmarked
-    assert st["sum_products"] == int(u.sum())
-    assert st["heavy_products"] == int(u[u > st["tau"]].sum())
-    rp, fake_rp, col, val = _rows_to_host(C, rows)
-    assert rp[-1] == st["nnz_c"]
-    compare(A, B, fake_rp, col, val, rows=rows, check_all_rowptr=False)
-    _check_properties(A, B, C, u)
-    _check_structural_stats(st, u)
-    del C
-    torch.cuda.empty_cache()
+    if _cache.get("name") != name:
+        _cache.clear()
+        torch.cuda.empty_cache()
+        A, B = synth.workload(name)
+        u = oracle.row_products(A, B)
+        res = []
+        for label, kw, path, nbatches in RUNS[name]:
+            C, st = _multiply(A, B, **kw)
+            res.append({"label": label, "C": C, "rp": C.rowptr.cpu().numpy(), "st": st,
+                        "path": path, "nbatches": nbatches})
+            torch.cuda.empty_cache()
+        _cache.update(name=name, A=A, B=B, u=u, cu=np.cumsum(u), res=res)
+    return _cache
+
+
+def _part_rows(cu, parts, k):
+    """Rows [r0, r1) of part k of `parts`, balanced by intermediate products."""
+    n = cu.size
+    tot = int(cu[-1]) if n else 0
+    b = [0] + [int(np.searchsorted(cu, tot * j // parts, side="right")) for j in range(1, parts)] + [n]
+    return b[k], max(b[k], b[k + 1])
+
+
+def _blocks(u, r0, r1):
+    """Consecutive row blocks of [r0, r1) with about BLOCK_PRODUCTS products each."""
+    cu = np.cumsum(u[r0:r1], dtype=np.int64)
+    out = []
+    a = 0
+    n = r1 - r0
+    while a < n:
+        base = int(cu[a - 1]) if a else 0
+        b = int(np.searchsorted(cu, base + BLOCK_PRODUCTS, side="right"))
+        b = max(b, a + 1)
+        out.append((r0 + a, r0 + min(b, n)))
+        a = b
+    return out
+
+
+def _check_piece(gcol, gval, rcol, rval, rabs):
+    """(columns equal, index of the first value outside the bound or -1)."""
+    if not np.array_equal(gcol, rcol):
+        return False, -1
+    ok = np.abs(gval - rval) <= BOUND * rabs  # NaN or Inf fails
+    if ok.all():
+        return True, -1
+    return True, int(np.argmin(ok))
+
+
+def _compare_block(pool, res, ref, r0, r1):
+    rp = res["rp"]
+    C = res["C"]
+    glen = np.diff(rp[r0:r1 + 1])
+    rlen = np.diff(ref.rowptr)
+    bad = np.nonzero(glen != rlen)[0]
+    assert bad.size == 0, (f"[{res['label']}] row lengths differ at rows {r0 + bad[:10]}: "
+                           f"gpu {glen[bad[:10]]} oracle {rlen[bad[:10]]}")
+    s, e = int(rp[r0]), int(rp[r1])
+    gcol = C.col[s:e].cpu().numpy()
+    gval = C.val[s:e].cpu().numpy()
+    nn = e - s
+    nthr = _threads()
+    cuts = np.linspace(0, nn, num=min(nthr, max(1, nn // (1 << 16))) + 1).astype(np.int64)
+    futs = [pool.submit(_check_piece, gcol[a:b], gval[a:b], ref.col[a:b], ref.val[a:b],
+                        ref.abssum[a:b]) for a, b in zip(cuts[:-1], cuts[1:])]
+    for (a, _), f in zip(zip(cuts[:-1], cuts[1:]), futs):
+        cols_ok, first_bad = f.result()
+        if not cols_ok:
+            j = a + int(np.argmax(gcol[a:] != ref.col[a:]))
+            row = r0 + int(np.searchsorted(ref.rowptr, j, side="right")) - 1
+            pytest.fail(f"[{res['label']}] column mismatch at row {row}: gpu {gcol[j]} "
+                        f"oracle {ref.col[j]}")
+        if first_bad >= 0:
+            j = a + first_bad
+            row = r0 + int(np.searchsorted(ref.rowptr, j, side="right")) - 1
+            pytest.fail(f"[{res['label']}] value outside the bound at row {row} col {gcol[j]}: "
+                        f"gpu {gval[j]!r} oracle {ref.val[j]!r} abssum {ref.abssum[j]!r}")
+
+
+CASES = [(name, k) for name in RUNS for k in range(PARTS[name])]
+
+
+@pytest.mark.parametrize("name,part", CASES, ids=[f"{n}-part{k}" for n, k in CASES])
+def test_large_every_row(name, part):
+    w = _workload_results(name)
+    A, B, u = w["A"], w["B"], w["u"]
+    for res in w["res"]:
+        st = res["st"]
+        assert st["numeric_path"] == res["path"], (res["label"], st["numeric_path"])
+        if res["nbatches"] == 1:
+            assert st["nbatches"] == 1, (res["label"], st["nbatches"])
+        else:
+            assert st["nbatches"] >= res["nbatches"], (res["label"], st["nbatches"])
+        assert st["sum_products"] == int(u.sum())
+        assert st["heavy_rows"] > 0
+        assert st["heavy_products"] == int(u[u > st["tau"]].sum())
+        rp = res["rp"]
+        assert rp[0] == 0 and rp[-1] == st["nnz_c"]
+    if part == 0:
+        # the results agree on C's size; the stats record's statistics hold
+        nnz = {r["st"]["nnz_c"] for r in w["res"]}
+        assert len(nnz) == 1, nnz
+        _check_structural_stats(w["res"][0]["st"], u)
+        if name == "rmat18_ef16":
+            # one batch of the page's dataflow holds more than 2^31 products
+            assert w["res"][1]["st"]["heavy_products"] > (1 << 31)
+        if name == "rmat20_ef8":
+            assert w["res"][0]["st"]["nnz_c"] > (1 << 31)
+    r0, r1 = _part_rows(w["cu"], PARTS[name], part)
+    nthr = _threads()
+    with cf.ThreadPoolExecutor(max_workers=nthr) as pool:
+        for a, b in _blocks(u, r0, r1):
+            ref = oracle.spgemm_rows(A, B, np.arange(a, b, dtype=np.int64), nthreads=nthr)
+            for res in w["res"]:
+                _compare_block(pool, res, ref, a, b)
+            del ref
+    if part == PARTS[name] - 1:
+        _cache.clear()
