@@ -55,7 +55,9 @@ typedef enum {
     SPGEMM_ERR_PLAN_MISMATCH = -6, /* numeric called with other shapes than symbolic */
     SPGEMM_ERR_HIP = -7,           /* a HIP runtime call failed                     */
     SPGEMM_ERR_NOT_READY = -8,     /* numeric called before a successful symbolic   */
-    SPGEMM_ERR_CAPACITY = -9       /* spgemm_multiply: C has more entries than room */
+    SPGEMM_ERR_CAPACITY = -9,      /* spgemm_multiply: C has more entries than room */
+    SPGEMM_ERR_SCRATCH_LIMIT = -10 /* spgemm_multiply_noalloc: the product needs more
+                                      workspace than its fixed scratch buffer holds */
 } spgemm_status;
 
 /* A CSR matrix (gMAGNUS page, Section II-A). `rowptr` has nrows+1 entries
@@ -226,6 +228,35 @@ SPGEMM_API int spgemm_numeric(spgemm_plan plan, const spgemm_csr* A, const spgem
 SPGEMM_API int spgemm_multiply(spgemm_plan plan, const spgemm_csr* A, const spgemm_csr* B,
                                int64_t* C_rowptr, int32_t* C_col, double* C_val,
                                int64_t capacity, int64_t* C_nnz, void* stream);
+
+/* Size of the fixed device scratch buffer of spgemm_multiply_noalloc. */
+#define SPGEMM_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Computes C = A * B as spgemm_multiply does on a fresh plan created with
+ * `opt` (NULL = defaults; timing and debug_dump must be 0, else
+ * INVALID_ARG), into the caller's C_rowptr (A.nrows+1 int64), C_col and
+ * C_val (`capacity` entries each), all device buffers. Every other piece of
+ * device memory the call needs comes from one buffer of
+ * SPGEMM_NOALLOC_SCRATCH_BYTES inside the library, which each device the
+ * library runs on holds from the first call until the process ends; no
+ * hipMalloc, hipFree or other device or pinned-host allocation is made (the
+ * host bookkeeping of the call uses the C++ heap). The light and heavy rows
+ * run on `stream` alone. Returns SCRATCH_LIMIT, with the outputs
+ * unspecified, when the product needs more workspace than the buffer holds,
+ * and CAPACITY, with C_rowptr and *C_nnz valid, when C does not fit
+ * `capacity` (call again with room for *C_nnz entries). Every call on a
+ * device shares that device's buffer and keeps the last call's contents
+ * there: calls that overlap on one device race, so the caller orders them
+ * (one stream, or a wait for the previous call's stream) and makes them
+ * from one host thread at a time. Blocks until *C_nnz is known; the numeric
+ * part is asynchronous on `stream`. Errors: those of spgemm_multiply (but
+ * never OUT_OF_MEMORY), SCRATCH_LIMIT. */
+SPGEMM_API int spgemm_multiply_noalloc(const spgemm_options* opt, const spgemm_csr* A,
+                                       const spgemm_csr* B, int64_t* C_rowptr, int32_t* C_col,
+                                       double* C_val, int64_t capacity, int64_t* C_nnz,
+                                       void* stream);
 
 /* Copy the statistics of the last symbolic + numeric pair into *out
  * (synchronises on pending timing events). Errors: INVALID_ARG. */

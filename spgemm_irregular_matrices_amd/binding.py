@@ -21,15 +21,17 @@ STATUS = {
     0: "SPGEMM_OK", -1: "SPGEMM_ERR_INVALID_ARG", -2: "SPGEMM_ERR_DIM_MISMATCH",
     -3: "SPGEMM_ERR_INDEX_RANGE", -4: "SPGEMM_ERR_OVERFLOW", -5: "SPGEMM_ERR_OUT_OF_MEMORY",
     -6: "SPGEMM_ERR_PLAN_MISMATCH", -7: "SPGEMM_ERR_HIP", -8: "SPGEMM_ERR_NOT_READY",
-    -9: "SPGEMM_ERR_CAPACITY",
+    -9: "SPGEMM_ERR_CAPACITY", -10: "SPGEMM_ERR_SCRATCH_LIMIT",
 }
 CAPACITY = -9
+SCRATCH_LIMIT = -10
+NOALLOC_SCRATCH_BYTES = 64 << 20
 PHASES = ["validate", "inter_prod_size", "binning", "csr_to_csc", "outer_prod", "histo",
           "multisplit", "heavy_accum", "light_accum", "prefix_sum", "direct_dense", "direct_rank"]
 MAX_LEVELS = 8
 EXPORTS = ["spgemm_options_default", "spgemm_plan_create", "spgemm_plan_destroy",
            "spgemm_symbolic", "spgemm_numeric", "spgemm_multiply", "spgemm_plan_stats",
-           "spgemm_plan_debug", "spgemm_status_string"]
+           "spgemm_plan_debug", "spgemm_status_string", "spgemm_multiply_noalloc"]
 
 
 class SpgemmError(RuntimeError):
@@ -115,6 +117,11 @@ def load():
         lib.spgemm_plan_stats.restype = ctypes.c_int
         lib.spgemm_plan_debug.argtypes = [P, ctypes.c_int, ctypes.POINTER(DebugMatrix)]
         lib.spgemm_plan_debug.restype = ctypes.c_int
+        lib.spgemm_multiply_noalloc.argtypes = [ctypes.POINTER(Options), ctypes.POINTER(CSRStruct),
+                                                ctypes.POINTER(CSRStruct), ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                                ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p]
+        lib.spgemm_multiply_noalloc.restype = ctypes.c_int
         lib.spgemm_status_string.argtypes = [ctypes.c_int]
         lib.spgemm_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -172,6 +179,26 @@ def _stream_handle(stream) -> int | None:
     return stream.cuda_stream or None
 
 
+def make_options(tau_override=0, chunk_width_override=0, nchunks_cap=0, lds_budget_bytes=0,
+                 validate_inputs=True, debug_dump=False, timing=False, max_batch_products=0,
+                 symbolic_mode=0, numeric_mode=0, workspace_limit_bytes=0) -> Options:
+    """An spgemm_options record: the library's defaults with these fields set."""
+    o = Options()
+    load().spgemm_options_default(ctypes.byref(o))
+    o.tau_override = tau_override
+    o.chunk_width_override = chunk_width_override
+    o.nchunks_cap = nchunks_cap
+    o.lds_budget_bytes = lds_budget_bytes
+    o.validate_inputs = 1 if validate_inputs else 0
+    o.debug_dump = 1 if debug_dump else 0
+    o.timing = 1 if timing else 0
+    o.max_batch_products = max_batch_products
+    o.symbolic_mode = symbolic_mode
+    o.numeric_mode = numeric_mode
+    o.workspace_limit_bytes = workspace_limit_bytes
+    return o
+
+
 class Plan:
     """An spgemm plan: owns device workspace and the symbolic structure."""
 
@@ -179,19 +206,11 @@ class Plan:
                  validate_inputs=True, debug_dump=False, timing=False, max_batch_products=0,
                  symbolic_mode=0, numeric_mode=0, workspace_limit_bytes=0):
         lib = load()
-        o = Options()
-        lib.spgemm_options_default(ctypes.byref(o))
-        o.tau_override = tau_override
-        o.chunk_width_override = chunk_width_override
-        o.nchunks_cap = nchunks_cap
-        o.lds_budget_bytes = lds_budget_bytes
-        o.validate_inputs = 1 if validate_inputs else 0
-        o.debug_dump = 1 if debug_dump else 0
-        o.timing = 1 if timing else 0
-        o.max_batch_products = max_batch_products
-        o.symbolic_mode = symbolic_mode
-        o.numeric_mode = numeric_mode
-        o.workspace_limit_bytes = workspace_limit_bytes
+        o = make_options(tau_override=tau_override, chunk_width_override=chunk_width_override,
+                         nchunks_cap=nchunks_cap, lds_budget_bytes=lds_budget_bytes,
+                         validate_inputs=validate_inputs, debug_dump=debug_dump, timing=timing,
+                         max_batch_products=max_batch_products, symbolic_mode=symbolic_mode,
+                         numeric_mode=numeric_mode, workspace_limit_bytes=workspace_limit_bytes)
         h = ctypes.c_void_p()
         _check(lib.spgemm_plan_create(ctypes.byref(h), ctypes.byref(o)), "spgemm_plan_create")
         self._h = h
@@ -302,6 +321,22 @@ class Plan:
             "row_key": grab(m.row_key, n, torch.int64),
             "chunk_width": int(m.chunk_width),
         }
+
+
+def multiply_noalloc(A: DeviceCSR, B: DeviceCSR, C_rowptr, C_col, C_val, stream=None,
+                     **options) -> int:
+    """spgemm_multiply_noalloc into caller-allocated C buffers (capacity = C_col's
+    length); returns nnz(C). Raises SpgemmError (CAPACITY too, with C_rowptr valid)."""
+    lib = load()
+    o = make_options(**options)
+    nnz = ctypes.c_int64(0)
+    sa, sb = A.struct(), B.struct()
+    rc = lib.spgemm_multiply_noalloc(ctypes.byref(o), ctypes.byref(sa), ctypes.byref(sb),
+                                     C_rowptr.data_ptr(), _ptr(C_col), _ptr(C_val),
+                                     int(C_col.numel()), ctypes.byref(nnz),
+                                     _stream_handle(stream))
+    _check(rc, "spgemm_multiply_noalloc")
+    return int(nnz.value)
 
 
 def _hip_copy(dst_tensor, src_ptr: int, nbytes: int):

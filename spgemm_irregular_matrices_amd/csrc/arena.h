@@ -21,11 +21,33 @@ class Arena {
     // pass it fails as if the device had no more memory.
     void set_limit(size_t bytes) { limit_ = bytes; }
 
+    // Carve every buffer out of the device range [base, base + bytes)
+    // instead of allocating: while a region is set the arena calls neither
+    // hipMalloc nor hipFree. Buffers are laid out one after the other in
+    // the order they are first asked for; a buffer asked for again with more
+    // room moves to the end (its contents are not kept, as when a heap
+    // buffer grows), and release() forgets them all.
+    void use_region(void* base, size_t bytes) {
+        release();
+        region_ = static_cast<char*>(base);
+        region_cap_ = bytes;
+    }
+
     // Device buffer `name` with room for at least `bytes`. Growing frees the
     // old buffer (hipFree waits for the device, so no kernel still uses it).
     void* get(const std::string& name, size_t bytes) {
         Buf& b = bufs_[name];
         if (bytes == 0) bytes = 1;
+        if (region_ && b.cap < bytes) {
+            const size_t off = (total_ + 255) & ~size_t(255);
+            const size_t cap = (bytes + 255) & ~size_t(255);
+            if (off > region_cap_ || cap > region_cap_ - off)
+                throw ScratchError("workspace '" + name + "' (" + std::to_string(bytes) +
+                                   " bytes) does not fit the fixed scratch buffer");
+            b.p = region_ + off;
+            b.cap = cap;
+            total_ = off + cap;
+        }
         if (b.cap < bytes) {
             if (b.p) {
                 (void)hipFree(b.p);
@@ -66,8 +88,9 @@ class Arena {
     size_t total_bytes() const { return total_; }
 
     void release() {
-        for (auto& kv : bufs_)
-            if (kv.second.p) (void)hipFree(kv.second.p);
+        if (!region_)
+            for (auto& kv : bufs_)
+                if (kv.second.p) (void)hipFree(kv.second.p);
         bufs_.clear();
         total_ = 0;
     }
@@ -78,8 +101,10 @@ class Arena {
         size_t cap = 0;
     };
     std::unordered_map<std::string, Buf> bufs_;
-    size_t total_ = 0;
+    size_t total_ = 0;  // bytes held (with a region: the end of its last buffer)
     size_t limit_ = 0;
+    char* region_ = nullptr;
+    size_t region_cap_ = 0;
 };
 
 }  // namespace sg

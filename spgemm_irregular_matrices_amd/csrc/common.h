@@ -25,6 +25,11 @@ struct OomError : std::runtime_error {
 struct OverflowError : std::runtime_error {
     using std::runtime_error::runtime_error;
 };
+// A call without allocation needs more workspace than its fixed scratch
+// buffer holds; carried as SPGEMM_ERR_SCRATCH_LIMIT.
+struct ScratchError : std::runtime_error {
+    using std::runtime_error::runtime_error;
+};
 
 #define SG_HIP(call)                                                              \
     do {                                                                          \

@@ -14,9 +14,10 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
-#include <cmath>
 
 #include "../../include/spgemm.h"
 #include "kernels.h"
@@ -944,7 +945,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
     ri.Cval = C_val;
     // light rows on the plan's second stream when there are heavy rows to
     // overlap with; the caller's stream waits for them on every way out
-    const bool fork = p->H > 0 && p->row_bins[RB_H8192 + 1] > p->row_bins[RB_T8];
+    const bool fork = p->lst != nullptr && p->H > 0 && p->row_bins[RB_H8192 + 1] > p->row_bins[RB_T8];
     // Armed as soon as the side stream has forked: whatever was queued on
     // it, also when a later launch throws, is waited for by the caller's
     // stream when this function returns.
@@ -1125,6 +1126,8 @@ int guarded(F&& f) {
         return SPGEMM_ERR_OUT_OF_MEMORY;
     } catch (const OverflowError&) {
         return SPGEMM_ERR_OVERFLOW;
+    } catch (const ScratchError&) {
+        return SPGEMM_ERR_SCRATCH_LIMIT;
     } catch (const HipError& e) {
         if (e.code == hipErrorOutOfMemory) return SPGEMM_ERR_OUT_OF_MEMORY;
         return SPGEMM_ERR_HIP;
@@ -1147,6 +1150,64 @@ int release_on_oom(spgemm_plan p, int rc) {
     return rc;
 }
 
+bool options_valid(const spgemm_options& o) {
+    if (o.lds_budget_bytes < 0 || o.tau_override < 0 || o.chunk_width_override < 0 ||
+        o.nchunks_cap < 0 || o.max_batch_products < 0 || o.workspace_limit_bytes < 0)
+        return false;
+    if (o.symbolic_mode < 0 || o.symbolic_mode > 2 || o.numeric_mode < 0 || o.numeric_mode > 3)
+        return false;
+    if (o.chunk_width_override > 0 &&
+        (o.chunk_width_override < 32 || (o.chunk_width_override & (o.chunk_width_override - 1))))
+        return false;
+    if (o.nchunks_cap > 0 && (o.nchunks_cap < 2 || (o.nchunks_cap & (o.nchunks_cap - 1))))
+        return false;
+    return true;
+}
+
+// ---------------------------------------------------------------- allocation-free calls
+// The device scratch of spgemm_multiply_noalloc. In host code this name is
+// only a stand-in for the symbol: its device address, which differs per
+// device, comes from hipGetSymbolAddress once per device and is the only
+// form host code passes on.
+static __device__ __align__(256) unsigned char scratch[SPGEMM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kNoallocDevices = 64;
+
+// Per device: the scratch address and the plan state that lives on it.
+struct NoallocDevice {
+    std::mutex mu;            // one host thread at a time in a device's call
+    bool ready = false;
+    void* ptr = nullptr;      // device address of `scratch` on this device
+    spgemm_plan_s plan;       // its arena carves buffers out of ptr
+    int64_t host[kHostWords]; // staging for the plan's small device-to-host reads
+};
+
+NoallocDevice g_noalloc[kNoallocDevices];
+
+// Set-up on the first call on the current device: the scratch address (with
+// the device current) and the plan's device properties; no stream, event or
+// memory is created.
+int noalloc_setup(NoallocDevice& d, int device) {
+    if (d.ready) return SPGEMM_OK;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+        (void)hipGetLastError();
+        return SPGEMM_ERR_HIP;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return SPGEMM_ERR_HIP;
+    d.ptr = ptr;
+    spgemm_plan_s& p = d.plan;
+    p.device = device;
+    p.dev_lds = (int64_t)prop.sharedMemPerBlock;
+    p.dev_cus = std::max(1, prop.multiProcessorCount);
+    p.host = d.host;
+    p.lst = nullptr;  // the light rows run on the caller's stream
+    p.ar.use_region(d.ptr, (size_t)SPGEMM_NOALLOC_SCRATCH_BYTES);
+    d.ready = true;
+    return SPGEMM_OK;
+}
+
 }  // namespace
 
 // ============================================================================
@@ -1166,16 +1227,7 @@ SPGEMM_API int spgemm_plan_create(spgemm_plan* out, const spgemm_options* opt) {
     spgemm_options o;
     spgemm_options_default(&o);
     if (opt) o = *opt;
-    if (o.lds_budget_bytes < 0 || o.tau_override < 0 || o.chunk_width_override < 0 ||
-        o.nchunks_cap < 0 || o.max_batch_products < 0 || o.workspace_limit_bytes < 0)
-        return SPGEMM_ERR_INVALID_ARG;
-    if (o.symbolic_mode < 0 || o.symbolic_mode > 2 || o.numeric_mode < 0 || o.numeric_mode > 3)
-        return SPGEMM_ERR_INVALID_ARG;
-    if (o.chunk_width_override > 0 &&
-        (o.chunk_width_override < 32 || (o.chunk_width_override & (o.chunk_width_override - 1))))
-        return SPGEMM_ERR_INVALID_ARG;
-    if (o.nchunks_cap > 0 && (o.nchunks_cap < 2 || (o.nchunks_cap & (o.nchunks_cap - 1))))
-        return SPGEMM_ERR_INVALID_ARG;
+    if (!options_valid(o)) return SPGEMM_ERR_INVALID_ARG;
     return guarded([&]() -> int {
         auto* p = new spgemm_plan_s();
         p->opt = o;
@@ -1275,6 +1327,30 @@ SPGEMM_API int spgemm_multiply(spgemm_plan p, const spgemm_csr* A, const spgemm_
     return spgemm_numeric(p, A, B, C_rowptr, C_col, C_val, stream);
 }
 
+SPGEMM_API int spgemm_multiply_noalloc(const spgemm_options* opt, const spgemm_csr* A,
+                                       const spgemm_csr* B, int64_t* C_rowptr, int32_t* C_col,
+                                       double* C_val, int64_t capacity, int64_t* C_nnz,
+                                       void* stream) {
+    if (!C_rowptr || !C_nnz || capacity < 0) return SPGEMM_ERR_INVALID_ARG;
+    spgemm_options o;
+    spgemm_options_default(&o);
+    if (opt) o = *opt;
+    if (!options_valid(o) || o.timing || o.debug_dump) return SPGEMM_ERR_INVALID_ARG;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return SPGEMM_ERR_HIP;
+    if (device < 0 || device >= kNoallocDevices) return SPGEMM_ERR_HIP;
+    NoallocDevice& d = g_noalloc[device];
+    std::lock_guard<std::mutex> lock(d.mu);
+    int rc = noalloc_setup(d, device);
+    if (rc != SPGEMM_OK) return rc;
+    spgemm_plan p = &d.plan;
+    p->opt = o;
+    p->opt.workspace_limit_bytes = 0;
+    p->ready = false;
+    p->ar.release();  // a fresh layout inside the scratch for this call
+    return spgemm_multiply(p, A, B, C_rowptr, C_col, C_val, capacity, C_nnz, stream);
+}
+
 SPGEMM_API int spgemm_plan_stats(spgemm_plan p, spgemm_stats* out) {
     if (!p || !out) return SPGEMM_ERR_INVALID_ARG;
     return guarded([&]() -> int {
@@ -1345,6 +1421,8 @@ SPGEMM_API const char* spgemm_status_string(int status) {
         case SPGEMM_ERR_HIP: return "HIP runtime error";
         case SPGEMM_ERR_NOT_READY: return "numeric called before a successful symbolic";
         case SPGEMM_ERR_CAPACITY: return "C has more entries than the room given";
+        case SPGEMM_ERR_SCRATCH_LIMIT:
+            return "product needs more workspace than the fixed scratch buffer holds";
         default: return "unknown status";
     }
 }
