@@ -91,6 +91,10 @@ def load():
     """Load the built library (raises if it is missing)."""
     global _lib
     if _lib is None:
+        # torch ships its own HIP runtime (same soname as ROCm's): load it
+        # first, so that the library binds to it rather than bringing a
+        # second runtime into the process beside torch's
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"HIP library not built: {LIB_PATH} is missing "
                               "(run __graft_entry__.build())")
@@ -342,7 +346,8 @@ def multiply_noalloc(A: DeviceCSR, B: DeviceCSR, C_rowptr, C_col, C_val, stream=
 def _hip_copy(dst_tensor, src_ptr: int, nbytes: int):
     """Device-to-device copy from a raw library pointer into a torch tensor."""
     import torch
-    hip = ctypes.CDLL("libamdhip64.so")
+    import torch  # noqa: F401  (its HIP runtime is the one already loaded)
+    hip = ctypes.CDLL("libamdhip64.so.7")  # by soname: the runtime already in the process
     hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
     hip.hipMemcpy.restype = ctypes.c_int
     rc = hip.hipMemcpy(dst_tensor.data_ptr(), src_ptr, nbytes, 3)  # hipMemcpyDeviceToDevice

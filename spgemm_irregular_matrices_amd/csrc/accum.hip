@@ -292,6 +292,85 @@ static void launch_thread(const RowItems& ri, int64_t p0, int64_t n, hipStream_t
 }
 
 // ---------------------------------------------------------------- hash
+// Output of a hash row without a sort. The row's distinct columns (nnz of
+// them, in the SPT table slots each thread holds in registers; empty slots
+// hold ~0) are ranked through a two-level bitmap: bucket b = column / 64 is
+// one bit of a top bitmap over the column range (tww words); a prefix of the
+// top words' popcounts numbers the nonempty buckets in column order; each
+// nonempty bucket has a 64-bit mask of its columns, and a prefix of the
+// masks' popcounts gives every bucket its first rank. A column's rank is its
+// bucket's first rank plus the columns below it in its mask, so it is
+// written straight to its place in the row. Uses 12 * nnz + 8 * tww bytes of
+// LDS at `lds` (the caller's table, free once read into registers).
+template <int TW, int SPT>
+__device__ __forceinline__ void emit_ranked(const uint32_t (&kk)[SPT], const double (&vv)[SPT],
+                                            int nnz, int tww, int64_t* lds, int* red_sh,
+                                            int32_t* oc, double* ov) {
+    const int tt = threadIdx.x;
+    uint64_t* bm = (uint64_t*)lds;           // nnz bucket masks
+    int* bpre = (int*)(bm + nnz);            // nnz first ranks
+    uint32_t* top = (uint32_t*)(bpre + nnz); // tww words: one bit per bucket
+    int* tpre = (int*)(top + tww);           // tww word prefixes
+    for (int w = tt; w < tww; w += TW) top[w] = 0u;
+    for (int c = tt; c < nnz; c += TW) bm[c] = 0ull;
+    team_sync<TW>();
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        if (kk[j] != 0xffffffffu) {
+            const uint32_t b = kk[j] >> 6;
+            atomicOr(&top[b >> 5], 1u << (b & 31));
+        }
+    }
+    team_sync<TW>();
+    // nonempty buckets before each top word (thread tt sums a run of words)
+    int tot;
+    {
+        const int per = (tww + TW - 1) / TW;
+        const int w0 = min(tww, tt * per), w1 = min(tww, w0 + per);
+        int pc = 0;
+        for (int w = w0; w < w1; ++w) pc += __popc(top[w]);
+        int pre = team_exclusive_scan<TW>(pc, red_sh, &tot);
+        for (int w = w0; w < w1; ++w) {
+            tpre[w] = pre;
+            pre += __popc(top[w]);
+        }
+    }
+    team_sync<TW>();
+    int cb[SPT];
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        cb[j] = -1;
+        if (kk[j] != 0xffffffffu) {
+            const uint32_t b = kk[j] >> 6, w = b >> 5;
+            cb[j] = tpre[w] + __popc(top[w] & ((1u << (b & 31)) - 1u));
+            atomicOr((unsigned long long*)&bm[cb[j]], 1ull << (kk[j] & 63));
+        }
+    }
+    team_sync<TW>();
+    // first rank of every nonempty bucket (tot <= nnz of them)
+    {
+        const int per = (tot + TW - 1) / TW;
+        const int c0 = min(tot, tt * per), c1 = min(tot, c0 + per);
+        int pc = 0;
+        for (int c = c0; c < c1; ++c) pc += __popcll(bm[c]);
+        int all;
+        int pre = team_exclusive_scan<TW>(pc, red_sh, &all);
+        for (int c = c0; c < c1; ++c) {
+            bpre[c] = pre;
+            pre += __popcll(bm[c]);
+        }
+    }
+    team_sync<TW>();
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        if (cb[j] >= 0) {
+            const int r = bpre[cb[j]] + __popcll(bm[cb[j]] & ((1ull << (kk[j] & 63)) - 1ull));
+            oc[r] = (int32_t)kk[j];
+            ov[r] = vv[j];
+        }
+    }
+}
+
 // One item per work group of TW threads; the table has S = 2^LOGS slots.
 template <int MODE, bool NUM, int TW, int LOGS>
 __global__ __launch_bounds__(TW) void k_acc_hash(RowItems ri, ChunkItems ci, int64_t p0,
@@ -348,7 +427,6 @@ __global__ __launch_bounds__(TW) void k_acc_hash(RowItems ri, ChunkItems ci, int
         if (tt == 0) write_count<MODE>(ri, ci, h, nnz);
         return;
     } else {
-        // compact the occupied slots to the front, in slot order
         __syncthreads();
         uint32_t kk[SPT];
         double vv[SPT];
@@ -359,6 +437,19 @@ __global__ __launch_bounds__(TW) void k_acc_hash(RowItems ri, ChunkItems ci, int
             vv[j] = vals[tt * SPT + j];
             occ += kk[j] != 0xffffffffu;
         }
+        if constexpr (MODE == MODE_ROW) {
+            // a row's columns lie in [0, B.ncols): when the two-level bitmap
+            // over that range fits the table's LDS, rank without a sort
+            const int tww = (int)((ri.B.m + 2047) >> 11);
+            if (8 * (int64_t)tww + 12 * (int64_t)nnz <= 12 * (int64_t)S) {
+                __syncthreads();  // the table is in registers: its LDS is reused
+                const int64_t off = out_offset<MODE>(ri, ci, h);
+                emit_ranked<TW, SPT>(kk, vv, nnz, tww, lds_a, red_sh, out_cols<MODE>(ri, ci) + off,
+                                     out_vals<MODE>(ri, ci) + off);
+                return;
+            }
+        }
+        // compact the occupied slots to the front, in slot order
         int tot;
         int pre = team_exclusive_scan<TW>(occ, red_sh, &tot);
         __syncthreads();

@@ -74,6 +74,12 @@ void brow_minmax(const DevCSR& B, int32_t* bmin, int32_t* bmax, hipStream_t st);
 // with u <= 512, 4096, 32768, [7]=sum of u^2 (a double); uhist counts the
 // rows per u bucket (kUHistBuckets: u < 64 exactly, then 64 per octave).
 constexpr int kUHistBuckets = 4096;
+// Entries of the row statistics record classify_rows fills: sum, max, heavy
+// rows and products of u(i), the F_h counts, the sum of u(i)^2, the A
+// entries of the light rows, and one word for the light rows' outputs.
+constexpr int kRowStats = 10;
+// out[0] = sum over j < n of cnt[perm[j]].
+void sum_rows(const int32_t* perm, int64_t n, const int64_t* cnt, int64_t* out, hipStream_t st);
 void classify_rows(const DevCSR& A, const int64_t* S, const int32_t* bmin, const int32_t* bmax,
                    int64_t tau, int32_t* rowlo, int32_t* perm, int64_t* bin_start,
                    int64_t* stats, int32_t* uhist, Arena& ar, hipStream_t st);

@@ -120,6 +120,8 @@ struct spgemm_plan_s {
     int64_t direct_W = 0;    // their width
     int64_t dir_bins[DC_COUNT + 1] = {};
     int64_t dir_tot[6] = {};  // dense / rank items: products, outputs, A entries read
+    int64_t light_annz = 0;   // A entries of the light rows
+    int64_t light_cnnz = 0;   // output entries of the light rows
     // debug dumps (kept for single-batch products)
     bool dbg_valid = false;
     bool dbg_chat = false;  // C-hat was dumped (separate outer product only)
@@ -658,7 +660,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     int32_t* rowlo = ar.get<int32_t>("rowlo", (size_t)n + 1);
     int32_t* rowperm = ar.get<int32_t>("rowperm", (size_t)n + 1);
     int64_t* rowbins = ar.get<int64_t>("rowbins", RB_COUNT + 1);
-    int64_t* st4 = ar.get<int64_t>("stats4", 8);
+    int64_t* st4 = ar.get<int64_t>("stats4", kRowStats);
     int32_t* uhist = ar.get<int32_t>("uhist", kUHistBuckets);
     {
         PhaseScope ps(p, 0, SPGEMM_PHASE_BINNING, st);
@@ -672,7 +674,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     {
         SG_HIP(hipMemcpyAsync(p->host, rowbins, (RB_COUNT + 1) * sizeof(int64_t),
                               hipMemcpyDeviceToHost, st));
-        SG_HIP(hipMemcpyAsync(p->host + 16, st4, 8 * sizeof(int64_t), hipMemcpyDeviceToHost, st));
+        SG_HIP(hipMemcpyAsync(p->host + 16, st4, 9 * sizeof(int64_t), hipMemcpyDeviceToHost, st));
         int32_t* hist = (int32_t*)(p->host + 64);
         SG_HIP(hipMemcpyAsync(hist, uhist, kUHistBuckets * sizeof(int32_t),
                               hipMemcpyDeviceToHost, st));
@@ -682,6 +684,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
         p->stats.max_products = p->host[17];
         p->stats.heavy_rows = p->host[18];
         p->stats.heavy_products = p->host[19];
+        p->light_annz = p->host[24];
         row_statistics(p, n, hist);
     }
     p->H = p->row_bins[RB_HEAVY + 1] - p->row_bins[RB_HEAVY];
@@ -704,6 +707,13 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
         PhaseScope ps(p, 0, SPGEMM_PHASE_LIGHT_ACCUM, st);
         for (int b = RB_T8; b <= RB_H8192; ++b)
             accumulate_rows(ri, b, p->row_bins[b], p->row_bins[b + 1] - p->row_bins[b], false, st);
+        // per light row: its A and C row pointers and bin entry (28 B); per A
+        // entry: column and B row bounds (20 B); per product: its B column
+        const int64_t nl = p->row_bins[RB_H8192 + 1] - p->row_bins[RB_T8];
+        add_bytes(p, 0, SPGEMM_PHASE_LIGHT_ACCUM,
+                  28.0 * nl + 20.0 * p->light_annz +
+                      4.0 * (p->stats.sum_products - p->stats.heavy_products));
+        sum_rows(rowperm + p->row_bins[RB_T8], nl, cnt_row, st4 + 9, st);
     }
 
     // heavy rows (Algorithm 3, the heavy-row branch), batch by batch
@@ -874,6 +884,8 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
         add_bytes(p, 0, SPGEMM_PHASE_PREFIX_SUM, 16.0 * n);
     }
     int64_t nnz_c = 0;
+    // the light rows' output entries, read back with nnz(C)
+    SG_HIP(hipMemcpyAsync(p->host + 40, st4 + 9, sizeof(int64_t), hipMemcpyDeviceToHost, st));
     if (p->direct) {
         // nnz(C) and the direct path's class starts and totals in one wait
         constexpr int kMeta = DC_COUNT + 1 + 6 + 1;
@@ -899,6 +911,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
                        ar.get<int64_t>("dist_fin", (size_t)(p->H * p->direct_req)),
                        ar.get<int64_t>("doff", (size_t)(p->H * p->direct_req)), st);
     }
+    p->light_cnnz = p->host[40];
     p->stats.numeric_path = p->H == 0 ? 0 : (p->direct ? 3 : (p->fused_num ? 1 : 2));
     p->stats.nrows = n;
     p->stats.ncols_c = B.m;
@@ -967,6 +980,13 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         PhaseScope ps(p, 1, SPGEMM_PHASE_LIGHT_ACCUM, lst);
         for (int b = RB_T8; b <= RB_H8192; ++b)
             accumulate_rows(ri, b, p->row_bins[b], p->row_bins[b + 1] - p->row_bins[b], true, lst);
+        // per light row: A and C row pointers and bin entry (28 B); per A
+        // entry: column, value and B row bounds (28 B); per product: its B
+        // column and value (12 B); per output entry: column and value (12 B)
+        const int64_t nl = p->row_bins[RB_H8192 + 1] - p->row_bins[RB_T8];
+        add_bytes(p, 1, SPGEMM_PHASE_LIGHT_ACCUM,
+                  28.0 * nl + 28.0 * p->light_annz + 12.0 * p->stats.light_products +
+                      12.0 * p->light_cnnz);
     }
     if (p->H == 0) return;
 

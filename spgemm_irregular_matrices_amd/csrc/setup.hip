@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
     __shared__ int hsmall[64];  // the exact buckets u < 64, gathered per block
     if (threadIdx.x < 64) hsmall[threadIdx.x] = 0;
     __syncthreads();
-    int64_t su = 0, heavy = 0, hprod = 0, c512 = 0, c4k = 0, c32k = 0, mu = 0;
+    int64_t su = 0, heavy = 0, hprod = 0, c512 = 0, c4k = 0, c32k = 0, mu = 0, alight = 0;
     double u2 = 0.0;
     for (int64_t base = (int64_t)blockIdx.x * 256; base < n; base += (int64_t)gridDim.x * 256) {
         const int64_t i = base + threadIdx.x;
@@ -168,7 +168,9 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
                 hprod += u;
             } else if (u <= kThreadMaxItems[2]) {
                 b = u <= kThreadMaxItems[0] ? RB_T8 : (u <= kThreadMaxItems[1] ? RB_T16 : RB_T32);
+                alight += a1 - a0;
             } else {
+                alight += a1 - a0;
                 int32_t lo = 0x7fffffff, hi = -1;
                 for (int64_t q = a0; q < a1; ++q) {
                     const int32_t k = acol[q];
@@ -224,6 +226,7 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
     c4k = block_reduce_sum<256>(c4k, sh);
     c32k = block_reduce_sum<256>(c32k, sh);
     u2 = block_reduce_sum<256>(u2, shd);
+    alight = block_reduce_sum<256>(alight, sh);
     // block_reduce_sum ends with a barrier: every wave's LDS histogram adds are in
     if (threadIdx.x < 64 && hsmall[threadIdx.x]) atomicAdd(&uhist[threadIdx.x], hsmall[threadIdx.x]);
 #pragma unroll
@@ -241,7 +244,29 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
         atomicAdd((unsigned long long*)&stats[5], (unsigned long long)c4k);
         atomicAdd((unsigned long long*)&stats[6], (unsigned long long)c32k);
         atomicAdd((double*)&stats[7], u2);
+        atomicAdd((unsigned long long*)&stats[8], (unsigned long long)alight);
     }
+}
+
+// Sum of cnt[perm[j]] over j < n, added into *out (the light rows' output
+// entries, for the light path's algorithmic bytes).
+__global__ __launch_bounds__(256) void k_sum_rows(const int32_t* perm, int64_t n,
+                                                  const int64_t* cnt, int64_t* out) {
+    __shared__ int64_t sh[8];
+    int64_t s = 0;
+    for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < n;
+         j += (int64_t)gridDim.x * 256)
+        s += cnt[perm[j]];
+    s = block_reduce_sum<256>(s, sh);
+    if (threadIdx.x == 0 && s) atomicAdd((unsigned long long*)out, (unsigned long long)s);
+}
+
+void sum_rows(const int32_t* perm, int64_t n, const int64_t* cnt, int64_t* out, hipStream_t st) {
+    fill<int64_t>(out, 1, 0, st);
+    if (n <= 0) return;
+    hipLaunchKernelGGL(k_sum_rows, dim3(grid_1d(std::min<int64_t>(ceil_div(n, 256), 256))),
+                       dim3(256), 0, st, perm, n, cnt, out);
+    SG_LAUNCH_CHECK();
 }
 
 struct RowBinOf {
@@ -253,7 +278,7 @@ void classify_rows(const DevCSR& A, const int64_t* S, const int32_t* bmin, const
                    int64_t tau, int32_t* rowlo, int32_t* perm, int64_t* bin_start,
                    int64_t* stats, int32_t* uhist, Arena& ar, hipStream_t st) {
     uint8_t* bin = ar.get<uint8_t>("row_bin", (size_t)A.n + 1);
-    fill<int64_t>(stats, 8, 0, st);
+    fill<int64_t>(stats, kRowStats, 0, st);
     fill<int32_t>(uhist, kUHistBuckets, 0, st);
     if (A.n > 0) {
         hipLaunchKernelGGL(k_classify_rows,

@@ -727,3 +727,18 @@ def test_every_multisplit_level_matches_oracle(numeric_mode, width, cap, nlevels
     assert all(lv["val"] is not None for lv in levels)
     _check_levels_against_oracle(A, B, tau, chat, levels)
     compare(A, B, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy())
+
+
+@pytest.mark.parametrize("ncols", [1 << 12, 1 << 20, 1 << 24])
+def test_light_hash_rows_wide_columns(ncols):
+    """Light rows whose columns spread over the whole range take the hash bins.
+    Up to about 6 M columns their output is ranked through the two-level
+    bitmap (no sort); at 2^24 columns the bitmap does not fit next to the
+    table and the rows are sorted instead. Both against the oracle."""
+    A = synth.random_csr(3000, 2000, seed=161, value_seed=162, mean_len=12, skew=1.2)
+    B = synth.random_csr(2000, ncols, seed=163, value_seed=164, mean_len=40, skew=1.1)
+    rp, col, val, st = run_gpu(A, B)
+    u = oracle.row_products(A, B)
+    assert st["heavy_rows"] == int(np.count_nonzero(u > st["tau"]))
+    assert np.count_nonzero((u > 64) & (u <= st["tau"])) > 100  # hash-bin rows
+    compare(A, B, rp, col, val)
