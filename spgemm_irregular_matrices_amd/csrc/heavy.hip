@@ -1156,6 +1156,71 @@ __global__ __launch_bounds__(kHsymNT) void k_hsym_finalize(const int64_t* off, i
     for (int sl = tt; sl < req; sl += kHsymNT) dist_fin[h * req + sl] = dsl_f[sl];
 }
 
+// Column parts of B for a symbolic pass taken in np column parts: B's
+// entries in part-major order (every row's entries of part 0, row by row,
+// then part 1, ...; a row's order is kept inside a part), and the start of
+// every (part, row) segment, so that the launch of part p reads only the
+// columns it keeps instead of every product of the row. One wavefront per B
+// row, its parts ranked by peeling as in k_bslot_rows; part of column c is
+// c >> shift.
+constexpr int kBpartNT = 256;
+
+__global__ __launch_bounds__(kBpartNT) void k_bpart_count(const int64_t* brp,
+                                                          const int32_t* bcol, int64_t nb,
+                                                          int shift, int np, int64_t* cnt) {
+    extern __shared__ int lds_p[];
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    int* c = lds_p + w * np;
+    const int64_t k = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    if (k >= nb) return;  // whole waves leave together; no block barrier below
+    for (int p = lane; p < np; p += kWave) c[p] = 0;
+    const int64_t e0 = brp[k], e1 = brp[k + 1];
+    for (int64_t eb = e0; eb < e1; eb += kWave) {
+        const int64_t e = eb + lane;
+        const int pt = e < e1 ? (int)((uint32_t)bcol[e] >> shift) : -1;
+        uint64_t act = __ballot(pt >= 0);
+        while (act) {
+            const int leader = __builtin_ctzll(act);
+            const int lp = __builtin_amdgcn_readlane(pt, leader);
+            const uint64_t m = __ballot(pt == lp);
+            if (lane == leader) c[lp] += __popcll(m);
+            act &= ~m;
+        }
+    }
+    for (int p = lane; p < np; p += kWave) cnt[(int64_t)p * nb + k] = c[p];
+}
+
+// ppos: exclusive scan of the part-major counts (np * nb + 1 values).
+__global__ __launch_bounds__(kBpartNT) void k_bpart_scatter(const int64_t* brp,
+                                                            const int32_t* bcol, int64_t nb,
+                                                            int shift, int np,
+                                                            const int64_t* ppos, int32_t* pcol) {
+    extern __shared__ int lds_p[];
+    const int w = threadIdx.x / kWave, lane = lane_id();
+    int* run = lds_p + w * np;
+    const int64_t k = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    if (k >= nb) return;
+    for (int p = lane; p < np; p += kWave) run[p] = 0;
+    const int64_t e0 = brp[k], e1 = brp[k + 1];
+    for (int64_t eb = e0; eb < e1; eb += kWave) {
+        const int64_t e = eb + lane;
+        const int32_t col = e < e1 ? bcol[e] : 0;
+        const int pt = e < e1 ? (int)((uint32_t)col >> shift) : -1;
+        uint64_t act = __ballot(pt >= 0);
+        while (act) {
+            const int leader = __builtin_ctzll(act);
+            const int lp = __builtin_amdgcn_readlane(pt, leader);
+            const uint64_t m = __ballot(pt == lp);
+            const int base = run[lp];  // read by every lane before the leader adds
+            if (pt == lp) pcol[ppos[(int64_t)lp * nb + k] + base + lane_prefix(m)] = col;
+            wave_lds_sync();
+            if (lane == leader) run[lp] = base + __popcll(m);
+            wave_lds_sync();
+            act &= ~m;
+        }
+    }
+}
+
 static size_t hsym_lds(int ew, int64_t nwp, int64_t reqp) {
     return (size_t)ew * 8 + (size_t)reqp * 8 + (size_t)ew * 4 * 2 + (size_t)(ew + 1) * 4 +
            (size_t)reqp * 4 + (size_t)((nwp + 3) & ~int64_t(3)) * 4;
@@ -1247,20 +1312,46 @@ void heavy_symbolic(const DevCSR& A, const DevCSR& B, const int64_t* S, const in
                        hrows, S, off, bmap, H, grid, grp);
     SG_LAUNCH_CHECK();
     const int nwp = nwords / np, reqp = (int)req / np;
+    // with column parts, B's columns split by part once, so that each part's
+    // launch reads only its own columns of every B row
+    const int64_t* ppos = nullptr;
+    const int32_t* pcol = nullptr;
+    if (np > 1 && B.n > 0) {
+        const int shift = ilog2((int64_t)nwp * 32);
+        int64_t* cnt = ar.get<int64_t>("bpart_cnt", (size_t)np * B.n + 1);
+        int64_t* pp = ar.get<int64_t>("bpart_pos", (size_t)np * B.n + 1);
+        int32_t* pc = ar.get<int32_t>("bpart_col", (size_t)B.nnz + 1);
+        const size_t plds = (size_t)(kBpartNT / kWave) * np * 4;
+        const unsigned blocks = grid_1d(ceil_div(B.n * kWave, kBpartNT));
+        hipLaunchKernelGGL(k_bpart_count, dim3(blocks), dim3(kBpartNT), plds, st, B.rp, B.col, B.n,
+                           shift, np, cnt);
+        SG_LAUNCH_CHECK();
+        scan_exclusive(LoadI64{cnt}, (int64_t)np * B.n, pp, ar, st);
+        hipLaunchKernelGGL(k_bpart_scatter, dim3(blocks), dim3(kBpartNT), plds, st, B.rp, B.col,
+                           B.n, shift, np, (const int64_t*)pp, pc);
+        SG_LAUNCH_CHECK();
+        ppos = pp;
+        pcol = pc;
+    }
     for (int part = 0; part < np; ++part) {
+        DevCSR Bp = B;
+        if (ppos) {
+            Bp.rp = ppos + (int64_t)part * B.n;  // [rp[k], rp[k+1]): row k's part-p columns
+            Bp.col = pcol;
+        }
         if (ew == kHsymEW) {
             if (B.nnz < (int64_t(1) << 31))
-                launch_hsym<kHsymEW, true>(lds, grid, st, grp, A, B, req, nwords, part, nwp, reqp,
+                launch_hsym<kHsymEW, true>(lds, grid, st, grp, A, Bp, req, nwords, part, nwp, reqp,
                                            bslot, elem_fin, dist_fin, gbits);
             else
-                launch_hsym<kHsymEW, false>(lds, grid, st, grp, A, B, req, nwords, part, nwp, reqp,
+                launch_hsym<kHsymEW, false>(lds, grid, st, grp, A, Bp, req, nwords, part, nwp, reqp,
                                             bslot, elem_fin, dist_fin, gbits);
         } else {
             if (B.nnz < (int64_t(1) << 31))
-                launch_hsym<kHsymEW / 2, true>(lds, grid, st, grp, A, B, req, nwords, part, nwp,
+                launch_hsym<kHsymEW / 2, true>(lds, grid, st, grp, A, Bp, req, nwords, part, nwp,
                                                reqp, bslot, elem_fin, dist_fin, gbits);
             else
-                launch_hsym<kHsymEW / 2, false>(lds, grid, st, grp, A, B, req, nwords, part, nwp,
+                launch_hsym<kHsymEW / 2, false>(lds, grid, st, grp, A, Bp, req, nwords, part, nwp,
                                                 reqp, bslot, elem_fin, dist_fin, gbits);
         }
     }
