@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--numeric-mode", type=int, default=0, choices=(0, 1, 2, 3),
                     help="heavy numeric dataflow of the timed steps: 0 the library's choice "
                          "(direct), 1 fused first level, 2 separate C-hat (the page's), 3 direct")
+    ap.add_argument("--pairs", action="store_true",
+                    help="time the gMAGNUS page's RMat set instead (Table III: independent A, B "
+                         "of scales 15-20, A.nnz/A.n 4..32, B.nnz/B.n 8); one line with every pair")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -366,7 +369,7 @@ def bench_workload(name: str, args, copy_gbps: float, with_paths: bool, with_cpu
     return {
         "value": value, "unit": "products/s", "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms,
-        "config": {"workload": name, "description": synth.WORKLOADS[name],
+        "config": {"workload": name, "description": synth.describe(name),
                    "nrows": A.nrows, "nnz_A": A.nnz, "sum_products": products,
                    "nnz_C": st["nnz_c"], "heavy_rows": st["heavy_rows"],
                    "heavy_products": st["heavy_products"], "tau": st["tau"],
@@ -406,6 +409,26 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.load()
     copy_gbps = copy_rate_GBps()
+    if args.pairs:
+        from spgemm_irregular_matrices_amd import synth
+        pairs = []
+        for s, a in synth.TABLE3_CELLS:
+            r = bench_workload(synth.pair_name(s, a), args, copy_gbps, False, False)
+            c = r["config"]
+            pairs.append({"scale": s, "a_density": a, "b_density": 8, "ms_per_step": r["ms_per_step"],
+                          "products_per_s": r["value"], "gflops": r["gflops"],
+                          "sum_products": c["sum_products"], "nnz_C": c["nnz_C"],
+                          "C_per_row": c["nnz_C"] / c["nrows"],
+                          "C_hat_per_row": c["sum_products"] / c["nrows"],
+                          "heavy_rows": c["heavy_rows"], "numeric_path": c["numeric_path"],
+                          "heavy_path_frac": r["heavy_path"]["frac"],
+                          "dominant": r["roofline"]["kernel"], "dominant_frac": r["roofline"]["frac"]})
+            print(json.dumps({"pair": pairs[-1]}), file=sys.stderr, flush=True)
+        print(json.dumps({"metric": "SpGEMM intermediate products/s, R-MAT A*B pairs (Table III set)",
+                          "unit": "products/s", "n_gpus": 1, "steps": args.steps,
+                          "warmup": args.warmup, "dtype": "f64", "data": "synthetic",
+                          "pairs": pairs}))
+        return
     head = bench_workload(args.workload, args, copy_gbps, not args.no_paths,
                           not args.no_cpu_baseline)
     others = {}

@@ -306,8 +306,41 @@ WORKLOADS = {
 }
 
 
+# The gMAGNUS page's RMat set (Sec. IV-A, Table III): A of scale s with
+# A.nnz/A.n in {4, 8, 16, 32} times an independent B of the same scale with
+# B.nnz/B.n = 8, at the scales the table fills for each A density.
+TABLE3_CELLS = [(s, a) for a, top in ((4, 20), (8, 19), (16, 18), (32, 18))
+                for s in range(15, top + 1)]
+
+
+def rmat_pair(scale: int, a_density: int, b_density: int = 8):
+    """A seeded pair of independent plain R-MATs (A, B) of one scale."""
+    A = rmat(scale, a_density, seed=700 + 10 * scale + a_density,
+             value_seed=800 + 10 * scale + a_density)
+    B = rmat(scale, b_density, seed=900 + scale + 100 * b_density,
+             value_seed=950 + scale + 100 * b_density)
+    return A, B
+
+
+def pair_name(scale: int, a_density: int, b_density: int = 8) -> str:
+    return f"rmat_pair_s{scale}_a{a_density}_b{b_density}"
+
+
+def describe(name: str) -> str:
+    """One-line description of a named workload."""
+    if name.startswith("rmat_pair_"):
+        s, a, b = (int(x[1:]) for x in name[len("rmat_pair_"):].split("_"))
+        return (f"R-MAT A*B, independent A and B of scale {s} (2^{s} square), "
+                f"A.nnz/A.n = {a}, B.nnz/B.n = {b}, (0.57,0.19,0.19,0.05)")
+    return WORKLOADS[name]
+
+
 def workload(name: str, values: str = "uniform"):
-    """Return (A, B) for one of the named workloads (B is A for the A*A cases)."""
+    """Return (A, B) for one of the named workloads (B is A for the A*A cases);
+    rmat_pair_s<S>_a<A>_b<B> names an independent R-MAT pair (rmat_pair)."""
+    if name.startswith("rmat_pair_"):
+        s, a, b = (int(x[1:]) for x in name[len("rmat_pair_"):].split("_"))
+        return rmat_pair(s, a, b)
     if name == "rmat10_ef8":
         A = rmat(10, 8, seed=1, value_seed=101, values=values)
         return A, A

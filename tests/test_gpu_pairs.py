@@ -1,16 +1,22 @@
 """GPU parity on a second workload family: products of two independent
-R-MAT matrices over the gMAGNUS page's grid of sizes and densities (Sec. IV-A:
-scales 15-20, A.nnz/A.n from 4 to 64, B.nnz/B.n from 4 to 16, here at the
-smaller scales the oracle checks row by row in seconds), and A*A^T for a
-rectangular power-law A. Every row is compared with the oracle, with the
-default heavy path and with the page's own dataflow (outer product into
-C-hat, multisplit), at the default threshold and with heavy rows forced.
+R-MAT matrices.
+
+* The gMAGNUS page's RMat set (Sec. IV-A, Table III): A of scale s with
+  A.nnz/A.n of 4, 8, 16 or 32 times an independent B of the same scale with
+  B.nnz/B.n = 8, at the table's scales 15-18 (every cell of the table at
+  those scales), with the default heavy path and with the page's own
+  dataflow (outer product into C-hat, multisplit); every row of both results
+  against one oracle pass.
+* Smaller pairs over a wider density grid (A.nnz/A.n up to 64, B.nnz/B.n 4 to
+  16), with heavy rows also forced through several multisplit levels, and
+  A*A^T for a rectangular power-law A.
 """
+import numpy as np
 import pytest
 
 import oracle
 from spgemm_irregular_matrices_amd import synth
-from tests.helpers import compare, run_gpu
+from tests.helpers import compare, compare_every_row, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -49,3 +55,32 @@ def test_rectangular_a_at():
         rp, col, val, st = run_gpu(A, At, **kw)
         assert st["heavy_rows"] > 0
         compare(A, At, rp, col, val)
+
+
+# Table III cells at scales 15-18: (scale, A.nnz/A.n); B.nnz/B.n = 8
+TABLE3 = [(s, a) for s, a in synth.TABLE3_CELLS if s <= 18]
+
+
+@pytest.mark.parametrize("scale,a_density", TABLE3, ids=[f"s{s}-a{a}" for s, a in TABLE3])
+def test_table3_pairs_every_row(scale, a_density):
+    import torch
+    from spgemm_irregular_matrices_amd import binding
+    A, B = synth.rmat_pair(scale, a_density)
+    u = oracle.row_products(A, B)
+    dA, dB = binding.DeviceCSR.from_host(A), binding.DeviceCSR.from_host(B)
+    results = []
+    for label, kw, path in (("default", {}, 3), ("page_dataflow", {"numeric_mode": 2}, 2)):
+        with binding.Plan(**kw) as p:
+            C = p.multiply(dA, dB)
+            torch.cuda.synchronize()
+            st = p.stats()
+        assert st["sum_products"] == int(u.sum())
+        assert st["heavy_products"] == int(u[u > st["tau"]].sum())
+        if st["heavy_rows"]:
+            assert st["numeric_path"] == path
+        rp = C.rowptr.cpu().numpy()
+        assert rp[0] == 0 and rp[-1] == st["nnz_c"]
+        results.append({"label": label, "C": C, "rp": rp, "st": st})
+    assert results[0]["st"]["nnz_c"] == results[1]["st"]["nnz_c"]
+    del dA, dB
+    compare_every_row(A, B, results, u)

@@ -14,15 +14,12 @@ columns bit for bit, every value within 1e-12 * sum|a*b| of its entry. The
 large workloads are split into several tests so that each one reports within
 a minute or so.
 """
-import concurrent.futures as cf
-import os
-
 import numpy as np
 import pytest
 
 import oracle
 from spgemm_irregular_matrices_amd import synth
-from tests.helpers import BOUND, compare
+from tests.helpers import compare, compare_every_row, oracle_threads
 
 pytestmark = pytest.mark.gpu
 
@@ -45,15 +42,6 @@ RUNS = {
     ],
 }
 PARTS = {"rmat18_ef16": 4, "rmat20_ef8": 8, "rect_zipf2.1_x_uniform16": 1}
-BLOCK_PRODUCTS = 1 << 27  # oracle work per row block
-
-
-def _threads() -> int:
-    try:
-        n = len(os.sched_getaffinity(0))
-    except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -116,7 +104,7 @@ def test_banded_1M_all_rows():
     i = np.arange(n)
     exp = np.minimum(n - 1, i + 16) - np.maximum(0, i - 16) + 1
     assert np.array_equal(np.diff(rp), exp)
-    compare(A, B, rp, C.col.cpu().numpy(), C.val.cpu().numpy(), nthreads=_threads())
+    compare(A, B, rp, C.col.cpu().numpy(), C.val.cpu().numpy(), nthreads=oracle_threads())
     _check_structural_stats(st, oracle.row_products(A, B))
 
 
@@ -150,61 +138,6 @@ def _part_rows(cu, parts, k):
     return b[k], max(b[k], b[k + 1])
 
 
-def _blocks(u, r0, r1):
-    """Consecutive row blocks of [r0, r1) with about BLOCK_PRODUCTS products each."""
-    cu = np.cumsum(u[r0:r1], dtype=np.int64)
-    out = []
-    a = 0
-    n = r1 - r0
-    while a < n:
-        base = int(cu[a - 1]) if a else 0
-        b = int(np.searchsorted(cu, base + BLOCK_PRODUCTS, side="right"))
-        b = max(b, a + 1)
-        out.append((r0 + a, r0 + min(b, n)))
-        a = b
-    return out
-
-
-def _check_piece(gcol, gval, rcol, rval, rabs):
-    """(columns equal, index of the first value outside the bound or -1)."""
-    if not np.array_equal(gcol, rcol):
-        return False, -1
-    ok = np.abs(gval - rval) <= BOUND * rabs  # NaN or Inf fails
-    if ok.all():
-        return True, -1
-    return True, int(np.argmin(ok))
-
-
-def _compare_block(pool, res, ref, r0, r1):
-    rp = res["rp"]
-    C = res["C"]
-    glen = np.diff(rp[r0:r1 + 1])
-    rlen = np.diff(ref.rowptr)
-    bad = np.nonzero(glen != rlen)[0]
-    assert bad.size == 0, (f"[{res['label']}] row lengths differ at rows {r0 + bad[:10]}: "
-                           f"gpu {glen[bad[:10]]} oracle {rlen[bad[:10]]}")
-    s, e = int(rp[r0]), int(rp[r1])
-    gcol = C.col[s:e].cpu().numpy()
-    gval = C.val[s:e].cpu().numpy()
-    nn = e - s
-    nthr = _threads()
-    cuts = np.linspace(0, nn, num=min(nthr, max(1, nn // (1 << 16))) + 1).astype(np.int64)
-    futs = [pool.submit(_check_piece, gcol[a:b], gval[a:b], ref.col[a:b], ref.val[a:b],
-                        ref.abssum[a:b]) for a, b in zip(cuts[:-1], cuts[1:])]
-    for (a, _), f in zip(zip(cuts[:-1], cuts[1:]), futs):
-        cols_ok, first_bad = f.result()
-        if not cols_ok:
-            j = a + int(np.argmax(gcol[a:] != ref.col[a:]))
-            row = r0 + int(np.searchsorted(ref.rowptr, j, side="right")) - 1
-            pytest.fail(f"[{res['label']}] column mismatch at row {row}: gpu {gcol[j]} "
-                        f"oracle {ref.col[j]}")
-        if first_bad >= 0:
-            j = a + first_bad
-            row = r0 + int(np.searchsorted(ref.rowptr, j, side="right")) - 1
-            pytest.fail(f"[{res['label']}] value outside the bound at row {row} col {gcol[j]}: "
-                        f"gpu {gval[j]!r} oracle {ref.val[j]!r} abssum {ref.abssum[j]!r}")
-
-
 CASES = [(name, k) for name in RUNS for k in range(PARTS[name])]
 
 
@@ -235,12 +168,6 @@ def test_large_every_row(name, part):
         if name == "rmat20_ef8":
             assert w["res"][0]["st"]["nnz_c"] > (1 << 31)
     r0, r1 = _part_rows(w["cu"], PARTS[name], part)
-    nthr = _threads()
-    with cf.ThreadPoolExecutor(max_workers=nthr) as pool:
-        for a, b in _blocks(u, r0, r1):
-            ref = oracle.spgemm_rows(A, B, np.arange(a, b, dtype=np.int64), nthreads=nthr)
-            for res in w["res"]:
-                _compare_block(pool, res, ref, a, b)
-            del ref
+    compare_every_row(A, B, w["res"], u, r0, r1)
     if part == PARTS[name] - 1:
         _cache.clear()
