@@ -125,6 +125,29 @@ def copy_calibration(mib: int):
     ms = e0.elapsed_time(e1) / reps
     print(json.dumps({"copy_calibration_bytes_each_way": n * 8, "launches": reps + 1,
                       "copy_ms": ms, "copy_GBps_read_plus_write": 2 * n * 8 / (ms * 1e-3) / 1e9}))
+    # the same streaming add on 2-byte elements (the split B's columns are 2 bytes)
+    s16 = src.view(torch.int16)
+    d16 = dst.view(torch.int16)
+    torch.add(s16, 1, out=d16)
+    torch.cuda.synchronize()
+    # isolated gathers: one element from each of ng distinct random 256-byte
+    # blocks of the 2 GiB buffer (far larger than the caches), from 8-byte and
+    # from 2-byte data; the indices themselves are read in a stream (8 B each)
+    blocks = (n * 8) // 256
+    ng = min(1 << 22, blocks // 2)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    sel = torch.randperm(blocks, generator=g)[:ng].sort().values
+    idx64 = (sel * 32).to("cuda")   # float64 element at the start of the block
+    idx16 = (sel * 128).to("cuda")  # int16 element at the start of the block
+    torch.cuda.synchronize()
+    out64 = torch.take(src, idx64)
+    out16 = torch.take(s16, idx16)
+    torch.cuda.synchronize()
+    print(json.dumps({"int16_add_bytes_each_way": n * 8,
+                      "gather_elements": ng, "gather_index_bytes": ng * 8,
+                      "gather_f64_useful_bytes": ng * 8, "gather_i16_useful_bytes": ng * 2,
+                      "dispatch_order": ["fill", "add f64 x4", "add i16", "take f64", "take i16"],
+                      "check": float(out64.sum().item()) + float(out16.sum().item())}))
 
 
 # kernels behind each timed phase, for the HBM traffic the counters measured

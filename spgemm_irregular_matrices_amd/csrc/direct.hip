@@ -362,7 +362,12 @@ __device__ __forceinline__ void rank_item(const DirectArgs& d, int32_t x, int64_
     const int NWD = W >> 5;
     const int tt = threadIdx.x;
     const int s = (int)((uint32_t)x & (uint32_t)(d.req - 1));  // req is a power of two
-    for (int wd = tt; wd < NWD; wd += TW) bits[wd] = 0u;
+    // one-wave items of at most 128 products are ranked through the
+    // two-level bitmap (work by product); larger ones through the chunk's
+    // full bitmap
+    constexpr bool kTwoLevel = TW == kWave && KPT <= 2;
+    if constexpr (!kTwoLevel)
+        for (int wd = tt; wd < NWD; wd += TW) bits[wd] = 0u;
 
     uint32_t idx[KPT];
     double v[KPT];
@@ -396,6 +401,12 @@ __device__ __forceinline__ void rank_item(const DirectArgs& d, int32_t x, int64_
         }
         done += tot;
         __syncthreads();  // the next round restages
+    }
+    if constexpr (kTwoLevel) {
+        // the staged B starts are free once the products are formed
+        wave_rank_emit<KPT>(idx, v, W, bits, vals, (uint16_t*)s_bo, s << d.logW, d.Ccol + off,
+                            d.Cval + off, true);
+        return;
     }
 #pragma unroll
     for (int k = 0; k < KPT; ++k)
@@ -712,7 +723,9 @@ constexpr int RANK_IPG_S = 4, RANK_IPG_L = 2;
 template <int TW, int KPT, int IPG>
 static void launch_direct_rank(const DirectArgs& d, int64_t p0, int64_t n, hipStream_t st) {
     const int64_t W = int64_t(1) << d.logW;
-    const size_t lds = (size_t)TW * KPT * 8 + (size_t)(W / 32) * 8;
+    size_t lds = (size_t)TW * KPT * 8 + (size_t)(W / 32) * 8;
+    if (TW == kWave && KPT <= 2)
+        lds = std::max(lds, (size_t)TW * KPT * 8 + (size_t)wave_rank_lds(KPT, W));
     auto kern = d.bocc ? k_direct_rank<TW, KPT, true, IPG> : k_direct_rank<TW, KPT, false, IPG>;
     SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds));
