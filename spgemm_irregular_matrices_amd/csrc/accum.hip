@@ -528,7 +528,11 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
     const int64_t start = ci.rp[p0 + item];
     const int count = (int)(ci.rp[p0 + item + 1] - start);
     const int64_t out = ci.map[p0 + item];
-    for (int w = tt; w < NWD; w += TW) bits[w] = 0u;
+    // one-wave chunks are ranked through the two-level bitmap (work by
+    // element); the larger ones through the chunk's full bitmap
+    constexpr bool kTwoLevel = TW == kWave;
+    if constexpr (!kTwoLevel)
+        for (int w = tt; w < NWD; w += TW) bits[w] = 0u;
     if (tt == 0) lo_sh = chunk_lo(ci, start, out, W);
     __syncthreads();
     const int32_t lo = lo_sh;
@@ -543,6 +547,20 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
                                : (uint32_t)(ci.bcol[start + t] - lo);
             if constexpr (NUM) v[k] = ci.bval[start + t];
         }
+    }
+    if constexpr (kTwoLevel) {
+        if constexpr (!NUM) {
+#pragma unroll
+            for (int k = 0; k < KPT; ++k) v[k] = 0.0;
+        }
+        // LDS from `bits` on: the two-level arrays, then the ranked columns
+        uint16_t* scol16 = (uint16_t*)((char*)bits + wave_rank_lds(KPT, W));
+        const int64_t off = NUM ? ci.off[out] : 0;
+        const int nnz = wave_rank_emit<KPT>(idx, v, W, bits, vals, scol16, lo, ci.Ccol + off,
+                                            ci.Cval + off, NUM);
+        if constexpr (!NUM)
+            if (tt == 0) ci.cnt[out] = nnz;
+        return;
     }
 #pragma unroll
     for (int k = 0; k < KPT; ++k)
@@ -714,6 +732,9 @@ template <bool NUM, int TW, int KPT>
 static void launch_rank(const ChunkItems& ci, int64_t p0, int64_t n, hipStream_t st) {
     const int64_t W = ci.width;
     size_t lds = (NUM ? (size_t)TW * KPT * 12 : 0) + (size_t)(W / 32) * 4 * (NUM ? 2 : 1);
+    if (TW == kWave)  // the two-level arrays and 16-bit ranked columns after the values
+        lds = (NUM ? (size_t)TW * KPT * 8 : 0) + (size_t)wave_rank_lds(KPT, W) +
+              (size_t)TW * KPT * 2;
     auto kern = k_acc_rank<NUM, TW, KPT>;
     SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds));
