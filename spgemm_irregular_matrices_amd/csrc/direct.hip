@@ -24,10 +24,11 @@ namespace sg {
 
 // ---------------------------------------------------------------- B split
 // bslot (row-major, B.n x req) to slot-major (req x B.n), in 32 x 32 tiles;
-// with bocc, also one bit per (slot, B row) that has entries, slot-major,
-// ceil(B.n / 32) words per slot (a half wave holds 32 rows of one slot).
+// also the rows' occupancy words, row-major: bit t of roc[k * nw + w] is set
+// if B row k has entries in slot 32 w + t (nw = ceil(req / 32) = gridDim.y;
+// each half wave holds the 32 slots of one row).
 __global__ __launch_bounds__(256) void k_bslot_transpose(const int32_t* bslot, int64_t nb, int req,
-                                                         int32_t* bslotT, uint32_t* bocc) {
+                                                         int32_t* bslotT, uint32_t* roc) {
     __shared__ int32_t tile[32][33];
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
     const int64_t k0 = (int64_t)blockIdx.x * 32;
@@ -35,7 +36,11 @@ __global__ __launch_bounds__(256) void k_bslot_transpose(const int32_t* bslot, i
     for (int r = ty; r < 32; r += 8) {
         const int64_t k = k0 + r;
         const int sl = s0 + tx;
-        tile[r][tx] = (k < nb && sl < req) ? bslot[k * req + sl] : 0;
+        const int32_t c = (k < nb && sl < req) ? bslot[k * req + sl] : 0;
+        tile[r][tx] = c;
+        const uint64_t m = __ballot(c != 0);
+        if (tx == 0 && k < nb)
+            roc[k * gridDim.y + blockIdx.y] = (uint32_t)(threadIdx.x & 32 ? m >> 32 : m);
     }
     __syncthreads();
     for (int r = ty; r < 32; r += 8) {
@@ -43,13 +48,25 @@ __global__ __launch_bounds__(256) void k_bslot_transpose(const int32_t* bslot, i
         const int64_t k = k0 + tx;
         const int32_t c = tile[tx][r];
         if (sl < req && k < nb) bslotT[(int64_t)sl * nb + k] = c;
-        if (bocc) {
-            const uint64_t m = __ballot(c != 0);
-            if (tx == 0 && sl < req)
-                bocc[(int64_t)sl * gridDim.x + blockIdx.x] =
-                    (uint32_t)(threadIdx.x & 32 ? m >> 32 : m);
-        }
     }
+}
+
+// eocc[w * annz + q]: occupancy word w of B row Acol[q], for every A entry q,
+// so that an item reads its entries' bits beside their columns, coalesced.
+__global__ __launch_bounds__(256) void k_entry_occ(const int32_t* acol, int64_t annz, int nw,
+                                                   const uint32_t* roc, uint32_t* eocc) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= annz) return;
+    const int64_t k = acol[q];
+    for (int w = 0; w < nw; ++w) eocc[(int64_t)w * annz + q] = roc[k * nw + w];
+}
+
+void direct_entry_occ(const int32_t* acol, int64_t annz, int req, const uint32_t* roc,
+                      uint32_t* eocc, hipStream_t st) {
+    if (annz <= 0) return;
+    hipLaunchKernelGGL(k_entry_occ, dim3(grid_1d(ceil_div(annz, 256))), dim3(256), 0, st, acol,
+                       annz, (int)ceil_div(req, 32), roc, eocc);
+    SG_LAUNCH_CHECK();
 }
 
 struct LoadI32 {
@@ -103,7 +120,7 @@ __global__ __launch_bounds__(kBpartNT) void k_bpartition(const int64_t* brp, con
 }
 
 void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int64_t* spos,
-                    uint32_t* bocc, int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st) {
+                    uint32_t* roc, int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st) {
     if (W > 65536 || req > kDirectMaxSlots) throw std::logic_error("direct split limits");
     const int64_t n = (int64_t)req * B.n;
     if (B.n <= 0) {
@@ -112,7 +129,7 @@ void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, i
     }
     int32_t* bslotT = ar.get<int32_t>("bslotT", (size_t)n);
     hipLaunchKernelGGL(k_bslot_transpose, dim3(grid_1d(ceil_div(B.n, 32)), ceil_div(req, 32)),
-                       dim3(256), 0, st, bslot, B.n, req, bslotT, bocc);
+                       dim3(256), 0, st, bslot, B.n, req, bslotT, roc);
     SG_LAUNCH_CHECK();
     scan_exclusive(LoadI32{bslotT}, n, spos, ar, st);
     if (B.nnz <= 0) return;
@@ -254,7 +271,7 @@ __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int6
         const double a = d.Aval[q];
         // with the occupancy bits, an empty (B row, slot) slice reads no bounds
         int64_t lo = 0;
-        if (!OCC || (d.bocc[(int64_t)s * d.nbw + (k >> 5)] >> (k & 31)) & 1u) {
+        if (!OCC || (d.eocc[(int64_t)(s >> 5) * d.annz + q] >> (s & 31)) & 1u) {
             const int64_t* sp = d.spos + (int64_t)s * d.nb + k;
             lo = sp[0];
             len = (int)(sp[1] - lo);
@@ -280,7 +297,7 @@ __device__ __forceinline__ void stage_load(const DirectArgs& d, int64_t q, bool 
     a = d.Aval[q];
     lo = 0;
     len = 0;
-    if (!OCC || (d.bocc[(int64_t)s * d.nbw + (k >> 5)] >> (k & 31)) & 1u) {
+    if (!OCC || (d.eocc[(int64_t)(s >> 5) * d.annz + q] >> (s & 31)) & 1u) {
         const int64_t* sp = d.spos + (int64_t)s * d.nb + k;
         lo = sp[0];
         len = (int)(sp[1] - lo);
@@ -528,6 +545,165 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
     }
 }
 
+// A run's products: each round gives every lane one (entry, slot) pair of
+// the run, lane = j * nns + t for entry eb + j of the row and the t-th slot
+// of the mask (epr = 64 / nns entries a round; the lanes past epr * nns
+// idle), the slices are scanned and each lane forms up to two of the run's
+// products. The two-level bitmap then ranks the run's columns over the
+// span of its slots and writes the run's output, which is its items'
+// outputs one after the other. The first round arrives in registers.
+template <bool OCC>
+__device__ __forceinline__ void run_item(const DirectArgs& d, int64_t hdr, int64_t q0, int ne,
+                                         int64_t off, int jl, int ds, int epr, double a0,
+                                         int64_t lo0, int len0, int WR, double* vals, void* rk,
+                                         int* s_pre, int64_t* s_bo, double* s_a, int* s_cb) {
+    constexpr int KPT = 2;
+    static_assert(kWave * KPT == kRunMax, "one wavefront holds a run's products");
+    const int lane = lane_id();
+    const int32_t x = (int32_t)hdr;
+    const int s0 = (int)((uint32_t)x & (uint32_t)(d.req - 1));  // req is a power of two
+    const int s = s0 + ds;
+    s_cb[lane] = ds << d.logW;
+    uint32_t idx[KPT];
+    double v[KPT];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+        idx[k] = 0xffffffffu;
+        v[k] = 0.0;
+    }
+    int done = 0;
+    for (int eb = 0; eb < ne; eb += epr) {
+        double a = a0;
+        int64_t lo = lo0;
+        int len = len0;
+        if (eb > 0) {
+            const int j = eb + jl;
+            const int64_t q = q0 + min(j, ne - 1);
+            const int32_t k = d.Acol[q];
+            a = d.Aval[q];
+            lo = 0;
+            len = 0;
+            // with the occupancy bits, an empty slice reads no bounds
+            if (!OCC || (d.eocc[(int64_t)(s >> 5) * d.annz + q] >> (s & 31)) & 1u) {
+                const int64_t* sp = d.spos + (int64_t)s * d.nb + k;
+                lo = sp[0];
+                len = (jl < epr && j < ne) ? (int)(sp[1] - lo) : 0;
+            }
+        }
+        s_bo[lane] = lo;
+        s_a[lane] = a;
+        const int inc = wave_inclusive_scan(len);
+        const int tot = __shfl(inc, kWave - 1, kWave);
+        s_pre[lane] = inc - len;
+        wave_lds_sync();
+        int64_t bi[KPT];
+        double av[KPT];
+        int cb[KPT];
+        int j = 0;
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const int p = k * kWave + lane - done;
+            bi[k] = -1;
+            if (p >= 0 && p < tot) {
+                j = direct_find(s_pre, kWave, p, j);
+                bi[k] = s_bo[j] + (p - s_pre[j]);
+                av[k] = s_a[j];
+                cb[k] = s_cb[j];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            if (bi[k] >= 0) {
+                idx[k] = (uint32_t)cb[k] + d.bcol16[bi[k]];
+                v[k] = av[k] * d.bval[bi[k]];
+            }
+        }
+        done += tot;
+        wave_lds_sync();  // the next round restages
+    }
+    // the staged B starts are free once the products are formed
+    wave_rank_emit<KPT>(idx, v, WR, rk, vals, (uint16_t*)s_bo, s0 << d.logW, d.Ccol + off,
+                        d.Cval + off, true);
+}
+
+// IPG runs per wavefront-sized work group: their headers, output offsets and
+// first rounds are loaded together, as in k_direct_rank.
+template <bool OCC, int IPG>
+__global__ __launch_bounds__(kWave) void k_direct_runs(DirectArgs d, int64_t nruns) {
+    extern __shared__ int64_t lds_u[];
+    double* vals = (double*)lds_u;     // kRunMax
+    void* rk = vals + kRunMax;         // wave_rank_lds(2, run width)
+    __shared__ int s_pre[kWave];
+    __shared__ int64_t s_bo[kWave];
+    __shared__ double s_a[kWave];
+    __shared__ int s_cb[kWave];
+    const int lane = lane_id();
+    const int64_t i0 = (int64_t)blockIdx.x * IPG;
+    if (i0 >= nruns) return;
+    const int nown = (int)min((int64_t)IPG, nruns - i0);  // uniform over the group
+    const int WR = run_span(d.logW) << d.logW;
+    int64_t hdr[IPG], q0[IPG], off[IPG];
+    int ne[IPG];
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) {
+        const int64_t i = i0 + min(u, nown - 1);
+        hdr[u] = d.rhdr[i];
+        q0[u] = d.rq0[i];
+        ne[u] = d.rne[i];
+    }
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) off[u] = d.off[(int32_t)hdr[u]];
+    // lane roles: entry jl of each round, slot s0 + ds (t = lane mod nns < nns,
+    // so the mask keeps a bit after t are cleared, also on idle lanes)
+    int jl[IPG], ds[IPG], epr[IPG];
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) {
+        uint32_t m = (uint32_t)(hdr[u] >> 32);
+        const int nns = __popc(m);
+        epr[u] = kWave / nns;
+        jl[u] = lane / nns;
+        for (int t = lane - jl[u] * nns; t > 0; --t) m &= m - 1;
+        ds[u] = __builtin_ctz(m);
+    }
+    // a run has products, so its row has an entry: the index is clamped
+    // into the row and every load stays in bounds
+    double a[IPG];
+    int64_t lo[IPG];
+    int len[IPG];
+    int32_t k[IPG];
+    int64_t q[IPG];
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) {
+        q[u] = q0[u] + min(jl[u], ne[u] - 1);
+        k[u] = d.Acol[q[u]];
+        a[u] = d.Aval[q[u]];
+    }
+    int64_t hi[IPG];
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) {
+        const int s = (int)((uint32_t)hdr[u] & (uint32_t)(d.req - 1)) + ds[u];
+        lo[u] = 0;
+        hi[u] = 0;
+        if (!OCC || (d.eocc[(int64_t)(s >> 5) * d.annz + q[u]] >> (s & 31)) & 1u) {
+            const int64_t* sp = d.spos + (int64_t)s * d.nb + k[u];
+            lo[u] = sp[0];
+            hi[u] = sp[1];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < IPG; ++u)
+        len[u] = (jl[u] < epr[u] && jl[u] < ne[u]) ? (int)(hi[u] - lo[u]) : 0;
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) {
+        if (u < nown) {
+            // the previous run's output has read the staging area
+            if (u > 0) wave_lds_sync();
+            run_item<OCC>(d, hdr[u], q0[u], ne[u], off[u], jl[u], ds[u], epr[u], a[u], lo[u],
+                          len[u], WR, vals, rk, s_pre, s_bo, s_a, s_cb);
+        }
+    }
+}
+
 // Dense window accumulation of the large items: the item's entries are
 // staged kDirectNE at a time and their products streamed through an LDS
 // array over the chunk's W columns (fp64 atomics) with one-byte presence
@@ -652,67 +828,196 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     }
 }
 
-// Per class of items (dense window / bitmap rank): products, output
-// entries, and A entries read (an item reads all of its row's entries), for
-// the algorithmic byte counts. out6 = {dense: products, outputs, entries,
-// rank: products, outputs, entries}.
+// Per class of items (dense window / bitmap rank / runs): products, output
+// entries, and A entries read (a dense or rank item reads all of its row's
+// entries; the runs count theirs when they are formed), for the algorithmic
+// byte counts. out8 = {dense: products, outputs, entries, rank: products,
+// outputs, entries, runs: products, outputs}.
+constexpr int kDirectTotals = 8;
+
 __global__ __launch_bounds__(256) void k_direct_totals(const int64_t* hq0, const int64_t* hq1,
                                                       int64_t nitems, int logreq,
                                                       const int64_t* elem_fin,
                                                       const int64_t* dist_fin, int64_t* part) {
     __shared__ int64_t sh[256 / kWave + 1];
-    int64_t dp = 0, dout = 0, de = 0, rp = 0, rout = 0, re = 0;
+    int64_t v[kDirectTotals] = {};
     int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (; x < nitems; x += stride) {
         const int64_t e = elem_fin[x];
         if (e == 0) continue;
         const int64_t h = x >> logreq;  // req is a power of two
-        const int64_t o = dist_fin[x], ne = hq1[h] - hq0[h];
-        if (e > kDirectDense) {
-            dp += e;
-            dout += o;
-            de += ne;
-        } else {
-            rp += e;
-            rout += o;
-            re += ne;
+        const int64_t o = dist_fin[x];
+        if (e <= kRunMax) {
+            v[6] += e;
+            v[7] += o;
+            continue;
         }
+        const int c = e > kDirectDense ? 0 : 3;
+        v[c] += e;
+        v[c + 1] += o;
+        v[c + 2] += hq1[h] - hq0[h];
     }
-    const int64_t v[6] = {dp, dout, de, rp, rout, re};
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < kDirectTotals; ++i) {
         const int64_t r = block_reduce_sum<256>(v[i], sh);
         if (threadIdx.x == 0) part[(int64_t)i * gridDim.x + blockIdx.x] = r;
     }
 }
 
-// out6[i] = sum of the groups' partial sums i (one work group).
-__global__ __launch_bounds__(256) void k_sum_parts(const int64_t* part, int nparts, int64_t* out6) {
+// out[i] = sum of the groups' partial sums i, for i < nv (one work group).
+__global__ __launch_bounds__(256) void k_sum_parts(const int64_t* part, int nparts, int nv,
+                                                   int64_t* out) {
     __shared__ int64_t sh[256 / kWave + 1];
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < nv; ++i) {
         int64_t v = 0;
         for (int b = threadIdx.x; b < nparts; b += 256) v += part[(int64_t)i * nparts + b];
         v = block_reduce_sum<256>(v, sh);
-        if (threadIdx.x == 0) out6[i] = v;
+        if (threadIdx.x == 0) out[i] = v;
     }
 }
 
 void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
-                   const int64_t* elem_fin, const int64_t* dist_fin, int64_t* out6, Arena& ar,
+                   const int64_t* elem_fin, const int64_t* dist_fin, int64_t* out8, Arena& ar,
                    hipStream_t st) {
     const int64_t n = H * req;
     if (n <= 0) {
-        fill<int64_t>(out6, 6, 0, st);
+        fill<int64_t>(out8, kDirectTotals, 0, st);
         return;
     }
     // partial sums per group, then one group adds them: no shared counter
     const int blocks = (int)std::min<int64_t>(ceil_div(n, 256), 2048);
-    int64_t* part = ar.get<int64_t>("dtot_parts", (size_t)6 * blocks);
+    int64_t* part = ar.get<int64_t>("dtot_parts", (size_t)kDirectTotals * blocks);
     hipLaunchKernelGGL(k_direct_totals, dim3(blocks), dim3(256), 0, st, hq0, hq1, n, ilog2(req),
                        elem_fin, dist_fin, part);
     SG_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_sum_parts, dim3(1), dim3(256), 0, st, part, blocks, out6);
+    hipLaunchKernelGGL(k_sum_parts, dim3(1), dim3(256), 0, st, part, blocks, kDirectTotals, out8);
+    SG_LAUNCH_CHECK();
+}
+
+// ---------------------------------------------------------------- runs
+// One thread per heavy row walks its slots in order and forms its runs (see
+// run_span and kRunMax): markT (slot-major, req x H bytes) receives the
+// run's slot mask at (s0, h) and 0 at every other slot of the row, so that
+// a scan in slot-major order numbers the runs slot by slot (the runs of
+// slot 0 of all rows first, as the rank items run). The row's 16-slot
+// batches of item counts are read 16 bytes a load. part: per work group,
+// the A entries and the (entry, slot) pairs its runs read.
+constexpr int kRunBatch = 16;
+
+__global__ __launch_bounds__(256) void k_runs_mark(const int64_t* elem_fin, int64_t H, int req,
+                                                   int span, const int64_t* hq0,
+                                                   const int64_t* hq1, uint8_t* markT,
+                                                   int64_t* part) {
+    __shared__ int64_t sh[256 / kWave + 1];
+    const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t ent = 0, pairs = 0;
+    if (h < H) {
+        const int64_t ne = hq1[h] - hq0[h];
+        const int64_t* e = elem_fin + h * req;
+        int s0 = -1;
+        uint32_t mask = 0;
+        int64_t cur = 0;
+        for (int sb = 0; sb < req; sb += kRunBatch) {
+            int64_t c[kRunBatch];
+            if (req >= kRunBatch) {
+                // req is a power of two: the batch is 128-byte aligned
+                const uint4* e4 = (const uint4*)(e + sb);
+#pragma unroll
+                for (int t = 0; t < kRunBatch / 2; ++t) {
+                    const uint4 v = e4[t];
+                    c[2 * t] = (int64_t)(((uint64_t)v.y << 32) | v.x);
+                    c[2 * t + 1] = (int64_t)(((uint64_t)v.w << 32) | v.z);
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < kRunBatch; ++t) c[t] = t < req ? e[t] : 0;
+            }
+#pragma unroll
+            for (int t = 0; t < kRunBatch; ++t) {
+                const int s = sb + t;
+                if (s >= req) break;
+                markT[(int64_t)s * H + h] = 0;
+                const int64_t cs = c[t];
+                if (cs == 0) continue;
+                // a larger item writes between: the run cannot span it
+                const bool big = cs > kRunMax;
+                if (s0 >= 0 && (big || cur + cs > kRunMax || s - s0 >= span)) {
+                    markT[(int64_t)s0 * H + h] = (uint8_t)mask;
+                    ent += ne;
+                    pairs += ne * __popc(mask);
+                    s0 = -1;
+                }
+                if (big) continue;
+                if (s0 < 0) {
+                    s0 = s;
+                    mask = 0;
+                    cur = 0;
+                }
+                cur += cs;
+                mask |= 1u << (s - s0);
+            }
+        }
+        if (s0 >= 0) {
+            markT[(int64_t)s0 * H + h] = (uint8_t)mask;
+            ent += ne;
+            pairs += ne * __popc(mask);
+        }
+    }
+    ent = block_reduce_sum<256>(ent, sh);
+    pairs = block_reduce_sum<256>(pairs, sh);
+    if (threadIdx.x == 0) {
+        part[blockIdx.x] = ent;
+        part[gridDim.x + blockIdx.x] = pairs;
+    }
+}
+
+struct RunStart {
+    const uint8_t* markT;
+    __device__ int64_t operator()(int64_t i) const { return markT[i] != 0; }
+};
+
+// rpos: exclusive scan of RunStart over req x H (+1).
+__global__ __launch_bounds__(256) void k_runs_scatter(const uint8_t* markT, const int64_t* rpos,
+                                                      int64_t H, int req, const int64_t* hq0,
+                                                      const int64_t* hq1, int64_t* rhdr,
+                                                      int64_t* rq0, int32_t* rne) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= H * req) return;
+    const uint32_t m = markT[i];
+    if (!m) return;
+    const int64_t s0 = i / H, h = i - s0 * H;
+    const int64_t j = rpos[i];
+    const int64_t q0 = hq0[h];
+    rhdr[j] = (h * req + s0) | ((int64_t)m << 32);
+    rq0[j] = q0;
+    rne[j] = (int32_t)(hq1[h] - q0);
+}
+
+__global__ void k_runs_total(const int64_t* rpos, int64_t n, int64_t* meta) { meta[0] = rpos[n]; }
+
+void direct_runs(const int64_t* elem_fin, int64_t H, int req, int logW, const int64_t* hq0,
+                 const int64_t* hq1, int64_t* rhdr, int64_t* rq0, int32_t* rne, int64_t* meta,
+                 Arena& ar, hipStream_t st) {
+    if (H <= 0) {
+        fill<int64_t>(meta, 3, 0, st);
+        return;
+    }
+    const int64_t n = H * req;
+    const int64_t blocks = ceil_div(H, 256);
+    uint8_t* markT = ar.get<uint8_t>("run_mark", (size_t)n);
+    int64_t* part = ar.get<int64_t>("run_parts", (size_t)(2 * blocks));
+    hipLaunchKernelGGL(k_runs_mark, dim3(grid_1d(blocks)), dim3(256), 0, st, elem_fin, H, req,
+                       run_span(logW), hq0, hq1, markT, part);
+    SG_LAUNCH_CHECK();
+    int64_t* rpos = ar.get<int64_t>("run_pos", (size_t)n + 1);
+    scan_exclusive(RunStart{markT}, n, rpos, ar, st);
+    hipLaunchKernelGGL(k_runs_scatter, dim3(grid_1d(ceil_div(n, 256))), dim3(256), 0, st, markT,
+                       rpos, H, req, hq0, hq1, rhdr, rq0, rne);
+    SG_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_runs_total, dim3(1), dim3(1), 0, st, rpos, n, meta);
+    SG_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_sum_parts, dim3(1), dim3(256), 0, st, part, (int)blocks, 2, meta + 1);
     SG_LAUNCH_CHECK();
 }
 
@@ -726,10 +1031,20 @@ static void launch_direct_rank(const DirectArgs& d, int64_t p0, int64_t n, hipSt
     size_t lds = (size_t)TW * KPT * 8 + (size_t)(W / 32) * 8;
     if (TW == kWave && KPT <= 2)
         lds = std::max(lds, (size_t)TW * KPT * 8 + (size_t)wave_rank_lds(KPT, W));
-    auto kern = d.bocc ? k_direct_rank<TW, KPT, true, IPG> : k_direct_rank<TW, KPT, false, IPG>;
+    auto kern = d.occ ? k_direct_rank<TW, KPT, true, IPG> : k_direct_rank<TW, KPT, false, IPG>;
     SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds));
     hipLaunchKernelGGL(kern, dim3(grid_1d((n + IPG - 1) / IPG)), dim3(TW), lds, st, d, p0, n);
+    SG_LAUNCH_CHECK();
+}
+
+void direct_accumulate_runs(const DirectArgs& d, int64_t nruns, hipStream_t st) {
+    if (nruns <= 0) return;
+    const int WR = run_span(d.logW) << d.logW;
+    const size_t lds = (size_t)kRunMax * 8 + (size_t)wave_rank_lds(2, WR);
+    constexpr int IPG = 2;
+    auto kern = d.eocc ? k_direct_runs<true, IPG> : k_direct_runs<false, IPG>;
+    hipLaunchKernelGGL(kern, dim3(grid_1d(ceil_div(nruns, IPG))), dim3(kWave), lds, st, d, nruns);
     SG_LAUNCH_CHECK();
 }
 
@@ -749,7 +1064,7 @@ void direct_accumulate(const DirectArgs& d, int cls, int64_t p0, int64_t n, hipS
         case DC_DENSE: {
             const int64_t W = int64_t(1) << d.logW;
             const size_t lds = direct_window_lds(W);
-            auto kern = d.bocc ? k_direct_window<true> : k_direct_window<false>;
+            auto kern = d.occ ? k_direct_window<true> : k_direct_window<false>;
             SG_HIP(hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
             hipLaunchKernelGGL(kern, dim3(grid_1d(n)), dim3(kDirectWinNT), lds, st, d,

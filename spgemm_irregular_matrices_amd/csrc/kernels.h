@@ -269,20 +269,40 @@ struct DirectArgs {
     const double* Aval;
     const int64_t* spos;    // req x B.nrows (+1): where row k's part of slot s starts in split B
     int64_t nb;             // B.nrows
-    const uint32_t* bocc;   // null, or req x nbw words: bit k of slot s set if the slice has entries
-    int64_t nbw;            // ceil(B.nrows / 32)
+    const uint32_t* eocc;   // ceil(req/32) x A.nnz words: bit s & 31 of word
+                            // (s >> 5) * annz + q set if B row Acol[q] has entries in slot s
+    int64_t annz;           // A.nnz
+    bool occ;               // dense and rank items test eocc (runs always do)
     const uint16_t* bcol16; // partitioned B: column offset inside the slot
     const double* bval;     // partitioned B: values
     const int64_t* off;     // per item: output offset in C
     int32_t* Ccol;
     double* Cval;
+    const int64_t* rhdr;    // per run: first item id h*req + s0 | slot mask << 32
+    const int64_t* rq0;     // per run: its row's first A entry
+    const int32_t* rne;     // per run: its row's A entries
 };
+// Runs: a heavy row's items of at most kRunMax products, taken together by
+// one wavefront. A run starts at a small item's slot s0 and holds the row's
+// next small items while their products stay within kRunMax, their slots
+// within s0 + run_span(logW), and no larger item lies between them; bit t
+// of its mask marks slot s0 + t. Its output is the concatenation of its
+// items' outputs (slots in column order, the empty ones write nothing).
+constexpr int64_t kRunMax = 128;
+static_assert(kRunMax == kRankClassMax[1], "runs take the two smallest rank classes");
+__host__ __device__ constexpr int run_span(int logW) {
+    return (65536 >> logW) < 8 ? (65536 >> logW) : 8;
+}
 // The split copy of B, slot by slot: spos (req*B.n + 1 int64) from the
 // per-row slot counts bslot; bperm[p] = B entry placed at p, bcol16[p] its
-// column inside its slot.
-// bocc (optional): the slices' occupancy bits (see DirectArgs).
+// column inside its slot; roc (B.n x ceil(req/32) words): bit t of word
+// k * ceil(req/32) + w set if B row k has entries in slot 32 w + t.
 void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int64_t* spos,
-                    uint32_t* bocc, int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st);
+                    uint32_t* roc, int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st);
+// The occupancy words of every A entry's B row, slot-word-major (see
+// DirectArgs::eocc).
+void direct_entry_occ(const int32_t* acol, int64_t annz, int req, const uint32_t* roc,
+                      uint32_t* eocc, hipStream_t st);
 // Items test the occupancy bits before reading a slice's bounds when the B
 // rows that the products come from average fewer than req / kOccSparse
 // entries (a product-weighted mean), so that most (B row, slot) slices of
@@ -301,11 +321,21 @@ void direct_classify(const int64_t* elem_fin, int64_t nitems, int req, const int
                      int64_t* bins, Arena& ar, hipStream_t st);
 void direct_gather_values(const int64_t* bperm, const double* bval, int64_t nnz, double* out,
                           hipStream_t st);
-// out6 = {dense items: products, outputs, A entries read; rank items: the same}.
+// out8 = {dense items: products, outputs, A entries read; rank items of more
+// than kRunMax products: the same; items of at most kRunMax: products,
+// outputs}.
 void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
-                   const int64_t* elem_fin, const int64_t* dist_fin, int64_t* out6, Arena& ar,
+                   const int64_t* elem_fin, const int64_t* dist_fin, int64_t* out8, Arena& ar,
                    hipStream_t st);
 size_t direct_window_lds(int64_t W);
 void direct_accumulate(const DirectArgs& d, int cls, int64_t p0, int64_t n, hipStream_t st);
+// Runs of the heavy rows' small items, in the order of their first slot
+// (all rows' runs that start in slot 0 first): rhdr/rq0/rne (at most H*req
+// of them), and meta = {runs, A entries read, (entry, slot) slice bounds
+// read}.
+void direct_runs(const int64_t* elem_fin, int64_t H, int req, int logW, const int64_t* hq0,
+                 const int64_t* hq1, int64_t* rhdr, int64_t* rq0, int32_t* rne, int64_t* meta,
+                 Arena& ar, hipStream_t st);
+void direct_accumulate_runs(const DirectArgs& d, int64_t nruns, hipStream_t st);
 
 }  // namespace sg

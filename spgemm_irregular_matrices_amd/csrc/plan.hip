@@ -80,6 +80,14 @@ struct BatchState {
 
 // Pinned host words: 64 for small scalars, then the u histogram (int32).
 constexpr int kHostWords = 64 + sg::kUHistBuckets / 2;
+// The direct path's metadata, read back in one copy: its class starts
+// (DC_COUNT + 1), the totals of direct_totals (8), the product-weighted
+// B-row length sum (a double), and the runs' count, A entries and
+// (entry, slot) pairs.
+constexpr int kDirTot = sg::DC_COUNT + 1;
+constexpr int kDirLenSq = kDirTot + 8;
+constexpr int kDirRuns = kDirLenSq + 1;
+constexpr int kDirMeta = kDirRuns + 3;
 
 struct spgemm_plan_s {
     spgemm_options opt{};
@@ -119,7 +127,9 @@ struct spgemm_plan_s {
     bool direct_occ = false;  // items test the slices' occupancy bits
     int64_t direct_W = 0;    // their width
     int64_t dir_bins[DC_COUNT + 1] = {};
-    int64_t dir_tot[6] = {};  // dense / rank items: products, outputs, A entries read
+    // dense / rank items: products, outputs, A entries read; runs: products, outputs
+    int64_t dir_tot[8] = {};
+    int64_t dir_runs[3] = {};  // runs, their A entries and (entry, slot) pairs read
     int64_t light_annz = 0;   // A entries of the light rows
     int64_t light_cnnz = 0;   // output entries of the light rows
     // debug dumps (kept for single-batch products)
@@ -793,22 +803,28 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
             direct_split_b(B, bslot, (int)req, wfin_d,
                            ar.get<int64_t>("spos", (size_t)(B.n * req + 1)),
-                           ar.get<uint32_t>("bocc", (size_t)(req * ceil_div(B.n, 32) + 1)),
+                           ar.get<uint32_t>("roc", (size_t)(B.n * ceil_div(req, 32) + 1)),
                            ar.get<int64_t>("bperm", (size_t)B.nnz + 1),
                            ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1), ar, st);
-            // class starts and totals side by side, read back with nnz(C)
-            int64_t* bins = ar.get<int64_t>("dmeta", DC_COUNT + 1 + 6 + 1);
-            entry_len_sq(S, A.nnz, (double*)(bins + DC_COUNT + 1 + 6), st);
+            // class starts, totals and the runs' counts side by side, read
+            // back with nnz(C)
+            int64_t* bins = ar.get<int64_t>("dmeta", kDirMeta);
+            entry_len_sq(S, A.nnz, (double*)(bins + kDirLenSq), st);
             direct_classify(elem_fin, p->H * req, (int)req, ar.get<int64_t>("h_q0", (size_t)p->H),
                             ar.get<int64_t>("h_q1", (size_t)p->H),
                             ar.get<int32_t>("ditems", (size_t)(p->H * req)),
                             ar.get<int64_t>("diq0", (size_t)(p->H * req)),
                             ar.get<int32_t>("dine", (size_t)(p->H * req)), bins, ar, st);
-            int64_t* tot6 = bins + DC_COUNT + 1;
             direct_totals(ar.get<int64_t>("h_q0", (size_t)p->H), ar.get<int64_t>("h_q1", (size_t)p->H),
-                          p->H, (int)req, elem_fin, dist_fin, tot6, ar, st);
+                          p->H, (int)req, elem_fin, dist_fin, bins + kDirTot, ar, st);
+            // the items of at most kRunMax products, merged per row into runs
+            direct_runs(elem_fin, p->H, (int)req, ilog2(wfin_d),
+                        ar.get<int64_t>("h_q0", (size_t)p->H), ar.get<int64_t>("h_q1", (size_t)p->H),
+                        ar.get<int64_t>("rhdr", (size_t)(p->H * req)),
+                        ar.get<int64_t>("rq0", (size_t)(p->H * req)),
+                        ar.get<int32_t>("rne", (size_t)(p->H * req)), bins + kDirRuns, ar, st);
             add_bytes(p, 0, SPGEMM_PHASE_HISTO, 20.0 * B.nnz + 4.0 * B.n * (req + 1) +
-                                                    8.0 * p->H * req);
+                                                    24.0 * p->H * req);
         }
         if (p->direct) {
             // the items are the final chunks: C-hat's row pointers and the
@@ -887,20 +903,30 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
     // the light rows' output entries, read back with nnz(C)
     SG_HIP(hipMemcpyAsync(p->host + 40, st4 + 9, sizeof(int64_t), hipMemcpyDeviceToHost, st));
     if (p->direct) {
-        // nnz(C) and the direct path's class starts and totals in one wait
-        constexpr int kMeta = DC_COUNT + 1 + 6 + 1;
-        static_assert(1 + kMeta <= 64, "staging buffer");
-        SG_HIP(hipMemcpyAsync(p->host + 1, ar.get<int64_t>("dmeta", kMeta),
-                              kMeta * sizeof(int64_t), hipMemcpyDeviceToHost, st));
+        // nnz(C) and the direct path's class starts, totals and runs in one wait
+        static_assert(1 + kDirMeta <= 40, "staging buffer");
+        SG_HIP(hipMemcpyAsync(p->host + 1, ar.get<int64_t>("dmeta", kDirMeta),
+                              kDirMeta * sizeof(int64_t), hipMemcpyDeviceToHost, st));
         const int64_t* h = d2h(p, C_rp + n, 1, st);
         nnz_c = h[0];
         for (int b = 0; b <= DC_COUNT; ++b) p->dir_bins[b] = h[1 + b];
-        for (int i = 0; i < 6; ++i) p->dir_tot[i] = h[2 + DC_COUNT + i];
+        for (int i = 0; i < 8; ++i) p->dir_tot[i] = h[1 + kDirTot + i];
+        for (int i = 0; i < 3; ++i) p->dir_runs[i] = h[1 + kDirRuns + i];
         double len_sq;
-        memcpy(&len_sq, &h[8 + DC_COUNT], sizeof(double));
+        memcpy(&len_sq, &h[1 + kDirLenSq], sizeof(double));
         // the mean B-row length a product sees, against the slots per row
         const double seen = p->stats.sum_products > 0 ? len_sq / (double)p->stats.sum_products : 0.0;
         p->direct_occ = seen * kOccSparse < (double)p->direct_req;
+        if (p->H > 0) {
+            // the runs test the bits always; the other items when most of
+            // their slices are empty
+            PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
+            const int64_t req = p->direct_req;
+            direct_entry_occ(A.col, A.nnz, (int)req,
+                             ar.get<uint32_t>("roc", (size_t)(B.n * ceil_div(req, 32) + 1)),
+                             ar.get<uint32_t>("eocc", (size_t)(ceil_div(req, 32) * A.nnz + 1)), st);
+            add_bytes(p, 0, SPGEMM_PHASE_HISTO, (4.0 + 8.0 * ceil_div(req, 32)) * A.nnz);
+        }
     } else {
         nnz_c = d2h(p, C_rp + n, 1, st)[0];
     }
@@ -1005,13 +1031,17 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         d.Aval = A.val;
         d.spos = ar.get<int64_t>("spos", (size_t)(B.n * req + 1));
         d.nb = B.n;
-        d.nbw = ceil_div(B.n, 32);
-        d.bocc = p->direct_occ ? ar.get<uint32_t>("bocc", (size_t)(req * d.nbw + 1)) : nullptr;
+        d.annz = A.nnz;
+        d.eocc = ar.get<uint32_t>("eocc", (size_t)(ceil_div(req, 32) * A.nnz + 1));
+        d.occ = p->direct_occ;
         d.bcol16 = ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1);
         d.bval = bpval;
         d.off = ar.get<int64_t>("doff", (size_t)(p->H * req));
         d.Ccol = C_col;
         d.Cval = C_val;
+        d.rhdr = ar.get<int64_t>("rhdr", (size_t)(p->H * req));
+        d.rq0 = ar.get<int64_t>("rq0", (size_t)(p->H * req));
+        d.rne = ar.get<int32_t>("rne", (size_t)(p->H * req));
         // Bytes per class: every product's B operand (16-bit column and
         // value, read once), every output entry written once, and each item's
         // reads of its row's entries (column, B row start, value, slice bounds).
@@ -1021,11 +1051,16 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
             // numeric calls; the structure may not)
             direct_gather_values(ar.get<int64_t>("bperm", (size_t)B.nnz + 1), B.val, B.nnz, bpval,
                                  st);
-            for (int b = DC_RANK0; b < DC_EMPTY; ++b)
+            // the two smallest classes are taken by the runs
+            direct_accumulate_runs(d, p->dir_runs[0], st);
+            for (int b = DC_RANK0 + 2; b < DC_EMPTY; ++b)
                 direct_accumulate(d, b, p->dir_bins[b], p->dir_bins[b + 1] - p->dir_bins[b], st);
+            // runs: each reads its row's entries (12 B) and the slice bounds
+            // of every (entry, slot) pair (16 B)
             add_bytes(p, 1, SPGEMM_PHASE_DIRECT_RANK,
-                      24.0 * B.nnz + 10.0 * p->dir_tot[3] + 12.0 * p->dir_tot[4] +
-                          28.0 * p->dir_tot[5]);
+                      24.0 * B.nnz + 10.0 * (p->dir_tot[3] + p->dir_tot[6]) +
+                          12.0 * (p->dir_tot[4] + p->dir_tot[7]) + 28.0 * p->dir_tot[5] +
+                          12.0 * p->dir_runs[1] + 16.0 * p->dir_runs[2]);
         }
         {
             PhaseScope ps(p, 1, SPGEMM_PHASE_DIRECT_DENSE, st);

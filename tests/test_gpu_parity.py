@@ -213,6 +213,65 @@ def test_rank_classes_with_partial_groups(counts):
     compare(A, B, rp, col, val)
 
 
+# (row pattern {slot: products}, one B row per product?) for the runs test
+RUN_PATTERNS = [
+    ({0: 5, 2: 7, 5: 9, 6: 3, 10: 2, 11: 1, 20: 4}, False),  # gaps, span breaks
+    ({0: 60, 1: 50, 2: 30, 3: 100, 4: 128, 5: 1}, False),    # product cap breaks
+    ({0: 10, 1: 200, 2: 10, 3: 10, 4: 3000, 5: 10}, False),  # larger items between
+    ({s: 2 for s in range(9)}, True),                        # nine one-product slots
+    ({s: 5 for s in range(8)}, True),                        # 40 entries x 8 slots
+    ({0: 35, 3: 35}, True),                                  # 70 entries x 2 slots
+    ({30: 4, 31: 23}, False),                                # the last slots
+    ({s: 2 for s in range(16)}, False),                      # two full spans
+]
+
+
+def _run_rows(W, ncols, seed):
+    """Heavy rows whose (row, slot) items hold given product counts: each
+    item is formed by B rows whose distinct columns all lie in that slot
+    (one product each when split, else at most W each), and one extra row
+    of 20 entries whose B rows each hold a column in slots 0, 1 and 3."""
+    rng = np.random.default_rng(seed)
+    brows, arows = [], []
+    for pat, split in RUN_PATTERNS:
+        row = []
+        for s, c in sorted(pat.items()):
+            pieces = [1] * c if split else [min(W, c - i) for i in range(0, c, W)]
+            for L in pieces:
+                row.append(len(brows))
+                brows.append(sorted((s * W + rng.choice(W, size=L, replace=False)).tolist()))
+        arows.append(row)
+    row = []
+    for _ in range(20):
+        row.append(len(brows))
+        brows.append([int(s * W + rng.integers(W)) for s in (0, 1, 3)])
+    arows.append(row)
+    nb = len(brows)
+    A0 = synth.from_rows(len(arows), nb, arows)
+    B0 = synth.from_rows(nb, ncols, brows)
+    A = synth.CSR(A0.nrows, nb, A0.rowptr, A0.col, synth.uniform_values(111, A0.nnz))
+    B = synth.CSR(nb, ncols, B0.rowptr, B0.col, synth.uniform_values(112, B0.nnz))
+    return A, B
+
+
+@pytest.mark.parametrize("W", [64, 1024, 8192, 16384])
+def test_runs_of_small_items(W):
+    """The items of at most 128 products are accumulated in runs: a run holds
+    a row's next small items while their products stay within 128, their
+    slots within min(8, 65536 / W) of its first and no larger item lies
+    between them. The rows cover runs with empty slots inside, breaks at the
+    product cap, at the span and at larger items, and runs whose (entry, slot)
+    pairs take several rounds; every row is heavy, over 32 slots of width W."""
+    A, B = _run_rows(W, 32 * W, seed=110 + W)
+    # a width of 16384 needs the whole 160 KiB of a CU's LDS for the window
+    lds = 160 * 1024 if W > 8192 else 0
+    rp, col, val, st = run_gpu(A, B, tau_override=16, chunk_width_override=W,
+                               lds_budget_bytes=lds)
+    assert st["numeric_path"] == 3 and st["final_chunk_width"] == W, st
+    assert st["heavy_rows"] == A.nrows
+    compare(A, B, rp, col, val)
+
+
 def test_short_b_rows_over_many_slots():
     """B rows of 4 entries over 2^18 columns (32 slots): most (B row, slot)
     slices of a heavy row's items are empty, so the items test the slices'
