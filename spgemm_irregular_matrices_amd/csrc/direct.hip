@@ -83,7 +83,7 @@ constexpr int kBpartNT = 256;
 
 __global__ __launch_bounds__(kBpartNT) void k_bpartition(const int64_t* brp, const int32_t* bcol,
                                                          int64_t nb, int logW, int req,
-                                                         const int64_t* spos, int64_t* bperm,
+                                                         const int32_t* spos, int32_t* bperm,
                                                          uint16_t* bcol16) {
     extern __shared__ int lds_b[];
     const int w = threadIdx.x / kWave, lane = lane_id();
@@ -109,8 +109,8 @@ __global__ __launch_bounds__(kBpartNT) void k_bpartition(const int64_t* brp, con
             const uint64_t m = __ballot(sl == ls);
             const int base = run[ls];
             if (sl == ls) {
-                const int64_t pos = spos[(int64_t)ls * nb + k] + base + __popcll(m & lt);
-                bperm[pos] = e;
+                const int32_t pos = spos[(int64_t)ls * nb + k] + base + __popcll(m & lt);
+                bperm[pos] = (int32_t)e;
                 bcol16[pos] = (uint16_t)((uint32_t)c & wmask);
             }
             if (lane == leader) run[ls] = base + __popcll(m);
@@ -119,19 +119,20 @@ __global__ __launch_bounds__(kBpartNT) void k_bpartition(const int64_t* brp, con
     }
 }
 
-void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int64_t* spos,
-                    uint32_t* roc, int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st) {
-    if (W > 65536 || req > kDirectMaxSlots) throw std::logic_error("direct split limits");
+void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int32_t* spos,
+                    uint32_t* roc, int32_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st) {
+    if (W > 65536 || req > kDirectMaxSlots || B.nnz > INT32_MAX)
+        throw std::logic_error("direct split limits");
     const int64_t n = (int64_t)req * B.n;
     if (B.n <= 0) {
-        fill<int64_t>(spos, 1, 0, st);
+        fill<int32_t>(spos, 1, 0, st);
         return;
     }
     int32_t* bslotT = ar.get<int32_t>("bslotT", (size_t)n);
     hipLaunchKernelGGL(k_bslot_transpose, dim3(grid_1d(ceil_div(B.n, 32)), ceil_div(req, 32)),
                        dim3(256), 0, st, bslot, B.n, req, bslotT, roc);
     SG_LAUNCH_CHECK();
-    scan_exclusive(LoadI32{bslotT}, n, spos, ar, st);
+    scan_exclusive<LoadI32, int32_t>(LoadI32{bslotT}, n, spos, ar, st);
     if (B.nnz <= 0) return;
     const size_t lds = (size_t)(kBpartNT / kWave) * req * 4;
     SG_HIP(hipFuncSetAttribute((const void*)k_bpartition,
@@ -241,14 +242,14 @@ void direct_classify(const int64_t* elem_fin, int64_t nitems, int req, const int
 }
 
 // ---------------------------------------------------------------- numeric
-__global__ void k_gather_bval(const int64_t* bperm, const double* bval, int64_t nnz,
+__global__ void k_gather_bval(const int32_t* bperm, const double* bval, int64_t nnz,
                               double* out) {
     int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (; j < nnz; j += stride) out[j] = bval[bperm[j]];
 }
 
-void direct_gather_values(const int64_t* bperm, const double* bval, int64_t nnz, double* out,
+void direct_gather_values(const int32_t* bperm, const double* bval, int64_t nnz, double* out,
                           hipStream_t st) {
     if (nnz <= 0) return;
     const int64_t blocks = std::min<int64_t>(ceil_div(nnz, 256), 8192);
@@ -272,7 +273,7 @@ __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int6
         // with the occupancy bits, an empty (B row, slot) slice reads no bounds
         int64_t lo = 0;
         if (!OCC || (d.eocc[(int64_t)(s >> 5) * d.annz + q] >> (s & 31)) & 1u) {
-            const int64_t* sp = d.spos + (int64_t)s * d.nb + k;
+            const int32_t* sp = d.spos + (int64_t)s * d.nb + k;
             lo = sp[0];
             len = (int)(sp[1] - lo);
         }
@@ -298,7 +299,7 @@ __device__ __forceinline__ void stage_load(const DirectArgs& d, int64_t q, bool 
     lo = 0;
     len = 0;
     if (!OCC || (d.eocc[(int64_t)(s >> 5) * d.annz + q] >> (s & 31)) & 1u) {
-        const int64_t* sp = d.spos + (int64_t)s * d.nb + k;
+        const int32_t* sp = d.spos + (int64_t)s * d.nb + k;
         lo = sp[0];
         len = (int)(sp[1] - lo);
     }
@@ -520,7 +521,7 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
 #pragma unroll
         for (int u = 0; u < IPG; ++u) {
             const int s = (int)((uint32_t)x[u] & (uint32_t)(d.req - 1));
-            const int64_t* sp = d.spos + (int64_t)s * d.nb + k[u];
+            const int32_t* sp = d.spos + (int64_t)s * d.nb + k[u];
             lo[u] = sp[0];
             hi[u] = sp[1];
         }
@@ -585,7 +586,7 @@ __device__ __forceinline__ void run_item(const DirectArgs& d, int64_t hdr, int64
             len = 0;
             // with the occupancy bits, an empty slice reads no bounds
             if (!OCC || (d.eocc[(int64_t)(s >> 5) * d.annz + q] >> (s & 31)) & 1u) {
-                const int64_t* sp = d.spos + (int64_t)s * d.nb + k;
+                const int32_t* sp = d.spos + (int64_t)s * d.nb + k;
                 lo = sp[0];
                 len = (jl < epr && j < ne) ? (int)(sp[1] - lo) : 0;
             }
@@ -685,7 +686,7 @@ __global__ __launch_bounds__(kWave) void k_direct_runs(DirectArgs d, int64_t nru
         lo[u] = 0;
         hi[u] = 0;
         if (!OCC || (d.eocc[(int64_t)(s >> 5) * d.annz + q[u]] >> (s & 31)) & 1u) {
-            const int64_t* sp = d.spos + (int64_t)s * d.nb + k[u];
+            const int32_t* sp = d.spos + (int64_t)s * d.nb + k[u];
             lo[u] = sp[0];
             hi[u] = sp[1];
         }

@@ -267,7 +267,7 @@ struct DirectArgs {
     const int32_t* ine;     // per position of items: its row's A entries
     const int32_t* Acol;
     const double* Aval;
-    const int64_t* spos;    // req x B.nrows (+1): where row k's part of slot s starts in split B
+    const int32_t* spos;    // req x B.nrows (+1): where row k's part of slot s starts in split B
     int64_t nb;             // B.nrows
     const uint32_t* eocc;   // ceil(req/32) x A.nnz words: bit s & 31 of word
                             // (s >> 5) * annz + q set if B row Acol[q] has entries in slot s
@@ -293,12 +293,12 @@ static_assert(kRunMax == kRankClassMax[1], "runs take the two smallest rank clas
 __host__ __device__ constexpr int run_span(int logW) {
     return (65536 >> logW) < 8 ? (65536 >> logW) : 8;
 }
-// The split copy of B, slot by slot: spos (req*B.n + 1 int64) from the
+// The split copy of B, slot by slot (B.nnz < 2^31): spos (req*B.n + 1) from the
 // per-row slot counts bslot; bperm[p] = B entry placed at p, bcol16[p] its
 // column inside its slot; roc (B.n x ceil(req/32) words): bit t of word
 // k * ceil(req/32) + w set if B row k has entries in slot 32 w + t.
-void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int64_t* spos,
-                    uint32_t* roc, int64_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st);
+void direct_split_b(const DevCSR& B, const int32_t* bslot, int req, int64_t W, int32_t* spos,
+                    uint32_t* roc, int32_t* bperm, uint16_t* bcol16, Arena& ar, hipStream_t st);
 // The occupancy words of every A entry's B row, slot-word-major (see
 // DirectArgs::eocc).
 void direct_entry_occ(const int32_t* acol, int64_t annz, int req, const uint32_t* roc,
@@ -319,7 +319,7 @@ void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int re
 void direct_classify(const int64_t* elem_fin, int64_t nitems, int req, const int64_t* hq0,
                      const int64_t* hq1, int32_t* items, int64_t* iq0, int32_t* ine,
                      int64_t* bins, Arena& ar, hipStream_t st);
-void direct_gather_values(const int64_t* bperm, const double* bval, int64_t nnz, double* out,
+void direct_gather_values(const int32_t* bperm, const double* bval, int64_t nnz, double* out,
                           hipStream_t st);
 // out8 = {dense items: products, outputs, A entries read; rank items of more
 // than kRunMax products: the same; items of at most kRunMax: products,

@@ -744,7 +744,7 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
         const bool direct_ok = p->fused_sym && wfin_d >= 32 && wfin_d <= 65536 &&
                                req <= kDirectMaxSlots &&
                                direct_window_lds(wfin_d) + 8192 <= (size_t)p->dev_lds &&
-                               p->H * req < (int64_t(1) << 31);
+                               p->H * req < (int64_t(1) << 31) && B.nnz <= INT32_MAX;
         p->direct = direct_ok && (p->opt.numeric_mode == 3 ||
                                   (p->opt.numeric_mode == 0 && !p->opt.debug_dump));
         p->direct_req = (int)req;
@@ -802,9 +802,9 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
             int32_t* bslot = ar.get<int32_t>("bslot", (size_t)(B.n * req + 1));
             direct_split_b(B, bslot, (int)req, wfin_d,
-                           ar.get<int64_t>("spos", (size_t)(B.n * req + 1)),
+                           ar.get<int32_t>("spos", (size_t)(B.n * req + 1)),
                            ar.get<uint32_t>("roc", (size_t)(B.n * ceil_div(req, 32) + 1)),
-                           ar.get<int64_t>("bperm", (size_t)B.nnz + 1),
+                           ar.get<int32_t>("bperm", (size_t)B.nnz + 1),
                            ar.get<uint16_t>("bcol16", (size_t)B.nnz + 1), ar, st);
             // class starts, totals and the runs' counts side by side, read
             // back with nnz(C)
@@ -1029,7 +1029,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         d.ine = ar.get<int32_t>("dine", (size_t)(p->H * req));
         d.Acol = A.col;
         d.Aval = A.val;
-        d.spos = ar.get<int64_t>("spos", (size_t)(B.n * req + 1));
+        d.spos = ar.get<int32_t>("spos", (size_t)(B.n * req + 1));
         d.nb = B.n;
         d.annz = A.nnz;
         d.eocc = ar.get<uint32_t>("eocc", (size_t)(ceil_div(req, 32) * A.nnz + 1));
@@ -1049,7 +1049,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
             PhaseScope ps(p, 1, SPGEMM_PHASE_DIRECT_RANK, st);
             // B's values in the split order (values may change between
             // numeric calls; the structure may not)
-            direct_gather_values(ar.get<int64_t>("bperm", (size_t)B.nnz + 1), B.val, B.nnz, bpval,
+            direct_gather_values(ar.get<int32_t>("bperm", (size_t)B.nnz + 1), B.val, B.nnz, bpval,
                                  st);
             // the two smallest classes are taken by the runs
             direct_accumulate_runs(d, p->dir_runs[0], st);

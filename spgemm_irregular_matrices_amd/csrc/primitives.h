@@ -68,10 +68,11 @@ __global__ __launch_bounds__(kScanNT) void k_scan_reduce(F f, int64_t n, int64_t
 }
 
 // out[i] = sum_{i' < i} f(i') for i in [0, n], so out[n] is the total.
-// `tile_off` holds the exclusive prefix of the tile sums.
-template <class F>
+// `tile_off` holds the exclusive prefix of the tile sums. T: the output
+// type (the caller guarantees that the total fits it).
+template <class F, class T = int64_t>
 __global__ __launch_bounds__(kScanNT) void k_scan_apply(F f, int64_t n, const int64_t* tile_off,
-                                                        int64_t* out) {
+                                                        T* out) {
     __shared__ int64_t sh[kScanNT / kWave + 1];
     int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanIPT;
     int64_t v[kScanIPT];
@@ -87,19 +88,19 @@ __global__ __launch_bounds__(kScanNT) void k_scan_apply(F f, int64_t n, const in
 #pragma unroll
     for (int j = 0; j < kScanIPT; ++j) {
         int64_t i = base + j;
-        if (i < n) out[i] = pre;
+        if (i < n) out[i] = (T)pre;
         pre += v[j];
-        if (i == n - 1) out[n] = pre;
+        if (i == n - 1) out[n] = (T)pre;
     }
 }
 
 // Exclusive scan of f over [0, n) into out[0..n]. `out` may alias the array
 // that f reads only when each element is read by the same tile that writes it
 // (true for an identity load of `out` itself).
-template <class F>
-void scan_exclusive(F f, int64_t n, int64_t* out, Arena& ar, hipStream_t st, int depth = 0) {
+template <class F, class T = int64_t>
+void scan_exclusive(F f, int64_t n, T* out, Arena& ar, hipStream_t st, int depth = 0) {
     if (n <= 0) {
-        fill<int64_t>(out, 1, 0, st);
+        fill<T>(out, 1, 0, st);
         return;
     }
     int64_t tiles = ceil_div(n, kScanTile);
@@ -111,7 +112,8 @@ void scan_exclusive(F f, int64_t n, int64_t* out, Arena& ar, hipStream_t st, int
         SG_LAUNCH_CHECK();
         scan_exclusive(LoadI64{ts}, tiles, ts, ar, st, depth + 1);
     }
-    hipLaunchKernelGGL(k_scan_apply<F>, dim3(grid_1d(tiles)), dim3(kScanNT), 0, st, f, n, ts, out);
+    auto apply = k_scan_apply<F, T>;  // (a template-id with a comma cannot be a macro argument)
+    hipLaunchKernelGGL(apply, dim3(grid_1d(tiles)), dim3(kScanNT), 0, st, f, n, ts, out);
     SG_LAUNCH_CHECK();
 }
 
