@@ -90,6 +90,16 @@ __device__ __forceinline__ int wave_inclusive_scan_i32(int x) {
     return x;
 }
 
+// Sum over each row of 16 lanes (DPP shifts by 1, 2, 4 and 8 inside the
+// row); the row's last lane (lane % 16 == 15) receives the row's total.
+__device__ __forceinline__ int row16_sum_i32(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    return x;
+}
+
 // Inclusive scan across the 64 lanes of a wavefront.
 template <class T>
 __device__ __forceinline__ T wave_inclusive_scan(T v) {

@@ -76,9 +76,11 @@ struct LoadI32 {
 
 // One wavefront per B row: each entry goes to its slot's part of the split
 // copy, at the row's start there plus its rank among the row's entries of
-// that slot. The wave ranks each batch of 64 entries by peeling one
-// distinct slot at a time (ballot of the lanes holding the first remaining
-// lane's slot); the row's running counts per slot live in the wave's LDS.
+// that slot. Every lane reads its slot's start first (one round of loads
+// for the batch); the wave then ranks each batch of 64 entries by peeling
+// one distinct slot at a time (ballot of the lanes holding the first
+// remaining lane's slot), touching only LDS, where the row's running counts
+// per slot live.
 constexpr int kBpartNT = 256;
 
 __global__ __launch_bounds__(kBpartNT) void k_bpartition(const int64_t* brp, const int32_t* bcol,
@@ -98,23 +100,26 @@ __global__ __launch_bounds__(kBpartNT) void k_bpartition(const int64_t* brp, con
         const int64_t e = eb + lane;
         int32_t c = 0;
         int sl = -1;
+        int32_t p0 = 0;
         if (e < e1) {
             c = bcol[e];
             sl = (int)((uint32_t)c >> logW);
+            p0 = spos[(int64_t)sl * nb + k];
         }
+        int rank = 0;
         uint64_t act = __ballot(sl >= 0);
         while (act) {
             const int leader = __builtin_ctzll(act);
             const int ls = __builtin_amdgcn_readlane(sl, leader);
             const uint64_t m = __ballot(sl == ls);
             const int base = run[ls];
-            if (sl == ls) {
-                const int32_t pos = spos[(int64_t)ls * nb + k] + base + __popcll(m & lt);
-                bperm[pos] = (int32_t)e;
-                bcol16[pos] = (uint16_t)((uint32_t)c & wmask);
-            }
+            if (sl == ls) rank = base + __popcll(m & lt);
             if (lane == leader) run[ls] = base + __popcll(m);
             act &= ~m;
+        }
+        if (sl >= 0) {
+            bperm[p0 + rank] = (int32_t)e;
+            bcol16[p0 + rank] = (uint16_t)((uint32_t)c & wmask);
         }
     }
 }

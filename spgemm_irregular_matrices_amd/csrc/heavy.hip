@@ -1106,15 +1106,22 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
     if (wps >= 8) {
         // eight consecutive words per thread (all in one slot), summed over
         // the lps lanes that share the slot (the active lanes of a wave are
-        // a prefix of whole slots: nwp and wps are powers of two)
+        // a prefix of whole slots: nwp and wps are powers of two); 16 or
+        // more lanes a slot: each row of 16 lanes sums by DPP and adds once
         const int lps = min(wps / 8, kWave);
+        const int lgw = __builtin_ctz(wps);
         for (int i0 = tt * 8; i0 < nwp; i0 += kHsymNT * 8) {
             const uint4 wa = *(const uint4*)&bits[i0];
             const uint4 wb = *(const uint4*)&bits[i0 + 4];
             int pc = __popc(wa.x) + __popc(wa.y) + __popc(wa.z) + __popc(wa.w) + __popc(wb.x) +
                      __popc(wb.y) + __popc(wb.z) + __popc(wb.w);
-            for (int dd = 1; dd < lps; dd <<= 1) pc += __shfl_xor(pc, dd, kWave);
-            if ((lane & (lps - 1)) == 0 && pc) atomicAdd(&dsl[i0 / wps], pc);
+            if (lps >= 16) {
+                pc = row16_sum_i32(pc);
+                if ((lane & 15) == 15 && pc) atomicAdd(&dsl[i0 >> lgw], pc);
+            } else {
+                for (int dd = 1; dd < lps; dd <<= 1) pc += __shfl_xor(pc, dd, kWave);
+                if ((lane & (lps - 1)) == 0 && pc) atomicAdd(&dsl[i0 >> lgw], pc);
+            }
         }
     } else {
         for (int i = tt; i < nwp; i += kHsymNT) {
@@ -1206,18 +1213,22 @@ __global__ __launch_bounds__(kBpartNT) void k_bpart_scatter(const int64_t* brp,
         const int64_t e = eb + lane;
         const int32_t col = e < e1 ? bcol[e] : 0;
         const int pt = e < e1 ? (int)((uint32_t)col >> shift) : -1;
+        // the segment starts are read before the ranking, one round a batch
+        const int64_t p0 = pt >= 0 ? ppos[(int64_t)pt * nb + k] : 0;
+        int rank = 0;
         uint64_t act = __ballot(pt >= 0);
         while (act) {
             const int leader = __builtin_ctzll(act);
             const int lp = __builtin_amdgcn_readlane(pt, leader);
             const uint64_t m = __ballot(pt == lp);
             const int base = run[lp];  // read by every lane before the leader adds
-            if (pt == lp) pcol[ppos[(int64_t)lp * nb + k] + base + lane_prefix(m)] = col;
+            if (pt == lp) rank = base + lane_prefix(m);
             wave_lds_sync();
             if (lane == leader) run[lp] = base + __popcll(m);
             wave_lds_sync();
             act &= ~m;
         }
+        if (pt >= 0) pcol[p0 + rank] = col;
     }
 }
 
