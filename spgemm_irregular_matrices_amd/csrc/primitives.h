@@ -69,28 +69,48 @@ __global__ __launch_bounds__(kScanNT) void k_scan_reduce(F f, int64_t n, int64_t
 
 // out[i] = sum_{i' < i} f(i') for i in [0, n], so out[n] is the total.
 // `tile_off` holds the exclusive prefix of the tile sums. T: the output
-// type (the caller guarantees that the total fits it).
+// type (the caller guarantees that the total fits it). The tile passes
+// through LDS, so that global loads and stores are coalesced (consecutive
+// lanes, consecutive elements) while each thread scans 16 consecutive
+// elements; one padding word every 32 keeps the per-thread reads apart in
+// the banks.
 template <class F, class T = int64_t>
 __global__ __launch_bounds__(kScanNT) void k_scan_apply(F f, int64_t n, const int64_t* tile_off,
                                                         T* out) {
     __shared__ int64_t sh[kScanNT / kWave + 1];
-    int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanIPT;
+    __shared__ int64_t tile[kScanTile + kScanTile / 32];
+    const int64_t base = (int64_t)blockIdx.x * kScanTile;
+#pragma unroll 4
+    for (int j = 0; j < kScanIPT; ++j) {
+        const int idx = j * kScanNT + threadIdx.x;
+        const int64_t i = base + idx;
+        tile[idx + (idx >> 5)] = i < n ? f(i) : 0;
+    }
+    __syncthreads();
     int64_t v[kScanIPT];
     int64_t s = 0;
 #pragma unroll
     for (int j = 0; j < kScanIPT; ++j) {
-        int64_t i = base + j;
-        v[j] = i < n ? f(i) : 0;
+        const int idx = threadIdx.x * kScanIPT + j;
+        v[j] = tile[idx + (idx >> 5)];
         s += v[j];
     }
     int64_t tot;
+    // (the scan's barriers also order the reads above before the writes below)
     int64_t pre = block_exclusive_scan<kScanNT>(s, sh, &tot) + tile_off[blockIdx.x];
 #pragma unroll
     for (int j = 0; j < kScanIPT; ++j) {
-        int64_t i = base + j;
-        if (i < n) out[i] = (T)pre;
+        const int idx = threadIdx.x * kScanIPT + j;
+        tile[idx + (idx >> 5)] = pre;
         pre += v[j];
-        if (i == n - 1) out[n] = (T)pre;
+        if (base + idx == n - 1) out[n] = (T)pre;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int j = 0; j < kScanIPT; ++j) {
+        const int idx = j * kScanNT + threadIdx.x;
+        const int64_t i = base + idx;
+        if (i < n) out[i] = (T)tile[idx + (idx >> 5)];
     }
 }
 
