@@ -1004,74 +1004,73 @@ __global__ __launch_bounds__(kHsymNT) void k_heavy_symbolic(
         if (tt == 0) ppre[ne] = tot;
         __syncthreads();
         constexpr int U = 8;  // pieces in flight per wave
-        int j0 = 0;  // entry of the wave's last piece (pieces rise per wave)
-        for (int piece = w; piece < tot; piece += NW * U) {
-            // The entries of this iteration's pieces, read once into the
-            // lanes: lane l holds entry j0+l (first piece, length, B start)
-            // and the first piece of entry j0+1+l. A ballot counts the
-            // entries after j0 that start at or before a piece (prefixes
-            // rise), and the piece's entry is read from that lane. Only if
-            // all 64 do is the rest walked one entry at a time.
-            const int wj = j0 + lane;
-            const int pw = wj + 1 <= ne ? ppre[wj + 1] : INT_MAX;
-            const int wp = wj < ne ? ppre[wj] : 0;
-            const int wn = wj < ne ? nbv[wj] : 0;
-            const BT wb = wj < ne ? bst[wj] : (BT)0;
-            uint32_t c[U];
-            int jl = j0;
-#pragma unroll
-            for (int uu = 0; uu < U; ++uu) {
-                const int pu = piece + uu * NW;
-                c[uu] = 0xffffffffu;
-                if (pu < tot) {
-                    const int cnt = __popcll(__ballot(pw <= pu));
-                    int pj, nj;
-                    int64_t bj;
-                    if (cnt < kWave) {
-                        jl = j0 + cnt;
-                        pj = __builtin_amdgcn_readlane(wp, cnt);
-                        nj = __builtin_amdgcn_readlane(wn, cnt);
-                        if constexpr (B32)
-                            bj = (uint32_t)__builtin_amdgcn_readlane((int)wb, cnt);
-                        else
-                            bj = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
-                                                (int)((uint64_t)wb >> 32), cnt) << 32) |
-                                           (uint32_t)__builtin_amdgcn_readlane((int)wb, cnt));
-                    } else {
-                        int j = j0 + cnt;
-                        j = jl > j ? jl : j;
-                        while (ppre[j + 1] <= pu) ++j;
-                        jl = j;
-                        // every lane read the same entry: keep it scalar
-                        pj = __builtin_amdgcn_readfirstlane(ppre[j]);
-                        nj = __builtin_amdgcn_readfirstlane(nbv[j]);
-                        const BT b = bst[j];
-                        if constexpr (B32)
-                            bj = (uint32_t)__builtin_amdgcn_readfirstlane((int)b);
-                        else
-                            bj = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(
-                                                (int)((uint64_t)b >> 32)) << 32) |
-                                           (uint32_t)__builtin_amdgcn_readfirstlane((int)b));
-                    }
-                    // the piece's B row start is uniform: a scalar base and a
-                    // 32-bit lane offset
-                    const int32_t* rowp = bcol + bj;
-                    const int off = (pu - pj) * kWave + lane;
-                    if (off < nj) c[uu] = (uint32_t)rowp[(uint32_t)off];
-                }
+        // Each wave takes a contiguous run of the window's pieces, so that
+        // consecutive pieces mostly continue the same entry (long B rows)
+        // and its first piece, length and B start stay in scalar
+        // registers; a piece past the entry's end looks its entry up with
+        // a ballot over the first pieces of the next 64 entries (the
+        // entries starting at or before it are a prefix of them, as the
+        // prefixes rise; zero-piece entries are passed over).
+        const int per = (tot + NW - 1) / NW;
+        const int pb = min(tot, w * per), pe = min(tot, pb + per);
+        auto entry_of = [&](int j, int pu) {
+            for (;;) {
+                const int wj = j + 1 + lane;
+                const int pw = wj <= ne ? ppre[wj] : INT_MAX;
+                const int cnt = __popcll(__ballot(pw <= pu));
+                j += cnt;
+                if (cnt < kWave) return j;
             }
-            j0 = jl;
-            // Column c = 32 q + r sets bit r of word q ^ (r & gm), a word of
-            // q's aligned group of gm + 1 words (which never spans two
-            // slots), so that the runs of nearby columns of a B row fall
-            // into different words and banks; only per-slot counts are read.
-            // (A lane without a product holds c = ~0: its word lies far past
-            // any bitmap that fits LDS, so the bound test drops it.)
+        };
+        // entry j's first piece, next entry's first piece, length and B
+        // start, all uniform: kept in scalar registers
+        int j = 0, pj = 0, pn = 0, nj = 0;
+        int64_t bj = 0;
+        auto load_entry = [&]() {
+            pj = __builtin_amdgcn_readfirstlane(ppre[j]);
+            pn = __builtin_amdgcn_readfirstlane(ppre[j + 1]);
+            nj = __builtin_amdgcn_readfirstlane(nbv[j]);
+            const BT b = bst[j];
+            if constexpr (B32)
+                bj = (uint32_t)__builtin_amdgcn_readfirstlane((int)b);
+            else
+                bj = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(
+                                    (int)((uint64_t)b >> 32)) << 32) |
+                               (uint32_t)__builtin_amdgcn_readfirstlane((int)b));
+        };
+        if (pb < pe) {
+            j = entry_of(0, pb);
+            load_entry();
+            for (int p0 = pb; p0 < pe; p0 += U) {
+                uint32_t c[U];
 #pragma unroll
-            for (int uu = 0; uu < U; ++uu) {
-                const uint32_t q = c[uu] >> 5, r = c[uu] & 31;
-                const uint32_t wd = (q ^ (r & gm)) - wl;
-                if (wd < (uint32_t)nwp) atomicOr(&bits[wd], 1u << r);
+                for (int uu = 0; uu < U; ++uu) {
+                    const int pu = p0 + uu;
+                    c[uu] = 0xffffffffu;
+                    if (pu < pe) {
+                        if (pu >= pn) {
+                            j = entry_of(j, pu);
+                            load_entry();
+                        }
+                        // a scalar base and a 32-bit lane offset
+                        const int32_t* rowp = bcol + bj;
+                        const int off = (pu - pj) * kWave + lane;
+                        if (off < nj) c[uu] = (uint32_t)rowp[(uint32_t)off];
+                    }
+                }
+                // Column c = 32 q + r sets bit r of word q ^ (r & gm), a word
+                // of q's aligned group of gm + 1 words (which never spans two
+                // slots), so that the runs of nearby columns of a B row fall
+                // into different words and banks; only per-slot counts are
+                // read. (A lane without a product holds c = ~0: its word lies
+                // far past any bitmap that fits LDS, so the bound test drops
+                // it.)
+#pragma unroll
+                for (int uu = 0; uu < U; ++uu) {
+                    const uint32_t q = c[uu] >> 5, r = c[uu] & 31;
+                    const uint32_t wd = (q ^ (r & gm)) - wl;
+                    if (wd < (uint32_t)nwp) atomicOr(&bits[wd], 1u << r);
+                }
             }
         }
         // element counts per slot: the sum of the window's B-row slot vectors
