@@ -176,76 +176,6 @@ void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int re
     SG_LAUNCH_CHECK();
 }
 
-// ---------------------------------------------------------------- item classes
-// Class of the item at position i of the pass order: row by row (x = i),
-// or slot by slot (x = (i mod H) * req + i / H).
-struct DirectBinOf {
-    const int64_t* elem;
-    int64_t H;
-    int logreq;
-    bool slot_major;
-    __device__ int64_t item(int64_t i) const {
-        return slot_major ? ((i % H) << logreq) + i / H : i;
-    }
-    __device__ int operator()(int64_t i) const {
-        const int64_t c = elem[item(i)];
-        if (c == 0) return DC_EMPTY;
-        if (c > kDirectDense) return DC_DENSE;
-        int r = 0;
-#pragma unroll
-        for (int j = 0; j + 1 < kNumRankClasses; ++j) r += c > kRankClassMax[j];
-        return DC_RANK0 + r;
-    }
-};
-
-// Per position of the class-ordered item list: the item's row's first A
-// entry and entry count, so that an item's kernel reads its header in one
-// step instead of item -> row -> entries.
-__global__ void k_item_heads(const int32_t* items, int64_t n, int logreq, const int64_t* hq0,
-                             const int64_t* hq1, int64_t* iq0, int32_t* ine) {
-    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (p >= n) return;
-    const int64_t h = items[p] >> logreq;  // req is a power of two
-    const int64_t q0 = hq0[h];
-    iq0[p] = q0;
-    ine[p] = (int32_t)(hq1[h] - q0);
-}
-
-// The bitmap-rank classes in slot order: positions [bins[DC_RANK0],
-// bins[DC_EMPTY]) of the slot-major partition, as item ids.
-__global__ void k_rank_slot_major(const int32_t* perm_sm, const int64_t* bins, DirectBinOf bf,
-                                  int64_t n, int32_t* items) {
-    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (p >= n || p < bins[DC_RANK0] || p >= bins[DC_EMPTY]) return;
-    items[p] = (int32_t)bf.item(perm_sm[p]);
-}
-
-void direct_classify(const int64_t* elem_fin, int64_t nitems, int req, const int64_t* hq0,
-                     const int64_t* hq1, int32_t* items, int64_t* iq0, int32_t* ine,
-                     int64_t* bins, Arena& ar, hipStream_t st) {
-    const int logreq = ilog2(req);
-    const int64_t H = nitems >> logreq;
-    partition(DirectBinOf{elem_fin, H, logreq, false}, nitems, DC_COUNT, items, (int32_t*)nullptr,
-              bins, ar, st);
-    if (nitems <= 0) return;
-    if (req > 1) {
-        // the same classes (a stable partition of the same counts), with the
-        // bitmap-rank items taken slot by slot: items of one slot that run
-        // together share that slot's slice starts and B entries in cache
-        // (the dense items keep row order, which measured faster for them)
-        const DirectBinOf sm{elem_fin, H, logreq, true};
-        int32_t* perm_sm = ar.get<int32_t>("ditems_sm", (size_t)nitems);
-        int64_t* bins_sm = ar.get<int64_t>("dbins_sm", DC_COUNT + 1);
-        partition(sm, nitems, DC_COUNT, perm_sm, (int32_t*)nullptr, bins_sm, ar, st);
-        hipLaunchKernelGGL(k_rank_slot_major, dim3(grid_1d(ceil_div(nitems, 256))), dim3(256), 0,
-                           st, perm_sm, bins, sm, nitems, items);
-        SG_LAUNCH_CHECK();
-    }
-    hipLaunchKernelGGL(k_item_heads, dim3(grid_1d(ceil_div(nitems, 256))), dim3(256), 0, st, items,
-                       nitems, ilog2(req), hq0, hq1, iq0, ine);
-    SG_LAUNCH_CHECK();
-}
-
 // ---------------------------------------------------------------- numeric
 __global__ void k_gather_bval(const int32_t* bperm, const double* bval, int64_t nnz,
                               double* out) {
@@ -563,7 +493,7 @@ __device__ __forceinline__ void run_item(const DirectArgs& d, int64_t hdr, int64
                                          int64_t off, int jl, int ds, int epr, double a0,
                                          int64_t lo0, int len0, int WR, double* vals, void* rk,
                                          int* s_pre, int64_t* s_bo, double* s_a, int* s_cb) {
-    constexpr int KPT = 2;
+    constexpr int KPT = kRunKPT;
     static_assert(kWave * KPT == kRunMax, "one wavefront holds a run's products");
     const int lane = lane_id();
     const int32_t x = (int32_t)hdr;
@@ -638,7 +568,7 @@ template <bool OCC, int IPG>
 __global__ __launch_bounds__(kWave) void k_direct_runs(DirectArgs d, int64_t nruns) {
     extern __shared__ int64_t lds_u[];
     double* vals = (double*)lds_u;     // kRunMax
-    void* rk = vals + kRunMax;         // wave_rank_lds(2, run width)
+    void* rk = vals + kRunMax;         // wave_rank_lds(kRunKPT, run width)
     __shared__ int s_pre[kWave];
     __shared__ int64_t s_bo[kWave];
     __shared__ double s_a[kWave];
@@ -901,26 +831,45 @@ void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
     SG_LAUNCH_CHECK();
 }
 
-// ---------------------------------------------------------------- runs
-// One thread per heavy row walks its slots in order and forms its runs (see
-// run_span and kRunMax): markT (slot-major, req x H bytes) receives the
-// run's slot mask at (s0, h) and 0 at every other slot of the row, so that
-// a scan in slot-major order numbers the runs slot by slot (the runs of
-// slot 0 of all rows first, as the rank items run). The row's 16-slot
-// batches of item counts are read 16 bytes a load. part: per work group,
-// the A entries and the (entry, slot) pairs its runs read.
+// ---------------------------------------------------------------- work lists
+// One thread per heavy row walks its slots in order (16-slot batches of the
+// item counts, 16 bytes a load) and
+// - forms the row's runs (see run_span and kRunMax): markT (slot-major,
+//   req x H bytes) receives the run's slot mask at (s0, h) and 0 at every
+//   other slot, so that a scan in slot-major order numbers the runs slot by
+//   slot;
+// - writes each item's class among the listed rank classes (those the runs
+//   do not take: 0 .. kListedRank - 1, else kNotListed) to clsT, slot-major;
+// - counts the row's dense items (dcnt).
+// part: per work group, the A entries and the (entry, slot) pairs its runs
+// read. With `fill`, the walk instead lists the row's dense items at
+// dpos[h] (items, and the row's first A entry and entry count).
 constexpr int kRunBatch = 16;
+constexpr int kListedRank = kNumRankClasses - kRunClasses;
+constexpr uint8_t kNotListed = 0xff;
 
-__global__ __launch_bounds__(256) void k_runs_mark(const int64_t* elem_fin, int64_t H, int req,
-                                                   int span, const int64_t* hq0,
-                                                   const int64_t* hq1, uint8_t* markT,
-                                                   int64_t* part) {
+__device__ __forceinline__ uint8_t listed_rank_class(int64_t c) {
+    if (c <= kRunMax || c > kDirectDense) return kNotListed;
+    int r = 0;
+#pragma unroll
+    for (int j = kRunClasses; j + 1 < kNumRankClasses; ++j) r += c > kRankClassMax[j];
+    return (uint8_t)r;
+}
+
+template <bool FILL>
+__global__ __launch_bounds__(256) void k_items_walk(const int64_t* elem_fin, int64_t H, int req,
+                                                    int span, const int64_t* hq0,
+                                                    const int64_t* hq1, uint8_t* markT,
+                                                    uint8_t* clsT, int64_t* dcnt, int64_t* part,
+                                                    const int64_t* dpos, int32_t* items,
+                                                    int64_t* iq0, int32_t* ine) {
     __shared__ int64_t sh[256 / kWave + 1];
     const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     int64_t ent = 0, pairs = 0;
     if (h < H) {
-        const int64_t ne = hq1[h] - hq0[h];
+        const int64_t q0 = hq0[h], ne = hq1[h] - q0;
         const int64_t* e = elem_fin + h * req;
+        int64_t nd = 0, dp = FILL ? dpos[h] : 0;
         int s0 = -1;
         uint32_t mask = 0;
         int64_t cur = 0;
@@ -943,8 +892,19 @@ __global__ __launch_bounds__(256) void k_runs_mark(const int64_t* elem_fin, int6
             for (int t = 0; t < kRunBatch; ++t) {
                 const int s = sb + t;
                 if (s >= req) break;
-                markT[(int64_t)s * H + h] = 0;
                 const int64_t cs = c[t];
+                if constexpr (FILL) {
+                    if (cs > kDirectDense) {
+                        items[dp] = (int32_t)(h * req + s);
+                        iq0[dp] = q0;
+                        ine[dp] = (int32_t)ne;
+                        ++dp;
+                    }
+                    continue;
+                }
+                markT[(int64_t)s * H + h] = 0;
+                clsT[(int64_t)s * H + h] = listed_rank_class(cs);
+                nd += cs > kDirectDense;
                 if (cs == 0) continue;
                 // a larger item writes between: the run cannot span it
                 const bool big = cs > kRunMax;
@@ -964,23 +924,38 @@ __global__ __launch_bounds__(256) void k_runs_mark(const int64_t* elem_fin, int6
                 mask |= 1u << (s - s0);
             }
         }
-        if (s0 >= 0) {
-            markT[(int64_t)s0 * H + h] = (uint8_t)mask;
-            ent += ne;
-            pairs += ne * __popc(mask);
+        if constexpr (!FILL) {
+            if (s0 >= 0) {
+                markT[(int64_t)s0 * H + h] = (uint8_t)mask;
+                ent += ne;
+                pairs += ne * __popc(mask);
+            }
+            dcnt[h] = nd;
         }
     }
-    ent = block_reduce_sum<256>(ent, sh);
-    pairs = block_reduce_sum<256>(pairs, sh);
-    if (threadIdx.x == 0) {
-        part[blockIdx.x] = ent;
-        part[gridDim.x + blockIdx.x] = pairs;
+    if constexpr (!FILL) {
+        ent = block_reduce_sum<256>(ent, sh);
+        pairs = block_reduce_sum<256>(pairs, sh);
+        if (threadIdx.x == 0) {
+            part[blockIdx.x] = ent;
+            part[gridDim.x + blockIdx.x] = pairs;
+        }
     }
 }
 
 struct RunStart {
     const uint8_t* markT;
     __device__ int64_t operator()(int64_t i) const { return markT[i] != 0; }
+};
+
+// Bin of slot-major position i for the partition of the listed rank
+// classes (-1: not listed).
+struct ListedClass {
+    const uint8_t* clsT;
+    __device__ int operator()(int64_t i) const {
+        const int c = clsT[i];
+        return c == kNotListed ? -1 : c;
+    }
 };
 
 // rpos: exclusive scan of RunStart over req x H (+1).
@@ -1000,30 +975,83 @@ __global__ __launch_bounds__(256) void k_runs_scatter(const uint8_t* markT, cons
     rne[j] = (int32_t)(hq1[h] - q0);
 }
 
-__global__ void k_runs_total(const int64_t* rpos, int64_t n, int64_t* meta) { meta[0] = rpos[n]; }
+// The listed rank classes' items after the dense ones: position p of the
+// slot-major partition (perm: slot-major index) goes to items[ndense + p].
+__global__ __launch_bounds__(256) void k_rank_items(const int32_t* perm, const int64_t* lbins,
+                                                    const int64_t* dpos, int64_t H, int req,
+                                                    const int64_t* hq0, const int64_t* hq1,
+                                                    int32_t* items, int64_t* iq0, int32_t* ine) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= lbins[kListedRank]) return;
+    const int64_t i = perm[p];
+    const int64_t s = i / H, h = i - s * H;
+    const int64_t d = dpos[H] + p;
+    const int64_t q0 = hq0[h];
+    items[d] = (int32_t)(h * req + s);
+    iq0[d] = q0;
+    ine[d] = (int32_t)(hq1[h] - q0);
+}
 
-void direct_runs(const int64_t* elem_fin, int64_t H, int req, int logW, const int64_t* hq0,
-                 const int64_t* hq1, int64_t* rhdr, int64_t* rq0, int32_t* rne, int64_t* meta,
-                 Arena& ar, hipStream_t st) {
+// The class starts (DC_COUNT + 1: dense, the rank classes, empty; the run
+// classes and the empty class are empty ranges) and the run count.
+__global__ void k_class_bins(const int64_t* dpos, int64_t H, const int64_t* lbins,
+                             const int64_t* rpos, int64_t n, int64_t* bins, int64_t* run_meta) {
+    const int64_t nd = dpos[H];
+    bins[DC_DENSE] = 0;
+    for (int r = 0; r <= kRunClasses; ++r) bins[DC_RANK0 + r] = nd;
+    for (int r = 1; r <= kListedRank; ++r) bins[DC_RANK0 + kRunClasses + r] = nd + lbins[r];
+    bins[DC_COUNT] = nd + lbins[kListedRank];
+    run_meta[0] = rpos[n];
+}
+
+void direct_classify(const int64_t* elem_fin, int64_t H, int req, int logW, const int64_t* hq0,
+                     const int64_t* hq1, int32_t* items, int64_t* iq0, int32_t* ine,
+                     int64_t* bins, int64_t* rhdr, int64_t* rq0, int32_t* rne, int64_t* run_meta,
+                     Arena& ar, hipStream_t st) {
+    static_assert(DC_RANK0 + kNumRankClasses == DC_EMPTY && DC_EMPTY + 1 == DC_COUNT,
+                  "class layout");
     if (H <= 0) {
-        fill<int64_t>(meta, 3, 0, st);
+        fill<int64_t>(bins, DC_COUNT + 1, 0, st);
+        fill<int64_t>(run_meta, 3, 0, st);
         return;
     }
     const int64_t n = H * req;
     const int64_t blocks = ceil_div(H, 256);
     uint8_t* markT = ar.get<uint8_t>("run_mark", (size_t)n);
+    uint8_t* clsT = ar.get<uint8_t>("item_cls", (size_t)n);
+    int64_t* dpos = ar.get<int64_t>("dense_pos", (size_t)H + 1);
     int64_t* part = ar.get<int64_t>("run_parts", (size_t)(2 * blocks));
-    hipLaunchKernelGGL(k_runs_mark, dim3(grid_1d(blocks)), dim3(256), 0, st, elem_fin, H, req,
-                       run_span(logW), hq0, hq1, markT, part);
+    const int span = run_span(logW);
+    hipLaunchKernelGGL(k_items_walk<false>, dim3(grid_1d(blocks)), dim3(256), 0, st, elem_fin, H,
+                       req, span, hq0, hq1, markT, clsT, dpos, part, (const int64_t*)nullptr,
+                       (int32_t*)nullptr, (int64_t*)nullptr, (int32_t*)nullptr);
     SG_LAUNCH_CHECK();
+    // the dense items, row by row
+    scan_exclusive(LoadI64{dpos}, H, dpos, ar, st);
+    hipLaunchKernelGGL(k_items_walk<true>, dim3(grid_1d(blocks)), dim3(256), 0, st, elem_fin, H,
+                       req, span, hq0, hq1, (uint8_t*)nullptr, (uint8_t*)nullptr,
+                       (int64_t*)nullptr, (int64_t*)nullptr, (const int64_t*)dpos, items, iq0,
+                       ine);
+    SG_LAUNCH_CHECK();
+    // the listed rank classes, slot by slot: items of one slot that run
+    // together share that slot's slice starts and B entries in cache
+    int32_t* perm = ar.get<int32_t>("item_perm", (size_t)n);
+    int64_t* lbins = ar.get<int64_t>("item_lbins", (size_t)kListedRank + 1);
+    partition(ListedClass{clsT}, n, kListedRank, perm, (int32_t*)nullptr, lbins, ar, st);
+    hipLaunchKernelGGL(k_rank_items, dim3(grid_1d(ceil_div(n, 256))), dim3(256), 0, st, perm,
+                       lbins, dpos, H, req, hq0, hq1, items, iq0, ine);
+    SG_LAUNCH_CHECK();
+    // the runs, in the order of their first slot
     int64_t* rpos = ar.get<int64_t>("run_pos", (size_t)n + 1);
     scan_exclusive(RunStart{markT}, n, rpos, ar, st);
     hipLaunchKernelGGL(k_runs_scatter, dim3(grid_1d(ceil_div(n, 256))), dim3(256), 0, st, markT,
                        rpos, H, req, hq0, hq1, rhdr, rq0, rne);
     SG_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_runs_total, dim3(1), dim3(1), 0, st, rpos, n, meta);
+    hipLaunchKernelGGL(k_class_bins, dim3(1), dim3(1), 0, st, dpos, H, lbins, rpos, n, bins,
+                       run_meta);
     SG_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_sum_parts, dim3(1), dim3(256), 0, st, part, (int)blocks, 2, meta + 1);
+    hipLaunchKernelGGL(k_sum_parts, dim3(1), dim3(256), 0, st, part, (int)blocks, 2,
+                       run_meta + 1);
     SG_LAUNCH_CHECK();
 }
 
@@ -1047,7 +1075,7 @@ static void launch_direct_rank(const DirectArgs& d, int64_t p0, int64_t n, hipSt
 void direct_accumulate_runs(const DirectArgs& d, int64_t nruns, hipStream_t st) {
     if (nruns <= 0) return;
     const int WR = run_span(d.logW) << d.logW;
-    const size_t lds = (size_t)kRunMax * 8 + (size_t)wave_rank_lds(2, WR);
+    const size_t lds = (size_t)kRunMax * 8 + (size_t)wave_rank_lds(kRunKPT, WR);
     constexpr int IPG = 2;
     auto kern = d.eocc ? k_direct_runs<true, IPG> : k_direct_runs<false, IPG>;
     hipLaunchKernelGGL(kern, dim3(grid_1d(ceil_div(nruns, IPG))), dim3(kWave), lds, st, d, nruns);

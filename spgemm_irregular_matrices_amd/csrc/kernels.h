@@ -288,8 +288,9 @@ struct DirectArgs {
 // within s0 + run_span(logW), and no larger item lies between them; bit t
 // of its mask marks slot s0 + t. Its output is the concatenation of its
 // items' outputs (slots in column order, the empty ones write nothing).
-constexpr int64_t kRunMax = 128;
-static_assert(kRunMax == kRankClassMax[1], "runs take the two smallest rank classes");
+constexpr int kRunClasses = 2;  // the smallest rank classes that runs take
+constexpr int64_t kRunMax = kRankClassMax[kRunClasses - 1];
+constexpr int kRunKPT = (int)(kRunMax / 64);  // products per lane of a run
 __host__ __device__ constexpr int run_span(int logW) {
     return (65536 >> logW) < 8 ? (65536 >> logW) : 8;
 }
@@ -310,15 +311,18 @@ void direct_entry_occ(const int32_t* acol, int64_t annz, int req, const uint32_t
 constexpr int kOccSparse = 4;
 void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int req,
                     const int64_t* dist_fin, int64_t* off, hipStream_t st);
-// Partition of the items x in [0, nitems) by class (DC_* classes, from the
-// exact product count elem_fin[x]; bins has DC_COUNT + 1 starts): the dense
-// class in row order, the bitmap-rank classes in slot order (all rows'
-// items of slot 0 first).
-// Also writes, per position, the item's row's first A entry (iq0) and entry
-// count (ine).
-void direct_classify(const int64_t* elem_fin, int64_t nitems, int req, const int64_t* hq0,
+// The direct path's work lists, from the exact product count of every item
+// (elem_fin, H x req): items[0, ndense) the dense items in row order, then
+// the bitmap-rank classes that the runs do not take, each in slot order
+// (all rows' items of slot 0 first), with per position the item's row's
+// first A entry and entry count (iq0, ine); bins: DC_COUNT + 1 class starts
+// (the run classes and the empty class are empty ranges); the runs
+// (rhdr, rq0, rne; at most H*req) in the order of their first slot; and
+// run_meta = {runs, A entries read, (entry, slot) slice bounds read}.
+void direct_classify(const int64_t* elem_fin, int64_t H, int req, int logW, const int64_t* hq0,
                      const int64_t* hq1, int32_t* items, int64_t* iq0, int32_t* ine,
-                     int64_t* bins, Arena& ar, hipStream_t st);
+                     int64_t* bins, int64_t* rhdr, int64_t* rq0, int32_t* rne, int64_t* run_meta,
+                     Arena& ar, hipStream_t st);
 void direct_gather_values(const int32_t* bperm, const double* bval, int64_t nnz, double* out,
                           hipStream_t st);
 // out8 = {dense items: products, outputs, A entries read; rank items of more
@@ -329,13 +333,6 @@ void direct_totals(const int64_t* hq0, const int64_t* hq1, int64_t H, int req,
                    hipStream_t st);
 size_t direct_window_lds(int64_t W);
 void direct_accumulate(const DirectArgs& d, int cls, int64_t p0, int64_t n, hipStream_t st);
-// Runs of the heavy rows' small items, in the order of their first slot
-// (all rows' runs that start in slot 0 first): rhdr/rq0/rne (at most H*req
-// of them), and meta = {runs, A entries read, (entry, slot) slice bounds
-// read}.
-void direct_runs(const int64_t* elem_fin, int64_t H, int req, int logW, const int64_t* hq0,
-                 const int64_t* hq1, int64_t* rhdr, int64_t* rq0, int32_t* rne, int64_t* meta,
-                 Arena& ar, hipStream_t st);
 void direct_accumulate_runs(const DirectArgs& d, int64_t nruns, hipStream_t st);
 
 }  // namespace sg

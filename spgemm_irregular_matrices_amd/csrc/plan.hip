@@ -810,19 +810,19 @@ int64_t symbolic_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, int64_t* 
             // back with nnz(C)
             int64_t* bins = ar.get<int64_t>("dmeta", kDirMeta);
             entry_len_sq(S, A.nnz, (double*)(bins + kDirLenSq), st);
-            direct_classify(elem_fin, p->H * req, (int)req, ar.get<int64_t>("h_q0", (size_t)p->H),
+            // the work lists: dense items, the rank classes, and the items
+            // of at most kRunMax products merged per row into runs
+            direct_classify(elem_fin, p->H, (int)req, ilog2(wfin_d),
+                            ar.get<int64_t>("h_q0", (size_t)p->H),
                             ar.get<int64_t>("h_q1", (size_t)p->H),
                             ar.get<int32_t>("ditems", (size_t)(p->H * req)),
                             ar.get<int64_t>("diq0", (size_t)(p->H * req)),
-                            ar.get<int32_t>("dine", (size_t)(p->H * req)), bins, ar, st);
+                            ar.get<int32_t>("dine", (size_t)(p->H * req)), bins,
+                            ar.get<int64_t>("rhdr", (size_t)(p->H * req)),
+                            ar.get<int64_t>("rq0", (size_t)(p->H * req)),
+                            ar.get<int32_t>("rne", (size_t)(p->H * req)), bins + kDirRuns, ar, st);
             direct_totals(ar.get<int64_t>("h_q0", (size_t)p->H), ar.get<int64_t>("h_q1", (size_t)p->H),
                           p->H, (int)req, elem_fin, dist_fin, bins + kDirTot, ar, st);
-            // the items of at most kRunMax products, merged per row into runs
-            direct_runs(elem_fin, p->H, (int)req, ilog2(wfin_d),
-                        ar.get<int64_t>("h_q0", (size_t)p->H), ar.get<int64_t>("h_q1", (size_t)p->H),
-                        ar.get<int64_t>("rhdr", (size_t)(p->H * req)),
-                        ar.get<int64_t>("rq0", (size_t)(p->H * req)),
-                        ar.get<int32_t>("rne", (size_t)(p->H * req)), bins + kDirRuns, ar, st);
             add_bytes(p, 0, SPGEMM_PHASE_HISTO, 20.0 * B.nnz + 4.0 * B.n * (req + 1) +
                                                     24.0 * p->H * req);
         }
@@ -1051,9 +1051,9 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
             // numeric calls; the structure may not)
             direct_gather_values(ar.get<int32_t>("bperm", (size_t)B.nnz + 1), B.val, B.nnz, bpval,
                                  st);
-            // the two smallest classes are taken by the runs
+            // the smallest classes are taken by the runs
             direct_accumulate_runs(d, p->dir_runs[0], st);
-            for (int b = DC_RANK0 + 2; b < DC_EMPTY; ++b)
+            for (int b = DC_RANK0 + kRunClasses; b < DC_EMPTY; ++b)
                 direct_accumulate(d, b, p->dir_bins[b], p->dir_bins[b + 1] - p->dir_bins[b], st);
             // runs: each reads its row's entries (12 B) and the slice bounds
             // of every (entry, slot) pair (16 B)

@@ -155,8 +155,10 @@ inline void tile_starts(const int64_t* a, int64_t n, int64_t step, int64_t ntile
 
 // ---------------------------------------------------------------- partition
 // Stable partition of items [0, n) into bins 0..nb-1 (bin order, then item
-// order). perm[pos] = item, pos_of[item] = pos (pos_of may be null),
-// bin_start[0..nb] = first position of each bin (bin_start[nb] = n).
+// order); an item whose bin is -1 is left out. perm[pos] = item,
+// pos_of[item] = pos (pos_of may be null), bin_start[0..nb] = first
+// position of each bin (bin_start[nb] = the items placed, n if none is
+// left out).
 constexpr int kPartNT = 256;
 constexpr int kPartIPT = 8;
 constexpr int kPartTile = kPartNT * kPartIPT;
@@ -171,7 +173,10 @@ __global__ __launch_bounds__(kPartNT) void k_part_count(BinF bf, int64_t n, int 
     int64_t base = (int64_t)blockIdx.x * kPartTile;
     for (int j = 0; j < kPartIPT; ++j) {
         int64_t i = base + (int64_t)j * kPartNT + threadIdx.x;
-        if (i < n) atomicAdd(&h[bf(i)], 1);
+        if (i < n) {
+            const int b = bf(i);  // bin -1: the element is left out
+            if (b >= 0) atomicAdd(&h[b], 1);
+        }
     }
     __syncthreads();
     if (threadIdx.x < nb) counts[(int64_t)threadIdx.x * nblocks + blockIdx.x] = h[threadIdx.x];

@@ -10,7 +10,8 @@ __global__ void k_part_bin_starts(const int64_t* offs, int nb, int64_t nblocks, 
                                   int64_t* bin_start) {
     int b = threadIdx.x;
     if (b < nb) bin_start[b] = offs[(int64_t)b * nblocks];
-    if (b == nb) bin_start[nb] = n;
+    // the elements placed (all n unless a bin function leaves some out)
+    if (b == nb) bin_start[nb] = offs[(int64_t)nb * nblocks];
 }
 
 __global__ void k_tile_starts(const int64_t* a, int64_t n, int64_t step, int64_t ntiles,
