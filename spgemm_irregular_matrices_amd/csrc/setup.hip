@@ -148,8 +148,9 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
                                                        int64_t* stats, int32_t* uhist) {
     __shared__ int64_t sh[8];
     __shared__ double shd[8];
-    __shared__ int hsmall[64];  // the exact buckets u < 64, gathered per block
-    if (threadIdx.x < 64) hsmall[threadIdx.x] = 0;
+    // the block's u histogram, added to the global one once at the end
+    __shared__ int hb[kUHistBuckets];
+    for (int b = threadIdx.x; b < kUHistBuckets; b += blockDim.x) hb[b] = 0;
     __syncthreads();
     int64_t su = 0, heavy = 0, hprod = 0, c512 = 0, c4k = 0, c32k = 0, mu = 0, alight = 0;
     double u2 = 0.0;
@@ -172,11 +173,19 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
                 alight += a1 - a0;
             } else {
                 alight += a1 - a0;
+                // the row's B column range, eight entries' loads in flight
                 int32_t lo = 0x7fffffff, hi = -1;
-                for (int64_t q = a0; q < a1; ++q) {
-                    const int32_t k = acol[q];
-                    lo = min(lo, bmin[k]);
-                    hi = max(hi, bmax[k]);
+                for (int64_t qb = a0; qb < a1; qb += 8) {
+                    int32_t k[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) k[t] = qb + t < a1 ? acol[qb + t] : -1;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        if (k[t] >= 0) {
+                            lo = min(lo, bmin[k[t]]);
+                            hi = max(hi, bmax[k[t]]);
+                        }
+                    }
                 }
                 const int64_t span = (int64_t)hi - lo + 1;
                 rowlo[i] = lo;
@@ -205,18 +214,14 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
             mu = u > mu ? u : mu;
         }
         // the u histogram: the lanes of a wave that share a bucket add once
-        // (a banded matrix puts nearly every row in one bucket); buckets
-        // below 64 gather in LDS first
+        // (a banded matrix puts nearly every row in one bucket)
         const int bk = in ? u_bucket(u) : -1;
         uint64_t act = __ballot(bk >= 0);
         while (act) {
             const int leader = __ffsll((unsigned long long)act) - 1;
             const int lb = __shfl(bk, leader);
             const uint64_t m = __ballot(bk == lb);
-            if (lane_id() == leader) {
-                if (lb < 64) atomicAdd(&hsmall[lb], __popcll(m));
-                else atomicAdd(&uhist[lb], __popcll(m));
-            }
+            if (lane_id() == leader) atomicAdd(&hb[lb], __popcll(m));
             act &= ~m;
         }
     }
@@ -229,7 +234,8 @@ __global__ __launch_bounds__(256) void k_classify_rows(const int64_t* arp, const
     u2 = block_reduce_sum<256>(u2, shd);
     alight = block_reduce_sum<256>(alight, sh);
     // block_reduce_sum ends with a barrier: every wave's LDS histogram adds are in
-    if (threadIdx.x < 64 && hsmall[threadIdx.x]) atomicAdd(&uhist[threadIdx.x], hsmall[threadIdx.x]);
+    for (int b = threadIdx.x; b < kUHistBuckets; b += blockDim.x)
+        if (hb[b]) atomicAdd(&uhist[b], hb[b]);
 #pragma unroll
     for (int d = kWave / 2; d > 0; d >>= 1) {
         const int64_t o = __shfl_xor(mu, d, kWave);
