@@ -1043,8 +1043,9 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         d.rq0 = ar.get<int64_t>("rq0", (size_t)(p->H * req));
         d.rne = ar.get<int32_t>("rne", (size_t)(p->H * req));
         // Bytes per class: every product's B operand (16-bit column and
-        // value, read once), every output entry written once, and each item's
-        // reads of its row's entries (column, B row start, value, slice bounds).
+        // value, read once), every output entry written once (12 B), and
+        // each item's reads of its row's entries (column and value, 12 B)
+        // with their slice bounds (two 32-bit starts, 8 B).
         {
             PhaseScope ps(p, 1, SPGEMM_PHASE_DIRECT_RANK, st);
             // B's values in the split order (values may change between
@@ -1055,19 +1056,21 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
             direct_accumulate_runs(d, p->dir_runs[0], st);
             for (int b = DC_RANK0 + kRunClasses; b < DC_EMPTY; ++b)
                 direct_accumulate(d, b, p->dir_bins[b], p->dir_bins[b + 1] - p->dir_bins[b], st);
-            // runs: each reads its row's entries (12 B) and the slice bounds
-            // of every (entry, slot) pair (16 B)
+            // the gather of B's values: its placement map (4 B), a value read
+            // and written (16 B) per B entry. Runs read their row's entries
+            // (12 B) and an occupancy word per (entry, slot) pair (4 B); the
+            // bounds of the nonempty slices they then read are not counted.
             add_bytes(p, 1, SPGEMM_PHASE_DIRECT_RANK,
-                      24.0 * B.nnz + 10.0 * (p->dir_tot[3] + p->dir_tot[6]) +
-                          12.0 * (p->dir_tot[4] + p->dir_tot[7]) + 28.0 * p->dir_tot[5] +
-                          12.0 * p->dir_runs[1] + 16.0 * p->dir_runs[2]);
+                      20.0 * B.nnz + 10.0 * (p->dir_tot[3] + p->dir_tot[6]) +
+                          12.0 * (p->dir_tot[4] + p->dir_tot[7]) + 20.0 * p->dir_tot[5] +
+                          12.0 * p->dir_runs[1] + 4.0 * p->dir_runs[2]);
         }
         {
             PhaseScope ps(p, 1, SPGEMM_PHASE_DIRECT_DENSE, st);
             direct_accumulate(d, DC_DENSE, p->dir_bins[DC_DENSE],
                               p->dir_bins[DC_DENSE + 1] - p->dir_bins[DC_DENSE], st);
             add_bytes(p, 1, SPGEMM_PHASE_DIRECT_DENSE,
-                      10.0 * p->dir_tot[0] + 12.0 * p->dir_tot[1] + 28.0 * p->dir_tot[2]);
+                      10.0 * p->dir_tot[0] + 12.0 * p->dir_tot[1] + 20.0 * p->dir_tot[2]);
         }
         return;
     }
