@@ -194,30 +194,35 @@ void direct_gather_values(const int32_t* bperm, const double* bval, int64_t nnz,
 }
 
 // Staging of one round of an item's A entries (at most NE of them, taken by
-// threads tt < NE): each entry's slice of the item's chunk (its start in the
-// partitioned B and its a value) and the exclusive prefix of slice lengths.
-// Returns the products of the round. Threads past the item's entries add 0.
+// threads tt < NE): each entry's a value, the exclusive prefix of slice
+// lengths (s_pre) and its slice's start in the partitioned B less that
+// prefix (s_bo), so that the round's product p of entry e is B entry
+// s_bo[e] + p. Returns the products of the round. Threads past the item's
+// entries add 0.
 template <int TW, int NE, bool OCC>
 __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int64_t q1, int s,
                                             int* s_pre, int64_t* s_bo, double* s_a, int* red_sh) {
     const int tt = threadIdx.x;
     int len = 0;
+    int64_t lo = 0;
+    double a = 0.0;
     if (tt < NE && q < q1) {
         const int32_t k = d.Acol[q];
-        const double a = d.Aval[q];
+        a = d.Aval[q];
         // with the occupancy bits, an empty (B row, slot) slice reads no bounds
-        int64_t lo = 0;
         if (!OCC || (d.eocc[(int64_t)(s >> 5) * d.annz + q] >> (s & 31)) & 1u) {
             const int32_t* sp = d.spos + (int64_t)s * d.nb + k;
             lo = sp[0];
             len = (int)(sp[1] - lo);
         }
-        s_bo[tt] = lo;
-        s_a[tt] = a;
     }
     int tot;
     const int pre = team_exclusive_scan<TW>(len, red_sh, &tot);
-    if (tt < NE) s_pre[tt] = pre;
+    if (tt < NE) {
+        s_pre[tt] = pre;
+        s_bo[tt] = lo - pre;
+        s_a[tt] = a;
+    }
     __syncthreads();
     return tot;
 }
@@ -247,11 +252,11 @@ template <int TW>
 __device__ __forceinline__ int stage_commit(double a, int64_t lo, int len, int* s_pre,
                                             int64_t* s_bo, double* s_a, int* red_sh) {
     const int tt = threadIdx.x;
-    s_bo[tt] = lo;
-    s_a[tt] = a;
     int tot;
     const int pre = team_exclusive_scan<TW>(len, red_sh, &tot);
     s_pre[tt] = pre;
+    s_bo[tt] = lo - pre;
+    s_a[tt] = a;
     __syncthreads();
     return tot;
 }
@@ -341,7 +346,7 @@ __device__ __forceinline__ void rank_item(const DirectArgs& d, int32_t x, int64_
             bi[k] = -1;
             if (p >= 0 && p < tot) {
                 j = direct_find(s_pre, ne, p, j);
-                bi[k] = s_bo[j] + (p - s_pre[j]);
+                bi[k] = s_bo[j] + p;
                 av[k] = s_a[j];
             }
         }
@@ -526,11 +531,11 @@ __device__ __forceinline__ void run_item(const DirectArgs& d, int64_t hdr, int64
                 len = (jl < epr && j < ne) ? (int)(sp[1] - lo) : 0;
             }
         }
-        s_bo[lane] = lo;
-        s_a[lane] = a;
         const int inc = wave_inclusive_scan(len);
         const int tot = __shfl(inc, kWave - 1, kWave);
         s_pre[lane] = inc - len;
+        s_bo[lane] = lo - (inc - len);
+        s_a[lane] = a;
         wave_lds_sync();
         int64_t bi[KPT];
         double av[KPT];
@@ -542,7 +547,7 @@ __device__ __forceinline__ void run_item(const DirectArgs& d, int64_t hdr, int64
             bi[k] = -1;
             if (p >= 0 && p < tot) {
                 j = direct_find(s_pre, kWave, p, j);
-                bi[k] = s_bo[j] + (p - s_pre[j]);
+                bi[k] = s_bo[j] + p;
                 av[k] = s_a[j];
                 cb[k] = s_cb[j];
             }
@@ -713,7 +718,7 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
                     jc = __builtin_amdgcn_readlane(e, kWave - 1);
                     const int p = base + lane;
                     if (p < tot) {
-                        bi[u] = s_bo[e] + (p - s_pre[e]);
+                        bi[u] = s_bo[e] + p;
                         av[u] = s_a[e];
                     }
                 }
