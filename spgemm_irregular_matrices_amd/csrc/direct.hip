@@ -193,15 +193,21 @@ void direct_gather_values(const int32_t* bperm, const double* bval, int64_t nnz,
     SG_LAUNCH_CHECK();
 }
 
+// One staged entry of a round: its slice's start in the partitioned B less
+// the round's product prefix at the entry, so that the round's product p of
+// the entry is B entry base + p, and its a value; 16 bytes, one LDS access.
+struct alignas(16) StagedEntry {
+    int64_t base;
+    double a;
+};
+
 // Staging of one round of an item's A entries (at most NE of them, taken by
-// threads tt < NE): each entry's a value, the exclusive prefix of slice
-// lengths (s_pre) and its slice's start in the partitioned B less that
-// prefix (s_bo), so that the round's product p of entry e is B entry
-// s_bo[e] + p. Returns the products of the round. Threads past the item's
-// entries add 0.
+// threads tt < NE): each entry's StagedEntry and the exclusive prefix of
+// slice lengths (s_pre). Returns the products of the round. Threads past
+// the item's entries add 0.
 template <int TW, int NE, bool OCC>
 __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int64_t q1, int s,
-                                            int* s_pre, int64_t* s_bo, double* s_a, int* red_sh) {
+                                            int* s_pre, StagedEntry* s_e, int* red_sh) {
     const int tt = threadIdx.x;
     int len = 0;
     int64_t lo = 0;
@@ -220,8 +226,7 @@ __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int6
     const int pre = team_exclusive_scan<TW>(len, red_sh, &tot);
     if (tt < NE) {
         s_pre[tt] = pre;
-        s_bo[tt] = lo - pre;
-        s_a[tt] = a;
+        s_e[tt] = StagedEntry{lo - pre, a};
     }
     __syncthreads();
     return tot;
@@ -250,13 +255,12 @@ __device__ __forceinline__ void stage_load(const DirectArgs& d, int64_t q, bool 
 // per thread of the team); returns the round's products.
 template <int TW>
 __device__ __forceinline__ int stage_commit(double a, int64_t lo, int len, int* s_pre,
-                                            int64_t* s_bo, double* s_a, int* red_sh) {
+                                            StagedEntry* s_e, int* red_sh) {
     const int tt = threadIdx.x;
     int tot;
     const int pre = team_exclusive_scan<TW>(len, red_sh, &tot);
     s_pre[tt] = pre;
-    s_bo[tt] = lo - pre;
-    s_a[tt] = a;
+    s_e[tt] = StagedEntry{lo - pre, a};
     __syncthreads();
     return tot;
 }
@@ -315,7 +319,7 @@ template <int TW, int KPT, bool OCC>
 __device__ __forceinline__ void rank_item(const DirectArgs& d, int32_t x, int64_t q0, int64_t q1,
                                           int64_t off, double a0, int64_t lo0, int len0,
                                           double* vals, uint32_t* bits, int* wpre, int* s_pre,
-                                          int64_t* s_bo, double* s_a, int* red_sh) {
+                                          StagedEntry* s_e, int* red_sh) {
     const int W = 1 << d.logW;
     const int NWD = W >> 5;
     const int tt = threadIdx.x;
@@ -334,8 +338,8 @@ __device__ __forceinline__ void rank_item(const DirectArgs& d, int32_t x, int64_
     int done = 0;
     for (int64_t qb = q0; qb < q1; qb += TW) {
         const int tot = qb == q0
-                            ? stage_commit<TW>(a0, lo0, len0, s_pre, s_bo, s_a, red_sh)
-                            : direct_stage<TW, TW, OCC>(d, qb + tt, q1, s, s_pre, s_bo, s_a, red_sh);
+                            ? stage_commit<TW>(a0, lo0, len0, s_pre, s_e, red_sh)
+                            : direct_stage<TW, TW, OCC>(d, qb + tt, q1, s, s_pre, s_e, red_sh);
         const int ne = (int)min((int64_t)TW, q1 - qb);
         int64_t bi[KPT];
         double av[KPT];
@@ -346,8 +350,9 @@ __device__ __forceinline__ void rank_item(const DirectArgs& d, int32_t x, int64_
             bi[k] = -1;
             if (p >= 0 && p < tot) {
                 j = direct_find(s_pre, ne, p, j);
-                bi[k] = s_bo[j] + p;
-                av[k] = s_a[j];
+                const StagedEntry se = s_e[j];
+                bi[k] = se.base + p;
+                av[k] = se.a;
             }
         }
 #pragma unroll
@@ -361,8 +366,8 @@ __device__ __forceinline__ void rank_item(const DirectArgs& d, int32_t x, int64_
         __syncthreads();  // the next round restages
     }
     if constexpr (kTwoLevel) {
-        // the staged B starts are free once the products are formed
-        wave_rank_emit<KPT>(idx, v, W, bits, vals, (uint16_t*)s_bo, s << d.logW, d.Ccol + off,
+        // the staged entries are free once the products are formed
+        wave_rank_emit<KPT>(idx, v, W, bits, vals, (uint16_t*)s_e, s << d.logW, d.Ccol + off,
                             d.Cval + off, true);
         return;
     }
@@ -392,8 +397,8 @@ __device__ __forceinline__ void rank_item(const DirectArgs& d, int32_t x, int64_
     }
     // each column at its rank, in the staging area (free once the products
     // are formed), so that columns and values are written out coalesced
-    static_assert(KPT * 2 <= 8, "the ranked columns fit the staged B starts");
-    uint16_t* scol = (uint16_t*)s_bo;
+    static_assert(KPT * 2 <= (int)sizeof(StagedEntry), "the ranked columns fit the staging area");
+    uint16_t* scol = (uint16_t*)s_e;
     for (int wd = w0; wd < w1; ++wd) {
         uint32_t bw = bits[wd];
         int r = wpre[wd];
@@ -423,8 +428,7 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
     uint32_t* bits = (uint32_t*)(vals + TW * KPT);  // W/32
     int* wpre = (int*)(bits + (W >> 5));            // W/32
     __shared__ int s_pre[TW];
-    __shared__ int64_t s_bo[TW];
-    __shared__ double s_a[TW];
+    __shared__ StagedEntry s_e[TW];
     __shared__ int red_sh[TW / kWave + 1];
     const int tt = threadIdx.x;
     const int64_t i0 = (int64_t)blockIdx.x * IPG;
@@ -481,7 +485,7 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
             // the previous item's output has read the staging area and bitmap
             if (u > 0) __syncthreads();
             rank_item<TW, KPT, OCC>(d, x[u], q0[u], q0[u] + ne[u], off[u], a[u], lo[u], len[u],
-                                    vals, bits, wpre, s_pre, s_bo, s_a, red_sh);
+                                    vals, bits, wpre, s_pre, s_e, red_sh);
         }
     }
 }
@@ -497,7 +501,7 @@ template <bool OCC>
 __device__ __forceinline__ void run_item(const DirectArgs& d, int64_t hdr, int64_t q0, int ne,
                                          int64_t off, int jl, int ds, int epr, double a0,
                                          int64_t lo0, int len0, int WR, double* vals, void* rk,
-                                         int* s_pre, int64_t* s_bo, double* s_a, int* s_cb) {
+                                         int* s_pre, StagedEntry* s_e, int* s_cb) {
     constexpr int KPT = kRunKPT;
     static_assert(kWave * KPT == kRunMax, "one wavefront holds a run's products");
     const int lane = lane_id();
@@ -534,8 +538,7 @@ __device__ __forceinline__ void run_item(const DirectArgs& d, int64_t hdr, int64
         const int inc = wave_inclusive_scan(len);
         const int tot = __shfl(inc, kWave - 1, kWave);
         s_pre[lane] = inc - len;
-        s_bo[lane] = lo - (inc - len);
-        s_a[lane] = a;
+        s_e[lane] = StagedEntry{lo - (inc - len), a};
         wave_lds_sync();
         int64_t bi[KPT];
         double av[KPT];
@@ -547,8 +550,9 @@ __device__ __forceinline__ void run_item(const DirectArgs& d, int64_t hdr, int64
             bi[k] = -1;
             if (p >= 0 && p < tot) {
                 j = direct_find(s_pre, kWave, p, j);
-                bi[k] = s_bo[j] + p;
-                av[k] = s_a[j];
+                const StagedEntry se = s_e[j];
+                bi[k] = se.base + p;
+                av[k] = se.a;
                 cb[k] = s_cb[j];
             }
         }
@@ -562,8 +566,8 @@ __device__ __forceinline__ void run_item(const DirectArgs& d, int64_t hdr, int64
         done += tot;
         wave_lds_sync();  // the next round restages
     }
-    // the staged B starts are free once the products are formed
-    wave_rank_emit<KPT>(idx, v, WR, rk, vals, (uint16_t*)s_bo, s0 << d.logW, d.Ccol + off,
+    // the staged entries are free once the products are formed
+    wave_rank_emit<KPT>(idx, v, WR, rk, vals, (uint16_t*)s_e, s0 << d.logW, d.Ccol + off,
                         d.Cval + off, true);
 }
 
@@ -575,8 +579,7 @@ __global__ __launch_bounds__(kWave) void k_direct_runs(DirectArgs d, int64_t nru
     double* vals = (double*)lds_u;     // kRunMax
     void* rk = vals + kRunMax;         // wave_rank_lds(kRunKPT, run width)
     __shared__ int s_pre[kWave];
-    __shared__ int64_t s_bo[kWave];
-    __shared__ double s_a[kWave];
+    __shared__ StagedEntry s_e[kWave];
     __shared__ int s_cb[kWave];
     const int lane = lane_id();
     const int64_t i0 = (int64_t)blockIdx.x * IPG;
@@ -640,7 +643,7 @@ __global__ __launch_bounds__(kWave) void k_direct_runs(DirectArgs d, int64_t nru
             // the previous run's output has read the staging area
             if (u > 0) wave_lds_sync();
             run_item<OCC>(d, hdr[u], q0[u], ne[u], off[u], jl[u], ds[u], epr[u], a[u], lo[u],
-                          len[u], WR, vals, rk, s_pre, s_bo, s_a, s_cb);
+                          len[u], WR, vals, rk, s_pre, s_e, s_cb);
         }
     }
 }
@@ -673,8 +676,7 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     // counts (kWinHistWords words from bits on; the launch sizes them)
     uint32_t* hw_all = bits;
     __shared__ int s_pre[kDirectNE];
-    __shared__ int64_t s_bo[kDirectNE];
-    __shared__ double s_a[kDirectNE];
+    __shared__ StagedEntry s_e[kDirectNE];
     __shared__ int red_sh[TW / kWave + 1];
     const int tt = threadIdx.x;
     const int64_t item = blockIdx.x;
@@ -697,7 +699,7 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     for (int64_t qb = q0; qb < q1; qb += kDirectNE) {
         __syncthreads();  // zeroing done / previous round's staging consumed
         const int tot = __builtin_amdgcn_readfirstlane(
-            direct_stage<TW, kDirectNE, OCC>(d, qb + tt, q1, s, s_pre, s_bo, s_a, red_sh));
+            direct_stage<TW, kDirectNE, OCC>(d, qb + tt, q1, s, s_pre, s_e, red_sh));
         const int ne = (int)min((int64_t)kDirectNE, q1 - qb);
         // each wave takes a contiguous run of 64-product chunks; lane l of a
         // chunk takes product base + l
@@ -718,8 +720,9 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
                     jc = __builtin_amdgcn_readlane(e, kWave - 1);
                     const int p = base + lane;
                     if (p < tot) {
-                        bi[u] = s_bo[e] + p;
-                        av[u] = s_a[e];
+                        const StagedEntry se = s_e[e];
+                        bi[u] = se.base + p;
+                        av[u] = se.a;
                     }
                 }
             }
