@@ -686,6 +686,14 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     const int64_t q1 = q0 + d.ine[p0 + item];
     const int64_t off = d.off[x];
     const int s = (int)((uint32_t)x & (uint32_t)(d.req - 1));  // req is a power of two
+    // the first round's entries and slice bounds are loaded before the
+    // window is cleared, so that the clearing runs while they arrive (a
+    // dense item has entries: the index is clamped into its row)
+    double a0 = 0.0;
+    int64_t lo0 = 0;
+    int len0 = 0;
+    if (tt < kDirectNE)
+        stage_load<OCC>(d, q0 + min((int64_t)tt, q1 - q0 - 1), q0 + tt < q1, s, a0, lo0, len0);
     // 16 bytes a store: W is a power of two of at least 32
     const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
     for (int i = tt; i < NWD * 2; i += TW) ((uint4*)flags)[i] = z4;
@@ -698,8 +706,18 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     constexpr int NWV = TW / kWave;
     for (int64_t qb = q0; qb < q1; qb += kDirectNE) {
         __syncthreads();  // zeroing done / previous round's staging consumed
-        const int tot = __builtin_amdgcn_readfirstlane(
-            direct_stage<TW, kDirectNE, OCC>(d, qb + tt, q1, s, s_pre, s_e, red_sh));
+        int tot;
+        if (qb == q0) {
+            const int pre = team_exclusive_scan<TW>(len0, red_sh, &tot);
+            if (tt < kDirectNE) {
+                s_pre[tt] = pre;
+                s_e[tt] = StagedEntry{lo0 - pre, a0};
+            }
+            __syncthreads();
+        } else {
+            tot = direct_stage<TW, kDirectNE, OCC>(d, qb + tt, q1, s, s_pre, s_e, red_sh);
+        }
+        tot = __builtin_amdgcn_readfirstlane(tot);
         const int ne = (int)min((int64_t)kDirectNE, q1 - qb);
         // each wave takes a contiguous run of 64-product chunks; lane l of a
         // chunk takes product base + l
