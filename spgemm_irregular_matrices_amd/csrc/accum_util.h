@@ -18,6 +18,33 @@ __device__ __forceinline__ int team_exclusive_scan(int v, int* sh, int* total) {
     }
 }
 
+// Exclusive scan of a block whose values sit in its first NA threads (NA a
+// multiple of 64; the other threads hold 0) with one barrier: wave scans,
+// each wave's total in sh[w], then every thread adds the totals of the
+// waves before its own. *total receives the sum. sh holds NA/64 values and
+// must not be rewritten before every thread has returned (the next barrier).
+template <int NA>
+__device__ __forceinline__ int block_scan_first(int v, int* sh, int* total) {
+    constexpr int NW = NA / kWave;
+    static_assert(NA % kWave == 0, "whole waves");
+    const int w = threadIdx.x / kWave;
+    int inc = 0;
+    if (w < NW) {
+        inc = wave_inclusive_scan_i32(v);
+        if (lane_id() == kWave - 1) sh[w] = inc;
+    }
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int t = sh[i];
+        before += i < w ? t : 0;
+        tot += t;
+    }
+    *total = tot;
+    return w < NW ? before + inc - v : tot;
+}
+
 template <int TW>
 __device__ __forceinline__ int team_sum(int v, int* sh) {
     if constexpr (TW == kWave) return wave_reduce_sum(v);

@@ -223,7 +223,11 @@ __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int6
         }
     }
     int tot;
-    const int pre = team_exclusive_scan<TW>(len, red_sh, &tot);
+    int pre;
+    if constexpr (NE < TW)
+        pre = block_scan_first<NE>(len, red_sh, &tot);  // one barrier
+    else
+        pre = team_exclusive_scan<TW>(len, red_sh, &tot);
     if (tt < NE) {
         s_pre[tt] = pre;
         s_e[tt] = StagedEntry{lo - pre, a};
@@ -708,7 +712,7 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
         __syncthreads();  // zeroing done / previous round's staging consumed
         int tot;
         if (qb == q0) {
-            const int pre = team_exclusive_scan<TW>(len0, red_sh, &tot);
+            const int pre = block_scan_first<kDirectNE>(len0, red_sh, &tot);
             if (tt < kDirectNE) {
                 s_pre[tt] = pre;
                 s_e[tt] = StagedEntry{lo0 - pre, a0};
@@ -772,7 +776,7 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
         pc += __popc(m);
     }
     int tot;
-    int pre = team_exclusive_scan<TW>(pc, red_sh, &tot);
+    int pre = block_scan_first<TW>(pc, red_sh, &tot);
     for (int wd = w0; wd < w1; ++wd) {
         wpre[wd] = pre;
         pre += __popc(bits[wd]);
