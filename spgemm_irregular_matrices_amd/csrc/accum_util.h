@@ -45,6 +45,14 @@ __device__ __forceinline__ int block_scan_first(int v, int* sh, int* total) {
     return w < NW ? before + inc - v : tot;
 }
 
+// Exclusive scan over a team of TW threads: a wave scan for one wavefront,
+// else block_scan_first (one barrier).
+template <int TW>
+__device__ __forceinline__ int team_scan_fast(int v, int* sh, int* total) {
+    if constexpr (TW == kWave) return team_exclusive_scan<TW>(v, sh, total);
+    else return block_scan_first<TW>(v, sh, total);
+}
+
 template <int TW>
 __device__ __forceinline__ int team_sum(int v, int* sh) {
     if constexpr (TW == kWave) return wave_reduce_sum(v);

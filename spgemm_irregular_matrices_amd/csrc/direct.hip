@@ -227,7 +227,7 @@ __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int6
     if constexpr (NE < TW)
         pre = block_scan_first<NE>(len, red_sh, &tot);  // one barrier
     else
-        pre = team_exclusive_scan<TW>(len, red_sh, &tot);
+        pre = team_scan_fast<TW>(len, red_sh, &tot);
     if (tt < NE) {
         s_pre[tt] = pre;
         s_e[tt] = StagedEntry{lo - pre, a};
@@ -262,7 +262,7 @@ __device__ __forceinline__ int stage_commit(double a, int64_t lo, int len, int* 
                                             StagedEntry* s_e, int* red_sh) {
     const int tt = threadIdx.x;
     int tot;
-    const int pre = team_exclusive_scan<TW>(len, red_sh, &tot);
+    const int pre = team_scan_fast<TW>(len, red_sh, &tot);
     s_pre[tt] = pre;
     s_e[tt] = StagedEntry{lo - pre, a};
     __syncthreads();
@@ -384,7 +384,7 @@ __device__ __forceinline__ void rank_item(const DirectArgs& d, int32_t x, int64_
     int pc = 0;
     for (int wd = w0; wd < w1; ++wd) pc += __popc(bits[wd]);
     int tot;
-    int pre = team_exclusive_scan<TW>(pc, red_sh, &tot);
+    int pre = team_scan_fast<TW>(pc, red_sh, &tot);
     for (int wd = w0; wd < w1; ++wd) {
         wpre[wd] = pre;
         pre += __popc(bits[wd]);
