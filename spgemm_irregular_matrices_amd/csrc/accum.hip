@@ -521,7 +521,6 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
     int* wpre = (int*)(bits + NWD);                               // NWD (NUM)
     int32_t* scol = (int32_t*)(wpre + NWD);                       // TW*KPT (NUM)
     __shared__ int red_sh[TW / kWave + 1];
-    __shared__ int32_t lo_sh;
     const int tt = threadIdx.x;
     const int64_t item = blockIdx.x;
     if (item >= nitems) return;
@@ -531,11 +530,10 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
     // one-wave chunks are ranked through the two-level bitmap (work by
     // element); the larger ones through the chunk's full bitmap
     constexpr bool kTwoLevel = TW == kWave;
-    if constexpr (!kTwoLevel)
-        for (int w = tt; w < NWD; w += TW) bits[w] = 0u;
-    if (tt == 0) lo_sh = chunk_lo(ci, start, out, W);
-    __syncthreads();
-    const int32_t lo = lo_sh;
+    // Every thread reads the chunk's first column itself (one address for
+    // the group), and the elements are loaded before the bitmap is cleared,
+    // so that no barrier stands between the chunk's header and its loads.
+    const int32_t lo = chunk_lo(ci, start, out, W);
     uint32_t idx[KPT];
     double v[KPT];
 #pragma unroll
@@ -547,6 +545,10 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
                                : (uint32_t)(ci.bcol[start + t] - lo);
             if constexpr (NUM) v[k] = ci.bval[start + t];
         }
+    }
+    if constexpr (!kTwoLevel) {
+        for (int w = tt; w < NWD; w += TW) bits[w] = 0u;
+        __syncthreads();
     }
     if constexpr (kTwoLevel) {
         if constexpr (!NUM) {
@@ -611,9 +613,11 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
 }
 
 // ---------------------------------------------------------------- dense window
-template <int MODE, bool NUM, int TW, int NI>
-__global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, ChunkItems ci, int64_t p0,
-                                                       int64_t nitems, int logW) {
+// Light rows whose columns fall in a short window (rows of banded matrices):
+// NI teams of TW threads per work group, one row each.
+template <bool NUM, int TW, int NI>
+__global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, int64_t p0, int64_t nitems,
+                                                       int logW) {
     static_assert(TW == kWave || NI == 1, "block-wide teams hold one item");
     extern __shared__ int64_t lds_w[];
     const int W = 1 << logW;
@@ -630,53 +634,23 @@ __global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, ChunkItems c
     const int64_t item = (int64_t)blockIdx.x * NI + team;
     const bool active = item < nitems;
     ItemHdr h;
-    if (active) h = load_item<MODE>(ri, ci, p0 + item);
+    if (active) h = load_item<MODE_ROW>(ri, ChunkItems{}, p0 + item);
     for (int w = tt; w < NWD * 8; w += TW) flags[w] = 0u;
     if constexpr (NUM)
         for (int s = tt; s < W; s += TW) acc[s] = 0.0;
-    if (tt == 0 && active) {
-        if constexpr (MODE == MODE_ROW) {
-            lo_sh[team] = ri.rowlo[h.out];
-        } else {
-            lo_sh[team] = chunk_lo(ci, h.start, h.out, ci.width);
-        }
-    }
+    if (tt == 0 && active) lo_sh[team] = ri.rowlo[h.out];
     __syncthreads();
     const int32_t lo = active ? lo_sh[team] : 0;
     uint8_t* fb = (uint8_t*)flags;
-    if constexpr (MODE == MODE_ROW) {
-        __shared__ RowStage<TW> stages[NI];
-        if (active) {
-            row_products<TW, 4, NUM>(ri, h, stages[team], red_sh, tt, [&](int32_t c, double v) {
-                const uint32_t idx = (uint32_t)(c - lo);
-                if (idx < (uint32_t)W) {
-                    fb[idx] = 1;
-                    if constexpr (NUM) atomicAdd(&acc[idx], v);
-                }
-            });
-        }
-    } else if (active) {
-        int64_t cur = h.a0;
-        constexpr int U = 4;  // loads in flight per thread
-        for (int64_t t0 = tt; t0 < h.count; t0 += (int64_t)TW * U) {
-            int32_t c[U];
-            double v[U];
-#pragma unroll
-            for (int uu = 0; uu < U; ++uu) {
-                const int64_t t = t0 + (int64_t)uu * TW;
-                c[uu] = lo - 1;  // out of the window: skipped below
-                v[uu] = 0.0;
-                if (t < h.count) load_elem<MODE, NUM>(ri, ci, h, t, cur, lo, c[uu], v[uu]);
+    __shared__ RowStage<TW> stages[NI];
+    if (active) {
+        row_products<TW, 4, NUM>(ri, h, stages[team], red_sh, tt, [&](int32_t c, double v) {
+            const uint32_t idx = (uint32_t)(c - lo);
+            if (idx < (uint32_t)W) {
+                fb[idx] = 1;
+                if constexpr (NUM) atomicAdd(&acc[idx], v);
             }
-#pragma unroll
-            for (int uu = 0; uu < U; ++uu) {
-                uint32_t idx = (uint32_t)(c[uu] - lo);
-                if (idx < (uint32_t)W) {
-                    fb[idx] = 1;
-                    if constexpr (NUM) atomicAdd(&acc[idx], v[uu]);
-                }
-            }
-        }
+        });
     }
     __syncthreads();
     // each thread owns a contiguous run of bitmap words
@@ -690,7 +664,7 @@ __global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, ChunkItems c
     }
     if constexpr (!NUM) {
         int tot = team_sum<TW>(pc, red_sh);
-        if (active && tt == 0) write_count<MODE>(ri, ci, h, tot);
+        if (active && tt == 0) ri.cnt[h.out] = tot;
     } else {
         int tot;
         int pre = team_exclusive_scan<TW>(pc, red_sh, &tot);
@@ -700,17 +674,110 @@ __global__ __launch_bounds__(TW* NI) void k_acc_window(RowItems ri, ChunkItems c
         }
         __syncthreads();
         if (active) {
-            int64_t off = out_offset<MODE>(ri, ci, h);
-            int32_t* oc = out_cols<MODE>(ri, ci);
-            double* ov = out_vals<MODE>(ri, ci);
+            const int64_t off = ri.Crp[h.out];
             for (int idx = tt; idx < W; idx += TW) {
                 uint32_t word = bits[idx >> 5];
                 uint32_t bit = 1u << (idx & 31);
                 if (word & bit) {
                     int rank = wpre[idx >> 5] + __popc(word & (bit - 1));
-                    oc[off + rank] = lo + idx;
-                    ov[off + rank] = acc[idx];
+                    ri.Ccol[off + rank] = lo + idx;
+                    ri.Cval[off + rank] = acc[idx];
                 }
+            }
+        }
+    }
+}
+
+// Dense window of one heavy chunk: the chunk mode of the window
+// accumulator in a kernel of its own. The first batch of elements is loaded
+// before the window is cleared (16 bytes a store), so that the clearing
+// runs while they arrive, and every thread reads the chunk's first column
+// itself instead of waiting on a barrier for it.
+constexpr int kChunkWinNT = 1024;
+
+template <bool NUM>
+__global__ __launch_bounds__(kChunkWinNT) void k_chunk_window(ChunkItems ci, int64_t p0,
+                                                             int64_t nitems, int logW) {
+    constexpr int TW = kChunkWinNT;
+    constexpr int U = 4;  // loads in flight per thread
+    extern __shared__ __align__(16) int64_t lds_c[];
+    const int W = 1 << logW;
+    const int NWD = W >> 5;  // bitmap words
+    double* acc = (double*)lds_c;                        // W (numeric)
+    uint32_t* flags = (uint32_t*)(acc + (NUM ? W : 0));  // W bytes
+    uint32_t* bits = flags + NWD * 8;                    // NWD
+    int* wpre = (int*)(bits + NWD);                      // NWD
+    __shared__ int red_sh[TW / kWave + 1];
+    const int tt = threadIdx.x;
+    const int64_t item = blockIdx.x;
+    if (item >= nitems) return;
+    const int64_t start = ci.rp[p0 + item];
+    const int64_t count = ci.rp[p0 + item + 1] - start;
+    const int64_t out = ci.map[p0 + item];
+    const int32_t lo = chunk_lo(ci, start, out, W);
+    uint32_t c[U];
+    double v[U];
+    auto load = [&](int64_t t0) {
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+            const int64_t t = t0 + (int64_t)uu * TW;
+            c[uu] = 0xffffffffu;  // past the window: skipped
+            v[uu] = 0.0;
+            if (t < count) {
+                c[uu] = ci.bcol16 ? (uint32_t)ci.bcol16[start + t]
+                                  : (uint32_t)(ci.bcol[start + t] - lo);
+                if constexpr (NUM) v[uu] = ci.bval[start + t];
+            }
+        }
+    };
+    load(tt);
+    // W is a power of two of at least 32: W bytes of flags are NWD * 2
+    // 16-byte stores, W doubles W / 2 of them
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tt; i < NWD * 2; i += TW) ((uint4*)flags)[i] = z4;
+    if constexpr (NUM)
+        for (int i = tt; i < W / 2; i += TW) ((uint4*)acc)[i] = z4;
+    __syncthreads();
+    uint8_t* fb = (uint8_t*)flags;
+    for (int64_t t0 = tt; t0 < count; t0 += (int64_t)TW * U) {
+        if (t0 != tt) load(t0);
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+            if (c[uu] < (uint32_t)W) {
+                fb[c[uu]] = 1;
+                if constexpr (NUM) atomicAdd(&acc[c[uu]], v[uu]);
+            }
+        }
+    }
+    __syncthreads();
+    // each thread packs a contiguous run of bitmap words
+    const int per = (NWD + TW - 1) / TW;
+    const int w0 = min(NWD, tt * per), w1 = min(NWD, w0 + per);
+    int pc = 0;
+    for (int w = w0; w < w1; ++w) {
+        const uint32_t m = pack_flags32(flags + w * 8);
+        bits[w] = m;
+        pc += __popc(m);
+    }
+    if constexpr (!NUM) {
+        const int tot = team_sum<TW>(pc, red_sh);
+        if (tt == 0) ci.cnt[out] = tot;
+    } else {
+        int tot;
+        int pre = block_scan_first<TW>(pc, red_sh, &tot);
+        for (int w = w0; w < w1; ++w) {
+            wpre[w] = pre;
+            pre += __popc(bits[w]);
+        }
+        __syncthreads();
+        const int64_t off = ci.off[out];
+        for (int i = tt; i < W; i += TW) {
+            const uint32_t word = bits[i >> 5];
+            const uint32_t bit = 1u << (i & 31);
+            if (word & bit) {
+                const int rank = wpre[i >> 5] + __popc(word & (bit - 1));
+                ci.Ccol[off + rank] = lo + i;
+                ci.Cval[off + rank] = acc[i];
             }
         }
     }
@@ -742,17 +809,16 @@ static void launch_rank(const ChunkItems& ci, int64_t p0, int64_t n, hipStream_t
     SG_LAUNCH_CHECK();
 }
 
-template <int MODE, bool NUM, int TW, int NI>
-static void launch_window(const RowItems& ri, const ChunkItems& ci, int64_t p0, int64_t n,
-                          int64_t W, hipStream_t st) {
+template <bool NUM, int TW, int NI>
+static void launch_window(const RowItems& ri, int64_t p0, int64_t n, int64_t W, hipStream_t st) {
     if (W < 32 || (W & (W - 1))) throw std::logic_error("window width must be a power of two >= 32");
     size_t lds = (size_t)NI * ((NUM ? W * 8 : 0) + W + (W / 32) * 4 * 2);
     if (lds > 160 * 1024) throw OverflowError("dense window exceeds LDS");
-    auto kern = k_acc_window<MODE, NUM, TW, NI>;
+    auto kern = k_acc_window<NUM, TW, NI>;
     SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds));
-    hipLaunchKernelGGL(kern, dim3(grid_1d(ceil_div(n, NI))), dim3(TW * NI), lds, st, ri, ci, p0,
-                       n, ilog2(W));
+    hipLaunchKernelGGL(kern, dim3(grid_1d(ceil_div(n, NI))), dim3(TW * NI), lds, st, ri, p0, n,
+                       ilog2(W));
     SG_LAUNCH_CHECK();
 }
 
@@ -791,9 +857,9 @@ static void rows_impl(const RowItems& it, int bin, int64_t p0, int64_t n, hipStr
         case RB_T8: launch_thread<NUM, 8>(it, p0, n, st); break;
         case RB_T16: launch_thread<NUM, 16>(it, p0, n, st); break;
         case RB_T32: launch_thread<NUM, 32>(it, p0, n, st); break;
-        case RB_WIN64: launch_window<MODE_ROW, NUM, 64, 4>(it, none, p0, n, kWinSmall, st); break;
+        case RB_WIN64: launch_window<NUM, 64, 4>(it, p0, n, kWinSmall, st); break;
         case RB_WIN1024:
-            launch_window<MODE_ROW, NUM, 256, 1>(it, none, p0, n, kWinLarge, st);
+            launch_window<NUM, 256, 1>(it, p0, n, kWinLarge, st);
             break;
         case RB_H128: launch_hash_bin<MODE_ROW, NUM>(0, it.hash_top_logS, it, none, p0, n, st); break;
         case RB_H512: launch_hash_bin<MODE_ROW, NUM>(1, it.hash_top_logS, it, none, p0, n, st); break;
@@ -814,9 +880,20 @@ template <bool NUM>
 static void chunks_impl(const ChunkItems& it, int bin, int64_t p0, int64_t n, hipStream_t st) {
     RowItems none{};
     switch (bin) {
-        case CB_DENSE:
-            launch_window<MODE_CHUNK, NUM, 1024, 1>(none, it, p0, n, it.width, st);
+        case CB_DENSE: {
+            const int64_t W = it.width;
+            if (W < 32 || (W & (W - 1)))
+                throw std::logic_error("window width must be a power of two >= 32");
+            const size_t lds = (size_t)((NUM ? W * 8 : 0) + W + (W / 32) * 4 * 2);
+            if (lds > 160 * 1024) throw OverflowError("dense window exceeds LDS");
+            auto kern = k_chunk_window<NUM>;
+            SG_HIP(hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+            hipLaunchKernelGGL(kern, dim3(grid_1d(n)), dim3(kChunkWinNT), lds, st, it, p0, n,
+                               ilog2(W));
+            SG_LAUNCH_CHECK();
             break;
+        }
         case CB_H128:
         case CB_H512:
         case CB_H2048:
