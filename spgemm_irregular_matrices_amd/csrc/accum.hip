@@ -546,8 +546,18 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
             if constexpr (NUM) v[k] = ci.bval[start + t];
         }
     }
+    // A numeric chunk whose W one-byte flags fit in its value array marks
+    // its columns there with plain byte stores (lanes of a wave often share
+    // a bitmap word, on which atomic ORs serialise), packed into the bitmap
+    // afterwards; the values take the array over once the flags are packed.
+    const bool flags = NUM && W <= TW * KPT * 8;
     if constexpr (!kTwoLevel) {
-        for (int w = tt; w < NWD; w += TW) bits[w] = 0u;
+        if (flags) {
+            const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+            for (int i = tt; i < W / 16; i += TW) ((uint4*)vals)[i] = z4;
+        } else {
+            for (int w = tt; w < NWD; w += TW) bits[w] = 0u;
+        }
         __syncthreads();
     }
     if constexpr (kTwoLevel) {
@@ -564,20 +574,35 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
             if (tt == 0) ci.cnt[out] = nnz;
         return;
     }
-#pragma unroll
-    for (int k = 0; k < KPT; ++k)
-        if (idx[k] < (uint32_t)W) atomicOr(&bits[idx[k] >> 5], 1u << (idx[k] & 31));
-    __syncthreads();
+    const int64_t off = NUM ? ci.off[out] : 0;
     const int per = (NWD + TW - 1) / TW;
     const int w0 = min(NWD, tt * per), w1 = min(NWD, w0 + per);
     int pc = 0;
-    for (int w = w0; w < w1; ++w) pc += __popc(bits[w]);
+    if (flags) {
+        uint8_t* fb = (uint8_t*)vals;
+#pragma unroll
+        for (int k = 0; k < KPT; ++k)
+            if (idx[k] < (uint32_t)W) fb[idx[k]] = 1;
+        __syncthreads();
+        for (int w = w0; w < w1; ++w) {
+            const uint32_t m = pack_flags32((const uint32_t*)vals + w * 8);
+            bits[w] = m;
+            pc += __popc(m);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < KPT; ++k)
+            if (idx[k] < (uint32_t)W) atomicOr(&bits[idx[k] >> 5], 1u << (idx[k] & 31));
+        __syncthreads();
+        for (int w = w0; w < w1; ++w) pc += __popc(bits[w]);
+    }
     if constexpr (!NUM) {
         int tot = team_sum<TW>(pc, red_sh);
         if (tt == 0) ci.cnt[out] = tot;
     } else {
+        // the scan's barrier also ends every thread's packing of the flags
         int tot;
-        int pre = team_exclusive_scan<TW>(pc, red_sh, &tot);
+        int pre = block_scan_first<TW>(pc, red_sh, &tot);
         for (int w = w0; w < w1; ++w) {
             wpre[w] = pre;
             pre += __popc(bits[w]);
@@ -604,7 +629,6 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
             }
         }
         __syncthreads();
-        const int64_t off = ci.off[out];
         for (int r = tt; r < tot; r += TW) {
             ci.Ccol[off + r] = scol[r];
             ci.Cval[off + r] = vals[r];
