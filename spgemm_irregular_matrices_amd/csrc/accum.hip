@@ -513,7 +513,7 @@ __global__ __launch_bounds__(TW) void k_acc_hash(RowItems ri, ChunkItems ci, int
 template <bool NUM, int TW, int KPT>
 __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int64_t nitems,
                                                  int logW) {
-    extern __shared__ int64_t lds_r[];
+    extern __shared__ __align__(16) int64_t lds_r[];
     const int W = 1 << logW;
     const int NWD = W >> 5;
     double* vals = (double*)lds_r;                                // TW*KPT (NUM)
