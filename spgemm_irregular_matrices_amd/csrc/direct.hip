@@ -196,8 +196,12 @@ void direct_gather_values(const int32_t* bperm, const double* bval, int64_t nnz,
 // One staged entry of a round: its slice's start in the partitioned B less
 // the round's product prefix at the entry, so that the round's product p of
 // the entry is B entry base + p, and its a value; 16 bytes, one LDS access.
+// The direct path takes B with at most INT32_MAX entries, so B positions
+// (and base, which lies above -2^31) are kept in 32 bits: fewer registers
+// per product in flight.
 struct alignas(16) StagedEntry {
-    int64_t base;
+    int32_t base;
+    int32_t pad;
     double a;
 };
 
@@ -210,7 +214,7 @@ __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int6
                                             int* s_pre, StagedEntry* s_e, int* red_sh) {
     const int tt = threadIdx.x;
     int len = 0;
-    int64_t lo = 0;
+    int32_t lo = 0;
     double a = 0.0;
     if (tt < NE && q < q1) {
         const int32_t k = d.Acol[q];
@@ -230,7 +234,7 @@ __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int6
         pre = team_scan_fast<TW>(len, red_sh, &tot);
     if (tt < NE) {
         s_pre[tt] = pre;
-        s_e[tt] = StagedEntry{lo - pre, a};
+        s_e[tt] = StagedEntry{(int32_t)(lo - pre), 0, a};
     }
     __syncthreads();
     return tot;
@@ -242,7 +246,7 @@ __device__ __forceinline__ int direct_stage(const DirectArgs& d, int64_t q, int6
 // slice then counts as empty).
 template <bool OCC>
 __device__ __forceinline__ void stage_load(const DirectArgs& d, int64_t q, bool valid, int s,
-                                           double& a, int64_t& lo, int& len) {
+                                           double& a, int32_t& lo, int& len) {
     const int32_t k = d.Acol[q];
     a = d.Aval[q];
     lo = 0;
@@ -258,13 +262,13 @@ __device__ __forceinline__ void stage_load(const DirectArgs& d, int64_t q, bool 
 // Puts a round loaded by stage_load into LDS as direct_stage does (one entry
 // per thread of the team); returns the round's products.
 template <int TW>
-__device__ __forceinline__ int stage_commit(double a, int64_t lo, int len, int* s_pre,
+__device__ __forceinline__ int stage_commit(double a, int32_t lo, int len, int* s_pre,
                                             StagedEntry* s_e, int* red_sh) {
     const int tt = threadIdx.x;
     int tot;
     const int pre = team_scan_fast<TW>(len, red_sh, &tot);
     s_pre[tt] = pre;
-    s_e[tt] = StagedEntry{lo - pre, a};
+    s_e[tt] = StagedEntry{(int32_t)(lo - pre), 0, a};
     __syncthreads();
     return tot;
 }
@@ -321,7 +325,7 @@ __device__ __forceinline__ int chunk_entry_fast(const int* s_pre, int ne, int ba
 // round arrives in registers (a0, lo0, len0: this thread's entry q0 + tt).
 template <int TW, int KPT, bool OCC>
 __device__ __forceinline__ void rank_item(const DirectArgs& d, int32_t x, int64_t q0, int64_t q1,
-                                          int64_t off, double a0, int64_t lo0, int len0,
+                                          int64_t off, double a0, int32_t lo0, int len0,
                                           double* vals, uint32_t* bits, int* wpre, int* s_pre,
                                           StagedEntry* s_e, int* red_sh) {
     const int W = 1 << d.logW;
@@ -345,7 +349,7 @@ __device__ __forceinline__ void rank_item(const DirectArgs& d, int32_t x, int64_
                             ? stage_commit<TW>(a0, lo0, len0, s_pre, s_e, red_sh)
                             : direct_stage<TW, TW, OCC>(d, qb + tt, q1, s, s_pre, s_e, red_sh);
         const int ne = (int)min((int64_t)TW, q1 - qb);
-        int64_t bi[KPT];
+        int32_t bi[KPT];
         double av[KPT];
         int j = 0;
 #pragma unroll
@@ -455,7 +459,7 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
     // index is clamped into the row so that every thread's loads stay in
     // bounds. All loads of the items are issued before any is used.
     double a[IPG];
-    int64_t lo[IPG];
+    int32_t lo[IPG];
     int len[IPG];
     if constexpr (!OCC) {
         int32_t k[IPG];
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
             k[u] = d.Acol[q];
             a[u] = d.Aval[q];
         }
-        int64_t hi[IPG];
+        int32_t hi[IPG];
 #pragma unroll
         for (int u = 0; u < IPG; ++u) {
             const int s = (int)((uint32_t)x[u] & (uint32_t)(d.req - 1));
@@ -504,7 +508,7 @@ __global__ __launch_bounds__(TW) void k_direct_rank(DirectArgs d, int64_t p0, in
 template <bool OCC>
 __device__ __forceinline__ void run_item(const DirectArgs& d, int64_t hdr, int64_t q0, int ne,
                                          int64_t off, int jl, int ds, int epr, double a0,
-                                         int64_t lo0, int len0, int WR, double* vals, void* rk,
+                                         int32_t lo0, int len0, int WR, double* vals, void* rk,
                                          int* s_pre, StagedEntry* s_e, int* s_cb) {
     constexpr int KPT = kRunKPT;
     static_assert(kWave * KPT == kRunMax, "one wavefront holds a run's products");
@@ -523,7 +527,7 @@ __device__ __forceinline__ void run_item(const DirectArgs& d, int64_t hdr, int64
     int done = 0;
     for (int eb = 0; eb < ne; eb += epr) {
         double a = a0;
-        int64_t lo = lo0;
+        int32_t lo = lo0;
         int len = len0;
         if (eb > 0) {
             const int j = eb + jl;
@@ -542,9 +546,9 @@ __device__ __forceinline__ void run_item(const DirectArgs& d, int64_t hdr, int64
         const int inc = wave_inclusive_scan(len);
         const int tot = __shfl(inc, kWave - 1, kWave);
         s_pre[lane] = inc - len;
-        s_e[lane] = StagedEntry{lo - (inc - len), a};
+        s_e[lane] = StagedEntry{(int32_t)(lo - (inc - len)), 0, a};
         wave_lds_sync();
-        int64_t bi[KPT];
+        int32_t bi[KPT];
         double av[KPT];
         int cb[KPT];
         int j = 0;
@@ -616,7 +620,7 @@ __global__ __launch_bounds__(kWave) void k_direct_runs(DirectArgs d, int64_t nru
     // a run has products, so its row has an entry: the index is clamped
     // into the row and every load stays in bounds
     double a[IPG];
-    int64_t lo[IPG];
+    int32_t lo[IPG];
     int len[IPG];
     int32_t k[IPG];
     int64_t q[IPG];
@@ -626,7 +630,7 @@ __global__ __launch_bounds__(kWave) void k_direct_runs(DirectArgs d, int64_t nru
         k[u] = d.Acol[q[u]];
         a[u] = d.Aval[q[u]];
     }
-    int64_t hi[IPG];
+    int32_t hi[IPG];
 #pragma unroll
     for (int u = 0; u < IPG; ++u) {
         const int s = (int)((uint32_t)hdr[u] & (uint32_t)(d.req - 1)) + ds[u];
@@ -694,7 +698,7 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
     // window is cleared, so that the clearing runs while they arrive (a
     // dense item has entries: the index is clamped into its row)
     double a0 = 0.0;
-    int64_t lo0 = 0;
+    int32_t lo0 = 0;
     int len0 = 0;
     if (tt < kDirectNE)
         stage_load<OCC>(d, q0 + min((int64_t)tt, q1 - q0 - 1), q0 + tt < q1, s, a0, lo0, len0);
@@ -715,7 +719,7 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
             const int pre = block_scan_first<kDirectNE>(len0, red_sh, &tot);
             if (tt < kDirectNE) {
                 s_pre[tt] = pre;
-                s_e[tt] = StagedEntry{lo0 - pre, a0};
+                s_e[tt] = StagedEntry{(int32_t)(lo0 - pre), 0, a0};
             }
             __syncthreads();
         } else {
@@ -730,7 +734,7 @@ __global__ __launch_bounds__(kDirectWinNT) void k_direct_window(DirectArgs d, in
         const int c0 = wv * cpw, c1 = min(nch, c0 + cpw);
         int jc = c0 < c1 ? direct_find(s_pre, ne, c0 * kWave, 0) : 0;
         for (int cb = c0; cb < c1; cb += kDirectU) {
-            int64_t bi[kDirectU];
+            int32_t bi[kDirectU];
             double av[kDirectU];
 #pragma unroll
             for (int u = 0; u < kDirectU; ++u) {
