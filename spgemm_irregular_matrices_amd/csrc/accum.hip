@@ -865,10 +865,12 @@ static void launch_rank_bin(int hb, const ChunkItems& ci, int64_t p0, int64_t n,
     switch (hb) {
         case 0: launch_rank<NUM, 64, 1>(ci, p0, n, st); break;
         case 1: launch_rank<NUM, 64, 4>(ci, p0, n, st); break;
-        case 2: launch_rank<NUM, 128, 8>(ci, p0, n, st); break;
+        // four elements a thread in the block-sized classes: with eight, the
+        // kernel reaches 64 VGPRs and LDS bounds its groups to 22 waves a CU
+        case 2: launch_rank<NUM, 256, 4>(ci, p0, n, st); break;
         default:
             // the top light class holds chunks of at most tau elements
-            if (ci.hash_top_logS <= 12) launch_rank<NUM, 256, 8>(ci, p0, n, st);
+            if (ci.hash_top_logS <= 12) launch_rank<NUM, 512, 4>(ci, p0, n, st);
             else launch_rank<NUM, 512, 16>(ci, p0, n, st);
             break;
     }
