@@ -154,7 +154,7 @@ def copy_calibration(mib: int):
 PHASE_KERNELS = {
     "numeric:multisplit": ["k_multisplit<true,"],
     "numeric:outer_prod": ["k_expand<true>"],
-    "numeric:heavy_accum": ["k_acc_window<1,true,", "k_acc_rank<true,", "k_acc_hash<1,true,"],
+    "numeric:heavy_accum": ["k_chunk_window<true", "k_acc_rank<true,", "k_acc_hash<1,true,"],
     "numeric:direct_dense": ["k_direct_window"],
     "numeric:direct_rank": ["k_direct_rank<", "k_gather_bval"],
 }
