@@ -272,6 +272,38 @@ def test_runs_of_small_items(W):
     compare(A, B, rp, col, val)
 
 
+@pytest.mark.parametrize("W", [8192, 16384])
+def test_page_dataflow_chunk_classes(W):
+    """The page's dataflow (outer product into C-hat, multisplit, chunk
+    accumulation) with final chunks of 257-1024, 1025-2048 and more than
+    tau = 2048 elements: the 256- and 512-thread rank teams and the chunk
+    window. At W = 8192 both rank teams mark columns with byte flags in
+    their value arrays; at W = 16384 the 256-thread team's flags no longer
+    fit there and it sets the bitmap with atomic ORs."""
+    ncols, nb = 4 * W, 2048
+    B = synth.distinct_uniform_rows(np.full(nb, 30, dtype=np.int64), ncols, seed=121,
+                                    value_seed=122)
+    lens = np.array([100] * 20 + [200] * 20 + [400] * 5 + [3] * 50, dtype=np.int64)
+    A = synth.distinct_uniform_rows(lens, nb, seed=123, value_seed=124)
+    # products per (heavy row, final chunk): every class above is populated
+    blen = np.diff(B.rowptr)
+    sizes = []
+    for i in range(A.nrows):
+        ks = A.col[A.rowptr[i]:A.rowptr[i + 1]]
+        cols = np.concatenate([B.col[B.rowptr[k]:B.rowptr[k + 1]] for k in ks])
+        if blen[ks].sum() > 2048:
+            sizes += np.bincount(cols // W, minlength=4).tolist()
+    sizes = np.array(sizes)
+    for lo, hi in ((256, 1024), (1024, 2048), (2048, 1 << 30)):
+        assert ((sizes > lo) & (sizes <= hi)).any(), (lo, hi)
+    lds = 160 * 1024 if W > 8192 else 0
+    rp, col, val, st = run_gpu(A, B, tau_override=2048, chunk_width_override=W,
+                               lds_budget_bytes=lds, numeric_mode=2)
+    assert st["numeric_path"] == 2 and st["final_chunk_width"] == W, st
+    assert st["heavy_rows"] == 45
+    compare(A, B, rp, col, val)
+
+
 def test_short_b_rows_over_many_slots():
     """B rows of 4 entries over 2^18 columns (32 slots): most (B row, slot)
     slices of a heavy row's items are empty, so the items test the slices'
