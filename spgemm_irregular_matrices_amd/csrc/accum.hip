@@ -506,46 +506,22 @@ __global__ __launch_bounds__(TW) void k_acc_hash(RowItems ri, ChunkItems ci, int
 // bitmap in LDS. Pass 1 sets the bitmap from the chunk's columns (kept in
 // registers); a prefix sum over the word popcounts gives every present
 // column its rank, i.e. its place in the sorted output; pass 2 adds each
-// value into a compact array at that rank. Output r is written by thread
-// r mod TW after finding the r-th set bit (binary search over the word
-// prefix, then a select inside the word), so writes are coalesced and the
-// work is proportional to the chunk, not to W.
+// value into a compact array at that rank. Each thread then writes the
+// columns of its own bitmap words at their ranks into LDS, and the chunk is
+// streamed out with coalesced writes.
+// One chunk of at most TW*KPT elements, its columns (idx, ~0 for none) and
+// values already in registers: bitmap, ranks, values summed at their rank,
+// the chunk written sorted (or its distinct count, symbolic).
 template <bool NUM, int TW, int KPT>
-__global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int64_t nitems,
-                                                 int logW) {
-    extern __shared__ __align__(16) int64_t lds_r[];
-    const int W = 1 << logW;
+__device__ __forceinline__ void rank_chunk(const ChunkItems& ci, int W, const uint32_t (&idx)[KPT],
+                                           double (&v)[KPT], int64_t out, int32_t lo,
+                                           double* vals, uint32_t* bits, int* wpre,
+                                           int32_t* scol, int* red_sh) {
     const int NWD = W >> 5;
-    double* vals = (double*)lds_r;                                // TW*KPT (NUM)
-    uint32_t* bits = (uint32_t*)(vals + (NUM ? TW * KPT : 0));    // NWD
-    int* wpre = (int*)(bits + NWD);                               // NWD (NUM)
-    int32_t* scol = (int32_t*)(wpre + NWD);                       // TW*KPT (NUM)
-    __shared__ int red_sh[TW / kWave + 1];
     const int tt = threadIdx.x;
-    const int64_t item = blockIdx.x;
-    if (item >= nitems) return;
-    const int64_t start = ci.rp[p0 + item];
-    const int count = (int)(ci.rp[p0 + item + 1] - start);
-    const int64_t out = ci.map[p0 + item];
     // one-wave chunks are ranked through the two-level bitmap (work by
     // element); the larger ones through the chunk's full bitmap
     constexpr bool kTwoLevel = TW == kWave;
-    // Every thread reads the chunk's first column itself (one address for
-    // the group), and the elements are loaded before the bitmap is cleared,
-    // so that no barrier stands between the chunk's header and its loads.
-    const int32_t lo = chunk_lo(ci, start, out, W);
-    uint32_t idx[KPT];
-    double v[KPT];
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) {
-        int t = tt + k * TW;
-        idx[k] = 0xffffffffu;
-        if (t < count) {
-            idx[k] = ci.bcol16 ? (uint32_t)ci.bcol16[start + t]
-                               : (uint32_t)(ci.bcol[start + t] - lo);
-            if constexpr (NUM) v[k] = ci.bval[start + t];
-        }
-    }
     // A numeric chunk whose W one-byte flags fit in its value array marks
     // its columns there with plain byte stores (lanes of a wave often share
     // a bitmap word, on which atomic ORs serialise), packed into the bitmap
@@ -632,6 +608,68 @@ __global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int6
         for (int r = tt; r < tot; r += TW) {
             ci.Ccol[off + r] = scol[r];
             ci.Cval[off + r] = vals[r];
+        }
+    }
+}
+
+// IPG consecutive chunks of a class per work group, one after the other:
+// every thread reads a chunk's first column itself (one address for the
+// group), and all the chunks' elements are loaded before the first is
+// ranked, so that no barrier stands between a chunk's header and its loads
+// and the later chunks' loads are paid while the first one is ranked.
+template <bool NUM, int TW, int KPT, int IPG>
+__global__ __launch_bounds__(TW) void k_acc_rank(ChunkItems ci, int64_t p0, int64_t nitems,
+                                                 int logW) {
+    extern __shared__ __align__(16) int64_t lds_r[];
+    const int W = 1 << logW;
+    const int NWD = W >> 5;
+    double* vals = (double*)lds_r;                                // TW*KPT (NUM)
+    uint32_t* bits = (uint32_t*)(vals + (NUM ? TW * KPT : 0));    // NWD
+    int* wpre = (int*)(bits + NWD);                               // NWD (NUM)
+    int32_t* scol = (int32_t*)(wpre + NWD);                       // TW*KPT (NUM)
+    __shared__ int red_sh[TW / kWave + 1];
+    const int tt = threadIdx.x;
+    const int64_t i0 = (int64_t)blockIdx.x * IPG;
+    if (i0 >= nitems) return;
+    const int nown = (int)min((int64_t)IPG, nitems - i0);  // uniform over the group
+    int64_t start[IPG], out[IPG];
+    int count[IPG];
+    int32_t lo[IPG];
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) {
+        const int64_t it = p0 + i0 + min(u, nown - 1);
+        start[u] = ci.rp[it];
+        count[u] = (int)(ci.rp[it + 1] - start[u]);
+        out[u] = ci.map[it];
+    }
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) lo[u] = chunk_lo(ci, start[u], out[u], W);
+    uint32_t idx[IPG][KPT];
+    double v[IPG][KPT];
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) {
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const int t = tt + k * TW;
+            idx[u][k] = 0xffffffffu;
+            v[u][k] = 0.0;
+            if (t < count[u]) {
+                idx[u][k] = ci.bcol16 ? (uint32_t)ci.bcol16[start[u] + t]
+                                      : (uint32_t)(ci.bcol[start[u] + t] - lo[u]);
+                if constexpr (NUM) v[u][k] = ci.bval[start[u] + t];
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < IPG; ++u) {
+        if (u < nown) {
+            // the previous chunk's output has read the LDS arrays
+            if (u > 0) {
+                if constexpr (TW == kWave) wave_lds_sync();
+                else __syncthreads();
+            }
+            rank_chunk<NUM, TW, KPT>(ci, W, idx[u], v[u], out[u], lo[u], vals, bits, wpre, scol,
+                                     red_sh);
         }
     }
 }
@@ -808,6 +846,9 @@ __global__ __launch_bounds__(kChunkWinNT) void k_chunk_window(ChunkItems ci, int
 }
 
 // ---------------------------------------------------------------- launchers
+// chunks per work group of the bitmap-rank classes
+constexpr int kRankIPG = 2;
+
 template <int MODE, bool NUM, int TW, int LOGS>
 static void launch_hash(const RowItems& ri, const ChunkItems& ci, int64_t p0, int64_t n,
                         hipStream_t st) {
@@ -819,17 +860,18 @@ static void launch_hash(const RowItems& ri, const ChunkItems& ci, int64_t p0, in
     SG_LAUNCH_CHECK();
 }
 
-template <bool NUM, int TW, int KPT>
+template <bool NUM, int TW, int KPT, int IPG = kRankIPG>
 static void launch_rank(const ChunkItems& ci, int64_t p0, int64_t n, hipStream_t st) {
     const int64_t W = ci.width;
     size_t lds = (NUM ? (size_t)TW * KPT * 12 : 0) + (size_t)(W / 32) * 4 * (NUM ? 2 : 1);
     if (TW == kWave)  // the two-level arrays and 16-bit ranked columns after the values
         lds = (NUM ? (size_t)TW * KPT * 8 : 0) + (size_t)wave_rank_lds(KPT, W) +
               (size_t)TW * KPT * 2;
-    auto kern = k_acc_rank<NUM, TW, KPT>;
+    auto kern = k_acc_rank<NUM, TW, KPT, IPG>;
     SG_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds));
-    hipLaunchKernelGGL(kern, dim3(grid_1d(n)), dim3(TW), lds, st, ci, p0, n, ilog2(W));
+    hipLaunchKernelGGL(kern, dim3(grid_1d(ceil_div(n, IPG))), dim3(TW), lds, st, ci, p0, n,
+                       ilog2(W));
     SG_LAUNCH_CHECK();
 }
 
@@ -871,7 +913,7 @@ static void launch_rank_bin(int hb, const ChunkItems& ci, int64_t p0, int64_t n,
         default:
             // the top light class holds chunks of at most tau elements
             if (ci.hash_top_logS <= 12) launch_rank<NUM, 512, 4>(ci, p0, n, st);
-            else launch_rank<NUM, 512, 16>(ci, p0, n, st);
+            else launch_rank<NUM, 512, 16, 1>(ci, p0, n, st);
             break;
     }
 }
