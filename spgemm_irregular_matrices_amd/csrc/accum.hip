@@ -509,6 +509,7 @@ __global__ __launch_bounds__(TW) void k_acc_hash(RowItems ri, ChunkItems ci, int
 // value into a compact array at that rank. Each thread then writes the
 // columns of its own bitmap words at their ranks into LDS, and the chunk is
 // streamed out with coalesced writes.
+
 // One chunk of at most TW*KPT elements, its columns (idx, ~0 for none) and
 // values already in registers: bitmap, ranks, values summed at their rank,
 // the chunk written sorted (or its distinct count, symbolic).
