@@ -56,8 +56,11 @@ typedef enum {
     SPGEMM_ERR_HIP = -7,           /* a HIP runtime call failed                     */
     SPGEMM_ERR_NOT_READY = -8,     /* numeric called before a successful symbolic   */
     SPGEMM_ERR_CAPACITY = -9,      /* spgemm_multiply: C has more entries than room */
-    SPGEMM_ERR_SCRATCH_LIMIT = -10 /* spgemm_multiply_noalloc: the product needs more
-                                      workspace than its fixed scratch buffer holds */
+    SPGEMM_ERR_SCRATCH_LIMIT = -10, /* spgemm_multiply_noalloc: the product needs more
+                                       workspace than its fixed scratch buffer holds */
+    SPGEMM_ERR_INTERNAL = -11       /* a self-check of a plan with debug_dump = 1 failed:
+                                       a multisplit level's chunk sizes do not add up to
+                                       its input (a library bug, not a caller error)  */
 } spgemm_status;
 
 /* A CSR matrix (gMAGNUS page, Section II-A). `rowptr` has nrows+1 entries
@@ -84,7 +87,11 @@ typedef struct {
     int64_t chunk_width_override; /* final chunk width (power of two >= 32); 0 = derived  */
     int32_t nchunks_cap;          /* cap on chunks per level (power of two >= 2); 0 = 32  */
     int32_t validate_inputs;      /* 1 = check rowptr and column ranges (default 1)       */
-    int32_t debug_dump;           /* 1 = keep copies of C-hat and each C-hat-reord level  */
+    int32_t debug_dump;           /* 1 = keep copies of C-hat and each C-hat-reord level,
+                                     fill new value workspace with NaN, and check after
+                                     each multisplit level that its chunk sizes add up to
+                                     the level's input (Sigma u of the heavy rows at level
+                                     0); a failed check returns INTERNAL                  */
     int32_t timing;               /* 1 = time every phase with HIP events                 */
     int64_t max_batch_products;   /* heavy products per row batch; 0 = one batch          */
     int32_t symbolic_mode;        /* heavy-row symbolic pass: 0 = auto, 1 = fused per-row

@@ -21,7 +21,7 @@ STATUS = {
     0: "SPGEMM_OK", -1: "SPGEMM_ERR_INVALID_ARG", -2: "SPGEMM_ERR_DIM_MISMATCH",
     -3: "SPGEMM_ERR_INDEX_RANGE", -4: "SPGEMM_ERR_OVERFLOW", -5: "SPGEMM_ERR_OUT_OF_MEMORY",
     -6: "SPGEMM_ERR_PLAN_MISMATCH", -7: "SPGEMM_ERR_HIP", -8: "SPGEMM_ERR_NOT_READY",
-    -9: "SPGEMM_ERR_CAPACITY", -10: "SPGEMM_ERR_SCRATCH_LIMIT",
+    -9: "SPGEMM_ERR_CAPACITY", -10: "SPGEMM_ERR_SCRATCH_LIMIT", -11: "SPGEMM_ERR_INTERNAL",
 }
 CAPACITY = -9
 SCRATCH_LIMIT = -10

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <string>
+#include <type_traits>
 #include <unordered_map>
 
 #include "common.h"
@@ -21,6 +22,13 @@ class Arena {
     // pass it fails as if the device had no more memory.
     void set_limit(size_t bytes) { limit_ = bytes; }
 
+    // Debug aid: floating-point buffers are filled with NaN (all bits set)
+    // when they are allocated, so that a read of workspace nothing wrote
+    // shows up in the results. Index buffers are left alone: a poisoned
+    // index would send a kernel outside its arrays. Not with a region (that
+    // mode promises no calls beyond the caller's kernels).
+    void set_poison(bool on) { poison_ = on; }
+
     // Carve every buffer out of the device range [base, base + bytes)
     // instead of allocating: while a region is set the arena calls neither
     // hipMalloc nor hipFree. Buffers are laid out one after the other in
@@ -35,7 +43,8 @@ class Arena {
 
     // Device buffer `name` with room for at least `bytes`. Growing frees the
     // old buffer (hipFree waits for the device, so no kernel still uses it).
-    void* get(const std::string& name, size_t bytes) {
+    void* get(const std::string& name, size_t bytes, bool* fresh = nullptr) {
+        if (fresh) *fresh = false;
         Buf& b = bufs_[name];
         if (bytes == 0) bytes = 1;
         if (region_ && b.cap < bytes) {
@@ -76,13 +85,23 @@ class Arena {
             b.p = p;
             b.cap = cap;
             total_ += cap;
+            if (fresh) *fresh = true;
         }
         return b.p;
     }
 
     template <class T>
     T* get(const std::string& name, size_t count) {
-        return static_cast<T*>(get(name, count * sizeof(T)));
+        bool fresh = false;
+        T* p = static_cast<T*>(get(name, count * sizeof(T), &fresh));
+        if constexpr (std::is_floating_point<T>::value) {
+            if (fresh && poison_ && !region_) {
+                if (hipMemset(p, 0xff, bufs_[name].cap) != hipSuccess ||
+                    hipDeviceSynchronize() != hipSuccess)
+                    throw HipError(hipGetLastError(), "poisoning a workspace buffer");
+            }
+        }
+        return p;
     }
 
     size_t total_bytes() const { return total_; }
@@ -103,6 +122,7 @@ class Arena {
     std::unordered_map<std::string, Buf> bufs_;
     size_t total_ = 0;  // bytes held (with a region: the end of its last buffer)
     size_t limit_ = 0;
+    bool poison_ = false;
     char* region_ = nullptr;
     size_t region_cap_ = 0;
 };

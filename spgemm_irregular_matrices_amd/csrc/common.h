@@ -30,6 +30,11 @@ struct OverflowError : std::runtime_error {
 struct ScratchError : std::runtime_error {
     using std::runtime_error::runtime_error;
 };
+// A debug self-check found a broken internal invariant; carried as
+// SPGEMM_ERR_INTERNAL.
+struct InternalError : std::runtime_error {
+    using std::runtime_error::runtime_error;
+};
 
 #define SG_HIP(call)                                                              \
     do {                                                                          \

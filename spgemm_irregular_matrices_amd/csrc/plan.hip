@@ -185,6 +185,40 @@ int64_t* d2h(spgemm_plan p, const int64_t* dsrc, int64_t n, hipStream_t st) {
     return p->host;
 }
 
+// Self-checks of a debug plan (debug_dump), on the host.
+// A level's chunk sizes add up to its input: every element of the level's
+// rows (Sigma u of the heavy rows at level 0, the heavy chunks' elements
+// below) falls in exactly one chunk. rp is the level's exclusive scan of the
+// sizes of its npos nonempty chunks.
+void check_level_sizes(spgemm_plan p, const int64_t* rp, int64_t npos, int64_t total, int l,
+                       hipStream_t st) {
+    if (!p->opt.debug_dump) return;
+    const int64_t sum = d2h(p, rp + npos, 1, st)[0];
+    if (sum != total)
+        throw InternalError("multisplit level " + std::to_string(l) + ": chunk sizes add up to " +
+                            std::to_string(sum) + ", the level's input is " +
+                            std::to_string(total));
+}
+
+// After a multisplit every chunk's cursor has moved from its start to the
+// next chunk's start: no element was lost or placed twice.
+void check_cursors(spgemm_plan p, const int64_t* cursor, const int64_t* rp, int64_t npos, int l,
+                   hipStream_t st) {
+    if (!p->opt.debug_dump || npos <= 0) return;
+    std::vector<int64_t> cur((size_t)npos), end((size_t)npos);
+    SG_HIP(hipMemcpyAsync(cur.data(), cursor, (size_t)npos * sizeof(int64_t),
+                          hipMemcpyDeviceToHost, st));
+    SG_HIP(hipMemcpyAsync(end.data(), rp + 1, (size_t)npos * sizeof(int64_t),
+                          hipMemcpyDeviceToHost, st));
+    SG_HIP(hipStreamSynchronize(st));
+    for (int64_t i = 0; i < npos; ++i)
+        if (cur[(size_t)i] != end[(size_t)i])
+            throw InternalError("multisplit level " + std::to_string(l) + ": chunk " +
+                                std::to_string(i) + " filled to " +
+                                std::to_string(cur[(size_t)i]) + ", it ends at " +
+                                std::to_string(end[(size_t)i]));
+}
+
 // GetMagnusParams (Section III-D). Readings of the garbled formulas:
 // Eq. (4): tau = s_LM / (alpha * (s_col + s_val)), alpha = 2, so that a hash
 // table of tau entries at load factor 1/alpha fills the local memory;
@@ -464,12 +498,14 @@ void symbolic_batch_multisplit(spgemm_plan p, BatchState& bt, const DevCSR& A, c
             reord_rowptr(counts, inv, S_l.npos, rp, ar, st);
             copy<int64_t>(cursor, rp, S_l.npos, st);
         }
+        check_level_sizes(p, rp, S_l.npos, total, l, st);
         int32_t* out = bufc[(l + 1) & 1];
         {
             PhaseScope ps(p, 0, SPGEMM_PHASE_MULTISPLIT, st);
             multisplit(g, bufc[l & 1], nullptr, pos, cursor, out, nullptr, false, ar, st);
             add_bytes(p, 0, SPGEMM_PHASE_MULTISPLIT, 8.0 * total + 8.0 * (R + 1));
         }
+        check_cursors(p, cursor, rp, S_l.npos, l, st);
         if (dump) debug_copy_level(p, l, S_l, rp, out, nullptr, inv, st);
         fill<int64_t>(nnz_l, S_l.nnat, 0, st);
         {
@@ -559,6 +595,7 @@ void symbolic_batch_fused(spgemm_plan p, BatchState& bt, const int64_t* elem_fin
             PhaseScope ps(p, 0, SPGEMM_PHASE_HISTO, st);
             reord_rowptr(counts, inv, S_l.npos, rp, ar, st);
         }
+        check_level_sizes(p, rp, S_l.npos, total, l, st);
         nat_cur[l] += S_l.nnat;
         rp_cur[l] += S_l.npos + 1;
         bt.L = l + 1;
@@ -1150,6 +1187,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
                               (c16 ? 22.0 : 24.0) * S_l.total_in + 8.0 * (S_l.R + 1));
                 }
             }
+            check_cursors(p, cursor, rp, S_l.npos, l, st);
             if (dump) debug_copy_level(p, l, S_l, rp, bufc[outb], bufv[outb], inv, st);
             {
                 ChunkItems ci{};
@@ -1186,6 +1224,8 @@ int guarded(F&& f) {
         return SPGEMM_ERR_OVERFLOW;
     } catch (const ScratchError&) {
         return SPGEMM_ERR_SCRATCH_LIMIT;
+    } catch (const InternalError&) {
+        return SPGEMM_ERR_INTERNAL;
     } catch (const HipError& e) {
         if (e.code == hipErrorOutOfMemory) return SPGEMM_ERR_OUT_OF_MEMORY;
         return SPGEMM_ERR_HIP;
@@ -1290,6 +1330,7 @@ SPGEMM_API int spgemm_plan_create(spgemm_plan* out, const spgemm_options* opt) {
         auto* p = new spgemm_plan_s();
         p->opt = o;
         p->ar.set_limit((size_t)o.workspace_limit_bytes);
+        p->ar.set_poison(o.debug_dump != 0);
         if (hipGetDevice(&p->device) != hipSuccess) {
             delete p;
             return SPGEMM_ERR_HIP;
@@ -1481,6 +1522,7 @@ SPGEMM_API const char* spgemm_status_string(int status) {
         case SPGEMM_ERR_CAPACITY: return "C has more entries than the room given";
         case SPGEMM_ERR_SCRATCH_LIMIT:
             return "product needs more workspace than the fixed scratch buffer holds";
+        case SPGEMM_ERR_INTERNAL: return "internal self-check failed (debug plan)";
         default: return "unknown status";
     }
 }

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(-10, 1):
+    for code in range(-11, 1):
         s = binding.status_string(code)
         assert s and s != "unknown status"
     assert binding.status_string(-99) == "unknown status"

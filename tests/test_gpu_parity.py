@@ -820,6 +820,34 @@ def test_every_multisplit_level_matches_oracle(numeric_mode, width, cap, nlevels
     compare(A, B, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), C.val.cpu().numpy())
 
 
+@pytest.mark.parametrize("modes", [(1, 1), (1, 2), (2, 1), (2, 2)])
+def test_debug_plan_self_checks(modes):
+    """A debug plan (debug_dump) fills new floating-point workspace with NaN
+    and checks on the host, after every multisplit level, that the level's
+    chunk sizes add up to its input and that every chunk was filled to its
+    end. Over three levels, in both symbolic and both level-forming numeric
+    modes, the checks pass (the call returns OK), with row batches too, and
+    the product still meets the oracle: no value was read from workspace
+    that nothing wrote."""
+    import torch
+    from spgemm_irregular_matrices_amd import binding
+    A = synth.random_csr(400, 300, seed=171, value_seed=172, mean_len=12, skew=1.3)
+    B = synth.random_csr(300, 700, seed=173, value_seed=174, mean_len=14, skew=1.3)
+    dA, dB = binding.DeviceCSR.from_host(A), binding.DeviceCSR.from_host(B)
+    for budget in (0, 4000):
+        with binding.Plan(tau_override=24, chunk_width_override=32, nchunks_cap=4,
+                          debug_dump=True, symbolic_mode=modes[0], numeric_mode=modes[1],
+                          max_batch_products=budget) as p:
+            C = p.multiply(dA, dB)
+            torch.cuda.synchronize()
+            st = p.stats()
+        assert st["nlevels"] == 3 and st["numeric_path"] == modes[1], st
+        assert (st["nbatches"] > 1) == (budget > 0), st
+        val = C.val.cpu().numpy()
+        assert not np.isnan(val).any()
+        compare(A, B, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), val)
+
+
 @pytest.mark.parametrize("ncols", [1 << 12, 1 << 20, 1 << 24])
 def test_light_hash_rows_wide_columns(ncols):
     """Light rows whose columns spread over the whole range take the hash bins.
