@@ -1034,12 +1034,19 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         }
     } join{false, st, p->lst, p->ev_join};
     const hipStream_t lst = fork ? p->lst : st;
-    if (fork) {
-        SG_HIP(hipEventRecord(p->ev_fork, st));
-        SG_HIP(hipStreamWaitEvent(p->lst, p->ev_fork, 0));
-        join.on = true;
-    }
-    {
+    // The light rows start beside the direct path's items at once. Beside
+    // the page's dataflow they start with its first accumulation, so that
+    // they share the GPU with the latency-bound accumulators rather than
+    // with the outer product and multisplit, which stream at HBM speed.
+    bool light_queued = false;
+    auto queue_light = [&]() {
+        if (light_queued) return;
+        light_queued = true;
+        if (fork) {
+            SG_HIP(hipEventRecord(p->ev_fork, st));
+            SG_HIP(hipStreamWaitEvent(p->lst, p->ev_fork, 0));
+            join.on = true;
+        }
         PhaseScope ps(p, 1, SPGEMM_PHASE_LIGHT_ACCUM, lst);
         for (int b = RB_T8; b <= RB_H8192; ++b)
             accumulate_rows(ri, b, p->row_bins[b], p->row_bins[b + 1] - p->row_bins[b], true, lst);
@@ -1050,7 +1057,8 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         add_bytes(p, 1, SPGEMM_PHASE_LIGHT_ACCUM,
                   28.0 * nl + 28.0 * p->light_annz + 12.0 * p->stats.light_products +
                       12.0 * p->light_cnnz);
-    }
+    };
+    if (p->H == 0 || p->direct) queue_light();
     if (p->H == 0) return;
 
     if (p->direct) {
@@ -1147,6 +1155,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
             ci.Ccol = C_col;
             ci.Cval = C_val;
             ci.width = q.final_width;
+            queue_light();
             PhaseScope ps(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, st);
             accumulate_chunks(ci, CB_DENSE, 0, R0, true, st);
             add_bytes(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, 12.0 * bt.N);
@@ -1204,6 +1213,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
                 ci.Ccol = C_col;
                 ci.Cval = C_val;
                 ci.width = q.width[l];
+                queue_light();
                 PhaseScope ps(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, st);
                 for (int b = CB_DENSE; b <= CB_H8192; ++b)
                     accumulate_chunks(ci, b, S_l.bins[b], S_l.bins[b + 1] - S_l.bins[b], true, st);
@@ -1212,6 +1222,7 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
             rp_in = rp;
         }
     }
+    queue_light();
 }
 
 template <class F>
