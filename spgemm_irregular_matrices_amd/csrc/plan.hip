@@ -1223,6 +1223,9 @@ void numeric_impl(spgemm_plan p, const DevCSR& A, const DevCSR& B, const int64_t
         }
     }
     queue_light();
+    // every heavy row's output entries, written once by the accumulators
+    // (column and value, 12 B)
+    add_bytes(p, 1, SPGEMM_PHASE_HEAVY_ACCUM, 12.0 * (p->stats.nnz_c - p->light_cnnz));
 }
 
 template <class F>
