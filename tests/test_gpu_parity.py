@@ -848,6 +848,23 @@ def test_debug_plan_self_checks(modes):
         compare(A, B, C.rowptr.cpu().numpy(), C.col.cpu().numpy(), val)
 
 
+def test_heavy_rows_beyond_the_direct_slots():
+    """Heavy rows over 2^26 columns: 8192 final chunks of 8192 columns are more
+    than the direct path's 4096 slots and the row bitmap of the fused
+    symbolic pass does not fit LDS, so the default options take the
+    multisplit symbolic pass and the fused first level (path 1). The
+    heaviest row (2.4 M products) needs all three levels (32 x 32 x 8
+    chunks); the one-entry rows stay light."""
+    lens = np.array([2000, 1800, 1500, 1200] + [1] * 200, dtype=np.int64)
+    A = synth.distinct_uniform_rows(lens, 2000, seed=182, value_seed=183)
+    B = synth.distinct_uniform_rows(np.full(2000, 1200, dtype=np.int64), 1 << 26, seed=184,
+                                    value_seed=185)
+    rp, col, val, st = run_gpu(A, B)
+    assert st["numeric_path"] == 1 and st["nlevels"] == 3, st
+    assert st["heavy_rows"] == 4 and st["vchunks"][:3] == [32, 32, 8], st
+    compare(A, B, rp, col, val)
+
+
 @pytest.mark.parametrize("ncols", [1 << 12, 1 << 20, 1 << 24])
 def test_light_hash_rows_wide_columns(ncols):
     """Light rows whose columns spread over the whole range take the hash bins.
