@@ -733,6 +733,7 @@ static void ms_launch(const LevelGeom& g, const int32_t* in_col, const double* i
 // measured fastest on MI355X among 128..1024 threads x 4..16 elements.
 constexpr int kMsNT = 256;
 constexpr int kMsK = 8;
+constexpr int kMsKFused = 4;  // the tiles that form their own products
 
 void multisplit(const LevelGeom& g, const int32_t* in_col, const double* in_val,
                 const int32_t* pos_of, int64_t* cursor, int32_t* out_col, double* out_val,
@@ -763,8 +764,10 @@ void expand_multisplit(const LevelGeom& g, const FusedRows& fr, const DevCSR& A,
     fs.Aval = A.val;
     fs.Bcol = B.col;
     fs.Bval = B.val;
-    if (out16) ms_launch<true, true, true, kMsNT, kMsK>(g, nullptr, nullptr, pos_of, cursor, out_col, out_val, fs, ar, st);
-    else ms_launch<true, false, true, kMsNT, kMsK>(g, nullptr, nullptr, pos_of, cursor, out_col, out_val, fs, ar, st);
+    // four elements a thread: with eight, forming the products in the tile
+    // takes 96 VGPRs (five waves a SIMD); with four, 52 (eight)
+    if (out16) ms_launch<true, true, true, kMsNT, kMsKFused>(g, nullptr, nullptr, pos_of, cursor, out_col, out_val, fs, ar, st);
+    else ms_launch<true, false, true, kMsNT, kMsKFused>(g, nullptr, nullptr, pos_of, cursor, out_col, out_val, fs, ar, st);
 }
 
 // First column of every chunk of a level: level 0 chunk c of a row starts at
