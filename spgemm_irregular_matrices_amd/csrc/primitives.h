@@ -73,18 +73,20 @@ __global__ __launch_bounds__(kScanNT) void k_scan_reduce(F f, int64_t n, int64_t
 // through LDS, so that global loads and stores are coalesced (consecutive
 // lanes, consecutive elements) while each thread scans 16 consecutive
 // elements; one padding word every 32 keeps the per-thread reads apart in
-// the banks.
+// the banks. The tile holds values of the output type (every element and
+// prefix fits it), so a 32-bit scan takes half the LDS and twice the
+// resident groups.
 template <class F, class T = int64_t>
 __global__ __launch_bounds__(kScanNT) void k_scan_apply(F f, int64_t n, const int64_t* tile_off,
                                                         T* out) {
     __shared__ int64_t sh[kScanNT / kWave + 1];
-    __shared__ int64_t tile[kScanTile + kScanTile / 32];
+    __shared__ T tile[kScanTile + kScanTile / 32];
     const int64_t base = (int64_t)blockIdx.x * kScanTile;
 #pragma unroll 4
     for (int j = 0; j < kScanIPT; ++j) {
         const int idx = j * kScanNT + threadIdx.x;
         const int64_t i = base + idx;
-        tile[idx + (idx >> 5)] = i < n ? f(i) : 0;
+        tile[idx + (idx >> 5)] = (T)(i < n ? f(i) : 0);
     }
     __syncthreads();
     int64_t v[kScanIPT];
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(kScanNT) void k_scan_apply(F f, int64_t n, const in
 #pragma unroll
     for (int j = 0; j < kScanIPT; ++j) {
         const int idx = threadIdx.x * kScanIPT + j;
-        tile[idx + (idx >> 5)] = pre;
+        tile[idx + (idx >> 5)] = (T)pre;
         pre += v[j];
         if (base + idx == n - 1) out[n] = (T)pre;
     }
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(kScanNT) void k_scan_apply(F f, int64_t n, const in
     for (int j = 0; j < kScanIPT; ++j) {
         const int idx = j * kScanNT + threadIdx.x;
         const int64_t i = base + idx;
-        if (i < n) out[i] = (T)tile[idx + (idx >> 5)];
+        if (i < n) out[i] = tile[idx + (idx >> 5)];
     }
 }
 
