@@ -177,19 +177,35 @@ void direct_offsets(const int64_t* C_rp, const int32_t* hrows, int64_t H, int re
 }
 
 // ---------------------------------------------------------------- numeric
-__global__ void k_gather_bval(const int32_t* bperm, const double* bval, int64_t nnz,
-                              double* out) {
-    int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (; j < nnz; j += stride) out[j] = bval[bperm[j]];
+// kGatherU placement-map entries a thread, their value loads issued together
+// (where B's columns are spread evenly over the slots, every load is a
+// random line: their latency, not bytes, bounds the gather).
+constexpr int kGatherU = 4;
+
+__global__ __launch_bounds__(256) void k_gather_bval(const int32_t* bperm, const double* bval,
+                                                     int64_t nnz, double* out) {
+    const int64_t j0 = (int64_t)blockIdx.x * (256 * kGatherU) + threadIdx.x;
+    int32_t src[kGatherU];
+#pragma unroll
+    for (int u = 0; u < kGatherU; ++u) {
+        const int64_t j = j0 + u * 256;
+        src[u] = j < nnz ? bperm[j] : -1;
+    }
+    double v[kGatherU];
+#pragma unroll
+    for (int u = 0; u < kGatherU; ++u) v[u] = src[u] >= 0 ? bval[src[u]] : 0.0;
+#pragma unroll
+    for (int u = 0; u < kGatherU; ++u) {
+        const int64_t j = j0 + u * 256;
+        if (j < nnz) out[j] = v[u];
+    }
 }
 
 void direct_gather_values(const int32_t* bperm, const double* bval, int64_t nnz, double* out,
                           hipStream_t st) {
     if (nnz <= 0) return;
-    const int64_t blocks = std::min<int64_t>(ceil_div(nnz, 256), 8192);
-    hipLaunchKernelGGL(k_gather_bval, dim3(grid_1d(blocks)), dim3(256), 0, st, bperm, bval, nnz,
-                       out);
+    hipLaunchKernelGGL(k_gather_bval, dim3(grid_1d(ceil_div(nnz, 256 * kGatherU))), dim3(256), 0,
+                       st, bperm, bval, nnz, out);
     SG_LAUNCH_CHECK();
 }
 
